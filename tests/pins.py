@@ -1,0 +1,191 @@
+"""Independent checks ("pins") of the fp64 oracle.
+
+Each function runs the oracle library given as ``lib`` on small inputs and
+returns the largest deviation from a result obtained another way: a dense
+product-sum of transition matrices, exact rational arithmetic, the single-chunk
+closed form solved by numpy, or closed forms of special cases.  None of them
+re-calls the oracle's own loop to produce the expected value.
+
+The update being pinned is the gated delta rule per head
+    S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,  o_t = S_t^T q_t,
+the reading taken for the channel-gated delta-rule attention the pages describe
+(blog.csdn.net article on the Kimi K3 report, section 一.1).
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+
+
+def _rand_inputs(rng, T, dk, dv, unit_keys=True, s0=True):
+    q = rng.standard_normal((T, dk))
+    k = rng.standard_normal((T, dk))
+    if unit_keys:
+        k /= np.linalg.norm(k, axis=1, keepdims=True)
+        q /= np.linalg.norm(q, axis=1, keepdims=True)
+    v = rng.standard_normal((T, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(T)))
+    la = -1.0 / (1.0 + np.exp(-rng.standard_normal((T, dk))))
+    S0 = rng.standard_normal((dk, dv)) * 0.5 if s0 else np.zeros((dk, dv))
+    return q, k, v, la, beta, S0
+
+
+def _run(lib, q, k, v, la, beta, S0):
+    o, ST = oracle.prefill(q[None, None], k[None, None], v[None, None], la[None, None],
+                           beta[None, None], S0[None, None], lib=lib, nthreads=1)
+    return o[0, 0], ST[0, 0]
+
+
+def pin_product_sum(lib, seed=0) -> float:
+    """Dense transition matrices A_t = (I - b k k^T) Diag(a); S_t as the unrolled
+    product-sum  A_t..A_1 S0 + sum_s A_t..A_{s+1} b_s k_s v_s^T;  o_t = S_t^T q_t."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (T, dk, dv) in [(1, 1, 1), (5, 2, 3), (9, 4, 4), (16, 8, 8), (13, 8, 2), (16, 3, 8)]:
+        q, k, v, la, beta, S0 = _rand_inputs(rng, T, dk, dv)
+        A = [(np.eye(dk) - beta[t] * np.outer(k[t], k[t])) @ np.diag(np.exp(la[t])) for t in range(T)]
+        o_ref = np.zeros((T, dv))
+        for t in range(T):
+            P = np.eye(dk)
+            for j in range(t, -1, -1):
+                P = P @ A[j]
+            S_t = P @ S0
+            for s in range(t + 1):
+                Ps = np.eye(dk)
+                for j in range(t, s, -1):
+                    Ps = Ps @ A[j]
+                S_t = S_t + Ps @ (beta[s] * np.outer(k[s], v[s]))
+            o_ref[t] = S_t.T @ q[t]
+        o, ST = _run(lib, q, k, v, la, beta, S0)
+        worst = max(worst, np.abs(o - o_ref).max(), np.abs(ST - S_t).max())
+    return float(worst)
+
+
+def pin_exact_rational(lib, seed=1) -> float:
+    """Exact Fraction arithmetic on dyadic inputs; the gate enters as log(a) of a
+    rational a, so the oracle sees exp(log a) = a to within one rounding."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (T, dk, dv) in [(3, 1, 1), (4, 2, 2), (6, 3, 2), (5, 2, 3)]:
+        def dy(n, lo=-8, hi=8, den=8):
+            return [Fraction(int(x), den) for x in rng.integers(lo, hi + 1, size=n)]
+        q = [dy(dk) for _ in range(T)]
+        k = [dy(dk) for _ in range(T)]
+        v = [dy(dv) for _ in range(T)]
+        beta = [Fraction(int(x), 8) for x in rng.integers(0, 9, size=T)]
+        a = [[Fraction(int(x), 16) for x in rng.integers(4, 17, size=dk)] for _ in range(T)]
+        S = [[Fraction(int(x), 4) for x in rng.integers(-4, 5, size=dv)] for _ in range(dk)]
+        S0 = [row[:] for row in S]
+        o_ref = []
+        for t in range(T):
+            D = [[a[t][i] * S[i][j] for j in range(dv)] for i in range(dk)]
+            kD = [sum(k[t][i] * D[i][j] for i in range(dk)) for j in range(dv)]
+            # (I - b k k^T) D + b k v^T, entry by entry
+            S = [[D[i][j] - beta[t] * k[t][i] * kD[j] + beta[t] * k[t][i] * v[t][j]
+                  for j in range(dv)] for i in range(dk)]
+            o_ref.append([sum(S[i][j] * q[t][i] for i in range(dk)) for j in range(dv)])
+        f = lambda m: np.array([[float(x) for x in r] for r in m])
+        la = np.array([[math.log(float(x)) for x in r] for r in a])
+        o, ST = _run(lib, f(q), f(k), f(v), la, np.array([float(b) for b in beta]), f(S0))
+        worst = max(worst, np.abs(o - f(o_ref)).max(), np.abs(ST - f(S)).max())
+    return float(worst)
+
+
+def pin_chunk_closed_form(lib, seed=2) -> float:
+    """One chunk in closed form: with g = cumsum(log a), Qh = q e^g, Kh = k e^g,
+    A = strict_lower((k e^g)(k e^-g)^T), P = lower((q e^g)(k e^-g)^T):
+        (I + diag(b) A) Delta = diag(b) (V - Kh S0)      (numpy.linalg.solve)
+        O = Qh S0 + P Delta,   S_T = Diag(e^{g_T}) S0 + (k e^{g_T - g})^T Delta."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (T, dk, dv) in [(1, 4, 4), (7, 8, 8), (16, 8, 4), (16, 16, 16), (11, 5, 7)]:
+        q, k, v, la, beta, S0 = _rand_inputs(rng, T, dk, dv)
+        g = np.cumsum(la, axis=0)
+        Qh, Kh, Kb = q * np.exp(g), k * np.exp(g), k * np.exp(-g)
+        A = np.tril(Kh @ Kb.T, -1)
+        P = np.tril(Qh @ Kb.T, 0)
+        Delta = np.linalg.solve(np.eye(T) + np.diag(beta) @ A, np.diag(beta) @ (v - Kh @ S0))
+        O = Qh @ S0 + P @ Delta
+        ST = np.diag(np.exp(g[-1])) @ S0 + (k * np.exp(g[-1] - g)).T @ Delta
+        o, st = _run(lib, q, k, v, la, beta, S0)
+        worst = max(worst, np.abs(o - O).max(), np.abs(st - ST).max())
+    return float(worst)
+
+
+def pin_beta_zero(lib, seed=3) -> float:
+    """beta = 0: nothing is written, S_t = Diag(prod_{j<=t} a_j) S0 and o_t = S_t^T q_t."""
+    rng = np.random.default_rng(seed)
+    T, dk, dv = 40, 8, 6
+    q, k, v, la, beta, S0 = _rand_inputs(rng, T, dk, dv)
+    beta[:] = 0.0
+    o, ST = _run(lib, q, k, v, la, beta, S0)
+    g = np.cumsum(la, axis=0)
+    o_ref = np.stack([(np.exp(g[t])[:, None] * S0).T @ q[t] for t in range(T)])
+    S_ref = np.exp(g[-1])[:, None] * S0
+    return float(max(np.abs(o - o_ref).max(), np.abs(ST - S_ref).max()))
+
+
+def pin_replacement(lib, seed=4) -> float:
+    """a = 1, b = 1, orthonormal keys: each write replaces the value stored under its
+    key, so k_s^T S_T = v_s^T for every s and S_T = (I - K^T K) S0 + K^T V."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (T, dk, dv) in [(1, 4, 3), (5, 8, 8), (8, 8, 5), (12, 16, 16)]:
+        Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+        k = Qm[:T].copy()
+        q = rng.standard_normal((T, dk))
+        v = rng.standard_normal((T, dv))
+        la = np.zeros((T, dk))
+        beta = np.ones(T)
+        S0 = rng.standard_normal((dk, dv))
+        _, ST = _run(lib, q, k, v, la, beta, S0)
+        worst = max(worst, np.abs(k @ ST - v).max(),
+                    np.abs(ST - ((np.eye(dk) - k.T @ k) @ S0 + k.T @ v)).max())
+    return float(worst)
+
+
+def pin_scalar(lib) -> float:
+    """dk = dv = 1: s_t = a_t (1 - b_t k_t^2) s_{t-1} + b_t k_t v_t, o_t = q_t s_t,
+    evaluated exactly with Fractions."""
+    a = [Fraction(1, 2), Fraction(3, 4), Fraction(1, 1), Fraction(7, 8)]
+    b = [Fraction(1, 2), Fraction(1, 4), Fraction(1, 1), Fraction(0, 1)]
+    k = [Fraction(1), Fraction(-1, 2), Fraction(3, 4), Fraction(2)]
+    v = [Fraction(2), Fraction(1), Fraction(-3, 2), Fraction(5)]
+    q = [Fraction(1), Fraction(2), Fraction(-1), Fraction(1, 2)]
+    s = Fraction(1)
+    outs = []
+    for t in range(4):
+        s = a[t] * (1 - b[t] * k[t] ** 2) * s + b[t] * k[t] * v[t]
+        outs.append(q[t] * s)
+    c = lambda xs: np.array([[float(x)] for x in xs])
+    o, ST = _run(lib, c(q), c(k), c(v), np.array([[math.log(float(x))] for x in a]),
+                 np.array([float(x) for x in b]), np.array([[1.0]]))
+    return float(max(np.abs(o[:, 0] - c(outs)[:, 0]).max(), abs(ST[0, 0] - float(s))))
+
+
+def pin_affine(lib, seed=5) -> float:
+    """The end state is affine in the start state: S_T(S0) = M S0 + S_T(0), where M is
+    the end state of the same tokens run from S0 = I with v = 0."""
+    rng = np.random.default_rng(seed)
+    T, dk, dv = 37, 8, 5
+    q, k, v, la, beta, S0 = _rand_inputs(rng, T, dk, dv)
+    la *= 0.05
+    _, S_full = _run(lib, q, k, v, la, beta, S0)
+    _, S_zero = _run(lib, q, k, v, la, beta, np.zeros((dk, dv)))
+    _, M = _run(lib, q, k, np.zeros((T, dk)), la, beta, np.eye(dk))
+    return float(np.abs(S_full - (M @ S0 + S_zero)).max())
+
+
+ALL_PINS = {
+    "product_sum": (pin_product_sum, 1e-12),
+    "exact_rational": (pin_exact_rational, 1e-12),
+    "chunk_closed_form": (pin_chunk_closed_form, 1e-10),
+    "beta_zero": (pin_beta_zero, 1e-13),
+    "replacement": (pin_replacement, 1e-12),
+    "scalar": (pin_scalar, 1e-14),
+    "affine": (pin_affine, 1e-12),
+}
