@@ -1,0 +1,179 @@
+"""Python binding of libkda (Kimi Delta Attention on MI355X).
+
+Argument marshalling only: every call checks tensor shapes, dtypes and devices,
+allocates outputs with torch, and passes raw device pointers plus the current
+HIP stream to the C-ABI in ``libkda.so`` (declared in ``include/libkda.h``).
+All arithmetic runs in the library's HIP kernels; there is no fallback.  If the
+library is missing, loading fails with an error that says how to build it.
+
+Entry points (same names as the C-ABI):
+    prefill(q, k, v, log_alpha, beta, S0=None)        -> (o, S_T)
+    decode_step(q, k, v, log_alpha, beta, S)           -> o          (S updated in place)
+    segment_transfer(k, v, log_alpha, beta, G)         -> (S_zero_end, M)
+    segment_merge(S_zero_end, M, S_in=None)            -> (S_start, S_T)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+_DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libkda.so (built by ``python __graft_entry__.py`` / ``build.py``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise KdaError(f"libkda.so not found at {LIB_PATH}; build it with "
+                       "`python gated_delta_rule_104_amd/build.py` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.kda_chunk_prefill.argtypes = [vp] * 8 + [i] * 6 + [vp]
+    lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
+    lib.kda_segment_transfer.argtypes = [vp] * 6 + [i] * 7 + [vp]
+    lib.kda_segment_merge.argtypes = [vp] * 5 + [i] * 5 + [vp]
+    for f in (lib.kda_chunk_prefill, lib.kda_decode_step, lib.kda_segment_transfer,
+              lib.kda_segment_merge):
+        f.restype = i
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        lib = load()
+        raise KdaError(f"{what}: {lib.kda_status_string(rc).decode()} "
+                       f"({lib.kda_last_error().decode()})")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _io(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
+    if not t.is_cuda:
+        raise KdaError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise KdaError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise KdaError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise KdaError(f"{name} must be contiguous")
+
+
+def prefill(q, k, v, log_alpha, beta, S0=None, o=None, S_T=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunked prefill.  q, k, log_alpha [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T];
+    S0 [B,H,dk,dv] fp32 or None.  Returns o [B,H,T,dv] (input dtype) and S_T fp32."""
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dt = k.dtype
+    if dt not in _DT:
+        raise KdaError(f"unsupported dtype {dt}")
+    for name, t, shp in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                         ("log_alpha", log_alpha, (B, H, T, dk)), ("beta", beta, (B, H, T))):
+        _io(t, name, dt, shp)
+    if S0 is not None:
+        _io(S0, "S0", torch.float32, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=k.device)
+    if S_T is None:
+        S_T = torch.empty(B, H, dk, dv, dtype=torch.float32, device=k.device)
+    _io(o, "o", dt, (B, H, T, dv))
+    _io(S_T, "S_T", torch.float32, (B, H, dk, dv))
+    rc = load().kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                                  _ptr(o), _ptr(S_T), B, H, T, dk, dv, _DT[dt], _stream())
+    _check(rc, "kda_chunk_prefill")
+    return o, S_T
+
+
+def decode_step(q, k, v, log_alpha, beta, S, o=None) -> torch.Tensor:
+    """One token for N*H heads.  q, k, log_alpha [N,H,dk]; v [N,H,dv]; beta [N,H];
+    S [N,H,dk,dv] fp32, updated in place.  Returns o [N,H,dv]."""
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    dt = k.dtype
+    if dt not in _DT:
+        raise KdaError(f"unsupported dtype {dt}")
+    for name, t, shp in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("v", v, (N, H, dv)),
+                         ("log_alpha", log_alpha, (N, H, dk)), ("beta", beta, (N, H))):
+        _io(t, name, dt, shp)
+    _io(S, "S", torch.float32, (N, H, dk, dv))
+    if o is None:
+        o = torch.empty(N, H, dv, dtype=dt, device=k.device)
+    _io(o, "o", dt, (N, H, dv))
+    rc = load().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                                _ptr(o), N, H, dk, dv, _DT[dt], _stream())
+    _check(rc, "kda_decode_step")
+    return o
+
+
+def segment_transfer(k, v, log_alpha, beta, G: int, S_zero_end=None, M=None):
+    """Per-segment zero-start end states [G,B,H,dk,dv] and transfer maps [G,B,H,dk,dk]
+    for sequences of T = G * Tseg tokens."""
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dt = k.dtype
+    if dt not in _DT:
+        raise KdaError(f"unsupported dtype {dt}")
+    if G <= 0 or T % G:
+        raise KdaError(f"T={T} is not a positive multiple of G={G}")
+    for name, t, shp in (("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                         ("log_alpha", log_alpha, (B, H, T, dk)), ("beta", beta, (B, H, T))):
+        _io(t, name, dt, shp)
+    if S_zero_end is None:
+        S_zero_end = torch.empty(G, B, H, dk, dv, dtype=torch.float32, device=k.device)
+    if M is None:
+        M = torch.empty(G, B, H, dk, dk, dtype=torch.float32, device=k.device)
+    _io(S_zero_end, "S_zero_end", torch.float32, (G, B, H, dk, dv))
+    _io(M, "M", torch.float32, (G, B, H, dk, dk))
+    rc = load().kda_segment_transfer(_ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S_zero_end),
+                                     _ptr(M), B, H, G, T // G, dk, dv, _DT[dt], _stream())
+    _check(rc, "kda_segment_transfer")
+    return S_zero_end, M
+
+
+def segment_merge(S_zero_end, M, S_in=None, want_start: bool = True, S_start=None, S_T=None):
+    """Sequential merge.  Returns (S_start [G,B,H,dk,dv] or None, S_T [B,H,dk,dv])."""
+    G, B, H, dk, dv = S_zero_end.shape
+    _io(S_zero_end, "S_zero_end", torch.float32, (G, B, H, dk, dv))
+    _io(M, "M", torch.float32, (G, B, H, dk, dk))
+    if S_in is not None:
+        _io(S_in, "S_in", torch.float32, (B, H, dk, dv))
+    if want_start and S_start is None:
+        S_start = torch.empty_like(S_zero_end)
+    if S_start is not None:
+        _io(S_start, "S_start", torch.float32, (G, B, H, dk, dv))
+    if S_T is None:
+        S_T = torch.empty(B, H, dk, dv, dtype=torch.float32, device=M.device)
+    _io(S_T, "S_T", torch.float32, (B, H, dk, dv))
+    rc = load().kda_segment_merge(_ptr(S_in), _ptr(S_zero_end), _ptr(M), _ptr(S_start), _ptr(S_T),
+                                  B, H, G, dk, dv, _stream())
+    _check(rc, "kda_segment_merge")
+    return S_start, S_T

@@ -1,0 +1,35 @@
+"""Build libkda.so (HIP, gfx950) in-tree with hipcc.
+
+All device code is compiled for gfx950 only, with packed-fp32 instructions
+disabled (hipcc is told `-target-feature -packed-fp32-ops`).  The library is
+written next to this file as ``libkda.so``.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libkda.so")
+SOURCES = ["kda_api.hip", "kda_chunk.hip", "kda_decode.hip", "kda_merge.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def build(out: str = LIB, verbose: bool = False, extra=()) -> str:
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-function", *extra,
+           "-I", os.path.join(HERE, "..", "include"),
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
+    sys.exit(0)

@@ -1,0 +1,236 @@
+// C-ABI of libkda: host-side validation, launch geometry and error mapping.
+// Every check runs before anything is enqueued, so a rejected call writes
+// nothing.  See include/libkda.h for the contract of each entry point.
+#include "../../include/libkda.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "kda_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kda_status fail(kda_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kda_status fail(kda_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kda_status ok() {
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+kda_status hip_fail(hipError_t e, const char* what) {
+  return fail(KDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device (cached per device id).
+int cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Consumer waves per workgroup: the largest of 4, 2, 1 that still gives at
+// least one workgroup per compute unit (or 1).  KDA_NC overrides for tuning.
+// The fp32 variant keeps more live state per wave and is capped at 2.
+int pick_nc(long long nseq, int ncol_tiles, bool bf16_io) {
+  const int ncmax = bf16_io ? 4 : 2;
+  const char* env = getenv("KDA_NC");
+  if (env) {
+    const int v = atoi(env);
+    if ((v == 1 || v == 2 || v == 4) && v <= ncmax && ncol_tiles % v == 0) return v;
+  }
+  const long long cus = cu_count();
+  for (int nc = ncmax; nc >= 1; nc >>= 1) {
+    if (ncol_tiles % nc) continue;
+    if (nseq * (ncol_tiles / nc) >= cus) return nc;
+  }
+  return 1;
+}
+
+kda_status check_dims(int dk, int dv) {
+  if (dk != dv) return fail(KDA_ERR_SHAPE, "dk (%d) must equal dv (%d)", dk, dv);
+  if (dk != 64 && dk != 128) return fail(KDA_ERR_UNSUPPORTED, "head size %d not supported (64 or 128)", dk);
+  return KDA_OK;
+}
+
+kda_status check_dtype(kda_dtype dt) {
+  if (dt != KDA_F32 && dt != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+  return KDA_OK;
+}
+
+#define KDA_REQUIRE(p, name)                                                     \
+  do {                                                                           \
+    if (!(p)) return fail(KDA_ERR_NULL, "%s is NULL", name);                     \
+    if (!aligned(p)) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define KDA_OPTIONAL(p, name)                                                    \
+  do {                                                                           \
+    if ((p) && !aligned(p)) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+const long long kMaxElems = (1LL << 40);
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_last_error(void) { return g_err; }
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "null pointer";
+    case KDA_ERR_SHAPE: return "invalid shape";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KDA_ERR_ALIGN: return "misaligned pointer";
+    case KDA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* beta, const float* S0, void* o, float* S_T, int B, int H,
+                             int T, int dk, int dv, kda_dtype dtype, hipStream_t stream) {
+  if (B < 0 || H < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size B=%d H=%d T=%d", B, H, T);
+  kda_status st;
+  if ((st = check_dtype(dtype)) != KDA_OK) return st;
+  if ((st = check_dims(dk, dv)) != KDA_OK) return st;
+  if (dtype == KDA_F32 && dk != 64)
+    return fail(KDA_ERR_UNSUPPORTED, "fp32 prefill supports dk = dv = 64 only (got %d)", dk);
+  const long long BH = (long long)B * H;
+  if (BH * T * dk > kMaxElems || BH > (1LL << 30)) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (BH == 0) return ok();
+  KDA_REQUIRE(S_T, "S_T");
+  KDA_OPTIONAL(S0, "S0");
+  if (T > 0) {
+    KDA_REQUIRE(q, "q");
+    KDA_REQUIRE(k, "k");
+    KDA_REQUIRE(v, "v");
+    KDA_REQUIRE(log_alpha, "log_alpha");
+    KDA_REQUIRE(beta, "beta");
+    KDA_REQUIRE(o, "o");
+  }
+  const int ntiles = dv / 16;
+  const int nc = pick_nc(BH, ntiles, dtype == KDA_BF16);
+  kda::ChunkArgs a;
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
+  a.S0 = S0; a.o = o; a.S_out = S_T; a.M_out = nullptr;
+  a.BH = (int)BH; a.G = 1; a.Tseg = T; a.vsplit = ntiles / nc;
+  const long long nwg = BH * a.vsplit;
+  if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (getenv("KDA_LOG"))
+    fprintf(stderr, "[libkda] prefill BH=%lld T=%d D=%d nc=%d vsplit=%d grid=%lld\n", BH, T, dk, nc,
+            a.vsplit, nwg);
+  hipError_t e = kda::launch_chunk(a, dtype == KDA_BF16, dk, true, nc, (int)nwg, stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_chunk_prefill launch");
+  return ok();
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                           const void* beta, float* S, void* o, int N, int H, int dk, int dv,
+                           kda_dtype dtype, hipStream_t stream) {
+  if (N < 0 || H < 0) return fail(KDA_ERR_SHAPE, "negative size N=%d H=%d", N, H);
+  kda_status st;
+  if ((st = check_dtype(dtype)) != KDA_OK) return st;
+  if ((st = check_dims(dk, dv)) != KDA_OK) return st;
+  const long long NH = (long long)N * H;
+  if (NH > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (NH == 0) return ok();
+  KDA_REQUIRE(q, "q");
+  KDA_REQUIRE(k, "k");
+  KDA_REQUIRE(v, "v");
+  KDA_REQUIRE(log_alpha, "log_alpha");
+  if (!beta) return fail(KDA_ERR_NULL, "beta is NULL");  // [N,H] rows: any element alignment
+  KDA_REQUIRE(S, "S");
+  KDA_REQUIRE(o, "o");
+  hipError_t e = kda::launch_decode(q, k, v, log_alpha, beta, S, o, (int)NH, dk, dtype == KDA_BF16, stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
+  return ok();
+}
+
+kda_status kda_segment_transfer(const void* k, const void* v, const void* log_alpha,
+                                const void* beta, float* S_zero_end, float* M, int B, int H, int G,
+                                int Tseg, int dk, int dv, kda_dtype dtype, hipStream_t stream) {
+  if (B < 0 || H < 0 || G < 0) return fail(KDA_ERR_SHAPE, "negative size B=%d H=%d G=%d", B, H, G);
+  if (Tseg < 1) return fail(KDA_ERR_SHAPE, "Tseg must be >= 1 (got %d)", Tseg);
+  kda_status st;
+  if ((st = check_dtype(dtype)) != KDA_OK) return st;
+  if ((st = check_dims(dk, dv)) != KDA_OK) return st;
+  if (dtype == KDA_F32 && dk != 64)
+    return fail(KDA_ERR_UNSUPPORTED, "fp32 segment transfer supports dk = dv = 64 only (got %d)", dk);
+  const long long BH = (long long)B * H;
+  const long long nseq = BH * G;
+  if (nseq * Tseg * dk > kMaxElems || nseq > (1LL << 30)) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (nseq == 0) return ok();
+  KDA_REQUIRE(k, "k");
+  KDA_REQUIRE(v, "v");
+  KDA_REQUIRE(log_alpha, "log_alpha");
+  KDA_REQUIRE(beta, "beta");
+  KDA_REQUIRE(S_zero_end, "S_zero_end");
+  KDA_REQUIRE(M, "M");
+  const int ntiles = (dv + dk) / 16;
+  const int nc = pick_nc(nseq, ntiles, dtype == KDA_BF16);
+  kda::ChunkArgs a;
+  a.q = nullptr; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
+  a.S0 = nullptr; a.o = nullptr; a.S_out = S_zero_end; a.M_out = M;
+  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.vsplit = ntiles / nc;
+  const long long nwg = nseq * a.vsplit;
+  if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (getenv("KDA_LOG"))
+    fprintf(stderr, "[libkda] transfer BH=%lld G=%d Tseg=%d D=%d nc=%d vsplit=%d grid=%lld\n", BH, G,
+            Tseg, dk, nc, a.vsplit, nwg);
+  hipError_t e = kda::launch_chunk(a, dtype == KDA_BF16, dk, false, nc, (int)nwg, stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_segment_transfer launch");
+  return ok();
+}
+
+kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const float* M,
+                             float* S_start, float* S_T, int B, int H, int G, int dk, int dv,
+                             hipStream_t stream) {
+  if (B < 0 || H < 0 || G < 0) return fail(KDA_ERR_SHAPE, "negative size B=%d H=%d G=%d", B, H, G);
+  kda_status st;
+  if ((st = check_dims(dk, dv)) != KDA_OK) return st;
+  const long long BH = (long long)B * H;
+  if (BH * G * dk * dk > kMaxElems || BH > (1LL << 24)) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (BH == 0) return ok();
+  KDA_REQUIRE(S_T, "S_T");
+  KDA_OPTIONAL(S_in, "S_in");
+  KDA_OPTIONAL(S_start, "S_start");
+  if (G > 0) {
+    KDA_REQUIRE(S_zero_end, "S_zero_end");
+    KDA_REQUIRE(M, "M");
+  }
+  hipError_t e = kda::launch_merge(S_in, S_zero_end, M, S_start, S_T, (int)BH, G, dk, stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_segment_merge launch");
+  return ok();
+}
+
+}  // extern "C"

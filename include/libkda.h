@@ -1,0 +1,126 @@
+/*
+ * libkda -- Kimi Delta Attention (KDA) on AMD Instinct MI355X (gfx950).
+ *
+ * KDA is a delta-rule linear attention with a channel-wise forget gate whose
+ * per-head state is a fixed-size dk x dv matrix ("Kimi K3 深度解析", section 3.1;
+ * blog.csdn.net article on the Kimi K3 report, section 一.1).  Per head and
+ * token t, with state S (dk x dv), gate alpha_t in (0,1]^dk and scalar beta_t:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                  (the output reads the updated state)
+ *
+ * No output scale and no normaliser is applied: q and k are used as given.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor pointer is a DEVICE pointer to a contiguous row-major array,
+ *    aligned to 16 bytes.  The caller owns all memory; the library allocates,
+ *    frees and synchronises nothing inside these calls.
+ *  - `dtype` gives the element type of q, k, v, log_alpha, beta and o.  States
+ *    (S0, S_T, S, S_zero_end, M, S_in, S_start) are always fp32.
+ *  - The gate is passed in log space: log_alpha = log(alpha), one value per key
+ *    channel, and must lie in [-1, 0].  The pages describe the gate as
+ *    lower-bounded so that long sequences neither overflow nor underflow
+ *    (blog.csdn.net article, section 一.1); the kernels rely on the bound
+ *    (|cumulative log-decay| <= 64 inside a 64-token chunk) and do not check it.
+ *  - Supported head sizes: dk == dv == 64 or 128.  fp32 prefill and segment
+ *    transfer support dk == dv == 64 only; decode supports both in both dtypes.
+ *  - Errors: arguments are validated on the host before anything is launched;
+ *    on error nothing is written and a status != KDA_OK is returned, with a
+ *    description in kda_last_error() (thread-local).  Work is enqueued
+ *    asynchronously on `stream`; a launch failure returns KDA_ERR_HIP.
+ *  - Calls never abort the process and keep no mutable global state other than
+ *    a per-device cache of the compute-unit count.
+ */
+#ifndef LIBKDA_H
+#define LIBKDA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,         /* a required pointer is NULL                    */
+  KDA_ERR_SHAPE = 2,        /* negative size, dk != dv, or size overflow      */
+  KDA_ERR_UNSUPPORTED = 3,  /* head size / dtype combination not built        */
+  KDA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned               */
+  KDA_ERR_HIP = 5           /* the HIP runtime reported an error              */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * Chunked prefill of B*H independent heads over T tokens.
+ * Evaluates the recurrence above exactly (up to rounding) in 64-token chunks:
+ * parallel inside a chunk, sequential across chunks ("Kimi K3 开源日来了",
+ * section "FlashKDA").
+ *   q, k, log_alpha : [B, H, T, dk]   dtype
+ *   v               : [B, H, T, dv]   dtype
+ *   beta            : [B, H, T]       dtype, in [0, 1]
+ *   S0              : [B, H, dk, dv]  fp32 start states, or NULL for zero
+ *   o               : [B, H, T, dv]   dtype, written
+ *   S_T             : [B, H, dk, dv]  fp32 end states, written; may alias S0
+ * Any T >= 0 is accepted (a last partial chunk is masked); T == 0 copies S0
+ * (or zeros) to S_T.
+ */
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* beta, const float* S0, void* o, float* S_T, int B, int H,
+                             int T, int dk, int dv, kda_dtype dtype, hipStream_t stream);
+
+/*
+ * One decode step for N*H independent heads: applies the recurrence for one
+ * token to the fp32 state held in place (the state is the fixed-size per-request
+ * KDA cache, "Kimi K3 开源日来了", section "针对适配的 Infra").
+ *   q, k, log_alpha : [N, H, dk]      dtype
+ *   v               : [N, H, dv]      dtype
+ *   beta            : [N, H]          dtype
+ *   S               : [N, H, dk, dv]  fp32, read and overwritten
+ *   o               : [N, H, dv]      dtype, written
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
+                           const void* beta, float* S, void* o, int N, int H, int dk, int dv,
+                           kda_dtype dtype, hipStream_t stream);
+
+/*
+ * First half of the context-parallel decomposition ("Kimi K3 开源日来了",
+ * section "针对适配的 Infra", KDA Context Parallelism): the sequence of every
+ * (b, h), of T = G * Tseg tokens, is cut into G segments; for each segment this
+ * computes, independently of the others,
+ *   S_zero_end : [G, B, H, dk, dv]  fp32, its end state when started from zero
+ *   M          : [G, B, H, dk, dk]  fp32, its transfer map, so that the end
+ *                state from any start state X is  M X + S_zero_end.
+ *   k, log_alpha : [B, H, T, dk] dtype;  v : [B, H, T, dv];  beta : [B, H, T].
+ * Tseg >= 1.  q is not needed.
+ */
+kda_status kda_segment_transfer(const void* k, const void* v, const void* log_alpha,
+                                const void* beta, float* S_zero_end, float* M, int B, int H, int G,
+                                int Tseg, int dk, int dv, kda_dtype dtype, hipStream_t stream);
+
+/*
+ * Second half: the exchange that recovers each segment's true start state
+ * (same section).  Per (b, h), sequentially over segments i = 0..G-1:
+ *     S_start[i] = S;   S = M[i] S + S_zero_end[i];       and finally S_T = S,
+ * starting from S = S_in (NULL for zero).  All arrays fp32:
+ *   S_in [B,H,dk,dv] or NULL; S_zero_end [G,B,H,dk,dv]; M [G,B,H,dk,dk];
+ *   S_start [G,B,H,dk,dv] or NULL (not written); S_T [B,H,dk,dv].
+ * S_T must not alias the other arrays.
+ */
+kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const float* M,
+                             float* S_start, float* S_T, int B, int H, int G, int dk, int dv,
+                             hipStream_t stream);
+
+const char* kda_status_string(kda_status status);
+const char* kda_last_error(void);
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBKDA_H */

@@ -1,0 +1,102 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every entry point
+that include/libkda.h declares, and rejects invalid arguments on the host before
+anything would be launched (these calls never reach the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libkda.h")
+
+import gated_delta_rule_104_amd as kda  # noqa: E402
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_HIP = range(6)
+F32, BF16 = 0, 1
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.lib_path()):
+        from gated_delta_rule_104_amd import build
+        build.build()
+    return kda.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("kda_chunk_prefill", "kda_decode_step", "kda_segment_transfer", "kda_segment_merge"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_abi_version() == 1
+    for st in range(6):
+        assert lib.kda_status_string(st)
+    assert lib.kda_status_string(99) == b"unknown status"
+
+
+def P(*xs):
+    return [ctypes.c_void_p(x) if x is not None else None for x in xs]
+
+
+def prefill(lib, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, o=FAKE, ST=FAKE,
+            B=1, H=1, T=64, dk=64, dv=64, dt=BF16):
+    return lib.kda_chunk_prefill(*P(q, k, v, la, beta, S0, o, ST), B, H, T, dk, dv, dt, None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, dk=64, dv=128) == ERR_SHAPE
+    assert prefill(lib, dk=96, dv=96) == ERR_UNSUPPORTED
+    assert prefill(lib, dk=128, dv=128, dt=F32) == ERR_UNSUPPORTED
+    assert prefill(lib, dt=7) == ERR_UNSUPPORTED
+    assert prefill(lib, T=-1) == ERR_SHAPE
+    assert prefill(lib, B=-2) == ERR_SHAPE
+    assert prefill(lib, q=None) == ERR_NULL
+    assert prefill(lib, ST=None) == ERR_NULL
+    assert prefill(lib, beta=FAKE + 4) == ERR_ALIGN
+    assert prefill(lib, S0=FAKE + 8) == ERR_ALIGN
+    assert b"16-byte" in lib.kda_last_error()
+    assert prefill(lib, B=1 << 20, H=1 << 10, T=1 << 20) == ERR_SHAPE
+    # nothing to do: no heads
+    assert prefill(lib, B=0) == OK
+
+
+def test_decode_validation(lib):
+    f = lib.kda_decode_step
+    assert f(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 4, 2, 128, 64, BF16, None) == ERR_SHAPE
+    assert f(*P(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE), 4, 2, 128, 128, BF16, None) == ERR_NULL
+    assert f(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE), 4, 2, 64, 64, F32, None) == ERR_ALIGN
+    assert f(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), -1, 2, 64, 64, F32, None) == ERR_SHAPE
+    assert f(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 0, 2, 64, 64, F32, None) == OK
+
+
+def test_segment_validation(lib):
+    t = lib.kda_segment_transfer
+    assert t(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1, 2, 4, 0, 128, 128, BF16, None) == ERR_SHAPE
+    assert t(*P(FAKE, FAKE, FAKE, FAKE, None, FAKE), 1, 2, 4, 64, 128, 128, BF16, None) == ERR_NULL
+    assert t(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1, 2, 4, 64, 128, 128, F32, None) == ERR_UNSUPPORTED
+    m = lib.kda_segment_merge
+    assert m(*P(None, FAKE, FAKE, None, None), 1, 2, 4, 128, 128, None) == ERR_NULL
+    assert m(*P(None, FAKE, FAKE, FAKE + 4, FAKE), 1, 2, 4, 128, 128, None) == ERR_ALIGN
+    assert m(*P(None, FAKE, FAKE, None, FAKE), 1, 2, 4, 64, 128, None) == ERR_SHAPE
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(kda.KdaError):
+        kda.prefill(x, x, x, x, torch.zeros(1, 1, 4))
