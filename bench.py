@@ -1,0 +1,234 @@
+"""Benchmark of the libkda hot path on one MI355X.
+
+One step = one kda_chunk_prefill call over B=1, H=32, T=65536, dk=dv=128, bf16
+inputs (seeded synthetic data already resident in HBM, S0 = 0).  `value` is
+sequence tokens per second of that step.  The same run also measures, outside
+the timed steps:
+  * decode: 1024 consecutive kda_decode_step calls on 256 sequences x 32 heads
+    (fp32 state 512 MiB in place), reported as % of HBM bandwidth;
+  * kcp: kda_segment_transfer + kda_segment_merge on T = 1,048,576 in 8
+    segments of 131,072 (H = 32), reported as time and effective bandwidth;
+  * cpu_baseline: the fp64 oracle on a bounded sample of the prefill workload.
+Kernel durations come from HIP events recorded on the stream the kernels are
+launched on.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gated_delta_rule_104_amd as kda  # noqa: E402
+import kda_inputs as ki  # noqa: E402
+
+METRIC = "KDA chunked-prefill tokens/sec (H=32,d=128,T=64K) + % MFMA peak; decode % HBM BW"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+CH = 64
+
+
+def prefill_bytes(B, H, T, D):
+    """Algorithmic HBM bytes of one bf16 prefill: q, k, log_alpha, v read and o
+    written once (2 B each per channel), beta read once, S_T written (fp32)."""
+    per_token_head = 2 * (3 * D + D + D) + 2
+    return B * H * T * per_token_head + B * H * D * D * 4
+
+
+def prefill_flops(B, H, T, D, triangle=False):
+    """Matrix flops per chunk-head of the chunked form (dense 16x16 tiles or
+    triangle-aware): scores A and P, the UT/WY products, the state chain."""
+    C, K, V = CH, D, D
+    if triangle:
+        per_chunk = 2 * C * C * K + C * C * (K + V) + 6 * C * K * V + C * C * V + C * C * C // 3
+    else:
+        per_chunk = 2 * (2 * C * C * K) + 2 * C * C * (K + V) + 6 * C * K * V + 2 * C * C * V \
+            + 2 * C * C * C // 3
+    nchunks = -(-T // C)
+    return B * H * nchunks * per_chunk
+
+
+def time_launches(fn, n):
+    """Mean and list of per-launch durations (ms) from events on the current stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in evs]
+    return sum(ts) / len(ts), ts
+
+
+def bench_prefill(args, dev):
+    B, H, T, D = 1, 32, 65536, 128
+    print(f"[bench] generating prefill inputs B={B} H={H} T={T} D={D} bf16", file=sys.stderr, flush=True)
+    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=2, device=dev)
+    o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    nws = kda.prefill_workspace_bytes(B, H, T, D, D, torch.bfloat16)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+
+    def step():
+        kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None, o=o, S_T=S_T, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    mean_ms, per = time_launches(step, args.steps)
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    return dict(B=B, H=H, T=T, D=D, mean_ms=mean_ms, wall_ms=wall_ms, per=per, g=g, ws_bytes=nws)
+
+
+def bench_decode(args, dev):
+    N, H, D, steps = 256, 32, 128, 1024
+    print(f"[bench] generating decode inputs N={N} H={H} D={D} steps={steps}", file=sys.stderr, flush=True)
+    S = ki.gen_decode_state(N, H, D, D, seed=4, device=dev)
+    pool = [ki.gen_decode_step(N, H, D, D, "bf16", seed=4, step=t, device=dev) for t in range(steps)]
+    o = torch.empty(N, H, D, dtype=torch.bfloat16, device=dev)
+    for t in range(8):
+        x = pool[t]
+        kda.decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], S, o=o)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for t in range(steps):
+        x = pool[t]
+        kda.decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], S, o=o)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    per_step_bytes = N * H * (2 * D * D * 4 + 2 * (3 * D + D + D) + 2)
+    step_ms = ms / steps
+    gbs = per_step_bytes / (step_ms * 1e-3) / 1e9
+    del pool
+    return dict(N=N, H=H, D=D, steps=steps, ms_total=ms, us_per_step=step_ms * 1e3,
+                tokens_per_s=N * steps / (ms * 1e-3), achieved_GBs=gbs, hbm_frac=gbs / PEAK_HBM_GBS,
+                bytes_per_step=per_step_bytes)
+
+
+def bench_kcp(args, dev):
+    B, H, G, Tseg, D = 1, 32, 8, 131072, 128
+    T = G * Tseg
+    print(f"[bench] generating kcp inputs H={H} T={T} G={G}", file=sys.stderr, flush=True)
+    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=3, device=dev)
+    del g["q"]
+    Z = torch.empty(G, B, H, D, D, dtype=torch.float32, device=dev)
+    M = torch.empty(G, B, H, D, D, dtype=torch.float32, device=dev)
+    S_start = torch.empty_like(Z)
+    S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+
+    def transfer():
+        kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], G, S_zero_end=Z, M=M)
+
+    def merge():
+        kda.segment_merge(Z, M, None, S_start=S_start, S_T=S_T)
+
+    transfer(); merge()
+    torch.cuda.synchronize()
+    t_ms, _ = time_launches(transfer, 3)
+    m_ms, _ = time_launches(merge, 3)
+    nbytes = B * H * T * (2 * (2 * D + D) + 2) + 2 * G * B * H * D * D * 4
+    del g
+    return dict(H=H, T=T, G=G, Tseg=Tseg, transfer_ms=t_ms, merge_ms=m_ms,
+                tokens_per_s=T / ((t_ms + m_ms) * 1e-3),
+                transfer_GBs=nbytes / (t_ms * 1e-3) / 1e9)
+
+
+def cpu_baseline(pf, budget_s):
+    """fp64 oracle on a bounded sample: the first `nh` heads and first `tt`
+    tokens of the same prefill inputs, sized to about `budget_s` seconds."""
+    import oracle
+    g = pf["g"]
+    H, T = pf["H"], pf["T"]
+    nthreads = oracle.max_threads()
+    nh = min(H, max(1, nthreads))
+    sl = lambda x, tt: x[:, :nh, :tt].cpu()
+    tt = 1024
+    t0 = time.perf_counter()
+    oracle.prefill(sl(g["q"], tt), sl(g["k"], tt), sl(g["v"], tt), sl(g["log_alpha"], tt), sl(g["beta"], tt))
+    cal = time.perf_counter() - t0
+    tt = int(min(T, max(1024, tt * budget_s / max(cal, 1e-3))))
+    tt = max(CH, tt - tt % CH)
+    args = [sl(g[n], tt) for n in ("q", "k", "v", "log_alpha", "beta")]
+    t0 = time.perf_counter()
+    oracle.prefill(*args, want_o=True)
+    el = time.perf_counter() - t0
+    token_heads_per_s = nh * tt / el
+    return {"value": token_heads_per_s / H, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{nh} of {H} heads x first {tt} tokens of the same inputs ({el:.1f} s); "
+                      f"scaled to whole tokens (all {H} heads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-kcp", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the KDA hot path here is single-GPU "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    kda.load()
+
+    pf = bench_prefill(args, dev)
+    B, H, T, D = pf["B"], pf["H"], pf["T"], pf["D"]
+    ms = pf["mean_ms"]
+    tok_s = B * T / (ms * 1e-3)
+    nbytes = prefill_bytes(B, H, T, D)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    fl_dense = prefill_flops(B, H, T, D)
+    fl_tri = prefill_flops(B, H, T, D, triangle=True)
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pf["wall_ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kda_prefill_b1_h32_t65536_d128_bf16", "B": B, "H": H, "T": T,
+                   "dk": D, "dv": D, "chunk": CH, "S0": "zero"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "kda_chunk_kernel<bf16,128,1,prefill>", "kernel_ms": ms,
+                     "algorithmic_bytes": nbytes},
+        "mfma": {"dense_tile_tflops": fl_dense / (ms * 1e-3) / 1e12,
+                 "dense_tile_frac": fl_dense / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                 "triangle_tflops": fl_tri / (ms * 1e-3) / 1e12,
+                 "triangle_frac": fl_tri / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                 "peak_tflops": PEAK_BF16_TFLOPS},
+    }
+    if not args.no_decode:
+        out["decode"] = bench_decode(args, dev)
+        torch.cuda.empty_cache()
+    if not args.no_kcp:
+        out["kcp"] = bench_kcp(args, dev)
+        torch.cuda.empty_cache()
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(pf, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

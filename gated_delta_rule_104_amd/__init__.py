@@ -47,7 +47,9 @@ def load() -> ctypes.CDLL:
                        "`python gated_delta_rule_104_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i = ctypes.c_void_p, ctypes.c_int
-    lib.kda_chunk_prefill.argtypes = [vp] * 8 + [i] * 6 + [vp]
+    lib.kda_chunk_prefill.argtypes = [vp] * 8 + [i] * 6 + [vp, ctypes.c_size_t, vp]
+    lib.kda_prefill_workspace_bytes.argtypes = [i] * 6
+    lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
     lib.kda_segment_transfer.argtypes = [vp] * 6 + [i] * 7 + [vp]
     lib.kda_segment_merge.argtypes = [vp] * 5 + [i] * 5 + [vp]
@@ -88,9 +90,19 @@ def _io(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> None:
         raise KdaError(f"{name} must be contiguous")
 
 
-def prefill(q, k, v, log_alpha, beta, S0=None, o=None, S_T=None) -> Tuple[torch.Tensor, torch.Tensor]:
+def prefill_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype: torch.dtype) -> int:
+    """Workspace that lets kda_chunk_prefill use its sequence-split path (0 if unused)."""
+    if dtype not in _DT:
+        raise KdaError(f"unsupported dtype {dtype}")
+    return int(load().kda_prefill_workspace_bytes(B, H, T, dk, dv, _DT[dtype]))
+
+
+def prefill(q, k, v, log_alpha, beta, S0=None, o=None, S_T=None,
+            workspace="auto") -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunked prefill.  q, k, log_alpha [B,H,T,dk]; v [B,H,T,dv]; beta [B,H,T];
-    S0 [B,H,dk,dv] fp32 or None.  Returns o [B,H,T,dv] (input dtype) and S_T fp32."""
+    S0 [B,H,dk,dv] fp32 or None.  Returns o [B,H,T,dv] (input dtype) and S_T fp32.
+    workspace: "auto" allocates what kda_prefill_workspace_bytes asks for, None
+    passes none (single-pass path), or a device uint8 tensor to use."""
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     dt = k.dtype
@@ -107,8 +119,13 @@ def prefill(q, k, v, log_alpha, beta, S0=None, o=None, S_T=None) -> Tuple[torch.
         S_T = torch.empty(B, H, dk, dv, dtype=torch.float32, device=k.device)
     _io(o, "o", dt, (B, H, T, dv))
     _io(S_T, "S_T", torch.float32, (B, H, dk, dv))
+    if isinstance(workspace, str):
+        nbytes = prefill_workspace_bytes(B, H, T, dk, dv, dt)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=k.device) if nbytes else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load().kda_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                                  _ptr(o), _ptr(S_T), B, H, T, dk, dv, _DT[dt], _stream())
+                                  _ptr(o), _ptr(S_T), B, H, T, dk, dv, _DT[dt], _ptr(workspace),
+                                  ws_bytes, _stream())
     _check(rc, "kda_chunk_prefill")
     return o, S_T
 

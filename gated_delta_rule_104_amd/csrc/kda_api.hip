@@ -54,15 +54,15 @@ int cu_count() {
   return cache[dev];
 }
 
-// Consumer waves per workgroup: the largest of 4, 2, 1 that still gives at
-// least one workgroup per compute unit (or 1).  KDA_NC overrides for tuning.
-// The fp32 variant keeps more live state per wave and is capped at 2.
+// Consumer waves per workgroup: the largest of 8, 4, 2, 1 that still gives at
+// least one workgroup per compute unit (or 1).  fp32 variants keep more live
+// state per wave and are capped at 2.  KDA_NC overrides for tuning.
 int pick_nc(long long nseq, int ncol_tiles, bool bf16_io) {
-  const int ncmax = bf16_io ? 4 : 2;
+  const int ncmax = bf16_io ? 8 : 2;
   const char* env = getenv("KDA_NC");
   if (env) {
     const int v = atoi(env);
-    if ((v == 1 || v == 2 || v == 4) && v <= ncmax && ncol_tiles % v == 0) return v;
+    if ((v == 1 || v == 2 || v == 4 || v == 8) && v <= ncmax && ncol_tiles % v == 0) return v;
   }
   const long long cus = cu_count();
   for (int nc = ncmax; nc >= 1; nc >>= 1) {
@@ -70,6 +70,46 @@ int pick_nc(long long nseq, int ncol_tiles, bool bf16_io) {
     if (nseq * (ncol_tiles / nc) >= cus) return nc;
   }
   return 1;
+}
+
+// Prefill of few heads over a long sequence: rather than splitting each head's
+// state columns over many workgroups (each of which then repeats the whole
+// per-chunk preparation), split the sequence into P segments and use the
+// context-parallel decomposition: each segment's zero-start end state and
+// transfer map, a sequential merge into true segment start states, then an
+// independent prefill of every segment.  The result is the same recurrence.
+struct PrefillPlan {
+  bool split = false;
+  int P = 1, Tseg = 0;
+  size_t ws = 0;
+};
+
+PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
+  PrefillPlan pl;
+  if (dt != KDA_BF16 || BH <= 0 || T <= 0) return pl;
+  const long long cus = cu_count();
+  const int ntiles = D / 16;
+  long long P = 0;
+  const char* env = getenv("KDA_SPLIT");
+  if (env) {
+    P = atoll(env);  // 0: never; >= 2: that many segments
+    if (P < 2) return pl;
+  } else {
+    // worth it when one pass cannot fill the chip without 4+ workgroups per head
+    if (BH * ntiles / 4 >= cus || T < 4096) return pl;
+    P = (cus + BH - 1) / BH;
+    if (P > T / 1024) P = T / 1024;
+    if (P < 2) return pl;
+  }
+  long long Tseg = (T + P - 1) / P;
+  Tseg = (Tseg + 63) / 64 * 64;
+  P = (T + Tseg - 1) / Tseg;
+  if (P < 2) return pl;
+  pl.split = true;
+  pl.P = (int)P;
+  pl.Tseg = (int)Tseg;
+  pl.ws = (size_t)3 * P * BH * D * D * sizeof(float);
+  return pl;
 }
 
 kda_status check_dims(int dk, int dv) {
@@ -96,6 +136,14 @@ kda_status check_dtype(kda_dtype dt) {
 
 const long long kMaxElems = (1LL << 40);
 
+// Kernels address one sequence through a 32-bit buffer range.
+kda_status check_seq_bytes(long long T, int dk, kda_dtype dt) {
+  const long long es = dt == KDA_BF16 ? 2 : 4;
+  if ((T + 64) * dk * es > INT32_MAX)
+    return fail(KDA_ERR_UNSUPPORTED, "sequence of %lld tokens exceeds 2 GiB per tensor and head", T);
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,9 +164,15 @@ const char* kda_status_string(kda_status s) {
   return "unknown status";
 }
 
+size_t kda_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtype dtype) {
+  if (B <= 0 || H <= 0 || T <= 0 || dk != dv || (dk != 64 && dk != 128)) return 0;
+  return plan_prefill((long long)B * H, T, dk, dtype).ws;
+}
+
 kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
                              const void* beta, const float* S0, void* o, float* S_T, int B, int H,
-                             int T, int dk, int dv, kda_dtype dtype, hipStream_t stream) {
+                             int T, int dk, int dv, kda_dtype dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || H < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size B=%d H=%d T=%d", B, H, T);
   kda_status st;
   if ((st = check_dtype(dtype)) != KDA_OK) return st;
@@ -127,6 +181,7 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
     return fail(KDA_ERR_UNSUPPORTED, "fp32 prefill supports dk = dv = 64 only (got %d)", dk);
   const long long BH = (long long)B * H;
   if (BH * T * dk > kMaxElems || BH > (1LL << 30)) return fail(KDA_ERR_SHAPE, "problem too large");
+  if ((st = check_seq_bytes(T, dk, dtype)) != KDA_OK) return st;
   if (BH == 0) return ok();
   KDA_REQUIRE(S_T, "S_T");
   KDA_OPTIONAL(S0, "S0");
@@ -138,19 +193,59 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
     KDA_REQUIRE(beta, "beta");
     KDA_REQUIRE(o, "o");
   }
+  KDA_OPTIONAL(workspace, "workspace");
+  const bool bf = dtype == KDA_BF16;
+  const int D = dk;
+  const PrefillPlan pl = plan_prefill(BH, T, D, dtype);
+  const bool split = pl.split && workspace && workspace_bytes >= pl.ws;
+  const bool log = getenv("KDA_LOG") != nullptr;
+  hipError_t e;
+  if (split) {
+    const long long nseq = BH * pl.P;
+    const size_t nS = (size_t)nseq * D * D;
+    float* Z = static_cast<float*>(workspace);
+    float* M = Z + nS;
+    float* Sst = M + nS;
+    // 1. per-segment zero-start end states and transfer maps
+    kda::ChunkArgs t;
+    t.q = nullptr; t.k = k; t.v = v; t.la = log_alpha; t.beta = beta;
+    t.S0 = nullptr; t.o = nullptr; t.S_out = Z; t.M_out = M;
+    t.BH = (int)BH; t.G = pl.P; t.Tseg = pl.Tseg; t.Ttot = T;
+    const int nt2 = 2 * D / 16, nc2 = pick_nc(nseq, nt2, bf);
+    t.vsplit = nt2 / nc2;
+    // 2. merge into true segment start states (S_T receives the merged end state,
+    //    then the segment prefill below overwrites it with its own)
+    // 3. prefill of every segment from its start state
+    kda::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
+    a.S0 = Sst; a.o = o; a.S_out = S_T; a.M_out = nullptr;
+    a.BH = (int)BH; a.G = pl.P; a.Tseg = pl.Tseg; a.Ttot = T;
+    const int nt = D / 16, nc = pick_nc(nseq, nt, bf);
+    a.vsplit = nt / nc;
+    if (log)
+      fprintf(stderr, "[libkda] prefill BH=%lld T=%d D=%d split P=%d Tseg=%d: transfer nc=%d vsplit=%d, "
+              "prefill nc=%d vsplit=%d\n", BH, T, D, pl.P, pl.Tseg, nc2, t.vsplit, nc, a.vsplit);
+    if ((e = kda::launch_chunk(t, bf, D, false, nc2, (int)(nseq * t.vsplit), stream)) != hipSuccess)
+      return hip_fail(e, "kda_chunk_prefill segment pass");
+    if ((e = kda::launch_merge(S0, Z, M, Sst, S_T, (int)BH, pl.P, D, stream)) != hipSuccess)
+      return hip_fail(e, "kda_chunk_prefill merge");
+    if ((e = kda::launch_chunk(a, bf, D, true, nc, (int)(nseq * a.vsplit), stream)) != hipSuccess)
+      return hip_fail(e, "kda_chunk_prefill segment prefill");
+    return ok();
+  }
   const int ntiles = dv / 16;
-  const int nc = pick_nc(BH, ntiles, dtype == KDA_BF16);
+  const int nc = pick_nc(BH, ntiles, bf);
   kda::ChunkArgs a;
   a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
   a.S0 = S0; a.o = o; a.S_out = S_T; a.M_out = nullptr;
-  a.BH = (int)BH; a.G = 1; a.Tseg = T; a.vsplit = ntiles / nc;
+  a.BH = (int)BH; a.G = 1; a.Tseg = T; a.Ttot = T; a.vsplit = ntiles / nc;
   const long long nwg = BH * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
-  if (getenv("KDA_LOG"))
+  if (log)
     fprintf(stderr, "[libkda] prefill BH=%lld T=%d D=%d nc=%d vsplit=%d grid=%lld\n", BH, T, dk, nc,
             a.vsplit, nwg);
-  hipError_t e = kda::launch_chunk(a, dtype == KDA_BF16, dk, true, nc, (int)nwg, stream);
-  if (e != hipSuccess) return hip_fail(e, "kda_chunk_prefill launch");
+  if ((e = kda::launch_chunk(a, bf, dk, true, nc, (int)nwg, stream)) != hipSuccess)
+    return hip_fail(e, "kda_chunk_prefill launch");
   return ok();
 }
 
@@ -181,6 +276,7 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
                                 int Tseg, int dk, int dv, kda_dtype dtype, hipStream_t stream) {
   if (B < 0 || H < 0 || G < 0) return fail(KDA_ERR_SHAPE, "negative size B=%d H=%d G=%d", B, H, G);
   if (Tseg < 1) return fail(KDA_ERR_SHAPE, "Tseg must be >= 1 (got %d)", Tseg);
+  if ((long long)G * Tseg > INT32_MAX) return fail(KDA_ERR_SHAPE, "G * Tseg exceeds 2^31 tokens");
   kda_status st;
   if ((st = check_dtype(dtype)) != KDA_OK) return st;
   if ((st = check_dims(dk, dv)) != KDA_OK) return st;
@@ -189,6 +285,7 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
   const long long BH = (long long)B * H;
   const long long nseq = BH * G;
   if (nseq * Tseg * dk > kMaxElems || nseq > (1LL << 30)) return fail(KDA_ERR_SHAPE, "problem too large");
+  if ((st = check_seq_bytes(Tseg, dk, dtype)) != KDA_OK) return st;
   if (nseq == 0) return ok();
   KDA_REQUIRE(k, "k");
   KDA_REQUIRE(v, "v");
@@ -201,7 +298,7 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
   kda::ChunkArgs a;
   a.q = nullptr; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
   a.S0 = nullptr; a.o = nullptr; a.S_out = S_zero_end; a.M_out = M;
-  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.vsplit = ntiles / nc;
+  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = G * Tseg; a.vsplit = ntiles / nc;
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (getenv("KDA_LOG"))

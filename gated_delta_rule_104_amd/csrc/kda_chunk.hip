@@ -8,37 +8,46 @@
 // 开源日来了", section "FlashKDA").  Within a chunk with start state S and
 // per-channel cumulative log-gate g_r = sum_{j<=r} log a_j (kept in log space,
 // blog.csdn.net article on the Kimi K3 report, section 一.1), write
-//   Qh = q*e^g, Kh = k*e^g, Kb = k*e^-g, Kt = k*e^(g_C - g), Gam = e^(g_C),
+//   Qh = q*e^g, Kh = k*e^g, Kb = k*e^-g, Gam = e^(g_C)  (g_C: last row),
 //   A = strict_lower(Kh Kb^T),  P = lower(Qh Kb^T),
 //   T = (I + diag(b) A)^-1,     Tb = T diag(b).
 // Unrolling the recurrence over the chunk gives exactly
-//   Delta = Tb (V - Kh S),  O = Qh S + P Delta,  S' = Diag(Gam) S + Kt^T Delta.
-// Only the last three depend on S; everything else is S-independent.
+//   Delta = Tb (V - Kh S),  O = Qh S + P Delta,  S' = Diag(Gam) (S + Kb^T Delta).
+// Only the last three depend on S; everything else is S-independent.  With
+// log a >= -1 the factors e^{+-g} stay within [e^-64, e^64] inside a chunk, far
+// from the fp32/bf16 range limits.
 //
 // Work split.  Columns of S evolve independently once the S-independent
 // products are known, so a workgroup owns 16*NC state columns of one
-// sequence; several workgroups share a sequence when that is needed to fill
-// the 256 compute units.  Inside a workgroup:
+// sequence.  Inside a workgroup:
 //   * NC consumer waves each hold a dk x 16 column slice of S in fp32 MFMA
 //     accumulators and run the serial chain for chunk n;
 //   * NP = dk/32 producer waves compute chunk n+1's S-independent products into
-//     the other half of a double-buffered LDS stage (two pipelines that do not
-//     wait on each other inside an iteration; the pages describe FlashKDA's
-//     split of intra-chunk work and state passing between independently
-//     scheduled thread groups in the same section).
+//     the other half of a double-buffered LDS stage.  The pages describe
+//     FlashKDA as splitting intra-chunk work and state passing between two
+//     independently scheduled thread groups (same section); here the two roles
+//     are wavefronts of one workgroup.
 // Three workgroup barriers per chunk separate the producer phases
-// (elementwise -> scores -> inverse); the consumer spreads its chain over the
-// same three intervals.  The fp32 variant has no room for two stages and runs
-// producer and consumer one after the other.
+// (elementwise -> scores + diagonal inverses -> off-diagonal inverse); the
+// consumer spreads its chain over the same three intervals.  The fp32 variant
+// has no room for two stages and runs producer and consumer one after the other.
+//
+// All global traffic goes through buffer descriptors sized to the sequence, so
+// rows past its end read as zero and stores to them are dropped: a ragged last
+// chunk needs no branches (zero k, q, log-gate and beta rows leave the state
+// and the valid outputs unchanged).
 //
 // Segment mode runs the same chain on the augmented state [S | M] started at
 // [0 | I] (columns >= dv see v = 0), skips q, P and O, and writes S and M.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
 constexpr int CH = 64;  // chunk length
+constexpr float LOG2E = 1.4426950408889634f;
 
 template <typename T, int D, int NC, bool PREFILL>
 struct ChunkCfg {
@@ -49,7 +58,6 @@ struct ChunkCfg {
   static constexpr int NP = D / 32;
   static constexpr int NW = NC + NP;
   static constexpr int THREADS = 64 * NW;
-  static constexpr int E16 = ES / 2;       // 16-byte pieces per 8 elements
   static constexpr int R_TD = D * ES;      // [CH][D] rows (time-major)
   static constexpr int R_DT = CH * ES;     // [D][CH] rows (channel-major)
   static constexpr int R_TT = CH * ES;     // [CH][CH] rows
@@ -70,15 +78,23 @@ struct ChunkCfg {
   static_assert(LDS % 16 == 0, "LDS size");
 };
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over [p, p + bytes): loads past the end return 0, stores are dropped.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // 8 consecutive elements of a token row, as loaded from HBM.
 template <typename T> struct Raw8 { u32x4 p[sizeof(T) / 2]; };
 
 template <typename T>
-__device__ __forceinline__ void raw_load(Raw8<T>& r, const T* ptr, bool ok) {
+__device__ __forceinline__ void raw_load(Raw8<T>& r, rsrc_t rs, uint32_t off) {
 #pragma unroll
-  for (int i = 0; i < (int)(sizeof(T) / 2); ++i)
-    r.p[i] = ok ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(ptr) + 16 * i)
-                : u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.p[i] = bload128(rs, off + 16 * i);
 }
 
 template <typename T>
@@ -95,84 +111,129 @@ __device__ __forceinline__ void raw_f32(const Raw8<T>& r, float* out) {
   }
 }
 
-template <typename T>
-__device__ __forceinline__ float exp_dev(float x) {
-  if constexpr (sizeof(T) == 2) return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
-  else return expf(x);
-}
-
 // Producer input registers for one chunk: 4 token rows x 8 channels of
-// log_alpha, k and q, plus one beta per lane.
+// log_alpha, k and q, plus one beta per lane (raw bits).
 template <typename T> struct ProdRaw {
   Raw8<T> la[4], k[4], q[4];
   uint32_t beta;
 };
 
-template <typename T> struct VRegs { T v[16]; };
+template <typename T> struct VRegs { uint32_t v[16]; };
+
+// Operand fragments.  bf16: one v_mfma_f32_16x16x32_bf16 per 32-deep k block;
+// fp32: four v_mfma_f32_16x16x4_f32 steps per 16-deep k block.  "ar" fragments
+// pair an LDS A operand with a B operand held as accumulator tiles (k positions
+// 4g..4g+3 of each 16-deep tile, g = lane/16); "ll" fragments read both
+// operands from LDS with k contiguous per lane.
+template <bool BF> struct Frag;
+template <> struct Frag<true> {
+  typedef bf16x8 A;
+  typedef bf16x8 B;
+  static constexpr int KB = 32;
+  template <int R>
+  __device__ __forceinline__ static A ar(const char* smem, uint32_t base, int row, int kk) {
+    return cat8(lds_ld<bf16x4>(smem, base + swz<R>(row, 2 * kk)),
+                lds_ld<bf16x4>(smem, base + swz<R>(row, 2 * (kk + 16))));
+  }
+  template <int R>
+  __device__ __forceinline__ static A ll(const char* smem, uint32_t base, int row, int k0, int ln) {
+    return lds_ld<bf16x8>(smem, base + swz<R>(row, 2 * (k0 + 8 * (ln >> 4))));
+  }
+  __device__ __forceinline__ static B bfrag(const f32x4* t, int m) { return pack8(t[2 * m], t[2 * m + 1]); }
+  __device__ __forceinline__ static f32x4 mma(f32x4 acc, A a, B b) { return mfma_bf16_k32(acc, a, b); }
+};
+template <> struct Frag<false> {
+  typedef f32x4 A;
+  typedef f32x4 B;
+  static constexpr int KB = 16;
+  template <int R>
+  __device__ __forceinline__ static A ar(const char* smem, uint32_t base, int row, int kk) {
+    return lds_ld<f32x4>(smem, base + swz<R>(row, 4 * kk));
+  }
+  template <int R>
+  __device__ __forceinline__ static A ll(const char* smem, uint32_t base, int row, int k0, int ln) {
+    return lds_ld<f32x4>(smem, base + swz<R>(row, 4 * (k0 + 4 * (ln >> 4))));
+  }
+  __device__ __forceinline__ static B bfrag(const f32x4* t, int m) { return t[m]; }
+  __device__ __forceinline__ static f32x4 mma(f32x4 acc, A a, B b) {
+    acc = mfma_f32_k4(acc, a[0], b[0]);
+    acc = mfma_f32_k4(acc, a[1], b[1]);
+    acc = mfma_f32_k4(acc, a[2], b[2]);
+    return mfma_f32_k4(acc, a[3], b[3]);
+  }
+};
 
 template <typename T, int D, int NC, bool PREFILL>
 struct ChunkKernel {
   using C = ChunkCfg<T, D, NC, PREFILL>;
+  using F = Frag<C::BF>;
+  static constexpr int KB = F::KB;
+  static constexpr int NKD = D / KB;    // k blocks over channels
+  static constexpr int NKT = CH / KB;   // k blocks over the tokens of a chunk
+  // last k block a lower-triangular row tile ti touches
+  static constexpr int tri(int ti) { return (16 * ti + 15) / KB; }
   char* smem;
   ChunkArgs a;
-  const T* q; const T* k; const T* v; const T* la; const T* beta;
-  size_t tok0;     // first token of this sequence
+  rsrc_t rq, rk, rv, rla, rbeta, ro;
   int Tlen, nch;
-  int wave, l, g4;  // wave index, lane, 4*(lane/16)
+  int wave, l;
   // consumer
   int col;          // global column of this lane's state slice
   bool isv;         // column reads v (value column) rather than being a map column
   f32x4 S[D / 16];
   f32x4 Dl[4];      // Delta tiles of the current chunk
-  bf16x8 SB[D / 32], DB[2];
+  typename F::B sb[NKD], db[NKT];
 
   __device__ __forceinline__ uint32_t stage(int chunk) const {
     return (C::STAGES == 2 ? (uint32_t)(chunk & 1) : 0u) * C::STAGE;
   }
 
   // ------------------------------------------------------------ producers
+  // Lane (tg = l/4, cs = l%4) of producer wave pw owns tokens 4*tg..4*tg+3 and
+  // channels 32*pw + 8*cs .. +7 of the chunk.
   __device__ __forceinline__ void load_raw(ProdRaw<T>& r, int chunk) const {
+    const int ln = fresh_lane(l);
     const int pw = wave - NC;
-    const int tg = l >> 2, cs = l & 3;
+    const int tg = ln >> 2, cs = ln & 3;
     const int ch = 32 * pw + 8 * cs;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = chunk * CH + 4 * tg + i;
-      const bool ok = t < Tlen;
-      const size_t off = (tok0 + (size_t)(ok ? t : 0)) * D + ch;
-      raw_load<T>(r.la[i], la + off, ok);
-      raw_load<T>(r.k[i], k + off, ok);
-      if constexpr (PREFILL) raw_load<T>(r.q[i], q + off, ok);
+      const uint32_t off = (uint32_t)((chunk * CH + 4 * tg + i) * D + ch) * C::ES;
+      raw_load<T>(r.la[i], rla, off);
+      raw_load<T>(r.k[i], rk, off);
+      if constexpr (PREFILL) raw_load<T>(r.q[i], rq, off);
     }
     if (pw == 0) {
-      const int t = chunk * CH + l;
-      if (t < Tlen) {
-        if constexpr (sizeof(T) == 2)
-          r.beta = (uint32_t)(*reinterpret_cast<const uint16_t*>(beta + tok0 + t)) << 16;
-        else
-          r.beta = __float_as_uint(beta[tok0 + t]);
-      } else {
-        r.beta = 0u;
-      }
+      const uint32_t off = (uint32_t)(chunk * CH + ln) * C::ES;
+      if constexpr (C::BF) r.beta = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rbeta, off, 0, 0);
+      else r.beta = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rbeta, off, 0, 0);
     }
   }
 
   // Phase 1: cumulative log-gate and the decayed operand tiles of one chunk.
+  // bf16 inputs: the gate is accumulated in log2 units and exponentiated with
+  // the hardware exp2; fp32 inputs use the accurate library exp.
   __device__ __forceinline__ void p1(const ProdRaw<T>& r, uint32_t st) {
+    const int ln = fresh_lane(l);
     const int pw = wave - NC;
-    const int tg = l >> 2, cs = l & 3;
+    const int tg = ln >> 2, cs = ln & 3;
     const int ch = 32 * pw + 8 * cs;
     float g[4][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) raw_f32<T>(r.la[i], g[i]);
-    float tot[8], inc[8], exc[8], gc[8];
+    for (int i = 0; i < 4; ++i) {
+      raw_f32<T>(r.la[i], g[i]);
+      if constexpr (C::BF) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) g[i][c] *= LOG2E;
+      }
+    }
+    float inc[8], exc[8], gc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       g[1][c] += g[0][c];
       g[2][c] += g[1][c];
       g[3][c] += g[2][c];
-      tot[c] = g[3][c];
-      inc[c] = tot[c];
+      inc[c] = g[3][c];
     }
     // inclusive scan of the 4-token totals over the 16 token groups (lane stride 4)
 #pragma unroll
@@ -180,37 +241,41 @@ struct ChunkKernel {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const float y = __shfl_up(inc[c], d);
-        if (l >= d) inc[c] += y;
+        if (ln >= d) inc[c] += y;
       }
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float y = __shfl_up(inc[c], 4);
-      exc[c] = (l >= 4) ? y : 0.f;
+      exc[c] = (ln >= 4) ? y : 0.f;
       gc[c] = __shfl(inc[c], 60 + cs);
     }
-    float kt[4][8];
+    float kb[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * tg + i;
-      float kk[8], qq[8], vq[8], vkh[8], vkb[8];
+      float kk[8], qq[8], vq[8], vkh[8];
       raw_f32<T>(r.k[i], kk);
       if constexpr (PREFILL) raw_f32<T>(r.q[i], qq);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const float gg = g[i][c] + exc[c];
-        const float eg = exp_dev<T>(gg);
-        const float emg = exp_dev<T>(-gg);
-        const float et = exp_dev<T>(gc[c] - gg);
+        float eg, emg;
+        if constexpr (C::BF) {
+          eg = __builtin_amdgcn_exp2f(gg);
+          emg = __builtin_amdgcn_exp2f(-gg);
+        } else {
+          eg = expf(gg);
+          emg = expf(-gg);
+        }
         vkh[c] = kk[c] * eg;
-        vkb[c] = kk[c] * emg;
+        kb[i][c] = kk[c] * emg;
         if constexpr (PREFILL) vq[c] = qq[c] * eg;
-        kt[i][c] = kk[c] * et;
       }
       if constexpr (C::BF) {
         bf16x8 h, b, qv;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) { h[c] = (bf16)vkh[c]; b[c] = (bf16)vkb[c]; qv[c] = (bf16)vq[c]; }
+        for (int c = 0; c < 8; ++c) { h[c] = (bf16)vkh[c]; b[c] = (bf16)kb[i][c]; qv[c] = (bf16)vq[c]; }
         lds_st<bf16x8>(smem, st + C::S_KH + swz<C::R_TD>(row, 2 * ch), h);
         lds_st<bf16x8>(smem, C::X_KB + swz<C::R_TD>(row, 2 * ch), b);
         if constexpr (PREFILL) lds_st<bf16x8>(smem, st + C::S_QH + swz<C::R_TD>(row, 2 * ch), qv);
@@ -218,7 +283,7 @@ struct ChunkKernel {
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
           f32x4 h = {vkh[4 * hlf], vkh[4 * hlf + 1], vkh[4 * hlf + 2], vkh[4 * hlf + 3]};
-          f32x4 b = {vkb[4 * hlf], vkb[4 * hlf + 1], vkb[4 * hlf + 2], vkb[4 * hlf + 3]};
+          f32x4 b = {kb[i][4 * hlf], kb[i][4 * hlf + 1], kb[i][4 * hlf + 2], kb[i][4 * hlf + 3]};
           lds_st<f32x4>(smem, st + C::S_KH + swz<C::R_TD>(row, 4 * (ch + 4 * hlf)), h);
           lds_st<f32x4>(smem, C::X_KB + swz<C::R_TD>(row, 4 * (ch + 4 * hlf)), b);
           if constexpr (PREFILL) {
@@ -228,109 +293,179 @@ struct ChunkKernel {
         }
       }
     }
-    // Kt^T: channel-major, 4 consecutive tokens per lane and channel
+    // Kb^T: channel-major, 4 consecutive tokens per lane and channel
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int rowc = ch + c;
       if constexpr (C::BF) {
         bf16x4 t4;
-        t4[0] = (bf16)kt[0][c]; t4[1] = (bf16)kt[1][c]; t4[2] = (bf16)kt[2][c]; t4[3] = (bf16)kt[3][c];
+        t4[0] = (bf16)kb[0][c]; t4[1] = (bf16)kb[1][c]; t4[2] = (bf16)kb[2][c]; t4[3] = (bf16)kb[3][c];
         lds_st<bf16x4>(smem, st + C::S_KT + swz<C::R_DT>(rowc, 2 * 4 * tg), t4);
       } else {
-        f32x4 t4 = {kt[0][c], kt[1][c], kt[2][c], kt[3][c]};
+        f32x4 t4 = {kb[0][c], kb[1][c], kb[2][c], kb[3][c]};
         lds_st<f32x4>(smem, st + C::S_KT + swz<C::R_DT>(rowc, 4 * 4 * tg), t4);
       }
     }
     if (tg == 15) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        lds_st<float>(smem, st + C::S_GM + 4 * (ch + c), exp_dev<T>(gc[c]));
+      for (int c = 0; c < 8; ++c) {
+        const float gm = C::BF ? __builtin_amdgcn_exp2f(gc[c]) : expf(gc[c]);
+        lds_st<float>(smem, st + C::S_GM + 4 * (ch + c), gm);
+      }
     }
-    if (pw == 0) lds_st<float>(smem, C::X_BETA + 4 * l, __uint_as_float(r.beta));
+    if (pw == 0) {
+      const float b = C::BF ? __uint_as_float(r.beta << 16) : __uint_as_float(r.beta);
+      lds_st<float>(smem, C::X_BETA + 4 * ln, b);
+    }
   }
 
   __device__ __forceinline__ void store_tt(uint32_t base, int r, int s, float x) {
     lds_st<T>(smem, base + swz<C::R_TT>(r, C::ES * s), from_f32<T>(x));
   }
 
-  // Phase 2: intra-chunk scores.  Row task (mat, i) computes tiles (i, 0..i) of
-  // L = diag(b) A (mat 0) or P (mat 1); an L row task then inverts its
-  // diagonal block (I + L_ii) by substitution, one column per lane.
-  __device__ __forceinline__ void p2(uint32_t st) {
-    const int pw = wave - NC;
-    constexpr int NTASK = PREFILL ? 8 : 4;
-    for (int task = pw; task < NTASK; task += C::NP) {
-      const int mat = PREFILL ? (task & 1) : 0;
-      const int i = 3 - (PREFILL ? (task >> 1) : task);
-      const uint32_t abase = mat ? st + C::S_QH : st + C::S_KH;
-      for (int j = 0; j <= i; ++j) {
-        f32x4 acc = zero4();
-        if constexpr (C::BF) acc = mma_ll_bf16<C::R_TD>(acc, smem, abase, 16 * i, C::X_KB, 16 * j, D);
-        else acc = mma_ll_f32<C::R_TD>(acc, smem, abase, 16 * i, C::X_KB, 16 * j, D);
-        const int s = 16 * j + (l & 15);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * i + g4 + e;
-          if (mat == 0) {
-            const float b = lds_ld<float>(smem, C::X_BETA + 4 * r);
-            store_tt(C::X_L, r, s, s < r ? acc[e] * b : 0.f);
-          } else {
-            store_tt(st + C::S_P, r, s, s <= r ? acc[e] : 0.f);
-          }
-        }
-      }
-      if (mat == 0) {
-        wave_lds_fence();
-        const int c = l & 15;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float sum = (r == c) ? 1.f : 0.f;
-#pragma unroll
-          for (int m = 0; m < r; ++m)
-            sum -= to_f32(lds_ld<T>(smem, C::X_L + swz<C::R_TT>(16 * i + r, C::ES * (16 * i + m)))) * x[m];
-          x[r] = sum;
-        }
-        if (l < 16) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            lds_st<T>(smem, C::X_TI + i * 16 * C::R_TI + swz<C::R_TI>(r, C::ES * c), from_f32<T>(x[r]));
-        }
-      }
+  // 16x16x16 product: A fragment (row l%16, k = 4*(l/16)..+3) times an
+  // accumulator tile used as B.
+  typedef typename std::conditional<C::BF, bf16x4, f32x4>::type A16;
+  template <int RR>
+  __device__ __forceinline__ A16 frag16(uint32_t base, int row, int k0, int ln) const {
+    if constexpr (C::BF) return lds_ld<bf16x4>(smem, base + swz<RR>(row, 2 * (k0 + 4 * (ln >> 4))));
+    else return lds_ld<f32x4>(smem, base + swz<RR>(row, 4 * (k0 + 4 * (ln >> 4))));
+  }
+  __device__ __forceinline__ static f32x4 mma16(f32x4 acc, A16 a, f32x4 b) {
+    if constexpr (C::BF) {
+      return mfma_bf16_k16(acc, a, pack4(b));
+    } else {
+      acc = mfma_f32_k4(acc, a[0], b[0]);
+      acc = mfma_f32_k4(acc, a[1], b[1]);
+      acc = mfma_f32_k4(acc, a[2], b[2]);
+      return mfma_f32_k4(acc, a[3], b[3]);
     }
   }
 
-  // acc of a 16x16 tile product A(16x16 from LDS tile at base, rows of RR bytes,
-  // row r0, col k0) times B (accumulator tile in registers).
-  template <int RR>
-  __device__ __forceinline__ f32x4 mma16(uint32_t base, int r0, int k0, f32x4 b, f32x4 acc) const {
-    if constexpr (C::BF) {
-      bf16x4 af = lds_ld<bf16x4>(smem, base + swz<RR>(r0 + (l & 15), 2 * (k0 + g4)));
-      return mfma_bf16_k16(acc, af, pack4(b));
-    } else {
-      return mma_ar_f32<RR>(acc, smem, base, r0, k0, &b, 1);
+  // Phase 2, one row task: tiles (I, 0..I) of L = diag(b) A (MAT 0) or P (MAT 1).
+  // All operand fragments of the task are fetched before its MFMAs.  An L task
+  // then inverts its diagonal block (I + L_II) with matrix cores.
+  template <int MAT, int I>
+  __device__ __forceinline__ void p2_row(uint32_t st) {
+    const int ln = fresh_lane(l);
+    const int g4 = 4 * (ln >> 4);
+    const uint32_t abase = MAT ? st + C::S_QH : st + C::S_KH;
+    const int s0 = ln & 15;
+    typename F::A fa[NKD], fb[I + 1][NKD];
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) {
+      fa[m] = F::template ll<C::R_TD>(smem, abase, 16 * I + s0, KB * m, ln);
+#pragma unroll
+      for (int j = 0; j <= I; ++j) fb[j][m] = F::template ll<C::R_TD>(smem, C::X_KB, 16 * j + s0, KB * m, ln);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[I + 1];
+#pragma unroll
+    for (int j = 0; j <= I; ++j) acc[j] = zero4();
+#pragma unroll
+    for (int m = 0; m < NKD; ++m)
+#pragma unroll
+      for (int j = 0; j <= I; ++j) acc[j] = F::mma(acc[j], fa[m], fb[j][m]);
+    float bet[4];
+    if (MAT == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bet[e] = lds_ld<float>(smem, C::X_BETA + 4 * (16 * I + g4 + e));
+    }
+#pragma unroll
+    for (int j = 0; j <= I; ++j) {
+      const int s = 16 * j + s0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * I + g4 + e;
+        if (MAT == 0) store_tt(C::X_L, r, s, s < r ? acc[j][e] * bet[e] : 0.f);
+        else store_tt(st + C::S_P, r, s, s <= r ? acc[j][e] : 0.f);
+      }
+    }
+    if constexpr (MAT == 0) {
+      // Inverse of the diagonal block, (I + N)^-1 with N = L_II strictly lower
+      // (nilpotent, N^16 = 0), as the exact product (I - N)(I + N^2)(I + N^4)(I + N^8).
+      // Each factor is applied as Y += N^(2^k) Y with Y accumulated in fp32; the
+      // powers of N pass through the block's 16x16 slot of the inverse scratch
+      // to serve as A operands.
+      f32x4 N, Y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * I + g4 + e, sc = 16 * I + s0;
+        N[e] = sc < r ? acc[I][e] * bet[e] : 0.f;
+        Y[e] = (g4 + e == s0 ? 1.f : 0.f) - N[e];
+      }
+      const uint32_t ti = C::X_TI + I * 16 * C::R_TI;
+      auto put = [&](const f32x4& t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lds_st<T>(smem, ti + swz<C::R_TI>(g4 + e, C::ES * s0), from_f32<T>(t[e]));
+      };
+      wave_lds_fence();  // L_II rows written above are read as the A operand of N * N
+      A16 an = frag16<C::R_TT>(C::X_L, 16 * I + s0, 16 * I, ln);
+      f32x4 P2 = mma16(zero4(), an, N);
+      put(P2);
+      wave_lds_fence();
+      A16 a2 = frag16<C::R_TI>(ti, s0, 0, ln);
+      Y = mma16(Y, a2, Y);
+      f32x4 P4 = mma16(zero4(), a2, P2);
+      put(P4);
+      wave_lds_fence();
+      A16 a4 = frag16<C::R_TI>(ti, s0, 0, ln);
+      Y = mma16(Y, a4, Y);
+      f32x4 P8 = mma16(zero4(), a4, P4);
+      put(P8);
+      wave_lds_fence();
+      A16 a8 = frag16<C::R_TI>(ti, s0, 0, ln);
+      Y = mma16(Y, a8, Y);
+      put(Y);
     }
   }
+
+  // Task K of the phase-2 list, heaviest rows first:
+  // prefill (A3, P3, A2, P2, A1, P1, A0, P0); segment pass (A3, A2, A1, A0).
+  template <int K>
+  __device__ __forceinline__ void p2_task(uint32_t st, int pw) {
+    constexpr int NTASK = PREFILL ? 8 : 4;
+    if constexpr (K < NTASK) {
+      if (K % C::NP == pw) {
+        constexpr int MAT = PREFILL ? (K & 1) : 0;
+        constexpr int I = 3 - (PREFILL ? (K >> 1) : K);
+        p2_row<MAT, I>(st);
+      }
+      p2_task<K + 1>(st, pw);
+    }
+  }
+
+  __device__ __forceinline__ void p2(uint32_t st) { p2_task<0>(st, wave - NC); }
 
   // Phase 3: off-diagonal blocks of T = (I + L)^-1 by block forward
   // substitution, T_ij = -T_ii sum_{m=j}^{i-1} L_im T_mj, then Tb = T diag(b).
-  // Column block J of T is one task.
+  // Column block J of T is one task; its LDS operands are fetched up front.
   template <int J>
   __device__ __forceinline__ void p3_col(uint32_t st) {
+    const int ln = fresh_lane(l);
+    const int g4 = 4 * (ln >> 4);
+    const int r16 = ln & 15;
+    A16 fl[4][4], ft[4];
+#pragma unroll
+    for (int i = J + 1; i < 4; ++i) {
+      ft[i] = frag16<C::R_TI>(C::X_TI + i * 16 * C::R_TI, r16, 0, ln);
+#pragma unroll
+      for (int m = J; m < i; ++m) fl[i][m] = frag16<C::R_TT>(C::X_L, 16 * i + r16, 16 * m, ln);
+    }
     f32x4 Tc[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      Tc[J][e] = to_f32(lds_ld<T>(smem, C::X_TI + J * 16 * C::R_TI + swz<C::R_TI>(g4 + e, C::ES * (l & 15))));
+      Tc[J][e] = to_f32(lds_ld<T>(smem, C::X_TI + J * 16 * C::R_TI + swz<C::R_TI>(g4 + e, C::ES * r16)));
+    const int s = 16 * J + r16;
+    const float b = lds_ld<float>(smem, C::X_BETA + 4 * s);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = J + 1; i < 4; ++i) {
       f32x4 y = zero4();
 #pragma unroll
-      for (int m = J; m < i; ++m) y = mma16<C::R_TT>(C::X_L, 16 * i, 16 * m, Tc[m], y);
-      f32x4 z = mma16<C::R_TI>(C::X_TI + i * 16 * C::R_TI, 0, 0, y, zero4());
-      Tc[i] = -z;
+      for (int m = J; m < i; ++m) y = mma16(y, fl[i][m], Tc[m]);
+      Tc[i] = -mma16(zero4(), ft[i], y);
     }
-    const int s = 16 * J + (l & 15);
-    const float b = lds_ld<float>(smem, C::X_BETA + 4 * s);
 #pragma unroll
     for (int m = J; m < 4; ++m) {
 #pragma unroll
@@ -347,83 +482,128 @@ struct ChunkKernel {
   }
 
   // ------------------------------------------------------------ consumers
+  // Lane l holds rows 16*ti + 4*(l/16) + e of its column (accumulator layout).
   __device__ __forceinline__ void load_v(VRegs<T>& vr, int chunk) const {
+    const int ln = fresh_lane(l);
+    const int g4 = 4 * (ln >> 4);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = chunk * CH + 16 * ti + g4 + e;
-        T x = from_f32<T>(0.f);
-        if (isv && t < Tlen) x = v[(tok0 + t) * D + col];
-        vr.v[4 * ti + e] = x;
+        // map columns (segment pass) read v = 0: their offset is past any buffer end
+        const uint32_t off = ((uint32_t)((chunk * CH + 16 * ti + g4 + e) * D + col) * C::ES) |
+                             (isv ? 0u : 0x80000000u);
+        if constexpr (C::BF) vr.v[4 * ti + e] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0);
+        else vr.v[4 * ti + e] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
       }
     }
+  }
+
+  __device__ __forceinline__ float vval(const VRegs<T>& vr, int i) const {
+    return C::BF ? __uint_as_float(vr.v[i] << 16) : __uint_as_float(vr.v[i]);
   }
 
   // Interval 1: Delta = Tb (V - Kh S).
   __device__ __forceinline__ void c1(const VRegs<T>& vr, uint32_t st) {
-    f32x4 X[4];
-    if constexpr (C::BF) {
+    const int ln = fresh_lane(l);
+    const int r16 = ln & 15, kk = 4 * (ln >> 4);
+    typename F::A fk[4][NKD], ft[4][NKT];
 #pragma unroll
-      for (int m = 0; m < D / 32; ++m) SB[m] = pack8(S[2 * m], S[2 * m + 1]);
+    for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        f32x4 y = mma_ar_bf16<C::R_TD>(zero4(), smem, st + C::S_KH, 16 * ti, 0, SB, D / 32);
+      for (int m = 0; m < NKD; ++m) fk[ti][m] = F::template ar<C::R_TD>(smem, st + C::S_KH, 16 * ti + r16, KB * m + kk);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[ti][e] = to_f32(vr.v[4 * ti + e]) - y[e];
-      }
-      bf16x8 XB[2] = {pack8(X[0], X[1]), pack8(X[2], X[3])};
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti)
-        Dl[ti] = mma_ar_bf16<C::R_TT>(zero4(), smem, st + C::S_TB, 16 * ti, 0, XB, (ti >> 1) + 1);
-      DB[0] = pack8(Dl[0], Dl[1]);
-      DB[1] = pack8(Dl[2], Dl[3]);
-    } else {
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        f32x4 y = mma_ar_f32<C::R_TD>(zero4(), smem, st + C::S_KH, 16 * ti, 0, S, D / 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) X[ti][e] = to_f32(vr.v[4 * ti + e]) - y[e];
-      }
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti)
-        Dl[ti] = mma_ar_f32<C::R_TT>(zero4(), smem, st + C::S_TB, 16 * ti, 0, X, ti + 1);
+      for (int m = 0; m <= tri(ti); ++m) ft[ti][m] = F::template ar<C::R_TT>(smem, st + C::S_TB, 16 * ti + r16, KB * m + kk);
     }
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) sb[m] = F::bfrag(S, m);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 X[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) X[ti] = zero4();
+#pragma unroll
+    for (int m = 0; m < NKD; ++m)
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) X[ti] = F::mma(X[ti], fk[ti][m], sb[m]);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) X[ti][e] = vval(vr, 4 * ti + e) - X[ti][e];
+    typename F::B xb[NKT];
+#pragma unroll
+    for (int m = 0; m < NKT; ++m) xb[m] = F::bfrag(X, m);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) Dl[ti] = zero4();
+#pragma unroll
+    for (int m = 0; m < NKT; ++m)
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti)
+        if (m <= tri(ti)) Dl[ti] = F::mma(Dl[ti], ft[ti][m], xb[m]);
+#pragma unroll
+    for (int m = 0; m < NKT; ++m) db[m] = F::bfrag(Dl, m);
   }
 
-  // Interval 2: O = Qh S + P Delta, stored.
+  // Interval 2: O = Qh S + P Delta, stored (rows past the sequence end are dropped).
   __device__ __forceinline__ void c2(uint32_t st, int chunk) {
     if constexpr (PREFILL) {
-      T* o = reinterpret_cast<T*>(a.o);
+      const int ln = fresh_lane(l);
+      const int r16 = ln & 15, kk = 4 * (ln >> 4);
+      typename F::A fq[4][NKD], fp[4][NKT];
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        f32x4 acc;
-        if constexpr (C::BF) {
-          acc = mma_ar_bf16<C::R_TD>(zero4(), smem, st + C::S_QH, 16 * ti, 0, SB, D / 32);
-          acc = mma_ar_bf16<C::R_TT>(acc, smem, st + C::S_P, 16 * ti, 0, DB, (ti >> 1) + 1);
-        } else {
-          acc = mma_ar_f32<C::R_TD>(zero4(), smem, st + C::S_QH, 16 * ti, 0, S, D / 16);
-          acc = mma_ar_f32<C::R_TT>(acc, smem, st + C::S_P, 16 * ti, 0, Dl, ti + 1);
-        }
+#pragma unroll
+        for (int m = 0; m < NKD; ++m) fq[ti][m] = F::template ar<C::R_TD>(smem, st + C::S_QH, 16 * ti + r16, KB * m + kk);
+#pragma unroll
+        for (int m = 0; m <= tri(ti); ++m) fp[ti][m] = F::template ar<C::R_TT>(smem, st + C::S_P, 16 * ti + r16, KB * m + kk);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 O[4];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) O[ti] = zero4();
+#pragma unroll
+      for (int m = 0; m < NKD; ++m)
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) O[ti] = F::mma(O[ti], fq[ti][m], sb[m]);
+#pragma unroll
+      for (int m = 0; m < NKT; ++m)
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+          if (m <= tri(ti)) O[ti] = F::mma(O[ti], fp[ti][m], db[m]);
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int t = chunk * CH + 16 * ti + g4 + e;
-          if (t < Tlen) o[(tok0 + t) * D + col] = from_f32<T>(acc[e]);
+          const uint32_t off = (uint32_t)((chunk * CH + 16 * ti + kk + e) * D + col) * C::ES;
+          if constexpr (C::BF) {
+            const bf16 hv = (bf16)O[ti][e];
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ro, off, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[ti][e]), ro, off, 0, 0);
+          }
         }
       }
     }
   }
 
-  // Interval 3: S = Diag(Gam) S + Kt^T Delta.
+  // Interval 3: S = Diag(Gam) (S + Kb^T Delta).
   __device__ __forceinline__ void c3(uint32_t st) {
+    const int ln = fresh_lane(l);
+    const int r16 = ln & 15, kk = 4 * (ln >> 4);
+    typename F::A fk[D / 16][NKT];
+    f32x4 gm[D / 16];
 #pragma unroll
     for (int ci = 0; ci < D / 16; ++ci) {
-      f32x4 gm = lds_ld<f32x4>(smem, st + C::S_GM + 4 * (16 * ci + g4));
-      f32x4 acc = S[ci] * gm;
-      if constexpr (C::BF) acc = mma_ar_bf16<C::R_DT>(acc, smem, st + C::S_KT, 16 * ci, 0, DB, 2);
-      else acc = mma_ar_f32<C::R_DT>(acc, smem, st + C::S_KT, 16 * ci, 0, Dl, 4);
-      S[ci] = acc;
+#pragma unroll
+      for (int m = 0; m < NKT; ++m) fk[ci][m] = F::template ar<C::R_DT>(smem, st + C::S_KT, 16 * ci + r16, KB * m + kk);
+      gm[ci] = lds_ld<f32x4>(smem, st + C::S_GM + 4 * (16 * ci + kk));
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < NKT; ++m)
+#pragma unroll
+      for (int ci = 0; ci < D / 16; ++ci) S[ci] = F::mma(S[ci], fk[ci][m], db[m]);
+#pragma unroll
+    for (int ci = 0; ci < D / 16; ++ci) S[ci] = S[ci] * gm[ci];
   }
 
   // Pipeline.  Iteration `it` has producers prepare chunk it while consumers
@@ -481,23 +661,28 @@ struct ChunkKernel {
     const int vs = id - seq * a.vsplit;
     const int gseg = seq / a.BH;
     const int bh = seq - gseg * a.BH;
-    tok0 = ((size_t)bh * a.G + gseg) * (size_t)a.Tseg;
-    Tlen = a.Tseg;
+    const size_t tok0 = (size_t)bh * a.Ttot + (size_t)gseg * a.Tseg;
+    Tlen = min(a.Tseg, a.Ttot - gseg * a.Tseg);
     nch = (Tlen + CH - 1) / CH;
     wave = threadIdx.x >> 6;
     l = lane_id();
-    g4 = 4 * (l >> 4);
-    q = reinterpret_cast<const T*>(a.q);
-    k = reinterpret_cast<const T*>(a.k);
-    v = reinterpret_cast<const T*>(a.v);
-    la = reinterpret_cast<const T*>(a.la);
-    beta = reinterpret_cast<const T*>(a.beta);
+    const int g4 = 4 * (l >> 4);
+    const uint32_t rowbytes = (uint32_t)Tlen * D * C::ES;
+    const size_t base = tok0 * D * C::ES;
+    rk = make_rsrc(reinterpret_cast<const char*>(a.k) + base, rowbytes);
+    rv = make_rsrc(reinterpret_cast<const char*>(a.v) + base, rowbytes);
+    rla = make_rsrc(reinterpret_cast<const char*>(a.la) + base, rowbytes);
+    rbeta = make_rsrc(reinterpret_cast<const char*>(a.beta) + tok0 * C::ES, (uint32_t)Tlen * C::ES);
+    if constexpr (PREFILL) {
+      rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, rowbytes);
+      ro = make_rsrc(reinterpret_cast<const char*>(a.o) + base, rowbytes);
+    }
 
     for (uint32_t i = threadIdx.x * 16; i < C::LDS; i += C::THREADS * 16)
       lds_st<u32x4>(smem, i, u32x4{0u, 0u, 0u, 0u});
 
     col = vs * 16 * NC + 16 * wave + (l & 15);
-    isv = col < D;
+    isv = PREFILL || col < D;
     const size_t sbase = (size_t)seq * D * D;
     if (wave < NC) {
 #pragma unroll
@@ -522,16 +707,22 @@ struct ChunkKernel {
     }
     consumer_loop();
 
-    if (wave < NC) {
-      float* dst;
-      int c = col;
-      if (PREFILL || isv) dst = a.S_out + sbase;
-      else { dst = a.M_out + sbase; c = col - D; }
-#pragma unroll
-      for (int ci = 0; ci < D / 16; ++ci)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ci + g4 + e) * D + c] = S[ci][e];
+    // prefill over several segments: only the last one's end state is the result
+    float* dst;
+    int c = col;
+    if (PREFILL) {
+      if (a.G > 1 && gseg != a.G - 1) return;
+      dst = a.S_out + (size_t)bh * D * D;
+    } else if (isv) {
+      dst = a.S_out + sbase;
+    } else {
+      dst = a.M_out + sbase;
+      c = col - D;
     }
+#pragma unroll
+    for (int ci = 0; ci < D / 16; ++ci)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ci + g4 + e) * D + c] = S[ci][e];
   }
 };
 
@@ -558,6 +749,9 @@ static hipError_t launch_nc(const ChunkArgs& a, int nc, int nwg, hipStream_t str
     case 1: return launch_one<T, D, 1, PREFILL>(a, nwg, stream);
     case 2: return launch_one<T, D, 2, PREFILL>(a, nwg, stream);
     case 4: return launch_one<T, D, 4, PREFILL>(a, nwg, stream);
+    case 8:
+      if constexpr (sizeof(T) == 2) return launch_one<T, D, 8, PREFILL>(a, nwg, stream);
+      else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }

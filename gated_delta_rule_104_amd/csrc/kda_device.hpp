@@ -23,6 +23,14 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
+// The lane id as a value the compiler must treat as freshly produced.  LDS
+// addresses derived from it are then recomputed (a few integer ops) inside a
+// loop instead of being hoisted out of it and pinned in registers.
+__device__ __forceinline__ int fresh_lane(int l) {
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
 // Workgroup barrier for LDS hand-off.  Waits only for this wave's LDS traffic
 // (not for outstanding global loads, which are prefetches consumed later).
 __device__ __forceinline__ void sync_lds() {
@@ -110,8 +118,7 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // acc += A[r0 .. r0+15][k0 .. k0+32*nkb) * B  (bf16; bfr[m] = pack8(bt[2m], bt[2m+1]))
 template <int R>
 __device__ __forceinline__ f32x4 mma_ar_bf16(f32x4 acc, const char* smem, uint32_t base, int r0,
-                                             int k0, const bf16x8* bfr, int nkb) {
-  const int l = lane_id();
+                                             int k0, const bf16x8* bfr, int nkb, int l) {
   const uint32_t row = r0 + (l & 15);
   const uint32_t g4 = 4 * (l >> 4);
   _Pragma("unroll") for (int m = 0; m < nkb; ++m) {
@@ -126,8 +133,7 @@ __device__ __forceinline__ f32x4 mma_ar_bf16(f32x4 acc, const char* smem, uint32
 // acc += A[r0 .. r0+15][k0 .. k0+16*ntile) * B  (fp32; bt[i] accumulator tiles)
 template <int R>
 __device__ __forceinline__ f32x4 mma_ar_f32(f32x4 acc, const char* smem, uint32_t base, int r0,
-                                            int k0, const f32x4* bt, int ntile) {
-  const int l = lane_id();
+                                            int k0, const f32x4* bt, int ntile, int l) {
   const uint32_t row = r0 + (l & 15);
   const uint32_t g4 = 4 * (l >> 4);
   _Pragma("unroll") for (int i = 0; i < ntile; ++i) {
@@ -145,8 +151,7 @@ __device__ __forceinline__ f32x4 mma_ar_f32(f32x4 acc, const char* smem, uint32_
 // (both LDS, k contiguous within a row).  bf16: 16x16x32 steps, k = 8g..8g+7.
 template <int R>
 __device__ __forceinline__ f32x4 mma_ll_bf16(f32x4 acc, const char* smem, uint32_t abase, int ra0,
-                                             uint32_t bbase, int rb0, int K) {
-  const int l = lane_id();
+                                             uint32_t bbase, int rb0, int K, int l) {
   const uint32_t g8 = 8 * (l >> 4);
   _Pragma("unroll") for (int k0 = 0; k0 < K; k0 += 32) {
     bf16x8 a = lds_ld<bf16x8>(smem, abase + swz<R>(ra0 + (l & 15), 2 * (k0 + g8)));
@@ -158,8 +163,7 @@ __device__ __forceinline__ f32x4 mma_ll_bf16(f32x4 acc, const char* smem, uint32
 
 template <int R>
 __device__ __forceinline__ f32x4 mma_ll_f32(f32x4 acc, const char* smem, uint32_t abase, int ra0,
-                                            uint32_t bbase, int rb0, int K) {
-  const int l = lane_id();
+                                            uint32_t bbase, int rb0, int K, int l) {
   const uint32_t g4 = 4 * (l >> 4);
   _Pragma("unroll") for (int k0 = 0; k0 < K; k0 += 16) {
     f32x4 a = lds_ld<f32x4>(smem, abase + swz<R>(ra0 + (l & 15), 4 * (k0 + g4)));

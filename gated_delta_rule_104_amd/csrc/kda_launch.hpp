@@ -7,27 +7,29 @@
 
 namespace kda {
 
-// One chunked pass over `G * BH` independent sequences of `Tseg` tokens each.
-// Sequence s = g * BH + bh reads tokens [g*Tseg, (g+1)*Tseg) of head bh, whose
-// rows start at token (bh * G + g) * Tseg of the [BH, G*Tseg, D] inputs.
+// One chunked pass over `G * BH` independent sequences (segments).  Sequence
+// s = g * BH + bh reads tokens [g*Tseg, min((g+1)*Tseg, Ttot)) of head bh,
+// whose rows start at token bh * Ttot of the [BH, Ttot, D] inputs.
 struct ChunkArgs {
   const void* q;
   const void* k;
   const void* v;
   const void* la;
   const void* beta;
-  const float* S0;  // prefill: start states [BH, D, D] or null
-  void* o;          // prefill: outputs [BH, Tseg, D]
-  float* S_out;     // prefill: S_T [BH, D, D]; segment pass: zero-start end states [G*BH, D, D]
+  const float* S0;  // prefill: start state of every segment [G*BH, D, D] or null
+  void* o;          // prefill: outputs [BH, Ttot, D]
+  float* S_out;     // prefill: S_T [BH, D, D] (end of the last segment);
+                    // segment pass: zero-start end states [G*BH, D, D]
   float* M_out;     // segment pass: transfer maps [G*BH, D, D]
   int BH;
   int G;
-  int Tseg;
+  int Tseg;         // tokens per segment (the last one may be shorter)
+  int Ttot;         // tokens per head
   int vsplit;       // workgroups per sequence (each owns 16*nc state columns)
 };
 
 // prefill: columns = D; segment pass: columns = 2*D (state + map).
-// nc in {1, 2, 4}; nwg = G * BH * vsplit.
+// nc in {1, 2, 4, 8}; nwg = G * BH * vsplit.
 hipError_t launch_chunk(const ChunkArgs& a, bool bf16_io, int D, bool prefill, int nc, int nwg,
                         hipStream_t stream);
 

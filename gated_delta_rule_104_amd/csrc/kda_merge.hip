@@ -16,11 +16,11 @@
 namespace kda {
 
 template <int D>
-__global__ __launch_bounds__(256) void kda_merge_kernel(const float* __restrict__ S_in,
-                                                        const float* __restrict__ Z,
+// S_T may alias S_in: a workgroup reads its slice of S_in before any write.
+__global__ __launch_bounds__(256) void kda_merge_kernel(const float* S_in, const float* __restrict__ Z,
                                                         const float* __restrict__ M,
-                                                        float* __restrict__ S_start,
-                                                        float* __restrict__ S_T, int BH, int G) {
+                                                        float* __restrict__ S_start, float* S_T,
+                                                        int BH, int G) {
   __shared__ float s[D][16];
   const int bh = blockIdx.x / (D / 16);
   const int c0 = (blockIdx.x % (D / 16)) * 16;

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
   KDA_OK = 0,
@@ -66,12 +66,25 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   S0              : [B, H, dk, dv]  fp32 start states, or NULL for zero
  *   o               : [B, H, T, dv]   dtype, written
  *   S_T             : [B, H, dk, dv]  fp32 end states, written; may alias S0
+ *   workspace       : device scratch of workspace_bytes bytes, or NULL
  * Any T >= 0 is accepted (a last partial chunk is masked); T == 0 copies S0
  * (or zeros) to S_T.
+ *
+ * With few heads and a long sequence, the call can cut every sequence into
+ * segments and apply the context-parallel decomposition of the same section
+ * ("针对适配的 Infra", KDA context parallelism) on this GPU: per-segment
+ * zero-start states and transfer maps, a sequential merge, then an independent
+ * prefill of each segment.  That path needs kda_prefill_workspace_bytes() of
+ * workspace (fp32 states, three per segment and head); with a smaller or NULL
+ * workspace the call runs the single-pass path instead.  The workspace is only
+ * used by work enqueued by this call; calls on one stream may share it.
  */
+size_t kda_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtype dtype);
+
 kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
                              const void* beta, const float* S0, void* o, float* S_T, int B, int H,
-                             int T, int dk, int dv, kda_dtype dtype, hipStream_t stream);
+                             int T, int dk, int dv, kda_dtype dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * One decode step for N*H independent heads: applies the recurrence for one
@@ -109,7 +122,7 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
  * starting from S = S_in (NULL for zero).  All arrays fp32:
  *   S_in [B,H,dk,dv] or NULL; S_zero_end [G,B,H,dk,dv]; M [G,B,H,dk,dk];
  *   S_start [G,B,H,dk,dv] or NULL (not written); S_T [B,H,dk,dv].
- * S_T must not alias the other arrays.
+ * S_T may alias S_in; it must not alias S_zero_end, M or S_start.
  */
 kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const float* M,
                              float* S_start, float* S_T, int B, int H, int G, int dk, int dv,

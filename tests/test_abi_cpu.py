@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for st in range(6):
         assert lib.kda_status_string(st)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -55,7 +55,7 @@ def P(*xs):
 
 def prefill(lib, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, o=FAKE, ST=FAKE,
             B=1, H=1, T=64, dk=64, dv=64, dt=BF16):
-    return lib.kda_chunk_prefill(*P(q, k, v, la, beta, S0, o, ST), B, H, T, dk, dv, dt, None)
+    return lib.kda_chunk_prefill(*P(q, k, v, la, beta, S0, o, ST), B, H, T, dk, dv, dt, None, 0, None)
 
 
 def test_prefill_validation(lib):
@@ -71,8 +71,24 @@ def test_prefill_validation(lib):
     assert prefill(lib, S0=FAKE + 8) == ERR_ALIGN
     assert b"16-byte" in lib.kda_last_error()
     assert prefill(lib, B=1 << 20, H=1 << 10, T=1 << 20) == ERR_SHAPE
+    assert prefill(lib, B=1, H=1, T=1 << 23, dk=128, dv=128) == ERR_UNSUPPORTED
+    assert lib.kda_chunk_prefill(*P(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE), 1, 1, 64, 64, 64,
+                                 BF16, ctypes.c_void_p(FAKE + 8), 1024, None) == ERR_ALIGN
     # nothing to do: no heads
     assert prefill(lib, B=0) == OK
+
+
+def test_prefill_workspace_query(lib):
+    """The sequence-split path asks for three fp32 states per segment and head;
+    it is not used for fp32 inputs, short sequences or many heads."""
+    ws = lib.kda_prefill_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    assert ws(1, 32, 65536, 128, 128, F32) == 0
+    assert ws(1, 32, 1024, 128, 128, BF16) == 0
+    assert ws(64, 32, 65536, 128, 128, BF16) == 0
+    assert ws(1, 32, 65536, 128, 64, BF16) == 0
+    n = ws(1, 32, 65536, 128, 128, BF16)
+    assert n > 0 and n % (3 * 32 * 128 * 128 * 4) == 0
 
 
 def test_decode_validation(lib):

@@ -254,3 +254,35 @@ def test_full_h32_t64k():
     torch.cuda.synchronize()
     eo, es = check_sampled_heads(g, o, S_T, [(0, 0), (0, 13), (0, 31)])
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------- sequence-split prefill
+
+@pytest.mark.parametrize("P,T,D,variant", [(2, 300, 128, "slow"), (3, 1000, 128, "slow"),
+                                            (4, 1000, 64, "none"), (5, 2000, 128, "alpha_one")])
+def test_prefill_sequence_split(P, T, D, variant, monkeypatch):
+    """The segment-transfer / merge / segment-prefill path gives the recurrence's
+    outputs and end state (ragged last segment, start state carried through)."""
+    monkeypatch.setenv("KDA_SPLIT", str(P))
+    B, H = 1, 3
+    print(f"[case] split prefill P={P} T={T} D={D} {variant}", flush=True)
+    d = ki.gen_prefill(B, H, T, D, D, "bf16", seed=400 + P, s0_std=0.1, variant=variant)
+    g = to_dev(d)
+    assert kda.prefill_workspace_bytes(B, H, T, D, D, torch.bfloat16) > 0
+    o, S_T = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    eo, es = oracle.max_rel_l2(o.cpu(), o_ref), oracle.max_rel_l2(S_T.cpu(), S_ref)
+    print(f"    o {eo:.3e}  S_T {es:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_prefill_split_without_workspace_falls_back(monkeypatch):
+    monkeypatch.setenv("KDA_SPLIT", "4")
+    d = ki.gen_prefill(1, 2, 500, 128, 128, "bf16", seed=410, s0_std=0.1, variant="slow")
+    g = to_dev(d)
+    o, S_T = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], workspace=None)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    assert oracle.max_rel_l2(o.cpu(), o_ref) <= TOL["bf16"]
+    assert oracle.max_rel_l2(S_T.cpu(), S_ref) <= TOL["bf16"]
