@@ -9,28 +9,30 @@
 // per-channel cumulative log-gate g_r = sum_{j<=r} log a_j (kept in log space,
 // blog.csdn.net article on the Kimi K3 report, section 一.1), write
 //   Qh = q*e^g, Kh = k*e^g, Kb = k*e^-g, Gam = e^(g_C)  (g_C: last row),
-//   A = strict_lower(Kh Kb^T),  P = lower(Qh Kb^T),
-//   T = (I + diag(b) A)^-1,     Tb = T diag(b).
+//   L = diag(b) strict_lower(Kh Kb^T),  P = lower(Qh Kb^T).
 // Unrolling the recurrence over the chunk gives exactly
-//   Delta = Tb (V - Kh S),  O = Qh S + P Delta,  S' = Diag(Gam) (S + Kb^T Delta).
-// Only the last three depend on S; everything else is S-independent.  With
+//   (I + L) Delta = diag(b) (V - Kh S),
+//   O = Qh S + P Delta,   S' = Diag(Gam) (S + Kb^T Delta).
+// Only the last three depend on S.  The unit lower triangular system is solved
+// by 16-row blocks: Delta_i = T_ii (b X_i - sum_{j<i} L_ij Delta_j) with the
+// diagonal-block inverses T_ii = (I + L_ii)^-1 computed in advance.  With
 // log a >= -1 the factors e^{+-g} stay within [e^-64, e^64] inside a chunk, far
 // from the fp32/bf16 range limits.
 //
 // Work split.  Columns of S evolve independently once the S-independent
 // products are known, so a workgroup owns 16*NC state columns of one
-// sequence.  Inside a workgroup:
+// sequence (segment).  Inside a workgroup:
 //   * NC consumer waves each hold a dk x 16 column slice of S in fp32 MFMA
-//     accumulators and run the serial chain for chunk n;
-//   * NP = dk/32 producer waves compute chunk n+1's S-independent products into
-//     the other half of a double-buffered LDS stage.  The pages describe
-//     FlashKDA as splitting intra-chunk work and state passing between two
-//     independently scheduled thread groups (same section); here the two roles
-//     are wavefronts of one workgroup.
-// Three workgroup barriers per chunk separate the producer phases
-// (elementwise -> scores + diagonal inverses -> off-diagonal inverse); the
-// consumer spreads its chain over the same three intervals.  The fp32 variant
-// has no room for two stages and runs producer and consumer one after the other.
+//     accumulators and run the serial chain;
+//   * NP = dk/32 producer waves load the next chunk and compute its decayed
+//     operand tiles.  The pages describe FlashKDA as splitting intra-chunk work
+//     and state passing between two independently scheduled thread groups
+//     (same section); here the two roles are wavefronts of one workgroup.
+// Each chunk takes two workgroup barriers: interval 1 has the producers build
+// chunk n+1's elementwise tiles while the consumers run the whole chain of
+// chunk n; in interval 2 every wave takes its share of chunk n+1's score tiles
+// and diagonal inverses.  Operand tiles live in a double-buffered LDS stage.
+// The fp32 variant has no room for two stages and runs the phases in turn.
 //
 // All global traffic goes through buffer descriptors sized to the sequence, so
 // rows past its end read as zero and stores to them are dropped: a ragged last
@@ -62,20 +64,21 @@ struct ChunkCfg {
   static constexpr int R_DT = CH * ES;     // [D][CH] rows (channel-major)
   static constexpr int R_TT = CH * ES;     // [CH][CH] rows
   static constexpr int R_TI = 16 * ES;     // [16][16] rows
-  static constexpr uint32_t S_KH = 0;
-  static constexpr uint32_t S_QH = S_KH + CH * R_TD;
-  static constexpr uint32_t S_KT = S_QH + (PREFILL ? CH * R_TD : 0);
-  static constexpr uint32_t S_TB = S_KT + D * R_DT;
-  static constexpr uint32_t S_P = S_TB + CH * R_TT;
-  static constexpr uint32_t S_GM = S_P + (PREFILL ? CH * R_TT : 0);
-  static constexpr uint32_t STAGE = S_GM + D * 4;
+  // stage: everything the chain of one chunk reads
+  static constexpr uint32_t S_KH = 0;                                   // Kh   [CH][D]
+  static constexpr uint32_t S_QH = S_KH + CH * R_TD;                    // Qh   [CH][D]
+  static constexpr uint32_t S_KT = S_QH + (PREFILL ? CH * R_TD : 0);    // Kb^T [D][CH]
+  static constexpr uint32_t S_L = S_KT + D * R_DT;                      // -L   [CH][CH]
+  static constexpr uint32_t S_P = S_L + CH * R_TT;                      // P    [CH][CH]
+  static constexpr uint32_t S_TI = S_P + (PREFILL ? CH * R_TT : 0);     // T_ii [4][16][16]
+  static constexpr uint32_t S_GM = S_TI + 4 * 16 * R_TI;                // Gam  [D] fp32
+  static constexpr uint32_t S_BETA = S_GM + D * 4;                      // beta [CH] fp32
+  static constexpr uint32_t STAGE = S_BETA + CH * 4;
+  // producer scratch: Kb time-major, the B operand of the score products
   static constexpr uint32_t X_KB = STAGES * STAGE;
-  static constexpr uint32_t X_L = X_KB + CH * R_TD;
-  static constexpr uint32_t X_TI = X_L + CH * R_TT;
-  static constexpr uint32_t X_BETA = X_TI + 4 * 16 * R_TI;
-  static constexpr uint32_t LDS = X_BETA + CH * 4;
+  static constexpr uint32_t LDS = X_KB + CH * R_TD;
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(LDS % 16 == 0, "LDS size");
+  static_assert(LDS % 16 == 0 && STAGE % 16 == 0, "LDS alignment");
 };
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -87,6 +90,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+
+// DPP moves within rows of 16 lanes (gfx9 encodings): row_shr:n shifts values
+// n lanes up inside the row (lanes below n read 0); row_share:15 broadcasts
+// lane 15 of the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_ROW_SHR = 0x110;
+constexpr int DPP_ROW_SHARE15 = 0x15F;
 
 // 8 consecutive elements of a token row, as loaded from HBM.
 template <typename T> struct Raw8 { u32x4 p[sizeof(T) / 2]; };
@@ -118,7 +131,20 @@ template <typename T> struct ProdRaw {
   uint32_t beta;
 };
 
-template <typename T> struct VRegs { uint32_t v[16]; };
+// Value rows of one chunk for a consumer lane (accumulator layout): 16 elements,
+// two bf16 per register or one fp32 per register.
+template <typename T> struct VRegs;
+template <> struct VRegs<bf16> {
+  typedef __attribute__((ext_vector_type(2))) unsigned short us2;
+  us2 v[8];
+  __device__ __forceinline__ void set(int i, unsigned short x) { v[i >> 1][i & 1] = x; }
+  __device__ __forceinline__ float get(int i) const { return __uint_as_float((uint32_t)v[i >> 1][i & 1] << 16); }
+};
+template <> struct VRegs<float> {
+  uint32_t v[16];
+  __device__ __forceinline__ void set(int i, uint32_t x) { v[i] = x; }
+  __device__ __forceinline__ float get(int i) const { return __uint_as_float(v[i]); }
+};
 
 // Operand fragments.  bf16: one v_mfma_f32_16x16x32_bf16 per 32-deep k block;
 // fp32: four v_mfma_f32_16x16x4_f32 steps per 16-deep k block.  "ar" fragments
@@ -129,11 +155,11 @@ template <bool BF> struct Frag;
 template <> struct Frag<true> {
   typedef bf16x8 A;
   typedef bf16x8 B;
+  typedef bf16x4 A16;
   static constexpr int KB = 32;
-  template <int R>
-  __device__ __forceinline__ static A ar(const char* smem, uint32_t base, int row, int kk) {
-    return cat8(lds_ld<bf16x4>(smem, base + swz<R>(row, 2 * kk)),
-                lds_ld<bf16x4>(smem, base + swz<R>(row, 2 * (kk + 16))));
+  // ar fragment at byte offsets o0 (k = kk..kk+3) and o1 (k = kk+16..kk+19)
+  __device__ __forceinline__ static A ar2(const char* smem, uint32_t o0, uint32_t o1) {
+    return cat8(lds_ld<bf16x4>(smem, o0), lds_ld<bf16x4>(smem, o1));
   }
   template <int R>
   __device__ __forceinline__ static A ll(const char* smem, uint32_t base, int row, int k0, int ln) {
@@ -141,14 +167,17 @@ template <> struct Frag<true> {
   }
   __device__ __forceinline__ static B bfrag(const f32x4* t, int m) { return pack8(t[2 * m], t[2 * m + 1]); }
   __device__ __forceinline__ static f32x4 mma(f32x4 acc, A a, B b) { return mfma_bf16_k32(acc, a, b); }
+  __device__ __forceinline__ static f32x4 mma16(f32x4 acc, A16 a, f32x4 b) {
+    return mfma_bf16_k16(acc, a, pack4(b));
+  }
 };
 template <> struct Frag<false> {
   typedef f32x4 A;
   typedef f32x4 B;
+  typedef f32x4 A16;
   static constexpr int KB = 16;
-  template <int R>
-  __device__ __forceinline__ static A ar(const char* smem, uint32_t base, int row, int kk) {
-    return lds_ld<f32x4>(smem, base + swz<R>(row, 4 * kk));
+  __device__ __forceinline__ static A ar2(const char* smem, uint32_t o0, uint32_t) {
+    return lds_ld<f32x4>(smem, o0);
   }
   template <int R>
   __device__ __forceinline__ static A ll(const char* smem, uint32_t base, int row, int k0, int ln) {
@@ -161,12 +190,14 @@ template <> struct Frag<false> {
     acc = mfma_f32_k4(acc, a[2], b[2]);
     return mfma_f32_k4(acc, a[3], b[3]);
   }
+  __device__ __forceinline__ static f32x4 mma16(f32x4 acc, A16 a, f32x4 b) { return mma(acc, a, b); }
 };
 
 template <typename T, int D, int NC, bool PREFILL>
 struct ChunkKernel {
   using C = ChunkCfg<T, D, NC, PREFILL>;
   using F = Frag<C::BF>;
+  typedef typename F::A16 A16;
   static constexpr int KB = F::KB;
   static constexpr int NKD = D / KB;    // k blocks over channels
   static constexpr int NKT = CH / KB;   // k blocks over the tokens of a chunk
@@ -181,20 +212,26 @@ struct ChunkKernel {
   int col;          // global column of this lane's state slice
   bool isv;         // column reads v (value column) rather than being a map column
   f32x4 S[D / 16];
-  f32x4 Dl[4];      // Delta tiles of the current chunk
   typename F::B sb[NKD], db[NKT];
+  // Per-lane LDS byte offsets of the consumer's A fragments inside a tile of
+  // each row size, for row tile 0 (the swizzle term depends only on the lane's
+  // row within 16, so row tile t adds 16*t*rowbytes).  [k block][half]
+  // (token-by-token tiles and channel-by-token tiles have the same row size.)
+  static_assert(C::R_TT == C::R_DT, "shared fragment offsets");
+  uint32_t oTD[NKD][2], oTT[NKT][2], o16;
 
   __device__ __forceinline__ uint32_t stage(int chunk) const {
     return (C::STAGES == 2 ? (uint32_t)(chunk & 1) : 0u) * C::STAGE;
   }
 
   // ------------------------------------------------------------ producers
-  // Lane (tg = l/4, cs = l%4) of producer wave pw owns tokens 4*tg..4*tg+3 and
-  // channels 32*pw + 8*cs .. +7 of the chunk.
+  // Lane (tg = l%16, cs = l/16) of producer wave pw owns tokens 4*tg..4*tg+3 and
+  // channels 32*pw + 8*cs .. +7 of the chunk; a channel's 16 token groups are
+  // one DPP row, so the prefix sum over tokens runs on row operations.
   __device__ __forceinline__ void load_raw(ProdRaw<T>& r, int chunk) const {
     const int ln = fresh_lane(l);
     const int pw = wave - NC;
-    const int tg = ln >> 2, cs = ln & 3;
+    const int tg = ln & 15, cs = ln >> 4;
     const int ch = 32 * pw + 8 * cs;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -216,7 +253,7 @@ struct ChunkKernel {
   __device__ __forceinline__ void p1(const ProdRaw<T>& r, uint32_t st) {
     const int ln = fresh_lane(l);
     const int pw = wave - NC;
-    const int tg = ln >> 2, cs = ln & 3;
+    const int tg = ln & 15, cs = ln >> 4;
     const int ch = 32 * pw + 8 * cs;
     float g[4][8];
 #pragma unroll
@@ -233,22 +270,15 @@ struct ChunkKernel {
       g[1][c] += g[0][c];
       g[2][c] += g[1][c];
       g[3][c] += g[2][c];
-      inc[c] = g[3][c];
-    }
-    // inclusive scan of the 4-token totals over the 16 token groups (lane stride 4)
-#pragma unroll
-    for (int d = 4; d < 64; d *= 2) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float y = __shfl_up(inc[c], d);
-        if (ln >= d) inc[c] += y;
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float y = __shfl_up(inc[c], 4);
-      exc[c] = (ln >= 4) ? y : 0.f;
-      gc[c] = __shfl(inc[c], 60 + cs);
+      // inclusive prefix of the 4-token totals over the 16 token groups of the row
+      float x = g[3][c];
+      x += dpp<DPP_ROW_SHR + 1>(x);
+      x += dpp<DPP_ROW_SHR + 2>(x);
+      x += dpp<DPP_ROW_SHR + 4>(x);
+      x += dpp<DPP_ROW_SHR + 8>(x);
+      inc[c] = x;
+      exc[c] = dpp<DPP_ROW_SHR + 1>(x);
+      gc[c] = dpp<DPP_ROW_SHARE15>(x);
     }
     float kb[4][8];
 #pragma unroll
@@ -315,7 +345,7 @@ struct ChunkKernel {
     }
     if (pw == 0) {
       const float b = C::BF ? __uint_as_float(r.beta << 16) : __uint_as_float(r.beta);
-      lds_st<float>(smem, C::X_BETA + 4 * ln, b);
+      lds_st<float>(smem, st + C::S_BETA + 4 * ln, b);
     }
   }
 
@@ -323,165 +353,147 @@ struct ChunkKernel {
     lds_st<T>(smem, base + swz<C::R_TT>(r, C::ES * s), from_f32<T>(x));
   }
 
-  // 16x16x16 product: A fragment (row l%16, k = 4*(l/16)..+3) times an
-  // accumulator tile used as B.
-  typedef typename std::conditional<C::BF, bf16x4, f32x4>::type A16;
   template <int RR>
   __device__ __forceinline__ A16 frag16(uint32_t base, int row, int k0, int ln) const {
     if constexpr (C::BF) return lds_ld<bf16x4>(smem, base + swz<RR>(row, 2 * (k0 + 4 * (ln >> 4))));
     else return lds_ld<f32x4>(smem, base + swz<RR>(row, 4 * (k0 + 4 * (ln >> 4))));
   }
-  __device__ __forceinline__ static f32x4 mma16(f32x4 acc, A16 a, f32x4 b) {
-    if constexpr (C::BF) {
-      return mfma_bf16_k16(acc, a, pack4(b));
-    } else {
-      acc = mfma_f32_k4(acc, a[0], b[0]);
-      acc = mfma_f32_k4(acc, a[1], b[1]);
-      acc = mfma_f32_k4(acc, a[2], b[2]);
-      return mfma_f32_k4(acc, a[3], b[3]);
-    }
-  }
 
-  // Phase 2, one row task: tiles (I, 0..I) of L = diag(b) A (MAT 0) or P (MAT 1).
-  // All operand fragments of the task are fetched before its MFMAs.  An L task
-  // then inverts its diagonal block (I + L_II) with matrix cores.
-  template <int MAT, int I>
-  __device__ __forceinline__ void p2_row(uint32_t st) {
+  // Phase 2, one tile task: tile (I, J), J <= I, of -L (MAT 0) or of P (MAT 1).
+  // Operand fragments are fetched before the MFMAs.  The diagonal L tile task
+  // also inverts its block (I + L_II) with matrix cores.
+  template <int MAT, int I, int J>
+  __device__ __forceinline__ void p2_tile(uint32_t st) {
     const int ln = fresh_lane(l);
     const int g4 = 4 * (ln >> 4);
     const uint32_t abase = MAT ? st + C::S_QH : st + C::S_KH;
     const int s0 = ln & 15;
-    typename F::A fa[NKD], fb[I + 1][NKD];
+    typename F::A fa[NKD], fb[NKD];
 #pragma unroll
     for (int m = 0; m < NKD; ++m) {
       fa[m] = F::template ll<C::R_TD>(smem, abase, 16 * I + s0, KB * m, ln);
-#pragma unroll
-      for (int j = 0; j <= I; ++j) fb[j][m] = F::template ll<C::R_TD>(smem, C::X_KB, 16 * j + s0, KB * m, ln);
+      fb[m] = F::template ll<C::R_TD>(smem, C::X_KB, 16 * J + s0, KB * m, ln);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc[I + 1];
-#pragma unroll
-    for (int j = 0; j <= I; ++j) acc[j] = zero4();
-#pragma unroll
-    for (int m = 0; m < NKD; ++m)
-#pragma unroll
-      for (int j = 0; j <= I; ++j) acc[j] = F::mma(acc[j], fa[m], fb[j][m]);
     float bet[4];
     if (MAT == 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bet[e] = lds_ld<float>(smem, C::X_BETA + 4 * (16 * I + g4 + e));
+      for (int e = 0; e < 4; ++e) bet[e] = lds_ld<float>(smem, st + C::S_BETA + 4 * (16 * I + g4 + e));
     }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc = zero4();
 #pragma unroll
-    for (int j = 0; j <= I; ++j) {
-      const int s = 16 * j + s0;
+    for (int m = 0; m < NKD; ++m) acc = F::mma(acc, fa[m], fb[m]);
+    const int s = 16 * J + s0;
+    f32x4 N;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * I + g4 + e;
-        if (MAT == 0) store_tt(C::X_L, r, s, s < r ? acc[j][e] * bet[e] : 0.f);
-        else store_tt(st + C::S_P, r, s, s <= r ? acc[j][e] : 0.f);
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * I + g4 + e;
+      if (MAT == 0) {
+        N[e] = s < r ? acc[e] * bet[e] : 0.f;
+        store_tt(st + C::S_L, r, s, -N[e]);
+      } else {
+        store_tt(st + C::S_P, r, s, s <= r ? acc[e] : 0.f);
       }
     }
-    if constexpr (MAT == 0) {
-      // Inverse of the diagonal block, (I + N)^-1 with N = L_II strictly lower
-      // (nilpotent, N^16 = 0), as the exact product (I - N)(I + N^2)(I + N^4)(I + N^8).
-      // Each factor is applied as Y += N^(2^k) Y with Y accumulated in fp32; the
-      // powers of N pass through the block's 16x16 slot of the inverse scratch
-      // to serve as A operands.
-      f32x4 N, Y;
+    if constexpr (MAT == 0 && I == J) {
+      // (I + N)^-1 with N = L_II strictly lower (nilpotent, N^16 = 0), as the
+      // exact product (I - N)(I + N^2)(I + N^4)(I + N^8).  Each factor is applied
+      // as Y += N^(2^k) Y with Y accumulated in fp32; N^2, N^4, N^8 pass through
+      // the block's slot of the stage to serve as A operands, and N itself is
+      // read back negated from the -L tile just written.
+      f32x4 Y, nN;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * I + g4 + e, sc = 16 * I + s0;
-        N[e] = sc < r ? acc[I][e] * bet[e] : 0.f;
         Y[e] = (g4 + e == s0 ? 1.f : 0.f) - N[e];
+        nN[e] = -N[e];
       }
-      const uint32_t ti = C::X_TI + I * 16 * C::R_TI;
+      const uint32_t ti = st + C::S_TI + I * 16 * C::R_TI;
       auto put = [&](const f32x4& t) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) lds_st<T>(smem, ti + swz<C::R_TI>(g4 + e, C::ES * s0), from_f32<T>(t[e]));
       };
-      wave_lds_fence();  // L_II rows written above are read as the A operand of N * N
-      A16 an = frag16<C::R_TT>(C::X_L, 16 * I + s0, 16 * I, ln);
-      f32x4 P2 = mma16(zero4(), an, N);
+      wave_lds_fence();  // the -L_II tile written above is the A operand of (-N)(-N)
+      A16 an = frag16<C::R_TT>(st + C::S_L, 16 * I + s0, 16 * I, ln);
+      f32x4 P2 = F::mma16(zero4(), an, nN);
       put(P2);
       wave_lds_fence();
       A16 a2 = frag16<C::R_TI>(ti, s0, 0, ln);
-      Y = mma16(Y, a2, Y);
-      f32x4 P4 = mma16(zero4(), a2, P2);
+      Y = F::mma16(Y, a2, Y);
+      f32x4 P4 = F::mma16(zero4(), a2, P2);
       put(P4);
       wave_lds_fence();
       A16 a4 = frag16<C::R_TI>(ti, s0, 0, ln);
-      Y = mma16(Y, a4, Y);
-      f32x4 P8 = mma16(zero4(), a4, P4);
+      Y = F::mma16(Y, a4, Y);
+      f32x4 P8 = F::mma16(zero4(), a4, P4);
       put(P8);
       wave_lds_fence();
       A16 a8 = frag16<C::R_TI>(ti, s0, 0, ln);
-      Y = mma16(Y, a8, Y);
+      Y = F::mma16(Y, a8, Y);
       put(Y);
     }
   }
 
-  // Task K of the phase-2 list, heaviest rows first:
-  // prefill (A3, P3, A2, P2, A1, P1, A0, P0); segment pass (A3, A2, A1, A0).
-  template <int K>
-  __device__ __forceinline__ void p2_task(uint32_t st, int pw) {
-    constexpr int NTASK = PREFILL ? 8 : 4;
-    if constexpr (K < NTASK) {
-      if (K % C::NP == pw) {
-        constexpr int MAT = PREFILL ? (K & 1) : 0;
-        constexpr int I = 3 - (PREFILL ? (K >> 1) : K);
-        p2_row<MAT, I>(st);
+  // Phase-2 task list, shared by every wave of the workgroup (task K runs on
+  // wave K mod NW): the four diagonal L tiles (with their inverses) first,
+  // then the P tiles (prefill only), then the off-diagonal L tiles.
+  static constexpr int NT2 = PREFILL ? 20 : 10;
+  static constexpr int task_mat(int K) { return K < 4 ? 0 : (PREFILL && K < 14 ? 1 : 0); }
+  static constexpr int task_i(int K) {
+    if (K < 4) return K;
+    int k = K - 4;
+    if (PREFILL) {
+      if (k < 10) {
+        const int ii[10] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
+        return ii[k];
       }
-      p2_task<K + 1>(st, pw);
+      k -= 10;
+    }
+    const int io[6] = {3, 3, 3, 2, 2, 1};
+    return io[k];
+  }
+  static constexpr int task_j(int K) {
+    if (K < 4) return K;
+    int k = K - 4;
+    if (PREFILL) {
+      if (k < 10) {
+        const int jj[10] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
+        return jj[k];
+      }
+      k -= 10;
+    }
+    const int jo[6] = {2, 1, 0, 1, 0, 0};
+    return jo[k];
+  }
+
+  template <int K>
+  __device__ __forceinline__ void p2_task(uint32_t st) {
+    if constexpr (K < NT2) {
+      if (K % C::NW == wave) p2_tile<task_mat(K), task_i(K), task_j(K)>(st);
+      p2_task<K + 1>(st);
     }
   }
 
-  __device__ __forceinline__ void p2(uint32_t st) { p2_task<0>(st, wave - NC); }
-
-  // Phase 3: off-diagonal blocks of T = (I + L)^-1 by block forward
-  // substitution, T_ij = -T_ii sum_{m=j}^{i-1} L_im T_mj, then Tb = T diag(b).
-  // Column block J of T is one task; its LDS operands are fetched up front.
-  template <int J>
-  __device__ __forceinline__ void p3_col(uint32_t st) {
-    const int ln = fresh_lane(l);
-    const int g4 = 4 * (ln >> 4);
-    const int r16 = ln & 15;
-    A16 fl[4][4], ft[4];
-#pragma unroll
-    for (int i = J + 1; i < 4; ++i) {
-      ft[i] = frag16<C::R_TI>(C::X_TI + i * 16 * C::R_TI, r16, 0, ln);
-#pragma unroll
-      for (int m = J; m < i; ++m) fl[i][m] = frag16<C::R_TT>(C::X_L, 16 * i + r16, 16 * m, ln);
-    }
-    f32x4 Tc[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      Tc[J][e] = to_f32(lds_ld<T>(smem, C::X_TI + J * 16 * C::R_TI + swz<C::R_TI>(g4 + e, C::ES * r16)));
-    const int s = 16 * J + r16;
-    const float b = lds_ld<float>(smem, C::X_BETA + 4 * s);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = J + 1; i < 4; ++i) {
-      f32x4 y = zero4();
-#pragma unroll
-      for (int m = J; m < i; ++m) y = mma16(y, fl[i][m], Tc[m]);
-      Tc[i] = -mma16(zero4(), ft[i], y);
-    }
-#pragma unroll
-    for (int m = J; m < 4; ++m) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) store_tt(st + C::S_TB, 16 * m + g4 + e, s, Tc[m][e] * b);
-    }
-  }
-
-  __device__ __forceinline__ void p3(uint32_t st) {
-    const int pw = wave - NC;
-    if (0 % C::NP == pw) p3_col<0>(st);
-    if (1 % C::NP == pw) p3_col<1>(st);
-    if (2 % C::NP == pw) p3_col<2>(st);
-    if (3 % C::NP == pw) p3_col<3>(st);
-  }
+  __device__ __forceinline__ void p2(uint32_t st) { p2_task<0>(st); }
 
   // ------------------------------------------------------------ consumers
+  __device__ __forceinline__ void init_offsets() {
+    const int r16 = l & 15, kk = 4 * (l >> 4);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int m = 0; m < NKD; ++m) oTD[m][h] = swz<C::R_TD>(r16, C::ES * (KB * m + kk + 16 * h));
+#pragma unroll
+      for (int m = 0; m < NKT; ++m) oTT[m][h] = swz<C::R_TT>(r16, C::ES * (KB * m + kk + 16 * h));
+    }
+    o16 = swz<C::R_TI>(r16, C::ES * kk);
+  }
+
+  // A fragment of row tile `t` and k block m of an LDS tile at `base`.
+  template <int R>
+  __device__ __forceinline__ typename F::A ar(uint32_t base, const uint32_t (*o)[2], int t, int m) const {
+    return F::ar2(smem, base + o[m][0] + 16 * t * R, base + o[m][1] + 16 * t * R);
+  }
+
   // Lane l holds rows 16*ti + 4*(l/16) + e of its column (accumulator layout).
   __device__ __forceinline__ void load_v(VRegs<T>& vr, int chunk) const {
     const int ln = fresh_lane(l);
@@ -493,108 +505,127 @@ struct ChunkKernel {
         // map columns (segment pass) read v = 0: their offset is past any buffer end
         const uint32_t off = ((uint32_t)((chunk * CH + 16 * ti + g4 + e) * D + col) * C::ES) |
                              (isv ? 0u : 0x80000000u);
-        if constexpr (C::BF) vr.v[4 * ti + e] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0);
-        else vr.v[4 * ti + e] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
+        if constexpr (C::BF) vr.set(4 * ti + e, __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0));
+        else vr.set(4 * ti + e, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0));
       }
     }
   }
 
-  __device__ __forceinline__ float vval(const VRegs<T>& vr, int i) const {
-    return C::BF ? __uint_as_float(vr.v[i] << 16) : __uint_as_float(vr.v[i]);
-  }
+  __device__ __forceinline__ float vval(const VRegs<T>& vr, int i) const { return vr.get(i); }
 
-  // Interval 1: Delta = Tb (V - Kh S).
-  __device__ __forceinline__ void c1(const VRegs<T>& vr, uint32_t st) {
-    const int ln = fresh_lane(l);
-    const int r16 = ln & 15, kk = 4 * (ln >> 4);
-    typename F::A fk[4][NKD], ft[4][NKT];
+  // X_t = b_t (v_t - (Kh S)_t) for row tiles H0, H0+1 (fragments fetched first).
+  template <int H0>
+  __device__ __forceinline__ void c1_half(const VRegs<T>& vr, uint32_t st, f32x4* X) {
+    typename F::A fk[2][NKD];
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int m = 0; m < NKD; ++m) fk[ti][m] = F::template ar<C::R_TD>(smem, st + C::S_KH, 16 * ti + r16, KB * m + kk);
-#pragma unroll
-      for (int m = 0; m <= tri(ti); ++m) ft[ti][m] = F::template ar<C::R_TT>(smem, st + C::S_TB, 16 * ti + r16, KB * m + kk);
-    }
-#pragma unroll
-    for (int m = 0; m < NKD; ++m) sb[m] = F::bfrag(S, m);
+      for (int m = 0; m < NKD; ++m) fk[h][m] = ar<C::R_TD>(st + C::S_KH, oTD, H0 + h, m);
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 X[4];
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) X[ti] = zero4();
+    X[H0] = zero4();
+    X[H0 + 1] = zero4();
 #pragma unroll
     for (int m = 0; m < NKD; ++m)
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) X[ti] = F::mma(X[ti], fk[ti][m], sb[m]);
+      for (int h = 0; h < 2; ++h) X[H0 + h] = F::mma(X[H0 + h], fk[h][m], sb[m]);
+    const int kk = 4 * (l >> 4);
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 bet = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * (H0 + h) + kk));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) X[ti][e] = vval(vr, 4 * ti + e) - X[ti][e];
-    typename F::B xb[NKT];
+      for (int e = 0; e < 4; ++e)
+        X[H0 + h][e] = bet[e] * (vval(vr, 4 * (H0 + h) + e) - X[H0 + h][e]);
+    }
+  }
+
+  // Delta from (I + L) Delta = diag(b) (V - Kh S) by 16-row blocks:
+  // Delta_i = T_ii (X_i + sum_{j<i} (-L_ij) Delta_j).
+  __device__ __forceinline__ void c1(const VRegs<T>& vr, uint32_t st) {
+    const int kk = 4 * (l >> 4);
 #pragma unroll
-    for (int m = 0; m < NKT; ++m) xb[m] = F::bfrag(X, m);
+    for (int m = 0; m < NKD; ++m) sb[m] = F::bfrag(S, m);
+    f32x4 X[4];
+    c1_half<0>(vr, st, X);
+    c1_half<2>(vr, st, X);
+    A16 ft[4], fl[4][4];
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) Dl[ti] = zero4();
+    for (int ti = 0; ti < 4; ++ti) {
+      ft[ti] = lds_ld<A16>(smem, st + C::S_TI + ti * 16 * C::R_TI + o16);
 #pragma unroll
-    for (int m = 0; m < NKT; ++m)
+      for (int j = 0; j < ti; ++j)
+        fl[ti][j] = lds_ld<A16>(smem, st + C::S_L + 16 * ti * C::R_TT +
+                                          swz<C::R_TT>(l & 15, C::ES * (16 * j + kk)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 Dl[4];
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti)
-        if (m <= tri(ti)) Dl[ti] = F::mma(Dl[ti], ft[ti][m], xb[m]);
+    for (int ti = 0; ti < 4; ++ti) {
+      f32x4 rr = X[ti];
+#pragma unroll
+      for (int j = 0; j < ti; ++j) rr = F::mma16(rr, fl[ti][j], Dl[j]);  // fl holds -L
+      Dl[ti] = F::mma16(zero4(), ft[ti], rr);
+    }
 #pragma unroll
     for (int m = 0; m < NKT; ++m) db[m] = F::bfrag(Dl, m);
   }
 
-  // Interval 2: O = Qh S + P Delta, stored (rows past the sequence end are dropped).
-  __device__ __forceinline__ void c2(uint32_t st, int chunk) {
-    if constexpr (PREFILL) {
-      const int ln = fresh_lane(l);
-      const int r16 = ln & 15, kk = 4 * (ln >> 4);
-      typename F::A fq[4][NKD], fp[4][NKT];
+  // O = Qh S + P Delta, stored (rows past the sequence end are dropped).  Two
+  // halves of two row tiles each keep the prefetched fragments small.
+  template <int H0>
+  __device__ __forceinline__ void c2_half(uint32_t st, int chunk) {
+    const int kk = 4 * (l >> 4);
+    typename F::A fq[2][NKD], fp[2][NKT];
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
+    for (int h = 0; h < 2; ++h) {
+      const int ti = H0 + h;
 #pragma unroll
-        for (int m = 0; m < NKD; ++m) fq[ti][m] = F::template ar<C::R_TD>(smem, st + C::S_QH, 16 * ti + r16, KB * m + kk);
+      for (int m = 0; m < NKD; ++m) fq[h][m] = ar<C::R_TD>(st + C::S_QH, oTD, ti, m);
 #pragma unroll
-        for (int m = 0; m <= tri(ti); ++m) fp[ti][m] = F::template ar<C::R_TT>(smem, st + C::S_P, 16 * ti + r16, KB * m + kk);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 O[4];
+      for (int m = 0; m <= tri(ti); ++m) fp[h][m] = ar<C::R_TT>(st + C::S_P, oTT, ti, m);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 O[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) O[ti] = zero4();
+    for (int m = 0; m < NKD; ++m)
 #pragma unroll
-      for (int m = 0; m < NKD; ++m)
+      for (int h = 0; h < 2; ++h) O[h] = F::mma(O[h], fq[h][m], sb[m]);
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) O[ti] = F::mma(O[ti], fq[ti][m], sb[m]);
+    for (int m = 0; m < NKT; ++m)
 #pragma unroll
-      for (int m = 0; m < NKT; ++m)
+      for (int h = 0; h < 2; ++h)
+        if (m <= tri(H0 + h)) O[h] = F::mma(O[h], fp[h][m], db[m]);
+    const uint32_t ob = (uint32_t)((chunk * CH + kk) * D + col) * C::ES;
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
-          if (m <= tri(ti)) O[ti] = F::mma(O[ti], fp[ti][m], db[m]);
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t off = (uint32_t)((chunk * CH + 16 * ti + kk + e) * D + col) * C::ES;
-          if constexpr (C::BF) {
-            const bf16 hv = (bf16)O[ti][e];
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ro, off, 0, 0);
-          } else {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[ti][e]), ro, off, 0, 0);
-          }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t off = ob + (uint32_t)((16 * (H0 + h) + e) * D * C::ES);
+        if constexpr (C::BF) {
+          const bf16 hv = (bf16)O[h][e];
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ro, off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[h][e]), ro, off, 0, 0);
         }
       }
     }
   }
 
-  // Interval 3: S = Diag(Gam) (S + Kb^T Delta).
+  __device__ __forceinline__ void c2(uint32_t st, int chunk) {
+    if constexpr (PREFILL) {
+      c2_half<0>(st, chunk);
+      c2_half<2>(st, chunk);
+    }
+  }
+
+  // S = Diag(Gam) (S + Kb^T Delta).
   __device__ __forceinline__ void c3(uint32_t st) {
-    const int ln = fresh_lane(l);
-    const int r16 = ln & 15, kk = 4 * (ln >> 4);
+    const int kk = 4 * (l >> 4);
     typename F::A fk[D / 16][NKT];
     f32x4 gm[D / 16];
 #pragma unroll
     for (int ci = 0; ci < D / 16; ++ci) {
 #pragma unroll
-      for (int m = 0; m < NKT; ++m) fk[ci][m] = F::template ar<C::R_DT>(smem, st + C::S_KT, 16 * ci + r16, KB * m + kk);
+      for (int m = 0; m < NKT; ++m) fk[ci][m] = ar<C::R_DT>(st + C::S_KT, oTT, ci, m);
       gm[ci] = lds_ld<f32x4>(smem, st + C::S_GM + 4 * (16 * ci + kk));
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -606,10 +637,19 @@ struct ChunkKernel {
     for (int ci = 0; ci < D / 16; ++ci) S[ci] = S[ci] * gm[ci];
   }
 
-  // Pipeline.  Iteration `it` has producers prepare chunk it while consumers
-  // run chunk it - LAG; both roles execute the same barrier sequence.  Each
-  // role keeps one set of prefetch registers: the loads for the next chunk
-  // are issued as soon as the current chunk's registers have been consumed.
+  __device__ __forceinline__ void chain(VRegs<T>& vr, int cc) {
+    c1(vr, stage(cc));
+    if (cc + 1 < nch) load_v(vr, cc + 1);
+    c2(stage(cc), cc);
+    c3(stage(cc));
+  }
+
+  // Pipeline.  Iteration `it` prepares chunk it and runs the serial chain of
+  // chunk it - LAG: interval 1 has the producer waves build the elementwise
+  // tiles while the consumer waves run the chain; in interval 2 every wave
+  // takes its share of the score tiles and diagonal inverses.  Producer waves
+  // keep one set of prefetch registers, refilled as soon as the current
+  // chunk's are consumed.
   __device__ __forceinline__ void producer_loop() {
     ProdRaw<T> r;
     if (nch > 0) load_raw(r, 0);
@@ -622,32 +662,24 @@ struct ChunkKernel {
       sync_lds();
       if (w) p2(stage(it));
       sync_lds();
-      if (w) p3(stage(it));
-      sync_lds();
       if (!C::LAG) sync_lds();
     }
   }
 
   __device__ __forceinline__ void consumer_loop() {
     VRegs<T> vr;
+    init_offsets();
     if (nch > 0) load_v(vr, 0);
     for (int it = 0; it < nch + C::LAG; ++it) {
       const int cc = it - C::LAG;
-      const bool w = cc >= 0;
-      if (!C::LAG) {
-        sync_lds();
-        sync_lds();
-        sync_lds();
-      }
-      if (w) {
-        c1(vr, stage(cc));
-        if (cc + 1 < nch) load_v(vr, cc + 1);
-      }
-      if (C::LAG) sync_lds();
-      if (w) c2(stage(cc), cc);
-      if (C::LAG) sync_lds();
-      if (w) c3(stage(cc));
+      if (C::LAG && cc >= 0) chain(vr, cc);
       sync_lds();
+      if (it < nch) p2(stage(it));
+      sync_lds();
+      if (!C::LAG) {
+        chain(vr, cc);
+        sync_lds();
+      }
     }
   }
 
