@@ -148,19 +148,16 @@ template <> struct VRegs<float> {
 
 // Operand fragments.  bf16: one v_mfma_f32_16x16x32_bf16 per 32-deep k block;
 // fp32: four v_mfma_f32_16x16x4_f32 steps per 16-deep k block.  "ar" fragments
-// pair an LDS A operand with a B operand held as accumulator tiles (k positions
-// 4g..4g+3 of each 16-deep tile, g = lane/16); "ll" fragments read both
-// operands from LDS with k contiguous per lane.
+// are LDS A operands against B operands held as accumulator tiles (bf16 tiles
+// stored in kpos order, so one 16-byte read per lane); "ll" fragments read both
+// operands from LDS, 8 (bf16) or 4 (fp32) consecutive stored positions per lane,
+// which is a valid contraction as long as both tiles use the same order.
 template <bool BF> struct Frag;
 template <> struct Frag<true> {
   typedef bf16x8 A;
   typedef bf16x8 B;
   typedef bf16x4 A16;
   static constexpr int KB = 32;
-  // ar fragment at byte offsets o0 (k = kk..kk+3) and o1 (k = kk+16..kk+19)
-  __device__ __forceinline__ static A ar2(const char* smem, uint32_t o0, uint32_t o1) {
-    return cat8(lds_ld<bf16x4>(smem, o0), lds_ld<bf16x4>(smem, o1));
-  }
   template <int R>
   __device__ __forceinline__ static A ll(const char* smem, uint32_t base, int row, int k0, int ln) {
     return lds_ld<bf16x8>(smem, base + swz<R>(row, 2 * (k0 + 8 * (ln >> 4))));
@@ -176,9 +173,6 @@ template <> struct Frag<false> {
   typedef f32x4 B;
   typedef f32x4 A16;
   static constexpr int KB = 16;
-  __device__ __forceinline__ static A ar2(const char* smem, uint32_t o0, uint32_t) {
-    return lds_ld<f32x4>(smem, o0);
-  }
   template <int R>
   __device__ __forceinline__ static A ll(const char* smem, uint32_t base, int row, int k0, int ln) {
     return lds_ld<f32x4>(smem, base + swz<R>(row, 4 * (k0 + 4 * (ln >> 4))));
@@ -201,6 +195,8 @@ struct ChunkKernel {
   static constexpr int KB = F::KB;
   static constexpr int NKD = D / KB;    // k blocks over channels
   static constexpr int NKT = CH / KB;   // k blocks over the tokens of a chunk
+  // stored position of k in tiles read as "ar" A operands
+  static constexpr int kp(int k) { return C::BF ? kpos(k) : k; }
   // last k block a lower-triangular row tile ti touches
   static constexpr int tri(int ti) { return (16 * ti + 15) / KB; }
   char* smem;
@@ -215,10 +211,10 @@ struct ChunkKernel {
   typename F::B sb[NKD], db[NKT];
   // Per-lane LDS byte offsets of the consumer's A fragments inside a tile of
   // each row size, for row tile 0 (the swizzle term depends only on the lane's
-  // row within 16, so row tile t adds 16*t*rowbytes).  [k block][half]
+  // row within 16, so row tile t adds 16*t*rowbytes).  [k block]
   // (token-by-token tiles and channel-by-token tiles have the same row size.)
   static_assert(C::R_TT == C::R_DT, "shared fragment offsets");
-  uint32_t oTD[NKD][2], oTT[NKT][2], o16;
+  uint32_t oTD[NKD], oTT[NKT], o16;
 
   __device__ __forceinline__ uint32_t stage(int chunk) const {
     return (C::STAGES == 2 ? (uint32_t)(chunk & 1) : 0u) * C::STAGE;
@@ -303,12 +299,21 @@ struct ChunkKernel {
         if constexpr (PREFILL) vq[c] = qq[c] * eg;
       }
       if constexpr (C::BF) {
-        bf16x8 h, b, qv;
+        // channels ch..ch+3 and ch+4..ch+7 go to their stored positions
 #pragma unroll
-        for (int c = 0; c < 8; ++c) { h[c] = (bf16)vkh[c]; b[c] = (bf16)kb[i][c]; qv[c] = (bf16)vq[c]; }
-        lds_st<bf16x8>(smem, st + C::S_KH + swz<C::R_TD>(row, 2 * ch), h);
-        lds_st<bf16x8>(smem, C::X_KB + swz<C::R_TD>(row, 2 * ch), b);
-        if constexpr (PREFILL) lds_st<bf16x8>(smem, st + C::S_QH + swz<C::R_TD>(row, 2 * ch), qv);
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          bf16x4 h, b, qv;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            h[c] = (bf16)vkh[4 * hlf + c];
+            b[c] = (bf16)kb[i][4 * hlf + c];
+            qv[c] = (bf16)vq[4 * hlf + c];
+          }
+          const uint32_t o = swz<C::R_TD>(row, 2 * kp(ch + 4 * hlf));
+          lds_st<bf16x4>(smem, st + C::S_KH + o, h);
+          lds_st<bf16x4>(smem, C::X_KB + o, b);
+          if constexpr (PREFILL) lds_st<bf16x4>(smem, st + C::S_QH + o, qv);
+        }
       } else {
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
@@ -330,7 +335,7 @@ struct ChunkKernel {
       if constexpr (C::BF) {
         bf16x4 t4;
         t4[0] = (bf16)kb[0][c]; t4[1] = (bf16)kb[1][c]; t4[2] = (bf16)kb[2][c]; t4[3] = (bf16)kb[3][c];
-        lds_st<bf16x4>(smem, st + C::S_KT + swz<C::R_DT>(rowc, 2 * 4 * tg), t4);
+        lds_st<bf16x4>(smem, st + C::S_KT + swz<C::R_DT>(rowc, 2 * kp(4 * tg)), t4);
       } else {
         f32x4 t4 = {kb[0][c], kb[1][c], kb[2][c], kb[3][c]};
         lds_st<f32x4>(smem, st + C::S_KT + swz<C::R_DT>(rowc, 4 * 4 * tg), t4);
@@ -392,7 +397,7 @@ struct ChunkKernel {
         N[e] = s < r ? acc[e] * bet[e] : 0.f;
         store_tt(st + C::S_L, r, s, -N[e]);
       } else {
-        store_tt(st + C::S_P, r, s, s <= r ? acc[e] : 0.f);
+        store_tt(st + C::S_P, r, kp(s), s <= r ? acc[e] : 0.f);
       }
     }
     if constexpr (MAT == 0 && I == J) {
@@ -478,20 +483,19 @@ struct ChunkKernel {
   // ------------------------------------------------------------ consumers
   __device__ __forceinline__ void init_offsets() {
     const int r16 = l & 15, kk = 4 * (l >> 4);
+    // the lane group's k positions start at stored position KB/4 * group
+    const int kg = (KB / 4) * (l >> 4);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int m = 0; m < NKD; ++m) oTD[m] = swz<C::R_TD>(r16, C::ES * (KB * m + kg));
 #pragma unroll
-      for (int m = 0; m < NKD; ++m) oTD[m][h] = swz<C::R_TD>(r16, C::ES * (KB * m + kk + 16 * h));
-#pragma unroll
-      for (int m = 0; m < NKT; ++m) oTT[m][h] = swz<C::R_TT>(r16, C::ES * (KB * m + kk + 16 * h));
-    }
+    for (int m = 0; m < NKT; ++m) oTT[m] = swz<C::R_TT>(r16, C::ES * (KB * m + kg));
     o16 = swz<C::R_TI>(r16, C::ES * kk);
   }
 
   // A fragment of row tile `t` and k block m of an LDS tile at `base`.
   template <int R>
-  __device__ __forceinline__ typename F::A ar(uint32_t base, const uint32_t (*o)[2], int t, int m) const {
-    return F::ar2(smem, base + o[m][0] + 16 * t * R, base + o[m][1] + 16 * t * R);
+  __device__ __forceinline__ typename F::A ar(uint32_t base, const uint32_t* o, int t, int m) const {
+    return lds_ld<typename F::A>(smem, base + o[m] + 16 * t * R);
   }
 
   // Lane l holds rows 16*ti + 4*(l/16) + e of its column (accumulator layout).

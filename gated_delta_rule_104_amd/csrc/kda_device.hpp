@@ -6,7 +6,10 @@
 // the B-operand layout of a 16-deep contraction (lane l supplies k = 4*(l/16)+e of
 // column l%16), so a tile produced by one product can feed the next one from
 // registers with no data movement; the A operand then reads the matching k
-// positions from LDS (see mma_ar_* below).
+// positions from LDS.  For the 32-deep bf16 product a B fragment packs two such
+// tiles, so lane group g supplies k = 4g..4g+3 and 16+4g..16+4g+3; LDS tiles
+// read as the A operand of such products store every 32-wide k block in that
+// order (kpos below), so that each A fragment is one 16-byte read.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -83,10 +86,16 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(f32x4 acc, float a, float b) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
 }
 
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 (round to nearest even), two elements per conversion
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
+}
 __device__ __forceinline__ bf16x4 pack4(f32x4 t) {
-  bf16x4 r;
-  r[0] = (bf16)t[0]; r[1] = (bf16)t[1]; r[2] = (bf16)t[2]; r[3] = (bf16)t[3];
-  return r;
+  return __builtin_bit_cast(bf16x4, (u32x2v){cvt2(t[0], t[1]), cvt2(t[2], t[3])});
 }
 __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
   bf16x8 r;
@@ -94,86 +103,15 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 lo, f32x4 hi) {
   r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
   return r;
 }
-__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
-  bf16x8 r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
+
+// Position of k inside its row for tiles stored in that order: within each
+// 32-wide block, granule g (8 elements) holds k = 4g..4g+3 then 16+4g..16+4g+3.
+__host__ __device__ constexpr int kpos(int k) {
+  return (k & ~31) | (((k & 15) >> 2) << 3) | ((k & 16) >> 2) | (k & 3);
 }
+static_assert(kpos(0) == 0 && kpos(3) == 3 && kpos(4) == 8 && kpos(16) == 4 && kpos(20) == 12 &&
+                  kpos(31) == 31 && kpos(33) == 33 && kpos(48) == 36, "kpos");
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// ---------------------------------------------------------------------------
-// Contractions whose A operand is an LDS tile of element type T (row-major,
-// swizzled rows of R bytes) and whose B operand is a set of accumulator tiles in
-// registers.  `bt[i]` holds k rows 16*i .. 16*i+15 of B for the lane's column.
-//
-// Operand fragments for the bf16 path use v_mfma_f32_16x16x32_bf16 with the k
-// positions of lane group g = l/16 taken as {4g..4g+3} from tile 2m and
-// {4g..4g+3} from tile 2m+1, i.e. k = 32m + 4g + p and 32m + 16 + 4g + p: the
-// accumulator tiles pack straight into B fragments, and A reads two 8-byte
-// pieces.  The fp32 path issues four 16x16x4 steps per 16-deep tile, step e
-// taking k = 4g + e from the lane's accumulator register e.
-
-// acc += A[r0 .. r0+15][k0 .. k0+32*nkb) * B  (bf16; bfr[m] = pack8(bt[2m], bt[2m+1]))
-template <int R>
-__device__ __forceinline__ f32x4 mma_ar_bf16(f32x4 acc, const char* smem, uint32_t base, int r0,
-                                             int k0, const bf16x8* bfr, int nkb, int l) {
-  const uint32_t row = r0 + (l & 15);
-  const uint32_t g4 = 4 * (l >> 4);
-  _Pragma("unroll") for (int m = 0; m < nkb; ++m) {
-    const uint32_t kk = k0 + 32 * m + g4;
-    bf16x4 lo = lds_ld<bf16x4>(smem, base + swz<R>(row, 2 * kk));
-    bf16x4 hi = lds_ld<bf16x4>(smem, base + swz<R>(row, 2 * (kk + 16)));
-    acc = mfma_bf16_k32(acc, cat8(lo, hi), bfr[m]);
-  }
-  return acc;
-}
-
-// acc += A[r0 .. r0+15][k0 .. k0+16*ntile) * B  (fp32; bt[i] accumulator tiles)
-template <int R>
-__device__ __forceinline__ f32x4 mma_ar_f32(f32x4 acc, const char* smem, uint32_t base, int r0,
-                                            int k0, const f32x4* bt, int ntile, int l) {
-  const uint32_t row = r0 + (l & 15);
-  const uint32_t g4 = 4 * (l >> 4);
-  _Pragma("unroll") for (int i = 0; i < ntile; ++i) {
-    const uint32_t kk = k0 + 16 * i + g4;
-    f32x4 a = lds_ld<f32x4>(smem, base + swz<R>(row, 4 * kk));
-    acc = mfma_f32_k4(acc, a[0], bt[i][0]);
-    acc = mfma_f32_k4(acc, a[1], bt[i][1]);
-    acc = mfma_f32_k4(acc, a[2], bt[i][2]);
-    acc = mfma_f32_k4(acc, a[3], bt[i][3]);
-  }
-  return acc;
-}
-
-// acc += A[ra0..+15][0..K) * B^T where B^T's rows rb0..+15 are stored like A
-// (both LDS, k contiguous within a row).  bf16: 16x16x32 steps, k = 8g..8g+7.
-template <int R>
-__device__ __forceinline__ f32x4 mma_ll_bf16(f32x4 acc, const char* smem, uint32_t abase, int ra0,
-                                             uint32_t bbase, int rb0, int K, int l) {
-  const uint32_t g8 = 8 * (l >> 4);
-  _Pragma("unroll") for (int k0 = 0; k0 < K; k0 += 32) {
-    bf16x8 a = lds_ld<bf16x8>(smem, abase + swz<R>(ra0 + (l & 15), 2 * (k0 + g8)));
-    bf16x8 b = lds_ld<bf16x8>(smem, bbase + swz<R>(rb0 + (l & 15), 2 * (k0 + g8)));
-    acc = mfma_bf16_k32(acc, a, b);
-  }
-  return acc;
-}
-
-template <int R>
-__device__ __forceinline__ f32x4 mma_ll_f32(f32x4 acc, const char* smem, uint32_t abase, int ra0,
-                                            uint32_t bbase, int rb0, int K, int l) {
-  const uint32_t g4 = 4 * (l >> 4);
-  _Pragma("unroll") for (int k0 = 0; k0 < K; k0 += 16) {
-    f32x4 a = lds_ld<f32x4>(smem, abase + swz<R>(ra0 + (l & 15), 4 * (k0 + g4)));
-    f32x4 b = lds_ld<f32x4>(smem, bbase + swz<R>(rb0 + (l & 15), 4 * (k0 + g4)));
-    acc = mfma_f32_k4(acc, a[0], b[0]);
-    acc = mfma_f32_k4(acc, a[1], b[1]);
-    acc = mfma_f32_k4(acc, a[2], b[2]);
-    acc = mfma_f32_k4(acc, a[3], b[3]);
-  }
-  return acc;
-}
 
 }  // namespace kda
