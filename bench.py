@@ -34,6 +34,29 @@ PEAK_BF16_TFLOPS = 2500.0
 CH = 64
 
 
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE on this
+# workload, each scaled by the counter's reading for a device copy of known size
+# (fetch x 2.0000, write x 1.0000).  Valid only for the kernel sources they were
+# taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
+# sources listed in kernel_sources_sha(); any change makes `traffic` null.
+TRAFFIC = {
+    "sources_sha": "3e91eacbfba1462c",
+    "segment_transfer": 1.6183e9 + 0.0367e9,
+    "segment_merge": 0.1678e9 + 0.0189e9,
+    "segment_prefill": 2.1898e9 + 0.5436e9,
+}
+
+
+def kernel_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kda_api.hip", "kda_chunk.hip", "kda_decode.hip", "kda_device.hpp", "kda_launch.hpp",
+              "kda_merge.hip"):
+        with open(os.path.join(ROOT, "gated_delta_rule_104_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def prefill_bytes(B, H, T, D):
     """Algorithmic HBM bytes of one bf16 prefill: q, k, log_alpha, v read and o
     written once (2 B each per channel), beta read once, S_T written (fp32)."""
@@ -64,6 +87,61 @@ def time_launches(fn, n):
     torch.cuda.synchronize()
     ts = [a.elapsed_time(b) for a, b in evs]
     return sum(ts) / len(ts), ts
+
+
+def segment_pass_bytes(B, H, T, D, G):
+    """Algorithmic bytes of the segment transfer pass: k, log_alpha, v and beta read
+    once; a zero-start end state and a transfer map (fp32, D x D) written per
+    segment and head."""
+    return B * H * T * (2 * 3 * D + 2) + 2 * G * B * H * D * D * 4
+
+
+def merge_bytes(B, H, D, G):
+    """Merge: read every segment's end state and map, write every start state and S_T."""
+    return G * B * H * D * D * 4 * 3 + B * H * D * D * 4
+
+
+def segment_prefill_bytes(B, H, T, D, G):
+    """Segmented prefill: q, k, log_alpha, v, beta read and o written once, a start
+    state read per segment and head, S_T written."""
+    return B * H * T * (2 * 5 * D + 2) + G * B * H * D * D * 4 + B * H * D * D * 4
+
+
+def bench_decomposition(pf, args):
+    """Per-kernel durations of the sequence-split prefill, through the three public
+    calls it is made of (same kernels and launch shapes as kda_chunk_prefill)."""
+    g = pf["g"]
+    B, H, T, D = pf["B"], pf["H"], pf["T"], pf["D"]
+    G, Tseg = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
+    if G == 1:
+        return None
+    assert G * Tseg == T, "decomposition timing needs T to be a multiple of the segment length"
+    dev = g["k"].device
+    Z = torch.empty(G, B, H, D, D, dtype=torch.float32, device=dev)
+    M = torch.empty_like(Z)
+    S_start = torch.empty_like(Z)
+    S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
+    parts = {
+        "segment_transfer": (lambda: kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], G,
+                                                          S_zero_end=Z, M=M),
+                             segment_pass_bytes(B, H, T, D, G)),
+        "segment_merge": (lambda: kda.segment_merge(Z, M, None, S_start=S_start, S_T=S_T),
+                          merge_bytes(B, H, D, G)),
+        "segment_prefill": (lambda: kda.prefill_segments(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"],
+                                                         S_start, Tseg, o=o, S_T=S_T),
+                            segment_prefill_bytes(B, H, T, D, G)),
+    }
+    for fn, _ in parts.values():
+        fn()
+    torch.cuda.synchronize()
+    res = {"G": G, "Tseg": Tseg}
+    n = max(5, args.steps)
+    for name, (fn, nbytes) in parts.items():
+        # each launch alone between events on the stream it runs on
+        ms, _ = time_launches(fn, n)
+        res[name] = {"ms": ms, "algorithmic_bytes": nbytes, "GBs": nbytes / (ms * 1e-3) / 1e9}
+    return res
 
 
 def bench_prefill(args, dev):
@@ -144,28 +222,33 @@ def bench_kcp(args, dev):
 
 
 def cpu_baseline(pf, budget_s):
-    """fp64 oracle on a bounded sample: the first `nh` heads and first `tt`
-    tokens of the same prefill inputs, sized to about `budget_s` seconds."""
+    """fp64 oracle on a bounded sample of the same prefill inputs: all heads and
+    tokens if that fits in about `budget_s` seconds, else the first `nh` heads and
+    the first `tt` tokens, sized from a short calibration run."""
     import oracle
     g = pf["g"]
     H, T = pf["H"], pf["T"]
     nthreads = oracle.max_threads()
     nh = min(H, max(1, nthreads))
-    sl = lambda x, tt: x[:, :nh, :tt].cpu()
+    sl = lambda x, nh, tt: x[:, :nh, :tt].cpu()
     tt = 1024
     t0 = time.perf_counter()
-    oracle.prefill(sl(g["q"], tt), sl(g["k"], tt), sl(g["v"], tt), sl(g["log_alpha"], tt), sl(g["beta"], tt))
-    cal = time.perf_counter() - t0
-    tt = int(min(T, max(1024, tt * budget_s / max(cal, 1e-3))))
-    tt = max(CH, tt - tt % CH)
-    args = [sl(g[n], tt) for n in ("q", "k", "v", "log_alpha", "beta")]
+    oracle.prefill(*(sl(g[n], nh, tt) for n in ("q", "k", "v", "log_alpha", "beta")))
+    per_tok = (time.perf_counter() - t0) / tt  # seconds per token over nh heads
+    if per_tok * T * (-(-H // nh)) <= budget_s:
+        nh, tt = H, T
+    else:
+        tt = int(min(T, max(1024, budget_s / max(per_tok, 1e-9))))
+        tt = max(CH, tt - tt % CH)
+    args = [sl(g[n], nh, tt) for n in ("q", "k", "v", "log_alpha", "beta")]
     t0 = time.perf_counter()
     oracle.prefill(*args, want_o=True)
     el = time.perf_counter() - t0
     token_heads_per_s = nh * tt / el
+    what = "the whole workload" if (nh, tt) == (H, T) else \
+        f"{nh} of {H} heads x first {tt} tokens of the same inputs"
     return {"value": token_heads_per_s / H, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"{nh} of {H} heads x first {tt} tokens of the same inputs ({el:.1f} s); "
-                      f"scaled to whole tokens (all {H} heads)"}
+            "sample": f"{what} ({el:.1f} s, fp64, outputs and end states); tokens/s over all {H} heads"}
 
 
 def main():
@@ -177,6 +260,9 @@ def main():
     ap.add_argument("--no-kcp", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the "
+                         "known-size reference for HBM traffic counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the KDA hot path here is single-GPU "
@@ -184,6 +270,15 @@ def main():
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_calib:
+        n = args.copy_calib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n, "launches": 3}), flush=True)
+        return
     kda.load()
 
     pf = bench_prefill(args, dev)
@@ -194,6 +289,24 @@ def main():
     gbs = nbytes / (ms * 1e-3) / 1e9
     fl_dense = prefill_flops(B, H, T, D)
     fl_tri = prefill_flops(B, H, T, D, triangle=True)
+    dec = bench_decomposition(pf, args)
+    if dec is not None:
+        names = ("segment_transfer", "segment_merge", "segment_prefill")
+        kern = {"segment_transfer": "kda_chunk_kernel<bf16,128,8,transfer>",
+                "segment_merge": "kda_merge_kernel<128>",
+                "segment_prefill": "kda_chunk_kernel<bf16,128,8,prefill>"}
+        dom = max(names, key=lambda n: dec[n]["ms"])
+        r = dec[dom]
+        traffic = TRAFFIC[dom] if kernel_sources_sha() == TRAFFIC["sources_sha"] else None
+        roofline = {"bound": "hbm", "achieved": r["GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": r["GBs"] / PEAK_HBM_GBS, "traffic": traffic, "kernel": kern[dom],
+                    "kernel_ms": r["ms"], "algorithmic_bytes": r["algorithmic_bytes"],
+                    "path_GBs": gbs, "path_frac": gbs / PEAK_HBM_GBS}
+    else:
+        dec = None
+        roofline = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "kda_chunk_kernel (single pass)",
+                    "kernel_ms": ms, "algorithmic_bytes": nbytes}
     out = {
         "metric": METRIC,
         "value": tok_s,
@@ -209,16 +322,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": "kda_prefill_b1_h32_t65536_d128_bf16", "B": B, "H": H, "T": T,
                    "dk": D, "dv": D, "chunk": CH, "S0": "zero"},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": gbs / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "kda_chunk_kernel<bf16,128,1,prefill>", "kernel_ms": ms,
-                     "algorithmic_bytes": nbytes},
+        "roofline": roofline,
         "mfma": {"dense_tile_tflops": fl_dense / (ms * 1e-3) / 1e12,
                  "dense_tile_frac": fl_dense / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                  "triangle_tflops": fl_tri / (ms * 1e-3) / 1e12,
                  "triangle_frac": fl_tri / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                  "peak_tflops": PEAK_BF16_TFLOPS},
     }
+    if dec is not None:
+        out["prefill_kernels"] = dec
     if not args.no_decode:
         out["decode"] = bench_decode(args, dev)
         torch.cuda.empty_cache()

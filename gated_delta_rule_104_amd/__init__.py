@@ -8,6 +8,8 @@ library is missing, loading fails with an error that says how to build it.
 
 Entry points (same names as the C-ABI):
     prefill(q, k, v, log_alpha, beta, S0=None)        -> (o, S_T)
+    prefill_plan(B, H, T, dk, dv, dtype)               -> (G, Tseg)
+    prefill_segments(q, k, v, log_alpha, beta, S_start, Tseg) -> (o, S_T)
     decode_step(q, k, v, log_alpha, beta, S)           -> o          (S updated in place)
     segment_transfer(k, v, log_alpha, beta, G)         -> (S_zero_end, M)
     segment_merge(S_zero_end, M, S_in=None)            -> (S_start, S_T)
@@ -50,11 +52,13 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_prefill.argtypes = [vp] * 8 + [i] * 6 + [vp, ctypes.c_size_t, vp]
     lib.kda_prefill_workspace_bytes.argtypes = [i] * 6
     lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_prefill_plan.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 2
+    lib.kda_chunk_prefill_segments.argtypes = [vp] * 8 + [i] * 7 + [vp]
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
     lib.kda_segment_transfer.argtypes = [vp] * 6 + [i] * 7 + [vp]
     lib.kda_segment_merge.argtypes = [vp] * 5 + [i] * 5 + [vp]
-    for f in (lib.kda_chunk_prefill, lib.kda_decode_step, lib.kda_segment_transfer,
-              lib.kda_segment_merge):
+    for f in (lib.kda_chunk_prefill, lib.kda_prefill_plan, lib.kda_chunk_prefill_segments,
+              lib.kda_decode_step, lib.kda_segment_transfer, lib.kda_segment_merge):
         f.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -127,6 +131,46 @@ def prefill(q, k, v, log_alpha, beta, S0=None, o=None, S_T=None,
                                   _ptr(o), _ptr(S_T), B, H, T, dk, dv, _DT[dt], _ptr(workspace),
                                   ws_bytes, _stream())
     _check(rc, "kda_chunk_prefill")
+    return o, S_T
+
+
+def prefill_plan(B: int, H: int, T: int, dk: int, dv: int, dtype: torch.dtype) -> Tuple[int, int]:
+    """(G, Tseg): the segmentation kda_chunk_prefill uses with its workspace (G == 1: single pass)."""
+    if dtype not in _DT:
+        raise KdaError(f"unsupported dtype {dtype}")
+    G, Tseg = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().kda_prefill_plan(B, H, T, dk, dv, _DT[dtype], ctypes.byref(G), ctypes.byref(Tseg)),
+           "kda_prefill_plan")
+    return G.value, Tseg.value
+
+
+def prefill_segments(q, k, v, log_alpha, beta, S_start, Tseg: int, o=None, S_T=None):
+    """Prefill of the G = ceil(T / Tseg) segments of every head, segment i from
+    S_start[i] ([G,B,H,dk,dv] fp32, or None for zero).  Returns (o, S_T of the
+    last segment)."""
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dt = k.dtype
+    if dt not in _DT:
+        raise KdaError(f"unsupported dtype {dt}")
+    if Tseg < 1 or T < 1:
+        raise KdaError(f"need T >= 1 and Tseg >= 1 (T={T}, Tseg={Tseg})")
+    G = -(-T // Tseg)
+    for name, t, shp in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                         ("log_alpha", log_alpha, (B, H, T, dk)), ("beta", beta, (B, H, T))):
+        _io(t, name, dt, shp)
+    if S_start is not None:
+        _io(S_start, "S_start", torch.float32, (G, B, H, dk, dv))
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=k.device)
+    if S_T is None:
+        S_T = torch.empty(B, H, dk, dv, dtype=torch.float32, device=k.device)
+    _io(o, "o", dt, (B, H, T, dv))
+    _io(S_T, "S_T", torch.float32, (B, H, dk, dv))
+    rc = load().kda_chunk_prefill_segments(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                           _ptr(S_start), _ptr(o), _ptr(S_T), B, H, T, Tseg, dk, dv,
+                                           _DT[dt], _stream())
+    _check(rc, "kda_chunk_prefill_segments")
     return o, S_T
 
 

@@ -144,6 +144,56 @@ kda_status check_seq_bytes(long long T, int dk, kda_dtype dt) {
   return KDA_OK;
 }
 
+// Prefill of G = ceil(T / Tseg) consecutive segments of every head, each from its
+// own start state (Sst: [G, BH, D, D] or null for zero); S_T receives the end
+// state of the last segment.
+kda_status launch_segment_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
+                                  const void* beta, const float* Sst, void* o, float* S_T,
+                                  long long BH, int T, int Tseg, int D, bool bf, hipStream_t stream,
+                                  const char* what) {
+  const int G = T > 0 ? (int)(((long long)T + Tseg - 1) / Tseg) : 1;  // T = 0: copy the start state
+  const long long nseq = BH * G;
+  const int nt = D / 16, nc = pick_nc(nseq, nt, bf);
+  kda::ChunkArgs a;
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
+  a.S0 = Sst; a.o = o; a.S_out = S_T; a.M_out = nullptr;
+  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = T; a.vsplit = nt / nc;
+  const long long nwg = nseq * a.vsplit;
+  if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (getenv("KDA_LOG"))
+    fprintf(stderr, "[libkda] %s BH=%lld T=%d Tseg=%d G=%d D=%d nc=%d vsplit=%d grid=%lld\n", what, BH,
+            T, Tseg, G, D, nc, a.vsplit, nwg);
+  const hipError_t e = kda::launch_chunk(a, bf, D, true, nc, (int)nwg, stream);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return KDA_OK;
+}
+
+// Validation shared by the prefill entry points.
+kda_status check_prefill_args(const void* q, const void* k, const void* v, const void* log_alpha,
+                              const void* beta, void* o, float* S_T, int B, int H, int T, int dk,
+                              int dv, kda_dtype dtype) {
+  if (B < 0 || H < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size B=%d H=%d T=%d", B, H, T);
+  kda_status st;
+  if ((st = check_dtype(dtype)) != KDA_OK) return st;
+  if ((st = check_dims(dk, dv)) != KDA_OK) return st;
+  if (dtype == KDA_F32 && dk != 64)
+    return fail(KDA_ERR_UNSUPPORTED, "fp32 prefill supports dk = dv = 64 only (got %d)", dk);
+  const long long BH = (long long)B * H;
+  if (BH * T * dk > kMaxElems || BH > (1LL << 30)) return fail(KDA_ERR_SHAPE, "problem too large");
+  if ((st = check_seq_bytes(T, dk, dtype)) != KDA_OK) return st;
+  if (BH == 0) return KDA_OK;
+  KDA_REQUIRE(S_T, "S_T");
+  if (T > 0) {
+    KDA_REQUIRE(q, "q");
+    KDA_REQUIRE(k, "k");
+    KDA_REQUIRE(v, "v");
+    KDA_REQUIRE(log_alpha, "log_alpha");
+    KDA_REQUIRE(beta, "beta");
+    KDA_REQUIRE(o, "o");
+  }
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,38 +219,32 @@ size_t kda_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtyp
   return plan_prefill((long long)B * H, T, dk, dtype).ws;
 }
 
-kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
-                             const void* beta, const float* S0, void* o, float* S_T, int B, int H,
-                             int T, int dk, int dv, kda_dtype dtype, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+kda_status kda_prefill_plan(int B, int H, int T, int dk, int dv, kda_dtype dtype, int* G, int* Tseg) {
+  if (!G || !Tseg) return fail(KDA_ERR_NULL, "G and Tseg must not be NULL");
   if (B < 0 || H < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size B=%d H=%d T=%d", B, H, T);
   kda_status st;
   if ((st = check_dtype(dtype)) != KDA_OK) return st;
   if ((st = check_dims(dk, dv)) != KDA_OK) return st;
-  if (dtype == KDA_F32 && dk != 64)
-    return fail(KDA_ERR_UNSUPPORTED, "fp32 prefill supports dk = dv = 64 only (got %d)", dk);
+  const PrefillPlan pl = plan_prefill((long long)B * H, T, dk, dtype);
+  *G = pl.split ? pl.P : 1;
+  *Tseg = pl.split ? pl.Tseg : T;
+  return ok();
+}
+
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* beta, const float* S0, void* o, float* S_T, int B, int H,
+                             int T, int dk, int dv, kda_dtype dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  kda_status st = check_prefill_args(q, k, v, log_alpha, beta, o, S_T, B, H, T, dk, dv, dtype);
+  if (st != KDA_OK) return st;
   const long long BH = (long long)B * H;
-  if (BH * T * dk > kMaxElems || BH > (1LL << 30)) return fail(KDA_ERR_SHAPE, "problem too large");
-  if ((st = check_seq_bytes(T, dk, dtype)) != KDA_OK) return st;
   if (BH == 0) return ok();
-  KDA_REQUIRE(S_T, "S_T");
   KDA_OPTIONAL(S0, "S0");
-  if (T > 0) {
-    KDA_REQUIRE(q, "q");
-    KDA_REQUIRE(k, "k");
-    KDA_REQUIRE(v, "v");
-    KDA_REQUIRE(log_alpha, "log_alpha");
-    KDA_REQUIRE(beta, "beta");
-    KDA_REQUIRE(o, "o");
-  }
   KDA_OPTIONAL(workspace, "workspace");
   const bool bf = dtype == KDA_BF16;
   const int D = dk;
   const PrefillPlan pl = plan_prefill(BH, T, D, dtype);
-  const bool split = pl.split && workspace && workspace_bytes >= pl.ws;
-  const bool log = getenv("KDA_LOG") != nullptr;
-  hipError_t e;
-  if (split) {
+  if (pl.split && workspace && workspace_bytes >= pl.ws) {
     const long long nseq = BH * pl.P;
     const size_t nS = (size_t)nseq * D * D;
     float* Z = static_cast<float*>(workspace);
@@ -213,40 +257,40 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
     t.BH = (int)BH; t.G = pl.P; t.Tseg = pl.Tseg; t.Ttot = T;
     const int nt2 = 2 * D / 16, nc2 = pick_nc(nseq, nt2, bf);
     t.vsplit = nt2 / nc2;
-    // 2. merge into true segment start states (S_T receives the merged end state,
-    //    then the segment prefill below overwrites it with its own)
-    // 3. prefill of every segment from its start state
-    kda::ChunkArgs a;
-    a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
-    a.S0 = Sst; a.o = o; a.S_out = S_T; a.M_out = nullptr;
-    a.BH = (int)BH; a.G = pl.P; a.Tseg = pl.Tseg; a.Ttot = T;
-    const int nt = D / 16, nc = pick_nc(nseq, nt, bf);
-    a.vsplit = nt / nc;
-    if (log)
-      fprintf(stderr, "[libkda] prefill BH=%lld T=%d D=%d split P=%d Tseg=%d: transfer nc=%d vsplit=%d, "
-              "prefill nc=%d vsplit=%d\n", BH, T, D, pl.P, pl.Tseg, nc2, t.vsplit, nc, a.vsplit);
+    if (getenv("KDA_LOG"))
+      fprintf(stderr, "[libkda] prefill split BH=%lld T=%d D=%d P=%d Tseg=%d: transfer nc=%d vsplit=%d\n",
+              BH, T, D, pl.P, pl.Tseg, nc2, t.vsplit);
+    hipError_t e;
     if ((e = kda::launch_chunk(t, bf, D, false, nc2, (int)(nseq * t.vsplit), stream)) != hipSuccess)
       return hip_fail(e, "kda_chunk_prefill segment pass");
+    // 2. merge into true segment start states (S_T receives the merged end state,
+    //    then the segment prefill below overwrites it with its own)
     if ((e = kda::launch_merge(S0, Z, M, Sst, S_T, (int)BH, pl.P, D, stream)) != hipSuccess)
       return hip_fail(e, "kda_chunk_prefill merge");
-    if ((e = kda::launch_chunk(a, bf, D, true, nc, (int)(nseq * a.vsplit), stream)) != hipSuccess)
-      return hip_fail(e, "kda_chunk_prefill segment prefill");
-    return ok();
+    // 3. prefill of every segment from its start state
+    st = launch_segment_prefill(q, k, v, log_alpha, beta, Sst, o, S_T, BH, T, pl.Tseg, D, bf, stream,
+                                "kda_chunk_prefill segment prefill");
+    return st == KDA_OK ? ok() : st;
   }
-  const int ntiles = dv / 16;
-  const int nc = pick_nc(BH, ntiles, bf);
-  kda::ChunkArgs a;
-  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
-  a.S0 = S0; a.o = o; a.S_out = S_T; a.M_out = nullptr;
-  a.BH = (int)BH; a.G = 1; a.Tseg = T; a.Ttot = T; a.vsplit = ntiles / nc;
-  const long long nwg = BH * a.vsplit;
-  if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
-  if (log)
-    fprintf(stderr, "[libkda] prefill BH=%lld T=%d D=%d nc=%d vsplit=%d grid=%lld\n", BH, T, dk, nc,
-            a.vsplit, nwg);
-  if ((e = kda::launch_chunk(a, bf, dk, true, nc, (int)nwg, stream)) != hipSuccess)
-    return hip_fail(e, "kda_chunk_prefill launch");
-  return ok();
+  st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, o, S_T, BH, T, T > 0 ? T : 1, D, bf,
+                              stream, "kda_chunk_prefill");
+  return st == KDA_OK ? ok() : st;
+}
+
+kda_status kda_chunk_prefill_segments(const void* q, const void* k, const void* v,
+                                      const void* log_alpha, const void* beta, const float* S_start,
+                                      void* o, float* S_T, int B, int H, int T, int Tseg, int dk,
+                                      int dv, kda_dtype dtype, hipStream_t stream) {
+  if (Tseg < 1) return fail(KDA_ERR_SHAPE, "Tseg must be >= 1 (got %d)", Tseg);
+  kda_status st = check_prefill_args(q, k, v, log_alpha, beta, o, S_T, B, H, T, dk, dv, dtype);
+  if (st != KDA_OK) return st;
+  const long long BH = (long long)B * H;
+  if (BH == 0) return ok();
+  KDA_OPTIONAL(S_start, "S_start");
+  if (T == 0) return fail(KDA_ERR_SHAPE, "T must be >= 1 for a segmented prefill");
+  st = launch_segment_prefill(q, k, v, log_alpha, beta, S_start, o, S_T, BH, T, Tseg, dk,
+                              dtype == KDA_BF16, stream, "kda_chunk_prefill_segments");
+  return st == KDA_OK ? ok() : st;
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
   KDA_OK = 0,
@@ -85,6 +85,31 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                              const void* beta, const float* S0, void* o, float* S_T, int B, int H,
                              int T, int dk, int dv, kda_dtype dtype, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The segmentation kda_chunk_prefill would use for this shape when given
+ * kda_prefill_workspace_bytes() of workspace: *G segments of *Tseg tokens (the
+ * last one possibly shorter); *G == 1 means the single-pass path.  Writes
+ * nothing else and launches nothing.
+ */
+kda_status kda_prefill_plan(int B, int H, int T, int dk, int dv, kda_dtype dtype, int* G, int* Tseg);
+
+/*
+ * Last step of the context-parallel decomposition (same section): every
+ * segment, once its true start state is known, runs its own prefill.  Here all
+ * G = ceil(T / Tseg) segments of all B*H heads run in one call, segment i
+ * covering tokens [i*Tseg, min((i+1)*Tseg, T)) and starting from S_start[i].
+ *   q, k, v, log_alpha, beta, o : as for kda_chunk_prefill (T >= 1 tokens)
+ *   S_start : [G, B, H, dk, dv] fp32 start states, or NULL for zero
+ *   S_T     : [B, H, dk, dv] fp32, written with the end state of the last segment
+ * With S_start from kda_segment_transfer + kda_segment_merge this reproduces
+ * kda_chunk_prefill over the whole sequence.  Tseg >= 1; S_T must not alias
+ * S_start.
+ */
+kda_status kda_chunk_prefill_segments(const void* q, const void* k, const void* v,
+                                      const void* log_alpha, const void* beta, const float* S_start,
+                                      void* o, float* S_T, int B, int H, int T, int Tseg, int dk,
+                                      int dv, kda_dtype dtype, hipStream_t stream);
 
 /*
  * One decode step for N*H independent heads: applies the recurrence for one

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     for st in range(6):
         assert lib.kda_status_string(st)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -89,6 +89,34 @@ def test_prefill_workspace_query(lib):
     assert ws(1, 32, 65536, 128, 64, BF16) == 0
     n = ws(1, 32, 65536, 128, 128, BF16)
     assert n > 0 and n % (3 * 32 * 128 * 128 * 4) == 0
+
+
+def test_prefill_plan(lib):
+    """The plan matches the workspace query: split exactly when workspace is asked for."""
+    G, Ts = ctypes.c_int(0), ctypes.c_int(0)
+    plan = lambda *a: lib.kda_prefill_plan(*a, ctypes.byref(G), ctypes.byref(Ts))
+    ws = lib.kda_prefill_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    assert plan(1, 32, 65536, 128, 128, BF16) == OK
+    assert G.value > 1 and Ts.value % 64 == 0 and (G.value - 1) * Ts.value < 65536 <= G.value * Ts.value
+    assert ws(1, 32, 65536, 128, 128, BF16) == 3 * G.value * 32 * 128 * 128 * 4
+    assert plan(64, 32, 65536, 128, 128, BF16) == OK and (G.value, Ts.value) == (1, 65536)
+    assert plan(1, 32, 65536, 128, 128, F32) == OK and G.value == 1
+    assert plan(1, 32, 100, 96, 96, BF16) == ERR_UNSUPPORTED
+    assert lib.kda_prefill_plan(1, 1, 64, 64, 64, BF16, None, ctypes.byref(Ts)) == ERR_NULL
+
+
+def test_prefill_segments_validation(lib):
+    f = lib.kda_chunk_prefill_segments
+    args = lambda **kw: [*P(FAKE, FAKE, FAKE, FAKE, FAKE, kw.get("S", None), FAKE, kw.get("ST", FAKE)),
+                         1, 2, kw.get("T", 256), kw.get("Tseg", 64), kw.get("dk", 128), 128,
+                         kw.get("dt", BF16), None]
+    assert f(*args(Tseg=0)) == ERR_SHAPE
+    assert f(*args(T=0)) == ERR_SHAPE
+    assert f(*args(ST=None)) == ERR_NULL
+    assert f(*args(S=FAKE + 4)) == ERR_ALIGN
+    assert f(*args(dk=64)) == ERR_SHAPE
+    assert f(*args(dt=F32)) == ERR_UNSUPPORTED
 
 
 def test_decode_validation(lib):
