@@ -61,13 +61,18 @@ struct ChunkCfg {
   static constexpr int NW = NC + NP;
   static constexpr int THREADS = 64 * NW;
   static constexpr int R_TD = D * ES;      // [CH][D] rows (time-major)
+  // [CH][D] tiles are stored as four 16-row blocks, each 16 bytes further along
+  // the banks than the previous one, so that the producer's stores (rows 4 apart)
+  // do not pile onto the same banks.
+  static constexpr int TD_TILE = 16 * R_TD + 16;
+  static constexpr int TD_SZ = 4 * TD_TILE;
   static constexpr int R_DT = CH * ES;     // [D][CH] rows (channel-major)
   static constexpr int R_TT = CH * ES;     // [CH][CH] rows
   static constexpr int R_TI = 16 * ES;     // [16][16] rows
   // stage: everything the chain of one chunk reads
   static constexpr uint32_t S_KH = 0;                                   // Kh   [CH][D]
-  static constexpr uint32_t S_QH = S_KH + CH * R_TD;                    // Qh   [CH][D]
-  static constexpr uint32_t S_KT = S_QH + (PREFILL ? CH * R_TD : 0);    // Kb^T [D][CH]
+  static constexpr uint32_t S_QH = S_KH + TD_SZ;                        // Qh   [CH][D]
+  static constexpr uint32_t S_KT = S_QH + (PREFILL ? TD_SZ : 0);        // Kb^T [D][CH]
   static constexpr uint32_t S_L = S_KT + D * R_DT;                      // -L   [CH][CH]
   static constexpr uint32_t S_P = S_L + CH * R_TT;                      // P    [CH][CH]
   static constexpr uint32_t S_TI = S_P + (PREFILL ? CH * R_TT : 0);     // T_ii [4][16][16]
@@ -76,7 +81,7 @@ struct ChunkCfg {
   static constexpr uint32_t STAGE = S_BETA + CH * 4;
   // producer scratch: Kb time-major, the B operand of the score products
   static constexpr uint32_t X_KB = STAGES * STAGE;
-  static constexpr uint32_t LDS = X_KB + CH * R_TD;
+  static constexpr uint32_t LDS = X_KB + TD_SZ;
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(LDS % 16 == 0 && STAGE % 16 == 0, "LDS alignment");
 };
@@ -158,10 +163,6 @@ template <> struct Frag<true> {
   typedef bf16x8 B;
   typedef bf16x4 A16;
   static constexpr int KB = 32;
-  template <int R>
-  __device__ __forceinline__ static A ll(const char* smem, uint32_t base, int row, int k0, int ln) {
-    return lds_ld<bf16x8>(smem, base + swz<R>(row, 2 * (k0 + 8 * (ln >> 4))));
-  }
   __device__ __forceinline__ static B bfrag(const f32x4* t, int m) { return pack8(t[2 * m], t[2 * m + 1]); }
   __device__ __forceinline__ static f32x4 mma(f32x4 acc, A a, B b) { return mfma_bf16_k32(acc, a, b); }
   __device__ __forceinline__ static f32x4 mma16(f32x4 acc, A16 a, f32x4 b) {
@@ -173,10 +174,6 @@ template <> struct Frag<false> {
   typedef f32x4 B;
   typedef f32x4 A16;
   static constexpr int KB = 16;
-  template <int R>
-  __device__ __forceinline__ static A ll(const char* smem, uint32_t base, int row, int k0, int ln) {
-    return lds_ld<f32x4>(smem, base + swz<R>(row, 4 * (k0 + 4 * (ln >> 4))));
-  }
   __device__ __forceinline__ static B bfrag(const f32x4* t, int m) { return t[m]; }
   __device__ __forceinline__ static f32x4 mma(f32x4 acc, A a, B b) {
     acc = mfma_f32_k4(acc, a[0], b[0]);
@@ -197,6 +194,10 @@ struct ChunkKernel {
   static constexpr int NKT = CH / KB;   // k blocks over the tokens of a chunk
   // stored position of k in tiles read as "ar" A operands
   static constexpr int kp(int k) { return C::BF ? kpos(k) : k; }
+  // byte offset of (row, byte) in a [CH][D] tile
+  __device__ __forceinline__ static uint32_t td(int row, int byte) {
+    return (uint32_t)(row >> 4) * C::TD_TILE + swz<C::R_TD>(row & 15, byte);
+  }
   // last k block a lower-triangular row tile ti touches
   static constexpr int tri(int ti) { return (16 * ti + 15) / KB; }
   char* smem;
@@ -309,7 +310,7 @@ struct ChunkKernel {
             b[c] = (bf16)kb[i][4 * hlf + c];
             qv[c] = (bf16)vq[4 * hlf + c];
           }
-          const uint32_t o = swz<C::R_TD>(row, 2 * kp(ch + 4 * hlf));
+          const uint32_t o = td(row, 2 * kp(ch + 4 * hlf));
           lds_st<bf16x4>(smem, st + C::S_KH + o, h);
           lds_st<bf16x4>(smem, C::X_KB + o, b);
           if constexpr (PREFILL) lds_st<bf16x4>(smem, st + C::S_QH + o, qv);
@@ -319,11 +320,11 @@ struct ChunkKernel {
         for (int hlf = 0; hlf < 2; ++hlf) {
           f32x4 h = {vkh[4 * hlf], vkh[4 * hlf + 1], vkh[4 * hlf + 2], vkh[4 * hlf + 3]};
           f32x4 b = {kb[i][4 * hlf], kb[i][4 * hlf + 1], kb[i][4 * hlf + 2], kb[i][4 * hlf + 3]};
-          lds_st<f32x4>(smem, st + C::S_KH + swz<C::R_TD>(row, 4 * (ch + 4 * hlf)), h);
-          lds_st<f32x4>(smem, C::X_KB + swz<C::R_TD>(row, 4 * (ch + 4 * hlf)), b);
+          lds_st<f32x4>(smem, st + C::S_KH + td(row, 4 * (ch + 4 * hlf)), h);
+          lds_st<f32x4>(smem, C::X_KB + td(row, 4 * (ch + 4 * hlf)), b);
           if constexpr (PREFILL) {
             f32x4 qv = {vq[4 * hlf], vq[4 * hlf + 1], vq[4 * hlf + 2], vq[4 * hlf + 3]};
-            lds_st<f32x4>(smem, st + C::S_QH + swz<C::R_TD>(row, 4 * (ch + 4 * hlf)), qv);
+            lds_st<f32x4>(smem, st + C::S_QH + td(row, 4 * (ch + 4 * hlf)), qv);
           }
         }
       }
@@ -354,14 +355,16 @@ struct ChunkKernel {
     }
   }
 
+  template <bool NARROW>
   __device__ __forceinline__ void store_tt(uint32_t base, int r, int s, float x) {
-    lds_st<T>(smem, base + swz<C::R_TT>(r, C::ES * s), from_f32<T>(x));
+    lds_st<T>(smem, base + swz<C::R_TT, NARROW>(r, C::ES * s), from_f32<T>(x));
   }
 
+  // 16-deep A fragment of an LDS tile read with 8-byte (bf16) fragments
   template <int RR>
   __device__ __forceinline__ A16 frag16(uint32_t base, int row, int k0, int ln) const {
-    if constexpr (C::BF) return lds_ld<bf16x4>(smem, base + swz<RR>(row, 2 * (k0 + 4 * (ln >> 4))));
-    else return lds_ld<f32x4>(smem, base + swz<RR>(row, 4 * (k0 + 4 * (ln >> 4))));
+    if constexpr (C::BF) return lds_ld<bf16x4>(smem, base + swz<RR, true>(row, 2 * (k0 + 4 * (ln >> 4))));
+    else return lds_ld<f32x4>(smem, base + swz<RR, true>(row, 4 * (k0 + 4 * (ln >> 4))));
   }
 
   // Phase 2, one tile task: tile (I, J), J <= I, of -L (MAT 0) or of P (MAT 1).
@@ -376,8 +379,10 @@ struct ChunkKernel {
     typename F::A fa[NKD], fb[NKD];
 #pragma unroll
     for (int m = 0; m < NKD; ++m) {
-      fa[m] = F::template ll<C::R_TD>(smem, abase, 16 * I + s0, KB * m, ln);
-      fb[m] = F::template ll<C::R_TD>(smem, C::X_KB, 16 * J + s0, KB * m, ln);
+      // both operands read the same stored k positions (any consistent order works)
+      const int kb = C::ES * (KB * m + (KB / 4) * (ln >> 4));
+      fa[m] = lds_ld<typename F::A>(smem, abase + td(16 * I + s0, kb));
+      fb[m] = lds_ld<typename F::A>(smem, C::X_KB + td(16 * J + s0, kb));
     }
     float bet[4];
     if (MAT == 0) {
@@ -395,9 +400,9 @@ struct ChunkKernel {
       const int r = 16 * I + g4 + e;
       if (MAT == 0) {
         N[e] = s < r ? acc[e] * bet[e] : 0.f;
-        store_tt(st + C::S_L, r, s, -N[e]);
+        store_tt<true>(st + C::S_L, r, s, -N[e]);
       } else {
-        store_tt(st + C::S_P, r, kp(s), s <= r ? acc[e] : 0.f);
+        store_tt<false>(st + C::S_P, r, kp(s), s <= r ? acc[e] : 0.f);
       }
     }
     if constexpr (MAT == 0 && I == J) {
@@ -415,7 +420,7 @@ struct ChunkKernel {
       const uint32_t ti = st + C::S_TI + I * 16 * C::R_TI;
       auto put = [&](const f32x4& t) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lds_st<T>(smem, ti + swz<C::R_TI>(g4 + e, C::ES * s0), from_f32<T>(t[e]));
+        for (int e = 0; e < 4; ++e) lds_st<T>(smem, ti + swz<C::R_TI, true>(g4 + e, C::ES * s0), from_f32<T>(t[e]));
       };
       wave_lds_fence();  // the -L_II tile written above is the A operand of (-N)(-N)
       A16 an = frag16<C::R_TT>(st + C::S_L, 16 * I + s0, 16 * I, ln);
@@ -489,13 +494,15 @@ struct ChunkKernel {
     for (int m = 0; m < NKD; ++m) oTD[m] = swz<C::R_TD>(r16, C::ES * (KB * m + kg));
 #pragma unroll
     for (int m = 0; m < NKT; ++m) oTT[m] = swz<C::R_TT>(r16, C::ES * (KB * m + kg));
-    o16 = swz<C::R_TI>(r16, C::ES * kk);
+    o16 = swz<C::R_TI, true>(r16, C::ES * kk);
   }
 
   // A fragment of row tile `t` and k block m of an LDS tile at `base`.
-  template <int R>
+  // (row tile t of a [CH][D] tile starts TD_TILE bytes after tile t-1; other
+  // tiles are plain, 16 * R bytes per row tile)
+  template <int TSTRIDE>
   __device__ __forceinline__ typename F::A ar(uint32_t base, const uint32_t* o, int t, int m) const {
-    return lds_ld<typename F::A>(smem, base + o[m] + 16 * t * R);
+    return lds_ld<typename F::A>(smem, base + o[m] + t * TSTRIDE);
   }
 
   // Lane l holds rows 16*ti + 4*(l/16) + e of its column (accumulator layout).
@@ -524,7 +531,7 @@ struct ChunkKernel {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int m = 0; m < NKD; ++m) fk[h][m] = ar<C::R_TD>(st + C::S_KH, oTD, H0 + h, m);
+      for (int m = 0; m < NKD; ++m) fk[h][m] = ar<C::TD_TILE>(st + C::S_KH, oTD, H0 + h, m);
     __builtin_amdgcn_sched_barrier(0);
     X[H0] = zero4();
     X[H0 + 1] = zero4();
@@ -558,7 +565,7 @@ struct ChunkKernel {
 #pragma unroll
       for (int j = 0; j < ti; ++j)
         fl[ti][j] = lds_ld<A16>(smem, st + C::S_L + 16 * ti * C::R_TT +
-                                          swz<C::R_TT>(l & 15, C::ES * (16 * j + kk)));
+                                          swz<C::R_TT, true>(l & 15, C::ES * (16 * j + kk)));
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 Dl[4];
@@ -583,9 +590,9 @@ struct ChunkKernel {
     for (int h = 0; h < 2; ++h) {
       const int ti = H0 + h;
 #pragma unroll
-      for (int m = 0; m < NKD; ++m) fq[h][m] = ar<C::R_TD>(st + C::S_QH, oTD, ti, m);
+      for (int m = 0; m < NKD; ++m) fq[h][m] = ar<C::TD_TILE>(st + C::S_QH, oTD, ti, m);
 #pragma unroll
-      for (int m = 0; m <= tri(ti); ++m) fp[h][m] = ar<C::R_TT>(st + C::S_P, oTT, ti, m);
+      for (int m = 0; m <= tri(ti); ++m) fp[h][m] = ar<16 * C::R_TT>(st + C::S_P, oTT, ti, m);
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 O[2] = {zero4(), zero4()};
@@ -629,7 +636,7 @@ struct ChunkKernel {
 #pragma unroll
     for (int ci = 0; ci < D / 16; ++ci) {
 #pragma unroll
-      for (int m = 0; m < NKT; ++m) fk[ci][m] = ar<C::R_DT>(st + C::S_KT, oTT, ci, m);
+      for (int m = 0; m < NKT; ++m) fk[ci][m] = ar<16 * C::R_DT>(st + C::S_KT, oTT, ci, m);
       gm[ci] = lds_ld<f32x4>(smem, st + C::S_GM + 4 * (16 * ci + kk));
     }
     __builtin_amdgcn_sched_barrier(0);

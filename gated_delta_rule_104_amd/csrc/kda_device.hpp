@@ -55,14 +55,24 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 
 // ---------------------------------------------------------------------------
-// LDS tiles: rows of R bytes (R a power of two >= 16), 16-byte granules XOR-
-// swizzled by the row index so that 16 lanes reading the same column range of
-// 16 consecutive rows hit distinct banks.
-template <int R>
+// LDS tiles: rows of R bytes (R a power of two >= 16) made of 16-byte granules.
+// A granule's position in its row is XORed with a function of the row index so
+// that 16 lanes reading one logical granule of 16 consecutive rows (the MFMA
+// operand pattern) spread over the banks.  The function depends only on
+// row % 16, so row tile t of a tile sits at a fixed offset from tile 0.  The
+// default suits 16-byte fragment reads; NARROW suits tiles read with 8-byte
+// fragments (chosen by measuring gfx950's LDS bank-conflict counter on these
+// access patterns):
+//   default : row & (min(G, 16) - 1)                       (G = R / 16)
+//   NARROW  : G = 8: (row & 7) ^ ((row >> 3) & 1);  G = 2: ((row >> 2) ^ (row >> 3)) & 1
+template <int R, bool NARROW = false>
 __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t byte) {
   constexpr uint32_t G = R / 16;
-  constexpr uint32_t MASK = (G < 16 ? G : 16) - 1;
-  return row * R + ((((byte >> 4) ^ (row & MASK)) << 4) | (byte & 15u));
+  uint32_t f;
+  if constexpr (NARROW && G == 8) f = (row & 7u) ^ ((row >> 3) & 1u);
+  else if constexpr (NARROW && G == 2) f = ((row >> 2) ^ (row >> 3)) & 1u;
+  else f = row & ((G < 16 ? G : 16) - 1);
+  return row * R + ((((byte >> 4) ^ f) << 4) | (byte & 15u));
 }
 
 template <typename V>
