@@ -54,20 +54,22 @@ int cu_count() {
   return cache[dev];
 }
 
-// Consumer waves per workgroup: the largest of 8, 4, 2, 1 that still gives at
-// least one workgroup per compute unit (or 1).  fp32 variants keep more live
-// state per wave and are capped at 2.  KDA_NC overrides for tuning.
+// Consumer waves per workgroup (each owns chunk_tiles_per_wave(bf16) 16-column
+// state tiles): the largest of 4, 2, 1 (fp32: 2, 1) that divides the column
+// tiles and still gives at least one workgroup per compute unit (or 1).
+// KDA_NC overrides for tuning and tests.
 int pick_nc(long long nseq, int ncol_tiles, bool bf16_io) {
-  const int ncmax = bf16_io ? 8 : 2;
+  const int ncmax = bf16_io ? 4 : 2;
+  const int tw = kda::chunk_tiles_per_wave(bf16_io);
   const char* env = getenv("KDA_NC");
   if (env) {
     const int v = atoi(env);
-    if ((v == 1 || v == 2 || v == 4 || v == 8) && v <= ncmax && ncol_tiles % v == 0) return v;
+    if ((v == 1 || v == 2 || v == 4) && v <= ncmax && ncol_tiles % (v * tw) == 0) return v;
   }
   const long long cus = cu_count();
   for (int nc = ncmax; nc >= 1; nc >>= 1) {
-    if (ncol_tiles % nc) continue;
-    if (nseq * (ncol_tiles / nc) >= cus) return nc;
+    if (ncol_tiles % (nc * tw)) continue;
+    if (nseq * (ncol_tiles / (nc * tw)) >= cus) return nc;
   }
   return 1;
 }
@@ -157,7 +159,7 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
   kda::ChunkArgs a;
   a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
   a.S0 = Sst; a.o = o; a.S_out = S_T; a.M_out = nullptr;
-  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = T; a.vsplit = nt / nc;
+  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = T; a.vsplit = nt / (nc * kda::chunk_tiles_per_wave(bf));
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (getenv("KDA_LOG"))
@@ -256,7 +258,7 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
     t.S0 = nullptr; t.o = nullptr; t.S_out = Z; t.M_out = M;
     t.BH = (int)BH; t.G = pl.P; t.Tseg = pl.Tseg; t.Ttot = T;
     const int nt2 = 2 * D / 16, nc2 = pick_nc(nseq, nt2, bf);
-    t.vsplit = nt2 / nc2;
+    t.vsplit = nt2 / (nc2 * kda::chunk_tiles_per_wave(bf));
     if (getenv("KDA_LOG"))
       fprintf(stderr, "[libkda] prefill split BH=%lld T=%d D=%d P=%d Tseg=%d: transfer nc=%d vsplit=%d\n",
               BH, T, D, pl.P, pl.Tseg, nc2, t.vsplit);
@@ -342,7 +344,8 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
   kda::ChunkArgs a;
   a.q = nullptr; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
   a.S0 = nullptr; a.o = nullptr; a.S_out = S_zero_end; a.M_out = M;
-  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = G * Tseg; a.vsplit = ntiles / nc;
+  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = G * Tseg;
+  a.vsplit = ntiles / (nc * kda::chunk_tiles_per_wave(dtype == KDA_BF16));
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (getenv("KDA_LOG"))

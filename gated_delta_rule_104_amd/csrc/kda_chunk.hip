@@ -57,6 +57,7 @@ struct ChunkCfg {
   static constexpr int ES = sizeof(T);
   static constexpr int STAGES = BF ? 2 : 1;
   static constexpr int LAG = STAGES - 1;
+  static constexpr int NCT = BF ? 2 : 1;   // 16-column state tiles per consumer wave
   static constexpr int NP = D / 32;
   static constexpr int NW = NC + NP;
   static constexpr int THREADS = 64 * NW;
@@ -205,11 +206,12 @@ struct ChunkKernel {
   rsrc_t rq, rk, rv, rla, rbeta, ro;
   int Tlen, nch;
   int wave, l;
-  // consumer
-  int col;          // global column of this lane's state slice
-  bool isv;         // column reads v (value column) rather than being a map column
-  f32x4 S[D / 16];
-  typename F::B sb[NKD], db[NKT];
+  // consumer: NCT adjacent 16-column tiles of the state, sharing every A fragment
+  static constexpr int NCT = C::NCT;
+  int colb;         // global column of this lane in tile 0 (tile j: colb + 16 j)
+  bool isv;         // columns read v (value columns) rather than being map columns
+  f32x4 S[NCT][D / 16];
+  typename F::B sb[NCT][NKD], db[NCT][NKT];
   // Per-lane LDS byte offsets of the consumer's A fragments inside a tile of
   // each row size, for row tile 0 (the swizzle term depends only on the lane's
   // row within 16, so row tile t adds 16*t*rowbytes).  [k block]
@@ -506,56 +508,64 @@ struct ChunkKernel {
   }
 
   // Lane l holds rows 16*ti + 4*(l/16) + e of its column (accumulator layout).
-  __device__ __forceinline__ void load_v(VRegs<T>& vr, int chunk) const {
+  __device__ __forceinline__ void load_v(VRegs<T>* vr, int chunk) const {
     const int ln = fresh_lane(l);
     const int g4 = 4 * (ln >> 4);
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
+    for (int j = 0; j < NCT; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // map columns (segment pass) read v = 0: their offset is past any buffer end
-        const uint32_t off = ((uint32_t)((chunk * CH + 16 * ti + g4 + e) * D + col) * C::ES) |
-                             (isv ? 0u : 0x80000000u);
-        if constexpr (C::BF) vr.set(4 * ti + e, __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0));
-        else vr.set(4 * ti + e, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0));
+      for (int ti = 0; ti < 4; ++ti) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // map columns (segment pass) read v = 0: their offset is past any buffer end
+          const uint32_t off = ((uint32_t)((chunk * CH + 16 * ti + g4 + e) * D + colb + 16 * j) * C::ES) |
+                               (isv ? 0u : 0x80000000u);
+          if constexpr (C::BF) vr[j].set(4 * ti + e, __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0));
+          else vr[j].set(4 * ti + e, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0));
+        }
       }
-    }
   }
 
   __device__ __forceinline__ float vval(const VRegs<T>& vr, int i) const { return vr.get(i); }
 
   // X_t = b_t (v_t - (Kh S)_t) for row tiles H0, H0+1 (fragments fetched first).
   template <int H0>
-  __device__ __forceinline__ void c1_half(const VRegs<T>& vr, uint32_t st, f32x4* X) {
+  __device__ __forceinline__ void c1_half(const VRegs<T>* vr, uint32_t st, f32x4 (*X)[4]) {
     typename F::A fk[2][NKD];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int m = 0; m < NKD; ++m) fk[h][m] = ar<C::TD_TILE>(st + C::S_KH, oTD, H0 + h, m);
     __builtin_amdgcn_sched_barrier(0);
-    X[H0] = zero4();
-    X[H0 + 1] = zero4();
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) X[j][H0] = X[j][H0 + 1] = zero4();
 #pragma unroll
     for (int m = 0; m < NKD; ++m)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) X[H0 + h] = F::mma(X[H0 + h], fk[h][m], sb[m]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) X[j][H0 + h] = F::mma(X[j][H0 + h], fk[h][m], sb[j][m]);
     const int kk = 4 * (l >> 4);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const f32x4 bet = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * (H0 + h) + kk));
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        X[H0 + h][e] = bet[e] * (vval(vr, 4 * (H0 + h) + e) - X[H0 + h][e]);
+      for (int j = 0; j < NCT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          X[j][H0 + h][e] = bet[e] * (vval(vr[j], 4 * (H0 + h) + e) - X[j][H0 + h][e]);
     }
   }
 
   // Delta from (I + L) Delta = diag(b) (V - Kh S) by 16-row blocks:
   // Delta_i = T_ii (X_i + sum_{j<i} (-L_ij) Delta_j).
-  __device__ __forceinline__ void c1(const VRegs<T>& vr, uint32_t st) {
+  __device__ __forceinline__ void c1(const VRegs<T>* vr, uint32_t st) {
     const int kk = 4 * (l >> 4);
 #pragma unroll
-    for (int m = 0; m < NKD; ++m) sb[m] = F::bfrag(S, m);
-    f32x4 X[4];
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int m = 0; m < NKD; ++m) sb[j][m] = F::bfrag(S[j], m);
+    f32x4 X[NCT][4];
     c1_half<0>(vr, st, X);
     c1_half<2>(vr, st, X);
     A16 ft[4], fl[4][4];
@@ -563,21 +573,26 @@ struct ChunkKernel {
     for (int ti = 0; ti < 4; ++ti) {
       ft[ti] = lds_ld<A16>(smem, st + C::S_TI + ti * 16 * C::R_TI + o16);
 #pragma unroll
-      for (int j = 0; j < ti; ++j)
-        fl[ti][j] = lds_ld<A16>(smem, st + C::S_L + 16 * ti * C::R_TT +
-                                          swz<C::R_TT, true>(l & 15, C::ES * (16 * j + kk)));
+      for (int jj = 0; jj < ti; ++jj)
+        fl[ti][jj] = lds_ld<A16>(smem, st + C::S_L + 16 * ti * C::R_TT +
+                                           swz<C::R_TT, true>(l & 15, C::ES * (16 * jj + kk)));
     }
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 Dl[4];
+    f32x4 Dl[NCT][4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
-      f32x4 rr = X[ti];
 #pragma unroll
-      for (int j = 0; j < ti; ++j) rr = F::mma16(rr, fl[ti][j], Dl[j]);  // fl holds -L
-      Dl[ti] = F::mma16(zero4(), ft[ti], rr);
+      for (int j = 0; j < NCT; ++j) {
+        f32x4 rr = X[j][ti];
+#pragma unroll
+        for (int jj = 0; jj < ti; ++jj) rr = F::mma16(rr, fl[ti][jj], Dl[j][jj]);  // fl holds -L
+        Dl[j][ti] = F::mma16(zero4(), ft[ti], rr);
+      }
     }
 #pragma unroll
-    for (int m = 0; m < NKT; ++m) db[m] = F::bfrag(Dl, m);
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int m = 0; m < NKT; ++m) db[j][m] = F::bfrag(Dl[j], m);
   }
 
   // O = Qh S + P Delta, stored (rows past the sequence end are dropped).  Two
@@ -595,30 +610,38 @@ struct ChunkKernel {
       for (int m = 0; m <= tri(ti); ++m) fp[h][m] = ar<16 * C::R_TT>(st + C::S_P, oTT, ti, m);
     }
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 O[2] = {zero4(), zero4()};
+    f32x4 O[NCT][2];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) O[j][0] = O[j][1] = zero4();
 #pragma unroll
     for (int m = 0; m < NKD; ++m)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) O[h] = F::mma(O[h], fq[h][m], sb[m]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) O[j][h] = F::mma(O[j][h], fq[h][m], sb[j][m]);
 #pragma unroll
     for (int m = 0; m < NKT; ++m)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        if (m <= tri(H0 + h)) O[h] = F::mma(O[h], fp[h][m], db[m]);
-    const uint32_t ob = (uint32_t)((chunk * CH + kk) * D + col) * C::ES;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+        for (int j = 0; j < NCT; ++j)
+          if (m <= tri(H0 + h)) O[j][h] = F::mma(O[j][h], fp[h][m], db[j][m]);
+    const uint32_t ob = (uint32_t)((chunk * CH + kk) * D + colb) * C::ES;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t off = ob + (uint32_t)((16 * (H0 + h) + e) * D * C::ES);
-        if constexpr (C::BF) {
-          const bf16 hv = (bf16)O[h][e];
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ro, off, 0, 0);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[h][e]), ro, off, 0, 0);
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off = ob + (uint32_t)(((16 * (H0 + h) + e) * D + 16 * j) * C::ES);
+          if constexpr (C::BF) {
+            const bf16 hv = (bf16)O[j][h][e];
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ro, off, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[j][h][e]), ro, off, 0, 0);
+          }
         }
       }
-    }
   }
 
   __device__ __forceinline__ void c2(uint32_t st, int chunk) {
@@ -628,27 +651,38 @@ struct ChunkKernel {
     }
   }
 
-  // S = Diag(Gam) (S + Kb^T Delta).
-  __device__ __forceinline__ void c3(uint32_t st) {
+  // S = Diag(Gam) (S + Kb^T Delta) for state row tiles C0 .. C0 + D/32 - 1.
+  template <int C0>
+  __device__ __forceinline__ void c3_half(uint32_t st) {
+    constexpr int NH = D / 32;
     const int kk = 4 * (l >> 4);
-    typename F::A fk[D / 16][NKT];
-    f32x4 gm[D / 16];
+    typename F::A fk[NH][NKT];
+    f32x4 gm[NH];
 #pragma unroll
-    for (int ci = 0; ci < D / 16; ++ci) {
+    for (int ci = 0; ci < NH; ++ci) {
 #pragma unroll
-      for (int m = 0; m < NKT; ++m) fk[ci][m] = ar<16 * C::R_DT>(st + C::S_KT, oTT, ci, m);
-      gm[ci] = lds_ld<f32x4>(smem, st + C::S_GM + 4 * (16 * ci + kk));
+      for (int m = 0; m < NKT; ++m) fk[ci][m] = ar<16 * C::R_DT>(st + C::S_KT, oTT, C0 + ci, m);
+      gm[ci] = lds_ld<f32x4>(smem, st + C::S_GM + 4 * (16 * (C0 + ci) + kk));
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < NKT; ++m)
 #pragma unroll
-      for (int ci = 0; ci < D / 16; ++ci) S[ci] = F::mma(S[ci], fk[ci][m], db[m]);
+      for (int ci = 0; ci < NH; ++ci)
 #pragma unroll
-    for (int ci = 0; ci < D / 16; ++ci) S[ci] = S[ci] * gm[ci];
+        for (int j = 0; j < NCT; ++j) S[j][C0 + ci] = F::mma(S[j][C0 + ci], fk[ci][m], db[j][m]);
+#pragma unroll
+    for (int ci = 0; ci < NH; ++ci)
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) S[j][C0 + ci] = S[j][C0 + ci] * gm[ci];
   }
 
-  __device__ __forceinline__ void chain(VRegs<T>& vr, int cc) {
+  __device__ __forceinline__ void c3(uint32_t st) {
+    c3_half<0>(st);
+    c3_half<D / 32>(st);
+  }
+
+  __device__ __forceinline__ void chain(VRegs<T>* vr, int cc) {
     c1(vr, stage(cc));
     if (cc + 1 < nch) load_v(vr, cc + 1);
     c2(stage(cc), cc);
@@ -678,7 +712,7 @@ struct ChunkKernel {
   }
 
   __device__ __forceinline__ void consumer_loop() {
-    VRegs<T> vr;
+    VRegs<T> vr[NCT];
     init_offsets();
     if (nch > 0) load_v(vr, 0);
     for (int it = 0; it < nch + C::LAG; ++it) {
@@ -724,23 +758,26 @@ struct ChunkKernel {
     for (uint32_t i = threadIdx.x * 16; i < C::LDS; i += C::THREADS * 16)
       lds_st<u32x4>(smem, i, u32x4{0u, 0u, 0u, 0u});
 
-    col = vs * 16 * NC + 16 * wave + (l & 15);
-    isv = PREFILL || col < D;
+    colb = vs * 16 * NC * NCT + 16 * NCT * wave + (l & 15);
+    isv = PREFILL || colb < D;  // a wave's tiles lie on one side of D
     const size_t sbase = (size_t)seq * D * D;
     if (wave < NC) {
 #pragma unroll
-      for (int ci = 0; ci < D / 16; ++ci)
+      for (int j = 0; j < NCT; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * ci + g4 + e;
-          float x = 0.f;
-          if (PREFILL) {
-            if (a.S0) x = a.S0[sbase + (size_t)r * D + col];
-          } else if (!isv) {
-            x = (r == col - D) ? 1.f : 0.f;
+        for (int ci = 0; ci < D / 16; ++ci)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * ci + g4 + e;
+            const int c = colb + 16 * j;
+            float x = 0.f;
+            if (PREFILL) {
+              if (a.S0) x = a.S0[sbase + (size_t)r * D + c];
+            } else if (!isv) {
+              x = (r == c - D) ? 1.f : 0.f;
+            }
+            S[j][ci][e] = x;
           }
-          S[ci][e] = x;
-        }
     }
     sync_lds();
 
@@ -752,7 +789,7 @@ struct ChunkKernel {
 
     // prefill over several segments: only the last one's end state is the result
     float* dst;
-    int c = col;
+    int c = colb;
     if (PREFILL) {
       if (a.G > 1 && gseg != a.G - 1) return;
       dst = a.S_out + (size_t)bh * D * D;
@@ -760,12 +797,14 @@ struct ChunkKernel {
       dst = a.S_out + sbase;
     } else {
       dst = a.M_out + sbase;
-      c = col - D;
+      c = colb - D;
     }
 #pragma unroll
-    for (int ci = 0; ci < D / 16; ++ci)
+    for (int j = 0; j < NCT; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ci + g4 + e) * D + c] = S[ci][e];
+      for (int ci = 0; ci < D / 16; ++ci)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ci + g4 + e) * D + c + 16 * j] = S[j][ci][e];
   }
 };
 
@@ -791,9 +830,8 @@ static hipError_t launch_nc(const ChunkArgs& a, int nc, int nwg, hipStream_t str
   switch (nc) {
     case 1: return launch_one<T, D, 1, PREFILL>(a, nwg, stream);
     case 2: return launch_one<T, D, 2, PREFILL>(a, nwg, stream);
-    case 4: return launch_one<T, D, 4, PREFILL>(a, nwg, stream);
-    case 8:
-      if constexpr (sizeof(T) == 2) return launch_one<T, D, 8, PREFILL>(a, nwg, stream);
+    case 4:
+      if constexpr (sizeof(T) == 2) return launch_one<T, D, 4, PREFILL>(a, nwg, stream);
       else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

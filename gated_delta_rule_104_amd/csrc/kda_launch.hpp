@@ -25,11 +25,15 @@ struct ChunkArgs {
   int G;
   int Tseg;         // tokens per segment (the last one may be shorter)
   int Ttot;         // tokens per head
-  int vsplit;       // workgroups per sequence (each owns 16*nc state columns)
+  int vsplit;       // workgroups per sequence (each owns 16 * nc * chunk_tiles_per_wave columns)
 };
 
+// 16-column state tiles each consumer wave of the chunk kernel owns.
+inline int chunk_tiles_per_wave(bool bf16_io) { return bf16_io ? 2 : 1; }
+
 // prefill: columns = D; segment pass: columns = 2*D (state + map).
-// nc in {1, 2, 4, 8}; nwg = G * BH * vsplit.
+// nc = consumer waves per workgroup: {1, 2, 4} for bf16, {1, 2} for fp32;
+// nwg = G * BH * vsplit.
 hipError_t launch_chunk(const ChunkArgs& a, bool bf16_io, int D, bool prefill, int nc, int nwg,
                         hipStream_t stream);
 
