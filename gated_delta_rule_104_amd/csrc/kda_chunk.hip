@@ -68,16 +68,20 @@ struct ChunkCfg {
   static constexpr int TD_TILE = 16 * R_TD + 16;
   static constexpr int TD_SZ = 4 * TD_TILE;
   static constexpr int R_DT = CH * ES;     // [D][CH] rows (channel-major)
-  static constexpr int R_TT = CH * ES;     // [CH][CH] rows
-  static constexpr int R_TI = 16 * ES;     // [16][16] rows
+  // Tiles the consumer reads only as MFMA A fragments (-L, P, T_ii) are stored in
+  // fragment order: 16-byte lane slots, lane l's slot holding exactly the values
+  // its fragment needs, so each fragment is one contiguous, conflict-free read.
+  static constexpr int KB = BF ? 32 : 16;  // MFMA depth of the dense products
+  static constexpr int JPB = KB / 16;      // 16x16 tiles per 16-byte lane slot of P
+  static constexpr int FR16 = 64 * 4 * ES; // one 16x16 tile as 16-deep fragments
   // stage: everything the chain of one chunk reads
   static constexpr uint32_t S_KH = 0;                                   // Kh   [CH][D]
   static constexpr uint32_t S_QH = S_KH + TD_SZ;                        // Qh   [CH][D]
   static constexpr uint32_t S_KT = S_QH + (PREFILL ? TD_SZ : 0);        // Kb^T [D][CH]
-  static constexpr uint32_t S_L = S_KT + D * R_DT;                      // -L   [CH][CH]
-  static constexpr uint32_t S_P = S_L + CH * R_TT;                      // P    [CH][CH]
-  static constexpr uint32_t S_TI = S_P + (PREFILL ? CH * R_TT : 0);     // T_ii [4][16][16]
-  static constexpr uint32_t S_GM = S_TI + 4 * 16 * R_TI;                // Gam  [D] fp32
+  static constexpr uint32_t S_L = S_KT + D * R_DT;                      // -L_IJ, J < I: 6 x FR16
+  static constexpr uint32_t S_P = S_L + 6 * FR16;                       // P: [4][CH/KB][64] slots
+  static constexpr uint32_t S_TI = S_P + (PREFILL ? 4 * (CH / KB) * 64 * 16 : 0);  // T_ii: 4 x FR16
+  static constexpr uint32_t S_GM = S_TI + 4 * FR16;                     // Gam  [D] fp32
   static constexpr uint32_t S_BETA = S_GM + D * 4;                      // beta [CH] fp32
   static constexpr uint32_t STAGE = S_BETA + CH * 4;
   // producer scratch: Kb time-major, the B operand of the score products
@@ -169,6 +173,8 @@ template <> struct Frag<true> {
   __device__ __forceinline__ static f32x4 mma16(f32x4 acc, A16 a, f32x4 b) {
     return mfma_bf16_k16(acc, a, pack4(b));
   }
+  // an accumulator tile as a 16-deep A operand (it then stands for its transpose)
+  __device__ __forceinline__ static A16 a16(f32x4 t) { return pack4(t); }
 };
 template <> struct Frag<false> {
   typedef f32x4 A;
@@ -183,6 +189,7 @@ template <> struct Frag<false> {
     return mfma_f32_k4(acc, a[3], b[3]);
   }
   __device__ __forceinline__ static f32x4 mma16(f32x4 acc, A16 a, f32x4 b) { return mma(acc, a, b); }
+  __device__ __forceinline__ static A16 a16(f32x4 t) { return t; }
 };
 
 template <typename T, int D, int NC, bool PREFILL>
@@ -216,8 +223,7 @@ struct ChunkKernel {
   // each row size, for row tile 0 (the swizzle term depends only on the lane's
   // row within 16, so row tile t adds 16*t*rowbytes).  [k block]
   // (token-by-token tiles and channel-by-token tiles have the same row size.)
-  static_assert(C::R_TT == C::R_DT, "shared fragment offsets");
-  uint32_t oTD[NKD], oTT[NKT], o16;
+  uint32_t oTD[NKD], oDT[NKT];
 
   __device__ __forceinline__ uint32_t stage(int chunk) const {
     return (C::STAGES == 2 ? (uint32_t)(chunk & 1) : 0u) * C::STAGE;
@@ -357,98 +363,96 @@ struct ChunkKernel {
     }
   }
 
-  template <bool NARROW>
-  __device__ __forceinline__ void store_tt(uint32_t base, int r, int s, float x) {
-    lds_st<T>(smem, base + swz<C::R_TT, NARROW>(r, C::ES * s), from_f32<T>(x));
-  }
-
-  // 16-deep A fragment of an LDS tile read with 8-byte (bf16) fragments
-  template <int RR>
-  __device__ __forceinline__ A16 frag16(uint32_t base, int row, int k0, int ln) const {
-    if constexpr (C::BF) return lds_ld<bf16x4>(smem, base + swz<RR, true>(row, 2 * (k0 + 4 * (ln >> 4))));
-    else return lds_ld<f32x4>(smem, base + swz<RR, true>(row, 4 * (k0 + 4 * (ln >> 4))));
-  }
-
-  // Phase 2, one tile task: tile (I, J), J <= I, of -L (MAT 0) or of P (MAT 1).
-  // Operand fragments are fetched before the MFMAs.  The diagonal L tile task
-  // also inverts its block (I + L_II) with matrix cores.
+  // Phase 2, one tile task: block (I, J), J <= I, of the score matrix M = X Kb^T
+  // with X = Kh (L, MAT 0) or Qh (P, MAT 1).  The product is taken transposed
+  // (A = Kb rows, B = X rows), so lane l ends up holding M[16I + l%16][16J + 4g + e]
+  // (g = l/16): exactly its A fragment for the consumer.
+  //   MAT 0, J < I : stores -L = -diag(b) M (all strictly lower)
+  //   MAT 1        : stores P = lower(M)
+  //   MAT 0, J = I : N = L_II (strictly lower), and T_ii = (I + N)^-1 as the exact
+  //                  product (I - N)(I + N^2)(I + N^4)(I + N^8) of commuting factors,
+  //                  computed in registers.  An accumulator tile of X, used as an A
+  //                  operand, stands for X^T; used as a B operand, for X.  Keeping
+  //                  both N and N^T as accumulators gives every power and its
+  //                  transpose, and Z = T_ii^T = (I + N^T)^-1 is accumulated as
+  //                  Z += (N^T)^(2^k) Z from Z = I - N^T.  Z is T_ii's A fragment.
   template <int MAT, int I, int J>
   __device__ __forceinline__ void p2_tile(uint32_t st) {
+    constexpr bool DIAG = MAT == 0 && I == J;
     const int ln = fresh_lane(l);
-    const int g4 = 4 * (ln >> 4);
-    const uint32_t abase = MAT ? st + C::S_QH : st + C::S_KH;
-    const int s0 = ln & 15;
-    typename F::A fa[NKD], fb[NKD];
+    const int g4 = 4 * (ln >> 4), s0 = ln & 15;
+    const uint32_t xbase = MAT ? st + C::S_QH : st + C::S_KH;
+    typename F::A fx[NKD], fb[NKD];
 #pragma unroll
     for (int m = 0; m < NKD; ++m) {
       // both operands read the same stored k positions (any consistent order works)
       const int kb = C::ES * (KB * m + (KB / 4) * (ln >> 4));
-      fa[m] = lds_ld<typename F::A>(smem, abase + td(16 * I + s0, kb));
+      fx[m] = lds_ld<typename F::A>(smem, xbase + td(16 * I + s0, kb));
       fb[m] = lds_ld<typename F::A>(smem, C::X_KB + td(16 * J + s0, kb));
     }
-    float bet[4];
-    if (MAT == 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bet[e] = lds_ld<float>(smem, st + C::S_BETA + 4 * (16 * I + g4 + e));
-    }
+    float bl = 0.f;
+    f32x4 bet4 = zero4();
+    if constexpr (MAT == 0) bl = lds_ld<float>(smem, st + C::S_BETA + 4 * (16 * I + s0));
+    if constexpr (DIAG) bet4 = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * I + g4));
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc = zero4();
 #pragma unroll
-    for (int m = 0; m < NKD; ++m) acc = F::mma(acc, fa[m], fb[m]);
-    const int s = 16 * J + s0;
-    f32x4 N;
+    for (int m = 0; m < NKD; ++m) acc = F::mma(acc, fb[m], fx[m]);
+    if constexpr (MAT == 0 && !DIAG) {
+      f32x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * I + g4 + e;
-      if (MAT == 0) {
-        N[e] = s < r ? acc[e] * bet[e] : 0.f;
-        store_tt<true>(st + C::S_L, r, s, -N[e]);
-      } else {
-        store_tt<false>(st + C::S_P, r, kp(s), s <= r ? acc[e] : 0.f);
-      }
-    }
-    if constexpr (MAT == 0 && I == J) {
-      // (I + N)^-1 with N = L_II strictly lower (nilpotent, N^16 = 0), as the
-      // exact product (I - N)(I + N^2)(I + N^4)(I + N^8).  Each factor is applied
-      // as Y += N^(2^k) Y with Y accumulated in fp32; N^2, N^4, N^8 pass through
-      // the block's slot of the stage to serve as A operands, and N itself is
-      // read back negated from the -L tile just written.
-      f32x4 Y, nN;
+      for (int e = 0; e < 4; ++e) v[e] = -bl * acc[e];
+      put_frag(st + C::S_L + (I * (I - 1) / 2 + J) * C::FR16 + ln * 4 * C::ES, v);
+    } else if constexpr (MAT == 1) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (J < I || g4 + e <= s0) ? acc[e] : 0.f;
+      put_frag(st + C::S_P + ((I * (CH / KB) + J / C::JPB) * 64 + ln) * 16 + (J % C::JPB) * 4 * C::ES, v);
+    } else {
+      f32x4 an = zero4();
+#pragma unroll
+      for (int m = 0; m < NKD; ++m) an = F::mma(an, fx[m], fb[m]);
+      f32x4 Nt, Nn, Z;  // acc(N^T), acc(N), acc(Z)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        Y[e] = (g4 + e == s0 ? 1.f : 0.f) - N[e];
-        nN[e] = -N[e];
+        Nt[e] = g4 + e < s0 ? bl * acc[e] : 0.f;     // N[16I + s0][16I + g4 + e]
+        Nn[e] = s0 < g4 + e ? bet4[e] * an[e] : 0.f;  // N[16I + g4 + e][16I + s0]
+        Z[e] = (g4 + e == s0 ? 1.f : 0.f) - Nt[e];
       }
-      const uint32_t ti = st + C::S_TI + I * 16 * C::R_TI;
-      auto put = [&](const f32x4& t) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lds_st<T>(smem, ti + swz<C::R_TI, true>(g4 + e, C::ES * s0), from_f32<T>(t[e]));
-      };
-      wave_lds_fence();  // the -L_II tile written above is the A operand of (-N)(-N)
-      A16 an = frag16<C::R_TT>(st + C::S_L, 16 * I + s0, 16 * I, ln);
-      f32x4 P2 = F::mma16(zero4(), an, nN);
-      put(P2);
-      wave_lds_fence();
-      A16 a2 = frag16<C::R_TI>(ti, s0, 0, ln);
-      Y = F::mma16(Y, a2, Y);
-      f32x4 P4 = F::mma16(zero4(), a2, P2);
-      put(P4);
-      wave_lds_fence();
-      A16 a4 = frag16<C::R_TI>(ti, s0, 0, ln);
-      Y = F::mma16(Y, a4, Y);
-      f32x4 P8 = F::mma16(zero4(), a4, P4);
-      put(P8);
-      wave_lds_fence();
-      A16 a8 = frag16<C::R_TI>(ti, s0, 0, ln);
-      Y = F::mma16(Y, a8, Y);
-      put(Y);
+      const f32x4 N2 = F::mma16(zero4(), F::a16(Nt), Nn);    // N N
+      const f32x4 Nt2 = F::mma16(zero4(), F::a16(Nn), Nt);   // N^T N^T
+      Z = F::mma16(Z, F::a16(N2), Z);                        // Z += (N^T)^2 Z
+      const f32x4 N4 = F::mma16(zero4(), F::a16(Nt2), N2);   // N^2 N^2
+      const f32x4 Nt4 = F::mma16(zero4(), F::a16(N2), Nt2);  // (N^T)^2 (N^T)^2
+      Z = F::mma16(Z, F::a16(N4), Z);                        // Z += (N^T)^4 Z
+      const f32x4 N8 = F::mma16(zero4(), F::a16(Nt4), N4);   // N^4 N^4
+      Z = F::mma16(Z, F::a16(N8), Z);                        // Z += (N^T)^8 Z
+      put_frag(st + C::S_TI + I * C::FR16 + ln * 4 * C::ES, Z);
     }
   }
 
-  // Phase-2 task list, shared by every wave of the workgroup (task K runs on
-  // wave K mod NW): the four diagonal L tiles (with their inverses) first,
-  // then the P tiles (prefill only), then the off-diagonal L tiles.
+  // 4 values of a 16-deep fragment into its lane slot (bf16: 8 bytes, fp32: 16)
+  __device__ __forceinline__ void put_frag(uint32_t off, const f32x4& v) {
+    if constexpr (C::BF) lds_st<bf16x4>(smem, off, pack4(v));
+    else lds_st<f32x4>(smem, off, v);
+  }
+
+  // Phase-2 tasks: the four diagonal L blocks (with their inverses, about twice
+  // the work of a tile) first, then the P tiles (prefill only), then the
+  // off-diagonal L tiles.  Each task goes to the wave with the least work so far
+  // (greedy, at compile time), every wave of the workgroup taking part.
   static constexpr int NT2 = PREFILL ? 20 : 10;
+  static constexpr int task_wave(int K) {
+    int load[C::NW] = {};
+    int w = 0;
+    for (int k = 0; k <= K; ++k) {
+      w = 0;
+      for (int i = 1; i < C::NW; ++i)
+        if (load[i] < load[w]) w = i;
+      load[w] += k < 4 ? 2 : 1;
+    }
+    return w;
+  }
   static constexpr int task_mat(int K) { return K < 4 ? 0 : (PREFILL && K < 14 ? 1 : 0); }
   static constexpr int task_i(int K) {
     if (K < 4) return K;
@@ -480,7 +484,8 @@ struct ChunkKernel {
   template <int K>
   __device__ __forceinline__ void p2_task(uint32_t st) {
     if constexpr (K < NT2) {
-      if (K % C::NW == wave) p2_tile<task_mat(K), task_i(K), task_j(K)>(st);
+      constexpr int W = task_wave(K);  // evaluated at compile time
+      if (W == wave) p2_tile<task_mat(K), task_i(K), task_j(K)>(st);
       p2_task<K + 1>(st);
     }
   }
@@ -489,14 +494,13 @@ struct ChunkKernel {
 
   // ------------------------------------------------------------ consumers
   __device__ __forceinline__ void init_offsets() {
-    const int r16 = l & 15, kk = 4 * (l >> 4);
+    const int r16 = l & 15;
     // the lane group's k positions start at stored position KB/4 * group
     const int kg = (KB / 4) * (l >> 4);
 #pragma unroll
     for (int m = 0; m < NKD; ++m) oTD[m] = swz<C::R_TD>(r16, C::ES * (KB * m + kg));
 #pragma unroll
-    for (int m = 0; m < NKT; ++m) oTT[m] = swz<C::R_TT>(r16, C::ES * (KB * m + kg));
-    o16 = swz<C::R_TI, true>(r16, C::ES * kk);
+    for (int m = 0; m < NKT; ++m) oDT[m] = swz<C::R_DT>(r16, C::ES * (KB * m + kg));
   }
 
   // A fragment of row tile `t` and k block m of an LDS tile at `base`.
@@ -560,7 +564,6 @@ struct ChunkKernel {
   // Delta from (I + L) Delta = diag(b) (V - Kh S) by 16-row blocks:
   // Delta_i = T_ii (X_i + sum_{j<i} (-L_ij) Delta_j).
   __device__ __forceinline__ void c1(const VRegs<T>* vr, uint32_t st) {
-    const int kk = 4 * (l >> 4);
 #pragma unroll
     for (int j = 0; j < NCT; ++j)
 #pragma unroll
@@ -569,13 +572,13 @@ struct ChunkKernel {
     c1_half<0>(vr, st, X);
     c1_half<2>(vr, st, X);
     A16 ft[4], fl[4][4];
+    const uint32_t lo = (uint32_t)fresh_lane(l) * 4 * C::ES;
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
-      ft[ti] = lds_ld<A16>(smem, st + C::S_TI + ti * 16 * C::R_TI + o16);
+      ft[ti] = lds_ld<A16>(smem, st + C::S_TI + ti * C::FR16 + lo);
 #pragma unroll
       for (int jj = 0; jj < ti; ++jj)
-        fl[ti][jj] = lds_ld<A16>(smem, st + C::S_L + 16 * ti * C::R_TT +
-                                           swz<C::R_TT, true>(l & 15, C::ES * (16 * jj + kk)));
+        fl[ti][jj] = lds_ld<A16>(smem, st + C::S_L + (ti * (ti - 1) / 2 + jj) * C::FR16 + lo);
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 Dl[NCT][4];
@@ -600,6 +603,7 @@ struct ChunkKernel {
   template <int H0>
   __device__ __forceinline__ void c2_half(uint32_t st, int chunk) {
     const int kk = 4 * (l >> 4);
+    const int ln = fresh_lane(l);
     typename F::A fq[2][NKD], fp[2][NKT];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -607,7 +611,8 @@ struct ChunkKernel {
 #pragma unroll
       for (int m = 0; m < NKD; ++m) fq[h][m] = ar<C::TD_TILE>(st + C::S_QH, oTD, ti, m);
 #pragma unroll
-      for (int m = 0; m <= tri(ti); ++m) fp[h][m] = ar<16 * C::R_TT>(st + C::S_P, oTT, ti, m);
+      for (int m = 0; m <= tri(ti); ++m)
+        fp[h][m] = lds_ld<typename F::A>(smem, st + C::S_P + ((ti * NKT + m) * 64 + ln) * 16);
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 O[NCT][2];
@@ -661,7 +666,7 @@ struct ChunkKernel {
 #pragma unroll
     for (int ci = 0; ci < NH; ++ci) {
 #pragma unroll
-      for (int m = 0; m < NKT; ++m) fk[ci][m] = ar<16 * C::R_DT>(st + C::S_KT, oTT, C0 + ci, m);
+      for (int m = 0; m < NKT; ++m) fk[ci][m] = ar<16 * C::R_DT>(st + C::S_KT, oDT, C0 + ci, m);
       gm[ci] = lds_ld<f32x4>(smem, st + C::S_GM + 4 * (16 * (C0 + ci) + kk));
     }
     __builtin_amdgcn_sched_barrier(0);
