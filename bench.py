@@ -109,7 +109,9 @@ def segment_prefill_bytes(B, H, T, D, G):
 
 def bench_decomposition(pf, args):
     """Per-kernel durations of the sequence-split prefill, through the three public
-    calls it is made of (same kernels and launch shapes as kda_chunk_prefill)."""
+    calls it is made of, with the same launch shapes as kda_chunk_prefill: the
+    segment pass over the first G-1 segments (the last one's zero-start state and
+    map are not needed), the merge of those, and the prefill of all G segments."""
     g = pf["g"]
     B, H, T, D = pf["B"], pf["H"], pf["T"], pf["D"]
     G, Tseg = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
@@ -117,17 +119,19 @@ def bench_decomposition(pf, args):
         return None
     assert G * Tseg == T, "decomposition timing needs T to be a multiple of the segment length"
     dev = g["k"].device
-    Z = torch.empty(G, B, H, D, D, dtype=torch.float32, device=dev)
+    T1 = (G - 1) * Tseg
+    lead = {n: g[n][:, :, :T1].contiguous() for n in ("k", "v", "log_alpha", "beta")}
+    Z = torch.empty(G - 1, B, H, D, D, dtype=torch.float32, device=dev)
     M = torch.empty_like(Z)
-    S_start = torch.empty_like(Z)
+    S_start = torch.empty(G, B, H, D, D, dtype=torch.float32, device=dev)
     S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
     o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
     parts = {
-        "segment_transfer": (lambda: kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], G,
-                                                          S_zero_end=Z, M=M),
-                             segment_pass_bytes(B, H, T, D, G)),
-        "segment_merge": (lambda: kda.segment_merge(Z, M, None, S_start=S_start, S_T=S_T),
-                          merge_bytes(B, H, D, G)),
+        "segment_transfer": (lambda: kda.segment_transfer(lead["k"], lead["v"], lead["log_alpha"], lead["beta"],
+                                                          G - 1, S_zero_end=Z, M=M),
+                             segment_pass_bytes(B, H, T1, D, G - 1)),
+        "segment_merge": (lambda: kda.segment_merge(Z, M, None, S_start=S_start[: G - 1], S_T=S_start[G - 1]),
+                          merge_bytes(B, H, D, G - 1)),
         "segment_prefill": (lambda: kda.prefill_segments(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"],
                                                          S_start, Tseg, o=o, S_T=S_T),
                             segment_prefill_bytes(B, H, T, D, G)),
@@ -141,6 +145,7 @@ def bench_decomposition(pf, args):
         # each launch alone between events on the stream it runs on
         ms, _ = time_launches(fn, n)
         res[name] = {"ms": ms, "algorithmic_bytes": nbytes, "GBs": nbytes / (ms * 1e-3) / 1e9}
+    del lead
     return res
 
 
@@ -292,9 +297,9 @@ def main():
     dec = bench_decomposition(pf, args)
     if dec is not None:
         names = ("segment_transfer", "segment_merge", "segment_prefill")
-        kern = {"segment_transfer": "kda_chunk_kernel<bf16,128,8,transfer>",
+        kern = {"segment_transfer": "kda_chunk_kernel<bf16,128,8,segment>",
                 "segment_merge": "kda_merge_kernel<128>",
-                "segment_prefill": "kda_chunk_kernel<bf16,128,8,prefill>"}
+                "segment_prefill": "kda_chunk_kernel<bf16,128,4,prefill>"}
         dom = max(names, key=lambda n: dec[n]["ms"])
         r = dec[dom]
         traffic = TRAFFIC[dom] if kernel_sources_sha() == TRAFFIC["sources_sha"] else None

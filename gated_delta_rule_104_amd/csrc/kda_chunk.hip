@@ -532,26 +532,34 @@ struct ChunkKernel {
 
   __device__ __forceinline__ float vval(const VRegs<T>& vr, int i) const { return vr.get(i); }
 
-  // X_t = b_t (v_t - (Kh S)_t) for row tiles H0, H0+1 (fragments fetched first).
+  // With three waves per SIMD (segment pass with 8 consumer waves) registers are
+  // tighter, and operand fragments are fetched in smaller batches.
+  static constexpr bool TIGHT = C::NW > 8;
+  static constexpr int C1B = 2;                    // row tiles per batch in c1
+  static constexpr int C3B = TIGHT ? 2 : D / 32;   // state row tiles per batch in c3
+
+  // X_t = b_t (v_t - (Kh S)_t) for row tiles H0 .. H0+C1B-1 (fragments fetched first).
   template <int H0>
-  __device__ __forceinline__ void c1_half(const VRegs<T>* vr, uint32_t st, f32x4 (*X)[4]) {
-    typename F::A fk[2][NKD];
+  __device__ __forceinline__ void c1_part(const VRegs<T>* vr, uint32_t st, f32x4 (*X)[4]) {
+    typename F::A fk[C1B][NKD];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < C1B; ++h)
 #pragma unroll
       for (int m = 0; m < NKD; ++m) fk[h][m] = ar<C::TD_TILE>(st + C::S_KH, oTD, H0 + h, m);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < NCT; ++j) X[j][H0] = X[j][H0 + 1] = zero4();
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int h = 0; h < C1B; ++h) X[j][H0 + h] = zero4();
 #pragma unroll
     for (int m = 0; m < NKD; ++m)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < C1B; ++h)
 #pragma unroll
         for (int j = 0; j < NCT; ++j) X[j][H0 + h] = F::mma(X[j][H0 + h], fk[h][m], sb[j][m]);
     const int kk = 4 * (l >> 4);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < C1B; ++h) {
       const f32x4 bet = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * (H0 + h) + kk));
 #pragma unroll
       for (int j = 0; j < NCT; ++j)
@@ -561,16 +569,54 @@ struct ChunkKernel {
     }
   }
 
+  // Tight variant of the X computation: one k block at a time over all four row
+  // tiles, so only that block of the bf16 copy of S is live (the segment pass
+  // has no later use for it).
+  template <int M>
+  __device__ __forceinline__ void c1_kblock(uint32_t st, f32x4 (*X)[4]) {
+    typename F::A fk[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) fk[t] = ar<C::TD_TILE>(st + C::S_KH, oTD, t, M);
+    typename F::B bm[NCT];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) bm[j] = F::bfrag(S[j], M);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) X[j][t] = F::mma(M == 0 ? zero4() : X[j][t], fk[t], bm[j]);
+  }
+  template <int M>
+  __device__ __forceinline__ void c1_kblocks(uint32_t st, f32x4 (*X)[4]) {
+    if constexpr (M < NKD) {
+      c1_kblock<M>(st, X);
+      c1_kblocks<M + 1>(st, X);
+    }
+  }
+
   // Delta from (I + L) Delta = diag(b) (V - Kh S) by 16-row blocks:
   // Delta_i = T_ii (X_i + sum_{j<i} (-L_ij) Delta_j).
   __device__ __forceinline__ void c1(const VRegs<T>* vr, uint32_t st) {
-#pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int m = 0; m < NKD; ++m) sb[j][m] = F::bfrag(S[j], m);
     f32x4 X[NCT][4];
-    c1_half<0>(vr, st, X);
-    c1_half<2>(vr, st, X);
+    if constexpr (TIGHT) {
+      c1_kblocks<0>(st, X);
+      const int kk = 4 * (l >> 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 bet = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * t + kk));
+#pragma unroll
+        for (int j = 0; j < NCT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) X[j][t][e] = bet[e] * (vval(vr[j], 4 * t + e) - X[j][t][e]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NCT; ++j)
+#pragma unroll
+        for (int m = 0; m < NKD; ++m) sb[j][m] = F::bfrag(S[j], m);
+      c1_part<0>(vr, st, X);
+      c1_part<2>(vr, st, X);
+    }
     A16 ft[4], fl[4][4];
     const uint32_t lo = (uint32_t)fresh_lane(l) * 4 * C::ES;
 #pragma unroll
@@ -656,10 +702,10 @@ struct ChunkKernel {
     }
   }
 
-  // S = Diag(Gam) (S + Kb^T Delta) for state row tiles C0 .. C0 + D/32 - 1.
+  // S = Diag(Gam) (S + Kb^T Delta) for state row tiles C0 .. C0 + C3B - 1.
   template <int C0>
-  __device__ __forceinline__ void c3_half(uint32_t st) {
-    constexpr int NH = D / 32;
+  __device__ __forceinline__ void c3_part(uint32_t st) {
+    constexpr int NH = C3B;
     const int kk = 4 * (l >> 4);
     typename F::A fk[NH][NKT];
     f32x4 gm[NH];
@@ -682,10 +728,14 @@ struct ChunkKernel {
       for (int j = 0; j < NCT; ++j) S[j][C0 + ci] = S[j][C0 + ci] * gm[ci];
   }
 
-  __device__ __forceinline__ void c3(uint32_t st) {
-    c3_half<0>(st);
-    c3_half<D / 32>(st);
+  template <int C0>
+  __device__ __forceinline__ void c3_from(uint32_t st) {
+    if constexpr (C0 < D / 16) {
+      c3_part<C0>(st);
+      c3_from<C0 + C3B>(st);
+    }
   }
+  __device__ __forceinline__ void c3(uint32_t st) { c3_from<0>(st); }
 
   __device__ __forceinline__ void chain(VRegs<T>* vr, int cc) {
     c1(vr, stage(cc));
@@ -837,6 +887,9 @@ static hipError_t launch_nc(const ChunkArgs& a, int nc, int nwg, hipStream_t str
     case 2: return launch_one<T, D, 2, PREFILL>(a, nwg, stream);
     case 4:
       if constexpr (sizeof(T) == 2) return launch_one<T, D, 4, PREFILL>(a, nwg, stream);
+      else return hipErrorInvalidValue;
+    case 8:
+      if constexpr (sizeof(T) == 2 && !PREFILL && D == 128) return launch_one<T, D, 8, PREFILL>(a, nwg, stream);
       else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

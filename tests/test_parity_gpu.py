@@ -114,6 +114,19 @@ def test_prefill_column_split_invariant(nc, monkeypatch):
     assert torch.equal(o, o1) and torch.equal(S_T, S1)
 
 
+@pytest.mark.parametrize("nc", ["1", "2", "4", "8"])
+def test_segment_pass_column_split_invariant(nc, monkeypatch):
+    """Every consumer-wave count of the segment pass gives bit-identical states
+    and maps (the columns are independent once the chunk operands are built)."""
+    d = ki.gen_prefill(1, 3, 4 * 200, 128, 128, "bf16", seed=62, variant="slow")
+    g = to_dev(d)
+    Z, M = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], 4)
+    monkeypatch.setenv("KDA_NC", nc)
+    Z1, M1 = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], 4)
+    torch.cuda.synchronize()
+    assert torch.equal(Z, Z1) and torch.equal(M, M1)
+
+
 # ----------------------------------------------------------------- decode
 
 def run_decode_case(N, H, D, dtype, steps, seed, variant="none"):
