@@ -8,103 +8,110 @@
 // This is one token of the recurrence S = (I - b k k^T) Diag(a) S + b k v^T,
 // o = S^T q, rearranged so that S is read once and written once.
 //
-// Workgroup = one head, 256 threads.  Thread t owns columns 4*(t%32)..+3 of
-// rows t/32 + 8*i (i = 0..D/8-1): every row is read as 32 coalesced 16-byte
-// pieces, and the state slice stays in registers between the read and the
-// write.  The column reductions over rows finish with a lane shuffle (the two
-// row groups of a wave) and an LDS pass over the four waves.
+// Workgroup = one head, four waves; wave w owns the D/4 columns
+// [w*D/4, (w+1)*D/4) and all D rows of them, so every reduction over rows
+// stays inside the wave (lane shuffles) and the waves never wait for each
+// other.  Lane l covers 4 columns (l % LPR) of RPL consecutive rows; a row
+// slice of the wave is LPR lanes x 16 bytes, so each load instruction reads
+// whole 128-byte (D = 128) or 64-byte (D = 64) row pieces.  The gate, key and
+// query vectors pass through a per-wave LDS area so that each lane reads its
+// rows' values as vectors.  The state is streamed with non-temporal accesses:
+// it is touched once per step and is larger than the caches.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
+
+template <typename T>
+__device__ __forceinline__ float ld1(const T* p) {
+  return to_f32(*p);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void kda_decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                          const T* __restrict__ v, const T* __restrict__ la,
                                                          const T* __restrict__ beta, float* __restrict__ S,
                                                          T* __restrict__ o) {
-  constexpr int RPT = D / 8;  // rows per thread
-  __shared__ float s_a[D], s_ak[D], s_aq[D];
-  __shared__ float s_red[4][2][D];
-  __shared__ float s_kq[4];
+  constexpr int CPW = D / 4;       // columns per wave
+  constexpr int LPR = CPW / 4;     // lanes per row slice (4 columns each)
+  constexpr int RG = 64 / LPR;     // row groups per wave
+  constexpr int RPL = D / RG;      // consecutive rows per lane
+  static_assert(RPL % 4 == 0, "row vectors");
+  // per wave: a, a*k, a*q, k for all D channels
+  __shared__ __attribute__((aligned(16))) float s_v[4][4][D];
   const int head = blockIdx.x;
-  const int t = threadIdx.x;
-  const int cg = t & 31, rg = t >> 5;
-  const int wave = t >> 6, lane = t & 63;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int cl = l % LPR, rg = l / LPR;
+  const int c0 = wave * CPW + 4 * cl;  // first of the lane's 4 columns
+  const int r0 = rg * RPL;             // first of the lane's rows
   float* Sh = S + (size_t)head * D * D;
 
-  f32x4 st[RPT];
+  f32x4 st[RPL];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i)
-    st[i] = (4 * cg < D) ? *reinterpret_cast<const f32x4*>(Sh + (size_t)(rg + 8 * i) * D + 4 * cg) : zero4();
+  for (int i = 0; i < RPL; ++i)
+    st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sh + (size_t)(r0 + i) * D + c0));
 
+  // gate, key and query: the wave's lanes cover the D channels
   float kq = 0.f;
-  if (t < D) {
-    const float kt = to_f32(k[(size_t)head * D + t]);
-    const float qt = to_f32(q[(size_t)head * D + t]);
-    const float at = expf(to_f32(la[(size_t)head * D + t]));
-    s_a[t] = at;
-    s_ak[t] = at * kt;
-    s_aq[t] = at * qt;
-    kq = kt * qt;
+  float* sa = s_v[wave][0];
+  float* sak = s_v[wave][1];
+  float* saq = s_v[wave][2];
+  float* sk = s_v[wave][3];
+#pragma unroll
+  for (int j = l; j < D; j += 64) {
+    const size_t idx = (size_t)head * D + j;
+    const float kt = ld1(k + idx), qt = ld1(q + idx);
+    const float at = expf(ld1(la + idx));
+    sa[j] = at;
+    sak[j] = at * kt;
+    saq[j] = at * qt;
+    sk[j] = kt;
+    kq += kt * qt;
   }
-  // k.q over the D channels (threads 0..D-1 hold one product each)
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off);
-  if (lane == 0) s_kq[wave] = kq;
-  __syncthreads();
+  wave_lds_fence();  // this wave's LDS writes before its reads
 
   float u[4] = {0.f, 0.f, 0.f, 0.f}, w[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rg + 8 * i;
-    const float ak = s_ak[r], aq = s_aq[r];
+  for (int i4 = 0; i4 < RPL; i4 += 4) {
+    const f32x4 ak = *reinterpret_cast<const f32x4*>(sak + r0 + i4);
+    const f32x4 aq = *reinterpret_cast<const f32x4*>(saq + r0 + i4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u[c] += ak[e] * st[i4 + e][c];
+        w[c] += aq[e] * st[i4 + e][c];
+      }
+  }
+  // sum over the row groups (lanes with the same column group)
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      u[c] += ak * st[i][c];
-      w[c] += aq * st[i][c];
+      u[c] += __shfl_xor(u[c], off);
+      w[c] += __shfl_xor(w[c], off);
     }
-  }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    u[c] += __shfl_xor(u[c], 32);
-    w[c] += __shfl_xor(w[c], 32);
-  }
-  if (lane < 32 && 4 * cg < D) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      s_red[wave][0][4 * cg + c] = u[c];
-      s_red[wave][1][4 * cg + c] = w[c];
-    }
-  }
-  __syncthreads();
-  if (4 * cg >= D) return;
-  const float b = to_f32(beta[head]);
-  const float kqs = s_kq[0] + s_kq[1] + s_kq[2] + s_kq[3];
+  const float b = ld1(beta + head);
   float dl[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int j = 4 * cg + c;
-    const float uu = s_red[0][0][j] + s_red[1][0][j] + s_red[2][0][j] + s_red[3][0][j];
-    dl[c] = b * (to_f32(v[(size_t)head * D + j]) - uu);
-  }
+  for (int c = 0; c < 4; ++c) dl[c] = b * (ld1(v + (size_t)head * D + c0 + c) - u[c]);
   if (rg == 0) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = 4 * cg + c;
-      const float ww = s_red[0][1][j] + s_red[1][1][j] + s_red[2][1][j] + s_red[3][1][j];
-      o[(size_t)head * D + j] = from_f32<T>(ww + kqs * dl[c]);
-    }
+    for (int c = 0; c < 4; ++c) o[(size_t)head * D + c0 + c] = from_f32<T>(w[c] + kq * dl[c]);
   }
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rg + 8 * i;
-    const float ar = s_a[r];
-    const float kr = to_f32(k[(size_t)head * D + r]);
-    f32x4 x;
+  for (int i4 = 0; i4 < RPL; i4 += 4) {
+    const f32x4 ar = *reinterpret_cast<const f32x4*>(sa + r0 + i4);
+    const f32x4 kr = *reinterpret_cast<const f32x4*>(sk + r0 + i4);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = ar * st[i][c] + kr * dl[c];
-    *reinterpret_cast<f32x4*>(Sh + (size_t)r * D + 4 * cg) = x;
+    for (int e = 0; e < 4; ++e) {
+      f32x4 x;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = ar[e] * st[i4 + e][c] + kr[e] * dl[c];
+      __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(Sh + (size_t)(r0 + i4 + e) * D + c0));
+    }
   }
 }
 
