@@ -101,15 +101,13 @@ __device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// DPP moves within rows of 16 lanes (gfx9 encodings): row_shr:n shifts values
-// n lanes up inside the row (lanes below n read 0); row_share:15 broadcasts
-// lane 15 of the row.
+// DPP moves within rows of 16 lanes (gfx9 encoding): row_shr:n shifts values
+// n lanes up inside the row (lanes below n read 0).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 constexpr int DPP_ROW_SHR = 0x110;
-constexpr int DPP_ROW_SHARE15 = 0x15F;
 
 // 8 consecutive elements of a token row, as loaded from HBM.
 template <typename T> struct Raw8 { u32x4 p[sizeof(T) / 2]; };
@@ -215,7 +213,8 @@ struct ChunkKernel {
   int wave, l;
   // consumer: NCT adjacent 16-column tiles of the state, sharing every A fragment
   static constexpr int NCT = C::NCT;
-  int colb;         // global column of this lane in tile 0 (tile j: colb + 16 j)
+  int colb;         // global column of this lane in tile 0 (tile j: colb + j, so a
+                    // lane's columns are adjacent and move as one 4-byte bf16 pair)
   bool isv;         // columns read v (value columns) rather than being map columns
   f32x4 S[NCT][D / 16];
   typename F::B sb[NCT][NKD], db[NCT][NKT];
@@ -269,7 +268,7 @@ struct ChunkKernel {
         for (int c = 0; c < 8; ++c) g[i][c] *= LOG2E;
       }
     }
-    float inc[8], exc[8], gc[8];
+    float exc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       g[1][c] += g[0][c];
@@ -281,10 +280,10 @@ struct ChunkKernel {
       x += dpp<DPP_ROW_SHR + 2>(x);
       x += dpp<DPP_ROW_SHR + 4>(x);
       x += dpp<DPP_ROW_SHR + 8>(x);
-      inc[c] = x;
       exc[c] = dpp<DPP_ROW_SHR + 1>(x);
-      gc[c] = dpp<DPP_ROW_SHARE15>(x);
     }
+    // e^g of the chunk's last token (row 3 of token group 15) is Gam
+    float eg3[8];
     float kb[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -303,6 +302,7 @@ struct ChunkKernel {
           eg = expf(gg);
           emg = expf(-gg);
         }
+        if (i == 3) eg3[c] = eg;
         vkh[c] = kk[c] * eg;
         kb[i][c] = kk[c] * emg;
         if constexpr (PREFILL) vq[c] = qq[c] * eg;
@@ -352,10 +352,7 @@ struct ChunkKernel {
     }
     if (tg == 15) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float gm = C::BF ? __builtin_amdgcn_exp2f(gc[c]) : expf(gc[c]);
-        lds_st<float>(smem, st + C::S_GM + 4 * (ch + c), gm);
-      }
+      for (int c = 0; c < 8; ++c) lds_st<float>(smem, st + C::S_GM + 4 * (ch + c), eg3[c]);
     }
     if (pw == 0) {
       const float b = C::BF ? __uint_as_float(r.beta << 16) : __uint_as_float(r.beta);
@@ -381,14 +378,15 @@ struct ChunkKernel {
     constexpr bool DIAG = MAT == 0 && I == J;
     const int ln = fresh_lane(l);
     const int g4 = 4 * (ln >> 4), s0 = ln & 15;
-    const uint32_t xbase = MAT ? st + C::S_QH : st + C::S_KH;
+    const uint32_t xbase = (MAT ? st + C::S_QH : st + C::S_KH) + I * C::TD_TILE;
     typename F::A fx[NKD], fb[NKD];
 #pragma unroll
     for (int m = 0; m < NKD; ++m) {
-      // both operands read the same stored k positions (any consistent order works)
-      const int kb = C::ES * (KB * m + (KB / 4) * (ln >> 4));
-      fx[m] = lds_ld<typename F::A>(smem, xbase + td(16 * I + s0, kb));
-      fb[m] = lds_ld<typename F::A>(smem, C::X_KB + td(16 * J + s0, kb));
+      // row s0 of row tile I (J), stored k positions of the lane group: the
+      // consumer's fragment offsets (both operands read the same positions,
+      // which is a valid contraction in any consistent order)
+      fx[m] = lds_ld<typename F::A>(smem, xbase + oTD[m]);
+      fb[m] = lds_ld<typename F::A>(smem, C::X_KB + J * C::TD_TILE + oTD[m]);
     }
     float bl = 0.f;
     f32x4 bet4 = zero4();
@@ -516,18 +514,23 @@ struct ChunkKernel {
     const int ln = fresh_lane(l);
     const int g4 = 4 * (ln >> 4);
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
+    for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // map columns (segment pass) read v = 0: their offset is past any buffer end
-          const uint32_t off = ((uint32_t)((chunk * CH + 16 * ti + g4 + e) * D + colb + 16 * j) * C::ES) |
-                               (isv ? 0u : 0x80000000u);
-          if constexpr (C::BF) vr[j].set(4 * ti + e, __builtin_amdgcn_raw_buffer_load_b16(rv, off, 0, 0));
-          else vr[j].set(4 * ti + e, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0));
+      for (int e = 0; e < 4; ++e) {
+        // map columns (segment pass) read v = 0: their offset is past any buffer end
+        const uint32_t off = ((uint32_t)((chunk * CH + 16 * ti + g4 + e) * D + colb) * C::ES) |
+                             (isv ? 0u : 0x80000000u);
+        if constexpr (C::BF) {
+          static_assert(NCT == 2, "bf16 lanes own a column pair");
+          const uint32_t pr = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
+          vr[0].set(4 * ti + e, (unsigned short)(pr & 0xffffu));
+          vr[1].set(4 * ti + e, (unsigned short)(pr >> 16));
+        } else {
+          static_assert(NCT == 1, "fp32 lanes own one column");
+          vr[0].set(4 * ti + e, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0));
         }
       }
+    }
   }
 
   __device__ __forceinline__ float vval(const VRegs<T>& vr, int i) const { return vr.get(i); }
@@ -679,20 +682,16 @@ struct ChunkKernel {
           if (m <= tri(H0 + h)) O[j][h] = F::mma(O[j][h], fp[h][m], db[j][m]);
     const uint32_t ob = (uint32_t)((chunk * CH + kk) * D + colb) * C::ES;
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t off = ob + (uint32_t)(((16 * (H0 + h) + e) * D + 16 * j) * C::ES);
-          if constexpr (C::BF) {
-            const bf16 hv = (bf16)O[j][h][e];
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), ro, off, 0, 0);
-          } else {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[j][h][e]), ro, off, 0, 0);
-          }
-        }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t off = ob + (uint32_t)((16 * (H0 + h) + e) * D * C::ES);
+        if constexpr (C::BF)
+          __builtin_amdgcn_raw_buffer_store_b32(cvt2(O[0][h][e], O[1][h][e]), ro, off, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[0][h][e]), ro, off, 0, 0);
       }
+    }
   }
 
   __device__ __forceinline__ void c2(uint32_t st, int chunk) {
@@ -752,6 +751,7 @@ struct ChunkKernel {
   // chunk's are consumed.
   __device__ __forceinline__ void producer_loop() {
     ProdRaw<T> r;
+    init_offsets();
     if (nch > 0) load_raw(r, 0);
     for (int it = 0; it < nch + C::LAG; ++it) {
       const bool w = it < nch;
@@ -813,7 +813,7 @@ struct ChunkKernel {
     for (uint32_t i = threadIdx.x * 16; i < C::LDS; i += C::THREADS * 16)
       lds_st<u32x4>(smem, i, u32x4{0u, 0u, 0u, 0u});
 
-    colb = vs * 16 * NC * NCT + 16 * NCT * wave + (l & 15);
+    colb = vs * 16 * NC * NCT + 16 * NCT * wave + NCT * (l & 15);
     isv = PREFILL || colb < D;  // a wave's tiles lie on one side of D
     const size_t sbase = (size_t)seq * D * D;
     if (wave < NC) {
@@ -824,7 +824,7 @@ struct ChunkKernel {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * ci + g4 + e;
-            const int c = colb + 16 * j;
+            const int c = colb + j;
             float x = 0.f;
             if (PREFILL) {
               if (a.S0) x = a.S0[sbase + (size_t)r * D + c];
@@ -859,7 +859,7 @@ struct ChunkKernel {
 #pragma unroll
       for (int ci = 0; ci < D / 16; ++ci)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ci + g4 + e) * D + c + 16 * j] = S[j][ci][e];
+        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ci + g4 + e) * D + c + j] = S[j][ci][e];
   }
 };
 
