@@ -6,62 +6,103 @@
 // "针对适配的 Infra", KDA context parallelism).  Per (b, h):
 //     S = S_in;  for i in 0..G-1:  S_start[i] = S;  S = M[i] S + S_zero_end[i];
 //     S_T = S.
-// Workgroup = one head and 16 state columns; 256 threads, thread t computes
-// row t/2 and columns (t%2)*8..+7 of the slice (threads with t/2 >= D idle).
-// The slice of S lives in LDS; M rows stream from L2.  fp32 VALU: the merge is
-// a few GFLOP in total and not worth matrix cores.
+//
+// Workgroup = one head and 16 state columns, four waves; wave w computes row
+// tiles w*D/64 .. of the new slice with fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32, full fp32 precision).  The slice of S is the B
+// operand, kept in LDS in accumulator layout (lane l holds rows 4*(l/16)+e of
+// column l%16 of each 16-row tile), so the A operand reads 4 consecutive
+// entries of an M row per lane.  The next segment's M rows are fetched into
+// registers while the current product runs.  The workgroups of one head sit on
+// one XCD, so M is read from HBM once per head and shared through that L2.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
 
 template <int D>
-// S_T may alias S_in: a workgroup reads its slice of S_in before any write.
+// S_T may alias S_in: every read of S_in happens before the first barrier, every
+// write of S_T after the last one, and each workgroup touches only its columns.
 __global__ __launch_bounds__(256) void kda_merge_kernel(const float* S_in, const float* __restrict__ Z,
                                                         const float* __restrict__ M,
                                                         float* __restrict__ S_start, float* S_T,
                                                         int BH, int G) {
-  __shared__ float s[D][16];
-  const int bh = blockIdx.x / (D / 16);
-  const int c0 = (blockIdx.x % (D / 16)) * 16;
-  const int t = threadIdx.x;
-  const int r = t >> 1, cb = (t & 1) * 8;
-  const bool active = r < D;
+  constexpr int NT = D / 16;   // 16-row tiles of the state (= k tiles of the product)
+  constexpr int RPW = NT / 4;  // row tiles per wave
+  __shared__ f32x4 sS[NT][64];
+  const int W = gridDim.x;
+  int id = blockIdx.x;
+  if ((W & 7) == 0) id = (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
+  const int bh = id / NT, ct = id - bh * NT;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int g4 = 4 * (l >> 4), r16 = l & 15;
+  const int col = 16 * ct + r16;
   const size_t hs = (size_t)bh * D * D;
-  if (active) {
+
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s[r][cb + c] = S_in ? S_in[hs + (size_t)r * D + c0 + cb + c] : 0.f;
+  for (int q = 0; q < RPW; ++q) {
+    const int rt = wave * RPW + q;
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = S_in ? S_in[hs + (size_t)(16 * rt + g4 + e) * D + col] : 0.f;
+    sS[rt][l] = x;
   }
+
+  // M rows of this wave's row tiles for segment i: a[q][t] = M[16 rt + r16][16 t + g4 .. +3]
+  auto load_m = [&](f32x4 (*a)[NT], int i) {
+    const float* Mi = M + ((size_t)i * BH + bh) * D * D;
+#pragma unroll
+    for (int q = 0; q < RPW; ++q)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        a[q][t] = *reinterpret_cast<const f32x4*>(Mi + (size_t)(16 * (wave * RPW + q) + r16) * D + 16 * t + g4);
+  };
+  f32x4 am[RPW][NT];
+  if (G > 0) load_m(am, 0);
   __syncthreads();
+
   for (int i = 0; i < G; ++i) {
     const size_t gs = ((size_t)i * BH + bh) * D * D;
-    float acc[8];
-    if (active) {
+    f32x4 b[NT];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        acc[c] = Z[gs + (size_t)r * D + c0 + cb + c];
-        if (S_start) S_start[gs + (size_t)r * D + c0 + cb + c] = s[r][cb + c];
-      }
-      const float* Mr = M + gs + (size_t)r * D;
-      for (int m = 0; m < D; m += 4) {
-        const f32x4 mv = *reinterpret_cast<const f32x4*>(Mr + m);
+    for (int t = 0; t < NT; ++t) b[t] = sS[t][l];
+    f32x4 acc[RPW];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+    for (int q = 0; q < RPW; ++q) {
+      const int rt = wave * RPW + q;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) acc[c] += mv[e] * s[m + e][cb + c];
-        }
+      for (int e = 0; e < 4; ++e) {
+        const size_t off = gs + (size_t)(16 * rt + g4 + e) * D + col;
+        acc[q][e] = Z[off];
+        if (S_start) S_start[off] = b[rt][e];
       }
     }
-    __syncthreads();
-    if (active) {
+    f32x4 an[RPW][NT];
+    if (i + 1 < G) load_m(an, i + 1);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) s[r][cb + c] = acc[c];
-    }
+    for (int q = 0; q < RPW; ++q)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[q] = mfma_f32_k4(acc[q], am[q][t][e], b[t][e]);
+    __syncthreads();  // every wave has read the old slice
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) sS[wave * RPW + q][l] = acc[q];
     __syncthreads();
+    if (i + 1 < G) {
+#pragma unroll
+      for (int q = 0; q < RPW; ++q)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) am[q][t] = an[q][t];
+    }
   }
-  if (active) {
+
 #pragma unroll
-    for (int c = 0; c < 8; ++c) S_T[hs + (size_t)r * D + c0 + cb + c] = s[r][cb + c];
+  for (int q = 0; q < RPW; ++q) {
+    const int rt = wave * RPW + q;
+    const f32x4 x = sS[rt][l];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S_T[hs + (size_t)(16 * rt + g4 + e) * D + col] = x[e];
   }
 }
 
