@@ -40,10 +40,11 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "3e91eacbfba1462c",
-    "segment_transfer": 1.6183e9 + 0.0367e9,
-    "segment_merge": 0.1678e9 + 0.0189e9,
-    "segment_prefill": 2.1898e9 + 0.5436e9,
+    "sources_sha": "3423df24f54a1ce8",
+    "segment_transfer": 1.4146e9 + 0.0307e9,
+    "segment_merge": 0.0295e9 + 0.0168e9,
+    "segment_prefill": 2.1689e9 + 0.5399e9,
+    "decode_step": 0.5454e9 + 0.5390e9,
 }
 
 
@@ -172,7 +173,7 @@ def bench_prefill(args, dev):
 
 
 def bench_decode(args, dev):
-    N, H, D, steps = 256, 32, 128, 1024
+    N, H, D, steps = 256, 32, 128, args.decode_steps
     print(f"[bench] generating decode inputs N={N} H={H} D={D} steps={steps}", file=sys.stderr, flush=True)
     S = ki.gen_decode_state(N, H, D, D, seed=4, device=dev)
     pool = [ki.gen_decode_step(N, H, D, D, "bf16", seed=4, step=t, device=dev) for t in range(steps)]
@@ -193,9 +194,10 @@ def bench_decode(args, dev):
     step_ms = ms / steps
     gbs = per_step_bytes / (step_ms * 1e-3) / 1e9
     del pool
+    traffic = TRAFFIC["decode_step"] if kernel_sources_sha() == TRAFFIC["sources_sha"] else None
     return dict(N=N, H=H, D=D, steps=steps, ms_total=ms, us_per_step=step_ms * 1e3,
                 tokens_per_s=N * steps / (ms * 1e-3), achieved_GBs=gbs, hbm_frac=gbs / PEAK_HBM_GBS,
-                bytes_per_step=per_step_bytes)
+                bytes_per_step=per_step_bytes, traffic_per_step=traffic)
 
 
 def bench_kcp(args, dev):
@@ -262,6 +264,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=1024,
+                    help="consecutive decode steps timed (the workload is 1024)")
     ap.add_argument("--no-kcp", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
