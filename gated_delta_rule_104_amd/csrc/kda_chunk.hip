@@ -139,20 +139,10 @@ template <typename T> struct ProdRaw {
   uint32_t beta;
 };
 
-// Value rows of one chunk for a consumer lane (accumulator layout): 16 elements,
-// two bf16 per register or one fp32 per register.
-template <typename T> struct VRegs;
-template <> struct VRegs<bf16> {
-  typedef __attribute__((ext_vector_type(2))) unsigned short us2;
-  us2 v[8];
-  __device__ __forceinline__ void set(int i, unsigned short x) { v[i >> 1][i & 1] = x; }
-  __device__ __forceinline__ float get(int i) const { return __uint_as_float((uint32_t)v[i >> 1][i & 1] << 16); }
-};
-template <> struct VRegs<float> {
-  uint32_t v[16];
-  __device__ __forceinline__ void set(int i, uint32_t x) { v[i] = x; }
-  __device__ __forceinline__ float get(int i) const { return __uint_as_float(v[i]); }
-};
+// Value rows of one chunk for a consumer lane (accumulator layout): 16 rows,
+// as loaded (bf16: the lane's two adjacent columns in one dword; fp32: one
+// value).  Kept raw so that the prefetch is not waited on until it is used.
+struct VRaw { uint32_t r[16]; };
 
 // Operand fragments.  bf16: one v_mfma_f32_16x16x32_bf16 per 32-deep k block;
 // fp32: four v_mfma_f32_16x16x4_f32 steps per 16-deep k block.  "ar" fragments
@@ -509,8 +499,9 @@ struct ChunkKernel {
     return lds_ld<typename F::A>(smem, base + o[m] + t * TSTRIDE);
   }
 
-  // Lane l holds rows 16*ti + 4*(l/16) + e of its column (accumulator layout).
-  __device__ __forceinline__ void load_v(VRegs<T>* vr, int chunk) const {
+  // Lane l holds rows 16*ti + 4*(l/16) + e of its columns (accumulator layout).
+  __device__ __forceinline__ void load_v(VRaw& vr, int chunk) const {
+    static_assert(NCT == (C::BF ? 2 : 1), "bf16 lanes own a column pair, fp32 lanes one column");
     const int ln = fresh_lane(l);
     const int g4 = 4 * (ln >> 4);
 #pragma unroll
@@ -520,20 +511,16 @@ struct ChunkKernel {
         // map columns (segment pass) read v = 0: their offset is past any buffer end
         const uint32_t off = ((uint32_t)((chunk * CH + 16 * ti + g4 + e) * D + colb) * C::ES) |
                              (isv ? 0u : 0x80000000u);
-        if constexpr (C::BF) {
-          static_assert(NCT == 2, "bf16 lanes own a column pair");
-          const uint32_t pr = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
-          vr[0].set(4 * ti + e, (unsigned short)(pr & 0xffffu));
-          vr[1].set(4 * ti + e, (unsigned short)(pr >> 16));
-        } else {
-          static_assert(NCT == 1, "fp32 lanes own one column");
-          vr[0].set(4 * ti + e, __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0));
-        }
+        vr.r[4 * ti + e] = __builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0);
       }
     }
   }
 
-  __device__ __forceinline__ float vval(const VRegs<T>& vr, int i) const { return vr.get(i); }
+  // value of row i (of 16) in column tile j
+  __device__ __forceinline__ static float vval(const VRaw& vr, int j, int i) {
+    if constexpr (C::BF) return __uint_as_float(j == 0 ? vr.r[i] << 16 : vr.r[i] & 0xffff0000u);
+    else return __uint_as_float(vr.r[i]);
+  }
 
   // With three waves per SIMD (segment pass with 8 consumer waves) registers are
   // tighter, and operand fragments are fetched in smaller batches.
@@ -543,7 +530,7 @@ struct ChunkKernel {
 
   // X_t = b_t (v_t - (Kh S)_t) for row tiles H0 .. H0+C1B-1 (fragments fetched first).
   template <int H0>
-  __device__ __forceinline__ void c1_part(const VRegs<T>* vr, uint32_t st, f32x4 (*X)[4]) {
+  __device__ __forceinline__ void c1_part(const VRaw& vr, uint32_t st, f32x4 (*X)[4]) {
     typename F::A fk[C1B][NKD];
 #pragma unroll
     for (int h = 0; h < C1B; ++h)
@@ -568,7 +555,7 @@ struct ChunkKernel {
       for (int j = 0; j < NCT; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          X[j][H0 + h][e] = bet[e] * (vval(vr[j], 4 * (H0 + h) + e) - X[j][H0 + h][e]);
+          X[j][H0 + h][e] = bet[e] * (vval(vr, j, 4 * (H0 + h) + e) - X[j][H0 + h][e]);
     }
   }
 
@@ -599,7 +586,7 @@ struct ChunkKernel {
 
   // Delta from (I + L) Delta = diag(b) (V - Kh S) by 16-row blocks:
   // Delta_i = T_ii (X_i + sum_{j<i} (-L_ij) Delta_j).
-  __device__ __forceinline__ void c1(const VRegs<T>* vr, uint32_t st) {
+  __device__ __forceinline__ void c1(const VRaw& vr, uint32_t st) {
     f32x4 X[NCT][4];
     if constexpr (TIGHT) {
       c1_kblocks<0>(st, X);
@@ -610,7 +597,7 @@ struct ChunkKernel {
 #pragma unroll
         for (int j = 0; j < NCT; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) X[j][t][e] = bet[e] * (vval(vr[j], 4 * t + e) - X[j][t][e]);
+          for (int e = 0; e < 4; ++e) X[j][t][e] = bet[e] * (vval(vr, j, 4 * t + e) - X[j][t][e]);
       }
     } else {
 #pragma unroll
@@ -736,7 +723,7 @@ struct ChunkKernel {
   }
   __device__ __forceinline__ void c3(uint32_t st) { c3_from<0>(st); }
 
-  __device__ __forceinline__ void chain(VRegs<T>* vr, int cc) {
+  __device__ __forceinline__ void chain(VRaw& vr, int cc) {
     c1(vr, stage(cc));
     if (cc + 1 < nch) load_v(vr, cc + 1);
     c2(stage(cc), cc);
@@ -767,7 +754,7 @@ struct ChunkKernel {
   }
 
   __device__ __forceinline__ void consumer_loop() {
-    VRegs<T> vr[NCT];
+    VRaw vr;
     init_offsets();
     if (nch > 0) load_v(vr, 0);
     for (int it = 0; it < nch + C::LAG; ++it) {
