@@ -736,20 +736,40 @@ struct ChunkKernel {
   // takes its share of the score tiles and diagonal inverses.  Producer waves
   // keep one set of prefetch registers, refilled as soon as the current
   // chunk's are consumed.
+  // One producer iteration: build chunk `it` from the registers in r and refill
+  // r with chunk it + PD: right away for PD = 1, and for PD = 2 once the first
+  // barrier has passed (the rest of the workgroup is then busy with the score
+  // tiles, and the data has a whole iteration to arrive).
+  template <int PD>
+  __device__ __forceinline__ void producer_step(ProdRaw<T>& r, int it) {
+    const bool w = it < nch;
+    if (w) p1(r, stage(it));
+    if (PD == 1 && it + PD < nch) load_raw(r, it + PD);
+    sync_lds();
+    if (PD == 2 && it + PD < nch) load_raw(r, it + PD);
+    if (w) p2(stage(it));
+    sync_lds();
+    if (!C::LAG) sync_lds();
+  }
+
+  // Producer inputs are prefetched two chunks ahead (two register sets, the
+  // loop unrolled by two), except in the three-waves-per-SIMD variant, which
+  // keeps one set and prefetches one chunk ahead.
   __device__ __forceinline__ void producer_loop() {
-    ProdRaw<T> r;
     init_offsets();
-    if (nch > 0) load_raw(r, 0);
-    for (int it = 0; it < nch + C::LAG; ++it) {
-      const bool w = it < nch;
-      if (w) {
-        p1(r, stage(it));
-        if (it + 1 < nch) load_raw(r, it + 1);
+    const int n = nch + C::LAG;
+    if constexpr (TIGHT) {
+      ProdRaw<T> r;
+      if (nch > 0) load_raw(r, 0);
+      for (int it = 0; it < n; ++it) producer_step<1>(r, it);
+    } else {
+      ProdRaw<T> ra, rb;
+      if (nch > 0) load_raw(ra, 0);
+      if (nch > 1) load_raw(rb, 1);
+      for (int it = 0; it < n; it += 2) {
+        producer_step<2>(ra, it);
+        if (it + 1 < n) producer_step<2>(rb, it + 1);
       }
-      sync_lds();
-      if (w) p2(stage(it));
-      sync_lds();
-      if (!C::LAG) sync_lds();
     }
   }
 
