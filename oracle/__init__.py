@@ -32,10 +32,11 @@ def load(path: str = LIB_PATH):
     dp = ctypes.POINTER(ctypes.c_double)
     i = ctypes.c_int
     lib.kda_oracle_prefill.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, i]
+    lib.kda_oracle_prefill_snap.argtypes = [i, i, i, i, i] + [dp] * 9 + [i, i]
     lib.kda_oracle_segments.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, i]
     lib.kda_oracle_merge.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp]
     lib.kda_oracle_decode_step.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i]
-    for f in (lib.kda_oracle_prefill, lib.kda_oracle_segments, lib.kda_oracle_merge,
+    for f in (lib.kda_oracle_prefill, lib.kda_oracle_prefill_snap, lib.kda_oracle_segments, lib.kda_oracle_merge,
               lib.kda_oracle_decode_step):
         f.restype = ctypes.c_int
     lib.kda_oracle_max_threads.restype = ctypes.c_int
@@ -82,6 +83,29 @@ def prefill(q, k, v, log_alpha, beta, S0=None, want_o: bool = True, nthreads: in
     if rc:
         raise RuntimeError(f"kda_oracle_prefill failed ({rc})")
     return o, ST
+
+
+def prefill_snap(q, k, v, log_alpha, beta, interval: int, S0=None, want_o: bool = True,
+                 nthreads: int = 0, lib=None):
+    """Token recurrence with state snapshots every `interval` tokens.  Returns
+    (o or None, S_T [B,H,dk,dv], snaps [B, T // interval, H, dk, dv]); snapshot j is
+    the state after the first (j + 1) * interval tokens."""
+    lib = lib or load()
+    q, k, v, la, beta, S0 = map(_f64, (q, k, v, log_alpha, beta, S0))
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    assert q.shape == k.shape == la.shape and v.shape == (B, H, T, dv) and beta.shape == (B, H, T)
+    assert interval >= 1
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    o = np.empty((B, H, T, dv)) if want_o else None
+    ST = np.empty((B, H, dk, dv))
+    snaps = np.empty((B, T // interval, H, dk, dv))
+    rc = lib.kda_oracle_prefill_snap(B, H, T, dk, dv, _p(q), _p(k), _p(v), _p(la), _p(beta), _p(S0),
+                                     _p(o), _p(ST), _p(snaps), int(interval), int(nthreads))
+    if rc:
+        raise RuntimeError(f"kda_oracle_prefill_snap failed ({rc})")
+    return o, ST, snaps
 
 
 def segments(k, v, log_alpha, beta, G: int, nthreads: int = 0, lib=None):

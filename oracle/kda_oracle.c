@@ -33,8 +33,14 @@
  * M = A_T ... A_1 with A_t = (I - beta_t k_t k_t^T) Diag(alpha_t).  The merge
  * is the plain definition S <- M_i S + S0_end_i over the segments in order.
  *
+ * State snapshots (same page and section, the prefix-cache paragraph): the KDA
+ * state of a request has a fixed size and is kept only at a sparse subset of the
+ * 512-token block boundaries used for prefix matching.  The oracle records the
+ * state after every `interval` tokens while running the same recurrence.
+ *
  * Layouts: row-major, [B][H][T][D] for per-token tensors, [B][H][T] for beta,
- * [B][H][dk][dv] for states.  All arrays are fp64.
+ * [B][H][dk][dv] for states, [B][n_snap][H][dk][dv] for snapshots.  All arrays
+ * are fp64.
  */
 #include <math.h>
 #include <stdlib.h>
@@ -47,7 +53,8 @@
  * normal build): 1 drops the decay, 2 flips the sign of the delta correction,
  * 3 reads the output from the pre-update state, 4 uses k for q in the output,
  * 5 applies the decay after the delta correction, 6 transposes the state read
- * in step 2 (uses row j instead of column j). */
+ * in step 2 (uses row j instead of column j), 7 records each snapshot one token
+ * late. */
 #ifndef KDA_ORACLE_MUTANT
 #define KDA_ORACLE_MUTANT 0
 #endif
@@ -141,6 +148,44 @@ int kda_oracle_prefill(int B, int H, int T, int dk, int dv, const double* q, con
         const size_t tk = (size_t)bh * T * dk, tv = (size_t)bh * T * dv;
         kda_head(T, dk, dv, q + tk, k + tk, v + tv, la + tk, beta + (size_t)bh * T, S,
                  o ? o + tv : NULL, u);
+        free(u);
+    }
+    return err;
+}
+
+/* Prefill with snapshots: as kda_oracle_prefill, and snap [B, T/interval, H, dk, dv]
+ * (n_snap = floor(T / interval)) receives the state after the first (j+1)*interval
+ * tokens in entry j.  interval >= 1. */
+int kda_oracle_prefill_snap(int B, int H, int T, int dk, int dv, const double* q, const double* k,
+                            const double* v, const double* la, const double* beta, const double* S0,
+                            double* o, double* S_T, double* snap, int interval, int nthreads) {
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0 || interval < 1) return 1;
+    set_threads(nthreads);
+    const int BH = B * H;
+    const int nsnap = T / interval;
+    const size_t nS = (size_t)dk * dv;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < BH; ++bh) {
+        double* u = (double*)malloc(sizeof(double) * (size_t)(dv > dk ? dv : dk));
+        if (!u) { err = 2; continue; }
+        const int b = bh / H, h = bh % H;
+        double* S = S_T + (size_t)bh * nS;
+        if (S0) memcpy(S, S0 + (size_t)bh * nS, sizeof(double) * nS);
+        else memset(S, 0, sizeof(double) * nS);
+        const size_t tk = (size_t)bh * T * dk, tv = (size_t)bh * T * dv;
+        /* tokens [t0, t1) per piece; a snapshot closes every full piece */
+        int t0 = 0;
+        for (int j = 0; j <= nsnap; ++j) {
+            int t1 = j < nsnap ? (j + 1) * interval : T;
+            if (KDA_ORACLE_MUTANT == 7 && j < nsnap && t1 < T) t1 += 1;
+            kda_head(t1 - t0, dk, dv, q + tk + (size_t)t0 * dk, k + tk + (size_t)t0 * dk,
+                     v + tv + (size_t)t0 * dv, la + tk + (size_t)t0 * dk, beta + (size_t)bh * T + t0,
+                     S, o ? o + tv + (size_t)t0 * dv : NULL, u);
+            if (j < nsnap)
+                memcpy(snap + (((size_t)b * nsnap + j) * H + h) * nS, S, sizeof(double) * nS);
+            t0 = t1;
+        }
         free(u);
     }
     return err;

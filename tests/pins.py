@@ -180,6 +180,56 @@ def pin_affine(lib, seed=5) -> float:
     return float(np.abs(S_full - (M @ S0 + S_zero)).max())
 
 
+def pin_snap_decay(lib, seed=6) -> float:
+    """Snapshots with b = 0: nothing is written, so the snapshot after the first n
+    tokens of head (b, h) is Diag(exp(sum_{t<n} log a_t)) S0[b, h], stored at
+    [b, n / interval - 1, h]."""
+    rng = np.random.default_rng(seed)
+    B, H, T, dk, dv, interval = 2, 3, 37, 4, 3, 5
+    la = -rng.random((B, H, T, dk))
+    S0 = rng.standard_normal((B, H, dk, dv))
+    q, k = rng.standard_normal((B, H, T, dk)), rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv))
+    _, ST, snaps = oracle.prefill_snap(q, k, v, la, np.zeros((B, H, T)), interval, S0, lib=lib,
+                                       nthreads=1)
+    nsnap = T // interval
+    if snaps.shape != (B, nsnap, H, dk, dv):
+        return float("inf")
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            for j in range(nsnap):
+                n = (j + 1) * interval
+                ref = np.exp(la[b, h, :n].sum(axis=0))[:, None] * S0[b, h]
+                worst = max(worst, np.abs(snaps[b, j, h] - ref).max())
+            worst = max(worst, np.abs(ST[b, h] - np.exp(la[b, h].sum(axis=0))[:, None] * S0[b, h]).max())
+    return float(worst)
+
+
+def pin_snap_overwrite(lib, seed=7) -> float:
+    """Snapshots with a = 1, b = 1 and standard basis keys k_t = e_{i_t}: each token
+    replaces row i_t of the state by v_t, so every snapshot is S0 with the rows
+    written so far replaced by their latest value (tracked here by plain row
+    bookkeeping), and o_t = S_t^T q_t."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (T, dk, dv, interval) in [(11, 4, 3, 1), (20, 6, 5, 3), (16, 8, 2, 16)]:
+        idx = rng.integers(0, dk, size=T)
+        k = np.eye(dk)[idx]
+        q, v = rng.standard_normal((T, dk)), rng.standard_normal((T, dv))
+        S0 = rng.standard_normal((dk, dv))
+        o, _, snaps = oracle.prefill_snap(q[None, None], k[None, None], v[None, None],
+                                          np.zeros((1, 1, T, dk)), np.ones((1, 1, T)), interval,
+                                          S0[None, None], lib=lib, nthreads=1)
+        rows = S0.copy()
+        for t in range(T):
+            rows[idx[t]] = v[t]
+            worst = max(worst, np.abs(o[0, 0, t] - rows.T @ q[t]).max())
+            if (t + 1) % interval == 0:
+                worst = max(worst, np.abs(snaps[0, (t + 1) // interval - 1, 0] - rows).max())
+    return float(worst)
+
+
 ALL_PINS = {
     "product_sum": (pin_product_sum, 1e-12),
     "exact_rational": (pin_exact_rational, 1e-12),
@@ -188,4 +238,6 @@ ALL_PINS = {
     "replacement": (pin_replacement, 1e-12),
     "scalar": (pin_scalar, 1e-14),
     "affine": (pin_affine, 1e-12),
+    "snap_decay": (pin_snap_decay, 1e-13),
+    "snap_overwrite": (pin_snap_overwrite, 1e-13),
 }

@@ -86,11 +86,37 @@ def test_empty_sequence(oracle_lib):
     assert o.shape == (1, 1, 0, 3) and np.array_equal(ST, S0)
 
 
-@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6])
+def test_snapshots_match_prefix_runs(oracle_lib):
+    """Snapshot j equals the end state of the same recurrence run on the first
+    (j + 1) * interval tokens alone; with T a multiple of the interval the last
+    snapshot is S_T."""
+    rng = np.random.default_rng(15)
+    B, H, T, dk, dv, interval = 2, 2, 24, 5, 4, 6
+    q, k = rng.standard_normal((B, H, T, dk)), rng.standard_normal((B, H, T, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, H, T, dv))
+    la = -0.2 * rng.random((B, H, T, dk))
+    beta = rng.random((B, H, T))
+    S0 = rng.standard_normal((B, H, dk, dv))
+    o, ST, snaps = oracle.prefill_snap(q, k, v, la, beta, interval, S0, lib=oracle_lib)
+    o_ref, ST_ref = oracle.prefill(q, k, v, la, beta, S0, lib=oracle_lib)
+    assert np.array_equal(o, o_ref) and np.array_equal(ST, ST_ref)
+    assert np.array_equal(snaps[:, -1], ST)
+    for j in range(T // interval):
+        n = (j + 1) * interval
+        _, Sj = oracle.prefill(q[:, :, :n], k[:, :, :n], v[:, :, :n], la[:, :, :n], beta[:, :, :n],
+                               S0, lib=oracle_lib)
+        assert np.array_equal(snaps[:, j], Sj)
+    _, _, none = oracle.prefill_snap(q[:, :, :5], k[:, :, :5], v[:, :, :5], la[:, :, :5],
+                                     beta[:, :, :5], interval, S0, lib=oracle_lib)
+    assert none.shape == (B, 0, H, dk, dv)
+
+
+@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6, 7])
 def test_planted_mistakes_are_caught(tmp_path, mutant):
     """Each planted mistake (dropped decay, flipped delta sign, pre-update output,
-    k in place of q, decay after the write, transposed state read) makes at least
-    one pin fail."""
+    k in place of q, decay after the write, transposed state read, snapshot one
+    token late) makes at least one pin fail."""
     path = build_oracle.build(str(tmp_path / f"mut{mutant}.so"), mutant=mutant)
     lib = oracle.load(path)
     failed = []
