@@ -8,6 +8,7 @@ library is missing, loading fails with an error that says how to build it.
 
 Entry points (same names as the C-ABI):
     prefill(q, k, v, log_alpha, beta, S0=None)        -> (o, S_T)
+    prefill_snap(q, k, v, log_alpha, beta, snap_interval, S0=None) -> (o, S_T, S_snap)
     prefill_plan(B, H, T, dk, dv, dtype)               -> (G, Tseg)
     prefill_segments(q, k, v, log_alpha, beta, S_start, Tseg) -> (o, S_T)
     decode_step(q, k, v, log_alpha, beta, S)           -> o          (S updated in place)
@@ -50,6 +51,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.kda_chunk_prefill.argtypes = [vp] * 8 + [i] * 6 + [vp, ctypes.c_size_t, vp]
+    lib.kda_chunk_prefill_snap.argtypes = [vp] * 9 + [i] * 7 + [vp, ctypes.c_size_t, vp]
     lib.kda_prefill_workspace_bytes.argtypes = [i] * 6
     lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_prefill_plan.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 2
@@ -57,7 +59,7 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
     lib.kda_segment_transfer.argtypes = [vp] * 6 + [i] * 7 + [vp]
     lib.kda_segment_merge.argtypes = [vp] * 5 + [i] * 5 + [vp]
-    for f in (lib.kda_chunk_prefill, lib.kda_prefill_plan, lib.kda_chunk_prefill_segments,
+    for f in (lib.kda_chunk_prefill, lib.kda_chunk_prefill_snap, lib.kda_prefill_plan, lib.kda_chunk_prefill_segments,
               lib.kda_decode_step, lib.kda_segment_transfer, lib.kda_segment_merge):
         f.restype = i
     lib.kda_status_string.argtypes = [i]
@@ -132,6 +134,46 @@ def prefill(q, k, v, log_alpha, beta, S0=None, o=None, S_T=None,
                                   ws_bytes, _stream())
     _check(rc, "kda_chunk_prefill")
     return o, S_T
+
+
+def prefill_snap(q, k, v, log_alpha, beta, snap_interval: int, S0=None, o=None, S_T=None,
+                 S_snap=None, workspace="auto"):
+    """Chunked prefill that also returns state snapshots for prefix caching:
+    S_snap [B, T // snap_interval, H, dk, dv] fp32, entry [b, j, h] being the state
+    after the first (j + 1) * snap_interval tokens (snap_interval: a positive
+    multiple of 64).  Returns (o, S_T, S_snap); o and S_T are those of prefill()."""
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dt = k.dtype
+    if dt not in _DT:
+        raise KdaError(f"unsupported dtype {dt}")
+    if snap_interval <= 0 or snap_interval % 64:
+        raise KdaError(f"snap_interval must be a positive multiple of 64 (got {snap_interval})")
+    for name, t, shp in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                         ("log_alpha", log_alpha, (B, H, T, dk)), ("beta", beta, (B, H, T))):
+        _io(t, name, dt, shp)
+    if S0 is not None:
+        _io(S0, "S0", torch.float32, (B, H, dk, dv))
+    nsnap = T // snap_interval
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=k.device)
+    if S_T is None:
+        S_T = torch.empty(B, H, dk, dv, dtype=torch.float32, device=k.device)
+    if S_snap is None:
+        S_snap = torch.empty(B, nsnap, H, dk, dv, dtype=torch.float32, device=k.device)
+    _io(o, "o", dt, (B, H, T, dv))
+    _io(S_T, "S_T", torch.float32, (B, H, dk, dv))
+    _io(S_snap, "S_snap", torch.float32, (B, nsnap, H, dk, dv))
+    if isinstance(workspace, str):
+        nbytes = prefill_workspace_bytes(B, H, T, dk, dv, dt)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=k.device) if nbytes else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().kda_chunk_prefill_snap(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                       _ptr(S0), _ptr(o), _ptr(S_T), _ptr(S_snap) if nsnap else None,
+                                       snap_interval, B, H, T, dk, dv, _DT[dt], _ptr(workspace),
+                                       ws_bytes, _stream())
+    _check(rc, "kda_chunk_prefill_snap")
+    return o, S_T, S_snap
 
 
 def prefill_plan(B: int, H: int, T: int, dk: int, dv: int, dtype: torch.dtype) -> Tuple[int, int]:

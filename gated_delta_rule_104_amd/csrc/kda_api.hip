@@ -154,10 +154,17 @@ kda_status check_seq_bytes(long long T, int dk, kda_dtype dt) {
 // Prefill of G = ceil(T / Tseg) consecutive segments of every head, each from its
 // own start state (Sst: [G, BH, D, D] or null for zero); S_T receives the end
 // state of the last segment.
+struct Snap {
+  float* p = nullptr;  // [B, nsnap, H, D, D] or null
+  int chunks = 0;      // chunks per snapshot interval
+  int n = 0;
+  int H = 1;
+};
+
 kda_status launch_segment_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
                                   const void* beta, const float* Sst, void* o, float* S_T,
                                   long long BH, int T, int Tseg, int D, bool bf, hipStream_t stream,
-                                  const char* what) {
+                                  const char* what, const Snap& sn = Snap()) {
   const int G = T > 0 ? (int)(((long long)T + Tseg - 1) / Tseg) : 1;  // T = 0: copy the start state
   const long long nseq = BH * G;
   const int nt = D / 16, nc = pick_nc(nseq, nt, bf);
@@ -165,6 +172,8 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
   a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
   a.S0 = Sst; a.o = o; a.S_out = S_T; a.M_out = nullptr;
   a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = T; a.vsplit = nt / (nc * kda::chunk_tiles_per_wave(bf));
+  a.snap = sn.n > 0 ? sn.p : nullptr; a.snap_chunks = sn.chunks > 0 ? sn.chunks : 1;
+  a.nsnap = sn.n; a.H = sn.H;
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (getenv("KDA_LOG"))
@@ -238,16 +247,28 @@ kda_status kda_prefill_plan(int B, int H, int T, int dk, int dv, kda_dtype dtype
   return ok();
 }
 
-kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
-                             const void* beta, const float* S0, void* o, float* S_T, int B, int H,
-                             int T, int dk, int dv, kda_dtype dtype, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, const void* log_alpha,
+                                  const void* beta, const float* S0, void* o, float* S_T,
+                                  float* S_snap, int snap_interval, int B, int H, int T, int dk,
+                                  int dv, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
   kda_status st = check_prefill_args(q, k, v, log_alpha, beta, o, S_T, B, H, T, dk, dv, dtype);
   if (st != KDA_OK) return st;
+  if (snap_interval < 0 || snap_interval % 64)
+    return fail(KDA_ERR_SHAPE, "snap_interval must be 0 or a positive multiple of 64 (got %d)",
+                snap_interval);
   const long long BH = (long long)B * H;
   if (BH == 0) return ok();
   KDA_OPTIONAL(S0, "S0");
   KDA_OPTIONAL(workspace, "workspace");
+  Snap sn;
+  if (snap_interval > 0 && T / snap_interval > 0) {
+    KDA_REQUIRE(S_snap, "S_snap");
+    sn.p = S_snap;
+    sn.chunks = snap_interval / 64;
+    sn.n = T / snap_interval;
+    sn.H = H;
+  }
   const bool bf = dtype == KDA_BF16;
   const int D = dk;
   const PrefillPlan pl = plan_prefill(BH, T, D, dtype);
@@ -280,13 +301,22 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
         hipSuccess)
       return hip_fail(e, "kda_chunk_prefill merge");
     // 3. prefill of every segment from its start state
+    // (plan_prefill makes Tseg a multiple of the chunk length, as snapshots need)
     st = launch_segment_prefill(q, k, v, log_alpha, beta, Sst, o, S_T, BH, T, pl.Tseg, D, bf, stream,
-                                "kda_chunk_prefill segment prefill");
+                                "kda_chunk_prefill segment prefill", sn);
     return st == KDA_OK ? ok() : st;
   }
   st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, o, S_T, BH, T, T > 0 ? T : 1, D, bf,
-                              stream, "kda_chunk_prefill");
+                              stream, "kda_chunk_prefill", sn);
   return st == KDA_OK ? ok() : st;
+}
+
+kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* beta, const float* S0, void* o, float* S_T, int B, int H,
+                             int T, int dk, int dv, kda_dtype dtype, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return kda_chunk_prefill_snap(q, k, v, log_alpha, beta, S0, o, S_T, nullptr, 0, B, H, T, dk, dv,
+                                dtype, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_chunk_prefill_segments(const void* q, const void* k, const void* v,

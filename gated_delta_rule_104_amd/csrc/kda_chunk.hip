@@ -41,6 +41,12 @@
 //
 // Segment mode runs the same chain on the augmented state [S | M] started at
 // [0 | I] (columns >= dv see v = 0), skips q, P and O, and writes S and M.
+//
+// Prefill can also write the state at every snapshot boundary (a multiple of
+// the chunk length, counted over the head's whole sequence): the KDA state of a
+// request is kept only at a sparse subset of the 512-token prefix-cache block
+// boundaries ("Kimi K3 开源日来了", section "针对适配的 Infra").  The consumer
+// waves store their columns of S right after the chunk that closes a boundary.
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -200,6 +206,8 @@ struct ChunkKernel {
   ChunkArgs a;
   rsrc_t rq, rk, rv, rla, rbeta, ro;
   int Tlen, nch;
+  int chunk0;        // chunks of the head's sequence before this segment
+  float* snap_head;  // snapshot 0 of this head (prefill with snapshots), else null
   int wave, l;
   // consumer: NCT adjacent 16-column tiles of the state, sharing every A fragment
   static constexpr int NCT = C::NCT;
@@ -723,11 +731,45 @@ struct ChunkKernel {
   }
   __device__ __forceinline__ void c3(uint32_t st) { c3_from<0>(st); }
 
+  // This lane's entries of the state, at row r, columns c .. c + NCT - 1 of a
+  // D x D fp32 matrix at dst.
+  __device__ __forceinline__ void store_state(float* dst, int c) const {
+    const rsrc_t r = make_rsrc(dst, D * D * 4);
+    const uint32_t vo = (uint32_t)(4 * (l >> 4) * D + c) * 4;  // the lane's first entry
+#pragma unroll
+    for (int ci = 0; ci < D / 16; ++ci)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int so = (16 * ci + e) * D * 4;
+        if constexpr (NCT == 2) {
+          const u32x2 x = {__float_as_uint(S[0][ci][e]), __float_as_uint(S[1][ci][e])};
+          __builtin_amdgcn_raw_buffer_store_b64(x, r, vo, so, 0);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NCT; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[j][ci][e]), r, vo + 4 * j, so, 0);
+        }
+      }
+  }
+
+  // Snapshot after chunk cc when it closes a snapshot interval of the sequence.
+  __device__ __forceinline__ void snapshot(int cc) const {
+    if constexpr (PREFILL) {
+      if (!snap_head) return;
+      const int gc = chunk0 + cc + 1;
+      if (gc % a.snap_chunks) return;
+      const int j = gc / a.snap_chunks - 1;
+      if (j >= a.nsnap) return;  // a ragged last chunk ends short of the boundary
+      store_state(snap_head + (size_t)j * a.H * D * D, colb);
+    }
+  }
+
   __device__ __forceinline__ void chain(VRaw& vr, int cc) {
     c1(vr, stage(cc));
     if (cc + 1 < nch) load_v(vr, cc + 1);
     c2(stage(cc), cc);
     c3(stage(cc));
+    snapshot(cc);
   }
 
   // Pipeline.  Iteration `it` prepares chunk it and runs the serial chain of
@@ -803,6 +845,12 @@ struct ChunkKernel {
     const size_t tok0 = (size_t)bh * a.Ttot + (size_t)gseg * a.Tseg;
     Tlen = min(a.Tseg, a.Ttot - gseg * a.Tseg);
     nch = (Tlen + CH - 1) / CH;
+    chunk0 = gseg * (a.Tseg / CH);
+    snap_head = nullptr;
+    if (PREFILL && a.snap) {
+      const int b = bh / a.H, h = bh - b * a.H;
+      snap_head = a.snap + ((size_t)b * a.nsnap * a.H + h) * D * D;
+    }
     wave = threadIdx.x >> 6;
     l = lane_id();
     const int g4 = 4 * (l >> 4);
@@ -861,12 +909,7 @@ struct ChunkKernel {
       dst = a.M_out + sbase;
       c = colb - D;
     }
-#pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int ci = 0; ci < D / 16; ++ci)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ci + g4 + e) * D + c + j] = S[j][ci][e];
+    store_state(dst, c);
   }
 };
 

@@ -26,6 +26,13 @@ struct ChunkArgs {
   int Tseg;         // tokens per segment (the last one may be shorter)
   int Ttot;         // tokens per head
   int vsplit;       // workgroups per sequence (each owns 16 * nc * chunk_tiles_per_wave columns)
+  // prefill only: state snapshots [B, nsnap, H, D, D] after every snap_chunks
+  // chunks of a head's whole sequence (null: none).  With snapshots and G > 1,
+  // Tseg must be a multiple of the chunk length.
+  float* snap = nullptr;
+  int snap_chunks = 1;
+  int nsnap = 0;
+  int H = 1;        // heads per sequence batch entry (bh = b * H + h)
 };
 
 // 16-column state tiles each consumer wave of the chunk kernel owns.

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
   KDA_OK = 0,
@@ -85,6 +85,31 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                              const void* beta, const float* S0, void* o, float* S_T, int B, int H,
                              int T, int dk, int dv, kda_dtype dtype, void* workspace,
                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_prefill that also keeps state snapshots for prefix caching.  The
+ * KDA state of a request has a fixed size and is stored only at a sparse subset
+ * of the 512-token block boundaries that prefix matching uses ("Kimi K3
+ * 开源日来了", section "针对适配的 Infra", prefix-cache paragraph); a cache hit
+ * then resumes from the longest stored boundary.
+ *   snap_interval : tokens between snapshots, a positive multiple of 64 (the
+ *                   chunk length; 512 or a multiple of it in the pages' use), or
+ *                   0 for none
+ *   S_snap        : [B, T / snap_interval, H, dk, dv] fp32 (floor division):
+ *                   entry [b, j, h] is head (b, h)'s state after its first
+ *                   (j + 1) * snap_interval tokens.  Required (16-byte aligned)
+ *                   when that count is nonzero, ignored otherwise; must not
+ *                   overlap any other argument.
+ * Every other argument, the workspace and the paths taken are as for
+ * kda_chunk_prefill, whose outputs this call reproduces bit for bit.
+ * Errors: KDA_ERR_SHAPE for a negative interval or one that is not a multiple
+ * of 64; the rest as for kda_chunk_prefill.
+ */
+kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, const void* log_alpha,
+                                  const void* beta, const float* S0, void* o, float* S_T,
+                                  float* S_snap, int snap_interval, int B, int H, int T, int dk,
+                                  int dv, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /*
  * The segmentation kda_chunk_prefill would use for this shape when given

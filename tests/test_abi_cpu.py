@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     for st in range(6):
         assert lib.kda_status_string(st)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -104,6 +104,25 @@ def test_prefill_plan(lib):
     assert plan(1, 32, 65536, 128, 128, F32) == OK and G.value == 1
     assert plan(1, 32, 100, 96, 96, BF16) == ERR_UNSUPPORTED
     assert lib.kda_prefill_plan(1, 1, 64, 64, 64, BF16, None, ctypes.byref(Ts)) == ERR_NULL
+
+
+def test_prefill_snap_validation(lib):
+    """Snapshot interval: 0 (none) or a positive multiple of the 64-token chunk;
+    the snapshot buffer is required only when at least one snapshot falls in T."""
+    f = lib.kda_chunk_prefill_snap
+    args = lambda **kw: [*P(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, kw.get("snap", FAKE)),
+                         kw.get("iv", 512), 1, 2, kw.get("T", 1024), 128, 128, BF16, None, 0, None]
+    assert f(*args(iv=-64)) == ERR_SHAPE
+    assert f(*args(iv=100)) == ERR_SHAPE
+    assert b"multiple of 64" in lib.kda_last_error()
+    assert f(*args(snap=None)) == ERR_NULL
+    assert f(*args(snap=FAKE + 8)) == ERR_ALIGN
+    # T = 0 with any valid interval and no heads: nothing to launch
+    assert f(*[*P(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None), 512, 0, 2, 1024, 128, 128,
+               BF16, None, 0, None]) == OK
+    # shape errors of the plain prefill come first
+    assert f(*[*P(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE), 512, 1, 2, 1024, 128, 64,
+               BF16, None, 0, None]) == ERR_SHAPE
 
 
 def test_prefill_segments_validation(lib):

@@ -400,3 +400,67 @@ def test_prefill_split_without_workspace_falls_back(monkeypatch):
     o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
     assert oracle.max_rel_l2(o.cpu(), o_ref) <= TOL["bf16"]
     assert oracle.max_rel_l2(S_T.cpu(), S_ref) <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------- state snapshots
+
+def run_snap_case(B, H, T, D, dtype, interval, seed, variant="slow", split=None, monkeypatch=None):
+    print(f"[case] snapshots B={B} H={H} T={T} D={D} {dtype} every {interval} split={split} {variant}",
+          flush=True)
+    if split is not None:
+        monkeypatch.setenv("KDA_SPLIT", str(split))
+    d = ki.gen_prefill(B, H, T, D, D, dtype, seed=seed, s0_std=0.1, variant=variant)
+    g = to_dev(d)
+    o, S_T, snaps = kda.prefill_snap(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], interval, g["S0"])
+    o1, S1 = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
+    torch.cuda.synchronize()
+    # the snapshots ride along: outputs and end state are those of the plain call
+    assert torch.equal(o, o1) and torch.equal(S_T, S1)
+    assert snaps.shape == (B, T // interval, H, D, D)
+    _, _, snap_ref = oracle.prefill_snap(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], interval,
+                                         d["S0"], want_o=False)
+    es = oracle.max_rel_l2(snaps.cpu(), snap_ref, lead=3, floor=1e-6) if T >= interval else 0.0
+    print(f"    snapshots {es:.3e}", flush=True)
+    if T % interval == 0 and T > 0:
+        assert torch.equal(snaps[:, -1], S_T)
+    return es
+
+
+@pytest.mark.parametrize("B,H,T,D,dtype,interval", [
+    (2, 3, 1000, 128, "bf16", 128), (1, 2, 640, 64, "bf16", 64), (1, 2, 63, 128, "bf16", 64),
+    (2, 2, 300, 64, "f32", 128), (1, 1, 1536, 128, "bf16", 512)])
+def test_prefill_snapshots(B, H, T, D, dtype, interval):
+    """Snapshots every `interval` tokens against the oracle's, ragged tails,
+    one snapshot per chunk, and none at all (T < interval)."""
+    es = run_snap_case(B, H, T, D, dtype, interval, seed=500 + T)
+    assert es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("P,T,interval", [(3, 1000, 128), (4, 2148, 512), (2, 700, 64)])
+def test_prefill_snapshots_sequence_split(P, T, interval, monkeypatch):
+    """On the sequence-split path each segment's workgroups write the snapshots
+    that fall inside the segment; boundaries on segment ends come from the
+    segment that ends there."""
+    es = run_snap_case(1, 3, T, 128, "bf16", interval, seed=520 + P, split=P, monkeypatch=monkeypatch)
+    assert es <= TOL["bf16"]
+
+
+def test_full_h32_t64k_snapshots():
+    """The headline workload with a snapshot every 512 tokens (128 per head):
+    outputs and end state bit-identical to the plain call, the last snapshot equal
+    to S_T, and every snapshot of sampled heads against the oracle's."""
+    print("[case] full h32_t64k snapshots every 512", flush=True)
+    B, H, T, D, iv = 1, 32, 65536, 128, 512
+    g = gpu_inputs(B, H, T, D, seed=2)
+    o, S_T, snaps = kda.prefill_snap(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], iv, None)
+    o1, S1 = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o1) and torch.equal(S_T, S1) and torch.equal(snaps[:, -1], S_T)
+    del o1, S1
+    heads = (6, 29)
+    sl = lambda t: t[:, list(heads)].cpu()
+    _, _, ref = oracle.prefill_snap(sl(g["q"]), sl(g["k"]), sl(g["v"]), sl(g["log_alpha"]),
+                                    sl(g["beta"]), iv, None, want_o=False)
+    es = oracle.max_rel_l2(snaps[:, :, list(heads)].cpu(), ref, lead=3, floor=1e-6)
+    print(f"    snapshots of heads {heads}: {es:.3e}", flush=True)
+    assert es <= TOL["bf16"]
