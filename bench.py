@@ -40,11 +40,11 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "3423df24f54a1ce8",
-    "segment_transfer": 1.4146e9 + 0.0307e9,
+    "sources_sha": "feda59e7c47d0156",
+    "segment_transfer": 1.4133e9 + 0.0294e9,
     "segment_merge": 0.0295e9 + 0.0168e9,
-    "segment_prefill": 2.1689e9 + 0.5399e9,
-    "decode_step": 0.5454e9 + 0.5390e9,
+    "segment_prefill": 2.1690e9 + 0.5390e9,
+    "decode_step": 0.5455e9 + 0.5390e9,
 }
 
 
@@ -172,6 +172,36 @@ def bench_prefill(args, dev):
     return dict(B=B, H=H, T=T, D=D, mean_ms=mean_ms, wall_ms=wall_ms, per=per, g=g, ws_bytes=nws)
 
 
+def bench_snapshots(pf, args, interval=512):
+    """The same prefill with a state snapshot every `interval` tokens (prefix
+    caching): time per call, the snapshot bytes written, and the cost over the
+    plain call measured in the same run."""
+    g = pf["g"]
+    B, H, T, D = pf["B"], pf["H"], pf["T"], pf["D"]
+    dev = g["k"].device
+    nsnap = T // interval
+    o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    snaps = torch.empty(B, nsnap, H, D, D, dtype=torch.float32, device=dev)
+    ws = torch.empty(pf["ws_bytes"], dtype=torch.uint8, device=dev) if pf["ws_bytes"] else None
+
+    def snap():
+        kda.prefill_snap(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], interval, None, o=o, S_T=S_T,
+                         S_snap=snaps, workspace=ws)
+
+    def plain():
+        kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None, o=o, S_T=S_T, workspace=ws)
+
+    snap(); plain()
+    torch.cuda.synchronize()
+    n = max(5, args.steps)
+    ms, _ = time_launches(snap, n)
+    base, _ = time_launches(plain, n)
+    del snaps
+    return {"interval": interval, "snapshots_per_head": nsnap, "ms": ms, "plain_ms": base,
+            "overhead": ms / base - 1.0, "snapshot_bytes": B * H * nsnap * D * D * 4}
+
+
 def bench_decode(args, dev):
     N, H, D, steps = 256, 32, 128, args.decode_steps
     print(f"[bench] generating decode inputs N={N} H={H} D={D} steps={steps}", file=sys.stderr, flush=True)
@@ -267,6 +297,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1024,
                     help="consecutive decode steps timed (the workload is 1024)")
     ap.add_argument("--no-kcp", action="store_true")
+    ap.add_argument("--no-snap", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -340,6 +371,9 @@ def main():
     }
     if dec is not None:
         out["prefill_kernels"] = dec
+    if not args.no_snap:
+        out["snapshots"] = bench_snapshots(pf, args)
+        torch.cuda.empty_cache()
     if not args.no_decode:
         out["decode"] = bench_decode(args, dev)
         torch.cuda.empty_cache()
