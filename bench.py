@@ -108,68 +108,69 @@ def segment_prefill_bytes(B, H, T, D, G):
     return B * H * T * (2 * 5 * D + 2) + G * B * H * D * D * 4 + B * H * D * D * 4
 
 
+def direct_part_bytes(B, H, T0, D):
+    """Direct prefill of the first T0 tokens: q, k, log_alpha, v, beta read and o
+    written once, its end state written (from a zero start, nothing read)."""
+    return B * H * T0 * (2 * 5 * D + 2) + B * H * D * D * 4
+
+
 def bench_decomposition(pf, args):
-    """Per-kernel durations of the sequence-split prefill, through the three public
-    calls it is made of, with the same launch shapes as kda_chunk_prefill: the
-    segment pass over the first G-1 segments (the last one's zero-start state and
-    map are not needed), the merge of those, and the prefill of all G segments."""
+    """Per-kernel durations of the sequence-split prefill, through the public calls
+    it is made of, with the same launch shapes as kda_chunk_prefill: the direct
+    prefill of the first T0 tokens (one workgroup per head), the segment pass over
+    the G-1 segments after it (the last segment's zero-start state and map are not
+    needed), the merge of those from the direct part's end state, and the prefill
+    of all G segments.  Inside kda_chunk_prefill the first two run side by side."""
     g = pf["g"]
     B, H, T, D = pf["B"], pf["H"], pf["T"], pf["D"]
-    G, Tseg = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
+    T0, G, Tseg = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
     if G == 1:
         return None
-    assert G * Tseg == T, "decomposition timing needs T to be a multiple of the segment length"
     dev = g["k"].device
-    T1 = (G - 1) * Tseg
-    lead = {n: g[n][:, :, :T1].contiguous() for n in ("k", "v", "log_alpha", "beta")}
+    T1 = T0 + (G - 1) * Tseg
+    names = ("q", "k", "v", "log_alpha", "beta")
+    head = {n: g[n][:, :, :T0].contiguous() for n in names}
+    mid = {n: g[n][:, :, T0:T1].contiguous() for n in names[1:]}
+    tail = {n: g[n][:, :, T0:].contiguous() for n in names}
     Z = torch.empty(G - 1, B, H, D, D, dtype=torch.float32, device=dev)
     M = torch.empty_like(Z)
+    S1 = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
     S_start = torch.empty(G, B, H, D, D, dtype=torch.float32, device=dev)
     S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
-    o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
+    o0 = torch.empty(B, H, T0, D, dtype=torch.bfloat16, device=dev)
+    o1 = torch.empty(B, H, T - T0, D, dtype=torch.bfloat16, device=dev)
+
+    def direct():
+        # the call's own choice for this part: 4 consumer waves, one workgroup per head
+        os.environ["KDA_NC"] = "4"
+        try:
+            kda.prefill(head["q"], head["k"], head["v"], head["log_alpha"], head["beta"], None, o=o0, S_T=S1,
+                        workspace=None)
+        finally:
+            del os.environ["KDA_NC"]
+
     parts = {
-        "segment_transfer": (lambda: kda.segment_transfer(lead["k"], lead["v"], lead["log_alpha"], lead["beta"],
+        "direct_part": (direct, direct_part_bytes(B, H, T0, D)),
+        "segment_transfer": (lambda: kda.segment_transfer(mid["k"], mid["v"], mid["log_alpha"], mid["beta"],
                                                           G - 1, S_zero_end=Z, M=M),
-                             segment_pass_bytes(B, H, T1, D, G - 1)),
-        "segment_merge": (lambda: kda.segment_merge(Z, M, None, S_start=S_start[: G - 1], S_T=S_start[G - 1]),
-                          merge_bytes(B, H, D, G - 1)),
-        "segment_prefill": (lambda: kda.prefill_segments(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"],
-                                                         S_start, Tseg, o=o, S_T=S_T),
-                            segment_prefill_bytes(B, H, T, D, G)),
+                             segment_pass_bytes(B, H, T1 - T0, D, G - 1)),
+        "segment_merge": (lambda: kda.segment_merge(Z, M, S1, S_start=S_start[: G - 1], S_T=S_start[G - 1]),
+                          merge_bytes(B, H, D, G - 1) + B * H * D * D * 4),
+        "segment_prefill": (lambda: kda.prefill_segments(tail["q"], tail["k"], tail["v"], tail["log_alpha"],
+                                                         tail["beta"], S_start, Tseg, o=o1, S_T=S_T),
+                            segment_prefill_bytes(B, H, T - T0, D, G)),
     }
     for fn, _ in parts.values():
         fn()
     torch.cuda.synchronize()
-    res = {"G": G, "Tseg": Tseg}
+    res = {"T0": T0, "G": G, "Tseg": Tseg}
     n = max(5, args.steps)
     for name, (fn, nbytes) in parts.items():
         # each launch alone between events on the stream it runs on
         ms, _ = time_launches(fn, n)
         res[name] = {"ms": ms, "algorithmic_bytes": nbytes, "GBs": nbytes / (ms * 1e-3) / 1e9}
-    del lead
+    del head, mid, tail
     return res
-
-
-def bench_prefill(args, dev):
-    B, H, T, D = 1, 32, 65536, 128
-    print(f"[bench] generating prefill inputs B={B} H={H} T={T} D={D} bf16", file=sys.stderr, flush=True)
-    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=2, device=dev)
-    o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
-    S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
-    nws = kda.prefill_workspace_bytes(B, H, T, D, D, torch.bfloat16)
-    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
-
-    def step():
-        kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None, o=o, S_T=S_T, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    mean_ms, per = time_launches(step, args.steps)
-    t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    return dict(B=B, H=H, T=T, D=D, mean_ms=mean_ms, wall_ms=wall_ms, per=per, g=g, ws_bytes=nws)
 
 
 def bench_snapshots(pf, args, interval=512):
@@ -331,13 +332,14 @@ def main():
     fl_tri = prefill_flops(B, H, T, D, triangle=True)
     dec = bench_decomposition(pf, args)
     if dec is not None:
-        names = ("segment_transfer", "segment_merge", "segment_prefill")
-        kern = {"segment_transfer": "kda_chunk_kernel<bf16,128,8,segment>",
+        names = ("direct_part", "segment_transfer", "segment_merge", "segment_prefill")
+        kern = {"direct_part": "kda_chunk_kernel<bf16,128,4,prefill> (first part, one workgroup per head)",
+                "segment_transfer": "kda_chunk_kernel<bf16,128,8,segment>",
                 "segment_merge": "kda_merge_kernel<128>",
                 "segment_prefill": "kda_chunk_kernel<bf16,128,4,prefill>"}
         dom = max(names, key=lambda n: dec[n]["ms"])
         r = dec[dom]
-        traffic = TRAFFIC[dom] if kernel_sources_sha() == TRAFFIC["sources_sha"] else None
+        traffic = TRAFFIC.get(dom) if kernel_sources_sha() == TRAFFIC["sources_sha"] else None
         roofline = {"bound": "hbm", "achieved": r["GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": r["GBs"] / PEAK_HBM_GBS, "traffic": traffic, "kernel": kern[dom],
                     "kernel_ms": r["ms"], "algorithmic_bytes": r["algorithmic_bytes"],

@@ -9,7 +9,7 @@ library is missing, loading fails with an error that says how to build it.
 Entry points (same names as the C-ABI):
     prefill(q, k, v, log_alpha, beta, S0=None)        -> (o, S_T)
     prefill_snap(q, k, v, log_alpha, beta, snap_interval, S0=None) -> (o, S_T, S_snap)
-    prefill_plan(B, H, T, dk, dv, dtype)               -> (G, Tseg)
+    prefill_plan(B, H, T, dk, dv, dtype)               -> (T0, G, Tseg)
     prefill_segments(q, k, v, log_alpha, beta, S_start, Tseg) -> (o, S_T)
     decode_step(q, k, v, log_alpha, beta, S)           -> o          (S updated in place)
     segment_transfer(k, v, log_alpha, beta, G)         -> (S_zero_end, M)
@@ -54,7 +54,7 @@ def load() -> ctypes.CDLL:
     lib.kda_chunk_prefill_snap.argtypes = [vp] * 9 + [i] * 7 + [vp, ctypes.c_size_t, vp]
     lib.kda_prefill_workspace_bytes.argtypes = [i] * 6
     lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
-    lib.kda_prefill_plan.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 2
+    lib.kda_prefill_plan.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 3
     lib.kda_chunk_prefill_segments.argtypes = [vp] * 8 + [i] * 7 + [vp]
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
     lib.kda_segment_transfer.argtypes = [vp] * 6 + [i] * 7 + [vp]
@@ -176,14 +176,15 @@ def prefill_snap(q, k, v, log_alpha, beta, snap_interval: int, S0=None, o=None, 
     return o, S_T, S_snap
 
 
-def prefill_plan(B: int, H: int, T: int, dk: int, dv: int, dtype: torch.dtype) -> Tuple[int, int]:
-    """(G, Tseg): the segmentation kda_chunk_prefill uses with its workspace (G == 1: single pass)."""
+def prefill_plan(B: int, H: int, T: int, dk: int, dv: int, dtype: torch.dtype) -> Tuple[int, int, int]:
+    """(T0, G, Tseg): the cut kda_chunk_prefill uses with its workspace: a first
+    part of T0 tokens, then G segments of Tseg tokens (T0 == 0, G == 1: single pass)."""
     if dtype not in _DT:
         raise KdaError(f"unsupported dtype {dtype}")
-    G, Tseg = ctypes.c_int(0), ctypes.c_int(0)
-    _check(load().kda_prefill_plan(B, H, T, dk, dv, _DT[dtype], ctypes.byref(G), ctypes.byref(Tseg)),
-           "kda_prefill_plan")
-    return G.value, Tseg.value
+    T0, G, Tseg = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().kda_prefill_plan(B, H, T, dk, dv, _DT[dtype], ctypes.byref(T0), ctypes.byref(G),
+                                   ctypes.byref(Tseg)), "kda_prefill_plan")
+    return T0.value, G.value, Tseg.value
 
 
 def prefill_segments(q, k, v, log_alpha, beta, S_start, Tseg: int, o=None, S_T=None):

@@ -81,42 +81,95 @@ int pick_nc(long long nseq, int ncol_tiles, bool bf16_io, bool allow8 = false) {
 
 // Prefill of few heads over a long sequence: rather than splitting each head's
 // state columns over many workgroups (each of which then repeats the whole
-// per-chunk preparation), split the sequence into P segments and use the
-// context-parallel decomposition: each segment's zero-start end state and
-// transfer map, a sequential merge into true segment start states, then an
-// independent prefill of every segment.  The result is the same recurrence.
+// per-chunk preparation), cut the sequence and use the context-parallel
+// decomposition.  The first T0 tokens start from the known S0 and are simply
+// prefilled; meanwhile the segment pass computes the zero-start end state and
+// transfer map of each of the next G - 1 segments of Tseg tokens.  A sequential
+// merge then gives the true start state of each of the G remaining segments
+// (the last one ends at T and may be shorter), which are prefilled
+// independently.  The result is the same recurrence.
+//
+// T0 is chosen so that the direct prefill and the segment pass, which run side
+// by side, end together: running beside each other, the segment pass costs
+// about 15/16 of the prefill per token (it skips q and the outputs but carries
+// twice the state columns); 11/16 to 17/16 were measured at 64K tokens and 32
+// heads, 15/16 being fastest.
 struct PrefillPlan {
   bool split = false;
-  int P = 1, Tseg = 0;
+  int T0 = 0, G = 1, Tseg = 0;
   size_t ws = 0;
 };
 
+constexpr int kTransferCost16 = 15;  // segment pass / prefill time per token, in 16ths
+
 PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
   PrefillPlan pl;
+  pl.Tseg = T;
   if (dt != KDA_BF16 || BH <= 0 || T <= 0) return pl;
   const long long cus = cu_count();
   const int ntiles = D / 16;
-  long long P = 0;
+  long long G = 0;
   const char* env = getenv("KDA_SPLIT");
   if (env) {
-    P = atoll(env);  // 0: never; >= 2: that many segments
-    if (P < 2) return pl;
+    G = atoll(env);  // 0: never; >= 2: that many segments after the first part
+    if (G < 2) return pl;
   } else {
     // worth it when one pass cannot fill the chip without 4+ workgroups per head
     if (BH * ntiles / 4 >= cus || T < 4096) return pl;
-    P = (cus + BH - 1) / BH;
-    if (P > T / 1024) P = T / 1024;
-    if (P < 2) return pl;
+    G = (cus + BH - 1) / BH;  // one round of segment prefills
+    if (G > T / 1024) G = T / 1024;
+    if (G < 2) return pl;
   }
-  long long Tseg = (T + P - 1) / P;
-  Tseg = (Tseg + 63) / 64 * 64;
-  P = (T + Tseg - 1) / Tseg;
-  if (P < 2) return pl;
-  pl.split = true;
-  pl.P = (int)P;
-  pl.Tseg = (int)Tseg;
-  pl.ws = (size_t)3 * P * BH * D * D * sizeof(float);
+  for (; G >= 2; --G) {
+    // T = T0 + (G - 1) * Tseg + last, 0 < last <= Tseg, T0 ~ (13/16) Tseg
+    const long long unit = 64LL * (16 * G + kTransferCost16);
+    long long Tseg = (16LL * T + unit - 1) / unit * 64;
+    long long T0 = kTransferCost16 * Tseg / 16 / 64 * 64;
+    if (T0 < 64) T0 = 64;
+    if (T - T0 > G * Tseg) T0 = (T - G * Tseg + 63) / 64 * 64;
+    const long long last = T - T0 - (G - 1) * Tseg;
+    if (last <= 0 || last > Tseg || T0 >= T) continue;
+    pl.split = true;
+    pl.T0 = (int)T0;
+    pl.G = (int)G;
+    pl.Tseg = (int)Tseg;
+    // Z and M of G - 1 segments, the direct part's end state, G start states
+    pl.ws = (size_t)(3 * G - 1) * BH * D * D * sizeof(float);
+    return pl;
+  }
   return pl;
+}
+
+// A second stream per device on which the segment pass runs beside the direct
+// prefill of the first part (default priority, non-blocking, kept for the
+// process lifetime), with the events that fork it from and join it to the
+// caller's stream.  The mutex keeps one call's record/wait sequence whole.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+
+kda_status side_stream(SideStream** out) {
+  static std::mutex mu;
+  static SideStream* cache[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(KDA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev]) {
+    SideStream* ss = new SideStream();
+    if ((e = hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ss->join, hipEventDisableTiming)) != hipSuccess) {
+      delete ss;  // (a partly created stream or event is left to process exit)
+      return hip_fail(e, "creating the side stream");
+    }
+    cache[dev] = ss;
+  }
+  *out = cache[dev];
+  return KDA_OK;
 }
 
 kda_status check_dims(int dk, int dv) {
@@ -161,24 +214,32 @@ struct Snap {
   int H = 1;
 };
 
+// Prefill of the G = ceil((Tend - t0) / Tseg) consecutive segments of tokens
+// [t0, Tend) of every head (sequences of T tokens), segment i from Sst[i] (null:
+// zero); S_T receives the end state of the last segment.  nc = 0 picks the
+// consumer-wave count.
 kda_status launch_segment_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
                                   const void* beta, const float* Sst, void* o, float* S_T,
-                                  long long BH, int T, int Tseg, int D, bool bf, hipStream_t stream,
-                                  const char* what, const Snap& sn = Snap()) {
-  const int G = T > 0 ? (int)(((long long)T + Tseg - 1) / Tseg) : 1;  // T = 0: copy the start state
+                                  long long BH, int T, int t0, int Tend, int Tseg, int D, bool bf,
+                                  hipStream_t stream, const char* what, const Snap& sn = Snap(),
+                                  int nc = 0) {
+  const int n = Tend - t0;
+  const int G = n > 0 ? (int)(((long long)n + Tseg - 1) / Tseg) : 1;  // no tokens: copy the start state
   const long long nseq = BH * G;
-  const int nt = D / 16, nc = pick_nc(nseq, nt, bf);
+  const int nt = D / 16;
+  if (nc == 0) nc = pick_nc(nseq, nt, bf);
   kda::ChunkArgs a;
   a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
   a.S0 = Sst; a.o = o; a.S_out = S_T; a.M_out = nullptr;
-  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = T; a.vsplit = nt / (nc * kda::chunk_tiles_per_wave(bf));
+  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = T; a.t0 = t0; a.Tend = Tend;
+  a.vsplit = nt / (nc * kda::chunk_tiles_per_wave(bf));
   a.snap = sn.n > 0 ? sn.p : nullptr; a.snap_chunks = sn.chunks > 0 ? sn.chunks : 1;
   a.nsnap = sn.n; a.H = sn.H;
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (getenv("KDA_LOG"))
-    fprintf(stderr, "[libkda] %s BH=%lld T=%d Tseg=%d G=%d D=%d nc=%d vsplit=%d grid=%lld\n", what, BH,
-            T, Tseg, G, D, nc, a.vsplit, nwg);
+    fprintf(stderr, "[libkda] %s BH=%lld T=%d tokens [%d,%d) Tseg=%d G=%d D=%d nc=%d vsplit=%d grid=%lld\n",
+            what, BH, T, t0, Tend, Tseg, G, D, nc, a.vsplit, nwg);
   const hipError_t e = kda::launch_chunk(a, bf, D, true, nc, (int)nwg, stream);
   if (e != hipSuccess) return hip_fail(e, what);
   return KDA_OK;
@@ -235,14 +296,16 @@ size_t kda_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtyp
   return plan_prefill((long long)B * H, T, dk, dtype).ws;
 }
 
-kda_status kda_prefill_plan(int B, int H, int T, int dk, int dv, kda_dtype dtype, int* G, int* Tseg) {
-  if (!G || !Tseg) return fail(KDA_ERR_NULL, "G and Tseg must not be NULL");
+kda_status kda_prefill_plan(int B, int H, int T, int dk, int dv, kda_dtype dtype, int* T0, int* G,
+                            int* Tseg) {
+  if (!T0 || !G || !Tseg) return fail(KDA_ERR_NULL, "T0, G and Tseg must not be NULL");
   if (B < 0 || H < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size B=%d H=%d T=%d", B, H, T);
   kda_status st;
   if ((st = check_dtype(dtype)) != KDA_OK) return st;
   if ((st = check_dims(dk, dv)) != KDA_OK) return st;
   const PrefillPlan pl = plan_prefill((long long)B * H, T, dk, dtype);
-  *G = pl.split ? pl.P : 1;
+  *T0 = pl.split ? pl.T0 : 0;
+  *G = pl.split ? pl.G : 1;
   *Tseg = pl.split ? pl.Tseg : T;
   return ok();
 }
@@ -273,40 +336,55 @@ kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, c
   const int D = dk;
   const PrefillPlan pl = plan_prefill(BH, T, D, dtype);
   if (pl.split && workspace && workspace_bytes >= pl.ws) {
-    // Only the first P-1 segments need their zero-start end state and map: the
-    // last segment's start state is the merge of those, and its own prefill
-    // produces S_T.
-    const int G1 = pl.P - 1;
-    const long long nseq1 = BH * G1;
-    const size_t nS = (size_t)BH * pl.P * D * D;
-    float* Z = static_cast<float*>(workspace);
-    float* M = Z + nS;
-    float* Sst = M + nS;
-    // 1. per-segment zero-start end states and transfer maps (segments 0 .. P-2)
+    const int G = pl.G, G1 = G - 1, T0 = pl.T0, Ts = pl.Tseg;
+    const size_t nS = (size_t)BH * D * D;
+    float* Z = static_cast<float*>(workspace);  // [G-1] zero-start end states
+    float* M = Z + G1 * nS;                     // [G-1] transfer maps
+    float* S1 = M + G1 * nS;                    // end state of the direct part
+    float* Sst = S1 + nS;                       // [G] start states of the segments
+    SideStream* ss = nullptr;
+    if ((st = side_stream(&ss)) != KDA_OK) return st;
     kda::ChunkArgs t;
     t.q = nullptr; t.k = k; t.v = v; t.la = log_alpha; t.beta = beta;
     t.S0 = nullptr; t.o = nullptr; t.S_out = Z; t.M_out = M;
-    t.BH = (int)BH; t.G = G1; t.Tseg = pl.Tseg; t.Ttot = T;
-    const int nt2 = 2 * D / 16, nc2 = pick_nc(nseq1, nt2, bf, D == 128);
+    t.BH = (int)BH; t.G = G1; t.Tseg = Ts; t.Ttot = T; t.t0 = T0; t.Tend = T0 + G1 * Ts;
+    const int nt2 = 2 * D / 16, nc2 = pick_nc(BH * G1, nt2, bf, D == 128);
     t.vsplit = nt2 / (nc2 * kda::chunk_tiles_per_wave(bf));
+    // the direct part: one workgroup per head (all of a head's column tiles) when
+    // the segment pass leaves room for it, else the usual choice
+    const int nc0 = BH * (G1 * t.vsplit + 1) <= cu_count() ? D / 16 / kda::chunk_tiles_per_wave(bf) : 0;
     if (getenv("KDA_LOG"))
-      fprintf(stderr, "[libkda] prefill split BH=%lld T=%d D=%d P=%d Tseg=%d: transfer nc=%d vsplit=%d\n",
-              BH, T, D, pl.P, pl.Tseg, nc2, t.vsplit);
+      fprintf(stderr, "[libkda] prefill split BH=%lld T=%d D=%d: direct [0,%d), %d x %d-token segments; "
+              "transfer nc=%d vsplit=%d\n", BH, T, D, T0, G, Ts, nc2, t.vsplit);
     hipError_t e;
-    if ((e = kda::launch_chunk(t, bf, D, false, nc2, (int)(nseq1 * t.vsplit), stream)) != hipSuccess)
-      return hip_fail(e, "kda_chunk_prefill segment pass");
-    // 2. merge into the true start states of segments 0 .. P-1 (the merged state
-    //    after segment P-2 is the last segment's start state)
-    if ((e = kda::launch_merge(S0, Z, M, Sst, Sst + (size_t)G1 * BH * D * D, (int)BH, G1, D, stream)) !=
-        hipSuccess)
+    {
+      // 1. beside each other: the direct prefill of tokens [0, T0) from S0, and
+      //    the segment pass over the G - 1 segments that follow it
+      std::lock_guard<std::mutex> lk(ss->mu);
+      if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess ||
+          (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
+        return hip_fail(e, "kda_chunk_prefill fork");
+      if ((e = kda::launch_chunk(t, bf, D, false, nc2, (int)(BH * G1 * t.vsplit), ss->s)) != hipSuccess)
+        return hip_fail(e, "kda_chunk_prefill segment pass");
+      st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, o, S1, BH, T, 0, T0, T0, D, bf, stream,
+                                  "kda_chunk_prefill direct part", sn, nc0);
+      // join even if the launch above failed, so the side stream's work is waited for
+      if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess ||
+          (e = hipStreamWaitEvent(stream, ss->join, 0)) != hipSuccess)
+        return hip_fail(e, "kda_chunk_prefill join");
+      if (st != KDA_OK) return st;
+    }
+    // 2. merge, from the direct part's end state, into the start states of all G
+    //    segments (the merged state after segment G-2 is the last one's start)
+    if ((e = kda::launch_merge(S1, Z, M, Sst, Sst + G1 * nS, (int)BH, G1, D, stream)) != hipSuccess)
       return hip_fail(e, "kda_chunk_prefill merge");
-    // 3. prefill of every segment from its start state
-    // (plan_prefill makes Tseg a multiple of the chunk length, as snapshots need)
-    st = launch_segment_prefill(q, k, v, log_alpha, beta, Sst, o, S_T, BH, T, pl.Tseg, D, bf, stream,
+    // 3. prefill of every segment from its start state (Tseg and T0 are multiples
+    //    of the chunk length, as snapshots need)
+    st = launch_segment_prefill(q, k, v, log_alpha, beta, Sst, o, S_T, BH, T, T0, T, Ts, D, bf, stream,
                                 "kda_chunk_prefill segment prefill", sn);
     return st == KDA_OK ? ok() : st;
   }
-  st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, o, S_T, BH, T, T > 0 ? T : 1, D, bf,
+  st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, o, S_T, BH, T, 0, T, T > 0 ? T : 1, D, bf,
                               stream, "kda_chunk_prefill", sn);
   return st == KDA_OK ? ok() : st;
 }
@@ -330,7 +408,7 @@ kda_status kda_chunk_prefill_segments(const void* q, const void* k, const void* 
   if (BH == 0) return ok();
   KDA_OPTIONAL(S_start, "S_start");
   if (T == 0) return fail(KDA_ERR_SHAPE, "T must be >= 1 for a segmented prefill");
-  st = launch_segment_prefill(q, k, v, log_alpha, beta, S_start, o, S_T, BH, T, Tseg, dk,
+  st = launch_segment_prefill(q, k, v, log_alpha, beta, S_start, o, S_T, BH, T, 0, T, Tseg, dk,
                               dtype == KDA_BF16, stream, "kda_chunk_prefill_segments");
   return st == KDA_OK ? ok() : st;
 }
@@ -384,7 +462,7 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
   kda::ChunkArgs a;
   a.q = nullptr; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
   a.S0 = nullptr; a.o = nullptr; a.S_out = S_zero_end; a.M_out = M;
-  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = G * Tseg;
+  a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = G * Tseg; a.t0 = 0; a.Tend = G * Tseg;
   a.vsplit = ntiles / (nc * kda::chunk_tiles_per_wave(dtype == KDA_BF16));
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");

@@ -842,10 +842,11 @@ struct ChunkKernel {
     const int vs = id - seq * a.vsplit;
     const int gseg = seq / a.BH;
     const int bh = seq - gseg * a.BH;
-    const size_t tok0 = (size_t)bh * a.Ttot + (size_t)gseg * a.Tseg;
-    Tlen = min(a.Tseg, a.Ttot - gseg * a.Tseg);
+    const int seg0 = a.t0 + gseg * a.Tseg;  // first token of this segment
+    const size_t tok0 = (size_t)bh * a.Ttot + seg0;
+    Tlen = min(a.Tseg, a.Tend - seg0);
     nch = (Tlen + CH - 1) / CH;
-    chunk0 = gseg * (a.Tseg / CH);
+    chunk0 = seg0 / CH;
     snap_head = nullptr;
     if (PREFILL && a.snap) {
       const int b = bh / a.H, h = bh - b * a.H;

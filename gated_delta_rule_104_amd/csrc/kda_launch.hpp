@@ -8,8 +8,8 @@
 namespace kda {
 
 // One chunked pass over `G * BH` independent sequences (segments).  Sequence
-// s = g * BH + bh reads tokens [g*Tseg, min((g+1)*Tseg, Ttot)) of head bh,
-// whose rows start at token bh * Ttot of the [BH, Ttot, D] inputs.
+// s = g * BH + bh reads tokens [t0 + g*Tseg, min(t0 + (g+1)*Tseg, Tend)) of head
+// bh, whose rows start at token bh * Ttot of the [BH, Ttot, D] inputs.
 struct ChunkArgs {
   const void* q;
   const void* k;
@@ -24,7 +24,9 @@ struct ChunkArgs {
   int BH;
   int G;
   int Tseg;         // tokens per segment (the last one may be shorter)
-  int Ttot;         // tokens per head
+  int Ttot;         // tokens per head (row stride of a head in tokens)
+  int t0 = 0;       // first token of segment 0
+  int Tend = 0;     // end of the covered tokens (t0 + G*Tseg or less, <= Ttot)
   int vsplit;       // workgroups per sequence (each owns 16 * nc * chunk_tiles_per_wave columns)
   // prefill only: state snapshots [B, nsnap, H, D, D] after every snap_chunks
   // chunks of a head's whole sequence (null: none).  With snapshots and G > 1,

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
   KDA_OK = 0,
@@ -70,14 +70,21 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * Any T >= 0 is accepted (a last partial chunk is masked); T == 0 copies S0
  * (or zeros) to S_T.
  *
- * With few heads and a long sequence, the call can cut every sequence into
- * segments and apply the context-parallel decomposition of the same section
- * ("针对适配的 Infra", KDA context parallelism) on this GPU: per-segment
- * zero-start states and transfer maps, a sequential merge, then an independent
- * prefill of each segment.  That path needs kda_prefill_workspace_bytes() of
- * workspace (fp32 states, three per segment and head); with a smaller or NULL
- * workspace the call runs the single-pass path instead.  The workspace is only
- * used by work enqueued by this call; calls on one stream may share it.
+ * With few heads and a long sequence, the call can cut every sequence and
+ * apply the context-parallel decomposition of the same section ("针对适配的
+ * Infra", KDA context parallelism) on this GPU.  The first T0 tokens are
+ * prefilled directly from S0 while, beside them, the segment pass computes the
+ * zero-start states and transfer maps of the next G - 1 segments; a sequential
+ * merge then gives the start states of the G segments after the first part,
+ * and each of them runs its own prefill (kda_prefill_plan reports T0, G and
+ * the segment length).  That path needs kda_prefill_workspace_bytes() of
+ * workspace (fp32 states, 3G - 1 per head); with a smaller or NULL workspace
+ * the call runs the single-pass path instead.  The workspace is only used by
+ * work enqueued by this call; calls on one stream may share it.
+ * The side-by-side part runs on a second stream of the library's own (created
+ * once per device, default priority), forked from and joined back to `stream`
+ * with events, so all of the call's work is ordered after earlier work on
+ * `stream` and before later work on it.
  */
 size_t kda_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtype dtype);
 
@@ -112,12 +119,15 @@ kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, c
                                   hipStream_t stream);
 
 /*
- * The segmentation kda_chunk_prefill would use for this shape when given
- * kda_prefill_workspace_bytes() of workspace: *G segments of *Tseg tokens (the
- * last one possibly shorter); *G == 1 means the single-pass path.  Writes
- * nothing else and launches nothing.
+ * The cut kda_chunk_prefill would use for this shape when given
+ * kda_prefill_workspace_bytes() of workspace: a first part of *T0 tokens
+ * prefilled directly, then *G segments of *Tseg tokens (the last one possibly
+ * shorter, ending at T).  *T0 == 0 and *G == 1 (*Tseg == T) mean the
+ * single-pass path.  T0 and Tseg are multiples of 64 on the split path.
+ * Writes nothing else and launches nothing.
  */
-kda_status kda_prefill_plan(int B, int H, int T, int dk, int dv, kda_dtype dtype, int* G, int* Tseg);
+kda_status kda_prefill_plan(int B, int H, int T, int dk, int dv, kda_dtype dtype, int* T0, int* G,
+                            int* Tseg);
 
 /*
  * Last step of the context-parallel decomposition (same section): every

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
     for st in range(6):
         assert lib.kda_status_string(st)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -79,8 +79,9 @@ def test_prefill_validation(lib):
 
 
 def test_prefill_workspace_query(lib):
-    """The sequence-split path asks for three fp32 states per segment and head;
-    it is not used for fp32 inputs, short sequences or many heads."""
+    """The sequence-split path asks for 3G - 1 fp32 states per head (G segments
+    after the directly prefilled first part); it is not used for fp32 inputs,
+    short sequences or many heads."""
     ws = lib.kda_prefill_workspace_bytes
     ws.restype = ctypes.c_size_t
     assert ws(1, 32, 65536, 128, 128, F32) == 0
@@ -88,22 +89,27 @@ def test_prefill_workspace_query(lib):
     assert ws(64, 32, 65536, 128, 128, BF16) == 0
     assert ws(1, 32, 65536, 128, 64, BF16) == 0
     n = ws(1, 32, 65536, 128, 128, BF16)
-    assert n > 0 and n % (3 * 32 * 128 * 128 * 4) == 0
+    assert n > 0 and n % (32 * 128 * 128 * 4) == 0 and (n // (32 * 128 * 128 * 4)) % 3 == 2
 
 
 def test_prefill_plan(lib):
-    """The plan matches the workspace query: split exactly when workspace is asked for."""
-    G, Ts = ctypes.c_int(0), ctypes.c_int(0)
-    plan = lambda *a: lib.kda_prefill_plan(*a, ctypes.byref(G), ctypes.byref(Ts))
+    """The plan matches the workspace query: split exactly when workspace is asked
+    for; the first part and the segments are whole chunks and cover T exactly,
+    the last segment being the only short one."""
+    T0, G, Ts = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    plan = lambda *a: lib.kda_prefill_plan(*a, ctypes.byref(T0), ctypes.byref(G), ctypes.byref(Ts))
     ws = lib.kda_prefill_workspace_bytes
     ws.restype = ctypes.c_size_t
-    assert plan(1, 32, 65536, 128, 128, BF16) == OK
-    assert G.value > 1 and Ts.value % 64 == 0 and (G.value - 1) * Ts.value < 65536 <= G.value * Ts.value
-    assert ws(1, 32, 65536, 128, 128, BF16) == 3 * G.value * 32 * 128 * 128 * 4
-    assert plan(64, 32, 65536, 128, 128, BF16) == OK and (G.value, Ts.value) == (1, 65536)
-    assert plan(1, 32, 65536, 128, 128, F32) == OK and G.value == 1
+    for T in (4096, 10000, 65536, 1 << 20):
+        assert plan(1, 32, T, 128, 128, BF16) == OK
+        t0, g, ts = T0.value, G.value, Ts.value
+        assert g > 1 and ts % 64 == 0 and t0 % 64 == 0 and t0 > 0, (T, t0, g, ts)
+        assert t0 + (g - 1) * ts < T <= t0 + g * ts, (T, t0, g, ts)
+        assert ws(1, 32, T, 128, 128, BF16) == (3 * g - 1) * 32 * 128 * 128 * 4
+    assert plan(64, 32, 65536, 128, 128, BF16) == OK and (T0.value, G.value, Ts.value) == (0, 1, 65536)
+    assert plan(1, 32, 65536, 128, 128, F32) == OK and (T0.value, G.value) == (0, 1)
     assert plan(1, 32, 100, 96, 96, BF16) == ERR_UNSUPPORTED
-    assert lib.kda_prefill_plan(1, 1, 64, 64, 64, BF16, None, ctypes.byref(Ts)) == ERR_NULL
+    assert lib.kda_prefill_plan(1, 1, 64, 64, 64, BF16, None, ctypes.byref(G), ctypes.byref(Ts)) == ERR_NULL
 
 
 def test_prefill_snap_validation(lib):

@@ -290,7 +290,9 @@ def test_full_b4_h32_t8k():
 def test_full_h32_t64k():
     """B=1, H=32, T=65536, dk=dv=128, bf16, S0 = 0 (the headline workload), in
     the sequence-split configuration the benchmark times; the same result comes
-    out of the three public calls of that decomposition, bit for bit."""
+    out of the public calls of that decomposition, bit for bit: the direct
+    prefill of the first part, the segment pass over the segments after it, the
+    merge from the first part's end state, and the prefill of every segment."""
     print("[case] full h32_t64k", flush=True)
     B, H, T, D = 1, 32, 65536, 128
     g = gpu_inputs(B, H, T, D, seed=2)
@@ -298,13 +300,18 @@ def test_full_h32_t64k():
     torch.cuda.synchronize()
     eo, es = check_sampled_heads(g, o, S_T, [(0, 0), (0, 13), (0, 31)])
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
-    G, Tseg = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
-    assert G > 1 and G * Tseg == T
-    Z, M = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], G)
-    S_start, _ = kda.segment_merge(Z, M, None)
-    o3, S3 = kda.prefill_segments(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], S_start, Tseg)
+    T0, G, Tseg = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
+    assert G > 1 and 0 < T0 and T0 + (G - 1) * Tseg < T <= T0 + G * Tseg
+    T1 = T0 + (G - 1) * Tseg
+    sl = lambda n, a, b: g[n][:, :, a:b].contiguous()
+    names = ("q", "k", "v", "log_alpha", "beta")
+    o0, S1 = kda.prefill(*(sl(n, 0, T0) for n in names), None, workspace=None)
+    Z, M = kda.segment_transfer(*(sl(n, T0, T1) for n in names[1:]), G - 1)
+    S_start, S_last = kda.segment_merge(Z, M, S1)
+    S_all = torch.cat([S_start, S_last[None]]).contiguous()
+    o3, S3 = kda.prefill_segments(*(sl(n, T0, T) for n in names), S_all, Tseg)
     torch.cuda.synchronize()
-    assert torch.equal(o3, o) and torch.equal(S3, S_T)
+    assert torch.equal(o0, o[:, :, :T0]) and torch.equal(o3, o[:, :, T0:]) and torch.equal(S3, S_T)
 
 
 def test_full_kcp_h32_t1m():
@@ -464,3 +471,29 @@ def test_full_h32_t64k_snapshots():
     es = oracle.max_rel_l2(snaps[:, :, list(heads)].cpu(), ref, lead=3, floor=1e-6)
     print(f"    snapshots of heads {heads}: {es:.3e}", flush=True)
     assert es <= TOL["bf16"]
+
+
+def test_prefill_split_on_user_stream(monkeypatch):
+    """The split path forks part of its work to the library's side stream and
+    joins it back: calls on a user stream, issued back to back with inputs that
+    change in between, give the results of calls on the default stream."""
+    monkeypatch.setenv("KDA_SPLIT", "6")
+    B, H, T, D = 1, 4, 3000, 128
+    d = ki.gen_prefill(B, H, T, D, D, "bf16", seed=430, s0_std=0.1, variant="slow")
+    g = to_dev(d)
+    ref = [kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])]
+    k2 = g["k"].flip(2).contiguous()
+    ref.append(kda.prefill(g["q"], k2, g["v"], g["log_alpha"], g["beta"], g["S0"]))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    kk = g["k"].clone()
+    with torch.cuda.stream(s):
+        a = kda.prefill(g["q"], kk, g["v"], g["log_alpha"], g["beta"], g["S0"])
+        kk.copy_(k2)  # ordered after the first call's side-stream work
+        b = kda.prefill(g["q"], kk, g["v"], g["log_alpha"], g["beta"], g["S0"])
+    torch.cuda.synchronize()
+    for (o, S), (o_r, S_r) in zip((a, b), ref):
+        assert torch.equal(o, o_r) and torch.equal(S, S_r)
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    assert oracle.max_rel_l2(a[0].cpu(), o_ref) <= TOL["bf16"]
+    assert oracle.max_rel_l2(a[1].cpu(), S_ref) <= TOL["bf16"]
