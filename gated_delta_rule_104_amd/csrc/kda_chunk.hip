@@ -230,29 +230,41 @@ struct ChunkKernel {
   // Lane (tg = l%16, cs = l/16) of producer wave pw owns tokens 4*tg..4*tg+3 and
   // channels 32*pw + 8*cs .. +7 of the chunk; a channel's 16 token groups are
   // one DPP row, so the prefix sum over tokens runs on row operations.
-  __device__ __forceinline__ void load_raw(ProdRaw<T>& r, int chunk) const {
+  // byte offset of token row i of the lane's token group, first of its channels
+  __device__ __forceinline__ uint32_t prod_off(int chunk, int i) const {
     const int ln = fresh_lane(l);
-    const int pw = wave - NC;
-    const int tg = ln & 15, cs = ln >> 4;
-    const int ch = 32 * pw + 8 * cs;
+    const int ch = 32 * (wave - NC) + 8 * (ln >> 4);
+    return (uint32_t)((chunk * CH + 4 * (ln & 15) + i) * D + ch) * C::ES;
+  }
+  __device__ __forceinline__ void load_la(ProdRaw<T>& r, int chunk) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t off = (uint32_t)((chunk * CH + 4 * tg + i) * D + ch) * C::ES;
-      raw_load<T>(r.la[i], rla, off);
-      raw_load<T>(r.k[i], rk, off);
-      if constexpr (PREFILL) raw_load<T>(r.q[i], rq, off);
-    }
-    if (pw == 0) {
-      const uint32_t off = (uint32_t)(chunk * CH + ln) * C::ES;
+    for (int i = 0; i < 4; ++i) raw_load<T>(r.la[i], rla, prod_off(chunk, i));
+  }
+  __device__ __forceinline__ void load_kq(ProdRaw<T>& r, int chunk, int i) const {
+    raw_load<T>(r.k[i], rk, prod_off(chunk, i));
+    if constexpr (PREFILL) raw_load<T>(r.q[i], rq, prod_off(chunk, i));
+  }
+  __device__ __forceinline__ void load_beta(ProdRaw<T>& r, int chunk) const {
+    if (wave == NC) {
+      const uint32_t off = (uint32_t)(chunk * CH + fresh_lane(l)) * C::ES;
       if constexpr (C::BF) r.beta = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rbeta, off, 0, 0);
       else r.beta = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rbeta, off, 0, 0);
     }
+  }
+  __device__ __forceinline__ void load_raw(ProdRaw<T>& r, int chunk) const {
+    load_la(r, chunk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_kq(r, chunk, i);
+    load_beta(r, chunk);
   }
 
   // Phase 1: cumulative log-gate and the decayed operand tiles of one chunk.
   // bf16 inputs: the gate is accumulated in log2 units and exponentiated with
   // the hardware exp2; fp32 inputs use the accurate library exp.
-  __device__ __forceinline__ void p1(const ProdRaw<T>& r, uint32_t st) {
+  // Each register of r is refilled with chunk `next` as soon as it has been
+  // read, so the prefetch loads issue spread over this VALU-heavy phase rather
+  // than in one burst.
+  __device__ __forceinline__ void p1(ProdRaw<T>& r, uint32_t st, int next) {
     const int ln = fresh_lane(l);
     const int pw = wave - NC;
     const int tg = ln & 15, cs = ln >> 4;
@@ -266,6 +278,7 @@ struct ChunkKernel {
         for (int c = 0; c < 8; ++c) g[i][c] *= LOG2E;
       }
     }
+    load_la(r, next);
     float exc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -289,6 +302,7 @@ struct ChunkKernel {
       float kk[8], qq[8], vq[8], vkh[8];
       raw_f32<T>(r.k[i], kk);
       if constexpr (PREFILL) raw_f32<T>(r.q[i], qq);
+      load_kq(r, next, i);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const float gg = g[i][c] + exc[c];
@@ -356,6 +370,7 @@ struct ChunkKernel {
       const float b = C::BF ? __uint_as_float(r.beta << 16) : __uint_as_float(r.beta);
       lds_st<float>(smem, st + C::S_BETA + 4 * ln, b);
     }
+    load_beta(r, next);
   }
 
   // Phase 2, one tile task: block (I, J), J <= I, of the score matrix M = X Kb^T
@@ -766,7 +781,7 @@ struct ChunkKernel {
 
   __device__ __forceinline__ void chain(VRaw& vr, int cc) {
     c1(vr, stage(cc));
-    if (cc + 1 < nch) load_v(vr, cc + 1);
+    load_v(vr, cc + 1);  // on every path (reads zero past the end), as for the producers
     c2(stage(cc), cc);
     c3(stage(cc));
     snapshot(cc);
@@ -782,36 +797,46 @@ struct ChunkKernel {
   // r with chunk it + PD: right away for PD = 1, and for PD = 2 once the first
   // barrier has passed (the rest of the workgroup is then busy with the score
   // tiles, and the data has a whole iteration to arrive).
+  //
+  // The prefetch loads are issued on every path, also past the last chunk
+  // (buffer loads beyond the sequence read zero): the compiler's count of
+  // loads in flight must be the same on all paths, or it waits for every
+  // load, including the prefetch of the next chunk, before using a register set.
+  //
+  // Every step does the same work, also the last one of a two-stage pipeline,
+  // which prepares a chunk past the end (zero inputs) into the stage nobody
+  // reads any more: with no data-dependent branches around the loads, the
+  // compiler counts them exactly.
   template <int PD>
   __device__ __forceinline__ void producer_step(ProdRaw<T>& r, int it) {
-    const bool w = it < nch;
-    if (w) p1(r, stage(it));
-    if (PD == 1 && it + PD < nch) load_raw(r, it + PD);
+    p1(r, stage(it), it + PD);
     sync_lds();
-    if (PD == 2 && it + PD < nch) load_raw(r, it + PD);
-    if (w) p2(stage(it));
+    p2(stage(it));
     sync_lds();
     if (!C::LAG) sync_lds();
   }
 
   // Producer inputs are prefetched two chunks ahead (two register sets, the
-  // loop unrolled by two), except in the three-waves-per-SIMD variant, which
-  // keeps one set and prefetches one chunk ahead.
+  // loop unrolled by two with the odd step peeled off, so that the loop's back
+  // edge always follows both steps), except in the three-waves-per-SIMD
+  // variant, which keeps one set and prefetches one chunk ahead.
   __device__ __forceinline__ void producer_loop() {
     init_offsets();
     const int n = nch + C::LAG;
     if constexpr (TIGHT) {
       ProdRaw<T> r;
-      if (nch > 0) load_raw(r, 0);
+      load_raw(r, 0);
       for (int it = 0; it < n; ++it) producer_step<1>(r, it);
     } else {
       ProdRaw<T> ra, rb;
-      if (nch > 0) load_raw(ra, 0);
-      if (nch > 1) load_raw(rb, 1);
-      for (int it = 0; it < n; it += 2) {
+      load_raw(ra, 0);
+      load_raw(rb, 1);
+      int it = 0;
+      for (; it + 1 < n; it += 2) {
         producer_step<2>(ra, it);
-        if (it + 1 < n) producer_step<2>(rb, it + 1);
+        producer_step<2>(rb, it + 1);
       }
+      if (it < n) producer_step<2>(ra, it);
     }
   }
 
@@ -823,7 +848,7 @@ struct ChunkKernel {
       const int cc = it - C::LAG;
       if (C::LAG && cc >= 0) chain(vr, cc);
       sync_lds();
-      if (it < nch) p2(stage(it));
+      p2(stage(it));  // (it == nch: the unread chunk past the end)
       sync_lds();
       if (!C::LAG) {
         chain(vr, cc);
@@ -889,6 +914,10 @@ struct ChunkKernel {
             }
             S[j][ci][e] = x;
           }
+      // Retire the start-state loads here: left pending into the chunk loop, they
+      // make the compiler wait for every load and store in flight at the top of
+      // each iteration (its count at the loop header merges in this path).
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt not waited for
     }
     sync_lds();
 
