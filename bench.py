@@ -173,6 +173,28 @@ def bench_decomposition(pf, args):
     return res
 
 
+def bench_prefill(args, dev):
+    B, H, T, D = 1, 32, 65536, 128
+    print(f"[bench] generating prefill inputs B={B} H={H} T={T} D={D} bf16", file=sys.stderr, flush=True)
+    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=2, device=dev)
+    o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    nws = kda.prefill_workspace_bytes(B, H, T, D, D, torch.bfloat16)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+
+    def step():
+        kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None, o=o, S_T=S_T, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    mean_ms, per = time_launches(step, args.steps)
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    return dict(B=B, H=H, T=T, D=D, mean_ms=mean_ms, wall_ms=wall_ms, per=per, g=g, ws_bytes=nws)
+
+
 def bench_snapshots(pf, args, interval=512):
     """The same prefill with a state snapshot every `interval` tokens (prefix
     caching): time per call, the snapshot bytes written, and the cost over the
@@ -229,6 +251,35 @@ def bench_decode(args, dev):
     return dict(N=N, H=H, D=D, steps=steps, ms_total=ms, us_per_step=step_ms * 1e3,
                 tokens_per_s=N * steps / (ms * 1e-3), achieved_GBs=gbs, hbm_frac=gbs / PEAK_HBM_GBS,
                 bytes_per_step=per_step_bytes, traffic_per_step=traffic)
+
+
+def bench_decode_tokens(args, dev, ntok=4):
+    """Speculative-decoding verification: ntok draft tokens for each of 256
+    sequences x 32 heads in one call (state read and written once), with and
+    without the per-token rollback states."""
+    N, H, D = 256, 32, 128
+    g = ki.gen_prefill(N, H, ntok, D, D, "bf16", seed=5, device=dev, s0_std=0.1)
+    S = g["S0"]
+    S_out = torch.empty_like(S)
+    o = torch.empty(N, H, ntok, D, dtype=torch.bfloat16, device=dev)
+    S_pos = torch.empty(N, ntok, H, D, D, dtype=torch.float32, device=dev)
+
+    def call(pos):
+        kda.decode_tokens(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], S, S_out=S_out, o=o,
+                          S_pos=S_pos if pos else None)
+
+    call(False); call(True)
+    torch.cuda.synchronize()
+    n = max(10, args.steps)
+    ms, _ = time_launches(lambda: call(False), n)
+    ms_pos, _ = time_launches(lambda: call(True), n)
+    nbytes = N * H * (2 * D * D * 4 + ntok * (2 * (3 * D + D + D) + 2))
+    pos_bytes = N * H * ntok * D * D * 4
+    del g, S_pos
+    return {"N": N, "H": H, "D": D, "ntok": ntok, "ms": ms, "tokens_per_s": N * ntok / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "with_positions_ms": ms_pos,
+            "with_positions_hbm_frac": (nbytes + pos_bytes) / (ms_pos * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
 def bench_kcp(args, dev):
@@ -378,6 +429,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_decode:
         out["decode"] = bench_decode(args, dev)
+        torch.cuda.empty_cache()
+    if not args.no_decode:
+        out["decode_tokens"] = bench_decode_tokens(args, dev)
         torch.cuda.empty_cache()
     if not args.no_kcp:
         out["kcp"] = bench_kcp(args, dev)

@@ -12,6 +12,7 @@ Entry points (same names as the C-ABI):
     prefill_plan(B, H, T, dk, dv, dtype)               -> (T0, G, Tseg)
     prefill_segments(q, k, v, log_alpha, beta, S_start, Tseg) -> (o, S_T)
     decode_step(q, k, v, log_alpha, beta, S)           -> o          (S updated in place)
+    decode_tokens(q, k, v, log_alpha, beta, S, S_out=None, positions=False) -> (o, S_pos or None)
     segment_transfer(k, v, log_alpha, beta, G)         -> (S_zero_end, M)
     segment_merge(S_zero_end, M, S_in=None)            -> (S_start, S_T)
 """
@@ -57,10 +58,12 @@ def load() -> ctypes.CDLL:
     lib.kda_prefill_plan.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 3
     lib.kda_chunk_prefill_segments.argtypes = [vp] * 8 + [i] * 7 + [vp]
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 5 + [vp]
+    lib.kda_decode_tokens.argtypes = [vp] * 9 + [i] * 6 + [vp]
     lib.kda_segment_transfer.argtypes = [vp] * 6 + [i] * 7 + [vp]
     lib.kda_segment_merge.argtypes = [vp] * 5 + [i] * 5 + [vp]
     for f in (lib.kda_chunk_prefill, lib.kda_chunk_prefill_snap, lib.kda_prefill_plan, lib.kda_chunk_prefill_segments,
-              lib.kda_decode_step, lib.kda_segment_transfer, lib.kda_segment_merge):
+              lib.kda_decode_step, lib.kda_decode_tokens, lib.kda_segment_transfer,
+              lib.kda_segment_merge):
         f.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -236,6 +239,37 @@ def decode_step(q, k, v, log_alpha, beta, S, o=None) -> torch.Tensor:
                                 _ptr(o), N, H, dk, dv, _DT[dt], _stream())
     _check(rc, "kda_decode_step")
     return o
+
+
+def decode_tokens(q, k, v, log_alpha, beta, S, S_out=None, positions: bool = False, o=None, S_pos=None):
+    """ntok consecutive tokens per sequence in one pass over the state (speculative
+    decoding's verification step).  q, k, log_alpha [N,H,ntok,dk]; v [N,H,ntok,dv];
+    beta [N,H,ntok]; S [N,H,dk,dv] fp32.  The state after the tokens goes to S_out
+    (default: S itself, in place).  With positions=True (or an S_pos tensor) the
+    state after each token is returned too, [N,ntok,H,dk,dv].  Returns (o, S_pos)."""
+    N, H, ntok, dk = k.shape
+    dv = v.shape[-1]
+    dt = k.dtype
+    if dt not in _DT:
+        raise KdaError(f"unsupported dtype {dt}")
+    for name, t, shp in (("q", q, (N, H, ntok, dk)), ("k", k, (N, H, ntok, dk)), ("v", v, (N, H, ntok, dv)),
+                         ("log_alpha", log_alpha, (N, H, ntok, dk)), ("beta", beta, (N, H, ntok))):
+        _io(t, name, dt, shp)
+    _io(S, "S", torch.float32, (N, H, dk, dv))
+    if S_out is None:
+        S_out = S
+    _io(S_out, "S_out", torch.float32, (N, H, dk, dv))
+    if o is None:
+        o = torch.empty(N, H, ntok, dv, dtype=dt, device=k.device)
+    _io(o, "o", dt, (N, H, ntok, dv))
+    if S_pos is None and positions:
+        S_pos = torch.empty(N, ntok, H, dk, dv, dtype=torch.float32, device=k.device)
+    if S_pos is not None:
+        _io(S_pos, "S_pos", torch.float32, (N, ntok, H, dk, dv))
+    rc = load().kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                                  _ptr(S_out), _ptr(o), _ptr(S_pos), N, H, ntok, dk, dv, _DT[dt], _stream())
+    _check(rc, "kda_decode_tokens")
+    return o, S_pos
 
 
 def segment_transfer(k, v, log_alpha, beta, G: int, S_zero_end=None, M=None):

@@ -430,8 +430,36 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
   if (!beta) return fail(KDA_ERR_NULL, "beta is NULL");  // [N,H] rows: any element alignment
   KDA_REQUIRE(S, "S");
   KDA_REQUIRE(o, "o");
-  hipError_t e = kda::launch_decode(q, k, v, log_alpha, beta, S, o, (int)NH, dk, dtype == KDA_BF16, stream);
+  hipError_t e = kda::launch_decode(q, k, v, log_alpha, beta, S, S, o, nullptr, (int)NH, H, 1, dk,
+                                    dtype == KDA_BF16, stream);
   if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
+  return ok();
+}
+
+kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* beta, const float* S_in, float* S_out, void* o, float* S_pos,
+                             int N, int H, int ntok, int dk, int dv, kda_dtype dtype, hipStream_t stream) {
+  if (N < 0 || H < 0 || ntok < 0) return fail(KDA_ERR_SHAPE, "negative size N=%d H=%d ntok=%d", N, H, ntok);
+  kda_status st;
+  if ((st = check_dtype(dtype)) != KDA_OK) return st;
+  if ((st = check_dims(dk, dv)) != KDA_OK) return st;
+  const long long NH = (long long)N * H;
+  if (NH > INT32_MAX || NH * ntok * dk > kMaxElems) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (NH == 0) return ok();
+  KDA_REQUIRE(S_in, "S_in");
+  KDA_REQUIRE(S_out, "S_out");
+  KDA_OPTIONAL(S_pos, "S_pos");
+  if (ntok > 0) {
+    KDA_REQUIRE(q, "q");
+    KDA_REQUIRE(k, "k");
+    KDA_REQUIRE(v, "v");
+    KDA_REQUIRE(log_alpha, "log_alpha");
+    if (!beta) return fail(KDA_ERR_NULL, "beta is NULL");  // [N,H,ntok] rows: any element alignment
+    KDA_REQUIRE(o, "o");
+  }
+  hipError_t e = kda::launch_decode(q, k, v, log_alpha, beta, S_in, S_out, o, ntok > 0 ? S_pos : nullptr,
+                                    (int)NH, H, ntok, dk, dtype == KDA_BF16, stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_decode_tokens launch");
   return ok();
 }
 

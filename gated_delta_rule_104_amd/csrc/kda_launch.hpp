@@ -46,9 +46,11 @@ inline int chunk_tiles_per_wave(bool bf16_io) { return bf16_io ? 2 : 1; }
 hipError_t launch_chunk(const ChunkArgs& a, bool bf16_io, int D, bool prefill, int nc, int nwg,
                         hipStream_t stream);
 
+// ntok tokens per head ([NH, ntok, D] inputs, beta [NH, ntok]); S_out may alias
+// S_in; S_pos [N, ntok, H, D, D] (NH = N * H) or null.
 hipError_t launch_decode(const void* q, const void* k, const void* v, const void* la,
-                         const void* beta, float* S, void* o, int NH, int D, bool bf16_io,
-                         hipStream_t stream);
+                         const void* beta, const float* S_in, float* S_out, void* o, float* S_pos,
+                         int NH, int H, int ntok, int D, bool bf16_io, hipStream_t stream);
 
 hipError_t launch_merge(const float* S_in, const float* Z, const float* M, float* S_start,
                         float* S_T, int BH, int G, int D, hipStream_t stream);

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum {
   KDA_OK = 0,
@@ -159,6 +159,28 @@ kda_status kda_chunk_prefill_segments(const void* q, const void* k, const void* 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* log_alpha,
                            const void* beta, float* S, void* o, int N, int H, int dk, int dv,
                            kda_dtype dtype, hipStream_t stream);
+
+/*
+ * Several consecutive tokens per sequence in one pass over the state: the
+ * verification step of speculative decoding, for which the K3 report
+ * fine-tunes a draft model (blog.csdn.net article on the Kimi K3 report,
+ * section 二, deployment-aware training).  Equivalent to ntok calls of
+ * kda_decode_step, reading and writing the state once.
+ *   q, k, log_alpha : [N, H, ntok, dk]   dtype
+ *   v               : [N, H, ntok, dv]   dtype
+ *   beta            : [N, H, ntok]       dtype (any element alignment)
+ *   S_in            : [N, H, dk, dv]     fp32 state before the tokens
+ *   S_out           : [N, H, dk, dv]     fp32, written with the state after all
+ *                                        ntok tokens; may alias S_in (in place)
+ *   o               : [N, H, ntok, dv]   dtype, written
+ *   S_pos           : [N, ntok, H, dk, dv] fp32 or NULL: entry [n, t, h] is the
+ *                     state after token t, the rollback point when only tokens
+ *                     0..t are accepted; must not overlap any other argument
+ * ntok == 0 copies S_in to S_out.  Errors: as for kda_decode_step.
+ */
+kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const void* log_alpha,
+                             const void* beta, const float* S_in, float* S_out, void* o, float* S_pos,
+                             int N, int H, int ntok, int dk, int dv, kda_dtype dtype, hipStream_t stream);
 
 /*
  * First half of the context-parallel decomposition ("Kimi K3 开源日来了",

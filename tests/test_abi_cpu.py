@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 5
+    assert lib.kda_abi_version() == 6
     for st in range(6):
         assert lib.kda_status_string(st)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -151,6 +151,20 @@ def test_decode_validation(lib):
     assert f(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE), 4, 2, 64, 64, F32, None) == ERR_ALIGN
     assert f(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), -1, 2, 64, 64, F32, None) == ERR_SHAPE
     assert f(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 0, 2, 64, 64, F32, None) == OK
+
+
+def test_decode_tokens_validation(lib):
+    f = lib.kda_decode_tokens
+    a = lambda *p, N=4, H=2, n=3, dk=128, dv=128, dt=BF16: [*P(*p), N, H, n, dk, dv, dt, None]
+    full = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert f(*a(*full, dv=64)) == ERR_SHAPE
+    assert f(*a(*full, n=-1)) == ERR_SHAPE
+    assert f(*a(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None)) == ERR_NULL  # S_in
+    assert f(*a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None)) == ERR_NULL  # S_out
+    assert f(*a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4)) == ERR_ALIGN  # S_pos
+    assert f(*a(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)) == ERR_NULL
+    assert f(*a(*full, dt=9)) == ERR_UNSUPPORTED
+    assert f(*a(*full, N=0)) == OK
 
 
 def test_segment_validation(lib):

@@ -497,3 +497,79 @@ def test_prefill_split_on_user_stream(monkeypatch):
     o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
     assert oracle.max_rel_l2(a[0].cpu(), o_ref) <= TOL["bf16"]
     assert oracle.max_rel_l2(a[1].cpu(), S_ref) <= TOL["bf16"]
+
+
+# ----------------------------------------------------------------- several decode tokens
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+@pytest.mark.parametrize("ntok", [1, 2, 5, 8])
+def test_decode_tokens(dtype, D, ntok):
+    """ntok draft tokens per sequence in one pass: outputs, final state and the
+    state after every token against the oracle's recurrence with a snapshot
+    after every token."""
+    N, H = 3, 2
+    print(f"[case] decode_tokens N={N} H={H} ntok={ntok} D={D} {dtype}", flush=True)
+    d = ki.gen_prefill(N, H, ntok, D, D, dtype, seed=600 + ntok, s0_std=0.1)
+    g = to_dev(d)
+    S_out = torch.empty_like(g["S0"])
+    o, S_pos = kda.decode_tokens(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], S_out=S_out,
+                                 positions=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g["S0"].cpu(), d["S0"])  # the input state is left as it was
+    o_ref, S_ref, pos_ref = oracle.prefill_snap(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], 1, d["S0"])
+    eo = oracle.max_rel_l2(o.cpu(), o_ref, floor=1e-6)
+    es = oracle.max_rel_l2(S_out.cpu(), S_ref, floor=1e-6)
+    ep = oracle.max_rel_l2(S_pos.cpu(), pos_ref, lead=3, floor=1e-6)
+    print(f"    o {eo:.3e}  S {es:.3e}  per-token states {ep:.3e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype] and ep <= TOL[dtype]
+    assert torch.equal(S_pos[:, -1], S_out)
+
+
+def test_decode_tokens_equals_decode_steps():
+    """One call over 4 tokens gives bit for bit what 4 decode steps give, in place
+    (the same per-token arithmetic, with the state kept in registers)."""
+    N, H, D, ntok = 5, 3, 128, 4
+    d = ki.gen_prefill(N, H, ntok, D, D, "bf16", seed=620, s0_std=0.1)
+    g = to_dev(d)
+    S1 = g["S0"].clone()
+    o1, _ = kda.decode_tokens(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], S1)  # in place
+    S2 = g["S0"].clone()
+    o2 = torch.empty_like(o1)
+    for t in range(ntok):
+        x = {n: g[n][:, :, t].contiguous() for n in ("q", "k", "v", "log_alpha", "beta")}
+        o2[:, :, t] = kda.decode_step(x["q"], x["k"], x["v"], x["log_alpha"], x["beta"], S2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_decode_tokens_zero_tokens_copies_state():
+    d = ki.gen_prefill(2, 2, 0, 64, 64, "bf16", seed=621, s0_std=0.1)
+    g = to_dev(d)
+    S_out = torch.zeros_like(g["S0"])
+    o, S_pos = kda.decode_tokens(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], S_out=S_out,
+                                 positions=True)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 2, 0, 64) and S_pos.shape == (2, 0, 2, 64, 64)
+    assert torch.equal(S_out, g["S0"])
+
+
+def test_full_decode_tokens_n256_h32():
+    """256 sequences x 32 heads verify 4 draft tokens each in one call (the
+    benchmark's launch), with per-token rollback states; sampled heads against
+    the oracle."""
+    print("[case] full decode_tokens n256_h32 x4", flush=True)
+    N, H, D, ntok = 256, 32, 128, 4
+    g = ki.gen_prefill(N, H, ntok, D, D, "bf16", seed=630, device=dev(), s0_std=0.1)
+    S_out = torch.empty_like(g["S0"])
+    o, S_pos = kda.decode_tokens(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], S_out=S_out,
+                                 positions=True)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for (n, h) in ((0, 0), (101, 7), (255, 31)):
+        sl = lambda t: t[n:n + 1, h:h + 1].cpu()
+        o_ref, S_ref, pos_ref = oracle.prefill_snap(sl(g["q"]), sl(g["k"]), sl(g["v"]), sl(g["log_alpha"]),
+                                                    sl(g["beta"]), 1, sl(g["S0"]))
+        worst = max(worst, oracle.rel_l2(o[n, h].cpu(), o_ref[0, 0]), oracle.rel_l2(S_out[n, h].cpu(), S_ref[0, 0]),
+                    oracle.max_rel_l2(S_pos[n:n + 1, :, h:h + 1].cpu(), pos_ref, lead=3))
+    print(f"    sampled heads: {worst:.3e}", flush=True)
+    assert worst <= TOL["bf16"]
