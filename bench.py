@@ -40,10 +40,11 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "feda59e7c47d0156",
-    "segment_transfer": 1.4133e9 + 0.0294e9,
-    "segment_merge": 0.0295e9 + 0.0168e9,
-    "segment_prefill": 2.1690e9 + 0.5390e9,
+    "sources_sha": "5044fefa8277453d",
+    "direct_part": 0.2254e9 + 0.0582e9,
+    "segment_transfer": 1.2698e9 + 0.0294e9,
+    "segment_merge": 0.0316e9 + 0.0168e9,
+    "segment_prefill": 1.9443e9 + 0.4829e9,
     "decode_step": 0.5455e9 + 0.5390e9,
 }
 
@@ -258,8 +259,10 @@ def bench_decode_tokens(args, dev, ntok=4):
     sequences x 32 heads in one call (state read and written once), with and
     without the per-token rollback states."""
     N, H, D = 256, 32, 128
-    g = ki.gen_prefill(N, H, ntok, D, D, "bf16", seed=5, device=dev, s0_std=0.1)
-    S = g["S0"]
+    # token t's inputs are decode step t's draws (one generator per token, over all heads)
+    steps = [ki.gen_decode_step(N, H, D, D, "bf16", seed=5, step=t, device=dev) for t in range(ntok)]
+    g = {n: torch.stack([x[n] for x in steps], dim=2).contiguous() for n in steps[0]}
+    S = ki.gen_decode_state(N, H, D, D, seed=5, device=dev)
     S_out = torch.empty_like(S)
     o = torch.empty(N, H, ntok, D, dtype=torch.bfloat16, device=dev)
     S_pos = torch.empty(N, ntok, H, D, D, dtype=torch.float32, device=dev)
@@ -350,6 +353,7 @@ def main():
                     help="consecutive decode steps timed (the workload is 1024)")
     ap.add_argument("--no-kcp", action="store_true")
     ap.add_argument("--no-snap", action="store_true")
+    ap.add_argument("--no-tokens", action="store_true", help="skip the several-token decode")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -430,7 +434,7 @@ def main():
     if not args.no_decode:
         out["decode"] = bench_decode(args, dev)
         torch.cuda.empty_cache()
-    if not args.no_decode:
+    if not args.no_decode and not args.no_tokens:
         out["decode_tokens"] = bench_decode_tokens(args, dev)
         torch.cuda.empty_cache()
     if not args.no_kcp:
