@@ -108,10 +108,11 @@ __device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t off) {
 }
 
 // DPP moves within rows of 16 lanes (gfx9 encoding): row_shr:n shifts values
-// n lanes up inside the row (lanes below n read 0).
+// n lanes up inside the row; lanes below n read 0 (bound control), so no old
+// value has to be materialised.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 constexpr int DPP_ROW_SHR = 0x110;
 
@@ -264,6 +265,23 @@ struct ChunkKernel {
   // Each register of r is refilled with chunk `next` as soon as it has been
   // read, so the prefetch loads issue spread over this VALU-heavy phase rather
   // than in one burst.
+  // The lane's LDS store offsets of phase 1, fixed for the whole loop:
+  // [token row i][channel half] in the [CH][D] tiles, and per channel in Kb^T.
+  uint32_t p_td[4][2], p_kt[8];
+  __device__ __forceinline__ void init_p1_offsets() {
+    const int ln = fresh_lane(l);
+    const int tg = ln & 15;
+    const int ch = 32 * (wave - NC) + 8 * (ln >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf)
+        p_td[i][hlf] = C::BF ? td(4 * tg + i, 2 * kp(ch + 4 * hlf)) : td(4 * tg + i, 4 * (ch + 4 * hlf));
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      p_kt[c] = C::BF ? swz<C::R_DT>(ch + c, 2 * kp(4 * tg)) : swz<C::R_DT>(ch + c, 4 * 4 * tg);
+  }
+
   __device__ __forceinline__ void p1(ProdRaw<T>& r, uint32_t st, int next) {
     const int ln = fresh_lane(l);
     const int pw = wave - NC;
@@ -298,7 +316,6 @@ struct ChunkKernel {
     float kb[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 4 * tg + i;
       float kk[8], qq[8], vq[8], vkh[8];
       raw_f32<T>(r.k[i], kk);
       if constexpr (PREFILL) raw_f32<T>(r.q[i], qq);
@@ -330,7 +347,7 @@ struct ChunkKernel {
             b[c] = (bf16)kb[i][4 * hlf + c];
             qv[c] = (bf16)vq[4 * hlf + c];
           }
-          const uint32_t o = td(row, 2 * kp(ch + 4 * hlf));
+          const uint32_t o = p_td[i][hlf];
           lds_st<bf16x4>(smem, st + C::S_KH + o, h);
           lds_st<bf16x4>(smem, C::X_KB + o, b);
           if constexpr (PREFILL) lds_st<bf16x4>(smem, st + C::S_QH + o, qv);
@@ -340,11 +357,11 @@ struct ChunkKernel {
         for (int hlf = 0; hlf < 2; ++hlf) {
           f32x4 h = {vkh[4 * hlf], vkh[4 * hlf + 1], vkh[4 * hlf + 2], vkh[4 * hlf + 3]};
           f32x4 b = {kb[i][4 * hlf], kb[i][4 * hlf + 1], kb[i][4 * hlf + 2], kb[i][4 * hlf + 3]};
-          lds_st<f32x4>(smem, st + C::S_KH + td(row, 4 * (ch + 4 * hlf)), h);
-          lds_st<f32x4>(smem, C::X_KB + td(row, 4 * (ch + 4 * hlf)), b);
+          lds_st<f32x4>(smem, st + C::S_KH + p_td[i][hlf], h);
+          lds_st<f32x4>(smem, C::X_KB + p_td[i][hlf], b);
           if constexpr (PREFILL) {
             f32x4 qv = {vq[4 * hlf], vq[4 * hlf + 1], vq[4 * hlf + 2], vq[4 * hlf + 3]};
-            lds_st<f32x4>(smem, st + C::S_QH + td(row, 4 * (ch + 4 * hlf)), qv);
+            lds_st<f32x4>(smem, st + C::S_QH + p_td[i][hlf], qv);
           }
         }
       }
@@ -352,14 +369,13 @@ struct ChunkKernel {
     // Kb^T: channel-major, 4 consecutive tokens per lane and channel
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int rowc = ch + c;
       if constexpr (C::BF) {
         bf16x4 t4;
         t4[0] = (bf16)kb[0][c]; t4[1] = (bf16)kb[1][c]; t4[2] = (bf16)kb[2][c]; t4[3] = (bf16)kb[3][c];
-        lds_st<bf16x4>(smem, st + C::S_KT + swz<C::R_DT>(rowc, 2 * kp(4 * tg)), t4);
+        lds_st<bf16x4>(smem, st + C::S_KT + p_kt[c], t4);
       } else {
         f32x4 t4 = {kb[0][c], kb[1][c], kb[2][c], kb[3][c]};
-        lds_st<f32x4>(smem, st + C::S_KT + swz<C::R_DT>(rowc, 4 * 4 * tg), t4);
+        lds_st<f32x4>(smem, st + C::S_KT + p_kt[c], t4);
       }
     }
     if (tg == 15) {
@@ -822,6 +838,7 @@ struct ChunkKernel {
   // variant, which keeps one set and prefetches one chunk ahead.
   __device__ __forceinline__ void producer_loop() {
     init_offsets();
+    init_p1_offsets();
     const int n = nch + C::LAG;
     if constexpr (TIGHT) {
       ProdRaw<T> r;
