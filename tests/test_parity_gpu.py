@@ -573,3 +573,26 @@ def test_full_decode_tokens_n256_h32():
                     oracle.max_rel_l2(S_pos[n:n + 1, :, h:h + 1].cpu(), pos_ref, lead=3))
     print(f"    sampled heads: {worst:.3e}", flush=True)
     assert worst <= TOL["bf16"]
+
+
+def test_prefill_snapshots_split_batched(monkeypatch):
+    """Snapshots on the sequence-split path with several sequences: each
+    sequence's snapshots land at [b, j, h] whichever segment writes them."""
+    es = run_snap_case(2, 3, 1500, 128, "bf16", 256, seed=540, split=3, monkeypatch=monkeypatch)
+    assert es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,H,T,P", [(2, 3, 1300, 3), (3, 2, 2100, 4)])
+def test_prefill_sequence_split_batched(B, H, T, P, monkeypatch):
+    """The split path with several sequences and heads (start states per
+    sequence, ragged last segment)."""
+    monkeypatch.setenv("KDA_SPLIT", str(P))
+    print(f"[case] split prefill B={B} H={H} T={T} P={P}", flush=True)
+    d = ki.gen_prefill(B, H, T, 128, 128, "bf16", seed=450 + P, s0_std=0.1, variant="slow")
+    g = to_dev(d)
+    o, S_T = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    eo, es = oracle.max_rel_l2(o.cpu(), o_ref), oracle.max_rel_l2(S_T.cpu(), S_ref)
+    print(f"    o {eo:.3e}  S_T {es:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
