@@ -567,19 +567,17 @@ struct ChunkKernel {
   static constexpr int C1B = 2;                    // row tiles per batch in c1
   static constexpr int C3B = TIGHT ? 2 : D / 32;   // state row tiles per batch in c3
 
-  // X_t = b_t (v_t - (Kh S)_t) for row tiles H0 .. H0+C1B-1 (fragments fetched first).
+  // X_t = b_t (v_t - (Kh S)_t) for row tiles H0 .. H0+C1B-1 (fragments fetched
+  // first).  X enters holding -v, so the products accumulate Kh S onto it and X
+  // ends as one multiply by -b.
   template <int H0>
-  __device__ __forceinline__ void c1_part(const VRaw& vr, uint32_t st, f32x4 (*X)[4]) {
+  __device__ __forceinline__ void c1_part(uint32_t st, f32x4 (*X)[4]) {
     typename F::A fk[C1B][NKD];
 #pragma unroll
     for (int h = 0; h < C1B; ++h)
 #pragma unroll
       for (int m = 0; m < NKD; ++m) fk[h][m] = ar<C::TD_TILE>(st + C::S_KH, oTD, H0 + h, m);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int h = 0; h < C1B; ++h) X[j][H0 + h] = zero4();
 #pragma unroll
     for (int m = 0; m < NKD; ++m)
 #pragma unroll
@@ -593,14 +591,13 @@ struct ChunkKernel {
 #pragma unroll
       for (int j = 0; j < NCT; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          X[j][H0 + h][e] = bet[e] * (vval(vr, j, 4 * (H0 + h) + e) - X[j][H0 + h][e]);
+        for (int e = 0; e < 4; ++e) X[j][H0 + h][e] = -bet[e] * X[j][H0 + h][e];
     }
   }
 
   // Tight variant of the X computation: one k block at a time over all four row
   // tiles, so only that block of the bf16 copy of S is live (the segment pass
-  // has no later use for it).
+  // has no later use for it).  X enters holding -v, as in c1_part.
   template <int M>
   __device__ __forceinline__ void c1_kblock(uint32_t st, f32x4 (*X)[4]) {
     typename F::A fk[4];
@@ -613,7 +610,7 @@ struct ChunkKernel {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int j = 0; j < NCT; ++j) X[j][t] = F::mma(M == 0 ? zero4() : X[j][t], fk[t], bm[j]);
+      for (int j = 0; j < NCT; ++j) X[j][t] = F::mma(X[j][t], fk[t], bm[j]);
   }
   template <int M>
   __device__ __forceinline__ void c1_kblocks(uint32_t st, f32x4 (*X)[4]) {
@@ -624,9 +621,8 @@ struct ChunkKernel {
   }
 
   // Delta from (I + L) Delta = diag(b) (V - Kh S) by 16-row blocks:
-  // Delta_i = T_ii (X_i + sum_{j<i} (-L_ij) Delta_j).
-  __device__ __forceinline__ void c1(const VRaw& vr, uint32_t st) {
-    f32x4 X[NCT][4];
+  // Delta_i = T_ii (X_i + sum_{j<i} (-L_ij) Delta_j).  X holds -v on entry.
+  __device__ __forceinline__ void c1(f32x4 (*X)[4], uint32_t st) {
     if constexpr (TIGHT) {
       c1_kblocks<0>(st, X);
       const int kk = 4 * (l >> 4);
@@ -636,15 +632,15 @@ struct ChunkKernel {
 #pragma unroll
         for (int j = 0; j < NCT; ++j)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) X[j][t][e] = bet[e] * (vval(vr, j, 4 * t + e) - X[j][t][e]);
+          for (int e = 0; e < 4; ++e) X[j][t][e] = -bet[e] * X[j][t][e];
       }
     } else {
 #pragma unroll
       for (int j = 0; j < NCT; ++j)
 #pragma unroll
         for (int m = 0; m < NKD; ++m) sb[j][m] = F::bfrag(S[j], m);
-      c1_part<0>(vr, st, X);
-      c1_part<2>(vr, st, X);
+      c1_part<0>(st, X);
+      c1_part<2>(st, X);
     }
     A16 ft[4], fl[4][4];
     const uint32_t lo = (uint32_t)fresh_lane(l) * 4 * C::ES;
@@ -796,8 +792,21 @@ struct ChunkKernel {
   }
 
   __device__ __forceinline__ void chain(VRaw& vr, int cc) {
-    c1(vr, stage(cc));
-    load_v(vr, cc + 1);  // on every path (reads zero past the end), as for the producers
+    // The value rows seed the accumulators of Kh S (as -v), which frees their
+    // registers for the next chunk's rows before the chain's products start.
+    // The three-waves-per-SIMD variant has no registers to spare for rows in
+    // flight during the products and loads them after the solve.  The loads are
+    // issued on every path (rows past the end read zero), as for the producers.
+    f32x4 X[NCT][4];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[j][t][e] = -vval(vr, j, 4 * t + e);
+    if constexpr (!TIGHT) load_v(vr, cc + 1);
+    c1(X, stage(cc));
+    if constexpr (TIGHT) load_v(vr, cc + 1);
     c2(stage(cc), cc);
     c3(stage(cc));
     snapshot(cc);
