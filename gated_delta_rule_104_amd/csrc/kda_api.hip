@@ -92,8 +92,9 @@ int pick_nc(long long nseq, int ncol_tiles, bool bf16_io, bool allow8 = false) {
 // T0 is chosen so that the direct prefill and the segment pass, which run side
 // by side, end together: running beside each other, the segment pass costs
 // about 15/16 of the prefill per token (it skips q and the outputs but carries
-// twice the state columns); 11/16 to 17/16 were measured at 64K tokens and 32
-// heads, 15/16 being fastest.
+// twice the state columns); 11/16 to 19/16 were measured at 64K tokens and 32
+// heads, 15/16 and 16/16 being fastest (within 1%).  KDA_TRANSFER_COST16
+// overrides the ratio for tuning.
 struct PrefillPlan {
   bool split = false;
   int T0 = 0, G = 1, Tseg = 0;
@@ -120,11 +121,14 @@ PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
     if (G > T / 1024) G = T / 1024;
     if (G < 2) return pl;
   }
+  const char* cenv = getenv("KDA_TRANSFER_COST16");
+  long long cost16 = cenv ? atoll(cenv) : kTransferCost16;
+  if (cost16 < 1 || cost16 > 64) cost16 = kTransferCost16;
   for (; G >= 2; --G) {
-    // T = T0 + (G - 1) * Tseg + last, 0 < last <= Tseg, T0 ~ (13/16) Tseg
-    const long long unit = 64LL * (16 * G + kTransferCost16);
+    // T = T0 + (G - 1) * Tseg + last, 0 < last <= Tseg, T0 ~ (cost16/16) Tseg
+    const long long unit = 64LL * (16 * G + cost16);
     long long Tseg = (16LL * T + unit - 1) / unit * 64;
-    long long T0 = kTransferCost16 * Tseg / 16 / 64 * 64;
+    long long T0 = cost16 * Tseg / 16 / 64 * 64;
     if (T0 < 64) T0 = 64;
     if (T - T0 > G * Tseg) T0 = (T - G * Tseg + 63) / 64 * 64;
     const long long last = T - T0 - (G - 1) * Tseg;
