@@ -40,11 +40,11 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "5044fefa8277453d",
+    "sources_sha": "cacb9b9d0e161424",
     "direct_part": 0.2254e9 + 0.0582e9,
     "segment_transfer": 1.2698e9 + 0.0294e9,
     "segment_merge": 0.0316e9 + 0.0168e9,
-    "segment_prefill": 1.9443e9 + 0.4829e9,
+    "segment_prefill": 1.9443e9 + 0.4830e9,
     "decode_step": 0.5455e9 + 0.5390e9,
 }
 
@@ -346,8 +346,8 @@ def cpu_baseline(pf, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024,
                     help="consecutive decode steps timed (the workload is 1024)")
