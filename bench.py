@@ -4,8 +4,14 @@ One step = one kda_chunk_prefill call over B=1, H=32, T=65536, dk=dv=128, bf16
 inputs (seeded synthetic data already resident in HBM, S0 = 0).  `value` is
 sequence tokens per second of that step.  The same run also measures, outside
 the timed steps:
+  * the per-kernel durations of the sequence-split path, through the public
+    calls it is made of (the roofline line is the slowest of them);
+  * the same prefill with a state snapshot every 512 tokens;
+  * the batched prefill B=4, H=32, T=8192 with an fp32 start state;
   * decode: 1024 consecutive kda_decode_step calls on 256 sequences x 32 heads
     (fp32 state 512 MiB in place), reported as % of HBM bandwidth;
+  * decode_tokens: 4 draft tokens per sequence in one call, with and without
+    the per-token states;
   * kcp: kda_segment_transfer + kda_segment_merge on T = 1,048,576 in 8
     segments of 131,072 (H = 32), reported as time and effective bandwidth;
   * cpu_baseline: the fp64 oracle on a bounded sample of the prefill workload.
@@ -196,6 +202,34 @@ def bench_prefill(args, dev):
     return dict(B=B, H=H, T=T, D=D, mean_ms=mean_ms, wall_ms=wall_ms, per=per, g=g, ws_bytes=nws)
 
 
+def bench_prefill_batched(args, dev):
+    """The batched prefill workload B=4, H=32, T=8192, d=128 (bf16 inputs, fp32
+    start state): time per call, tokens/s and the fractions of the MFMA and HBM
+    roofs, measured after the headline steps."""
+    B, H, T, D = 4, 32, 8192, 128
+    print(f"[bench] generating prefill inputs B={B} H={H} T={T} D={D} bf16", file=sys.stderr, flush=True)
+    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=1, s0_std=0.1, device=dev)
+    o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    nws = kda.prefill_workspace_bytes(B, H, T, D, D, torch.bfloat16)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+
+    def call():
+        kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], o=o, S_T=S_T, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ms, _ = time_launches(call, max(5, args.steps))
+    nbytes = prefill_bytes(B, H, T, D) + B * H * D * D * 4  # + the start state read
+    fl = prefill_flops(B, H, T, D)
+    del g, o, ws
+    return {"B": B, "H": H, "T": T, "D": D, "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "mfma_dense_tile_frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "plan": list(kda.prefill_plan(B, H, T, D, D, torch.bfloat16))}
+
+
 def bench_snapshots(pf, args, interval=512):
     """The same prefill with a state snapshot every `interval` tokens (prefix
     caching): time per call, the snapshot bytes written, and the cost over the
@@ -353,6 +387,7 @@ def main():
                     help="consecutive decode steps timed (the workload is 1024)")
     ap.add_argument("--no-kcp", action="store_true")
     ap.add_argument("--no-snap", action="store_true")
+    ap.add_argument("--no-batched", action="store_true", help="skip the B=4 T=8192 prefill")
     ap.add_argument("--no-tokens", action="store_true", help="skip the several-token decode")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -430,6 +465,9 @@ def main():
         out["prefill_kernels"] = dec
     if not args.no_snap:
         out["snapshots"] = bench_snapshots(pf, args)
+        torch.cuda.empty_cache()
+    if not args.no_batched:
+        out["prefill_b4_h32_t8k"] = bench_prefill_batched(args, dev)
         torch.cuda.empty_cache()
     if not args.no_decode:
         out["decode"] = bench_decode(args, dev)
