@@ -80,19 +80,25 @@ struct ChunkCfg {
   static constexpr int KB = BF ? 32 : 16;  // MFMA depth of the dense products
   static constexpr int JPB = KB / 16;      // 16x16 tiles per 16-byte lane slot of P
   static constexpr int FR16 = 64 * 4 * ES; // one 16x16 tile as 16-deep fragments
-  // stage: everything the chain of one chunk reads
+  // stage: everything the chain of one chunk reads.  bf16: Kb is kept
+  // time-major only; the chain reads it as Kb^T with transposing LDS reads.
+  // fp32 (no 16-bit transposing read): a channel-major copy Kb^T sits in the
+  // stage and the time-major Kb, which only the score tiles read, in scratch.
   static constexpr uint32_t S_KH = 0;                                   // Kh   [CH][D]
   static constexpr uint32_t S_QH = S_KH + TD_SZ;                        // Qh   [CH][D]
-  static constexpr uint32_t S_KT = S_QH + (PREFILL ? TD_SZ : 0);        // Kb^T [D][CH]
-  static constexpr uint32_t S_L = S_KT + D * R_DT;                      // -L_IJ, J < I: 6 x FR16
+  static constexpr uint32_t S_KB = S_QH + (PREFILL ? TD_SZ : 0);        // Kb [CH][D] (bf16) / Kb^T [D][CH]
+  static constexpr uint32_t S_L = S_KB + (BF ? TD_SZ : D * R_DT);       // -L_IJ, J < I: 6 x FR16
   static constexpr uint32_t S_P = S_L + 6 * FR16;                       // P: [4][CH/KB][64] slots
   static constexpr uint32_t S_TI = S_P + (PREFILL ? 4 * (CH / KB) * 64 * 16 : 0);  // T_ii: 4 x FR16
   static constexpr uint32_t S_GM = S_TI + 4 * FR16;                     // Gam  [D] fp32
   static constexpr uint32_t S_BETA = S_GM + D * 4;                      // beta [CH] fp32
   static constexpr uint32_t STAGE = S_BETA + CH * 4;
-  // producer scratch: Kb time-major, the B operand of the score products
+  // Kb time-major for the score products: in the stage (bf16) or in producer
+  // scratch after the stages (fp32)
   static constexpr uint32_t X_KB = STAGES * STAGE;
-  static constexpr uint32_t LDS = X_KB + TD_SZ;
+  static constexpr uint32_t LDS = X_KB + (BF ? 0 : TD_SZ);
+  // where the score products find Kb of the chunk in stage st
+  __device__ __forceinline__ static uint32_t kb_td(uint32_t st) { return BF ? st + S_KB : X_KB; }
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(LDS % 16 == 0 && STAGE % 16 == 0, "LDS alignment");
 };
@@ -222,6 +228,9 @@ struct ChunkKernel {
   // row within 16, so row tile t adds 16*t*rowbytes).  [k block]
   // (token-by-token tiles and channel-by-token tiles have the same row size.)
   uint32_t oTD[NKD], oDT[NKT];
+  // bf16: per-lane LDS byte offsets of the transposing reads of Kb^T fragments,
+  // for row tile pair a (channels 32a .. 32a+31), row tile 0 of the time-major Kb
+  uint32_t oTR[D / 32];
 
   __device__ __forceinline__ uint32_t stage(int chunk) const {
     return (C::STAGES == 2 ? (uint32_t)(chunk & 1) : 0u) * C::STAGE;
@@ -279,7 +288,7 @@ struct ChunkKernel {
         p_td[i][hlf] = C::BF ? td(4 * tg + i, 2 * kp(ch + 4 * hlf)) : td(4 * tg + i, 4 * (ch + 4 * hlf));
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      p_kt[c] = C::BF ? swz<C::R_DT>(ch + c, 2 * kp(4 * tg)) : swz<C::R_DT>(ch + c, 4 * 4 * tg);
+      p_kt[c] = C::BF ? 0u : swz<C::R_DT>(ch + c, 4 * 4 * tg);  // (fp32 only)
   }
 
   __device__ __forceinline__ void p1(ProdRaw<T>& r, uint32_t st, int next) {
@@ -349,7 +358,7 @@ struct ChunkKernel {
           }
           const uint32_t o = p_td[i][hlf];
           lds_st<bf16x4>(smem, st + C::S_KH + o, h);
-          lds_st<bf16x4>(smem, C::X_KB + o, b);
+          lds_st<bf16x4>(smem, st + C::S_KB + o, b);
           if constexpr (PREFILL) lds_st<bf16x4>(smem, st + C::S_QH + o, qv);
         }
       } else {
@@ -366,16 +375,12 @@ struct ChunkKernel {
         }
       }
     }
-    // Kb^T: channel-major, 4 consecutive tokens per lane and channel
+    // fp32: Kb^T, channel-major, 4 consecutive tokens per lane and channel
+    if constexpr (!C::BF) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      if constexpr (C::BF) {
-        bf16x4 t4;
-        t4[0] = (bf16)kb[0][c]; t4[1] = (bf16)kb[1][c]; t4[2] = (bf16)kb[2][c]; t4[3] = (bf16)kb[3][c];
-        lds_st<bf16x4>(smem, st + C::S_KT + p_kt[c], t4);
-      } else {
+      for (int c = 0; c < 8; ++c) {
         f32x4 t4 = {kb[0][c], kb[1][c], kb[2][c], kb[3][c]};
-        lds_st<f32x4>(smem, st + C::S_KT + p_kt[c], t4);
+        lds_st<f32x4>(smem, st + C::S_KB + p_kt[c], t4);
       }
     }
     if (tg == 15) {
@@ -415,7 +420,7 @@ struct ChunkKernel {
       // consumer's fragment offsets (both operands read the same positions,
       // which is a valid contraction in any consistent order)
       fx[m] = lds_ld<typename F::A>(smem, xbase + oTD[m]);
-      fb[m] = lds_ld<typename F::A>(smem, C::X_KB + J * C::TD_TILE + oTD[m]);
+      fb[m] = lds_ld<typename F::A>(smem, C::kb_td(st) + J * C::TD_TILE + oTD[m]);
     }
     float bl = 0.f;
     f32x4 bet4 = zero4();
@@ -528,6 +533,29 @@ struct ChunkKernel {
     for (int m = 0; m < NKD; ++m) oTD[m] = swz<C::R_TD>(r16, C::ES * (KB * m + kg));
 #pragma unroll
     for (int m = 0; m < NKT; ++m) oDT[m] = swz<C::R_DT>(r16, C::ES * (KB * m + kg));
+    if constexpr (C::BF) {
+      // lane i of lane group g reads channels 32a + 4(i%4) .. +3 (an even row
+      // tile; odd ones are 8 bytes further) of token row 4g + i/4
+      const int f = 4 * (l >> 4) + (r16 >> 2), q = r16 & 3;
+#pragma unroll
+      for (int a = 0; a < D / 32; ++a) oTR[a] = swz<C::R_TD>(f, 2 * kpos(32 * a + 4 * q));
+    }
+  }
+
+  // bf16 A fragment of Kb^T for state row tile ct (channels 16ct .. 16ct+15) and
+  // k block m (tokens 32m .. 32m+31, in the kpos order of the B fragments of
+  // Delta), read from the time-major Kb with two transposing 8-byte LDS reads.
+  // ds_read_b64_tr_b16 treats the 8-byte reads of a row of 16 lanes as a 16 x 4
+  // matrix E (lane i, element j) and returns E[4e + i/4][i % 4] as element e of
+  // lane i (checked on gfx950 with a probe of known LDS contents).  So lane i of
+  // lane group g, reading channels 16ct + 4(i%4) .. +3 of token 32m + 16h + 4g +
+  // i/4, receives tokens 32m + 16h + 4g + e of channel 16ct + i: half h of its
+  // fragment.
+  __device__ __forceinline__ bf16x8 kbt_frag(uint32_t st, int ct, int m) const {
+    const uint32_t base = st + C::S_KB + oTR[ct >> 1] + 8u * (uint32_t)(ct & 1);
+    const bf16x4 lo = lds_tr16(smem, base + (uint32_t)(2 * m) * C::TD_TILE);
+    const bf16x4 hi = lds_tr16(smem, base + (uint32_t)(2 * m + 1) * C::TD_TILE);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 
   // A fragment of row tile `t` and k block m of an LDS tile at `base`.
@@ -733,7 +761,10 @@ struct ChunkKernel {
 #pragma unroll
     for (int ci = 0; ci < NH; ++ci) {
 #pragma unroll
-      for (int m = 0; m < NKT; ++m) fk[ci][m] = ar<16 * C::R_DT>(st + C::S_KT, oDT, C0 + ci, m);
+      for (int m = 0; m < NKT; ++m) {
+        if constexpr (C::BF) fk[ci][m] = kbt_frag(st, C0 + ci, m);
+        else fk[ci][m] = ar<16 * C::R_DT>(st + C::S_KB, oDT, C0 + ci, m);
+      }
       gm[ci] = lds_ld<f32x4>(smem, st + C::S_GM + 4 * (16 * (C0 + ci) + kk));
     }
     __builtin_amdgcn_sched_barrier(0);

@@ -85,6 +85,16 @@ __device__ __forceinline__ void lds_st(char* smem, uint32_t off, V v) {
   *reinterpret_cast<V*>(smem + off) = v;
 }
 
+// Transposing 8-byte LDS read of 16-bit elements (ds_read_b64_tr_b16, gfx950):
+// see the chunk kernel's Kb^T fragments for the lane mapping.
+__device__ __forceinline__ bf16x4 lds_tr16(const char* smem, uint32_t off) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)const_cast<char*>(smem) + off));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
 // ---------------------------------------------------------------------------
 // MFMA wrappers.
 __device__ __forceinline__ f32x4 mfma_bf16_k32(f32x4 acc, bf16x8 a, bf16x8 b) {
