@@ -112,6 +112,31 @@ def test_prefill_plan(lib):
     assert lib.kda_prefill_plan(1, 1, 64, 64, 64, BF16, None, ctypes.byref(G), ctypes.byref(Ts)) == ERR_NULL
 
 
+def test_prefill_plan_cost_override(lib, monkeypatch):
+    """KDA_TRANSFER_COST16 (the segment pass's cost per token relative to the
+    prefill, in 16ths) moves the first part's length; the cut still covers T
+    exactly, and values outside 1..64 fall back to the built-in ratio."""
+    T0, G, Ts = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+
+    def plan(T=65536):
+        assert lib.kda_prefill_plan(1, 32, T, 128, 128, BF16, ctypes.byref(T0), ctypes.byref(G),
+                                    ctypes.byref(Ts)) == OK
+        return T0.value, G.value, Ts.value
+
+    monkeypatch.delenv("KDA_TRANSFER_COST16", raising=False)
+    default = plan()
+    first = {}
+    for c in ("11", "15", "19"):
+        monkeypatch.setenv("KDA_TRANSFER_COST16", c)
+        t0, g, ts = plan()
+        assert t0 % 64 == 0 and ts % 64 == 0 and t0 + (g - 1) * ts < 65536 <= t0 + g * ts
+        first[c] = t0 / ts
+    assert first["11"] < first["15"] < first["19"]
+    for bad in ("0", "65", "-3", "x"):
+        monkeypatch.setenv("KDA_TRANSFER_COST16", bad)
+        assert plan() == default
+
+
 def test_prefill_snap_validation(lib):
     """Snapshot interval: 0 (none) or a positive multiple of the 64-token chunk;
     the snapshot buffer is required only when at least one snapshot falls in T."""
