@@ -13,7 +13,8 @@ the timed steps:
   * decode_tokens: 4 draft tokens per sequence in one call, with and without
     the per-token states;
   * kcp: kda_segment_transfer + kda_segment_merge on T = 1,048,576 in 8
-    segments of 131,072 (H = 32), reported as time and effective bandwidth;
+    segments of 131,072 (H = 32), reported as time and effective bandwidth,
+    then kda_chunk_prefill_segments from the merged start states (outputs);
   * cpu_baseline: the fp64 oracle on a bounded sample of the prefill workload.
 Kernel durations come from HIP events recorded on the stream the kernels are
 launched on.  Prints one JSON line.
@@ -320,15 +321,21 @@ def bench_decode_tokens(args, dev, ntok=4):
 
 
 def bench_kcp(args, dev):
+    """The context-parallel decomposition on one GPU at T = 1,048,576 in 8
+    segments of 131,072 tokens (H = 32): the segment pass (each segment's
+    zero-start end state and transfer map), the sequential merge (every
+    segment's true start state), and the prefill of every segment from its start
+    state, which produces the outputs."""
     B, H, G, Tseg, D = 1, 32, 8, 131072, 128
     T = G * Tseg
     print(f"[bench] generating kcp inputs H={H} T={T} G={G}", file=sys.stderr, flush=True)
     g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=3, device=dev)
-    del g["q"]
     Z = torch.empty(G, B, H, D, D, dtype=torch.float32, device=dev)
     M = torch.empty(G, B, H, D, D, dtype=torch.float32, device=dev)
     S_start = torch.empty_like(Z)
     S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    S_T2 = torch.empty_like(S_T)
+    o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
 
     def transfer():
         kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], G, S_zero_end=Z, M=M)
@@ -336,15 +343,23 @@ def bench_kcp(args, dev):
     def merge():
         kda.segment_merge(Z, M, None, S_start=S_start, S_T=S_T)
 
-    transfer(); merge()
+    def prefill():
+        kda.prefill_segments(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], S_start, Tseg, o=o, S_T=S_T2)
+
+    transfer(); merge(); prefill()
     torch.cuda.synchronize()
     t_ms, _ = time_launches(transfer, 3)
     m_ms, _ = time_launches(merge, 3)
+    p_ms, _ = time_launches(prefill, 3)
     nbytes = B * H * T * (2 * (2 * D + D) + 2) + 2 * G * B * H * D * D * 4
-    del g
+    pbytes = segment_prefill_bytes(B, H, T, D, G)
+    del g, o
     return dict(H=H, T=T, G=G, Tseg=Tseg, transfer_ms=t_ms, merge_ms=m_ms,
                 tokens_per_s=T / ((t_ms + m_ms) * 1e-3),
-                transfer_GBs=nbytes / (t_ms * 1e-3) / 1e9)
+                transfer_GBs=nbytes / (t_ms * 1e-3) / 1e9,
+                segment_prefill_ms=p_ms, segment_prefill_GBs=pbytes / (p_ms * 1e-3) / 1e9,
+                with_outputs_ms=t_ms + m_ms + p_ms,
+                with_outputs_tokens_per_s=T / ((t_ms + m_ms + p_ms) * 1e-3))
 
 
 def cpu_baseline(pf, budget_s):
