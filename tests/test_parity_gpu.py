@@ -324,11 +324,14 @@ def test_full_kcp_h32_t1m():
     transfer map, whose 2-norm is at most prod_t max_i alpha_{t,i} (each factor
     (I - b k k^T) Diag(alpha) has norm <= max_i alpha_i for b in [0,1] and
     |k| ~ 1); the test computes that bound from the inputs and requires it to be
-    far below fp32 resolution, so the window result equals the full-segment one."""
+    far below fp32 resolution, so the window result equals the full-segment one.
+    Then every segment is prefilled from its merged start state, and the outputs
+    are checked on windows that straddle a segment boundary (so they depend on
+    the merged start state) and inside a segment, by the same argument: the
+    oracle runs from a zero state W tokens before the checked tokens."""
     print("[case] full kcp_h32_t1m", flush=True)
     B, H, G, Tseg, D, W = 1, 32, 8, 131072, 128, 2048
     g = gpu_inputs(B, H, G * Tseg, D, seed=3)
-    del g["q"]
     Z, M = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], G)
     S_start, S_T = kda.segment_merge(Z, M, None)
     torch.cuda.synchronize()
@@ -351,6 +354,21 @@ def test_full_kcp_h32_t1m():
         em = oracle.rel_l2(M[i, :, h:h + 1].cpu(), Mr[0], floor=1e-3)
         print(f"    segment {i} head {h}: Z {ez:.3e}  M {em:.3e}  (log window bound {log_bound:.0f})", flush=True)
         assert ez <= TOL["bf16"] and em <= TOL["bf16"]
+    # outputs: the prefill of every segment from its merged start state
+    o, S_T2 = kda.prefill_segments(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], S_start, Tseg)
+    torch.cuda.synchronize()
+    assert torch.equal(S_T2, S_T) or oracle.rel_l2(S_T2.cpu(), S_T.cpu(), floor=1e-3) <= TOL["bf16"]
+    n_chk = 512
+    for (t1, h) in ((3 * Tseg + 256, 5), (5 * Tseg + 70000, 26), (7 * Tseg + 64, 12)):
+        t0 = t1 - n_chk - W
+        burn = slice(t0, t0 + W)
+        log_bound = float(g["log_alpha"][0, h, burn].float().max(dim=-1).values.sum())
+        assert log_bound < -100.0, log_bound
+        win = [g[n][:, h:h + 1, t0:t1].cpu() for n in ("q", "k", "v", "log_alpha", "beta")]
+        o_ref, _ = oracle.prefill(*win)
+        eo = oracle.rel_l2(o[:, h:h + 1, t1 - n_chk:t1].cpu(), o_ref[:, :, W:], floor=1e-3)
+        print(f"    outputs of head {h}, tokens [{t1 - n_chk}, {t1}): {eo:.3e}", flush=True)
+        assert eo <= TOL["bf16"]
 
 
 def test_full_decode_n256_h32():
