@@ -29,8 +29,14 @@
  *    on error nothing is written and a status != KDA_OK is returned, with a
  *    description in kda_last_error() (thread-local).  Work is enqueued
  *    asynchronously on `stream`; a launch failure returns KDA_ERR_HIP.
- *  - Calls never abort the process and keep no mutable global state other than
- *    a per-device cache of the compute-unit count.
+ *  - Calls never abort the process.  The only global state is per device and
+ *    created on first use: the compute-unit count, and for the sequence-split
+ *    prefill a second stream with two events (kept for the process lifetime).
+ *  - Environment overrides, for tuning and tests only: KDA_SPLIT (segments of
+ *    the sequence-split prefill; 0 = never split), KDA_TRANSFER_COST16 (the
+ *    first part's length ratio, in 16ths), KDA_NC (consumer waves per
+ *    workgroup), KDA_LOG (print each launch's shape to stderr).  Every choice
+ *    they make gives the same result up to rounding.
  */
 #ifndef LIBKDA_H
 #define LIBKDA_H
