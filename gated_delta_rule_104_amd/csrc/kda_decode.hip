@@ -73,14 +73,39 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const T* __restrict__ q
   float* sak = s_v[wave][1];
   float* saq = s_v[wave][2];
   float* sk = s_v[wave][3];
+  // One token's inputs for this lane: its D/64 gate, key and query channels,
+  // its four value columns and beta.  With several tokens, token t + 1's are
+  // loaded while token t is applied, so only the first token's load latency is
+  // exposed (and that one overlaps the state load).
+  struct Tok {
+    float k[D / 64], q[D / 64], la[D / 64], v[4], b;
+  };
+  auto load_tok = [&](int t, Tok& x) {
+    const size_t tb = ((size_t)head * ntok + t) * D;
+#pragma unroll
+    for (int jj = 0; jj < D / 64; ++jj) {
+      x.k[jj] = ld1(k + tb + l + 64 * jj);
+      x.q[jj] = ld1(q + tb + l + 64 * jj);
+      x.la[jj] = ld1(la + tb + l + 64 * jj);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x.v[c] = ld1(v + tb + c0 + c);
+    x.b = ld1(beta + (size_t)head * ntok + t);
+  };
+  Tok cur;
+  if (ntok > 0) load_tok(0, cur);
   for (int t = 0; t < ntok; ++t) {
     const size_t tb = ((size_t)head * ntok + t) * D;  // row of token t
+    const bool more = !ONE && t + 1 < ntok;
+    Tok nxt;
+    if (more) load_tok(t + 1, nxt);
     // gate, key and query: the wave's lanes cover the D channels
     float kq = 0.f;
 #pragma unroll
-    for (int j = l; j < D; j += 64) {
-      const float kt = ld1(k + tb + j), qt = ld1(q + tb + j);
-      const float at = expf(ld1(la + tb + j));
+    for (int jj = 0; jj < D / 64; ++jj) {
+      const int j = l + 64 * jj;
+      const float kt = cur.k[jj], qt = cur.q[jj];
+      const float at = expf(cur.la[jj]);
       sa[j] = at;
       sak[j] = at * kt;
       saq[j] = at * qt;
@@ -112,10 +137,9 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const T* __restrict__ q
         u[c] += __shfl_xor(u[c], off);
         w[c] += __shfl_xor(w[c], off);
       }
-    const float b = ld1(beta + (size_t)head * ntok + t);
     float dl[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dl[c] = b * (ld1(v + tb + c0 + c) - u[c]);
+    for (int c = 0; c < 4; ++c) dl[c] = cur.b * (cur.v[c] - u[c]);
     if (rg == 0) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[tb + c0 + c] = from_f32<T>(w[c] + kq * dl[c]);
@@ -136,6 +160,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(const T* __restrict__ q
       for (int i = 0; i < RPL; ++i)
         __builtin_nontemporal_store(st[i], reinterpret_cast<f32x4*>(dst + (size_t)(r0 + i) * D + c0));
     }
+    if (more) cur = nxt;
   }
 #pragma unroll
   for (int i = 0; i < RPL; ++i)
