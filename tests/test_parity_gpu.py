@@ -416,6 +416,25 @@ def test_prefill_sequence_split(P, T, D, variant, monkeypatch):
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("cost16", ["11", "19"])
+def test_prefill_sequence_split_other_cut(cost16, monkeypatch):
+    """A different first-part length (KDA_TRANSFER_COST16) moves every segment
+    boundary; the outputs and end state still follow the recurrence."""
+    monkeypatch.setenv("KDA_SPLIT", "4")
+    monkeypatch.setenv("KDA_TRANSFER_COST16", cost16)
+    B, H, T, D = 1, 2, 3000, 128
+    print(f"[case] split prefill, cost16={cost16}, plan {kda.prefill_plan(B, H, T, D, D, torch.bfloat16)}",
+          flush=True)
+    d = ki.gen_prefill(B, H, T, D, D, "bf16", seed=430, s0_std=0.1, variant="slow")
+    g = to_dev(d)
+    o, S_T = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    eo, es = oracle.max_rel_l2(o.cpu(), o_ref), oracle.max_rel_l2(S_T.cpu(), S_ref)
+    print(f"    o {eo:.3e}  S_T {es:.3e}", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_prefill_split_without_workspace_falls_back(monkeypatch):
     monkeypatch.setenv("KDA_SPLIT", "4")
     d = ki.gen_prefill(1, 2, 500, 128, 128, "bf16", seed=410, s0_std=0.1, variant="slow")
