@@ -948,8 +948,16 @@ struct ChunkKernel {
       ro = make_rsrc(reinterpret_cast<const char*>(a.o) + base, rowbytes);
     }
 
-    for (uint32_t i = threadIdx.x * 16; i < C::LDS; i += C::THREADS * 16)
-      lds_st<u32x4>(smem, i, u32x4{0u, 0u, 0u, 0u});
+    // Every LDS byte the kernel reads is written by it first, except the halves
+    // of the 32-deep P lane slots that pair a diagonal tile with the tile above
+    // it (tiles (0,1) and (2,3)): nothing writes them, and they must hold the
+    // zeros of P's upper triangle.
+    if constexpr (PREFILL && C::JPB == 2) {
+      for (uint32_t t = threadIdx.x; t < 2u * 64u * C::STAGES; t += C::THREADS) {
+        const uint32_t slot = (t & 64u) ? 2u * (CH / KB) + 1u : 0u;  // (I = 2, m = 1) or (I = 0, m = 0)
+        lds_st<u32x2>(smem, (t >> 7) * C::STAGE + C::S_P + (slot * 64u + (t & 63u)) * 16u + 8u, u32x2{0u, 0u});
+      }
+    }
 
     colb = vs * 16 * NC * NCT + 16 * NCT * wave + NCT * (l & 15);
     isv = PREFILL || colb < D;  // a wave's tiles lie on one side of D
