@@ -863,10 +863,14 @@ struct ChunkKernel {
   // which prepares a chunk past the end (zero inputs) into the stage nobody
   // reads any more: with no data-dependent branches around the loads, the
   // compiler counts them exactly.
+  // The two-stage pipeline's last step prepares the chunk past the end, whose
+  // elementwise tiles nobody reads: its score tiles and their barrier are
+  // skipped by every wave alike (p1 stays, with its loads, on every path).
   template <int PD>
   __device__ __forceinline__ void producer_step(ProdRaw<T>& r, int it) {
     p1(r, stage(it), it + PD);
     sync_lds();
+    if (C::LAG && it == nch) return;
     p2(stage(it));
     sync_lds();
     if (!C::LAG) sync_lds();
@@ -905,7 +909,8 @@ struct ChunkKernel {
       const int cc = it - C::LAG;
       if (C::LAG && cc >= 0) chain(vr, cc);
       sync_lds();
-      p2(stage(it));  // (it == nch: the unread chunk past the end)
+      if (C::LAG && it == nch) break;  // the chunk past the end: no score tiles
+      p2(stage(it));
       sync_lds();
       if (!C::LAG) {
         chain(vr, cc);
