@@ -968,22 +968,36 @@ struct ChunkKernel {
     isv = PREFILL || colb < D;  // a wave's tiles lie on one side of D
     const size_t sbase = (size_t)seq * D * D;
     if (wave < NC) {
-#pragma unroll
-      for (int j = 0; j < NCT; ++j)
+      if (PREFILL && NCT == 2 && a.S0) {
+        // the lane's two adjacent columns of a row as one 8-byte load
+        const rsrc_t rs = make_rsrc(a.S0 + sbase, D * D * 4);
 #pragma unroll
         for (int ci = 0; ci < D / 16; ++ci)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 16 * ci + g4 + e;
-            const int c = colb + j;
-            float x = 0.f;
-            if (PREFILL) {
-              if (a.S0) x = a.S0[sbase + (size_t)r * D + c];
-            } else if (!isv) {
-              x = (r == c - D) ? 1.f : 0.f;
-            }
-            S[j][ci][e] = x;
+            const u32x2 x = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (uint32_t)((16 * ci + g4 + e) * D + colb) * 4u, 0, 0));
+            S[0][ci][e] = __uint_as_float(x[0]);
+            S[NCT - 1][ci][e] = __uint_as_float(x[1]);
           }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NCT; ++j)
+#pragma unroll
+          for (int ci = 0; ci < D / 16; ++ci)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 16 * ci + g4 + e;
+              const int c = colb + j;
+              float x = 0.f;
+              if (PREFILL) {
+                if (a.S0) x = a.S0[sbase + (size_t)r * D + c];
+              } else if (!isv) {
+                x = (r == c - D) ? 1.f : 0.f;
+              }
+              S[j][ci][e] = x;
+            }
+      }
       // Retire the start-state loads here: left pending into the chunk loop, they
       // make the compiler wait for every load and store in flight at the top of
       // each iteration (its count at the loop header merges in this path).
