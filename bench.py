@@ -47,7 +47,7 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "1032b9585f5ce19b",
+    "sources_sha": "ce47afdd3aaf9276",
     "direct_part": 0.2254e9 + 0.0582e9,
     "segment_transfer": 1.2698e9 + 0.0294e9,
     "segment_merge": 0.0316e9 + 0.0168e9,

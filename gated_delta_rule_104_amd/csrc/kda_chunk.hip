@@ -859,13 +859,11 @@ struct ChunkKernel {
   // loads in flight must be the same on all paths, or it waits for every
   // load, including the prefetch of the next chunk, before using a register set.
   //
-  // Every step does the same work, also the last one of a two-stage pipeline,
-  // which prepares a chunk past the end (zero inputs) into the stage nobody
-  // reads any more: with no data-dependent branches around the loads, the
-  // compiler counts them exactly.
-  // The two-stage pipeline's last step prepares the chunk past the end, whose
-  // elementwise tiles nobody reads: its score tiles and their barrier are
-  // skipped by every wave alike (p1 stays, with its loads, on every path).
+  // Every step runs the elementwise phase with its loads, also the last one of
+  // a two-stage pipeline, which prepares a chunk past the end (zero inputs)
+  // into the stage nobody reads any more: with no data-dependent branches
+  // around the loads, the compiler counts them exactly.  That step's score
+  // tiles and their barrier are skipped, by every wave alike.
   template <int PD>
   __device__ __forceinline__ void producer_step(ProdRaw<T>& r, int it) {
     p1(r, stage(it), it + PD);
