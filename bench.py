@@ -15,6 +15,8 @@ the timed steps:
   * kcp: kda_segment_transfer + kda_segment_merge on T = 1,048,576 in 8
     segments of 131,072 (H = 32), reported as time and effective bandwidth,
     then kda_chunk_prefill_segments from the merged start states (outputs);
+  * calibration: a large bf16 torch matmul and a device copy, the rates this
+    box reaches beside the spec peaks;
   * cpu_baseline: the fp64 oracle on a bounded sample of the prefill workload.
 Kernel durations come from HIP events recorded on the stream the kernels are
 launched on.  Prints one JSON line.
@@ -362,6 +364,31 @@ def bench_kcp(args, dev):
                 with_outputs_tokens_per_s=T / ((t_ms + m_ms + p_ms) * 1e-3))
 
 
+def bench_calibration(dev):
+    """What this machine reaches beside the spec peaks the fractions are taken
+    against: a large bf16 matrix product through torch (hipBLASLt) and a plain
+    device-to-device copy (read + write), each timed with events."""
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    mm_ms, _ = time_launches(lambda: torch.matmul(a, b), 10)
+    del a, b
+    nbytes = 1 << 30
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    cp_ms, _ = time_launches(lambda: dst.copy_(src), 10)
+    del src, dst
+    return {"bf16_gemm_8192_tflops": 2 * n ** 3 / (mm_ms * 1e-3) / 1e12,
+            "copy_1GiB_GBs": 2 * nbytes / (cp_ms * 1e-3) / 1e9,
+            "spec_bf16_tflops": PEAK_BF16_TFLOPS, "spec_hbm_GBs": PEAK_HBM_GBS}
+
+
 def cpu_baseline(pf, budget_s):
     """fp64 oracle on a bounded sample of the same prefill inputs: all heads and
     tokens if that fits in about `budget_s` seconds, else the first `nh` heads and
@@ -405,6 +432,7 @@ def main():
     ap.add_argument("--no-batched", action="store_true", help="skip the B=4 T=8192 prefill")
     ap.add_argument("--no-tokens", action="store_true", help="skip the several-token decode")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-calib", action="store_true", help="skip the GEMM and copy reference rates")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
@@ -492,6 +520,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_kcp:
         out["kcp"] = bench_kcp(args, dev)
+        torch.cuda.empty_cache()
+    if not args.no_calib:
+        out["calibration"] = bench_calibration(dev)
         torch.cuda.empty_cache()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(pf, args.cpu_budget)
