@@ -49,11 +49,11 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "ce47afdd3aaf9276",
-    "direct_part": 0.2254e9 + 0.0582e9,
-    "segment_transfer": 1.2698e9 + 0.0294e9,
+    "sources_sha": "23cda59e7dd1a229",
+    "direct_part": 0.1855e9 + 0.0482e9,
+    "segment_transfer": 1.3029e9 + 0.0294e9,
     "segment_merge": 0.0316e9 + 0.0168e9,
-    "segment_prefill": 1.9443e9 + 0.4830e9,
+    "segment_prefill": 1.9842e9 + 0.4929e9,
     "decode_step": 0.5455e9 + 0.5390e9,
 }
 

@@ -54,6 +54,14 @@ int cu_count() {
   return cache[dev];
 }
 
+// KDA_MAP_SKIP=0 keeps the segment pass updating map columns that have become
+// exactly zero (for tests that compare both ways); any other value, or none,
+// lets it stop.
+bool map_skip_enabled() {
+  const char* env = getenv("KDA_MAP_SKIP");
+  return !(env && env[0] == '0' && env[1] == '\0');
+}
+
 // Consumer waves per workgroup (each owns chunk_tiles_per_wave(bf16) 16-column
 // state tiles): the largest of 4, 2, 1 (fp32: 2, 1) that divides the column
 // tiles and still gives at least one workgroup per compute unit (or 1).
@@ -90,18 +98,20 @@ int pick_nc(long long nseq, int ncol_tiles, bool bf16_io, bool allow8 = false) {
 // independently.  The result is the same recurrence.
 //
 // T0 is chosen so that the direct prefill and the segment pass, which run side
-// by side, end together: running beside each other, the segment pass costs
-// about 15/16 of the prefill per token (it skips q and the outputs but carries
-// twice the state columns); 11/16 to 19/16 were measured at 64K tokens and 32
-// heads, 15/16 and 16/16 being fastest (within 1%).  KDA_TRANSFER_COST16
-// overrides the ratio for tuning.
+// by side, end together.  The segment pass skips q and the outputs but carries
+// twice the state columns, and stops updating map columns once they have
+// decayed to exact zero; running beside the prefill it costs about 12/16 of it
+// per token when the gates decay as fast as in the 64K-token, 32-head workload
+// (10/16 to 15/16 measured there: 12/16 fastest, 15/16 3% slower) and about
+// 15/16 when the map never reaches zero (11/16 to 19/16 within 1% of each
+// other).  KDA_TRANSFER_COST16 overrides the ratio for tuning.
 struct PrefillPlan {
   bool split = false;
   int T0 = 0, G = 1, Tseg = 0;
   size_t ws = 0;
 };
 
-constexpr int kTransferCost16 = 15;  // segment pass / prefill time per token, in 16ths
+constexpr int kTransferCost16 = 12;  // segment pass / prefill time per token, in 16ths
 
 PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
   PrefillPlan pl;
@@ -354,6 +364,7 @@ kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, c
     t.BH = (int)BH; t.G = G1; t.Tseg = Ts; t.Ttot = T; t.t0 = T0; t.Tend = T0 + G1 * Ts;
     const int nt2 = 2 * D / 16, nc2 = pick_nc(BH * G1, nt2, bf, D == 128);
     t.vsplit = nt2 / (nc2 * kda::chunk_tiles_per_wave(bf));
+    t.map_skip = map_skip_enabled();
     // the direct part: one workgroup per head (all of a head's column tiles) when
     // the segment pass leaves room for it, else the usual choice
     const int nc0 = BH * (G1 * t.vsplit + 1) <= cu_count() ? D / 16 / kda::chunk_tiles_per_wave(bf) : 0;
@@ -496,6 +507,7 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
   a.S0 = nullptr; a.o = nullptr; a.S_out = S_zero_end; a.M_out = M;
   a.BH = (int)BH; a.G = G; a.Tseg = Tseg; a.Ttot = G * Tseg; a.t0 = 0; a.Tend = G * Tseg;
   a.vsplit = ntiles / (nc * kda::chunk_tiles_per_wave(dtype == KDA_BF16));
+  a.map_skip = map_skip_enabled();
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (getenv("KDA_LOG"))

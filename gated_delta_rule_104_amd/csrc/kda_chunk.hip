@@ -221,6 +221,8 @@ struct ChunkKernel {
   int colb;         // global column of this lane in tile 0 (tile j: colb + j, so a
                     // lane's columns are adjacent and move as one 4-byte bf16 pair)
   bool isv;         // columns read v (value columns) rather than being map columns
+  bool mskip;       // segment pass: this wave owns map columns and may stop on zero
+  bool mzero;       // ... and they have all become exactly zero
   f32x4 S[NCT][D / 16];
   typename F::B sb[NCT][NKD], db[NCT][NKT];
   // Per-lane LDS byte offsets of the consumer's A fragments inside a tile of
@@ -843,6 +845,33 @@ struct ChunkKernel {
     snapshot(cc);
   }
 
+  // Segment pass: once a wave's map columns are all exactly zero they stay
+  // zero for finite inputs (their value rows are zero, and every step of the
+  // chain is linear in the columns it updates), so the wave stops running the
+  // chain for them and keeps only its share of the score tiles.  The columns are
+  // checked after every second chunk.
+  __device__ __forceinline__ void chain_step(VRaw& vr, int cc) {
+    if constexpr (!PREFILL) {
+      if (mzero) return;
+    }
+    chain(vr, cc);
+    if constexpr (!PREFILL) {
+      if (mskip && (cc & 1)) mzero = state_is_zero();
+    }
+  }
+
+  // every state entry of the wave is +0 or -0 (a wave-uniform answer)
+  __device__ __forceinline__ bool state_is_zero() const {
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int ci = 0; ci < D / 16; ++ci)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc |= __float_as_uint(S[j][ci][e]);
+    return __builtin_amdgcn_ballot_w64((acc & 0x7fffffffu) != 0u) == 0u;
+  }
+
   // Pipeline.  Iteration `it` prepares chunk it and runs the serial chain of
   // chunk it - LAG: interval 1 has the producer waves build the elementwise
   // tiles while the consumer waves run the chain; in interval 2 every wave
@@ -905,13 +934,13 @@ struct ChunkKernel {
     if (nch > 0) load_v(vr, 0);
     for (int it = 0; it < nch + C::LAG; ++it) {
       const int cc = it - C::LAG;
-      if (C::LAG && cc >= 0) chain(vr, cc);
+      if (C::LAG && cc >= 0) chain_step(vr, cc);
       sync_lds();
       if (C::LAG && it == nch) break;  // the chunk past the end: no score tiles
       p2(stage(it));
       sync_lds();
       if (!C::LAG) {
-        chain(vr, cc);
+        chain_step(vr, cc);
         sync_lds();
       }
     }
@@ -964,6 +993,8 @@ struct ChunkKernel {
 
     colb = vs * 16 * NC * NCT + 16 * NCT * wave + NCT * (l & 15);
     isv = PREFILL || colb < D;  // a wave's tiles lie on one side of D
+    mskip = !PREFILL && a.map_skip && __builtin_amdgcn_readfirstlane(isv ? 0 : 1);
+    mzero = false;
     const size_t sbase = (size_t)seq * D * D;
     if (wave < NC) {
       if (PREFILL && NCT == 2 && a.S0) {

@@ -35,6 +35,9 @@ struct ChunkArgs {
   int snap_chunks = 1;
   int nsnap = 0;
   int H = 1;        // heads per sequence batch entry (bh = b * H + h)
+  // segment pass: a wave stops updating its map columns once they are all
+  // exactly zero (they stay zero for finite inputs); 0 keeps updating them
+  int map_skip = 1;
 };
 
 // 16-column state tiles each consumer wave of the chunk kernel owns.

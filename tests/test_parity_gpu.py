@@ -127,6 +127,68 @@ def test_segment_pass_column_split_invariant(nc, monkeypatch):
     assert torch.equal(Z, Z1) and torch.equal(M, M1)
 
 
+@pytest.mark.parametrize("dtype,D,variant", [("bf16", 128, "none"), ("bf16", 128, "slow"),
+                                             ("bf16", 64, "none"), ("f32", 64, "none")])
+def test_segment_pass_map_skip_bit_identical(dtype, D, variant, monkeypatch):
+    """Map columns that have reached exact zero are no longer updated: the
+    states and maps equal those of a pass that keeps updating them."""
+    print(f"[case] map skip {dtype} D={D} {variant}", flush=True)
+    d = ki.gen_prefill(1, 3, 3 * 320, D, D, dtype, seed=64, variant=variant)
+    g = to_dev(d)
+    Z, M = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], 3)
+    monkeypatch.setenv("KDA_MAP_SKIP", "0")
+    Z1, M1 = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], 3)
+    torch.cuda.synchronize()
+    assert torch.equal(Z, Z1) and torch.equal(M, M1)
+
+
+def partial_decay_inputs(H, T, seed):
+    """k lives on channels 0..63 only, whose gates decay slowly; channels 64..127
+    decay at the lower bound (log alpha = -1).  The map's columns 64..127 then
+    stay e_j scaled by e^-t and reach exact zero in fp32 after two chunks, while
+    columns 0..63 stay far from zero."""
+    d = ki.gen_prefill(1, H, T, 128, 128, "bf16", seed=seed, s0_std=0.1, variant="slow")
+    k = d["k"].float()
+    k[..., 64:] = 0.0
+    k[..., :64] = k[..., :64] / k[..., :64].norm(dim=-1, keepdim=True)
+    d["k"] = k.to(torch.bfloat16)
+    la = d["log_alpha"].clone()
+    la[..., 64:] = -1.0
+    d["log_alpha"] = la
+    return d
+
+
+def test_segment_pass_map_partial_zero(monkeypatch):
+    """Half of the map's column blocks reach zero and stop, the other half keep
+    going; both match the oracle and a pass without the stop, and the split
+    prefill built on them reproduces the recurrence."""
+    H, G, Tseg = 2, 3, 320
+    print(f"[case] partial map zero H={H} G={G} Tseg={Tseg}", flush=True)
+    d = partial_decay_inputs(H, G * Tseg, 65)
+    g = to_dev(d)
+    Z, M = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], G)
+    monkeypatch.setenv("KDA_MAP_SKIP", "0")
+    Z1, M1 = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], G)
+    monkeypatch.delenv("KDA_MAP_SKIP")
+    torch.cuda.synchronize()
+    assert torch.equal(Z, Z1) and torch.equal(M, M1)
+    assert torch.count_nonzero(M[..., 64:]) == 0
+    assert float(M[..., :64, :64].abs().amax()) > 0.1
+    Zr, Mr = oracle.segments(d["k"], d["v"], d["log_alpha"], d["beta"], G)
+    assert oracle.max_rel_l2(Z.cpu(), Zr, 3, floor=1e-3) <= TOL["bf16"]
+    assert oracle.max_rel_l2(M.cpu(), Mr, 3, floor=1e-3) <= TOL["bf16"]
+
+    monkeypatch.setenv("KDA_SPLIT", "3")
+    o, S_T = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
+    monkeypatch.setenv("KDA_MAP_SKIP", "0")
+    o1, S1 = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o1) and torch.equal(S_T, S1)
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    assert oracle.max_rel_l2(o.cpu(), o_ref) <= TOL["bf16"]
+    assert oracle.max_rel_l2(S_T.cpu(), S_ref) <= TOL["bf16"]
+
+
 # ----------------------------------------------------------------- decode
 
 def run_decode_case(N, H, D, dtype, steps, seed, variant="none"):
