@@ -7,6 +7,8 @@ the timed steps:
   * the per-kernel durations of the sequence-split path, through the public
     calls it is made of (the roofline line is the slowest of them);
   * the same prefill with a state snapshot every 512 tokens;
+  * the same prefill shape with slowly decaying gates, where no transfer-map
+    column of the segment pass reaches zero;
   * the batched prefill B=4, H=32, T=8192 with an fp32 start state;
   * decode: 1024 consecutive kda_decode_step calls on 256 sequences x 32 heads
     (fp32 state 512 MiB in place), reported as % of HBM bandwidth;
@@ -233,6 +235,33 @@ def bench_prefill_batched(args, dev):
             "plan": list(kda.prefill_plan(B, H, T, D, D, torch.bfloat16))}
 
 
+def bench_prefill_slow_decay(args, dev):
+    """The headline prefill shape with slowly decaying gates (log_alpha x 1e-3,
+    beta x 0.05, the stress variant of the parity tests).  Under these gates the
+    segment pass's transfer-map columns never reach zero, so none of its waves
+    stop early: this is the split path's cost when nothing decays away."""
+    B, H, T, D = 1, 32, 65536, 128
+    print(f"[bench] generating slow-decay prefill inputs B={B} H={H} T={T} D={D} bf16", file=sys.stderr,
+          flush=True)
+    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=2, device=dev, variant="slow")
+    o = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
+    S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    nws = kda.prefill_workspace_bytes(B, H, T, D, D, torch.bfloat16)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev) if nws else None
+
+    def call():
+        kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None, o=o, S_T=S_T, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ms, _ = time_launches(call, max(5, args.steps))
+    del g, o, ws
+    return {"B": B, "H": H, "T": T, "D": D, "gates": "log_alpha x 1e-3, beta x 0.05", "ms": ms,
+            "tokens_per_s": B * T / (ms * 1e-3),
+            "mfma_dense_tile_frac": prefill_flops(B, H, T, D) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+
+
 def bench_snapshots(pf, args, interval=512):
     """The same prefill with a state snapshot every `interval` tokens (prefix
     caching): time per call, the snapshot bytes written, and the cost over the
@@ -430,6 +459,7 @@ def main():
     ap.add_argument("--no-kcp", action="store_true")
     ap.add_argument("--no-snap", action="store_true")
     ap.add_argument("--no-batched", action="store_true", help="skip the B=4 T=8192 prefill")
+    ap.add_argument("--no-slow", action="store_true", help="skip the slow-decay prefill")
     ap.add_argument("--no-tokens", action="store_true", help="skip the several-token decode")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-calib", action="store_true", help="skip the GEMM and copy reference rates")
@@ -508,6 +538,9 @@ def main():
         out["prefill_kernels"] = dec
     if not args.no_snap:
         out["snapshots"] = bench_snapshots(pf, args)
+        torch.cuda.empty_cache()
+    if not args.no_slow:
+        out["prefill_slow_decay"] = bench_prefill_slow_decay(args, dev)
         torch.cuda.empty_cache()
     if not args.no_batched:
         out["prefill_b4_h32_t8k"] = bench_prefill_batched(args, dev)
