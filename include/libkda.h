@@ -35,9 +35,9 @@
  *  - Environment overrides, for tuning and tests only: KDA_SPLIT (segments of
  *    the sequence-split prefill; 0 = never split), KDA_TRANSFER_COST16 (the
  *    first part's length ratio, in 16ths), KDA_MAP_SKIP=0 (the segment pass
- *    keeps updating transfer-map columns that have become exactly zero; the
- *    results are the same bit for bit), KDA_NC (consumer waves per
- *    workgroup), KDA_LOG (print each launch's shape to stderr).  Every choice
+ *    keeps updating transfer-map columns that have become exactly zero; for
+ *    finite inputs the results are the same bit for bit), KDA_NC (consumer
+ *    waves per workgroup), KDA_LOG (print each launch's shape to stderr).  Every choice
  *    they make gives the same result up to rounding.
  */
 #ifndef LIBKDA_H
