@@ -37,8 +37,8 @@
  *    first part's length ratio, in 16ths), KDA_MAP_SKIP=0 (the segment pass
  *    keeps updating transfer-map columns that have become exactly zero; for
  *    finite inputs the results are the same bit for bit), KDA_NC (consumer
- *    waves per workgroup), KDA_LOG (print each launch's shape to stderr).  Every choice
- *    they make gives the same result up to rounding.
+ *    waves per workgroup), KDA_LOG (print each launch's shape to stderr).
+ *    Every choice they make gives the same result up to rounding.
  */
 #ifndef LIBKDA_H
 #define LIBKDA_H
