@@ -36,8 +36,9 @@ def load(path: str = LIB_PATH):
     lib.kda_oracle_segments.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, i]
     lib.kda_oracle_merge.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp]
     lib.kda_oracle_decode_step.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i]
+    lib.kda_oracle_backward.argtypes = [i, i, i, i, i] + [dp] * 14 + [i]
     for f in (lib.kda_oracle_prefill, lib.kda_oracle_prefill_snap, lib.kda_oracle_segments, lib.kda_oracle_merge,
-              lib.kda_oracle_decode_step):
+              lib.kda_oracle_decode_step, lib.kda_oracle_backward):
         f.restype = ctypes.c_int
     lib.kda_oracle_max_threads.restype = ctypes.c_int
     _lib_cache[path] = lib
@@ -150,6 +151,32 @@ def decode_step(q, k, v, log_alpha, beta, S, nthreads: int = 0, lib=None):
     if rc:
         raise RuntimeError(f"kda_oracle_decode_step failed ({rc})")
     return o, S
+
+
+def backward(q, k, v, log_alpha, beta, S0=None, dO=None, dS_T=None, nthreads: int = 0, lib=None):
+    """Gradients of L = sum(dO * o) + sum(dS_T * S_T) for the prefill on [B,H,T,*]
+    inputs (dO [B,H,T,dv] and dS_T [B,H,dk,dv], either may be None for zero).
+    Returns a dict with dq, dk, dlog_alpha [B,H,T,dk], dv [B,H,T,dv],
+    dbeta [B,H,T] and dS0 [B,H,dk,dv]."""
+    lib = lib or load()
+    q, k, v, la, beta, S0, dO, dS_T = map(_f64, (q, k, v, log_alpha, beta, S0, dO, dS_T))
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    assert q.shape == k.shape == la.shape and v.shape == (B, H, T, dv) and beta.shape == (B, H, T)
+    if S0 is not None:
+        assert S0.shape == (B, H, dk, dv)
+    if dO is not None:
+        assert dO.shape == (B, H, T, dv)
+    if dS_T is not None:
+        assert dS_T.shape == (B, H, dk, dv)
+    out = dict(dq=np.empty((B, H, T, dk)), dk=np.empty((B, H, T, dk)), dv=np.empty((B, H, T, dv)),
+               dlog_alpha=np.empty((B, H, T, dk)), dbeta=np.empty((B, H, T)), dS0=np.empty((B, H, dk, dv)))
+    rc = lib.kda_oracle_backward(B, H, T, dk, dv, _p(q), _p(k), _p(v), _p(la), _p(beta), _p(S0), _p(dO),
+                                 _p(dS_T), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]),
+                                 _p(out["dlog_alpha"]), _p(out["dbeta"]), _p(out["dS0"]), int(nthreads))
+    if rc:
+        raise RuntimeError(f"kda_oracle_backward failed ({rc})")
+    return out
 
 
 def rel_l2(x, ref, floor: float = 0.0) -> float:

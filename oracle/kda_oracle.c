@@ -38,6 +38,20 @@
  * 512-token block boundaries used for prefix matching.  The oracle records the
  * state after every `interval` tokens while running the same recurrence.
  *
+ * Gradients (for training; the K3 report credits FlashKDA with faster training
+ * as well as inference, "Kimi K3 开源日来了", section "FlashKDA").  For a loss
+ * L with dL/do_t = dO_t and dL/dS_T = dS_T, the oracle runs the same token
+ * steps backwards, applying the chain rule to each of steps 1-5 in reverse
+ * order (reverse-mode differentiation of the recurrence as written):
+ *     5. dq_t = S_t dO_t;             dS += q_t dO_t^T
+ *     4. dk_t = dS delta;             d_delta = dS^T k_t;   dD = dS
+ *     3. dbeta_t = d_delta . (v_t - u);  dv_t = beta_t d_delta;  du = -beta_t d_delta
+ *     2. dk_t += D du;                dD += k_t du^T
+ *     1. dlog_alpha_t[i] = sum_j D[i][j] dD[i][j];   dS = Diag(alpha_t) dD
+ * and dS0 is the dS left after token 0.  The forward states are recomputed by
+ * a forward pass that stores the state before every token (T dk dv doubles per
+ * head: sized for test inputs).
+ *
  * Layouts: row-major, [B][H][T][D] for per-token tensors, [B][H][T] for beta,
  * [B][H][dk][dv] for states, [B][n_snap][H][dk][dv] for snapshots.  All arrays
  * are fp64.
@@ -54,7 +68,9 @@
  * 3 reads the output from the pre-update state, 4 uses k for q in the output,
  * 5 applies the decay after the delta correction, 6 transposes the state read
  * in step 2 (uses row j instead of column j), 7 records each snapshot one token
- * late. */
+ * late; in the gradients, 8 drops the output's term q dO^T from dS, 9 flips the
+ * sign of du, 10 takes dlog_alpha from the state before the decay, 11 passes dD
+ * back without the decay. */
 #ifndef KDA_ORACLE_MUTANT
 #define KDA_ORACLE_MUTANT 0
 #endif
@@ -271,6 +287,135 @@ int kda_oracle_decode_step(int N, int H, int dk, int dv, const double* q, const 
         kda_head(1, dk, dv, q + (size_t)nh * dk, k + (size_t)nh * dk, v + (size_t)nh * dv,
                  la + (size_t)nh * dk, beta + nh, S + (size_t)nh * dk * dv, o + (size_t)nh * dv, u);
         free(u);
+    }
+    return err;
+}
+
+/* Gradients of L = sum(dO * o) + sum(dS_T * S_T) with respect to every input of
+ * kda_oracle_prefill.  dO [B,H,T,dv] or NULL (= 0), dS_T [B,H,dk,dv] or NULL
+ * (= 0).  Outputs dq, dk, dla [B,H,T,dk], dv [B,H,T,dv], dbeta [B,H,T],
+ * dS0 [B,H,dk,dv]; every output must be given.  S0 NULL means a zero start. */
+int kda_oracle_backward(int B, int H, int T, int dk, int dv, const double* q, const double* k,
+                        const double* v, const double* la, const double* beta, const double* S0,
+                        const double* dO, const double* dS_T, double* dq, double* dkk, double* dvv,
+                        double* dla, double* dbeta, double* dS0, int nthreads) {
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return 1;
+    if (!dq || !dkk || !dvv || !dla || !dbeta || !dS0) return 1;
+    set_threads(nthreads);
+    const int BH = B * H;
+    const size_t nS = (size_t)dk * dv;
+    int err = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < BH; ++bh) {
+        double* hist = (double*)malloc(sizeof(double) * nS * (size_t)(T > 0 ? T : 1));
+        double* S = (double*)malloc(sizeof(double) * nS);
+        double* D = (double*)malloc(sizeof(double) * nS);
+        double* dS = (double*)malloc(sizeof(double) * nS);
+        double* u = (double*)malloc(sizeof(double) * (size_t)(dv > dk ? dv : dk));
+        double* del = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* ddel = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!hist || !S || !D || !dS || !u || !del || !ddel) {
+            err = 2;
+            free(hist); free(S); free(D); free(dS); free(u); free(del); free(ddel);
+            continue;
+        }
+        const size_t tk = (size_t)bh * T * dk, tv = (size_t)bh * T * dv;
+        const double* qh = q + tk; const double* kh = k + tk; const double* vh = v + tv;
+        const double* lh = la + tk; const double* bh_ = beta + (size_t)bh * T;
+
+        /* forward, keeping the state before every token */
+        if (S0) memcpy(S, S0 + (size_t)bh * nS, sizeof(double) * nS);
+        else memset(S, 0, sizeof(double) * nS);
+        for (int t = 0; t < T; ++t) {
+            memcpy(hist + (size_t)t * nS, S, sizeof(double) * nS);
+            kda_head(1, dk, dv, NULL, kh + (size_t)t * dk, vh + (size_t)t * dv, lh + (size_t)t * dk,
+                     bh_ + t, S, NULL, u);
+        }
+
+        /* backward */
+        if (dS_T) memcpy(dS, dS_T + (size_t)bh * nS, sizeof(double) * nS);
+        else memset(dS, 0, sizeof(double) * nS);
+        for (int t = T - 1; t >= 0; --t) {
+            const double* qt = qh + (size_t)t * dk;
+            const double* kt = kh + (size_t)t * dk;
+            const double* vt = vh + (size_t)t * dv;
+            const double* lat = lh + (size_t)t * dk;
+            const double bt = bh_[t];
+            const double* dot = dO ? dO + tv + (size_t)t * dv : NULL;
+            const double* Sprev = hist + (size_t)t * nS;
+            double* dqt = dq + tk + (size_t)t * dk;
+            double* dkt = dkk + tk + (size_t)t * dk;
+            double* dvt = dvv + tv + (size_t)t * dv;
+            double* dlat = dla + tk + (size_t)t * dk;
+
+            /* recompute step 1-4: D, u, delta and the updated state S */
+            for (int i = 0; i < dk; ++i) {
+                const double a = exp(lat[i]);
+                for (int j = 0; j < dv; ++j) D[(size_t)i * dv + j] = a * Sprev[(size_t)i * dv + j];
+            }
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i) acc += D[(size_t)i * dv + j] * kt[i];
+                u[j] = acc;
+                del[j] = bt * (vt[j] - acc);
+            }
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] = D[(size_t)i * dv + j] + kt[i] * del[j];
+
+            /* 5. o_t = S^T q_t */
+            for (int i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                if (dot)
+                    for (int j = 0; j < dv; ++j) acc += S[(size_t)i * dv + j] * dot[j];
+                dqt[i] = acc;
+            }
+            if (dot && KDA_ORACLE_MUTANT != 8)
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] += qt[i] * dot[j];
+
+            /* 4. S = D + k delta^T  (dS now stands for dD) */
+            for (int i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) acc += dS[(size_t)i * dv + j] * del[j];
+                dkt[i] = acc;
+            }
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i) acc += dS[(size_t)i * dv + j] * kt[i];
+                ddel[j] = acc;
+            }
+
+            /* 3. delta = beta (v - u) */
+            double db = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                db += ddel[j] * (vt[j] - u[j]);
+                dvt[j] = bt * ddel[j];
+                ddel[j] = (KDA_ORACLE_MUTANT == 9) ? bt * ddel[j] : -bt * ddel[j];  /* now du */
+            }
+            dbeta[(size_t)bh * T + t] = db;
+
+            /* 2. u = D^T k */
+            for (int i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) acc += D[(size_t)i * dv + j] * ddel[j];
+                dkt[i] += acc;
+            }
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] += kt[i] * ddel[j];
+
+            /* 1. D = Diag(alpha) S_prev */
+            for (int i = 0; i < dk; ++i) {
+                const double a = exp(lat[i]);
+                const double* src = (KDA_ORACLE_MUTANT == 10) ? Sprev : D;
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) acc += src[(size_t)i * dv + j] * dS[(size_t)i * dv + j];
+                dlat[i] = acc;
+                if (KDA_ORACLE_MUTANT != 11)
+                    for (int j = 0; j < dv; ++j) dS[(size_t)i * dv + j] *= a;
+            }
+        }
+        memcpy(dS0 + (size_t)bh * nS, dS, sizeof(double) * nS);
+        free(hist); free(S); free(D); free(dS); free(u); free(del); free(ddel);
     }
     return err;
 }

@@ -230,6 +230,92 @@ def pin_snap_overwrite(lib, seed=7) -> float:
     return float(worst)
 
 
+def _grad_loss(lib, q, k, v, la, beta, S0, dO, dST):
+    o, ST = _run(lib, q, k, v, la, beta, S0)
+    return float((o * dO).sum() + (ST * dST).sum())
+
+
+def pin_grad_finite_difference(lib, seed=8) -> float:
+    """Gradients of L = sum(dO * o) + sum(dS_T * S_T) against central differences
+    of the forward recurrence (step 1e-6, fp64), for every element of every input,
+    on tiny non-square heads.  Returns the largest error relative to max(|grad|, 1)."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    names = (("q", "dq"), ("k", "dk"), ("v", "dv"), ("la", "dlog_alpha"), ("beta", "dbeta"), ("S0", "dS0"))
+    for (T, dk, dv, unit) in [(1, 1, 1, True), (7, 3, 4, True), (5, 4, 2, False), (6, 2, 5, True)]:
+        q, k, v, la, beta, S0 = _rand_inputs(rng, T, dk, dv, unit_keys=unit)
+        dO = rng.standard_normal((T, dv))
+        dST = rng.standard_normal((dk, dv))
+        E = lambda x: x[None, None]
+        g = oracle.backward(E(q), E(k), E(v), E(la), E(beta), E(S0), E(dO), E(dST), lib=lib, nthreads=1)
+        args = dict(q=q, k=k, v=v, la=la, beta=beta, S0=S0)
+        h = 1e-6
+        for n, gn in names:
+            x = args[n]
+            an = g[gn][0, 0]
+            for idx in np.ndindex(x.shape):
+                xp = x.copy()
+                xm = x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                lp = _grad_loss(lib, **{**args, n: xp}, dO=dO, dST=dST)
+                lm = _grad_loss(lib, **{**args, n: xm}, dO=dO, dST=dST)
+                fd = (lp - lm) / (2 * h)
+                worst = max(worst, abs(fd - an[idx]) / max(abs(an[idx]), 1.0))
+    return float(worst)
+
+
+def pin_grad_beta_zero(lib, seed=9) -> float:
+    """beta = 0: S_t = Diag(e^{g_t}) S0 with g_t = sum_{s<=t} log a_s, so by hand
+        dS_t (total) = sum_{s>=t} Diag(e^{g_s - g_t}) q_s dO_s^T + Diag(e^{g_T - g_t}) dS_T
+        dq_t = S_t dO_t,   dbeta_t = (dS_t^T k_t) . (v_t - S'_t^T k_t),  S'_t = Diag(e^{g_t}) S0
+        dlog_alpha_s[i] = sum_{t>=s} e^{g_t[i]} q_t[i] (S0 dO_t)[i] + e^{g_T[i]} (S0 * dS_T)[i, :].sum()
+        dv = dk = 0,  dS0 = sum_t Diag(e^{g_t}) q_t dO_t^T + Diag(e^{g_T}) dS_T."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (T, dk, dv) in [(1, 2, 3), (9, 4, 3), (12, 3, 5)]:
+        q, k, v, la, _, S0 = _rand_inputs(rng, T, dk, dv)
+        beta = np.zeros(T)
+        dO = rng.standard_normal((T, dv))
+        dST = rng.standard_normal((dk, dv))
+        E = lambda x: x[None, None]
+        g = oracle.backward(E(q), E(k), E(v), E(la), E(beta), E(S0), E(dO), E(dST), lib=lib, nthreads=1)
+        G = np.cumsum(la, axis=0)  # g_t, t = 0..T-1
+        gT = G[-1]
+        dq = np.stack([(np.exp(G[t])[:, None] * S0) @ dO[t] for t in range(T)])
+        dbeta = np.zeros(T)
+        for t in range(T):
+            dSt = np.exp(gT - G[t])[:, None] * dST
+            for s_ in range(t, T):
+                dSt = dSt + np.exp(G[s_] - G[t])[:, None] * np.outer(q[s_], dO[s_])
+            Sp = np.exp(G[t])[:, None] * S0
+            dbeta[t] = (dSt.T @ k[t]) @ (v[t] - Sp.T @ k[t])
+        per_t = np.stack([np.exp(G[t]) * q[t] * (S0 @ dO[t]) for t in range(T)])
+        fin = np.exp(gT) * (S0 * dST).sum(axis=1)
+        dla = np.cumsum(per_t[::-1], axis=0)[::-1] + fin
+        dS0 = sum(np.exp(G[t])[:, None] * np.outer(q[t], dO[t]) for t in range(T)) + np.exp(gT)[:, None] * dST
+        for got, ref in ((g["dq"][0, 0], dq), (g["dbeta"][0, 0], dbeta), (g["dlog_alpha"][0, 0], dla),
+                         (g["dS0"][0, 0], dS0), (g["dv"][0, 0], 0.0), (g["dk"][0, 0], 0.0)):
+            worst = max(worst, float(np.abs(got - ref).max()))
+    return worst
+
+
+def pin_grad_transfer_adjoint(lib, seed=10) -> float:
+    """With dO = 0 only S_T = M S0 + Z carries the loss, so dS0 = M^T dS_T, with
+    M the segment transfer map (the recurrence run from S0 = I with v = 0)."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (T, dk, dv) in [(4, 3, 5), (20, 6, 4)]:
+        q, k, v, la, beta, S0 = _rand_inputs(rng, T, dk, dv)
+        dST = rng.standard_normal((dk, dv))
+        E = lambda x: x[None, None]
+        g = oracle.backward(E(q), E(k), E(v), E(la), E(beta), E(S0), None, E(dST), lib=lib, nthreads=1)
+        _, M = oracle.segments(E(k), E(v), E(la), E(beta), 1, lib=lib, nthreads=1)
+        worst = max(worst, float(np.abs(g["dS0"][0, 0] - M[0, 0, 0].T @ dST).max()))
+        worst = max(worst, float(np.abs(g["dq"][0, 0]).max()))  # no output term: dq = 0
+    return worst
+
+
 ALL_PINS = {
     "product_sum": (pin_product_sum, 1e-12),
     "exact_rational": (pin_exact_rational, 1e-12),
@@ -240,4 +326,7 @@ ALL_PINS = {
     "affine": (pin_affine, 1e-12),
     "snap_decay": (pin_snap_decay, 1e-13),
     "snap_overwrite": (pin_snap_overwrite, 1e-13),
+    "grad_finite_difference": (pin_grad_finite_difference, 1e-7),
+    "grad_beta_zero": (pin_grad_beta_zero, 1e-12),
+    "grad_transfer_adjoint": (pin_grad_transfer_adjoint, 1e-12),
 }

@@ -112,11 +112,13 @@ def test_snapshots_match_prefix_runs(oracle_lib):
     assert none.shape == (B, 0, H, dk, dv)
 
 
-@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11])
 def test_planted_mistakes_are_caught(tmp_path, mutant):
     """Each planted mistake (dropped decay, flipped delta sign, pre-update output,
     k in place of q, decay after the write, transposed state read, snapshot one
-    token late) makes at least one pin fail."""
+    token late; in the gradients: the output's term dropped, du's sign flipped,
+    dlog_alpha from the undecayed state, dD passed back without the decay)
+    makes at least one pin fail."""
     path = build_oracle.build(str(tmp_path / f"mut{mutant}.so"), mutant=mutant)
     lib = oracle.load(path)
     failed = []
