@@ -61,9 +61,12 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_tokens.argtypes = [vp] * 9 + [i] * 6 + [vp]
     lib.kda_segment_transfer.argtypes = [vp] * 6 + [i] * 7 + [vp]
     lib.kda_segment_merge.argtypes = [vp] * 5 + [i] * 5 + [vp]
+    lib.kda_backward_workspace_bytes.argtypes = [i] * 5
+    lib.kda_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_prefill_backward.argtypes = [vp] * 14 + [i] * 6 + [vp, ctypes.c_size_t, vp]
     for f in (lib.kda_chunk_prefill, lib.kda_chunk_prefill_snap, lib.kda_prefill_plan, lib.kda_chunk_prefill_segments,
               lib.kda_decode_step, lib.kda_decode_tokens, lib.kda_segment_transfer,
-              lib.kda_segment_merge):
+              lib.kda_segment_merge, lib.kda_prefill_backward):
         f.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -315,3 +318,45 @@ def segment_merge(S_zero_end, M, S_in=None, want_start: bool = True, S_start=Non
                                   B, H, G, dk, dv, _stream())
     _check(rc, "kda_segment_merge")
     return S_start, S_T
+
+
+def backward_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int) -> int:
+    """Workspace kda_prefill_backward needs (0 for an unsupported shape)."""
+    return int(load().kda_backward_workspace_bytes(B, H, T, dk, dv))
+
+
+def prefill_backward(q, k, v, log_alpha, beta, S0=None, dO=None, dS_T=None, workspace=None):
+    """Gradients of L = sum(dO * o) + sum(dS_T * S_T) of the prefill with respect
+    to its inputs.  Returns a dict of fp32 tensors: dq, dk, dlog_alpha [B,H,T,dk],
+    dv [B,H,T,dv], dbeta [B,H,T], dS0 [B,H,dk,dv]."""
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dt = k.dtype
+    if dt not in _DT:
+        raise KdaError(f"unsupported dtype {dt}")
+    for t, n, shp in ((q, "q", (B, H, T, dk)), (k, "k", (B, H, T, dk)), (v, "v", (B, H, T, dv)),
+                      (log_alpha, "log_alpha", (B, H, T, dk)), (beta, "beta", (B, H, T))):
+        _io(t, n, dt, shp)
+    if S0 is not None:
+        _io(S0, "S0", torch.float32, (B, H, dk, dv))
+    if dO is not None:
+        _io(dO, "dO", dt, (B, H, T, dv))
+    if dS_T is not None:
+        _io(dS_T, "dS_T", torch.float32, (B, H, dk, dv))
+    dev = k.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty(B, H, T, dk, **f32), dk=torch.empty(B, H, T, dk, **f32),
+               dv=torch.empty(B, H, T, dv, **f32), dlog_alpha=torch.empty(B, H, T, dk, **f32),
+               dbeta=torch.empty(B, H, T, **f32), dS0=torch.empty(B, H, dk, dv, **f32))
+    need = backward_workspace_bytes(B, H, T, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    if not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+        raise KdaError(f"workspace must be a device tensor of at least {need} bytes")
+    rc = load().kda_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(dO),
+                                     _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                     _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dS0"]), B, H, T, dk, dv,
+                                     _DT[dt], _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream())
+    _check(rc, "kda_prefill_backward")
+    return out

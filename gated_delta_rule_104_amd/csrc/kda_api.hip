@@ -539,4 +539,51 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
   return ok();
 }
 
+size_t kda_backward_workspace_bytes(int B, int H, int T, int dk, int dv) {
+  if (B <= 0 || H <= 0 || T < 0 || dk != dv || (dk != 64 && dk != 128)) return 0;
+  return kda::backward_ws_floats((long long)B * H, T, dk) * sizeof(float);
+}
+
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const void* log_alpha,
+                                const void* beta, const float* S0, const void* dO, const float* dS_T,
+                                float* dq, float* dk_, float* dv_, float* dlog_alpha, float* dbeta,
+                                float* dS0, int B, int H, int T, int dk, int dv, kda_dtype dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || H < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size B=%d H=%d T=%d", B, H, T);
+  kda_status st;
+  if ((st = check_dtype(dtype)) != KDA_OK) return st;
+  if ((st = check_dims(dk, dv)) != KDA_OK) return st;
+  const long long BH = (long long)B * H;
+  if (BH > INT32_MAX || BH * T * dk > kMaxElems) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (BH == 0) return ok();
+  KDA_REQUIRE(dS0, "dS0");
+  KDA_OPTIONAL(S0, "S0");
+  KDA_OPTIONAL(dS_T, "dS_T");
+  if (T > 0) {
+    KDA_REQUIRE(q, "q");
+    KDA_REQUIRE(k, "k");
+    KDA_REQUIRE(v, "v");
+    KDA_REQUIRE(log_alpha, "log_alpha");
+    if (!beta) return fail(KDA_ERR_NULL, "beta is NULL");  // [B,H,T]: any element alignment
+    KDA_OPTIONAL(dO, "dO");
+    KDA_REQUIRE(dq, "dq");
+    KDA_REQUIRE(dk_, "dk_");
+    KDA_REQUIRE(dv_, "dv_");
+    KDA_REQUIRE(dlog_alpha, "dlog_alpha");
+    if (!dbeta) return fail(KDA_ERR_NULL, "dbeta is NULL");
+  }
+  const size_t need = kda::backward_ws_floats(BH, T, dk) * sizeof(float);
+  KDA_REQUIRE(workspace, "workspace");
+  if (workspace_bytes < need)
+    return fail(KDA_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  kda::BackwardArgs a;
+  a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta; a.S0 = S0; a.dO = dO; a.dS_T = dS_T;
+  a.dq = dq; a.dk = dk_; a.dv = dv_; a.dla = dlog_alpha; a.dbeta = dbeta; a.dS0 = dS0;
+  a.ws = static_cast<float*>(workspace);
+  a.T = T;
+  hipError_t e = kda::launch_backward(a, (int)BH, dk, dtype == KDA_BF16, stream);
+  if (e != hipSuccess) return hip_fail(e, "kda_prefill_backward launch");
+  return ok();
+}
+
 }  // extern "C"

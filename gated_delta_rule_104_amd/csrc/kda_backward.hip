@@ -1,0 +1,239 @@
+// KDA prefill gradients per head, token by token.
+//
+// For a loss L with dL/do_t = dO_t and dL/dS_T = dS_T, the gradients of the
+// recurrence (blog.csdn.net article on the Kimi K3 report, section 一.1; the
+// update itself is the gated delta rule taken for it)
+//     D = Diag(a_t) S_{t-1},  u = D^T k_t,  delta = b_t (v_t - u),
+//     S_t = D + k_t delta^T,  o_t = S_t^T q_t,          a_t = exp(log_alpha_t)
+// follow by running the same steps backwards with the chain rule (training is
+// what the K3 report also speeds up with FlashKDA: "Kimi K3 开源日来了", section
+// "FlashKDA"):
+//     dq_t = S_t dO_t;  dS += q_t dO_t^T
+//     dk_t = dS delta + D du;  d_delta = dS^T k_t
+//     dbeta_t = d_delta . (v_t - u);  dv_t = b_t d_delta;  du = -b_t d_delta
+//     dS += k_t du^T;  dlog_alpha_t = rowsum(D * dS);  dS = Diag(a_t) dS
+// and dS0 is the dS left after token 0.
+//
+// The backward walk needs the state before every token, newest first.  The
+// kernel runs the forward recurrence once, keeping the state at the start of
+// every 64-token interval in the workspace; then, interval by interval from the
+// last, it runs the interval forward again from its checkpoint, keeping each
+// token's entering state in the workspace, and walks those tokens backwards.
+//
+// One workgroup of 4 D threads per head.  Thread tid owns row i = tid / 4 of
+// the state and of dS, columns [c0, c0 + D/4) with c0 = (tid % 4) D/4, in
+// registers.  Sums over a row (dq, dk, dlog_alpha) stay in the thread and the
+// 4 adjacent lanes of its row.  Sums over the rows (u, d_delta) go through a
+// lane butterfly inside each wave and one LDS exchange between the waves.
+// Every step is evaluated in fp32 on inputs read as fp32.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+namespace {
+
+template <int D>
+struct BwLayout {
+  static constexpr int TPR = 4;                // threads per state row
+  static constexpr int THREADS = TPR * D;      // one thread per (row, column quarter)
+  static constexpr int NW = THREADS / 64;      // waves
+  static constexpr int CPT = D / TPR;          // columns per thread
+  static_assert(THREADS % 64 == 0 && CPT % 4 == 0, "layout");
+};
+
+// Sum of x over the TPR adjacent lanes that share a state row.
+template <int D>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < BwLayout<D>::TPR; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Column sums over all D rows of the workgroup's state layout, into tot[D].
+// p holds this thread's row contributions for its CPT columns.  The butterfly
+// over the lane bits that select the row leaves every lane with its wave's sum
+// for its columns; lanes of the wave's first row write it to red[wave][.], and
+// after a barrier D threads add the waves' sums of one column each.  tot is
+// readable after the second barrier.
+template <int D>
+__device__ __forceinline__ void col_reduce(float* p, float (*red)[D], float* tot, int tid, int c0) {
+  using L = BwLayout<D>;
+#pragma unroll
+  for (int m = L::TPR; m < 64; m <<= 1)
+#pragma unroll
+    for (int c = 0; c < L::CPT; ++c) p[c] += __shfl_xor(p[c], m);
+  if ((tid & 63) < L::TPR)
+#pragma unroll
+    for (int c = 0; c < L::CPT; ++c) red[tid >> 6][c0 + c] = p[c];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < L::NW; ++w) s += red[w][tid];
+    tot[tid] = s;
+  }
+  __syncthreads();
+}
+
+}  // namespace
+
+template <typename T, int D>
+__global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) {
+  using L = BwLayout<D>;
+  constexpr int CPT = L::CPT;
+  constexpr int NS = D * D;
+  __shared__ float s_k[D], s_a[D], s_v[D], s_q[D], s_do[D];
+  __shared__ float s_b;
+  __shared__ float red[L::NW][D];
+  __shared__ float s_u[D], s_dd[D];
+
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int i = tid / L::TPR;
+  const int part = tid % L::TPR;
+  const int c0 = part * CPT;
+  const int nt = a.T;
+  const int nch = (nt + kBwInterval - 1) / kBwInterval;
+
+  const size_t tok0 = (size_t)bh * nt;
+  const T* q = static_cast<const T*>(a.q) + tok0 * D;
+  const T* k = static_cast<const T*>(a.k) + tok0 * D;
+  const T* v = static_cast<const T*>(a.v) + tok0 * D;
+  const T* la = static_cast<const T*>(a.la) + tok0 * D;
+  const T* beta = static_cast<const T*>(a.beta) + tok0;
+  const T* dO = a.dO ? static_cast<const T*>(a.dO) + tok0 * D : nullptr;
+  float* ckpt = a.ws + (size_t)bh * (size_t)(nch + kBwInterval) * NS;
+  float* hist = ckpt + (size_t)nch * NS;
+  const size_t my = (size_t)i * D + c0;  // this thread's first state entry
+
+  // token t's vectors into LDS (threads < D, one channel each); with_q also
+  // loads q and dO for the backward step
+  auto load_tok = [&](int t, bool with_q) {
+    if (tid < D) {
+      const size_t o = (size_t)t * D + tid;
+      s_k[tid] = to_f32(k[o]);
+      s_a[tid] = expf(to_f32(la[o]));
+      s_v[tid] = to_f32(v[o]);
+      if (with_q) {
+        s_q[tid] = to_f32(q[o]);
+        s_do[tid] = dO ? to_f32(dO[o]) : 0.f;
+      }
+    }
+    if (tid == 0) s_b = to_f32(beta[t]);
+    __syncthreads();
+  };
+
+  float S[CPT], p[CPT];
+  // one forward token on S (the state entering token t -> leaving it)
+  auto forward = [&](int t) {
+    load_tok(t, false);
+    const float ai = s_a[i], ki = s_k[i];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      S[c] *= ai;
+      p[c] = ki * S[c];
+    }
+    col_reduce<D>(p, red, s_u, tid, c0);
+    const float b = s_b;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) S[c] += ki * b * (s_v[c0 + c] - s_u[c0 + c]);
+    __syncthreads();  // LDS reads done before the next token's loads
+  };
+
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) S[c] = a.S0 ? a.S0[(size_t)bh * NS + my + c] : 0.f;
+  for (int t = 0; t < nt; ++t) {
+    if (t % kBwInterval == 0) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) ckpt[(size_t)(t / kBwInterval) * NS + my + c] = S[c];
+    }
+    forward(t);
+  }
+
+  float dS[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) dS[c] = a.dS_T ? a.dS_T[(size_t)bh * NS + my + c] : 0.f;
+
+  for (int ch = nch - 1; ch >= 0; --ch) {
+    const int t0 = ch * kBwInterval;
+    const int t1 = min(t0 + kBwInterval, nt);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) S[c] = ckpt[(size_t)ch * NS + my + c];
+    for (int t = t0; t < t1; ++t) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) hist[(size_t)(t - t0) * NS + my + c] = S[c];
+      forward(t);
+    }
+    for (int t = t1 - 1; t >= t0; --t) {
+      load_tok(t, true);
+      const float ai = s_a[i], ki = s_k[i], qi = s_q[i], b = s_b;
+      // D = Diag(a) S_{t-1} (in S), u = D^T k
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        S[c] = ai * hist[(size_t)(t - t0) * NS + my + c];
+        p[c] = ki * S[c];
+      }
+      col_reduce<D>(p, red, s_u, tid, c0);
+      // dq = S_t dO with S_t = D + k delta^T; dS += q dO^T; dk (first part) = dS delta
+      float dq = 0.f, dk = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const float del = b * (s_v[c0 + c] - s_u[c0 + c]);
+        const float d_o = s_do[c0 + c];
+        dq += (S[c] + ki * del) * d_o;
+        dS[c] += qi * d_o;
+        dk += dS[c] * del;
+        p[c] = ki * dS[c];
+      }
+      // d_delta = dS^T k
+      col_reduce<D>(p, red, s_dd, tid, c0);
+      float db = 0.f, dla = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const float dd = s_dd[c0 + c];
+        db += dd * (s_v[c0 + c] - s_u[c0 + c]);
+        const float du = -b * dd;
+        dk += S[c] * du;
+        dS[c] += ki * du;
+        dla += S[c] * dS[c];
+        dS[c] *= ai;
+      }
+      dq = row_sum<D>(dq);
+      dk = row_sum<D>(dk);
+      dla = row_sum<D>(dla);
+      db = row_sum<D>(db);
+      const size_t o = (tok0 + t) * D;
+      if (part == 0) {
+        a.dq[o + i] = dq;
+        a.dk[o + i] = dk;
+        a.dla[o + i] = dla;
+      }
+      if (tid < L::TPR) {  // the threads of row 0 hold d_delta for all columns
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) a.dv[o + c0 + c] = b * s_dd[c0 + c];
+        if (tid == 0) a.dbeta[tok0 + t] = db;
+      }
+      __syncthreads();  // LDS reads done before the next token's loads
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) a.dS0[(size_t)bh * NS + my + c] = dS[c];
+}
+
+hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, hipStream_t stream) {
+  if (BH <= 0) return hipSuccess;
+#define KDA_BW(TY, DD) \
+  hipLaunchKernelGGL((kda_backward_kernel<TY, DD>), dim3(BH), dim3(4 * DD), 0, stream, a)
+  if (bf16_io) {
+    if (D == 128) KDA_BW(bf16, 128);
+    else KDA_BW(bf16, 64);
+  } else {
+    if (D == 128) KDA_BW(float, 128);
+    else KDA_BW(float, 64);
+  }
+#undef KDA_BW
+  return hipGetLastError();
+}
+
+}  // namespace kda

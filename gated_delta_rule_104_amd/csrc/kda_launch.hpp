@@ -55,6 +55,34 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
                          const void* beta, const float* S_in, float* S_out, void* o, float* S_pos,
                          int NH, int H, int ntok, int D, bool bf16_io, hipStream_t stream);
 
+// Prefill gradients, one workgroup per head over [BH, T, D] inputs.  The
+// workspace holds (ceil(T / kBwInterval) + kBwInterval) fp32 D x D states per
+// head: a checkpoint at the start of every interval and the entering state of
+// every token of the interval being walked.
+constexpr int kBwInterval = 64;
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* la;
+  const void* beta;
+  const float* S0;    // [BH, D, D] or null (= 0)
+  const void* dO;     // [BH, T, D] or null (= 0)
+  const float* dS_T;  // [BH, D, D] or null (= 0)
+  float* dq;          // [BH, T, D]
+  float* dk;          // [BH, T, D]
+  float* dv;          // [BH, T, D]
+  float* dla;         // [BH, T, D]
+  float* dbeta;       // [BH, T]
+  float* dS0;         // [BH, D, D]
+  float* ws;
+  int T;
+};
+inline size_t backward_ws_floats(long long BH, int T, int D) {
+  return (size_t)BH * (size_t)((T + kBwInterval - 1) / kBwInterval + kBwInterval) * (size_t)D * D;
+}
+hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, hipStream_t stream);
+
 hipError_t launch_merge(const float* S_in, const float* Z, const float* M, float* S_start,
                         float* S_T, int BH, int G, int D, hipStream_t stream);
 

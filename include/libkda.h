@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 typedef enum {
   KDA_OK = 0,
@@ -217,6 +217,32 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
 kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const float* M,
                              float* S_start, float* S_T, int B, int H, int G, int dk, int dv,
                              hipStream_t stream);
+
+/*
+ * Gradients of the prefill, for training (the K3 report credits FlashKDA with
+ * faster training as well as inference: myzaker "Kimi K3 开源日来了", section
+ * "FlashKDA").  For a loss L with dL/do = dO and dL/dS_T = dS_T this computes
+ * the gradients with respect to every input of kda_chunk_prefill, by running
+ * the recurrence's token steps backwards (reverse-mode chain rule), token by
+ * token, one workgroup per head.
+ *   q, k, v, log_alpha, beta, S0 : as for kda_chunk_prefill (S0 NULL = zero)
+ *   dO   : [B, H, T, dv] dtype, or NULL (= 0)
+ *   dS_T : [B, H, dk, dv] fp32, or NULL (= 0)
+ *   dq, dk_, dlog_alpha : [B, H, T, dk] fp32;  dv_ : [B, H, T, dv] fp32;
+ *   dbeta : [B, H, T] fp32;  dS0 : [B, H, dk, dv] fp32.
+ * The workspace (device memory, at least kda_backward_workspace_bytes, 16-byte
+ * aligned) holds a state checkpoint every 64 tokens and the entering states of
+ * one 64-token interval per head; its contents on return are undefined.  No
+ * output may alias an input or the workspace.  Errors: KDA_ERR_NULL for a
+ * missing workspace or required pointer, KDA_ERR_SHAPE for a workspace below
+ * the required size.
+ */
+size_t kda_backward_workspace_bytes(int B, int H, int T, int dk, int dv);
+kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const void* log_alpha,
+                                const void* beta, const float* S0, const void* dO, const float* dS_T,
+                                float* dq, float* dk_, float* dv_, float* dlog_alpha, float* dbeta,
+                                float* dS0, int B, int H, int T, int dk, int dv, kda_dtype dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 const char* kda_status_string(kda_status status);
 const char* kda_last_error(void);

@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 6
+    assert lib.kda_abi_version() == 7
     for st in range(6):
         assert lib.kda_status_string(st)
     assert lib.kda_status_string(99) == b"unknown status"

@@ -1,0 +1,105 @@
+"""GPU parity of the prefill gradients (kda_prefill_backward, through the
+C-ABI) against the fp64 oracle's reverse-mode gradients.
+
+The loss is L = sum(dO * o) + sum(dS_T * S_T) with seeded random dO and dS_T.
+Errors are the largest relative L2 error over (b, h) slices, per gradient; the
+bars are those of the forward outputs (1e-4 for fp32 inputs, 2e-2 for bf16
+inputs), although the kernel evaluates every step in fp32 on both.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_104_amd as kda
+import kda_inputs as ki
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+NAMES = ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0")
+
+
+def dev():
+    assert torch.cuda.is_available()
+    return torch.device("cuda:0")
+
+
+def grads_case(B, H, T, D, dtype, seed, s0_std=0.1, variant="none", with_dO=True, with_dST=True):
+    print(f"[case] backward B={B} H={H} T={T} D={D} {dtype} {variant} dO={with_dO} dS_T={with_dST}",
+          flush=True)
+    d = ki.gen_prefill(B, H, T, D, D, dtype, seed=seed, s0_std=s0_std, variant=variant)
+    gen = torch.Generator().manual_seed(1000 + seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dO = torch.randn(B, H, T, D, generator=gen).to(tdt) if with_dO else None
+    dST = torch.randn(B, H, D, D, generator=gen) if with_dST else None
+    g = {n: (x.to(dev()) if x is not None else None) for n, x in d.items()}
+    out = kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"],
+                               dO.to(dev()) if dO is not None else None,
+                               dST.to(dev()) if dST is not None else None)
+    torch.cuda.synchronize()
+    ref = oracle.backward(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"], dO, dST)
+    err = {}
+    for n in NAMES:
+        got = out[n].cpu()
+        assert torch.isfinite(got).all(), n
+        lead = 2 if n != "dbeta" else 1
+        err[n] = oracle.max_rel_l2(got, ref[n], lead, floor=1e-6) if got.numel() else 0.0
+    print("    " + "  ".join(f"{k} {v:.2e}" for k, v in err.items()), flush=True)
+    return err
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130])
+def test_backward_f32_d64(T):
+    err = grads_case(1, 2, T, 64, "f32", 70 + T)
+    assert max(err.values()) <= TOL["f32"], err
+
+
+@pytest.mark.parametrize("T,variant", [(130, "none"), (200, "slow"), (64, "beta_one")])
+def test_backward_bf16_d128(T, variant):
+    err = grads_case(2, 2, T, 128, "bf16", 80 + T, variant=variant)
+    assert max(err.values()) <= TOL["bf16"], err
+
+
+def test_backward_bf16_d64_batch():
+    err = grads_case(2, 3, 100, 64, "bf16", 91, variant="slow")
+    assert max(err.values()) <= TOL["bf16"], err
+
+
+def test_backward_f32_d128():
+    err = grads_case(1, 2, 96, 128, "f32", 92, variant="slow")
+    assert max(err.values()) <= TOL["f32"], err
+
+
+def test_backward_only_end_state_gradient():
+    """dO = 0: only S_T carries the loss; dq is zero and dS0 = M^T dS_T."""
+    err = grads_case(1, 2, 150, 128, "bf16", 93, variant="slow", with_dO=False)
+    assert max(err.values()) <= TOL["bf16"], err
+
+
+def test_backward_only_output_gradient():
+    err = grads_case(1, 2, 90, 64, "f32", 94, with_dST=False)
+    assert max(err.values()) <= TOL["f32"], err
+
+
+def test_backward_zero_tokens():
+    """T = 0: the end state is the start state, so dS0 = dS_T exactly."""
+    B, H, D = 1, 2, 64
+    e = torch.empty(B, H, 0, D, dtype=torch.float32, device=dev())
+    beta = torch.empty(B, H, 0, dtype=torch.float32, device=dev())
+    S0 = torch.randn(B, H, D, D, device=dev())
+    dST = torch.randn(B, H, D, D, device=dev())
+    out = kda.prefill_backward(e, e, e, e, beta, S0, None, dST)
+    torch.cuda.synchronize()
+    assert torch.equal(out["dS0"], dST)
+
+
+def test_backward_deterministic():
+    d = ki.gen_prefill(1, 2, 100, 128, 128, "bf16", seed=95, s0_std=0.1)
+    g = {n: (x.to(dev()) if x is not None else None) for n, x in d.items()}
+    dO = torch.randn(1, 2, 100, 128, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(dev())
+    a = kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], dO, None)
+    b = kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], dO, None)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
