@@ -10,6 +10,7 @@ the timed steps:
   * the same prefill shape with slowly decaying gates, where no transfer-map
     column of the segment pass reaches zero;
   * the batched prefill B=4, H=32, T=8192 with an fp32 start state;
+  * the gradients of that batched prefill (kda_prefill_backward);
   * decode: 1024 consecutive kda_decode_step calls on 256 sequences x 32 heads
     (fp32 state 512 MiB in place), reported as % of HBM bandwidth;
   * decode_tokens: 4 draft tokens per sequence in one call, with and without
@@ -262,6 +263,37 @@ def bench_prefill_slow_decay(args, dev):
             "mfma_dense_tile_frac": prefill_flops(B, H, T, D) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def backward_bytes(B, H, T, D):
+    """Algorithmic bytes of kda_prefill_backward with bf16 inputs: q, k, v,
+    log_alpha, dO (2 B x D each) and beta read per token-head; dq, dk, dv,
+    dlog_alpha (4 B x D each) and dbeta written; S0 and dS_T read and dS0
+    written per head.  The workspace's checkpoints are not counted."""
+    return B * H * T * (2 * 5 * D + 2 + 4 * 4 * D + 4) + 3 * B * H * D * D * 4
+
+
+def bench_backward(args, dev):
+    """Gradients of the batched prefill workload B=4, H=32, T=8192, d=128 (bf16
+    inputs, fp32 start state, dO and dS_T given): time per call and tokens/s."""
+    B, H, T, D = 4, 32, 8192, 128
+    print(f"[bench] generating backward inputs B={B} H={H} T={T} D={D} bf16", file=sys.stderr, flush=True)
+    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=1, s0_std=0.1, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(6)
+    dO = torch.randn(B, H, T, D, generator=gen, device=dev).to(torch.bfloat16)
+    dST = torch.randn(B, H, D, D, generator=gen, device=dev)
+    ws = torch.empty(kda.backward_workspace_bytes(B, H, T, D, D), dtype=torch.uint8, device=dev)
+
+    def call():
+        kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], dO, dST, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ms, _ = time_launches(call, 3)
+    nbytes = backward_bytes(B, H, T, D)
+    del g, dO, ws
+    return {"B": B, "H": H, "T": T, "D": D, "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 def bench_snapshots(pf, args, interval=512):
     """The same prefill with a state snapshot every `interval` tokens (prefix
     caching): time per call, the snapshot bytes written, and the cost over the
@@ -460,6 +492,7 @@ def main():
     ap.add_argument("--no-snap", action="store_true")
     ap.add_argument("--no-batched", action="store_true", help="skip the B=4 T=8192 prefill")
     ap.add_argument("--no-slow", action="store_true", help="skip the slow-decay prefill")
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill gradients")
     ap.add_argument("--no-tokens", action="store_true", help="skip the several-token decode")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-calib", action="store_true", help="skip the GEMM and copy reference rates")
@@ -544,6 +577,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_batched:
         out["prefill_b4_h32_t8k"] = bench_prefill_batched(args, dev)
+        torch.cuda.empty_cache()
+    if not args.no_backward:
+        out["backward_b4_h32_t8k"] = bench_backward(args, dev)
         torch.cuda.empty_cache()
     if not args.no_decode:
         out["decode"] = bench_decode(args, dev)

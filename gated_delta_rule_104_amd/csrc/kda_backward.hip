@@ -23,8 +23,8 @@
 // One workgroup of 4 D threads per head.  Thread tid owns row i = tid / 4 of
 // the state and of dS, columns [c0, c0 + D/4) with c0 = (tid % 4) D/4, in
 // registers.  Sums over a row (dq, dk, dlog_alpha) stay in the thread and the
-// 4 adjacent lanes of its row.  Sums over the rows (u, d_delta) go through a
-// lane butterfly inside each wave and one LDS exchange between the waves.
+// 4 adjacent lanes of its row.  Sums over the rows (u, d_delta) go through an
+// LDS transpose: every thread stores its row piece, then sums a quarter column.
 // Every step is evaluated in fp32 on inputs read as fp32.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
@@ -51,28 +51,28 @@ __device__ __forceinline__ float row_sum(float x) {
 }
 
 // Column sums over all D rows of the workgroup's state layout, into tot[D].
-// p holds this thread's row contributions for its CPT columns.  The butterfly
-// over the lane bits that select the row leaves every lane with its wave's sum
-// for its columns; lanes of the wave's first row write it to red[wave][.], and
-// after a barrier D threads add the waves' sums of one column each.  tot is
-// readable after the second barrier.
+// p holds this thread's contributions for row i, columns [c0, c0 + CPT).  They
+// go to the LDS matrix P (row pitch D + 4 floats) as 16-byte stores; after a
+// barrier thread tid adds a quarter of column tid % D (rows (tid / D) D/4 ..),
+// the four quarters meet in quar[4][D], and D threads add them into tot.  tot
+// is readable after the third barrier.
 template <int D>
-__device__ __forceinline__ void col_reduce(float* p, float (*red)[D], float* tot, int tid, int c0) {
+__device__ __forceinline__ void col_reduce(const float* p, float* P, float (*quar)[D], float* tot, int tid, int i,
+                                           int c0) {
   using L = BwLayout<D>;
+  constexpr int PITCH = D + 4;
+  static_assert(L::THREADS == 4 * D, "one quarter column per thread");
 #pragma unroll
-  for (int m = L::TPR; m < 64; m <<= 1)
-#pragma unroll
-    for (int c = 0; c < L::CPT; ++c) p[c] += __shfl_xor(p[c], m);
-  if ((tid & 63) < L::TPR)
-#pragma unroll
-    for (int c = 0; c < L::CPT; ++c) red[tid >> 6][c0 + c] = p[c];
+  for (int c = 0; c < L::CPT; c += 4)
+    *reinterpret_cast<f32x4*>(P + i * PITCH + c0 + c) = f32x4{p[c], p[c + 1], p[c + 2], p[c + 3]};
   __syncthreads();
-  if (tid < D) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < L::NW; ++w) s += red[w][tid];
-    tot[tid] = s;
-  }
+  const int j = tid % D, r = tid / D;
+  float s = 0.f;
+#pragma unroll 8
+  for (int rr = 0; rr < D / 4; ++rr) s += P[(r * (D / 4) + rr) * PITCH + j];
+  quar[r][j] = s;
+  __syncthreads();
+  if (tid < D) tot[tid] = (quar[0][tid] + quar[1][tid]) + (quar[2][tid] + quar[3][tid]);
   __syncthreads();
 }
 
@@ -85,7 +85,8 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
   constexpr int NS = D * D;
   __shared__ float s_k[D], s_a[D], s_v[D], s_q[D], s_do[D];
   __shared__ float s_b;
-  __shared__ float red[L::NW][D];
+  __shared__ __attribute__((aligned(16))) float s_P[D * (D + 4)];
+  __shared__ float quar[4][D];
   __shared__ float s_u[D], s_dd[D];
 
   const int bh = blockIdx.x;
@@ -107,34 +108,50 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
   float* hist = ckpt + (size_t)nch * NS;
   const size_t my = (size_t)i * D + c0;  // this thread's first state entry
 
-  // token t's vectors into LDS (threads < D, one channel each); with_q also
-  // loads q and dO for the backward step
-  auto load_tok = [&](int t, bool with_q) {
+  // Token vectors: threads < D fetch one channel of the next token into
+  // registers while the current token is processed (fetch), and move them to
+  // LDS when that token starts (commit, then a barrier).  with_q also takes q
+  // and dO for the backward step.
+  float nk = 0.f, nla = 0.f, nv = 0.f, nq = 0.f, ndo = 0.f, nb = 0.f;
+  auto fetch = [&](int t, bool with_q) {
     if (tid < D) {
       const size_t o = (size_t)t * D + tid;
-      s_k[tid] = to_f32(k[o]);
-      s_a[tid] = expf(to_f32(la[o]));
-      s_v[tid] = to_f32(v[o]);
+      nk = to_f32(k[o]);
+      nla = to_f32(la[o]);
+      nv = to_f32(v[o]);
       if (with_q) {
-        s_q[tid] = to_f32(q[o]);
-        s_do[tid] = dO ? to_f32(dO[o]) : 0.f;
+        nq = to_f32(q[o]);
+        ndo = dO ? to_f32(dO[o]) : 0.f;
       }
     }
-    if (tid == 0) s_b = to_f32(beta[t]);
+    if (tid == 0) nb = to_f32(beta[t]);
+  };
+  auto commit = [&](bool with_q) {
+    if (tid < D) {
+      s_k[tid] = nk;
+      s_a[tid] = expf(nla);
+      s_v[tid] = nv;
+      if (with_q) {
+        s_q[tid] = nq;
+        s_do[tid] = ndo;
+      }
+    }
+    if (tid == 0) s_b = nb;
     __syncthreads();
   };
 
   float S[CPT], p[CPT];
-  // one forward token on S (the state entering token t -> leaving it)
-  auto forward = [&](int t) {
-    load_tok(t, false);
+  // one forward token; `next` (or -1) is the token whose vectors to fetch meanwhile
+  auto forward = [&](int next) {
+    commit(false);
+    if (next >= 0) fetch(next, false);
     const float ai = s_a[i], ki = s_k[i];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       S[c] *= ai;
       p[c] = ki * S[c];
     }
-    col_reduce<D>(p, red, s_u, tid, c0);
+    col_reduce<D>(p, s_P, quar, s_u, tid, i, c0);
     const float b = s_b;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) S[c] += ki * b * (s_v[c0 + c] - s_u[c0 + c]);
@@ -143,12 +160,13 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
 
 #pragma unroll
   for (int c = 0; c < CPT; ++c) S[c] = a.S0 ? a.S0[(size_t)bh * NS + my + c] : 0.f;
+  if (nt > 0) fetch(0, false);
   for (int t = 0; t < nt; ++t) {
     if (t % kBwInterval == 0) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) ckpt[(size_t)(t / kBwInterval) * NS + my + c] = S[c];
     }
-    forward(t);
+    forward(t + 1 < nt ? t + 1 : -1);
   }
 
   float dS[CPT];
@@ -160,13 +178,16 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
     const int t1 = min(t0 + kBwInterval, nt);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) S[c] = ckpt[(size_t)ch * NS + my + c];
+    fetch(t0, false);
     for (int t = t0; t < t1; ++t) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) hist[(size_t)(t - t0) * NS + my + c] = S[c];
-      forward(t);
+      forward(t + 1 < t1 ? t + 1 : -1);
     }
+    fetch(t1 - 1, true);
     for (int t = t1 - 1; t >= t0; --t) {
-      load_tok(t, true);
+      commit(true);
+      if (t > t0) fetch(t - 1, true);
       const float ai = s_a[i], ki = s_k[i], qi = s_q[i], b = s_b;
       // D = Diag(a) S_{t-1} (in S), u = D^T k
 #pragma unroll
@@ -174,7 +195,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
         S[c] = ai * hist[(size_t)(t - t0) * NS + my + c];
         p[c] = ki * S[c];
       }
-      col_reduce<D>(p, red, s_u, tid, c0);
+      col_reduce<D>(p, s_P, quar, s_u, tid, i, c0);
       // dq = S_t dO with S_t = D + k delta^T; dS += q dO^T; dk (first part) = dS delta
       float dq = 0.f, dk = 0.f;
 #pragma unroll
@@ -187,7 +208,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
         p[c] = ki * dS[c];
       }
       // d_delta = dS^T k
-      col_reduce<D>(p, red, s_dd, tid, c0);
+      col_reduce<D>(p, s_P, quar, s_dd, tid, i, c0);
       float db = 0.f, dla = 0.f;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
