@@ -271,6 +271,18 @@ def backward_bytes(B, H, T, D):
     return B * H * T * (2 * 5 * D + 2 + 4 * 4 * D + 4) + 3 * B * H * D * D * 4
 
 
+PEAK_F32_TFLOPS = 157.3
+
+
+def backward_flops(B, H, T, D):
+    """fp32 arithmetic of one gradient evaluation per token-head: the forward
+    step (decay, u = D^T k, the rank-1 update: 5 D^2) that rebuilds the entering
+    state, and the backward step (decay, u and d_delta, dq, the two dS updates,
+    dk's two terms, dlog_alpha, the decay of dS: 20 D^2).  The kernel's second
+    forward pass over each interval (checkpoint recompute) is not counted."""
+    return B * H * T * 25 * D * D
+
+
 def bench_backward(args, dev):
     """Gradients of the batched prefill workload B=4, H=32, T=8192, d=128 (bf16
     inputs, fp32 start state, dO and dS_T given): time per call and tokens/s."""
@@ -289,9 +301,12 @@ def bench_backward(args, dev):
     torch.cuda.synchronize()
     ms, _ = time_launches(call, 3)
     nbytes = backward_bytes(B, H, T, D)
+    fl = backward_flops(B, H, T, D)
     del g, dO, ws
     return {"B": B, "H": H, "T": T, "D": D, "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
-            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "bound": "alu", "alu_tflops": fl / (ms * 1e-3) / 1e12,
+            "alu_frac": fl / (ms * 1e-3) / 1e12 / PEAK_F32_TFLOPS, "alu_peak_tflops": PEAK_F32_TFLOPS}
 
 
 def bench_snapshots(pf, args, interval=512):
