@@ -208,3 +208,42 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(kda.KdaError):
         kda.prefill(x, x, x, x, torch.zeros(1, 1, 4))
+
+
+def backward(lib, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, dO=FAKE, dST=None,
+             dq=FAKE, dk=FAKE, dv=FAKE, dla=FAKE, db=FAKE, dS0=FAKE, B=1, H=1, T=64, D=64, dt=BF16,
+             ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.kda_backward_workspace_bytes(B, H, T, D, D)
+    return lib.kda_prefill_backward(*P(q, k, v, la, beta, S0, dO, dST, dq, dk, dv, dla, db, dS0),
+                                    B, H, T, D, D, dt, ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
+
+
+def test_backward_workspace_query(lib):
+    """A checkpoint every 64 tokens plus 64 entering states, fp32 D x D, per head."""
+    q = lib.kda_backward_workspace_bytes
+    q.restype = ctypes.c_size_t
+    assert q(1, 1, 64, 64, 64) == (1 + 64) * 64 * 64 * 4
+    assert q(2, 3, 65, 128, 128) == 6 * (2 + 64) * 128 * 128 * 4
+    assert q(1, 1, 0, 64, 64) == 64 * 64 * 64 * 4
+    assert q(1, 1, 64, 64, 128) == 0 and q(1, 1, 64, 96, 96) == 0 and q(0, 1, 64, 64, 64) == 0
+
+
+def test_backward_validation(lib):
+    assert backward(lib, D=96) == ERR_UNSUPPORTED
+    assert backward(lib, dt=7) == ERR_UNSUPPORTED
+    assert backward(lib, T=-1, ws_bytes=0) == ERR_SHAPE
+    assert backward(lib, q=None) == ERR_NULL
+    assert backward(lib, dS0=None) == ERR_NULL
+    assert backward(lib, db=None) == ERR_NULL
+    assert backward(lib, ws=None) == ERR_NULL
+    assert backward(lib, ws_bytes=1024) == ERR_SHAPE
+    assert b"needed" in lib.kda_last_error()
+    assert backward(lib, dq=FAKE + 4) == ERR_ALIGN
+    assert backward(lib, dO=FAKE + 8) == ERR_ALIGN
+    assert backward(lib, B=1 << 20, H=1 << 12, T=1 << 10) == ERR_SHAPE
+    # no tokens: the per-token arrays are not needed, the workspace still is
+    assert backward(lib, T=0, q=None, k=None, v=None, la=None, beta=None, dO=None, dq=None, dk=None,
+                    dv=None, dla=None, db=None, ws=None) == ERR_NULL
+    # no heads: nothing to do
+    assert backward(lib, B=0, ws=None, ws_bytes=0) == OK
