@@ -103,3 +103,28 @@ def test_backward_deterministic():
     torch.cuda.synchronize()
     for n in NAMES:
         assert torch.equal(a[n], b[n]), n
+
+
+def test_backward_full_b4_h32_t8k():
+    """The bench's launch (B=4, H=32, T=8192, d=128, bf16, with S0, dO and dS_T,
+    drawn on the device as the bench draws them) on every head; the oracle
+    checks two sampled heads, read back from the device (heads are independent)."""
+    B, H, T, D = 4, 32, 8192, 128
+    print(f"[case] backward full B={B} H={H} T={T} D={D} bf16", flush=True)
+    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=1, s0_std=0.1, device=dev())
+    gen = torch.Generator(device=dev()).manual_seed(6)
+    dO = torch.randn(B, H, T, D, generator=gen, device=dev()).to(torch.bfloat16)
+    dST = torch.randn(B, H, D, D, generator=gen, device=dev())
+    out = kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], dO, dST)
+    torch.cuda.synchronize()
+    for (b, h) in ((0, 0), (3, 31)):
+        sl = lambda x: x[b:b + 1, h:h + 1].cpu()
+        ref = oracle.backward(sl(g["q"]), sl(g["k"]), sl(g["v"]), sl(g["log_alpha"]), sl(g["beta"]),
+                              sl(g["S0"]), sl(dO), sl(dST))
+        err = {}
+        for n in NAMES:
+            got = sl(out[n])
+            assert torch.isfinite(got).all(), n
+            err[n] = oracle.max_rel_l2(got, ref[n], 2 if n != "dbeta" else 1, floor=1e-6)
+        print(f"    head ({b},{h}) " + "  ".join(f"{k} {v:.2e}" for k, v in err.items()), flush=True)
+        assert max(err.values()) <= TOL["bf16"], err
