@@ -51,20 +51,20 @@ __device__ __forceinline__ float row_sum(float x) {
 }
 
 // Column sums over all D rows of the workgroup's state layout, into tot[D].
-// p holds this thread's contributions for row i, columns [c0, c0 + CPT).  They
-// go to the LDS matrix P (row pitch D + 4 floats) as 16-byte stores; after a
-// barrier thread tid adds a quarter of column tid % D (rows (tid / D) D/4 ..),
-// the four quarters meet in quar[4][D], and D threads add them into tot.  tot
-// is readable after the third barrier.
+// Every thread first stores its contributions for row i, columns [c0, c0 + CPT)
+// into the LDS matrix P (row pitch D + 4 floats) as 16-byte stores (put4).
+// col_sum then, after a barrier, has thread tid add a quarter of column
+// tid % D (rows (tid / D) D/4 ..); the four quarters meet in quar[4][D], and
+// D threads add them into tot.  tot is readable when col_sum returns.
 template <int D>
-__device__ __forceinline__ void col_reduce(const float* p, float* P, float (*quar)[D], float* tot, int tid, int i,
-                                           int c0) {
-  using L = BwLayout<D>;
+__device__ __forceinline__ void put4(float* P, int i, int col, float x0, float x1, float x2, float x3) {
+  *reinterpret_cast<f32x4*>(P + i * (D + 4) + col) = f32x4{x0, x1, x2, x3};
+}
+
+template <int D>
+__device__ __forceinline__ void col_sum(const float* P, float (*quar)[D], float* tot, int tid) {
+  static_assert(BwLayout<D>::THREADS == 4 * D, "one quarter column per thread");
   constexpr int PITCH = D + 4;
-  static_assert(L::THREADS == 4 * D, "one quarter column per thread");
-#pragma unroll
-  for (int c = 0; c < L::CPT; c += 4)
-    *reinterpret_cast<f32x4*>(P + i * PITCH + c0 + c) = f32x4{p[c], p[c + 1], p[c + 2], p[c + 3]};
   __syncthreads();
   const int j = tid % D, r = tid / D;
   float s = 0.f;
@@ -140,18 +140,21 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
     __syncthreads();
   };
 
-  float S[CPT], p[CPT];
+  float S[CPT];
   // one forward token; `next` (or -1) is the token whose vectors to fetch meanwhile
   auto forward = [&](int next) {
     commit(false);
     if (next >= 0) fetch(next, false);
     const float ai = s_a[i], ki = s_k[i];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
+    for (int c = 0; c < CPT; c += 4) {
       S[c] *= ai;
-      p[c] = ki * S[c];
+      S[c + 1] *= ai;
+      S[c + 2] *= ai;
+      S[c + 3] *= ai;
+      put4<D>(s_P, i, c0 + c, ki * S[c], ki * S[c + 1], ki * S[c + 2], ki * S[c + 3]);
     }
-    col_reduce<D>(p, s_P, quar, s_u, tid, i, c0);
+    col_sum<D>(s_P, quar, s_u, tid);
     const float b = s_b;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) S[c] += ki * b * (s_v[c0 + c] - s_u[c0 + c]);
@@ -184,6 +187,10 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
       for (int c = 0; c < CPT; ++c) hist[(size_t)(t - t0) * NS + my + c] = S[c];
       forward(t + 1 < t1 ? t + 1 : -1);
     }
+    // the entering state of the next token to walk is read one token ahead
+    float Sn[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) Sn[c] = hist[(size_t)(t1 - 1 - t0) * NS + my + c];
     fetch(t1 - 1, true);
     for (int t = t1 - 1; t >= t0; --t) {
       commit(true);
@@ -191,11 +198,18 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
       const float ai = s_a[i], ki = s_k[i], qi = s_q[i], b = s_b;
       // D = Diag(a) S_{t-1} (in S), u = D^T k
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        S[c] = ai * hist[(size_t)(t - t0) * NS + my + c];
-        p[c] = ki * S[c];
+      for (int c = 0; c < CPT; c += 4) {
+        S[c] = ai * Sn[c];
+        S[c + 1] = ai * Sn[c + 1];
+        S[c + 2] = ai * Sn[c + 2];
+        S[c + 3] = ai * Sn[c + 3];
+        put4<D>(s_P, i, c0 + c, ki * S[c], ki * S[c + 1], ki * S[c + 2], ki * S[c + 3]);
       }
-      col_reduce<D>(p, s_P, quar, s_u, tid, i, c0);
+      if (t > t0) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) Sn[c] = hist[(size_t)(t - 1 - t0) * NS + my + c];
+      }
+      col_sum<D>(s_P, quar, s_u, tid);
       // dq = S_t dO with S_t = D + k delta^T; dS += q dO^T; dk (first part) = dS delta
       float dq = 0.f, dk = 0.f;
 #pragma unroll
@@ -205,10 +219,12 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
         dq += (S[c] + ki * del) * d_o;
         dS[c] += qi * d_o;
         dk += dS[c] * del;
-        p[c] = ki * dS[c];
       }
+#pragma unroll
+      for (int c = 0; c < CPT; c += 4)
+        put4<D>(s_P, i, c0 + c, ki * dS[c], ki * dS[c + 1], ki * dS[c + 2], ki * dS[c + 3]);
       // d_delta = dS^T k
-      col_reduce<D>(p, s_P, quar, s_dd, tid, i, c0);
+      col_sum<D>(s_P, quar, s_dd, tid);
       float db = 0.f, dla = 0.f;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
