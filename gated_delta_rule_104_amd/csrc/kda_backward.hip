@@ -20,9 +20,9 @@
 // last, it runs the interval forward again from its checkpoint, keeping each
 // token's entering state in the workspace, and walks those tokens backwards.
 //
-// One workgroup of 4 D threads per head.  Thread tid owns row i = tid / 4 of
-// the state and of dS, columns [c0, c0 + D/4) with c0 = (tid % 4) D/4, in
-// registers.  Sums over a row (dq, dk, dlog_alpha) stay in the thread and the
+// One workgroup of 4 D threads per head.  In the backward walk thread tid owns
+// row i = tid / 4 of the state and of dS, columns [c0, c0 + D/4) with
+// c0 = (tid % 4) D/4, in registers (the forward passes own columns instead).  Sums over a row (dq, dk, dlog_alpha) stay in the thread and the
 // 4 adjacent lanes of its row.  Sums over the rows (u, d_delta) go through an
 // LDS transpose: every thread stores its row piece, then sums a quarter column.
 // Every step is evaluated in fp32 on inputs read as fp32.
@@ -140,38 +140,45 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
     __syncthreads();
   };
 
-  float S[CPT];
+  // Forward passes in the column layout: thread tid owns column jc = tid / 4,
+  // rows [r0, r0 + D/4) with r0 = (tid % 4) D/4, so u_j = sum_i k_i D[i][j] is a
+  // sum inside the thread and over the 4 adjacent lanes of the column.  The
+  // states go to the workspace row-major, where the backward walk (row layout)
+  // reads them after a barrier.
+  const int jc = tid >> 2;
+  const int r0 = (tid & 3) * (D / 4);
+  float Sc[CPT];
+  auto store_col = [&](float* dst) {
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) dst[(size_t)(r0 + m) * D + jc] = Sc[m];
+  };
   // one forward token; `next` (or -1) is the token whose vectors to fetch meanwhile
   auto forward = [&](int next) {
     commit(false);
     if (next >= 0) fetch(next, false);
-    const float ai = s_a[i], ki = s_k[i];
+    float u = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPT; c += 4) {
-      S[c] *= ai;
-      S[c + 1] *= ai;
-      S[c + 2] *= ai;
-      S[c + 3] *= ai;
-      put4<D>(s_P, i, c0 + c, ki * S[c], ki * S[c + 1], ki * S[c + 2], ki * S[c + 3]);
+    for (int m = 0; m < CPT; ++m) {
+      Sc[m] *= s_a[r0 + m];
+      u += s_k[r0 + m] * Sc[m];
     }
-    col_sum<D>(s_P, quar, s_u, tid);
-    const float b = s_b;
+    u += __shfl_xor(u, 1);
+    u += __shfl_xor(u, 2);
+    const float w = s_b * (s_v[jc] - u);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) S[c] += ki * b * (s_v[c0 + c] - s_u[c0 + c]);
-    __syncthreads();  // LDS reads done before the next token's loads
+    for (int m = 0; m < CPT; ++m) Sc[m] += s_k[r0 + m] * w;
+    __syncthreads();  // LDS reads done before the next token's vectors land
   };
 
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) S[c] = a.S0 ? a.S0[(size_t)bh * NS + my + c] : 0.f;
+  for (int m = 0; m < CPT; ++m) Sc[m] = a.S0 ? a.S0[(size_t)bh * NS + (size_t)(r0 + m) * D + jc] : 0.f;
   if (nt > 0) fetch(0, false);
   for (int t = 0; t < nt; ++t) {
-    if (t % kBwInterval == 0) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) ckpt[(size_t)(t / kBwInterval) * NS + my + c] = S[c];
-    }
+    if (t % kBwInterval == 0) store_col(ckpt + (size_t)(t / kBwInterval) * NS);
     forward(t + 1 < nt ? t + 1 : -1);
   }
 
+  float S[CPT];
   float dS[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) dS[c] = a.dS_T ? a.dS_T[(size_t)bh * NS + my + c] : 0.f;
@@ -180,11 +187,10 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
     const int t0 = ch * kBwInterval;
     const int t1 = min(t0 + kBwInterval, nt);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) S[c] = ckpt[(size_t)ch * NS + my + c];
+    for (int m = 0; m < CPT; ++m) Sc[m] = ckpt[(size_t)ch * NS + (size_t)(r0 + m) * D + jc];
     fetch(t0, false);
     for (int t = t0; t < t1; ++t) {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) hist[(size_t)(t - t0) * NS + my + c] = S[c];
+      store_col(hist + (size_t)(t - t0) * NS);
       forward(t + 1 < t1 ? t + 1 : -1);
     }
     // the entering state of the next token to walk is read one token ahead
