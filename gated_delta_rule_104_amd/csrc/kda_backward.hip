@@ -104,16 +104,18 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
   const T* la = static_cast<const T*>(a.la) + tok0 * D;
   const T* beta = static_cast<const T*>(a.beta) + tok0;
   const T* dO = a.dO ? static_cast<const T*>(a.dO) + tok0 * D : nullptr;
-  float* ckpt = a.ws + (size_t)bh * (size_t)(nch + kBwInterval) * NS;
+  float* ckpt = a.ws + (size_t)bh * ((size_t)(nch + kBwInterval) * NS + (size_t)kBwInterval * D);
   float* hist = ckpt + (size_t)nch * NS;
+  float* hu = hist + (size_t)kBwInterval * NS;  // u of each token of the interval
   const size_t my = (size_t)i * D + c0;  // this thread's first state entry
 
   // Token vectors: threads < D fetch one channel of the next token into
   // registers while the current token is processed (fetch), and move them to
   // LDS when that token starts (commit, then a barrier).  with_q also takes q
   // and dO for the backward step.
-  float nk = 0.f, nla = 0.f, nv = 0.f, nq = 0.f, ndo = 0.f, nb = 0.f;
-  auto fetch = [&](int t, bool with_q) {
+  // with_q also takes the token's u, kept by the forward pass at hu[tl].
+  float nk = 0.f, nla = 0.f, nv = 0.f, nq = 0.f, ndo = 0.f, nu = 0.f, nb = 0.f;
+  auto fetch = [&](int t, bool with_q, int tl = 0) {
     if (tid < D) {
       const size_t o = (size_t)t * D + tid;
       nk = to_f32(k[o]);
@@ -122,6 +124,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
       if (with_q) {
         nq = to_f32(q[o]);
         ndo = dO ? to_f32(dO[o]) : 0.f;
+        nu = hu[(size_t)tl * D + tid];
       }
     }
     if (tid == 0) nb = to_f32(beta[t]);
@@ -134,6 +137,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
       if (with_q) {
         s_q[tid] = nq;
         s_do[tid] = ndo;
+        s_u[tid] = nu;
       }
     }
     if (tid == 0) s_b = nb;
@@ -152,8 +156,9 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
 #pragma unroll
     for (int m = 0; m < CPT; ++m) dst[(size_t)(r0 + m) * D + jc] = Sc[m];
   };
-  // one forward token; `next` (or -1) is the token whose vectors to fetch meanwhile
-  auto forward = [&](int next) {
+  // one forward token; `next` (or -1) is the token whose vectors to fetch
+  // meanwhile; with keep >= 0 the token's u goes to hu[keep]
+  auto forward = [&](int next, int keep) {
     commit(false);
     if (next >= 0) fetch(next, false);
     float u = 0.f;
@@ -164,6 +169,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
     }
     u += __shfl_xor(u, 1);
     u += __shfl_xor(u, 2);
+    if (keep >= 0 && (tid & 3) == 0) hu[(size_t)keep * D + jc] = u;
     const float w = s_b * (s_v[jc] - u);
 #pragma unroll
     for (int m = 0; m < CPT; ++m) Sc[m] += s_k[r0 + m] * w;
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
   if (nt > 0) fetch(0, false);
   for (int t = 0; t < nt; ++t) {
     if (t % kBwInterval == 0) store_col(ckpt + (size_t)(t / kBwInterval) * NS);
-    forward(t + 1 < nt ? t + 1 : -1);
+    forward(t + 1 < nt ? t + 1 : -1, -1);
   }
 
   float S[CPT];
@@ -191,31 +197,24 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
     fetch(t0, false);
     for (int t = t0; t < t1; ++t) {
       store_col(hist + (size_t)(t - t0) * NS);
-      forward(t + 1 < t1 ? t + 1 : -1);
+      forward(t + 1 < t1 ? t + 1 : -1, t - t0);
     }
     // the entering state of the next token to walk is read one token ahead
     float Sn[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) Sn[c] = hist[(size_t)(t1 - 1 - t0) * NS + my + c];
-    fetch(t1 - 1, true);
+    fetch(t1 - 1, true, t1 - 1 - t0);
     for (int t = t1 - 1; t >= t0; --t) {
       commit(true);
-      if (t > t0) fetch(t - 1, true);
+      if (t > t0) fetch(t - 1, true, t - 1 - t0);
       const float ai = s_a[i], ki = s_k[i], qi = s_q[i], b = s_b;
-      // D = Diag(a) S_{t-1} (in S), u = D^T k
+      // D = Diag(a) S_{t-1} (in S); u = D^T k came with the token's vectors
 #pragma unroll
-      for (int c = 0; c < CPT; c += 4) {
-        S[c] = ai * Sn[c];
-        S[c + 1] = ai * Sn[c + 1];
-        S[c + 2] = ai * Sn[c + 2];
-        S[c + 3] = ai * Sn[c + 3];
-        put4<D>(s_P, i, c0 + c, ki * S[c], ki * S[c + 1], ki * S[c + 2], ki * S[c + 3]);
-      }
+      for (int c = 0; c < CPT; ++c) S[c] = ai * Sn[c];
       if (t > t0) {
 #pragma unroll
         for (int c = 0; c < CPT; ++c) Sn[c] = hist[(size_t)(t - 1 - t0) * NS + my + c];
       }
-      col_sum<D>(s_P, quar, s_u, tid);
       // dq = S_t dO with S_t = D + k delta^T; dS += q dO^T; dk (first part) = dS delta
       float dq = 0.f, dk = 0.f;
 #pragma unroll

@@ -56,9 +56,10 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
                          int NH, int H, int ntok, int D, bool bf16_io, hipStream_t stream);
 
 // Prefill gradients, one workgroup per head over [BH, T, D] inputs.  The
-// workspace holds (ceil(T / kBwInterval) + kBwInterval) fp32 D x D states per
-// head: a checkpoint at the start of every interval and the entering state of
-// every token of the interval being walked.
+// workspace holds, per head, (ceil(T / kBwInterval) + kBwInterval) fp32 D x D
+// states (a checkpoint at the start of every interval and the entering state
+// of every token of the interval being walked) and kBwInterval fp32 D-vectors
+// (u = D^T k of each token of that interval).
 constexpr int kBwInterval = 64;
 struct BackwardArgs {
   const void* q;
@@ -79,7 +80,8 @@ struct BackwardArgs {
   int T;
 };
 inline size_t backward_ws_floats(long long BH, int T, int D) {
-  return (size_t)BH * (size_t)((T + kBwInterval - 1) / kBwInterval + kBwInterval) * (size_t)D * D;
+  return (size_t)BH * ((size_t)((T + kBwInterval - 1) / kBwInterval + kBwInterval) * (size_t)D * D +
+                       (size_t)kBwInterval * D);
 }
 hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, hipStream_t stream);
 

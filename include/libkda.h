@@ -231,8 +231,9 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
  *   dq, dk_, dlog_alpha : [B, H, T, dk] fp32;  dv_ : [B, H, T, dv] fp32;
  *   dbeta : [B, H, T] fp32;  dS0 : [B, H, dk, dv] fp32.
  * The workspace (device memory, at least kda_backward_workspace_bytes, 16-byte
- * aligned) holds a state checkpoint every 64 tokens and the entering states of
- * one 64-token interval per head; its contents on return are undefined.  No
+ * aligned) holds a state checkpoint every 64 tokens, and the entering states
+ * and the vectors u = (Diag(alpha) S)^T k of one 64-token interval, per head;
+ * its contents on return are undefined.  No
  * output may alias an input or the workspace.  Errors: KDA_ERR_NULL for a
  * missing workspace or required pointer, KDA_ERR_SHAPE for a workspace below
  * the required size.
