@@ -83,11 +83,13 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
   using L = BwLayout<D>;
   constexpr int CPT = L::CPT;
   constexpr int NS = D * D;
-  __shared__ float s_k[D], s_a[D], s_v[D], s_q[D], s_do[D];
-  __shared__ float s_b;
+  // per-token vectors, double-buffered: consecutive commits alternate buffers,
+  // so a token's vectors land while the previous token may still be read
+  __shared__ float s_k[2][D], s_a[2][D], s_v[2][D], s_q[2][D], s_do[2][D], s_u[2][D];
+  __shared__ float s_b[2];
   __shared__ __attribute__((aligned(16))) float s_P[D * (D + 4)];
   __shared__ float quar[4][D];
-  __shared__ float s_u[D], s_dd[D];
+  __shared__ float s_dd[D];
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
@@ -129,19 +131,25 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
     }
     if (tid == 0) nb = to_f32(beta[t]);
   };
+  // Returns the buffer the token's vectors are in.  Its barrier also orders
+  // every LDS access of the tokens before it against the ones after it.
+  int ncommit = 0;
   auto commit = [&](bool with_q) {
+    const int cb = ncommit & 1;
+    ++ncommit;
     if (tid < D) {
-      s_k[tid] = nk;
-      s_a[tid] = expf(nla);
-      s_v[tid] = nv;
+      s_k[cb][tid] = nk;
+      s_a[cb][tid] = expf(nla);
+      s_v[cb][tid] = nv;
       if (with_q) {
-        s_q[tid] = nq;
-        s_do[tid] = ndo;
-        s_u[tid] = nu;
+        s_q[cb][tid] = nq;
+        s_do[cb][tid] = ndo;
+        s_u[cb][tid] = nu;
       }
     }
-    if (tid == 0) s_b = nb;
+    if (tid == 0) s_b[cb] = nb;
     __syncthreads();
+    return cb;
   };
 
   // Forward passes in the column layout: thread tid owns column jc = tid / 4,
@@ -159,21 +167,20 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
   // one forward token; `next` (or -1) is the token whose vectors to fetch
   // meanwhile; with keep >= 0 the token's u goes to hu[keep]
   auto forward = [&](int next, int keep) {
-    commit(false);
+    const int cb = commit(false);
     if (next >= 0) fetch(next, false);
     float u = 0.f;
 #pragma unroll
     for (int m = 0; m < CPT; ++m) {
-      Sc[m] *= s_a[r0 + m];
-      u += s_k[r0 + m] * Sc[m];
+      Sc[m] *= s_a[cb][r0 + m];
+      u += s_k[cb][r0 + m] * Sc[m];
     }
     u += __shfl_xor(u, 1);
     u += __shfl_xor(u, 2);
     if (keep >= 0 && (tid & 3) == 0) hu[(size_t)keep * D + jc] = u;
-    const float w = s_b * (s_v[jc] - u);
+    const float w = s_b[cb] * (s_v[cb][jc] - u);
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) Sc[m] += s_k[r0 + m] * w;
-    __syncthreads();  // LDS reads done before the next token's vectors land
+    for (int m = 0; m < CPT; ++m) Sc[m] += s_k[cb][r0 + m] * w;
   };
 
 #pragma unroll
@@ -199,15 +206,18 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
       store_col(hist + (size_t)(t - t0) * NS);
       forward(t + 1 < t1 ? t + 1 : -1, t - t0);
     }
+    // the last token's u (written after its barrier) and every stored state
+    // are read below by other threads
+    __syncthreads();
     // the entering state of the next token to walk is read one token ahead
     float Sn[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) Sn[c] = hist[(size_t)(t1 - 1 - t0) * NS + my + c];
     fetch(t1 - 1, true, t1 - 1 - t0);
     for (int t = t1 - 1; t >= t0; --t) {
-      commit(true);
+      const int cb = commit(true);
       if (t > t0) fetch(t - 1, true, t - 1 - t0);
-      const float ai = s_a[i], ki = s_k[i], qi = s_q[i], b = s_b;
+      const float ai = s_a[cb][i], ki = s_k[cb][i], qi = s_q[cb][i], b = s_b[cb];
       // D = Diag(a) S_{t-1} (in S); u = D^T k came with the token's vectors
 #pragma unroll
       for (int c = 0; c < CPT; ++c) S[c] = ai * Sn[c];
@@ -219,8 +229,8 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
       float dq = 0.f, dk = 0.f;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        const float del = b * (s_v[c0 + c] - s_u[c0 + c]);
-        const float d_o = s_do[c0 + c];
+        const float del = b * (s_v[cb][c0 + c] - s_u[cb][c0 + c]);
+        const float d_o = s_do[cb][c0 + c];
         dq += (S[c] + ki * del) * d_o;
         dS[c] += qi * d_o;
         dk += dS[c] * del;
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const float dd = s_dd[c0 + c];
-        db += dd * (s_v[c0 + c] - s_u[c0 + c]);
+        db += dd * (s_v[cb][c0 + c] - s_u[cb][c0 + c]);
         const float du = -b * dd;
         dk += S[c] * du;
         dS[c] += ki * du;
@@ -256,7 +266,6 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
         for (int c = 0; c < CPT; ++c) a.dv[o + c0 + c] = b * s_dd[c0 + c];
         if (tid == 0) a.dbeta[tok0 + t] = db;
       }
-      __syncthreads();  // LDS reads done before the next token's loads
     }
   }
 #pragma unroll
