@@ -71,6 +71,25 @@ def test_backward_f32_d128():
     assert max(err.values()) <= TOL["f32"], err
 
 
+def test_backward_small_f32_workload():
+    """The small fp32 workload's shape: B=1, H=2, T=256, d=64."""
+    err = grads_case(1, 2, 256, 64, "f32", 0, s0_std=0.0)
+    assert max(err.values()) <= TOL["f32"], err
+
+
+@pytest.mark.parametrize("variant", ["alpha_one", "alpha_min", "beta_zero"])
+def test_backward_gate_extremes(variant):
+    """No decay (alpha = 1), the lower bound (log alpha = -1), and beta = 0."""
+    err = grads_case(1, 2, 100, 64, "f32", 96, variant=variant)
+    assert max(err.values()) <= TOL["f32"], err
+
+
+def test_backward_many_intervals():
+    """1000 tokens: 15 full 64-token intervals and a ragged one of 40."""
+    err = grads_case(1, 2, 1000, 64, "bf16", 97, variant="slow")
+    assert max(err.values()) <= TOL["bf16"], err
+
+
 def test_backward_only_end_state_gradient():
     """dO = 0: only S_T carries the loss; dq is zero and dS0 = M^T dS_T."""
     err = grads_case(1, 2, 150, 128, "bf16", 93, variant="slow", with_dO=False)
