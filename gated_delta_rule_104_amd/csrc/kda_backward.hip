@@ -20,11 +20,18 @@
 // last, it runs the interval forward again from its checkpoint, keeping each
 // token's entering state in the workspace, and walks those tokens backwards.
 //
-// One workgroup of 4 D threads per head.  In the backward walk thread tid owns
-// row i = tid / 4 of the state and of dS, columns [c0, c0 + D/4) with
-// c0 = (tid % 4) D/4, in registers (the forward passes own columns instead).  Sums over a row (dq, dk, dlog_alpha) stay in the thread and the
-// 4 adjacent lanes of its row.  Sums over the rows (u, d_delta) go through an
-// LDS transpose: every thread stores its row piece, then sums a quarter column.
+// One workgroup of 4 D threads per head.
+//  - Forward passes: thread tid owns column tid / 4 of the state, a quarter of
+//    its rows, so u = D^T k is a sum inside the thread and its 3 neighbours.
+//    The states go to the workspace row-major; the interval's pass also keeps
+//    each token's u for the backward walk.
+//  - Backward walk: thread tid owns row i = tid / 4 of the state and of dS,
+//    columns [c0, c0 + D/4) with c0 = (tid % 4) D/4.  Sums over a row (dq, dk,
+//    dlog_alpha) stay in the thread and its 3 neighbours; the sum over the
+//    rows d_delta = dS^T k goes through an LDS transpose (every thread stores
+//    its row piece, then adds a quarter column).
+//  - The per-token vectors pass through LDS, double-buffered, and the next
+//    token's are fetched into registers while the current one runs.
 // Every step is evaluated in fp32 on inputs read as fp32.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
@@ -113,9 +120,9 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
 
   // Token vectors: threads < D fetch one channel of the next token into
   // registers while the current token is processed (fetch), and move them to
-  // LDS when that token starts (commit, then a barrier).  with_q also takes q
-  // and dO for the backward step.
-  // with_q also takes the token's u, kept by the forward pass at hu[tl].
+  // LDS when that token starts (commit, then a barrier).  with_q also takes q,
+  // dO and the token's u (kept by the interval's forward pass at hu[tl]) for
+  // the backward step.
   float nk = 0.f, nla = 0.f, nv = 0.f, nq = 0.f, ndo = 0.f, nu = 0.f, nb = 0.f;
   auto fetch = [&](int t, bool with_q, int tl = 0) {
     if (tid < D) {
