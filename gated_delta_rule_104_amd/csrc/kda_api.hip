@@ -581,7 +581,14 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
   a.dq = dq; a.dk = dk_; a.dv = dv_; a.dla = dlog_alpha; a.dbeta = dbeta; a.dS0 = dS0;
   a.ws = static_cast<float*>(workspace);
   a.T = T;
-  hipError_t e = kda::launch_backward(a, (int)BH, dk, dtype == KDA_BF16, stream);
+  // two workgroups per head (each with half of the state's columns) when that
+  // still fits the chip in one round; KDA_BW_SPLIT=1 or 2 forces the choice
+  int split = 2 * BH <= cu_count() ? 2 : 1;
+  if (const char* env = getenv("KDA_BW_SPLIT")) {
+    const int v = atoi(env);
+    if (v == 1 || v == 2) split = v;
+  }
+  hipError_t e = kda::launch_backward(a, (int)BH, dk, dtype == KDA_BF16, split, stream);
   if (e != hipSuccess) return hip_fail(e, "kda_prefill_backward launch");
   return ok();
 }

@@ -20,19 +20,25 @@
 // last, it runs the interval forward again from its checkpoint, keeping each
 // token's entering state in the workspace, and walks those tokens backwards.
 //
-// One workgroup of 4 D threads per head.
-//  - Forward passes: thread tid owns column tid / 4 of the state, a quarter of
-//    its rows, so u = D^T k is a sum inside the thread and its 3 neighbours.
+// SPLIT workgroups per head (2 when that still fits the chip in one round),
+// each owning DC = D / SPLIT of the state's columns: the forward recurrence and
+// d_delta are column by column, so only the row sums (dq, dk, dlog_alpha,
+// dbeta) need the other workgroup's half; with SPLIT = 2 each half goes to the
+// workspace and a second kernel adds them.  A workgroup has 4 DC threads.
+//  - Forward passes: thread tid owns column tid / 4 of its slice, a quarter of
+//    the rows, so u = D^T k is a sum inside the thread and its 3 neighbours.
 //    The states go to the workspace row-major; the interval's pass also keeps
 //    each token's u for the backward walk.
-//  - Backward walk: thread tid owns row i = tid / 4 of the state and of dS,
-//    columns [c0, c0 + D/4) with c0 = (tid % 4) D/4.  Sums over a row (dq, dk,
-//    dlog_alpha) stay in the thread and its 3 neighbours; the sum over the
-//    rows d_delta = dS^T k goes through an LDS transpose (every thread stores
-//    its row piece, then adds a quarter column).
+//  - Backward walk: thread tid owns row i = tid / TPR of the slice of the
+//    state and of dS, D/4 columns from c0 = (tid % TPR) D/4 (TPR = 4 / SPLIT).
+//    Sums over a row (dq, dk, dlog_alpha) stay in the thread and its TPR - 1
+//    neighbours; the sum over the rows d_delta = dS^T k goes through an LDS
+//    transpose (every thread stores its row piece, then adds a quarter column).
 //  - The per-token vectors pass through LDS, double-buffered, and the next
 //    token's are fetched into registers while the current one runs.
 // Every step is evaluated in fp32 on inputs read as fp32.
+#include <algorithm>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -40,100 +46,116 @@ namespace kda {
 
 namespace {
 
-template <int D>
+template <int D, int SPLIT>
 struct BwLayout {
-  static constexpr int TPR = 4;                // threads per state row
-  static constexpr int THREADS = TPR * D;      // one thread per (row, column quarter)
-  static constexpr int NW = THREADS / 64;      // waves
-  static constexpr int CPT = D / TPR;          // columns per thread
-  static_assert(THREADS % 64 == 0 && CPT % 4 == 0, "layout");
+  static constexpr int DC = D / SPLIT;      // state columns per workgroup
+  static constexpr int THREADS = 4 * DC;    // forward: one thread per (column, row quarter)
+  static constexpr int TPR = THREADS / D;   // backward: threads per state row
+  static constexpr int CPT = DC / TPR;      // backward: columns per thread (D / 4)
+  static constexpr int RPT = D / 4;         // forward: rows per thread
+  static_assert(THREADS % 64 == 0 && THREADS >= D && TPR >= 1 && CPT % 4 == 0, "layout");
 };
 
 // Sum of x over the TPR adjacent lanes that share a state row.
-template <int D>
+template <int TPR>
 __device__ __forceinline__ float row_sum(float x) {
 #pragma unroll
-  for (int m = 1; m < BwLayout<D>::TPR; m <<= 1) x += __shfl_xor(x, m);
+  for (int m = 1; m < TPR; m <<= 1) x += __shfl_xor(x, m);
   return x;
 }
 
-// Column sums over all D rows of the workgroup's state layout, into tot[D].
-// Every thread first stores its contributions for row i, columns [c0, c0 + CPT)
-// into the LDS matrix P (row pitch D + 4 floats) as 16-byte stores (put4).
+// Column sums over all D rows of a workgroup's state slice, into tot[DC].
+// Every thread first stores its contributions for row i (CPT columns from c0)
+// into the LDS matrix P (row pitch DC + 4 floats) as 16-byte stores (put4).
 // col_sum then, after a barrier, has thread tid add a quarter of column
-// tid % D (rows (tid / D) D/4 ..); the four quarters meet in quar[4][D], and
-// D threads add them into tot.  tot is readable when col_sum returns.
-template <int D>
+// tid % DC (rows (tid / DC) D/4 ..); the four quarters meet in quar[4][DC], and
+// DC threads add them into tot.  tot is readable when col_sum returns.
+template <int DC>
 __device__ __forceinline__ void put4(float* P, int i, int col, float x0, float x1, float x2, float x3) {
-  *reinterpret_cast<f32x4*>(P + i * (D + 4) + col) = f32x4{x0, x1, x2, x3};
+  *reinterpret_cast<f32x4*>(P + i * (DC + 4) + col) = f32x4{x0, x1, x2, x3};
 }
 
-template <int D>
-__device__ __forceinline__ void col_sum(const float* P, float (*quar)[D], float* tot, int tid) {
-  static_assert(BwLayout<D>::THREADS == 4 * D, "one quarter column per thread");
-  constexpr int PITCH = D + 4;
+template <int D, int DC>
+__device__ __forceinline__ void col_sum(const float* P, float (*quar)[DC], float* tot, int tid) {
+  constexpr int PITCH = DC + 4;
   __syncthreads();
-  const int j = tid % D, r = tid / D;
+  const int j = tid % DC, r = tid / DC;
   float s = 0.f;
 #pragma unroll 8
   for (int rr = 0; rr < D / 4; ++rr) s += P[(r * (D / 4) + rr) * PITCH + j];
   quar[r][j] = s;
   __syncthreads();
-  if (tid < D) tot[tid] = (quar[0][tid] + quar[1][tid]) + (quar[2][tid] + quar[3][tid]);
+  if (tid < DC) tot[tid] = (quar[0][tid] + quar[1][tid]) + (quar[2][tid] + quar[3][tid]);
   __syncthreads();
+}
+
+// Floats of one head's checkpoint / interval area; workgroup half hc of the
+// head uses the hc-th 1/SPLIT of it.
+__host__ __device__ inline size_t bw_head_floats(int T, int D) {
+  return (size_t)((T + kBwInterval - 1) / kBwInterval + kBwInterval) * D * D + (size_t)kBwInterval * D;
 }
 
 }  // namespace
 
-template <typename T, int D>
-__global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) {
-  using L = BwLayout<D>;
-  constexpr int CPT = L::CPT;
-  constexpr int NS = D * D;
+template <typename T, int D, int SPLIT>
+__global__ __launch_bounds__(4 * (D / SPLIT), 1) void kda_backward_kernel(BackwardArgs a) {
+  using L = BwLayout<D, SPLIT>;
+  constexpr int DC = L::DC, CPT = L::CPT, RPT = L::RPT, TPR = L::TPR;
+  constexpr int NS = D * DC;  // floats of one workgroup's state slice ([D][DC])
   // per-token vectors, double-buffered: consecutive commits alternate buffers,
   // so a token's vectors land while the previous token may still be read
-  __shared__ float s_k[2][D], s_a[2][D], s_v[2][D], s_q[2][D], s_do[2][D], s_u[2][D];
+  __shared__ float s_k[2][D], s_a[2][D], s_q[2][D];        // per row
+  __shared__ float s_v[2][DC], s_do[2][DC], s_u[2][DC];    // per own column
   __shared__ float s_b[2];
-  __shared__ __attribute__((aligned(16))) float s_P[D * (D + 4)];
-  __shared__ float quar[4][D];
-  __shared__ float s_dd[D];
+  __shared__ __attribute__((aligned(16))) float s_P[D * (DC + 4)];
+  __shared__ float quar[4][DC];
+  __shared__ float s_dd[DC];
 
-  const int bh = blockIdx.x;
+  const int nbh = gridDim.x / SPLIT;
+  const int bh = blockIdx.x / SPLIT, hc = blockIdx.x % SPLIT;
+  const int col0 = hc * DC;  // first state column of this workgroup
   const int tid = threadIdx.x;
-  const int i = tid / L::TPR;
-  const int part = tid % L::TPR;
-  const int c0 = part * CPT;
+  const int i = tid / TPR;
+  const int part = tid % TPR;
+  const int c0 = part * CPT;  // local column
   const int nt = a.T;
   const int nch = (nt + kBwInterval - 1) / kBwInterval;
 
   const size_t tok0 = (size_t)bh * nt;
+  const size_t st0 = (size_t)bh * D * D;  // this head's D x D states
   const T* q = static_cast<const T*>(a.q) + tok0 * D;
   const T* k = static_cast<const T*>(a.k) + tok0 * D;
   const T* v = static_cast<const T*>(a.v) + tok0 * D;
   const T* la = static_cast<const T*>(a.la) + tok0 * D;
   const T* beta = static_cast<const T*>(a.beta) + tok0;
   const T* dO = a.dO ? static_cast<const T*>(a.dO) + tok0 * D : nullptr;
-  float* ckpt = a.ws + (size_t)bh * ((size_t)(nch + kBwInterval) * NS + (size_t)kBwInterval * D);
+  const size_t hf = bw_head_floats(nt, D);
+  float* ckpt = a.ws + (size_t)bh * hf + (size_t)hc * (hf / SPLIT);
   float* hist = ckpt + (size_t)nch * NS;
-  float* hu = hist + (size_t)kBwInterval * NS;  // u of each token of the interval
-  const size_t my = (size_t)i * D + c0;  // this thread's first state entry
+  float* hu = hist + (size_t)kBwInterval * NS;  // u of each token of the interval, own columns
+  // SPLIT = 2: this half's row sums, [hc][bh][t][3D + 1] after every head's area
+  float* part_sums = a.ws + (size_t)nbh * hf + ((size_t)hc * nbh + bh) * (size_t)nt * (3 * D + 1);
+  const size_t my = (size_t)i * DC + c0;  // this thread's first entry of the slice
 
-  // Token vectors: threads < D fetch one channel of the next token into
-  // registers while the current token is processed (fetch), and move them to
-  // LDS when that token starts (commit, then a barrier).  with_q also takes q,
-  // dO and the token's u (kept by the interval's forward pass at hu[tl]) for
-  // the backward step.
-  float nk = 0.f, nla = 0.f, nv = 0.f, nq = 0.f, ndo = 0.f, nu = 0.f, nb = 0.f;
+  // Token vectors: threads < D fetch one row channel (k, log_alpha, q) and
+  // threads < DC one own column (v, dO, u) of the next token into registers
+  // while the current token is processed (fetch), and move them to LDS when
+  // that token starts (commit, then a barrier).  with_q also takes q, dO and
+  // the token's u (kept by the interval's forward pass at hu[tl]) for the
+  // backward step.
+  float nk = 0.f, nla = 0.f, nq = 0.f, nv = 0.f, ndo = 0.f, nu = 0.f, nb = 0.f;
   auto fetch = [&](int t, bool with_q, int tl = 0) {
+    const size_t o = (size_t)t * D;
     if (tid < D) {
-      const size_t o = (size_t)t * D + tid;
-      nk = to_f32(k[o]);
-      nla = to_f32(la[o]);
-      nv = to_f32(v[o]);
+      nk = to_f32(k[o + tid]);
+      nla = to_f32(la[o + tid]);
+      if (with_q) nq = to_f32(q[o + tid]);
+    }
+    if (tid < DC) {
+      nv = to_f32(v[o + col0 + tid]);
       if (with_q) {
-        nq = to_f32(q[o]);
-        ndo = dO ? to_f32(dO[o]) : 0.f;
-        nu = hu[(size_t)tl * D + tid];
+        ndo = dO ? to_f32(dO[o + col0 + tid]) : 0.f;
+        nu = hu[(size_t)tl * DC + tid];
       }
     }
     if (tid == 0) nb = to_f32(beta[t]);
@@ -147,9 +169,11 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
     if (tid < D) {
       s_k[cb][tid] = nk;
       s_a[cb][tid] = expf(nla);
+      if (with_q) s_q[cb][tid] = nq;
+    }
+    if (tid < DC) {
       s_v[cb][tid] = nv;
       if (with_q) {
-        s_q[cb][tid] = nq;
         s_do[cb][tid] = ndo;
         s_u[cb][tid] = nu;
       }
@@ -159,17 +183,17 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
     return cb;
   };
 
-  // Forward passes in the column layout: thread tid owns column jc = tid / 4,
-  // rows [r0, r0 + D/4) with r0 = (tid % 4) D/4, so u_j = sum_i k_i D[i][j] is a
-  // sum inside the thread and over the 4 adjacent lanes of the column.  The
-  // states go to the workspace row-major, where the backward walk (row layout)
-  // reads them after a barrier.
+  // Forward passes in the column layout: thread tid owns local column jc =
+  // tid / 4, rows [r0, r0 + D/4) with r0 = (tid % 4) D/4, so u_j = sum_i k_i
+  // D[i][j] is a sum inside the thread and over the 4 adjacent lanes of the
+  // column.  The states go to the workspace as [D][DC] slices, where the
+  // backward walk (row layout) reads them after a barrier.
   const int jc = tid >> 2;
-  const int r0 = (tid & 3) * (D / 4);
-  float Sc[CPT];
+  const int r0 = (tid & 3) * RPT;
+  float Sc[RPT];
   auto store_col = [&](float* dst) {
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) dst[(size_t)(r0 + m) * D + jc] = Sc[m];
+    for (int m = 0; m < RPT; ++m) dst[(size_t)(r0 + m) * DC + jc] = Sc[m];
   };
   // one forward token; `next` (or -1) is the token whose vectors to fetch
   // meanwhile; with keep >= 0 the token's u goes to hu[keep]
@@ -178,20 +202,20 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
     if (next >= 0) fetch(next, false);
     float u = 0.f;
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) {
+    for (int m = 0; m < RPT; ++m) {
       Sc[m] *= s_a[cb][r0 + m];
       u += s_k[cb][r0 + m] * Sc[m];
     }
     u += __shfl_xor(u, 1);
     u += __shfl_xor(u, 2);
-    if (keep >= 0 && (tid & 3) == 0) hu[(size_t)keep * D + jc] = u;
+    if (keep >= 0 && (tid & 3) == 0) hu[(size_t)keep * DC + jc] = u;
     const float w = s_b[cb] * (s_v[cb][jc] - u);
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) Sc[m] += s_k[cb][r0 + m] * w;
+    for (int m = 0; m < RPT; ++m) Sc[m] += s_k[cb][r0 + m] * w;
   };
 
 #pragma unroll
-  for (int m = 0; m < CPT; ++m) Sc[m] = a.S0 ? a.S0[(size_t)bh * NS + (size_t)(r0 + m) * D + jc] : 0.f;
+  for (int m = 0; m < RPT; ++m) Sc[m] = a.S0 ? a.S0[st0 + (size_t)(r0 + m) * D + col0 + jc] : 0.f;
   if (nt > 0) fetch(0, false);
   for (int t = 0; t < nt; ++t) {
     if (t % kBwInterval == 0) store_col(ckpt + (size_t)(t / kBwInterval) * NS);
@@ -201,13 +225,13 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
   float S[CPT];
   float dS[CPT];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) dS[c] = a.dS_T ? a.dS_T[(size_t)bh * NS + my + c] : 0.f;
+  for (int c = 0; c < CPT; ++c) dS[c] = a.dS_T ? a.dS_T[st0 + (size_t)i * D + col0 + c0 + c] : 0.f;
 
   for (int ch = nch - 1; ch >= 0; --ch) {
     const int t0 = ch * kBwInterval;
     const int t1 = min(t0 + kBwInterval, nt);
 #pragma unroll
-    for (int m = 0; m < CPT; ++m) Sc[m] = ckpt[(size_t)ch * NS + (size_t)(r0 + m) * D + jc];
+    for (int m = 0; m < RPT; ++m) Sc[m] = ckpt[(size_t)ch * NS + (size_t)(r0 + m) * DC + jc];
     fetch(t0, false);
     for (int t = t0; t < t1; ++t) {
       store_col(hist + (size_t)(t - t0) * NS);
@@ -244,9 +268,9 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
       }
 #pragma unroll
       for (int c = 0; c < CPT; c += 4)
-        put4<D>(s_P, i, c0 + c, ki * dS[c], ki * dS[c + 1], ki * dS[c + 2], ki * dS[c + 3]);
-      // d_delta = dS^T k
-      col_sum<D>(s_P, quar, s_dd, tid);
+        put4<DC>(s_P, i, c0 + c, ki * dS[c], ki * dS[c + 1], ki * dS[c + 2], ki * dS[c + 3]);
+      // d_delta = dS^T k (own columns)
+      col_sum<D, DC>(s_P, quar, s_dd, tid);
       float db = 0.f, dla = 0.f;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
@@ -258,39 +282,85 @@ __global__ __launch_bounds__(4 * D, 1) void kda_backward_kernel(BackwardArgs a) 
         dla += S[c] * dS[c];
         dS[c] *= ai;
       }
-      dq = row_sum<D>(dq);
-      dk = row_sum<D>(dk);
-      dla = row_sum<D>(dla);
-      db = row_sum<D>(db);
+      dq = row_sum<TPR>(dq);
+      dk = row_sum<TPR>(dk);
+      dla = row_sum<TPR>(dla);
+      db = row_sum<TPR>(db);
       const size_t o = (tok0 + t) * D;
-      if (part == 0) {
-        a.dq[o + i] = dq;
-        a.dk[o + i] = dk;
-        a.dla[o + i] = dla;
-      }
-      if (tid < L::TPR) {  // the threads of row 0 hold d_delta for all columns
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) a.dv[o + c0 + c] = b * s_dd[c0 + c];
+      if (SPLIT == 1) {
+        if (part == 0) {
+          a.dq[o + i] = dq;
+          a.dk[o + i] = dk;
+          a.dla[o + i] = dla;
+        }
         if (tid == 0) a.dbeta[tok0 + t] = db;
+      } else {
+        float* ps = part_sums + (size_t)t * (3 * D + 1);
+        if (part == 0) {
+          ps[i] = dq;
+          ps[D + i] = dk;
+          ps[2 * D + i] = dla;
+        }
+        if (tid == 0) ps[3 * D] = db;
+      }
+      if (tid < TPR) {  // the threads of row 0 hold d_delta for all own columns
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) a.dv[o + col0 + c0 + c] = b * s_dd[c0 + c];
       }
     }
   }
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) a.dS0[(size_t)bh * NS + my + c] = dS[c];
+  for (int c = 0; c < CPT; ++c) a.dS0[st0 + (size_t)i * D + col0 + c0 + c] = dS[c];
 }
 
-hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, hipStream_t stream) {
-  if (BH <= 0) return hipSuccess;
-#define KDA_BW(TY, DD) \
-  hipLaunchKernelGGL((kda_backward_kernel<TY, DD>), dim3(BH), dim3(4 * DD), 0, stream, a)
-  if (bf16_io) {
-    if (D == 128) KDA_BW(bf16, 128);
-    else KDA_BW(bf16, 64);
-  } else {
-    if (D == 128) KDA_BW(float, 128);
-    else KDA_BW(float, 64);
+// SPLIT = 2: adds the two workgroups' row sums of every token, [2][n] with
+// n = BH T (3D + 1), into dq, dk, dlog_alpha and dbeta (fixed order, so the
+// result is deterministic).
+__global__ __launch_bounds__(256) void kda_backward_sum_kernel(const float* __restrict__ ps, float* dq, float* dk,
+                                                                float* dla, float* dbeta, long long rows, int D) {
+  const int W = 3 * D + 1;
+  const long long n = rows * W;
+  for (long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (long long)gridDim.x * blockDim.x) {
+    const long long row = x / W;
+    const int e = (int)(x - row * W);
+    const float s = ps[x] + ps[x + n];
+    if (e < D) dq[row * D + e] = s;
+    else if (e < 2 * D) dk[row * D + e - D] = s;
+    else if (e < 3 * D) dla[row * D + e - 2 * D] = s;
+    else dbeta[row] = s;
   }
+}
+
+size_t backward_ws_floats(long long BH, int T, int D) {
+  return (size_t)BH * bw_head_floats(T, D) + 2 * (size_t)BH * (size_t)T * (3 * D + 1);
+}
+
+hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, int split, hipStream_t stream) {
+  if (BH <= 0) return hipSuccess;
+#define KDA_BW(TY, DD, SP)                                                                             \
+  hipLaunchKernelGGL((kda_backward_kernel<TY, DD, SP>), dim3((long long)BH * SP),                    \
+                     dim3(4 * ((DD) / (SP))), 0, stream, a)
+#define KDA_BW_D(TY, SP) \
+  do {                   \
+    if (D == 128) KDA_BW(TY, 128, SP); \
+    else KDA_BW(TY, 64, SP);           \
+  } while (0)
+  if (split == 2) {
+    if (bf16_io) KDA_BW_D(bf16, 2);
+    else KDA_BW_D(float, 2);
+  } else {
+    if (bf16_io) KDA_BW_D(bf16, 1);
+    else KDA_BW_D(float, 1);
+  }
+#undef KDA_BW_D
 #undef KDA_BW
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || split != 2 || a.T == 0) return e;
+  const long long rows = (long long)BH * a.T;
+  const long long n = rows * (3 * D + 1);
+  const int blocks = (int)std::min<long long>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(kda_backward_sum_kernel, dim3(blocks), dim3(256), 0, stream,
+                     a.ws + (size_t)BH * bw_head_floats(a.T, D), a.dq, a.dk, a.dla, a.dbeta, rows, D);
   return hipGetLastError();
 }
 

@@ -55,11 +55,12 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
                          const void* beta, const float* S_in, float* S_out, void* o, float* S_pos,
                          int NH, int H, int ntok, int D, bool bf16_io, hipStream_t stream);
 
-// Prefill gradients, one workgroup per head over [BH, T, D] inputs.  The
-// workspace holds, per head, (ceil(T / kBwInterval) + kBwInterval) fp32 D x D
-// states (a checkpoint at the start of every interval and the entering state
-// of every token of the interval being walked) and kBwInterval fp32 D-vectors
-// (u = D^T k of each token of that interval).
+// Prefill gradients over [BH, T, D] inputs, split workgroups (1 or 2) per
+// head.  The workspace holds, per head, (ceil(T / kBwInterval) + kBwInterval)
+// fp32 D x D states (a checkpoint at the start of every interval and the
+// entering state of every token of the interval being walked) and kBwInterval
+// fp32 D-vectors (u = D^T k of each token of that interval), then, for all
+// heads, two halves of the row sums of every token (2 BH T (3D + 1) floats).
 constexpr int kBwInterval = 64;
 struct BackwardArgs {
   const void* q;
@@ -79,11 +80,8 @@ struct BackwardArgs {
   float* ws;
   int T;
 };
-inline size_t backward_ws_floats(long long BH, int T, int D) {
-  return (size_t)BH * ((size_t)((T + kBwInterval - 1) / kBwInterval + kBwInterval) * (size_t)D * D +
-                       (size_t)kBwInterval * D);
-}
-hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, hipStream_t stream);
+size_t backward_ws_floats(long long BH, int T, int D);
+hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, int split, hipStream_t stream);
 
 hipError_t launch_merge(const float* S_in, const float* Z, const float* M, float* S_start,
                         float* S_T, int BH, int G, int D, hipStream_t stream);

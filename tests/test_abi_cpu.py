@@ -221,11 +221,12 @@ def backward(lib, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, dO=FAKE, 
 
 def test_backward_workspace_query(lib):
     """A checkpoint every 64 tokens plus 64 entering states (fp32 D x D) and 64
-    fp32 D-vectors, per head."""
+    fp32 D-vectors per head, then two halves of every token's row sums (dq, dk,
+    dlog_alpha, dbeta: 3D + 1 floats)."""
     q = lib.kda_backward_workspace_bytes
     q.restype = ctypes.c_size_t
-    assert q(1, 1, 64, 64, 64) == ((1 + 64) * 64 * 64 + 64 * 64) * 4
-    assert q(2, 3, 65, 128, 128) == 6 * ((2 + 64) * 128 * 128 + 64 * 128) * 4
+    assert q(1, 1, 64, 64, 64) == ((1 + 64) * 64 * 64 + 64 * 64 + 2 * 64 * (3 * 64 + 1)) * 4
+    assert q(2, 3, 65, 128, 128) == 6 * ((2 + 64) * 128 * 128 + 64 * 128 + 2 * 65 * (3 * 128 + 1)) * 4
     assert q(1, 1, 0, 64, 64) == (64 * 64 * 64 + 64 * 64) * 4
     assert q(1, 1, 64, 64, 128) == 0 and q(1, 1, 64, 96, 96) == 0 and q(0, 1, 64, 64, 64) == 0
 

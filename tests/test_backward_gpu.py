@@ -90,6 +90,16 @@ def test_backward_many_intervals():
     assert max(err.values()) <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("split", ["1", "2"])
+@pytest.mark.parametrize("dtype,D,T", [("bf16", 128, 130), ("f32", 64, 100)])
+def test_backward_split_choice(split, dtype, D, T, monkeypatch):
+    """One workgroup per head, or two each owning half of the state's columns
+    (their row sums added by a second kernel): both match the oracle."""
+    monkeypatch.setenv("KDA_BW_SPLIT", split)
+    err = grads_case(1, 3, T, D, dtype, 98, variant="slow")
+    assert max(err.values()) <= TOL[dtype], err
+
+
 def test_backward_only_end_state_gradient():
     """dO = 0: only S_T carries the loss; dq is zero and dS0 = M^T dS_T."""
     err = grads_case(1, 2, 150, 128, "bf16", 93, variant="slow", with_dO=False)
