@@ -155,12 +155,9 @@ def bench_decomposition(pf, args):
 
     def direct():
         # the call's own choice for this part: 4 consumer waves, one workgroup per head
-        os.environ["KDA_NC"] = "4"
-        try:
+        with kda.options(nc=4):
             kda.prefill(head["q"], head["k"], head["v"], head["log_alpha"], head["beta"], None, o=o0, S_T=S1,
                         workspace=None)
-        finally:
-            del os.environ["KDA_NC"]
 
     parts = {
         "direct_part": (direct, direct_part_bytes(B, H, T0, D)),

@@ -15,9 +15,12 @@ Entry points (same names as the C-ABI):
     decode_tokens(q, k, v, log_alpha, beta, S, S_out=None, positions=False) -> (o, S_pos or None)
     segment_transfer(k, v, log_alpha, beta, G)         -> (S_zero_end, M)
     segment_merge(S_zero_end, M, S_in=None)            -> (S_start, S_T)
+    prefill_backward(q, k, v, log_alpha, beta, S0, dO, dS_T) -> dict of gradients
+    set_option(name, value), get_option(name), options(**values) (context manager)
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -29,12 +32,20 @@ LIB_PATH = os.path.join(HERE, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
 _DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+# status codes (include/libkda.h)
+(KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_UNSUPPORTED, KDA_ERR_ALIGN, KDA_ERR_WORKSPACE,
+ KDA_ERR_PRECONDITION, KDA_ERR_HIP) = range(8)
 
 _lib = None
 
 
 class KdaError(RuntimeError):
-    pass
+    """A libkda call returned a status other than KDA_OK (``status`` holds it;
+    None for errors the binding itself raises)."""
+
+    def __init__(self, msg: str, status: Optional[int] = None):
+        super().__init__(msg)
+        self.status = status
 
 
 def lib_path() -> str:
@@ -68,6 +79,10 @@ def load() -> ctypes.CDLL:
               lib.kda_decode_step, lib.kda_decode_tokens, lib.kda_segment_transfer,
               lib.kda_segment_merge, lib.kda_prefill_backward):
         f.restype = i
+    lib.kda_set_option.argtypes = [ctypes.c_char_p, ctypes.c_longlong]
+    lib.kda_set_option.restype = i
+    lib.kda_get_option.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_longlong)]
+    lib.kda_get_option.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.restype = ctypes.c_char_p
@@ -80,7 +95,32 @@ def _check(rc: int, what: str) -> None:
     if rc != 0:
         lib = load()
         raise KdaError(f"{what}: {lib.kda_status_string(rc).decode()} "
-                       f"({lib.kda_last_error().decode()})")
+                       f"({lib.kda_last_error().decode()})", rc)
+
+
+def set_option(name: str, value: Optional[int]) -> None:
+    """Set a process-wide library option (kda_set_option); None restores the default."""
+    _check(load().kda_set_option(name.encode(), -1 if value is None else int(value)), f"set_option({name})")
+
+
+def get_option(name: str) -> Optional[int]:
+    """The option's value in effect, or None for the library's default."""
+    v = ctypes.c_longlong(0)
+    _check(load().kda_get_option(name.encode(), ctypes.byref(v)), f"get_option({name})")
+    return None if v.value == -1 else int(v.value)
+
+
+@contextlib.contextmanager
+def options(**values):
+    """Set options for the duration of a with-block, then restore the old values."""
+    old = {n: get_option(n) for n in values}
+    try:
+        for n, v in values.items():
+            set_option(n, v)
+        yield
+    finally:
+        for n, v in old.items():
+            set_option(n, v)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

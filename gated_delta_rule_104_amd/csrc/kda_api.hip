@@ -10,6 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "kda_launch.hpp"
@@ -38,6 +39,52 @@ kda_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ------------------------------------------------------------------ options
+// Process-wide switches (see kda_set_option in libkda.h).  Each starts from its
+// environment variable, read once; -1 means the library's default.
+enum Opt { OPT_SPLIT, OPT_COST16, OPT_MAP_SKIP, OPT_NC, OPT_BW_SPLIT, OPT_CHECK, OPT_LOG, OPT_COUNT };
+struct OptDesc {
+  const char* name;
+  const char* env;
+};
+const OptDesc kOpts[OPT_COUNT] = {{"split", "KDA_SPLIT"},       {"transfer_cost16", "KDA_TRANSFER_COST16"},
+                                  {"map_skip", "KDA_MAP_SKIP"}, {"nc", "KDA_NC"},
+                                  {"bw_split", "KDA_BW_SPLIT"}, {"check", "KDA_CHECK"},
+                                  {"log", "KDA_LOG"}};
+std::atomic<long long> g_opt[OPT_COUNT];
+std::once_flag g_opt_once;
+
+bool opt_valid(int o, long long v) {
+  if (v == -1) return true;
+  switch (o) {
+    case OPT_SPLIT: return v == 0 || (v >= 2 && v <= 4096);
+    case OPT_COST16: return v >= 1 && v <= 64;
+    case OPT_NC: return v == 1 || v == 2 || v == 4 || v == 8;
+    case OPT_BW_SPLIT: return v == 1 || v == 2;
+    default: return v == 0 || v == 1;  // map_skip, check, log
+  }
+}
+
+void init_opts() {
+  for (int o = 0; o < OPT_COUNT; ++o) {
+    long long v = -1;
+    if (const char* env = getenv(kOpts[o].env)) {
+      char* end = nullptr;
+      const long long x = strtoll(env, &end, 10);
+      if (end != env && opt_valid(o, x)) v = x;
+      else if (o == OPT_LOG && env[0]) v = 1;  // any non-numeric KDA_LOG turns logging on
+    }
+    g_opt[o].store(v, std::memory_order_relaxed);
+  }
+}
+
+long long opt(Opt o) {
+  std::call_once(g_opt_once, init_opts);
+  return g_opt[o].load(std::memory_order_relaxed);
+}
+
+bool log_on() { return opt(OPT_LOG) == 1; }
+
 // Compute units of the current device (cached per device id).
 int cu_count() {
   static std::mutex mu;
@@ -54,26 +101,19 @@ int cu_count() {
   return cache[dev];
 }
 
-// KDA_MAP_SKIP=0 keeps the segment pass updating map columns that have become
-// exactly zero (for tests that compare both ways); any other value, or none,
-// lets it stop.
-bool map_skip_enabled() {
-  const char* env = getenv("KDA_MAP_SKIP");
-  return !(env && env[0] == '0' && env[1] == '\0');
-}
+// Option map_skip = 0 keeps the segment pass updating map columns that have
+// become exactly zero (for tests that compare both ways); by default it stops.
+bool map_skip_enabled() { return opt(OPT_MAP_SKIP) != 0; }
 
 // Consumer waves per workgroup (each owns chunk_tiles_per_wave(bf16) 16-column
 // state tiles): the largest of 4, 2, 1 (fp32: 2, 1) that divides the column
 // tiles and still gives at least one workgroup per compute unit (or 1).
-// KDA_NC overrides for tuning and tests.
+// Option nc overrides for tuning and tests, where that count is built.
 int pick_nc(long long nseq, int ncol_tiles, bool bf16_io, bool allow8 = false) {
   const int ncmax = bf16_io ? (allow8 ? 8 : 4) : 2;
   const int tw = kda::chunk_tiles_per_wave(bf16_io);
-  const char* env = getenv("KDA_NC");
-  if (env) {
-    const int v = atoi(env);
-    if ((v == 1 || v == 2 || v == 4 || v == 8) && v <= ncmax && ncol_tiles % (v * tw) == 0) return v;
-  }
+  const long long v = opt(OPT_NC);
+  if (v > 0 && v <= ncmax && ncol_tiles % (v * tw) == 0) return (int)v;
   const long long cus = cu_count();
   // 8 consumer waves (segment pass, 2*D columns in one workgroup): when one
   // workgroup per sequence fills one round of the chip but 4 waves would need
@@ -104,7 +144,7 @@ int pick_nc(long long nseq, int ncol_tiles, bool bf16_io, bool allow8 = false) {
 // per token when the gates decay as fast as in the 64K-token, 32-head workload
 // (10/16 to 15/16 measured there: 12/16 fastest, 15/16 3% slower) and about
 // 15/16 when the map never reaches zero (11/16 to 19/16 within 1% of each
-// other).  KDA_TRANSFER_COST16 overrides the ratio for tuning.
+// other).  Option transfer_cost16 overrides the ratio for tuning.
 struct PrefillPlan {
   bool split = false;
   int T0 = 0, G = 1, Tseg = 0;
@@ -119,10 +159,8 @@ PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
   if (dt != KDA_BF16 || BH <= 0 || T <= 0) return pl;
   const long long cus = cu_count();
   const int ntiles = D / 16;
-  long long G = 0;
-  const char* env = getenv("KDA_SPLIT");
-  if (env) {
-    G = atoll(env);  // 0: never; >= 2: that many segments after the first part
+  long long G = opt(OPT_SPLIT);  // 0: never; >= 2: that many segments after the first part
+  if (G >= 0) {
     if (G < 2) return pl;
   } else {
     // worth it when one pass cannot fill the chip without 4+ workgroups per head
@@ -131,8 +169,7 @@ PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
     if (G > T / 1024) G = T / 1024;
     if (G < 2) return pl;
   }
-  const char* cenv = getenv("KDA_TRANSFER_COST16");
-  long long cost16 = cenv ? atoll(cenv) : kTransferCost16;
+  long long cost16 = opt(OPT_COST16);
   if (cost16 < 1 || cost16 > 64) cost16 = kTransferCost16;
   for (; G >= 2; --G) {
     // T = T0 + (G - 1) * Tseg + last, 0 < last <= Tseg, T0 ~ (cost16/16) Tseg
@@ -154,35 +191,69 @@ PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
   return pl;
 }
 
-// A second stream per device on which the segment pass runs beside the direct
-// prefill of the first part (default priority, non-blocking, kept for the
-// process lifetime), with the events that fork it from and join it to the
-// caller's stream.  The mutex keeps one call's record/wait sequence whole.
+// A second stream on which the segment pass runs beside the direct prefill of
+// the first part (default priority, non-blocking, kept for the process
+// lifetime), with the events that fork it from and join it to the caller's
+// stream: one per (device, caller stream), so that split calls issued on
+// independent streams do not queue behind each other.  The table holds
+// kSideSlots caller streams per device; past that, a caller stream shares the
+// slot its handle hashes to (still correct, only no longer independent).  The
+// mutex keeps one call's record/wait sequence whole.
 struct SideStream {
+  hipStream_t owner = nullptr;  // the caller stream this slot serves
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   std::mutex mu;
 };
+constexpr int kSideSlots = 64;
 
-kda_status side_stream(SideStream** out) {
+kda_status side_stream(hipStream_t caller, SideStream** out) {
   static std::mutex mu;
-  static SideStream* cache[64] = {nullptr};
+  static SideStream* table[64][kSideSlots] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev < 0 || dev >= 64) return fail(KDA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  const uint64_t hsh = (reinterpret_cast<uintptr_t>(caller) >> 4) * 0x9E3779B97F4A7C15ull;
+  const int home = (int)(hsh >> 58);  // 0 .. 63
   std::lock_guard<std::mutex> lk(mu);
-  if (!cache[dev]) {
-    SideStream* ss = new SideStream();
-    if ((e = hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&ss->join, hipEventDisableTiming)) != hipSuccess) {
-      delete ss;  // (a partly created stream or event is left to process exit)
-      return hip_fail(e, "creating the side stream");
+  SideStream** row = table[dev];
+  for (int i = 0; i < kSideSlots; ++i) {
+    const int slot = (home + i) % kSideSlots;
+    if (row[slot] && row[slot]->owner == caller) {
+      *out = row[slot];
+      return KDA_OK;
     }
-    cache[dev] = ss;
+    if (!row[slot]) {
+      SideStream* ss = new SideStream();
+      ss->owner = caller;
+      if ((e = hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking)) != hipSuccess ||
+          (e = hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming)) != hipSuccess ||
+          (e = hipEventCreateWithFlags(&ss->join, hipEventDisableTiming)) != hipSuccess) {
+        delete ss;  // (a partly created stream or event is left to process exit)
+        return hip_fail(e, "creating the side stream");
+      }
+      row[slot] = ss;
+      *out = ss;
+      return KDA_OK;
+    }
   }
-  *out = cache[dev];
+  *out = row[home];  // table full: share
+  return KDA_OK;
+}
+
+// With the check option set: log_alpha (n_la values) and beta (n_beta) are
+// read on the device and KDA_ERR_PRECONDITION is returned if any is out of
+// range or not finite.  Synchronises `stream`.
+kda_status check_gates(const void* la, long long n_la, const void* beta, long long n_beta, kda_dtype dt,
+                       hipStream_t stream) {
+  if (opt(OPT_CHECK) != 1 || (n_la == 0 && n_beta == 0)) return KDA_OK;
+  unsigned int bits = 0u;
+  const hipError_t e = kda::check_gates(la, n_la, beta, n_beta, dt == KDA_BF16, stream, &bits);
+  if (e != hipSuccess) return hip_fail(e, "input check");
+  if (bits & 1u)
+    return fail(KDA_ERR_PRECONDITION, "log_alpha has values outside [-1, 0] or not finite (check mode)");
+  if (bits & 2u) return fail(KDA_ERR_PRECONDITION, "beta has values outside [0, 1] or not finite (check mode)");
   return KDA_OK;
 }
 
@@ -251,7 +322,7 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
   a.nsnap = sn.n; a.H = sn.H;
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
-  if (getenv("KDA_LOG"))
+  if (log_on())
     fprintf(stderr, "[libkda] %s BH=%lld T=%d tokens [%d,%d) Tseg=%d G=%d D=%d nc=%d vsplit=%d grid=%lld\n",
             what, BH, T, t0, Tend, Tseg, G, D, nc, a.vsplit, nwg);
   const hipError_t e = kda::launch_chunk(a, bf, D, true, nc, (int)nwg, stream);
@@ -267,8 +338,6 @@ kda_status check_prefill_args(const void* q, const void* k, const void* v, const
   kda_status st;
   if ((st = check_dtype(dtype)) != KDA_OK) return st;
   if ((st = check_dims(dk, dv)) != KDA_OK) return st;
-  if (dtype == KDA_F32 && dk != 64)
-    return fail(KDA_ERR_UNSUPPORTED, "fp32 prefill supports dk = dv = 64 only (got %d)", dk);
   const long long BH = (long long)B * H;
   if (BH * T * dk > kMaxElems || BH > (1LL << 30)) return fail(KDA_ERR_SHAPE, "problem too large");
   if ((st = check_seq_bytes(T, dk, dtype)) != KDA_OK) return st;
@@ -291,6 +360,28 @@ extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
+kda_status kda_set_option(const char* name, long long value) {
+  if (!name) return fail(KDA_ERR_NULL, "option name is NULL");
+  for (int o = 0; o < OPT_COUNT; ++o) {
+    if (strcmp(name, kOpts[o].name) != 0) continue;
+    if (!opt_valid(o, value)) return fail(KDA_ERR_SHAPE, "option %s does not take the value %lld", name, value);
+    opt((Opt)o);  // environment defaults first, so they do not overwrite this later
+    g_opt[o].store(value, std::memory_order_relaxed);
+    return ok();
+  }
+  return fail(KDA_ERR_SHAPE, "unknown option '%s'", name);
+}
+
+kda_status kda_get_option(const char* name, long long* value) {
+  if (!name || !value) return fail(KDA_ERR_NULL, "option name or value pointer is NULL");
+  for (int o = 0; o < OPT_COUNT; ++o) {
+    if (strcmp(name, kOpts[o].name) != 0) continue;
+    *value = opt((Opt)o);
+    return ok();
+  }
+  return fail(KDA_ERR_SHAPE, "unknown option '%s'", name);
+}
+
 const char* kda_last_error(void) { return g_err; }
 
 const char* kda_status_string(kda_status s) {
@@ -300,6 +391,8 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_SHAPE: return "invalid shape";
     case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
     case KDA_ERR_ALIGN: return "misaligned pointer";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_PRECONDITION: return "input precondition violated";
     case KDA_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";
@@ -346,6 +439,7 @@ kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, c
     sn.n = T / snap_interval;
     sn.H = H;
   }
+  if (T > 0 && (st = check_gates(log_alpha, BH * T * dk, beta, BH * T, dtype, stream)) != KDA_OK) return st;
   const bool bf = dtype == KDA_BF16;
   const int D = dk;
   const PrefillPlan pl = plan_prefill(BH, T, D, dtype);
@@ -357,7 +451,7 @@ kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, c
     float* S1 = M + G1 * nS;                    // end state of the direct part
     float* Sst = S1 + nS;                       // [G] start states of the segments
     SideStream* ss = nullptr;
-    if ((st = side_stream(&ss)) != KDA_OK) return st;
+    if ((st = side_stream(stream, &ss)) != KDA_OK) return st;
     kda::ChunkArgs t;
     t.q = nullptr; t.k = k; t.v = v; t.la = log_alpha; t.beta = beta;
     t.S0 = nullptr; t.o = nullptr; t.S_out = Z; t.M_out = M;
@@ -368,7 +462,7 @@ kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, c
     // the direct part: one workgroup per head (all of a head's column tiles) when
     // the segment pass leaves room for it, else the usual choice
     const int nc0 = BH * (G1 * t.vsplit + 1) <= cu_count() ? D / 16 / kda::chunk_tiles_per_wave(bf) : 0;
-    if (getenv("KDA_LOG"))
+    if (log_on())
       fprintf(stderr, "[libkda] prefill split BH=%lld T=%d D=%d: direct [0,%d), %d x %d-token segments; "
               "transfer nc=%d vsplit=%d\n", BH, T, D, T0, G, Ts, nc2, t.vsplit);
     hipError_t e;
@@ -423,6 +517,7 @@ kda_status kda_chunk_prefill_segments(const void* q, const void* k, const void* 
   if (BH == 0) return ok();
   KDA_OPTIONAL(S_start, "S_start");
   if (T == 0) return fail(KDA_ERR_SHAPE, "T must be >= 1 for a segmented prefill");
+  if ((st = check_gates(log_alpha, BH * T * dk, beta, BH * T, dtype, stream)) != KDA_OK) return st;
   st = launch_segment_prefill(q, k, v, log_alpha, beta, S_start, o, S_T, BH, T, 0, T, Tseg, dk,
                               dtype == KDA_BF16, stream, "kda_chunk_prefill_segments");
   return st == KDA_OK ? ok() : st;
@@ -445,6 +540,7 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
   if (!beta) return fail(KDA_ERR_NULL, "beta is NULL");  // [N,H] rows: any element alignment
   KDA_REQUIRE(S, "S");
   KDA_REQUIRE(o, "o");
+  if ((st = check_gates(log_alpha, NH * dk, beta, NH, dtype, stream)) != KDA_OK) return st;
   hipError_t e = kda::launch_decode(q, k, v, log_alpha, beta, S, S, o, nullptr, (int)NH, H, 1, dk,
                                     dtype == KDA_BF16, stream);
   if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
@@ -471,6 +567,7 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const 
     KDA_REQUIRE(log_alpha, "log_alpha");
     if (!beta) return fail(KDA_ERR_NULL, "beta is NULL");  // [N,H,ntok] rows: any element alignment
     KDA_REQUIRE(o, "o");
+    if ((st = check_gates(log_alpha, NH * ntok * dk, beta, NH * ntok, dtype, stream)) != KDA_OK) return st;
   }
   hipError_t e = kda::launch_decode(q, k, v, log_alpha, beta, S_in, S_out, o, ntok > 0 ? S_pos : nullptr,
                                     (int)NH, H, ntok, dk, dtype == KDA_BF16, stream);
@@ -487,8 +584,6 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
   kda_status st;
   if ((st = check_dtype(dtype)) != KDA_OK) return st;
   if ((st = check_dims(dk, dv)) != KDA_OK) return st;
-  if (dtype == KDA_F32 && dk != 64)
-    return fail(KDA_ERR_UNSUPPORTED, "fp32 segment transfer supports dk = dv = 64 only (got %d)", dk);
   const long long BH = (long long)B * H;
   const long long nseq = BH * G;
   if (nseq * Tseg * dk > kMaxElems || nseq > (1LL << 30)) return fail(KDA_ERR_SHAPE, "problem too large");
@@ -500,6 +595,7 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
   KDA_REQUIRE(beta, "beta");
   KDA_REQUIRE(S_zero_end, "S_zero_end");
   KDA_REQUIRE(M, "M");
+  if ((st = check_gates(log_alpha, nseq * Tseg * dk, beta, nseq * Tseg, dtype, stream)) != KDA_OK) return st;
   const int ntiles = (dv + dk) / 16;
   const int nc = pick_nc(nseq, ntiles, dtype == KDA_BF16, dk == 128);
   kda::ChunkArgs a;
@@ -510,7 +606,7 @@ kda_status kda_segment_transfer(const void* k, const void* v, const void* log_al
   a.map_skip = map_skip_enabled();
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
-  if (getenv("KDA_LOG"))
+  if (log_on())
     fprintf(stderr, "[libkda] transfer BH=%lld G=%d Tseg=%d D=%d nc=%d vsplit=%d grid=%lld\n", BH, G,
             Tseg, dk, nc, a.vsplit, nwg);
   hipError_t e = kda::launch_chunk(a, dtype == KDA_BF16, dk, false, nc, (int)nwg, stream);
@@ -573,21 +669,20 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
     if (!dbeta) return fail(KDA_ERR_NULL, "dbeta is NULL");
   }
   const size_t need = kda::backward_ws_floats(BH, T, dk) * sizeof(float);
-  KDA_REQUIRE(workspace, "workspace");
+  if (!workspace) return fail(KDA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(workspace)) return fail(KDA_ERR_ALIGN, "workspace is not 16-byte aligned");
   if (workspace_bytes < need)
-    return fail(KDA_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (T > 0 && (st = check_gates(log_alpha, BH * T * dk, beta, BH * T, dtype, stream)) != KDA_OK) return st;
   kda::BackwardArgs a;
   a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta; a.S0 = S0; a.dO = dO; a.dS_T = dS_T;
   a.dq = dq; a.dk = dk_; a.dv = dv_; a.dla = dlog_alpha; a.dbeta = dbeta; a.dS0 = dS0;
   a.ws = static_cast<float*>(workspace);
   a.T = T;
   // two workgroups per head (each with half of the state's columns) when that
-  // still fits the chip in one round; KDA_BW_SPLIT=1 or 2 forces the choice
+  // still fits the chip in one round; option bw_split forces the choice
   int split = 2 * BH <= cu_count() ? 2 : 1;
-  if (const char* env = getenv("KDA_BW_SPLIT")) {
-    const int v = atoi(env);
-    if (v == 1 || v == 2) split = v;
-  }
+  if (const long long v = opt(OPT_BW_SPLIT); v == 1 || v == 2) split = (int)v;
   hipError_t e = kda::launch_backward(a, (int)BH, dk, dtype == KDA_BF16, split, stream);
   if (e != hipSuccess) return hip_fail(e, "kda_prefill_backward launch");
   return ok();

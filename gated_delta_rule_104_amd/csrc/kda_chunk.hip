@@ -594,6 +594,10 @@ struct ChunkKernel {
   // With three waves per SIMD (segment pass with 8 consumer waves) registers are
   // tighter, and operand fragments are fetched in smaller batches.
   static constexpr bool TIGHT = C::NW > 8;
+  // One producer prefetch set (one chunk ahead) instead of two: the
+  // three-waves-per-SIMD variant, and fp32 at D = 128, whose 8-byte-per-element
+  // rows make two sets too large for 256 registers.
+  static constexpr bool ONESET = TIGHT || (!C::BF && D > 64);
   static constexpr int C1B = 2;                    // row tiles per batch in c1
   static constexpr int C3B = TIGHT ? 2 : D / 32;   // state row tiles per batch in c3
 
@@ -905,13 +909,13 @@ struct ChunkKernel {
 
   // Producer inputs are prefetched two chunks ahead (two register sets, the
   // loop unrolled by two with the odd step peeled off, so that the loop's back
-  // edge always follows both steps), except in the three-waves-per-SIMD
-  // variant, which keeps one set and prefetches one chunk ahead.
+  // edge always follows both steps), except in the ONESET variants, which keep
+  // one set and prefetch one chunk ahead.
   __device__ __forceinline__ void producer_loop() {
     init_offsets();
     init_p1_offsets();
     const int n = nch + C::LAG;
-    if constexpr (TIGHT) {
+    if constexpr (ONESET) {
       ProdRaw<T> r;
       load_raw(r, 0);
       for (int it = 0; it < n; ++it) producer_step<1>(r, it);
@@ -1096,6 +1100,8 @@ hipError_t launch_chunk(const ChunkArgs& a, bool bf16_io, int D, bool prefill, i
     if (D == 64) return prefill ? launch_nc<bf16, 64, true>(a, nc, nwg, stream)
                                 : launch_nc<bf16, 64, false>(a, nc, nwg, stream);
   } else {
+    if (D == 128) return prefill ? launch_nc<float, 128, true>(a, nc, nwg, stream)
+                                 : launch_nc<float, 128, false>(a, nc, nwg, stream);
     if (D == 64) return prefill ? launch_nc<float, 64, true>(a, nc, nwg, stream)
                                 : launch_nc<float, 64, false>(a, nc, nwg, stream);
   }

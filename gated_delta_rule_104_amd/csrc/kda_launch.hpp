@@ -86,4 +86,12 @@ hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, i
 hipError_t launch_merge(const float* S_in, const float* Z, const float* M, float* S_start,
                         float* S_T, int BH, int G, int D, hipStream_t stream);
 
+// Reads n_la gate values and n_beta betas (bf16 or fp32) on `stream`, waits for
+// the result, and sets *bits_out to bit 0 if a log_alpha value lies outside
+// [-1, 0] or is not finite and bit 1 if a beta lies outside [0, 1] or is not
+// finite.  Synchronises `stream`.  n_la is a multiple of 8 and la 16-byte
+// aligned; beta may have any element alignment.
+hipError_t check_gates(const void* la, long long n_la, const void* beta, long long n_beta, bool bf16_io,
+                       hipStream_t stream, unsigned int* bits_out);
+
 }  // namespace kda

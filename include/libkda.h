@@ -19,26 +19,28 @@
  *  - `dtype` gives the element type of q, k, v, log_alpha, beta and o.  States
  *    (S0, S_T, S, S_zero_end, M, S_in, S_start) are always fp32.
  *  - The gate is passed in log space: log_alpha = log(alpha), one value per key
- *    channel, and must lie in [-1, 0].  The pages describe the gate as
- *    lower-bounded so that long sequences neither overflow nor underflow
- *    (blog.csdn.net article, section 一.1); the kernels rely on the bound
- *    (|cumulative log-decay| <= 64 inside a 64-token chunk) and do not check it.
- *  - Supported head sizes: dk == dv == 64 or 128.  fp32 prefill and segment
- *    transfer support dk == dv == 64 only; decode supports both in both dtypes.
+ *    channel, and must lie in [-1, 0]; beta must lie in [0, 1].  The pages
+ *    describe the gate as lower-bounded so that long sequences neither overflow
+ *    nor underflow (blog.csdn.net article, section 一.1); the kernels rely on
+ *    the bound (|cumulative log-decay| <= 64 inside a 64-token chunk).  By
+ *    default nothing checks it: a gate below the bound can give inf or NaN
+ *    outputs with KDA_OK.  With the "check" option set (below), every call that
+ *    takes log_alpha and beta first reduces them on the device, waits for the
+ *    answer (it synchronises `stream`), and returns KDA_ERR_PRECONDITION,
+ *    launching nothing else, when a value is out of range or not finite.
+ *  - Supported head sizes: dk == dv == 64 or 128, for both dtypes.
  *  - Errors: arguments are validated on the host before anything is launched;
  *    on error nothing is written and a status != KDA_OK is returned, with a
  *    description in kda_last_error() (thread-local).  Work is enqueued
  *    asynchronously on `stream`; a launch failure returns KDA_ERR_HIP.
  *  - Calls never abort the process.  The only global state is per device and
- *    created on first use: the compute-unit count, and for the sequence-split
- *    prefill a second stream with two events (kept for the process lifetime).
- *  - Environment overrides, for tuning and tests only: KDA_SPLIT (segments of
- *    the sequence-split prefill; 0 = never split), KDA_TRANSFER_COST16 (the
- *    first part's length ratio, in 16ths), KDA_MAP_SKIP=0 (the segment pass
- *    keeps updating transfer-map columns that have become exactly zero; for
- *    finite inputs the results are the same bit for bit), KDA_NC (consumer
- *    waves per workgroup), KDA_LOG (print each launch's shape to stderr).
- *    Every choice they make gives the same result up to rounding.
+ *    created on first use: the compute-unit count, the check flag, and for the
+ *    sequence-split prefill a second stream (with two events) per caller
+ *    stream, kept for the process lifetime; plus the process-wide options.
+ *  - Options (kda_set_option): process-wide tuning and debugging switches,
+ *    read from the environment once, at the first call that needs them, and
+ *    changed at run time with kda_set_option.  Every choice they make gives the
+ *    same result up to rounding.  See kda_set_option for the list.
  */
 #ifndef LIBKDA_H
 #define LIBKDA_H
@@ -50,7 +52,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 7
+#define KDA_ABI_VERSION 8
 
 typedef enum {
   KDA_OK = 0,
@@ -58,7 +60,10 @@ typedef enum {
   KDA_ERR_SHAPE = 2,        /* negative size, dk != dv, or size overflow      */
   KDA_ERR_UNSUPPORTED = 3,  /* head size / dtype combination not built        */
   KDA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned               */
-  KDA_ERR_HIP = 5           /* the HIP runtime reported an error              */
+  KDA_ERR_WORKSPACE = 5,    /* a required workspace is missing or too small   */
+  KDA_ERR_PRECONDITION = 6, /* check mode: log_alpha outside [-1, 0] or beta
+                               outside [0, 1] (or not finite)                 */
+  KDA_ERR_HIP = 7           /* the HIP runtime reported an error              */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -89,10 +94,12 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * workspace (fp32 states, 3G - 1 per head); with a smaller or NULL workspace
  * the call runs the single-pass path instead.  The workspace is only used by
  * work enqueued by this call; calls on one stream may share it.
- * The side-by-side part runs on a second stream of the library's own (created
- * once per device, default priority), forked from and joined back to `stream`
- * with events, so all of the call's work is ordered after earlier work on
- * `stream` and before later work on it.
+ * The side-by-side part runs on a second stream of the library's own, one per
+ * (device, caller stream) pair (created at the first split call on that stream,
+ * default priority), forked from and joined back to `stream` with events, so
+ * all of the call's work is ordered after earlier work on `stream` and before
+ * later work on it, and split calls on different caller streams do not wait for
+ * each other.
  */
 size_t kda_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtype dtype);
 
@@ -235,8 +242,8 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
  * and the vectors u = (Diag(alpha) S)^T k of one 64-token interval, per head;
  * its contents on return are undefined.  No
  * output may alias an input or the workspace.  Errors: KDA_ERR_NULL for a
- * missing workspace or required pointer, KDA_ERR_SHAPE for a workspace below
- * the required size.
+ * missing required pointer, KDA_ERR_WORKSPACE for a missing workspace or one
+ * below the required size.
  */
 size_t kda_backward_workspace_bytes(int B, int H, int T, int dk, int dv);
 kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -244,6 +251,32 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
                                 float* dq, float* dk_, float* dv_, float* dlog_alpha, float* dbeta,
                                 float* dS0, int B, int H, int T, int dk, int dv, kda_dtype dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Process-wide options.  Each starts from the environment variable of the same
+ * name in capitals with a KDA_ prefix (KDA_SPLIT, ...), read once, at the first
+ * call that needs the options; kda_set_option changes one for every later call
+ * (thread-safe; calls already enqueued are not affected).  value -1 restores the
+ * library's default.  Names:
+ *   "split"            segments after the first part of the sequence-split
+ *                      prefill (0 = never split, >= 2 = that many; default:
+ *                      chosen from the shape and the compute-unit count)
+ *   "transfer_cost16"  that path's first-part length ratio, in 16ths (1..64)
+ *   "map_skip"         0: the segment pass keeps updating transfer-map columns
+ *                      that have become exactly zero (same results bit for bit
+ *                      for finite inputs); default 1
+ *   "nc"               consumer waves per workgroup of the chunk kernels
+ *                      (1, 2, 4, 8 where built; default: chosen from the shape)
+ *   "bw_split"         workgroups per head of the backward's chunk kernels (1 or
+ *                      2; default: chosen from the shape)
+ *   "check"            1: validate log_alpha and beta on the device before every
+ *                      call that reads them (see the conventions above); default 0
+ *   "log"              1: print every launch's shape to stderr; default 0
+ * kda_set_option returns KDA_ERR_SHAPE for an unknown name or a value the option
+ * does not take; kda_get_option writes the value in effect (-1: default).
+ */
+kda_status kda_set_option(const char* name, long long value);
+kda_status kda_get_option(const char* name, long long* value);
 
 const char* kda_status_string(kda_status status);
 const char* kda_last_error(void);

@@ -19,3 +19,20 @@ def oracle_lib():
     from oracle import build_oracle
     build_oracle.build()
     return oracle.load()
+
+
+@pytest.fixture
+def kda_opts():
+    """Set libkda options for one test: kda_opts(name, value) calls
+    kda.set_option; every option the test touched is restored afterwards."""
+    import gated_delta_rule_104_amd as kda
+    saved = {}
+
+    def setopt(name, value):
+        if name not in saved:
+            saved[name] = kda.get_option(name)
+        kda.set_option(name, value)
+
+    yield setopt
+    for name, value in saved.items():
+        kda.set_option(name, value)

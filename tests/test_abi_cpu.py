@@ -12,7 +12,7 @@ HEADER = os.path.join(ROOT, "include", "libkda.h")
 
 import gated_delta_rule_104_amd as kda  # noqa: E402
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_HIP = range(6)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_PRECONDITION, ERR_HIP = range(8)
 F32, BF16 = 0, 1
 FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
 
@@ -43,9 +43,11 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 7
-    for st in range(6):
-        assert lib.kda_status_string(st)
+    assert lib.kda_abi_version() == 8
+    names = [lib.kda_status_string(st) for st in range(8)]
+    assert all(names) and len(set(names)) == 8
+    assert b"workspace" in names[ERR_WORKSPACE] and b"precondition" in names[ERR_PRECONDITION]
+    assert b"HIP" in names[ERR_HIP]
     assert lib.kda_status_string(99) == b"unknown status"
 
 
@@ -61,7 +63,7 @@ def prefill(lib, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, o=FAKE, ST
 def test_prefill_validation(lib):
     assert prefill(lib, dk=64, dv=128) == ERR_SHAPE
     assert prefill(lib, dk=96, dv=96) == ERR_UNSUPPORTED
-    assert prefill(lib, dk=128, dv=128, dt=F32) == ERR_UNSUPPORTED
+    assert prefill(lib, dk=96, dv=96, dt=F32) == ERR_UNSUPPORTED
     assert prefill(lib, dt=7) == ERR_UNSUPPORTED
     assert prefill(lib, T=-1) == ERR_SHAPE
     assert prefill(lib, B=-2) == ERR_SHAPE
@@ -112,10 +114,10 @@ def test_prefill_plan(lib):
     assert lib.kda_prefill_plan(1, 1, 64, 64, 64, BF16, None, ctypes.byref(G), ctypes.byref(Ts)) == ERR_NULL
 
 
-def test_prefill_plan_cost_override(lib, monkeypatch):
-    """KDA_TRANSFER_COST16 (the segment pass's cost per token relative to the
-    prefill, in 16ths) moves the first part's length; the cut still covers T
-    exactly, and values outside 1..64 fall back to the built-in ratio."""
+def test_prefill_plan_cost_override(lib, kda_opts):
+    """Option transfer_cost16 (the segment pass's cost per token relative to
+    the prefill, in 16ths) moves the first part's length; the cut still covers T
+    exactly, and values outside 1..64 are refused."""
     T0, G, Ts = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
 
     def plan(T=65536):
@@ -123,17 +125,19 @@ def test_prefill_plan_cost_override(lib, monkeypatch):
                                     ctypes.byref(Ts)) == OK
         return T0.value, G.value, Ts.value
 
-    monkeypatch.delenv("KDA_TRANSFER_COST16", raising=False)
+    kda_opts("transfer_cost16", None)
     default = plan()
     first = {}
-    for c in ("11", "15", "19"):
-        monkeypatch.setenv("KDA_TRANSFER_COST16", c)
+    for c in (11, 15, 19):
+        kda_opts("transfer_cost16", c)
         t0, g, ts = plan()
         assert t0 % 64 == 0 and ts % 64 == 0 and t0 + (g - 1) * ts < 65536 <= t0 + g * ts
         first[c] = t0 / ts
-    assert first["11"] < first["15"] < first["19"]
-    for bad in ("0", "65", "-3", "x"):
-        monkeypatch.setenv("KDA_TRANSFER_COST16", bad)
+    assert first[11] < first[15] < first[19]
+    kda_opts("transfer_cost16", 12)
+    assert plan() == default
+    for bad in (0, 65, -3):
+        assert lib.kda_set_option(b"transfer_cost16", bad) == ERR_SHAPE
         assert plan() == default
 
 
@@ -166,7 +170,7 @@ def test_prefill_segments_validation(lib):
     assert f(*args(ST=None)) == ERR_NULL
     assert f(*args(S=FAKE + 4)) == ERR_ALIGN
     assert f(*args(dk=64)) == ERR_SHAPE
-    assert f(*args(dt=F32)) == ERR_UNSUPPORTED
+    assert f(*args(dt=5)) == ERR_UNSUPPORTED
 
 
 def test_decode_validation(lib):
@@ -196,7 +200,8 @@ def test_segment_validation(lib):
     t = lib.kda_segment_transfer
     assert t(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1, 2, 4, 0, 128, 128, BF16, None) == ERR_SHAPE
     assert t(*P(FAKE, FAKE, FAKE, FAKE, None, FAKE), 1, 2, 4, 64, 128, 128, BF16, None) == ERR_NULL
-    assert t(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1, 2, 4, 64, 128, 128, F32, None) == ERR_UNSUPPORTED
+    assert t(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1, 2, 4, 64, 96, 96, F32, None) == ERR_UNSUPPORTED
+    assert t(*P(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE), 1, 2, 4, 64, 128, 128, 3, None) == ERR_UNSUPPORTED
     m = lib.kda_segment_merge
     assert m(*P(None, FAKE, FAKE, None, None), 1, 2, 4, 128, 128, None) == ERR_NULL
     assert m(*P(None, FAKE, FAKE, FAKE + 4, FAKE), 1, 2, 4, 128, 128, None) == ERR_ALIGN
@@ -238,14 +243,51 @@ def test_backward_validation(lib):
     assert backward(lib, q=None) == ERR_NULL
     assert backward(lib, dS0=None) == ERR_NULL
     assert backward(lib, db=None) == ERR_NULL
-    assert backward(lib, ws=None) == ERR_NULL
-    assert backward(lib, ws_bytes=1024) == ERR_SHAPE
+    assert backward(lib, ws=None) == ERR_WORKSPACE
+    assert backward(lib, ws_bytes=1024) == ERR_WORKSPACE
     assert b"needed" in lib.kda_last_error()
+    assert backward(lib, ws=FAKE + 8) == ERR_ALIGN
     assert backward(lib, dq=FAKE + 4) == ERR_ALIGN
     assert backward(lib, dO=FAKE + 8) == ERR_ALIGN
     assert backward(lib, B=1 << 20, H=1 << 12, T=1 << 10) == ERR_SHAPE
     # no tokens: the per-token arrays are not needed, the workspace still is
     assert backward(lib, T=0, q=None, k=None, v=None, la=None, beta=None, dO=None, dq=None, dk=None,
-                    dv=None, dla=None, db=None, ws=None) == ERR_NULL
+                    dv=None, dla=None, db=None, ws=None) == ERR_WORKSPACE
     # no heads: nothing to do
     assert backward(lib, B=0, ws=None, ws_bytes=0) == OK
+
+
+def test_options(lib, kda_opts):
+    """Options are validated by name and value, read back as set, and -1 restores
+    the library default; calls that only validate are unaffected."""
+    v = ctypes.c_longlong(0)
+    get = lambda n: (lib.kda_get_option(n, ctypes.byref(v)), v.value)[1]
+    for name, good, bad in ((b"split", (0, 2, 64), (1, -2)), (b"transfer_cost16", (1, 64), (0, 65)),
+                            (b"map_skip", (0, 1), (2,)), (b"nc", (1, 2, 4, 8), (3, 16)),
+                            (b"bw_split", (1, 2), (3,)), (b"check", (0, 1), (2,)), (b"log", (0, 1), (5,))):
+        kda_opts(name.decode(), None)
+        assert get(name) == -1
+        for x in good:
+            assert lib.kda_set_option(name, x) == OK and get(name) == x
+        for x in bad:
+            assert lib.kda_set_option(name, x) == ERR_SHAPE and get(name) == good[-1]
+        assert lib.kda_set_option(name, -1) == OK and get(name) == -1
+    assert lib.kda_set_option(b"no_such_option", 1) == ERR_SHAPE
+    assert b"unknown option" in lib.kda_last_error()
+    assert lib.kda_get_option(b"no_such_option", ctypes.byref(v)) == ERR_SHAPE
+    assert lib.kda_set_option(None, 1) == ERR_NULL
+    assert lib.kda_get_option(b"nc", None) == ERR_NULL
+
+
+def test_options_from_environment():
+    """Each option starts from its KDA_* environment variable, read once; values
+    an option does not take are ignored (the default applies)."""
+    import subprocess
+    import sys
+    code = ("import gated_delta_rule_104_amd as k; "
+            "print(k.get_option('nc'), k.get_option('split'), k.get_option('check'), k.get_option('log'), "
+            "k.get_option('map_skip'))")
+    env = dict(os.environ, KDA_NC="2", KDA_SPLIT="1", KDA_CHECK="1", KDA_LOG="yes", KDA_MAP_SKIP="0")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                         check=True, timeout=120).stdout.split()
+    assert out == ["2", "None", "1", "1", "0"], out

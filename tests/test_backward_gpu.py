@@ -92,10 +92,10 @@ def test_backward_many_intervals():
 
 @pytest.mark.parametrize("split", ["1", "2"])
 @pytest.mark.parametrize("dtype,D,T", [("bf16", 128, 130), ("f32", 64, 100)])
-def test_backward_split_choice(split, dtype, D, T, monkeypatch):
+def test_backward_split_choice(split, dtype, D, T, kda_opts):
     """One workgroup per head, or two each owning half of the state's columns
     (their row sums added by a second kernel): both match the oracle."""
-    monkeypatch.setenv("KDA_BW_SPLIT", split)
+    kda_opts("bw_split", int(split))
     err = grads_case(1, 3, T, D, dtype, 98, variant="slow")
     assert max(err.values()) <= TOL[dtype], err
 

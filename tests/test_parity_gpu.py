@@ -58,13 +58,14 @@ def test_prefill_tails_bf16(T, D):
 
 
 @pytest.mark.parametrize("T", [1, 17, 64, 130])
-def test_prefill_tails_f32(T):
-    eo, es = run_prefill_case(2, 2, T, 64, "f32", 200 + T, s0_std=0.1)
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_tails_f32(T, D):
+    eo, es = run_prefill_case(2, 2, T, D, "f32", 200 + T, s0_std=0.1)
     assert eo <= TOL["f32"] and es <= TOL["f32"]
 
 
 @pytest.mark.parametrize("variant", ["slow", "alpha_one", "alpha_min", "beta_zero", "beta_one"])
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("f32", 128)])
 def test_prefill_variants(variant, dtype, D):
     """Gate and beta extremes; 'slow' keeps S0 alive for thousands of tokens."""
     T = 1024 if variant == "slow" else 320
@@ -102,26 +103,26 @@ def test_prefill_deterministic():
 
 
 @pytest.mark.parametrize("nc", ["1", "2", "4"])
-def test_prefill_column_split_invariant(nc, monkeypatch):
+def test_prefill_column_split_invariant(nc, kda_opts):
     """The number of state columns per workgroup changes the launch, not the result."""
     d = ki.gen_prefill(1, 2, 200, 128, 128, "bf16", seed=12, s0_std=0.1)
     g = to_dev(d)
-    monkeypatch.setenv("KDA_NC", nc)
+    kda_opts("nc", int(nc))
     o, S_T = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
-    monkeypatch.delenv("KDA_NC")
+    kda_opts("nc", None)
     o1, S1 = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
     torch.cuda.synchronize()
     assert torch.equal(o, o1) and torch.equal(S_T, S1)
 
 
 @pytest.mark.parametrize("nc", ["1", "2", "4", "8"])
-def test_segment_pass_column_split_invariant(nc, monkeypatch):
+def test_segment_pass_column_split_invariant(nc, kda_opts):
     """Every consumer-wave count of the segment pass gives bit-identical states
     and maps (the columns are independent once the chunk operands are built)."""
     d = ki.gen_prefill(1, 3, 4 * 200, 128, 128, "bf16", seed=62, variant="slow")
     g = to_dev(d)
     Z, M = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], 4)
-    monkeypatch.setenv("KDA_NC", nc)
+    kda_opts("nc", int(nc))
     Z1, M1 = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], 4)
     torch.cuda.synchronize()
     assert torch.equal(Z, Z1) and torch.equal(M, M1)
@@ -129,14 +130,14 @@ def test_segment_pass_column_split_invariant(nc, monkeypatch):
 
 @pytest.mark.parametrize("dtype,D,variant", [("bf16", 128, "none"), ("bf16", 128, "slow"),
                                              ("bf16", 64, "none"), ("f32", 64, "none")])
-def test_segment_pass_map_skip_bit_identical(dtype, D, variant, monkeypatch):
+def test_segment_pass_map_skip_bit_identical(dtype, D, variant, kda_opts):
     """Map columns that have reached exact zero are no longer updated: the
     states and maps equal those of a pass that keeps updating them."""
     print(f"[case] map skip {dtype} D={D} {variant}", flush=True)
     d = ki.gen_prefill(1, 3, 3 * 320, D, D, dtype, seed=64, variant=variant)
     g = to_dev(d)
     Z, M = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], 3)
-    monkeypatch.setenv("KDA_MAP_SKIP", "0")
+    kda_opts("map_skip", 0)
     Z1, M1 = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], 3)
     torch.cuda.synchronize()
     assert torch.equal(Z, Z1) and torch.equal(M, M1)
@@ -158,7 +159,7 @@ def partial_decay_inputs(H, T, seed):
     return d
 
 
-def test_segment_pass_map_partial_zero(monkeypatch):
+def test_segment_pass_map_partial_zero(kda_opts):
     """Half of the map's column blocks reach zero and stop, the other half keep
     going; both match the oracle and a pass without the stop, and the split
     prefill built on them reproduces the recurrence."""
@@ -167,9 +168,9 @@ def test_segment_pass_map_partial_zero(monkeypatch):
     d = partial_decay_inputs(H, G * Tseg, 65)
     g = to_dev(d)
     Z, M = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], G)
-    monkeypatch.setenv("KDA_MAP_SKIP", "0")
+    kda_opts("map_skip", 0)
     Z1, M1 = kda.segment_transfer(g["k"], g["v"], g["log_alpha"], g["beta"], G)
-    monkeypatch.delenv("KDA_MAP_SKIP")
+    kda_opts("map_skip", None)
     torch.cuda.synchronize()
     assert torch.equal(Z, Z1) and torch.equal(M, M1)
     assert torch.count_nonzero(M[..., 64:]) == 0
@@ -178,9 +179,9 @@ def test_segment_pass_map_partial_zero(monkeypatch):
     assert oracle.max_rel_l2(Z.cpu(), Zr, 3, floor=1e-3) <= TOL["bf16"]
     assert oracle.max_rel_l2(M.cpu(), Mr, 3, floor=1e-3) <= TOL["bf16"]
 
-    monkeypatch.setenv("KDA_SPLIT", "3")
+    kda_opts("split", 3)
     o, S_T = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
-    monkeypatch.setenv("KDA_MAP_SKIP", "0")
+    kda_opts("map_skip", 0)
     o1, S1 = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
     torch.cuda.synchronize()
     assert torch.equal(o, o1) and torch.equal(S_T, S1)
@@ -263,9 +264,26 @@ def test_segments_bf16(variant):
     assert max(err.values()) <= TOL["bf16"], err
 
 
-def test_segments_f32():
-    err = run_segment_case(1, 2, 3, 100, 64, "f32", 51, "slow")
+@pytest.mark.parametrize("D", [64, 128])
+def test_segments_f32(D):
+    err = run_segment_case(1, 2, 3, 100, D, "f32", 51, "slow")
     assert max(err.values()) <= TOL["f32"], err
+
+
+@pytest.mark.parametrize("nc", [1, 2])
+def test_prefill_f32_d128_column_split_invariant(nc, kda_opts):
+    """fp32 at dk = dv = 128: one or two consumer waves per workgroup give the
+    same result bit for bit, and it matches the oracle."""
+    d = ki.gen_prefill(1, 2, 300, 128, 128, "f32", seed=13, s0_std=0.1, variant="slow")
+    g = to_dev(d)
+    kda_opts("nc", nc)
+    o, S_T = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
+    kda_opts("nc", None)
+    o1, S1 = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o1) and torch.equal(S_T, S1)
+    o_ref, S_ref = oracle.prefill(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], d["S0"])
+    assert oracle.max_rel_l2(o.cpu(), o_ref) <= TOL["f32"] and oracle.max_rel_l2(S_T.cpu(), S_ref) <= TOL["f32"]
 
 
 def test_segments_then_prefill_reproduce_whole_sequence():
@@ -461,10 +479,10 @@ def test_full_decode_n256_h32():
 
 @pytest.mark.parametrize("P,T,D,variant", [(2, 300, 128, "slow"), (3, 1000, 128, "slow"),
                                             (4, 1000, 64, "none"), (5, 2000, 128, "alpha_one")])
-def test_prefill_sequence_split(P, T, D, variant, monkeypatch):
+def test_prefill_sequence_split(P, T, D, variant, kda_opts):
     """The segment-transfer / merge / segment-prefill path gives the recurrence's
     outputs and end state (ragged last segment, start state carried through)."""
-    monkeypatch.setenv("KDA_SPLIT", str(P))
+    kda_opts("split", P)
     B, H = 1, 3
     print(f"[case] split prefill P={P} T={T} D={D} {variant}", flush=True)
     d = ki.gen_prefill(B, H, T, D, D, "bf16", seed=400 + P, s0_std=0.1, variant=variant)
@@ -479,11 +497,11 @@ def test_prefill_sequence_split(P, T, D, variant, monkeypatch):
 
 
 @pytest.mark.parametrize("cost16", ["11", "19"])
-def test_prefill_sequence_split_other_cut(cost16, monkeypatch):
-    """A different first-part length (KDA_TRANSFER_COST16) moves every segment
+def test_prefill_sequence_split_other_cut(cost16, kda_opts):
+    """A different first-part length (option transfer_cost16) moves every segment
     boundary; the outputs and end state still follow the recurrence."""
-    monkeypatch.setenv("KDA_SPLIT", "4")
-    monkeypatch.setenv("KDA_TRANSFER_COST16", cost16)
+    kda_opts("split", 4)
+    kda_opts("transfer_cost16", int(cost16))
     B, H, T, D = 1, 2, 3000, 128
     print(f"[case] split prefill, cost16={cost16}, plan {kda.prefill_plan(B, H, T, D, D, torch.bfloat16)}",
           flush=True)
@@ -497,8 +515,8 @@ def test_prefill_sequence_split_other_cut(cost16, monkeypatch):
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
-def test_prefill_split_without_workspace_falls_back(monkeypatch):
-    monkeypatch.setenv("KDA_SPLIT", "4")
+def test_prefill_split_without_workspace_falls_back(kda_opts):
+    kda_opts("split", 4)
     d = ki.gen_prefill(1, 2, 500, 128, 128, "bf16", seed=410, s0_std=0.1, variant="slow")
     g = to_dev(d)
     o, S_T = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], workspace=None)
@@ -510,11 +528,11 @@ def test_prefill_split_without_workspace_falls_back(monkeypatch):
 
 # ----------------------------------------------------------------- state snapshots
 
-def run_snap_case(B, H, T, D, dtype, interval, seed, variant="slow", split=None, monkeypatch=None):
+def run_snap_case(B, H, T, D, dtype, interval, seed, variant="slow", split=None, kda_opts=None):
     print(f"[case] snapshots B={B} H={H} T={T} D={D} {dtype} every {interval} split={split} {variant}",
           flush=True)
     if split is not None:
-        monkeypatch.setenv("KDA_SPLIT", str(split))
+        kda_opts("split", split)
     d = ki.gen_prefill(B, H, T, D, D, dtype, seed=seed, s0_std=0.1, variant=variant)
     g = to_dev(d)
     o, S_T, snaps = kda.prefill_snap(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], interval, g["S0"])
@@ -543,11 +561,11 @@ def test_prefill_snapshots(B, H, T, D, dtype, interval):
 
 
 @pytest.mark.parametrize("P,T,interval", [(3, 1000, 128), (4, 2148, 512), (2, 700, 64)])
-def test_prefill_snapshots_sequence_split(P, T, interval, monkeypatch):
+def test_prefill_snapshots_sequence_split(P, T, interval, kda_opts):
     """On the sequence-split path each segment's workgroups write the snapshots
     that fall inside the segment; boundaries on segment ends come from the
     segment that ends there."""
-    es = run_snap_case(1, 3, T, 128, "bf16", interval, seed=520 + P, split=P, monkeypatch=monkeypatch)
+    es = run_snap_case(1, 3, T, 128, "bf16", interval, seed=520 + P, split=P, kda_opts=kda_opts)
     assert es <= TOL["bf16"]
 
 
@@ -572,11 +590,11 @@ def test_full_h32_t64k_snapshots():
     assert es <= TOL["bf16"]
 
 
-def test_prefill_split_on_user_stream(monkeypatch):
+def test_prefill_split_on_user_stream(kda_opts):
     """The split path forks part of its work to the library's side stream and
     joins it back: calls on a user stream, issued back to back with inputs that
     change in between, give the results of calls on the default stream."""
-    monkeypatch.setenv("KDA_SPLIT", "6")
+    kda_opts("split", 6)
     B, H, T, D = 1, 4, 3000, 128
     d = ki.gen_prefill(B, H, T, D, D, "bf16", seed=430, s0_std=0.1, variant="slow")
     g = to_dev(d)
@@ -674,18 +692,18 @@ def test_full_decode_tokens_n256_h32():
     assert worst <= TOL["bf16"]
 
 
-def test_prefill_snapshots_split_batched(monkeypatch):
+def test_prefill_snapshots_split_batched(kda_opts):
     """Snapshots on the sequence-split path with several sequences: each
     sequence's snapshots land at [b, j, h] whichever segment writes them."""
-    es = run_snap_case(2, 3, 1500, 128, "bf16", 256, seed=540, split=3, monkeypatch=monkeypatch)
+    es = run_snap_case(2, 3, 1500, 128, "bf16", 256, seed=540, split=3, kda_opts=kda_opts)
     assert es <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("B,H,T,P", [(2, 3, 1300, 3), (3, 2, 2100, 4)])
-def test_prefill_sequence_split_batched(B, H, T, P, monkeypatch):
+def test_prefill_sequence_split_batched(B, H, T, P, kda_opts):
     """The split path with several sequences and heads (start states per
     sequence, ragged last segment)."""
-    monkeypatch.setenv("KDA_SPLIT", str(P))
+    kda_opts("split", P)
     print(f"[case] split prefill B={B} H={H} T={T} P={P}", flush=True)
     d = ki.gen_prefill(B, H, T, 128, 128, "bf16", seed=450 + P, s0_std=0.1, variant="slow")
     g = to_dev(d)
