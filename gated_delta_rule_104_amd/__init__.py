@@ -8,6 +8,7 @@ library is missing, loading fails with an error that says how to build it.
 
 Entry points (same names as the C-ABI):
     prefill(q, k, v, log_alpha, beta, S0=None)        -> (o, S_T)
+    prefill_noalloc(q, k, v, log_alpha, beta, S0=None)  -> (o, S_T)  (no workspace, allocates nothing)
     prefill_snap(q, k, v, log_alpha, beta, snap_interval, S0=None) -> (o, S_T, S_snap)
     prefill_plan(B, H, T, dk, dv, dtype)               -> (T0, G, Tseg)
     prefill_segments(q, k, v, log_alpha, beta, S_start, Tseg) -> (o, S_T)
@@ -64,6 +65,7 @@ def load() -> ctypes.CDLL:
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.kda_chunk_prefill.argtypes = [vp] * 8 + [i] * 6 + [vp, ctypes.c_size_t, vp]
     lib.kda_chunk_prefill_snap.argtypes = [vp] * 9 + [i] * 7 + [vp, ctypes.c_size_t, vp]
+    lib.kda_chunk_prefill_noalloc.argtypes = [vp] * 8 + [i] * 6 + [vp]
     lib.kda_prefill_workspace_bytes.argtypes = [i] * 6
     lib.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_prefill_plan.argtypes = [i] * 6 + [ctypes.POINTER(i)] * 3
@@ -75,7 +77,7 @@ def load() -> ctypes.CDLL:
     lib.kda_backward_workspace_bytes.argtypes = [i] * 5
     lib.kda_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_prefill_backward.argtypes = [vp] * 14 + [i] * 6 + [vp, ctypes.c_size_t, vp]
-    for f in (lib.kda_chunk_prefill, lib.kda_chunk_prefill_snap, lib.kda_prefill_plan, lib.kda_chunk_prefill_segments,
+    for f in (lib.kda_chunk_prefill, lib.kda_chunk_prefill_snap, lib.kda_chunk_prefill_noalloc, lib.kda_prefill_plan, lib.kda_chunk_prefill_segments,
               lib.kda_decode_step, lib.kda_decode_tokens, lib.kda_segment_transfer,
               lib.kda_segment_merge, lib.kda_prefill_backward):
         f.restype = i
@@ -179,6 +181,32 @@ def prefill(q, k, v, log_alpha, beta, S0=None, o=None, S_T=None,
                                   _ptr(o), _ptr(S_T), B, H, T, dk, dv, _DT[dt], _ptr(workspace),
                                   ws_bytes, _stream())
     _check(rc, "kda_chunk_prefill")
+    return o, S_T
+
+
+def prefill_noalloc(q, k, v, log_alpha, beta, S0=None, o=None, S_T=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """prefill() through kda_chunk_prefill_noalloc: the library's own scratch
+    array replaces the workspace (calls on one device must not overlap).  o and
+    S_T are allocated here when not given; pass them to allocate nothing."""
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    dt = k.dtype
+    if dt not in _DT:
+        raise KdaError(f"unsupported dtype {dt}")
+    for name, t, shp in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                         ("log_alpha", log_alpha, (B, H, T, dk)), ("beta", beta, (B, H, T))):
+        _io(t, name, dt, shp)
+    if S0 is not None:
+        _io(S0, "S0", torch.float32, (B, H, dk, dv))
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=k.device)
+    if S_T is None:
+        S_T = torch.empty(B, H, dk, dv, dtype=torch.float32, device=k.device)
+    _io(o, "o", dt, (B, H, T, dv))
+    _io(S_T, "S_T", torch.float32, (B, H, dk, dv))
+    rc = load().kda_chunk_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                                          _ptr(o), _ptr(S_T), B, H, T, dk, dv, _DT[dt], _stream())
+    _check(rc, "kda_chunk_prefill_noalloc")
     return o, S_T
 
 

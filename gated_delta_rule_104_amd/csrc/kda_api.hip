@@ -417,11 +417,47 @@ kda_status kda_prefill_plan(int B, int H, int T, int dk, int dv, kda_dtype dtype
   return ok();
 }
 
-kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, const void* log_alpha,
-                                  const void* beta, const float* S0, void* o, float* S_T,
-                                  float* S_snap, int snap_interval, int B, int H, int T, int dk,
-                                  int dv, kda_dtype dtype, void* workspace, size_t workspace_bytes,
-                                  hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Scratch of the no-allocation prefill entry point: the sequence-split path's
+// states (Z, M, the first part's end state, the segments' start states) when
+// the caller cannot pass a workspace.  Every default plan on a 256-CU device
+// fits (at most 63.5 MiB, for 127 heads of d = 128); each device the library
+// runs on holds its own copy until the process ends.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+
+// The scratch array's device address on the current device, looked up once per
+// device (with that device current) with hipGetSymbolAddress.  The array's name
+// in host code is only a host-side stand-in and must never be passed to a
+// kernel or a copy.
+kda_status scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* cache[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(KDA_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cache[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    cache[dev] = p;
+  }
+  *out = cache[dev];
+  return KDA_OK;
+}
+
+// The prefill with or without snapshots.  noalloc: the split path's workspace is
+// the library's scratch array (workspace / workspace_bytes are ignored), and a
+// plan that needs more than the array holds is refused.
+kda_status prefill_impl(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                        const float* S0, void* o, float* S_T, float* S_snap, int snap_interval, int B, int H,
+                        int T, int dk, int dv, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                        bool noalloc, hipStream_t stream) {
   kda_status st = check_prefill_args(q, k, v, log_alpha, beta, o, S_T, B, H, T, dk, dv, dtype);
   if (st != KDA_OK) return st;
   if (snap_interval < 0 || snap_interval % 64)
@@ -443,6 +479,18 @@ kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, c
   const bool bf = dtype == KDA_BF16;
   const int D = dk;
   const PrefillPlan pl = plan_prefill(BH, T, D, dtype);
+  if (noalloc) {
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (pl.split) {
+      if (pl.ws > kScratchBytes)
+        return fail(KDA_ERR_WORKSPACE,
+                    "the sequence-split plan needs %zu bytes of scratch; the no-allocation entry point "
+                    "holds %zu", pl.ws, kScratchBytes);
+      if ((st = scratch_ptr(&workspace)) != KDA_OK) return st;
+      workspace_bytes = kScratchBytes;
+    }
+  }
   if (pl.split && workspace && workspace_bytes >= pl.ws) {
     const int G = pl.G, G1 = G - 1, T0 = pl.T0, Ts = pl.Tseg;
     const size_t nS = (size_t)BH * D * D;
@@ -496,6 +544,26 @@ kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, c
   st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, o, S_T, BH, T, 0, T, T > 0 ? T : 1, D, bf,
                               stream, "kda_chunk_prefill", sn);
   return st == KDA_OK ? ok() : st;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, const void* log_alpha,
+                                  const void* beta, const float* S0, void* o, float* S_T,
+                                  float* S_snap, int snap_interval, int B, int H, int T, int dk,
+                                  int dv, kda_dtype dtype, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  return prefill_impl(q, k, v, log_alpha, beta, S0, o, S_T, S_snap, snap_interval, B, H, T, dk, dv, dtype,
+                      workspace, workspace_bytes, false, stream);
+}
+
+kda_status kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                                     const void* beta, const float* S0, void* o, float* S_T, int B, int H,
+                                     int T, int dk, int dv, kda_dtype dtype, hipStream_t stream) {
+  return prefill_impl(q, k, v, log_alpha, beta, S0, o, S_T, nullptr, 0, B, H, T, dk, dv, dtype, nullptr, 0,
+                      true, stream);
 }
 
 kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const void* log_alpha,

@@ -109,6 +109,25 @@ kda_status kda_chunk_prefill(const void* q, const void* k, const void* v, const 
                              size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_chunk_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * Same arguments and results as kda_chunk_prefill without the workspace: the
+ * sequence-split path takes its workspace from a scratch array the library
+ * holds on each device (64 MiB, a file-scope device array that the device keeps
+ * until the process ends), and the call itself allocates nothing.  The split
+ * plan of every shape fits it on a 256-CU device with the default options; a
+ * plan that needs more (e.g. a large "split" option) returns KDA_ERR_WORKSPACE
+ * and launches nothing.  Nothing in the scratch array has to start at any value
+ * (every byte the call reads there it has written first), but all calls on one
+ * device share it: calls that can overlap on one device (on different streams,
+ * or from different threads) race and must not be issued; calls on one stream
+ * are ordered and safe.
+ */
+kda_status kda_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const void* log_alpha,
+                                     const void* beta, const float* S0, void* o, float* S_T, int B, int H,
+                                     int T, int dk, int dv, kda_dtype dtype, hipStream_t stream);
+
+/*
  * kda_chunk_prefill that also keeps state snapshots for prefix caching.  The
  * KDA state of a request has a fixed size and is stored only at a sparse subset
  * of the 512-token block boundaries that prefix matching uses ("Kimi K3
