@@ -29,6 +29,8 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -91,8 +93,14 @@ def prefill_flops(B, H, T, D, triangle=False):
     return B * H * nchunks * per_chunk
 
 
-def time_launches(fn, n):
-    """Mean and list of per-launch durations (ms) from events on the current stream."""
+MIN_TIMED = 20  # every figure is the median of at least this many event-timed launches
+
+
+def time_launches(fn, n, exact=False):
+    """Median and list of per-launch durations (ms) from events on the current
+    stream, each launch between its own pair of events: n launches if exact (the
+    headline's K steps), else at least MIN_TIMED."""
+    n = n if exact else max(n, MIN_TIMED)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for a, b in evs:
         a.record()
@@ -100,7 +108,7 @@ def time_launches(fn, n):
         b.record()
     torch.cuda.synchronize()
     ts = [a.elapsed_time(b) for a, b in evs]
-    return sum(ts) / len(ts), ts
+    return statistics.median(ts), ts
 
 
 def segment_pass_bytes(B, H, T, D, G):
@@ -199,10 +207,11 @@ def bench_prefill(args, dev):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    mean_ms, per = time_launches(step, args.steps)
+    med_ms, per = time_launches(step, args.steps, exact=True)
     t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    return dict(B=B, H=H, T=T, D=D, mean_ms=mean_ms, wall_ms=wall_ms, per=per, g=g, ws_bytes=nws)
+    wall_ms = (t1 - t0) * 1e3 / len(per)
+    return dict(B=B, H=H, T=T, D=D, median_ms=med_ms, mean_ms=sum(per) / len(per), wall_ms=wall_ms,
+                per=per, g=g, ws_bytes=nws)
 
 
 def bench_prefill_batched(args, dev):
@@ -296,7 +305,7 @@ def bench_backward(args, dev):
 
     call()
     torch.cuda.synchronize()
-    ms, _ = time_launches(call, 3)
+    ms, _ = time_launches(call, MIN_TIMED)
     nbytes = backward_bytes(B, H, T, D)
     fl = backward_flops(B, H, T, D)
     del g, dO, ws
@@ -423,9 +432,9 @@ def bench_kcp(args, dev):
 
     transfer(); merge(); prefill()
     torch.cuda.synchronize()
-    t_ms, _ = time_launches(transfer, 3)
-    m_ms, _ = time_launches(merge, 3)
-    p_ms, _ = time_launches(prefill, 3)
+    t_ms, _ = time_launches(transfer, MIN_TIMED)
+    m_ms, _ = time_launches(merge, MIN_TIMED)
+    p_ms, _ = time_launches(prefill, MIN_TIMED)
     nbytes = B * H * T * (2 * (2 * D + D) + 2) + 2 * G * B * H * D * D * 4
     pbytes = segment_prefill_bytes(B, H, T, D, G)
     del g, o
@@ -462,6 +471,18 @@ def bench_calibration(dev):
             "spec_bf16_tflops": PEAK_BF16_TFLOPS, "spec_hbm_GBs": PEAK_HBM_GBS}
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo where present)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(pf, budget_s):
     """fp64 oracle on a bounded sample of the same prefill inputs: all heads and
     tokens if that fits in about `budget_s` seconds, else the first `nh` heads and
@@ -489,6 +510,7 @@ def cpu_baseline(pf, budget_s):
     what = "the whole workload" if (nh, tt) == (H, T) else \
         f"{nh} of {H} heads x first {tt} tokens of the same inputs"
     return {"value": token_heads_per_s / H, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{what} ({el:.1f} s, fp64, outputs and end states); tokens/s over all {H} heads"}
 
 
@@ -532,7 +554,7 @@ def main():
 
     pf = bench_prefill(args, dev)
     B, H, T, D = pf["B"], pf["H"], pf["T"], pf["D"]
-    ms = pf["mean_ms"]
+    ms = pf["median_ms"]
     tok_s = B * T / (ms * 1e-3)
     nbytes = prefill_bytes(B, H, T, D)
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -548,10 +570,16 @@ def main():
         dom = max(names, key=lambda n: dec[n]["ms"])
         r = dec[dom]
         traffic = TRAFFIC.get(dom) if kernel_sources_sha() == TRAFFIC["sources_sha"] else None
+        counters_valid = kernel_sources_sha() == TRAFFIC["sources_sha"]
+        path_counter = sum(TRAFFIC[n] for n in names) if counters_valid else None
         roofline = {"bound": "hbm", "achieved": r["GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": r["GBs"] / PEAK_HBM_GBS, "traffic": traffic, "kernel": kern[dom],
                     "kernel_ms": r["ms"], "algorithmic_bytes": r["algorithmic_bytes"],
-                    "path_GBs": gbs, "path_frac": gbs / PEAK_HBM_GBS}
+                    "path_GBs": gbs, "path_frac": gbs / PEAK_HBM_GBS,
+                    # whole call: the four kernels' counter bytes against the single-pass
+                    # algorithmic bytes (the split path re-reads k, v, log_alpha, beta)
+                    "path_traffic": {"counter_bytes": path_counter, "algorithmic_bytes": nbytes,
+                                     "ratio": path_counter / nbytes if path_counter else None}}
     else:
         dec = None
         roofline = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
