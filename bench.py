@@ -298,7 +298,7 @@ def bench_backward(args, dev):
     gen = torch.Generator(device=dev).manual_seed(6)
     dO = torch.randn(B, H, T, D, generator=gen, device=dev).to(torch.bfloat16)
     dST = torch.randn(B, H, D, D, generator=gen, device=dev)
-    ws = torch.empty(kda.backward_workspace_bytes(B, H, T, D, D), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kda.backward_workspace_bytes(B, H, T, D, D, torch.bfloat16), dtype=torch.uint8, device=dev)
 
     def call():
         kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], dO, dST, workspace=ws)

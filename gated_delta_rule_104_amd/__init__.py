@@ -74,7 +74,7 @@ def load() -> ctypes.CDLL:
     lib.kda_decode_tokens.argtypes = [vp] * 9 + [i] * 6 + [vp]
     lib.kda_segment_transfer.argtypes = [vp] * 6 + [i] * 7 + [vp]
     lib.kda_segment_merge.argtypes = [vp] * 5 + [i] * 5 + [vp]
-    lib.kda_backward_workspace_bytes.argtypes = [i] * 5
+    lib.kda_backward_workspace_bytes.argtypes = [i] * 6
     lib.kda_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_prefill_backward.argtypes = [vp] * 14 + [i] * 6 + [vp, ctypes.c_size_t, vp]
     for f in (lib.kda_chunk_prefill, lib.kda_chunk_prefill_snap, lib.kda_chunk_prefill_noalloc, lib.kda_prefill_plan, lib.kda_chunk_prefill_segments,
@@ -388,9 +388,11 @@ def segment_merge(S_zero_end, M, S_in=None, want_start: bool = True, S_start=Non
     return S_start, S_T
 
 
-def backward_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int) -> int:
-    """Workspace kda_prefill_backward needs (0 for an unsupported shape)."""
-    return int(load().kda_backward_workspace_bytes(B, H, T, dk, dv))
+def backward_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace kda_prefill_backward needs for inputs of this dtype (0 for an unsupported shape)."""
+    if dtype not in _DT:
+        raise KdaError(f"unsupported dtype {dtype}")
+    return int(load().kda_backward_workspace_bytes(B, H, T, dk, dv, _DT[dtype]))
 
 
 def prefill_backward(q, k, v, log_alpha, beta, S0=None, dO=None, dS_T=None, workspace=None):
@@ -416,7 +418,7 @@ def prefill_backward(q, k, v, log_alpha, beta, S0=None, dO=None, dS_T=None, work
     out = dict(dq=torch.empty(B, H, T, dk, **f32), dk=torch.empty(B, H, T, dk, **f32),
                dv=torch.empty(B, H, T, dv, **f32), dlog_alpha=torch.empty(B, H, T, dk, **f32),
                dbeta=torch.empty(B, H, T, **f32), dS0=torch.empty(B, H, dk, dv, **f32))
-    need = backward_workspace_bytes(B, H, T, dk, dv)
+    need = backward_workspace_bytes(B, H, T, dk, dv, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     if not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:

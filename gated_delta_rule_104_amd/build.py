@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.hip", "kda_chunk.hip", "kda_decode.hip", "kda_merge.hip", "kda_backward.hip",
-           "kda_check.hip"]
+           "kda_check.hip", "kda_bwgrad.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

@@ -546,6 +546,81 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
   return st == KDA_OK ? ok() : st;
 }
 
+// Workspace of the chunked backward (bf16 inputs), fp32: the forward's state
+// after every whole chunk ([B, T / 64, H, D, D], the layout of the prefill's
+// snapshots), dU = Diag(Gam) dS' of every chunk ([BH, nch, D, D]), and the
+// forward pass's end state, which is not needed ([BH, D, D]).
+size_t chunk_bw_ws_floats(long long BH, int T, int D) {
+  const long long nch = (T + 63) / 64;
+  return (size_t)(BH * (T / 64) + BH * nch + BH) * D * D;
+}
+
+// Gradients of the prefill in the chunked form (bf16 inputs; arguments already
+// validated):
+//  1. beside each other: the forward pass from S0 with a state checkpoint after
+//     every chunk (its outputs are not written), on the side stream; and the
+//     reverse chain from dS_T over the chunks, last to first, which writes
+//     dU = Diag(Gam) dS' of every chunk and dS0 (it needs no forward state);
+//  2. the per-chunk gradients, one workgroup per (head, chunk).
+kda_status chunk_backward(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                          const float* S0, const void* dO, const float* dS_T, float* dq, float* dk_, float* dv_,
+                          float* dlog_alpha, float* dbeta, float* dS0, int B, int H, int T, int D, float* ws,
+                          hipStream_t stream) {
+  const long long BH = (long long)B * H;
+  const long long nch = (T + 63) / 64;
+  const size_t nS = (size_t)D * D;
+  float* ckpt = ws;                          // [B, T / 64, H, D, D]
+  float* dU = ckpt + (size_t)BH * (T / 64) * nS;  // [BH, nch, D, D]
+  float* ST = dU + (size_t)BH * nch * nS;    // [BH, D, D], discarded
+  const int nt = D / 16;
+  kda::ChunkArgs r;
+  r.q = q; r.k = k; r.v = dO; r.la = log_alpha; r.beta = beta;
+  r.S0 = dS_T; r.o = nullptr; r.S_out = dS0; r.M_out = nullptr;
+  r.BH = (int)BH; r.G = 1; r.Tseg = T > 0 ? T : 1; r.Ttot = T; r.t0 = 0; r.Tend = T;
+  r.dU_out = dU;
+  // The forward pass and the reverse chain run side by side: their column
+  // split is chosen so that both together fill the chip once.
+  const int ncb = pick_nc(2 * BH, nt, true);
+  r.vsplit = nt / (ncb * kda::chunk_tiles_per_wave(true));
+  if (BH * r.vsplit > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (log_on())
+    fprintf(stderr, "[libkda] backward BH=%lld T=%d D=%d: reverse chain nc=%d vsplit=%d, %lld x %lld chunk gradients\n",
+            BH, T, D, ncb, r.vsplit, BH, nch);
+  hipError_t e;
+  if (T == 0) {  // dS0 = dS_T
+    if ((e = kda::launch_chunk_bwd(r, D, ncb, (int)(BH * r.vsplit), stream)) != hipSuccess)
+      return hip_fail(e, "kda_prefill_backward reverse chain");
+    return ok();
+  }
+  SideStream* ss = nullptr;
+  kda_status st;
+  if ((st = side_stream(stream, &ss)) != KDA_OK) return st;
+  {
+    std::lock_guard<std::mutex> lk(ss->mu);
+    if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess || (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
+      return hip_fail(e, "kda_prefill_backward fork");
+    Snap sn;
+    sn.p = ckpt;
+    sn.chunks = 1;
+    sn.n = T / 64;
+    sn.H = H;
+    st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, nullptr, ST, BH, T, 0, T, T, D, true, ss->s,
+                                "kda_prefill_backward forward checkpoints", sn, ncb);
+    if (st == KDA_OK && (e = kda::launch_chunk_bwd(r, D, ncb, (int)(BH * r.vsplit), stream)) != hipSuccess)
+      st = hip_fail(e, "kda_prefill_backward reverse chain");
+    // join even if a launch above failed, so the side stream's work is waited for
+    if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess || (e = hipStreamWaitEvent(stream, ss->join, 0)) != hipSuccess)
+      return hip_fail(e, "kda_prefill_backward join");
+    if (st != KDA_OK) return st;
+  }
+  kda::BwGradArgs g;
+  g.q = q; g.k = k; g.v = v; g.la = log_alpha; g.beta = beta; g.dO = dO; g.S0 = S0;
+  g.ckpt = ckpt; g.nckpt = T / 64; g.H = H; g.dU = dU;
+  g.dq = dq; g.dk = dk_; g.dv = dv_; g.dla = dlog_alpha; g.dbeta = dbeta; g.T = T;
+  if ((e = kda::launch_bwgrad(g, (int)BH, D, stream)) != hipSuccess) return hip_fail(e, "kda_prefill_backward gradients");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -703,9 +778,11 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
   return ok();
 }
 
-size_t kda_backward_workspace_bytes(int B, int H, int T, int dk, int dv) {
+size_t kda_backward_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtype dtype) {
   if (B <= 0 || H <= 0 || T < 0 || dk != dv || (dk != 64 && dk != 128)) return 0;
-  return kda::backward_ws_floats((long long)B * H, T, dk) * sizeof(float);
+  if (dtype == KDA_BF16) return chunk_bw_ws_floats((long long)B * H, T, dk) * sizeof(float);
+  if (dtype == KDA_F32) return kda::backward_ws_floats((long long)B * H, T, dk) * sizeof(float);
+  return 0;
 }
 
 kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const void* log_alpha,
@@ -736,12 +813,15 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
     KDA_REQUIRE(dlog_alpha, "dlog_alpha");
     if (!dbeta) return fail(KDA_ERR_NULL, "dbeta is NULL");
   }
-  const size_t need = kda::backward_ws_floats(BH, T, dk) * sizeof(float);
+  const bool bf = dtype == KDA_BF16;
+  const size_t need = (bf ? chunk_bw_ws_floats(BH, T, dk) : kda::backward_ws_floats(BH, T, dk)) * sizeof(float);
   if (!workspace) return fail(KDA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (!aligned(workspace)) return fail(KDA_ERR_ALIGN, "workspace is not 16-byte aligned");
   if (workspace_bytes < need)
     return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if (T > 0 && (st = check_gates(log_alpha, BH * T * dk, beta, BH * T, dtype, stream)) != KDA_OK) return st;
+  if (bf) return chunk_backward(q, k, v, log_alpha, beta, S0, dO, dS_T, dq, dk_, dv_, dlog_alpha, dbeta, dS0, B, H,
+                                T, dk, static_cast<float*>(workspace), stream);
   kda::BackwardArgs a;
   a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta; a.S0 = S0; a.dO = dO; a.dS_T = dS_T;
   a.dq = dq; a.dk = dk_; a.dv = dv_; a.dla = dlog_alpha; a.dbeta = dbeta; a.dS0 = dS0;

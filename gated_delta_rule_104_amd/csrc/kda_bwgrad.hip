@@ -1,0 +1,860 @@
+// Per-chunk gradients of the prefill: the chunk-parallel part of the backward.
+//
+// For a loss L with dL/do = dO and dL/dS_T = dS_T, the gradients of a 64-token
+// chunk follow from its start state S, the gradient dU = Diag(Gam) dS' with
+// respect to its end state (scaled by the chunk's decay; the reverse chain
+// computes it), and the chunk's own inputs.  With the chunked form of the
+// recurrence (blog.csdn.net article on the Kimi K3 report, section 一.1, for the
+// gated delta rule; "Kimi K3 开源日来了", section "FlashKDA", for the chunking;
+// training is what the K3 report also speeds up with FlashKDA)
+//   g = cumsum(log alpha),  Qh = q e^g,  Kh = k e^g,  Kb = k e^-g,  Gam = e^(g_C)
+//   L = diag(b) strict_lower(Kh Kb^T),  P = lower(Qh Kb^T),  T = (I + L)^-1
+//   W = V - Kh S,  X = diag(b) W,  Delta = T X
+//   O = Qh S + P Delta,  S' = Diag(Gam) (S + Kb^T Delta)
+// the chain rule gives, per chunk:
+//   dDelta = Kb dU + P^T dO,  Xbar = T^T dDelta
+//   dP = lower(dO Delta^T),  Lbar = strict_lower(-Xbar Delta^T),  Abar = diag(b) Lbar
+//   dQh = dO S^T + dP Kb
+//   dKh = -diag(b) Xbar S^T + Abar Kb
+//   dKb = Delta dU^T + Abar^T Kh + dP^T Qh
+//   dv = diag(b) Xbar,  dbeta_r = sum_j Xbar_rj W_rj + sum_{s<r} Lbar_rs (Kh Kb^T)_rs
+//   dq = dQh e^g,  dk = dKh e^g + dKb e^-g
+//   dlog_alpha_r = sum_{t >= r} dg_t + rowsum(dU . S) + sum_{s < r} k_s e^-g_s (Delta dU^T)_s
+//     with dg = q dq + k (dKh e^g - (dKb - Delta dU^T) e^-g)
+// The last line is the gradient with respect to g (g = cumsum(log alpha) within
+// the chunk) summed over later tokens, with Gam's part (every token of the
+// chunk: rowsum(dU . (S + Kb^T Delta))) taken apart: its Kb^T Delta piece and
+// the Delta dU^T piece of dKb cancel for s >= r, so that sum_{s < r} is formed
+// directly, which in bf16 products avoids a cancellation between large terms.
+//
+// One workgroup per (head, chunk), one wave per 16 columns of the head
+// dimension (8 waves at d = 128, two per SIMD).  Phases, each ended by a
+// workgroup barrier:
+//   1. elementwise: the cumulative gate (DPP row scan) and the bf16 operand
+//      tiles Qh, Kh, Kb, dO, with Gam and beta, into LDS;
+//   2. score tiles: T_ii, -L (forward solve), T_ii^T, -L^T (back solve), P^T;
+//   3. per wave, 16-column tiles of the value dimension: W, Delta, dDelta,
+//      Xbar, dv and the first part of dbeta; Delta and Xbar go to LDS;
+//   4. the 64 x 64 gradients dP, dP^T, Abar, Abar^T (as MFMA A fragments) and
+//      the second part of dbeta;
+//   5. per wave, 16-column tiles of the key dimension: dQh, dKh, dKb (the
+//      products with the 64 x 64 gradients on fp32 Kb, Kh, Qh split into two
+//      bf16 parts);
+//   6. the gate's chain rule, written out per (token, channel).
+// Operand conventions are those of the chunk kernel: bf16 MFMA 16x16x32 tiles,
+// time-major LDS tiles with 32-wide k blocks in the kpos order, transposing LDS
+// reads for operands that contract over tokens, and 16x16 tiles that feed a
+// product as A operands stored in fragment order.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+namespace {
+
+constexpr int GCH = 64;  // chunk length
+constexpr float G_LOG2E = 1.4426950408889634f;
+
+template <int D>
+struct GradCfg {
+  static constexpr int NW = D / 16;            // waves: one 16-column tile of the value (key) dimension each
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int NCT = D / (16 * NW);    // 16-column tiles per wave
+  static constexpr int NKD = D / 32;           // 32-deep k blocks over channels
+  static constexpr int NKT = GCH / 32;         // 32-deep k blocks over the chunk's tokens
+  static constexpr int NP = D / 32;            // waves that build the elementwise tiles
+  static constexpr int R_TD = D * 2;           // bf16 row of a [64][D] tile
+  static constexpr int TD_TILE = 16 * R_TD + 16;
+  static constexpr int TD_SZ = 4 * TD_TILE;
+  static constexpr int FR16 = 64 * 4 * 2;      // a 16x16 tile as 16-deep bf16 A fragments
+  static constexpr int FR64 = 4 * NKT * 64 * 16;  // a 64x64 matrix as 32-deep A fragments
+  static constexpr uint32_t KH = 0;
+  static constexpr uint32_t QH = KH + TD_SZ;
+  static constexpr uint32_t KB = QH + TD_SZ;
+  static constexpr uint32_t DO = KB + TD_SZ;
+  static constexpr uint32_t DL = DO + TD_SZ;   // Delta
+  static constexpr uint32_t XB = DL + TD_SZ;   // Xbar
+  static constexpr uint32_t TI = XB + TD_SZ;   // T_ii as A fragments (forward solve)
+  static constexpr uint32_t LO = TI + 4 * FR16;  // -L_ij, i > j
+  static constexpr uint32_t TT = LO + 6 * FR16;  // T_ii^T (back solve)
+  static constexpr uint32_t LT = TT + 4 * FR16;  // -L_ij^T, i > j
+  static constexpr uint32_t PT = LT + 6 * FR16;  // P^T, 32-deep over tokens
+  static constexpr uint32_t DP = PT + FR64;      // dP
+  static constexpr uint32_t DPT = DP + FR64;     // dP^T
+  static constexpr uint32_t AB = DPT + FR64;     // Abar
+  static constexpr uint32_t ABT = AB + FR64;     // Abar^T
+  static constexpr uint32_t GM = ABT + FR64;     // Gam [D] fp32
+  static constexpr uint32_t BETA = GM + 4 * D;   // beta [64] fp32
+  static constexpr uint32_t DBP = BETA + 4 * GCH;  // dbeta partials [2 NW][64] fp32
+  static constexpr uint32_t LDS = DBP + 4 * GCH * 2 * NW;
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(LDS % 16 == 0, "LDS alignment");
+};
+
+template <int D>
+struct GradKernel {
+  using C = GradCfg<D>;
+  static constexpr int NCT = C::NCT, NKD = C::NKD, NKT = C::NKT;
+  char* smem;
+  BwGradArgs a;
+  int wave, l, g4, s0;
+  int nrows;  // valid tokens of this chunk
+  rsrc_t rq, rk, rv, rla, rbeta, rdo, rdq, rdk, rdv, rdla, rdb, rS, rU;
+  uint32_t oTD[NKD];   // A fragments of [64][D] tiles, row tile 0
+  int tr_f, tr_q;      // transposing reads: the lane's row and channel quad
+
+  __device__ __forceinline__ static uint32_t td(int row, int byte) {
+    return (uint32_t)(row >> 4) * C::TD_TILE + swz<C::R_TD>(row & 15, byte);
+  }
+  // A fragment of row tile t, k block m (channels) of a [64][D] tile
+  __device__ __forceinline__ bf16x8 ar(uint32_t tile, int t, int m) const {
+    return lds_ld<bf16x8>(smem, tile + oTD[m] + t * C::TD_TILE);
+  }
+  // Fragment of channels 16ct .. 16ct+15 over tokens 32m .. 32m+31 of a [64][D]
+  // tile, read with transposing LDS reads: lane i of lane group g receives the
+  // tokens of its k positions of channel 16ct + i (the A fragment of the tile's
+  // transpose, equally the B fragment of the tile over tokens).
+  __device__ __forceinline__ bf16x8 tr_frag(uint32_t tile, int ct, int m) const {
+    // (computed, not tabled: ct depends on the wave, and a table indexed at run
+    // time would live in scratch memory)
+    const uint32_t base = tile + swz<C::R_TD>(tr_f, 2 * kpos(32 * (ct >> 1) + 4 * tr_q)) + 8u * (uint32_t)(ct & 1);
+    const bf16x4 lo = lds_tr16(smem, base + (uint32_t)(2 * m) * C::TD_TILE);
+    const bf16x4 hi = lds_tr16(smem, base + (uint32_t)(2 * m + 1) * C::TD_TILE);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // 32-deep A fragment slot of a 64x64 matrix stored at `base`: row tile t, k block m
+  __device__ __forceinline__ bf16x8 fr64(uint32_t base, int t, int m) const {
+    return lds_ld<bf16x8>(smem, base + ((t * NKT + m) * 64 + fresh_lane(l)) * 16);
+  }
+  __device__ __forceinline__ void put16(uint32_t off, const f32x4& v) { lds_st<bf16x4>(smem, off, pack4(v)); }
+  // 32-deep slot of block (row tile R, column tile S) of a 64x64 matrix: its 4 values
+  __device__ __forceinline__ uint32_t slot64(uint32_t base, int R, int S) const {
+    return base + ((R * NKT + S / 2) * 64 + fresh_lane(l)) * 16 + (S % 2) * 8;
+  }
+
+  __device__ __forceinline__ void init_offsets() {
+    const int r16 = l & 15;
+    const int kg = 8 * (l >> 4);
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) oTD[m] = swz<C::R_TD>(r16, 2 * (32 * m + kg));
+    tr_f = 4 * (l >> 4) + (r16 >> 2);
+    tr_q = r16 & 3;
+  }
+
+  // ------------------------------------------------------------ phase 1
+  // Wave pw < NP: lane (tg = l%16, cs = l/16) owns tokens 4tg .. 4tg+3 and
+  // channels 32pw + 8cs .. +7; a channel's 16 token groups form one DPP row.
+  __device__ __forceinline__ void phase1() {
+    if (wave >= C::NP) return;
+    const int tg = l & 15, cs = l >> 4;
+    const int ch = 32 * wave + 8 * cs;
+    Raw8<bf16> rla_[4], rk_[4], rq_[4], rdo_[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t off = (uint32_t)((4 * tg + i) * D + ch) * 2;
+      raw_load<bf16>(rla_[i], rla, off);
+      raw_load<bf16>(rk_[i], rk, off);
+      raw_load<bf16>(rq_[i], rq, off);
+      raw_load<bf16>(rdo_[i], rdo, off);
+    }
+    float bet = 0.f;
+    if (wave == 0)
+      bet = __uint_as_float((uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rbeta, 2 * l, 0, 0) << 16);
+    float g[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      raw_f32<bf16>(rla_[i], g[i]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) g[i][c] *= G_LOG2E;
+    }
+    float exc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      g[1][c] += g[0][c];
+      g[2][c] += g[1][c];
+      g[3][c] += g[2][c];
+      float x = g[3][c];
+      x += dpp<DPP_ROW_SHR + 1>(x);
+      x += dpp<DPP_ROW_SHR + 2>(x);
+      x += dpp<DPP_ROW_SHR + 4>(x);
+      x += dpp<DPP_ROW_SHR + 8>(x);
+      exc[c] = dpp<DPP_ROW_SHR + 1>(x);
+    }
+    float eg3[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float kk[8], qq[8];
+      raw_f32<bf16>(rk_[i], kk);
+      raw_f32<bf16>(rq_[i], qq);
+      float vkh[8], vkb[8], vq[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float gg = g[i][c] + exc[c];
+        const float eg = __builtin_amdgcn_exp2f(gg);
+        const float emg = __builtin_amdgcn_exp2f(-gg);
+        if (i == 3) eg3[c] = eg;
+        vkh[c] = kk[c] * eg;
+        vkb[c] = kk[c] * emg;
+        vq[c] = qq[c] * eg;
+      }
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        bf16x4 h, b, qv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          h[c] = (bf16)vkh[4 * hlf + c];
+          b[c] = (bf16)vkb[4 * hlf + c];
+          qv[c] = (bf16)vq[4 * hlf + c];
+        }
+        const uint32_t o = td(4 * tg + i, 2 * kpos(ch + 4 * hlf));
+        lds_st<bf16x4>(smem, C::KH + o, h);
+        lds_st<bf16x4>(smem, C::KB + o, b);
+        lds_st<bf16x4>(smem, C::QH + o, qv);
+        lds_st<u32x2>(smem, C::DO + o, u32x2{rdo_[i].p[0][2 * hlf], rdo_[i].p[0][2 * hlf + 1]});
+      }
+    }
+    if (tg == 15) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) lds_st<float>(smem, C::GM + 4 * (ch + c), eg3[c]);
+    }
+    if (wave == 0) lds_st<float>(smem, C::BETA + 4 * l, bet);
+  }
+
+  // ------------------------------------------------------------ phase 2
+  // Score tile tasks.  With fx = rows of X's row tile I and fb = rows of Kb's row
+  // tile J (both as A/B fragments over channels), mma(A = fb, B = fx) leaves lane
+  // l holding M[16I + l%16][16J + 4g + e] (the A fragment of M_IJ) and
+  // mma(A = fx, B = fb) leaves M[16I + 4g + e][16J + l%16] (the accumulator
+  // tile of M_IJ: the A fragment of M_IJ^T).
+  template <int KIND, int I, int J>  // KIND 0: diagonal, 1: off-diagonal L, 2: P
+  __device__ __forceinline__ void p2_tile() {
+    const int ln = fresh_lane(l);
+    const uint32_t xb = (KIND == 2 ? C::QH : C::KH) + I * C::TD_TILE;
+    bf16x8 fx[NKD], fb[NKD];
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) {
+      fx[m] = lds_ld<bf16x8>(smem, xb + oTD[m]);
+      fb[m] = lds_ld<bf16x8>(smem, C::KB + J * C::TD_TILE + oTD[m]);
+    }
+    const float bl = lds_ld<float>(smem, C::BETA + 4 * (16 * I + s0));
+    const f32x4 bet4 = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * I + g4));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 at = zero4();  // M[16I + 4g + e][16J + s0]
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) at = mfma_bf16_k32(at, fx[m], fb[m]);
+    if constexpr (KIND == 2) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (I > J || g4 + e >= s0) ? at[e] : 0.f;
+      put16(slot64(C::PT, J, I), v);  // P_IJ^T: row tile J, token tile I
+      return;
+    }
+    f32x4 af = zero4();  // M[16I + s0][16J + 4g + e]
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) af = mfma_bf16_k32(af, fb[m], fx[m]);
+    if constexpr (KIND == 1) {
+      f32x4 vf, vb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[e] = -bl * af[e];
+        vb[e] = -bet4[e] * at[e];
+      }
+      put16(C::LO + (I * (I - 1) / 2 + J) * C::FR16 + ln * 8, vf);
+      put16(C::LT + (I * (I - 1) / 2 + J) * C::FR16 + ln * 8, vb);
+    } else {
+      // N = L_II (strictly lower).  T_ii = (I - N)(I + N^2)(I + N^4)(I + N^8); both
+      // T_ii and T_ii^T are accumulated, from the accumulators of N and N^T.
+      f32x4 Nt, Nn, Zf, Zb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Nt[e] = g4 + e < s0 ? bl * af[e] : 0.f;      // N[16I + s0][16I + g4 + e]
+        Nn[e] = s0 < g4 + e ? bet4[e] * at[e] : 0.f;  // N[16I + g4 + e][16I + s0]
+        const float id = g4 + e == s0 ? 1.f : 0.f;
+        Zf[e] = id - Nt[e];  // acc(T^T)
+        Zb[e] = id - Nn[e];  // acc(T)
+      }
+      const f32x4 N2 = mfma_bf16_k16(zero4(), pack4(Nt), pack4(Nn));
+      const f32x4 Nt2 = mfma_bf16_k16(zero4(), pack4(Nn), pack4(Nt));
+      Zf = mfma_bf16_k16(Zf, pack4(N2), pack4(Zf));
+      Zb = mfma_bf16_k16(Zb, pack4(Nt2), pack4(Zb));
+      const f32x4 N4 = mfma_bf16_k16(zero4(), pack4(Nt2), pack4(N2));
+      const f32x4 Nt4 = mfma_bf16_k16(zero4(), pack4(N2), pack4(Nt2));
+      Zf = mfma_bf16_k16(Zf, pack4(N4), pack4(Zf));
+      Zb = mfma_bf16_k16(Zb, pack4(Nt4), pack4(Zb));
+      const f32x4 N8 = mfma_bf16_k16(zero4(), pack4(Nt4), pack4(N4));
+      const f32x4 Nt8 = mfma_bf16_k16(zero4(), pack4(N4), pack4(Nt4));
+      Zf = mfma_bf16_k16(Zf, pack4(N8), pack4(Zf));
+      Zb = mfma_bf16_k16(Zb, pack4(Nt8), pack4(Zb));
+      put16(C::TI + I * C::FR16 + ln * 8, Zf);
+      put16(C::TT + I * C::FR16 + ln * 8, Zb);
+    }
+  }
+  // tasks: 4 diagonal (weight 3), 6 off-diagonal (2), 10 P (1), greedy over the waves
+  static constexpr int p2_kind(int K) { return K < 4 ? 0 : (K < 10 ? 1 : 2); }
+  static constexpr int p2_i(int K) {
+    if (K < 4) return K;
+    if (K < 10) {
+      const int io[6] = {3, 3, 3, 2, 2, 1};
+      return io[K - 4];
+    }
+    const int ii[10] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
+    return ii[K - 10];
+  }
+  static constexpr int p2_j(int K) {
+    if (K < 4) return K;
+    if (K < 10) {
+      const int jo[6] = {2, 1, 0, 1, 0, 0};
+      return jo[K - 4];
+    }
+    const int jj[10] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
+    return jj[K - 10];
+  }
+  static constexpr int greedy_wave(int K, int ntask, const int* weight) {
+    int load[C::NW] = {};
+    int w = 0;
+    for (int k = 0; k <= K && k < ntask; ++k) {
+      w = 0;
+      for (int i = 1; i < C::NW; ++i)
+        if (load[i] < load[w]) w = i;
+      load[w] += weight[k];
+    }
+    return w;
+  }
+  static constexpr int p2_wave(int K) {
+    int wt[20] = {};
+    for (int k = 0; k < 20; ++k) wt[k] = k < 4 ? 3 : (k < 10 ? 2 : 1);
+    return greedy_wave(K, 20, wt);
+  }
+  template <int K>
+  __device__ __forceinline__ void p2_tasks() {
+    if constexpr (K < 20) {
+      constexpr int W = p2_wave(K);  // evaluated at compile time
+      if (W == wave) p2_tile<p2_kind(K), p2_i(K), p2_j(K)>();
+      p2_tasks<K + 1>();
+    }
+  }
+
+  // ------------------------------------------------------------ phase 3
+  // Wave w owns value columns of tiles ct = NCT w + j: lane l holds, in an
+  // accumulator tile, rows 16t + 4g + e of column c_j = 16 ct + l%16.
+  __device__ __forceinline__ int col(int j) const { return 16 * (NCT * wave + j) + s0; }
+
+  // fp32 state columns as B fragments over the state's rows (channels)
+  __device__ __forceinline__ void state_cols(rsrc_t r, bf16x8 (*out)[NKD]) const {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      f32x4 t[D / 16];
+#pragma unroll
+      for (int ci = 0; ci < D / 16; ++ci)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          t[ci][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              r, (uint32_t)((16 * ci + g4 + e) * D + col(j)) * 4u, 0, 0));
+#pragma unroll
+      for (int m = 0; m < NKD; ++m) out[j][m] = pack8(t[2 * m], t[2 * m + 1]);
+    }
+  }
+
+  // bf16 value at (row, column) of the chunk's [64][D] input
+  __device__ __forceinline__ float in_val(rsrc_t r, int row, int c) const {
+    return __uint_as_float((uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+                               r, (uint32_t)(row * D + c) * 2u, 0, 0) << 16);
+  }
+
+  // sum over the 16 lanes of each lane row; lane 15 of the row holds it
+  __device__ __forceinline__ static float row_sum16(float x) {
+    x += dpp<DPP_ROW_SHR + 1>(x);
+    x += dpp<DPP_ROW_SHR + 2>(x);
+    x += dpp<DPP_ROW_SHR + 4>(x);
+    x += dpp<DPP_ROW_SHR + 8>(x);
+    return x;
+  }
+
+  __device__ __forceinline__ void store_tile_lds(uint32_t tile, const f32x4 (*x)[4]) {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          lds_st<bf16>(smem, tile + td(16 * t + g4 + e, 2 * kpos(col(j))), (bf16)x[j][t][e]);
+  }
+
+  __device__ __forceinline__ void phase3() {
+    bf16x8 sb[NCT][NKD];
+    state_cols(rS, sb);
+    // W = V - Kh S, from -V
+    f32x4 X[NCT][4];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) X[j][t][e] = -in_val(rv, 16 * t + g4 + e, col(j));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bf16x8 fk[NKD];
+#pragma unroll
+      for (int m = 0; m < NKD; ++m) fk[m] = ar(C::KH, t, m);
+#pragma unroll
+      for (int m = 0; m < NKD; ++m)
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) X[j][t] = mfma_bf16_k32(X[j][t], fk[m], sb[j][m]);
+    }
+    f32x4 W[NCT][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f32x4 bet = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * t + g4));
+#pragma unroll
+      for (int j = 0; j < NCT; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          W[j][t][e] = -X[j][t][e];
+          X[j][t][e] = bet[e] * W[j][t][e];
+        }
+    }
+    // Delta = T X: Delta_t = T_tt (X_t - sum_{u<t} L_tu Delta_u)
+    const uint32_t lo = (uint32_t)fresh_lane(l) * 8;
+    f32x4 Dl[NCT][4];
+    {
+      bf16x4 ft[4], fl[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        ft[t] = lds_ld<bf16x4>(smem, C::TI + t * C::FR16 + lo);
+#pragma unroll
+        for (int u = 0; u < t; ++u) fl[t][u] = lds_ld<bf16x4>(smem, C::LO + (t * (t - 1) / 2 + u) * C::FR16 + lo);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          f32x4 rr = X[j][t];
+#pragma unroll
+          for (int u = 0; u < t; ++u) rr = mfma_bf16_k16(rr, fl[t][u], pack4(Dl[j][u]));
+          Dl[j][t] = mfma_bf16_k16(zero4(), ft[t], pack4(rr));
+        }
+    }
+    store_tile_lds(C::DL, Dl);
+    // dDelta = Kb dU + P^T dO
+    bf16x8 ub[NCT][NKD];
+    state_cols(rU, ub);
+    bf16x8 dob[NCT][NKT];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int m = 0; m < NKT; ++m) dob[j][m] = tr_frag(C::DO, NCT * wave + j, m);
+    f32x4 Xb[NCT][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      bf16x8 fk[NKD], fp[NKT];
+#pragma unroll
+      for (int m = 0; m < NKD; ++m) fk[m] = ar(C::KB, t, m);
+#pragma unroll
+      for (int m = t / 2; m < NKT; ++m) fp[m] = fr64(C::PT, t, m);
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int m = 0; m < NKD; ++m) acc = mfma_bf16_k32(acc, fk[m], ub[j][m]);
+#pragma unroll
+        for (int m = t / 2; m < NKT; ++m) acc = mfma_bf16_k32(acc, fp[m], dob[j][m]);
+        Xb[j][t] = acc;
+      }
+    }
+    // Xbar = T^T dDelta: Xbar_t = T_tt^T (dDelta_t - sum_{u>t} L_ut^T Xbar_u)
+    {
+      bf16x4 ft[4], fl[4][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        ft[t] = lds_ld<bf16x4>(smem, C::TT + t * C::FR16 + lo);
+#pragma unroll
+        for (int u = t + 1; u < 4; ++u) fl[t][u] = lds_ld<bf16x4>(smem, C::LT + (u * (u - 1) / 2 + t) * C::FR16 + lo);
+      }
+#pragma unroll
+      for (int t = 3; t >= 0; --t)
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          f32x4 rr = Xb[j][t];
+#pragma unroll
+          for (int u = t + 1; u < 4; ++u) rr = mfma_bf16_k16(rr, fl[t][u], pack4(Xb[j][u]));
+          Xb[j][t] = mfma_bf16_k16(zero4(), ft[t], pack4(rr));
+        }
+    }
+    store_tile_lds(C::XB, Xb);
+    // dv = diag(b) Xbar; first part of dbeta: sum_j Xbar_rj W_rj over this wave's columns
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f32x4 bet = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * t + g4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * t + g4 + e;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bet[e] * Xb[j][t][e]), rdv,
+                                                (uint32_t)(row * D + col(j)) * 4u, 0, 0);
+          s += Xb[j][t][e] * W[j][t][e];
+        }
+        s = row_sum16(s);
+        if (s0 == 15) lds_st<float>(smem, C::DBP + 4 * (wave * GCH + row), s);
+      }
+    }
+  }
+
+  // ------------------------------------------------------------ phase 4
+  // Block (R, S), R >= S, of the 64x64 gradients, from row tiles of dO, Xbar, Kh
+  // (R) and of Delta, Kb (S), contracting over D.
+  template <int R, int S>
+  __device__ __forceinline__ void p4_tile() {
+    bf16x8 fo[NKD], fd[NKD], fxb[NKD], fkh[NKD], fkb[NKD];
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) {
+      fo[m] = ar(C::DO, R, m);
+      fd[m] = ar(C::DL, S, m);
+      fxb[m] = ar(C::XB, R, m);
+      fkh[m] = ar(C::KH, R, m);
+      fkb[m] = ar(C::KB, S, m);
+    }
+    const float bl = lds_ld<float>(smem, C::BETA + 4 * (16 * R + s0));
+    const f32x4 bet4 = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * R + g4));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4(), a4 = zero4(), a5 = zero4();
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) {
+      a1 = mfma_bf16_k32(a1, fd[m], fo[m]);    // dP[16R + s0][16S + 4g + e]
+      a2 = mfma_bf16_k32(a2, fo[m], fd[m]);    // dP[16R + 4g + e][16S + s0]
+      a3 = mfma_bf16_k32(a3, fd[m], fxb[m]);   // -Lbar[16R + s0][16S + 4g + e]
+      a4 = mfma_bf16_k32(a4, fxb[m], fd[m]);   // -Lbar[16R + 4g + e][16S + s0]
+      a5 = mfma_bf16_k32(a5, fkh[m], fkb[m]);  // (Kh Kb^T)[16R + 4g + e][16S + s0]
+    }
+    f32x4 v1, v2, v3, v4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool lo1 = R > S || s0 >= g4 + e, st1 = R > S || s0 > g4 + e;  // (row s0, col 4g+e)
+      const bool lo2 = R > S || g4 + e >= s0, st2 = R > S || g4 + e > s0;  // (row 4g+e, col s0)
+      v1[e] = lo1 ? a1[e] : 0.f;
+      v2[e] = lo2 ? a2[e] : 0.f;
+      v3[e] = st1 ? -bl * a3[e] : 0.f;       // Abar = diag(b) Lbar
+      v4[e] = st2 ? -bet4[e] * a4[e] : 0.f;
+    }
+    put16(slot64(C::DP, R, S), v1);
+    put16(slot64(C::DPT, S, R), v2);
+    put16(slot64(C::AB, R, S), v3);
+    put16(slot64(C::ABT, S, R), v4);
+    // second part of dbeta: sum_{s < r} Lbar_rs (Kh Kb^T)_rs, rows 16R + 4g + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool st2 = R > S || g4 + e > s0;
+      float x = st2 ? -a4[e] * a5[e] : 0.f;
+      x = row_sum16(x);
+      if (s0 == 15) {
+        const uint32_t o = C::DBP + 4 * ((C::NW + wave) * GCH + 16 * R + g4 + e);
+        lds_st<float>(smem, o, lds_ld<float>(smem, o) + x);
+      }
+    }
+  }
+  static constexpr int p4_r(int K) {
+    const int rr[10] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
+    return rr[K];
+  }
+  static constexpr int p4_s(int K) {
+    const int ss[10] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
+    return ss[K];
+  }
+  static constexpr int p4_wave(int K) {
+    int wt[10] = {1, 1, 1, 1, 1, 1, 1, 1, 1, 1};
+    return greedy_wave(K, 10, wt);
+  }
+  template <int K>
+  __device__ __forceinline__ void p4_tasks() {
+    if constexpr (K < 10) {
+      constexpr int W = p4_wave(K);
+      if (W == wave) p4_tile<p4_r(K), p4_s(K)>();
+      p4_tasks<K + 1>();
+    }
+  }
+
+  // ------------------------------------------------------------ phase 5 / 6
+  // fp32 values a (rows 4g+e of one 16-row tile) and b (the next tile) as a
+  // 32-deep B fragment over tokens, split into a bf16 part and the bf16 of the
+  // remainder: two products with them carry about 16 bits of the operand.
+  __device__ __forceinline__ static void split8(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+    hi = pack8(a, b);
+    f32x4 ra, rb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ra[e] = a[e] - (float)hi[e];
+      rb[e] = b[e] - (float)hi[4 + e];
+    }
+    lo = pack8(ra, rb);
+  }
+
+  // Key column tile j of this wave (columns c = 16 ct + l%16, ct = NCT w + j),
+  // start to end: dQh, dKh, dKb (its Delta dU^T part apart) and rowsum(dU . S),
+  // then the gate's chain rule.
+  //
+  // The products with the 64 x 64 gradients (dP Kb, Abar Kb, Abar^T Kh,
+  // dP^T Qh) give each pair of tokens (r, s) a term in dg_r and the opposite
+  // one in dg_s; the suffix sum over tokens cancels them except for pairs that
+  // straddle the token, so their rounding error would pile up against a small
+  // result.  Their operands Kb, Kh, Qh are therefore formed here in fp32, at
+  // this lane's own positions (tokens 16t + 4g + e of column c: exactly the
+  // positions of its B fragments over tokens), and fed as a bf16 part plus the
+  // bf16 of the remainder.
+  __device__ __forceinline__ void phase5_6(int j) {
+    const int c = col(j);
+    // rows c of S and dU as B fragments over the state's columns (the kpos
+    // positions of each 32-wide block), and rowsum(dU . S) over the lane's
+    // positions in fp32
+    bf16x8 sr[NKD], ur[NKD];
+    float dgc = 0.f;
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) {
+      const uint32_t base = (uint32_t)(c * D + 32 * m + g4) * 4u;
+      const f32x4 s_lo = __builtin_bit_cast(f32x4, bload128(rS, base));
+      const f32x4 s_hi = __builtin_bit_cast(f32x4, bload128(rS, base + 64u));
+      const f32x4 u_lo = __builtin_bit_cast(f32x4, bload128(rU, base));
+      const f32x4 u_hi = __builtin_bit_cast(f32x4, bload128(rU, base + 64u));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dgc += s_lo[e] * u_lo[e] + s_hi[e] * u_hi[e];
+      sr[m] = pack8(s_lo, s_hi);
+      ur[m] = pack8(u_lo, u_hi);
+    }
+    // rowsum(dU . S): the four lane groups (l%16 fixed) hold the rest of the row's sum
+    dgc += __shfl_xor(dgc, 16);
+    dgc += __shfl_xor(dgc, 32);
+    // the gate at this lane's positions: g from log_alpha by a prefix over the
+    // lane's 4 rows, then over the lane groups and row tiles
+    f32x4 qv[4], kv[4], eg[4], emg[4];
+    {
+      float tot[4];
+      f32x4 gv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float run = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * t + g4 + e;
+          run += in_val(rla, row, c);
+          gv[t][e] = run;
+          qv[t][e] = in_val(rq, row, c);
+          kv[t][e] = in_val(rk, row, c);
+        }
+        tot[t] = run;
+      }
+      float base = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float a0 = __shfl(tot[t], s0), a1 = __shfl(tot[t], s0 + 16), a2 = __shfl(tot[t], s0 + 32),
+                    a3 = __shfl(tot[t], s0 + 48);
+        const float pre = (g4 > 0 ? a0 : 0.f) + (g4 > 4 ? a1 : 0.f) + (g4 > 8 ? a2 : 0.f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gg = (gv[t][e] + base + pre) * G_LOG2E;
+          eg[t][e] = __builtin_amdgcn_exp2f(gg);
+          emg[t][e] = __builtin_amdgcn_exp2f(-gg);
+        }
+        base += (a0 + a1) + (a2 + a3);
+      }
+    }
+    f32x4 dqh[4], dkh[4], dks[4], dkb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 b = zero4(), q = zero4(), h = zero4();
+#pragma unroll
+      for (int m = 0; m < NKD; ++m) {
+        b = mfma_bf16_k32(b, ar(C::DL, t, m), ur[m]);  // Delta dU^T
+        q = mfma_bf16_k32(q, ar(C::DO, t, m), sr[m]);  // dO S^T
+        h = mfma_bf16_k32(h, ar(C::XB, t, m), sr[m]);  // Xbar S^T
+      }
+      dks[t] = b;
+      dkb[t] = zero4();
+      dqh[t] = q;
+      dkh[t] = h;
+    }
+    // dKh = -diag(b) Xbar S^T + Abar Kb;  dQh += dP Kb;  dKb = Abar^T Kh + dP^T Qh (+ dks)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f32x4 bet = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * t + g4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dkh[t][e] *= -bet[e];
+    }
+#pragma unroll
+    for (int m = 0; m < NKT; ++m) {
+      bf16x8 kbH, kbL, khH, khL, qhH, qhL;
+      split8(kv[2 * m] * emg[2 * m], kv[2 * m + 1] * emg[2 * m + 1], kbH, kbL);
+      split8(kv[2 * m] * eg[2 * m], kv[2 * m + 1] * eg[2 * m + 1], khH, khL);
+      split8(qv[2 * m] * eg[2 * m], qv[2 * m + 1] * eg[2 * m + 1], qhH, qhL);
+#pragma unroll
+      for (int t = 2 * m; t < 4; ++t) {  // m <= t / 2
+        const bf16x8 fdp = fr64(C::DP, t, m), fab = fr64(C::AB, t, m);
+        dqh[t] = mfma_bf16_k32(dqh[t], fdp, kbH);
+        dqh[t] = mfma_bf16_k32(dqh[t], fdp, kbL);
+        dkh[t] = mfma_bf16_k32(dkh[t], fab, kbH);
+        dkh[t] = mfma_bf16_k32(dkh[t], fab, kbL);
+      }
+#pragma unroll
+      for (int t = 0; t <= 2 * m + 1; ++t) {  // m >= t / 2
+        const bf16x8 fabt = fr64(C::ABT, t, m), fdpt = fr64(C::DPT, t, m);
+        dkb[t] = mfma_bf16_k32(dkb[t], fabt, khH);
+        dkb[t] = mfma_bf16_k32(dkb[t], fabt, khL);
+        dkb[t] = mfma_bf16_k32(dkb[t], fdpt, qhH);
+        dkb[t] = mfma_bf16_k32(dkb[t], fdpt, qhL);
+      }
+    }
+    // phase 6: the gate's chain rule
+    float dg[4][4], ps[4][4];  // dg, and k e^-g (Delta dU^T) for the prefix over earlier tokens
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * t + g4 + e;
+        const float dq = dqh[t][e] * eg[t][e];
+        const float t1 = dkh[t][e] * eg[t][e], t2 = dkb[t][e] * emg[t][e], t3 = dks[t][e] * emg[t][e];
+        const uint32_t off = (uint32_t)(row * D + c) * 4u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq), rdq, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(t1 + t2 + t3), rdk, off, 0, 0);
+        dg[t][e] = qv[t][e] * dq + kv[t][e] * (t1 - t2);
+        ps[t][e] = kv[t][e] * t3;
+      }
+    // dlog_alpha_r = sum_{r' >= r} dg_r' + rowsum(dU . S) + sum_{s < r} ps_s: a
+    // suffix and an exclusive prefix over the lane's rows, then over the lane
+    // groups and row tiles
+    float stot[4], ptot[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float run = 0.f, pre = 0.f;
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        run += dg[t][e];
+        dg[t][e] = run;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = ps[t][e];
+        ps[t][e] = pre;
+        pre += x;
+      }
+      stot[t] = run;
+      ptot[t] = pre;
+    }
+    float after = 0.f, before = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float a0 = __shfl(ptot[t], s0), a1 = __shfl(ptot[t], s0 + 16), a2 = __shfl(ptot[t], s0 + 32),
+                  a3 = __shfl(ptot[t], s0 + 48);
+      const float pre = (g4 > 0 ? a0 : 0.f) + (g4 > 4 ? a1 : 0.f) + (g4 > 8 ? a2 : 0.f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ps[t][e] += before + pre;
+      before += (a0 + a1) + (a2 + a3);
+    }
+#pragma unroll
+    for (int t = 3; t >= 0; --t) {
+      const float a0 = __shfl(stot[t], s0), a1 = __shfl(stot[t], s0 + 16), a2 = __shfl(stot[t], s0 + 32),
+                  a3 = __shfl(stot[t], s0 + 48);
+      const float post = (g4 < 4 ? a1 : 0.f) + (g4 < 8 ? a2 : 0.f) + (g4 < 12 ? a3 : 0.f);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * t + g4 + e;
+        const float dla = (dg[t][e] + post + after) + dgc + ps[t][e];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dla), rdla, (uint32_t)(row * D + c) * 4u, 0, 0);
+      }
+      after += (a0 + a1) + (a2 + a3);
+    }
+  }
+
+  __device__ __forceinline__ void run() {
+    const int nch = (a.T + GCH - 1) / GCH;
+    const int bh = blockIdx.x / nch;
+    const int n = blockIdx.x - bh * nch;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    l = lane_id();
+    g4 = 4 * (l >> 4);
+    s0 = l & 15;
+    nrows = min(GCH, a.T - n * GCH);
+    const size_t tok0 = (size_t)bh * a.T + (size_t)n * GCH;
+    const uint32_t in_bytes = (uint32_t)nrows * D * 2u, out_bytes = (uint32_t)nrows * D * 4u;
+    rq = make_rsrc(static_cast<const bf16*>(a.q) + tok0 * D, in_bytes);
+    rk = make_rsrc(static_cast<const bf16*>(a.k) + tok0 * D, in_bytes);
+    rv = make_rsrc(static_cast<const bf16*>(a.v) + tok0 * D, in_bytes);
+    rla = make_rsrc(static_cast<const bf16*>(a.la) + tok0 * D, in_bytes);
+    rdo = make_rsrc(a.dO ? static_cast<const bf16*>(a.dO) + tok0 * D : nullptr, a.dO ? in_bytes : 0u);
+    rbeta = make_rsrc(static_cast<const bf16*>(a.beta) + tok0, (uint32_t)nrows * 2u);
+    rdq = make_rsrc(a.dq + tok0 * D, out_bytes);
+    rdk = make_rsrc(a.dk + tok0 * D, out_bytes);
+    rdv = make_rsrc(a.dv + tok0 * D, out_bytes);
+    rdla = make_rsrc(a.dla + tok0 * D, out_bytes);
+    // the chunk's start state: S0 for the first chunk, else the forward's
+    // checkpoint after the previous chunk ([B, nsnap, H, D, D])
+    const float* S = nullptr;
+    if (n == 0) {
+      S = a.S0 ? a.S0 + (size_t)bh * D * D : nullptr;
+    } else {
+      const int b = bh / a.H, h = bh - b * a.H;
+      S = a.ckpt + (((size_t)b * a.nckpt + (n - 1)) * a.H + h) * D * D;
+    }
+    rS = make_rsrc(S, S ? D * D * 4u : 0u);
+    rU = make_rsrc(a.dU + ((size_t)bh * nch + n) * D * D, D * D * 4u);
+    init_offsets();
+    // zero halves of the 32-deep slots that pair a block of the upper triangle
+    // with a stored one (nothing writes them): dP and Abar slots (0, 0) and
+    // (2, 1), second half; P^T, dP^T and Abar^T slots (1, 0) and (3, 1), first half
+    for (int t = threadIdx.x; t < 64 * 2 * 5; t += C::THREADS) {
+      const int which = t >> 7, lane = t & 63, sel = (t >> 6) & 1;
+      uint32_t off;
+      if (which < 2) {
+        const uint32_t base = which == 0 ? C::DP : C::AB;
+        off = base + (uint32_t)(((sel ? 2 * NKT + 1 : 0) * 64 + lane) * 16 + 8);
+      } else {
+        const uint32_t base = which == 2 ? C::PT : (which == 3 ? C::DPT : C::ABT);
+        off = base + (uint32_t)(((sel ? 3 * NKT + 1 : 1 * NKT) * 64 + lane) * 16);
+      }
+      lds_st<u32x2>(smem, off, u32x2{0u, 0u});
+    }
+    for (int i = threadIdx.x; i < 2 * C::NW * GCH; i += C::THREADS) lds_st<float>(smem, C::DBP + 4 * i, 0.f);
+    phase1();
+    __syncthreads();
+    p2_tasks<0>();
+    __syncthreads();
+    phase3();
+    __syncthreads();
+    p4_tasks<0>();
+    __syncthreads();
+    if (wave == 0 && l < nrows) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < 2 * C::NW; ++w) s += lds_ld<float>(smem, C::DBP + 4 * (w * GCH + l));
+      a.dbeta[tok0 + l] = s;
+    }
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) phase5_6(j);
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(GradCfg<D>::THREADS, 1) void kda_bwgrad_kernel(BwGradArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[GradCfg<D>::LDS];
+  GradKernel<D> k;
+  k.smem = smem;
+  k.a = a;
+  k.run();
+}
+
+}  // namespace
+
+hipError_t launch_bwgrad(const BwGradArgs& a, int BH, int D, hipStream_t stream) {
+  const long long nch = (a.T + GCH - 1) / GCH;
+  const long long nwg = (long long)BH * nch;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (D == 128) {
+    hipLaunchKernelGGL(kda_bwgrad_kernel<128>, dim3((unsigned)nwg), dim3(GradCfg<128>::THREADS), 0, stream, a);
+  } else if (D == 64) {
+    hipLaunchKernelGGL(kda_bwgrad_kernel<64>, dim3((unsigned)nwg), dim3(GradCfg<64>::THREADS), 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

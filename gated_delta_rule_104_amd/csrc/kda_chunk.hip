@@ -103,48 +103,6 @@ struct ChunkCfg {
   static_assert(LDS % 16 == 0 && STAGE % 16 == 0, "LDS alignment");
 };
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer over [p, p + bytes): loads past the end return 0, stores are dropped.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-// DPP moves within rows of 16 lanes (gfx9 encoding): row_shr:n shifts values
-// n lanes up inside the row; lanes below n read 0 (bound control), so no old
-// value has to be materialised.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
-}
-constexpr int DPP_ROW_SHR = 0x110;
-
-// 8 consecutive elements of a token row, as loaded from HBM.
-template <typename T> struct Raw8 { u32x4 p[sizeof(T) / 2]; };
-
-template <typename T>
-__device__ __forceinline__ void raw_load(Raw8<T>& r, rsrc_t rs, uint32_t off) {
-#pragma unroll
-  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.p[i] = bload128(rs, off + 16 * i);
-}
-
-template <typename T>
-__device__ __forceinline__ void raw_f32(const Raw8<T>& r, float* out) {
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __uint_as_float(r.p[0][i] << 16);
-      out[2 * i + 1] = __uint_as_float(r.p[0][i] & 0xffff0000u);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[i] = __uint_as_float(r.p[i >> 2][i & 3]);
-  }
-}
-
 // Producer input registers for one chunk: 4 token rows x 8 channels of
 // log_alpha, k and q, plus one beta per lane (raw bits).
 template <typename T> struct ProdRaw {
@@ -193,8 +151,13 @@ template <> struct Frag<false> {
   __device__ __forceinline__ static A16 a16(f32x4 t) { return t; }
 };
 
-template <typename T, int D, int NC, bool PREFILL>
+template <typename T, int D, int NC, bool PREFILL, bool BWD = false>
 struct ChunkKernel {
+  // BWD: the reverse chain of the prefill's gradients (see chain_bw); it uses
+  // the prefill's stage layout and producer, visits the chunks last to first,
+  // and is built for bf16 inputs (its transposed operands use the 16-bit
+  // transposing LDS read).
+  static_assert(!BWD || (PREFILL && sizeof(T) == 2), "the backward chain is a bf16 prefill-layout mode");
   using C = ChunkCfg<T, D, NC, PREFILL>;
   using F = Frag<C::BF>;
   typedef typename F::A16 A16;
@@ -213,6 +176,7 @@ struct ChunkKernel {
   ChunkArgs a;
   rsrc_t rq, rk, rv, rla, rbeta, ro;
   int Tlen, nch;
+  int bh_seq;        // the sequence (segment) this workgroup works on
   int chunk0;        // chunks of the head's sequence before this segment
   float* snap_head;  // snapshot 0 of this head (prefill with snapshots), else null
   int wave, l;
@@ -238,15 +202,21 @@ struct ChunkKernel {
     return (C::STAGES == 2 ? (uint32_t)(chunk & 1) : 0u) * C::STAGE;
   }
 
+  // The chunk that pipeline step `it` works on: the chunks in order, or last to
+  // first for the backward chain.  Steps past the end map to chunk indices past
+  // either end of the sequence, whose loads (negative offsets become offsets
+  // beyond any buffer's size) read zero.
+  __device__ __forceinline__ int chunk_of(int it) const { return BWD ? nch - 1 - it : it; }
+
   // ------------------------------------------------------------ producers
   // Lane (tg = l%16, cs = l/16) of producer wave pw owns tokens 4*tg..4*tg+3 and
   // channels 32*pw + 8*cs .. +7 of the chunk; a channel's 16 token groups are
   // one DPP row, so the prefix sum over tokens runs on row operations.
   // byte offset of token row i of the lane's token group, first of its channels
-  __device__ __forceinline__ uint32_t prod_off(int chunk, int i) const {
+  __device__ __forceinline__ uint32_t prod_off(int it, int i) const {
     const int ln = fresh_lane(l);
     const int ch = 32 * (wave - NC) + 8 * (ln >> 4);
-    return (uint32_t)((chunk * CH + 4 * (ln & 15) + i) * D + ch) * C::ES;
+    return (uint32_t)((chunk_of(it) * CH + 4 * (ln & 15) + i) * D + ch) * C::ES;
   }
   __device__ __forceinline__ void load_la(ProdRaw<T>& r, int chunk) const {
 #pragma unroll
@@ -258,7 +228,7 @@ struct ChunkKernel {
   }
   __device__ __forceinline__ void load_beta(ProdRaw<T>& r, int chunk) const {
     if (wave == NC) {
-      const uint32_t off = (uint32_t)(chunk * CH + fresh_lane(l)) * C::ES;
+      const uint32_t off = (uint32_t)(chunk_of(chunk) * CH + fresh_lane(l)) * C::ES;
       if constexpr (C::BF) r.beta = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rbeta, off, 0, 0);
       else r.beta = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rbeta, off, 0, 0);
     }
@@ -524,7 +494,107 @@ struct ChunkKernel {
     }
   }
 
-  __device__ __forceinline__ void p2(uint32_t st) { p2_task<0>(st); }
+  __device__ __forceinline__ void p2(uint32_t st) {
+    if constexpr (BWD) p2_task_bw<0>(st);
+    else p2_task<0>(st);
+  }
+  // ------------------------------------------------ backward-chain tile tasks
+  // The reverse chain needs the transposes of the forward's A operands: P^T,
+  // L^T and T_ii^T.  Block (I, J) of M = X Kb^T (X = Kh or Qh) is computed
+  // with A = X rows of row tile I and B = Kb rows of row tile J, so that lane l
+  // holds M[16I + 4g + e][16J + l%16] (g = l/16): the accumulator layout of
+  // M_IJ, which is exactly the A fragment of M_IJ^T.
+  //   MAT 0, I > J : -L_IJ^T (L = diag(b) strict_lower(Kh Kb^T)), slot I(I-1)/2 + J
+  //   MAT 1, I >= J: P_IJ^T (P = lower(Qh Kb^T)) in the 32-deep slot of row tile J,
+  //                  token block I / 2 (half I % 2)
+  //   MAT 0, I = J : T_ii as an accumulator tile (the A fragment of T_ii^T), from
+  //                  N = L_ii: T_ii = (I - N)(I + N^2)(I + N^4)(I + N^8), accumulated
+  //                  as Z += N^(2^k) Z; N^(2^k) as an A operand is the A fragment
+  //                  of the accumulator of (N^T)^(2^k).
+  template <int MAT, int I, int J>
+  __device__ __forceinline__ void p2_tile_bw(uint32_t st) {
+    constexpr bool DIAG = MAT == 0 && I == J;
+    const int ln = fresh_lane(l);
+    const int g4 = 4 * (ln >> 4), s0 = ln & 15;
+    const uint32_t xbase = (MAT ? st + C::S_QH : st + C::S_KH) + I * C::TD_TILE;
+    typename F::A fx[NKD], fb[NKD];
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) {
+      fx[m] = lds_ld<typename F::A>(smem, xbase + oTD[m]);
+      fb[m] = lds_ld<typename F::A>(smem, C::kb_td(st) + J * C::TD_TILE + oTD[m]);
+    }
+    f32x4 bet4 = zero4();
+    float bl = 0.f;
+    if constexpr (MAT == 0) bet4 = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * I + g4));
+    if constexpr (DIAG) bl = lds_ld<float>(smem, st + C::S_BETA + 4 * (16 * I + s0));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int m = 0; m < NKD; ++m) acc = F::mma(acc, fx[m], fb[m]);
+    if constexpr (MAT == 0 && !DIAG) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = -bet4[e] * acc[e];
+      put_frag(st + C::S_L + (I * (I - 1) / 2 + J) * C::FR16 + ln * 4 * C::ES, v);
+    } else if constexpr (MAT == 1) {
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (I > J || g4 + e >= s0) ? acc[e] : 0.f;
+      put_frag(st + C::S_P + ((J * NKT + I / C::JPB) * 64 + ln) * 16 + (I % C::JPB) * 4 * C::ES, v);
+    } else {
+      f32x4 at = zero4();
+#pragma unroll
+      for (int m = 0; m < NKD; ++m) at = F::mma(at, fb[m], fx[m]);
+      f32x4 Nt, Nn, Z;  // acc(N^T), acc(N), acc(T_ii)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Nn[e] = s0 < g4 + e ? bet4[e] * acc[e] : 0.f;  // N[16I + g4 + e][16I + s0]
+        Nt[e] = g4 + e < s0 ? bl * at[e] : 0.f;       // N[16I + s0][16I + g4 + e]
+        Z[e] = (g4 + e == s0 ? 1.f : 0.f) - Nn[e];
+      }
+      const f32x4 N2 = F::mma16(zero4(), F::a16(Nt), Nn);    // N N
+      const f32x4 Nt2 = F::mma16(zero4(), F::a16(Nn), Nt);   // N^T N^T
+      Z = F::mma16(Z, F::a16(Nt2), Z);                       // Z += N^2 Z
+      const f32x4 N4 = F::mma16(zero4(), F::a16(Nt2), N2);   // N^2 N^2
+      const f32x4 Nt4 = F::mma16(zero4(), F::a16(N2), Nt2);  // (N^T)^2 (N^T)^2
+      Z = F::mma16(Z, F::a16(Nt4), Z);                       // Z += N^4 Z
+      const f32x4 Nt8 = F::mma16(zero4(), F::a16(N4), Nt4);  // (N^T)^4 (N^T)^4
+      Z = F::mma16(Z, F::a16(Nt8), Z);                       // Z += N^8 Z
+      put_frag(st + C::S_TI + I * C::FR16 + ln * 4 * C::ES, Z);
+    }
+  }
+
+  // The same 20 tasks as the forward's (4 diagonal, 10 P, 6 off-diagonal L),
+  // with the same greedy balance over the waves.
+  static constexpr int task_i_bw(int K) {
+    if (K < 4) return K;
+    int k = K - 4;
+    if (k < 10) {
+      const int ii[10] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
+      return ii[k];
+    }
+    const int io[6] = {3, 3, 3, 2, 2, 1};
+    return io[k - 10];
+  }
+  static constexpr int task_j_bw(int K) {
+    if (K < 4) return K;
+    int k = K - 4;
+    if (k < 10) {
+      const int jj[10] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
+      return jj[k];
+    }
+    const int jo[6] = {2, 1, 0, 1, 0, 0};
+    return jo[k - 10];
+  }
+  template <int K>
+  __device__ __forceinline__ void p2_task_bw(uint32_t st) {
+    if constexpr (K < 20) {
+      constexpr int W = task_wave(K);
+      if (W == wave) p2_tile_bw<(K >= 4 && K < 14) ? 1 : 0, task_i_bw(K), task_j_bw(K)>(st);
+      p2_task_bw<K + 1>(st);
+    }
+  }
+
 
   // ------------------------------------------------------------ consumers
   __device__ __forceinline__ void init_offsets() {
@@ -553,8 +623,10 @@ struct ChunkKernel {
   // lane group g, reading channels 16ct + 4(i%4) .. +3 of token 32m + 16h + 4g +
   // i/4, receives tokens 32m + 16h + 4g + e of channel 16ct + i: half h of its
   // fragment.
-  __device__ __forceinline__ bf16x8 kbt_frag(uint32_t st, int ct, int m) const {
-    const uint32_t base = st + C::S_KB + oTR[ct >> 1] + 8u * (uint32_t)(ct & 1);
+  __device__ __forceinline__ bf16x8 kbt_frag(uint32_t st, int ct, int m) const { return tr_frag(st + C::S_KB, ct, m); }
+  // the same for any time-major [CH][D] tile of the stage at `tile`
+  __device__ __forceinline__ bf16x8 tr_frag(uint32_t tile, int ct, int m) const {
+    const uint32_t base = tile + oTR[ct >> 1] + 8u * (uint32_t)(ct & 1);
     const bf16x4 lo = lds_tr16(smem, base + (uint32_t)(2 * m) * C::TD_TILE);
     const bf16x4 hi = lds_tr16(smem, base + (uint32_t)(2 * m + 1) * C::TD_TILE);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -569,10 +641,11 @@ struct ChunkKernel {
   }
 
   // Lane l holds rows 16*ti + 4*(l/16) + e of its columns (accumulator layout).
-  __device__ __forceinline__ void load_v(VRaw& vr, int chunk) const {
+  __device__ __forceinline__ void load_v(VRaw& vr, int it) const {
     static_assert(NCT == (C::BF ? 2 : 1), "bf16 lanes own a column pair, fp32 lanes one column");
     const int ln = fresh_lane(l);
     const int g4 = 4 * (ln >> 4);
+    const int chunk = chunk_of(it);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
 #pragma unroll
@@ -751,7 +824,7 @@ struct ChunkKernel {
   }
 
   __device__ __forceinline__ void c2(uint32_t st, int chunk) {
-    if constexpr (PREFILL) {
+    if constexpr (PREFILL && !BWD) {
       c2_half<0>(st, chunk);
       c2_half<2>(st, chunk);
     }
@@ -818,7 +891,7 @@ struct ChunkKernel {
 
   // Snapshot after chunk cc when it closes a snapshot interval of the sequence.
   __device__ __forceinline__ void snapshot(int cc) const {
-    if constexpr (PREFILL) {
+    if constexpr (PREFILL && !BWD) {
       if (!snap_head) return;
       const int gc = chunk0 + cc + 1;
       if (gc % a.snap_chunks) return;
@@ -849,12 +922,139 @@ struct ChunkKernel {
     snapshot(cc);
   }
 
+  // Backward chain of one chunk (pipeline step cc, chunk chunk_of(cc)), run
+  // last chunk to first.  S holds dS', the gradient of the loss with respect
+  // to the chunk's end state (dS_T for the last chunk), for this wave's
+  // columns.  With the chunk's forward S' = Diag(Gam) (S + Kb^T Delta),
+  // (I + L) Delta = diag(b) (V - Kh S) and O = Qh S + P Delta, the chain rule
+  // gives, column by column (nothing here depends on the forward state):
+  //   dU = Diag(Gam) dS'                     (stored: the per-chunk gradients use it)
+  //   dDelta = Kb dU + P^T dO
+  //   Xbar = (I + L)^-T dDelta               (block back substitution with T_ii^T, L^T)
+  //   dS = dU + Qh^T dO - Kh^T diag(b) Xbar  (the gradient at the chunk's start)
+  // The value registers hold the chunk's dO rows (the v pointer is dO here).
+  __device__ __forceinline__ void chain_bw(VRaw& vr, int cc) {
+    if constexpr (BWD) {
+      const uint32_t st = stage(cc);
+      const int chunk = chunk_of(cc);
+      const int kk = 4 * (l >> 4);
+      // dO of the chunk as B fragments over its tokens
+      typename F::B dob[NCT][NKT];
+      {
+        f32x4 dt[NCT][4];
+#pragma unroll
+        for (int j = 0; j < NCT; ++j)
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dt[j][t][e] = vval(vr, j, 4 * t + e);
+#pragma unroll
+        for (int j = 0; j < NCT; ++j)
+#pragma unroll
+          for (int m = 0; m < NKT; ++m) dob[j][m] = F::bfrag(dt[j], m);
+      }
+      load_v(vr, cc + 1);
+      // dU = Diag(Gam) dS', in place, and stored for the per-chunk gradients
+#pragma unroll
+      for (int ci = 0; ci < D / 16; ++ci) {
+        const f32x4 gm = lds_ld<f32x4>(smem, st + C::S_GM + 4 * (16 * ci + kk));
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) S[j][ci] = S[j][ci] * gm;
+      }
+      store_state(a.dU_out + ((size_t)bh_seq * nch + chunk) * D * D, colb);
+#pragma unroll
+      for (int j = 0; j < NCT; ++j)
+#pragma unroll
+        for (int m = 0; m < NKD; ++m) sb[j][m] = F::bfrag(S[j], m);
+      // dDelta = Kb dU + P^T dO, row tile by row tile
+      f32x4 Xb[NCT][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        typename F::A fk[NKD], fp[NKT];
+#pragma unroll
+        for (int m = 0; m < NKD; ++m) fk[m] = ar<C::TD_TILE>(st + C::S_KB, oTD, t, m);
+#pragma unroll
+        for (int m = t / C::JPB; m < NKT; ++m)
+          fp[m] = lds_ld<typename F::A>(smem, st + C::S_P + ((t * NKT + m) * 64 + fresh_lane(l)) * 16);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int m = 0; m < NKD; ++m) acc = F::mma(acc, fk[m], sb[j][m]);
+#pragma unroll
+          for (int m = t / C::JPB; m < NKT; ++m) acc = F::mma(acc, fp[m], dob[j][m]);
+          Xb[j][t] = acc;
+        }
+      }
+      // Xbar_t = T_tt^T (dDelta_t - sum_{u > t} L_ut^T Xbar_u), from the last row tile
+      {
+        A16 ft[4], fl[4][4];
+        const uint32_t lo = (uint32_t)fresh_lane(l) * 4 * C::ES;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          ft[t] = lds_ld<A16>(smem, st + C::S_TI + t * C::FR16 + lo);
+#pragma unroll
+          for (int u = t + 1; u < 4; ++u)
+            fl[t][u] = lds_ld<A16>(smem, st + C::S_L + (u * (u - 1) / 2 + t) * C::FR16 + lo);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 3; t >= 0; --t) {
+#pragma unroll
+          for (int j = 0; j < NCT; ++j) {
+            f32x4 rr = Xb[j][t];
+#pragma unroll
+            for (int u = t + 1; u < 4; ++u) rr = F::mma16(rr, fl[t][u], Xb[j][u]);  // fl holds -L^T
+            Xb[j][t] = F::mma16(zero4(), ft[t], rr);
+          }
+        }
+      }
+      // -diag(b) Xbar as B fragments over the chunk's tokens
+      typename F::B yb[NCT][NKT];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f32x4 bet = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * t + kk));
+#pragma unroll
+        for (int j = 0; j < NCT; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Xb[j][t][e] = -bet[e] * Xb[j][t][e];
+      }
+#pragma unroll
+      for (int j = 0; j < NCT; ++j)
+#pragma unroll
+        for (int m = 0; m < NKT; ++m) yb[j][m] = F::bfrag(Xb[j], m);
+      // dS = dU + Qh^T dO + Kh^T (-diag(b) Xbar), state row tile by row tile
+#pragma unroll
+      for (int ci = 0; ci < D / 16; ++ci) {
+        typename F::A fq[NKT], fh[NKT];
+#pragma unroll
+        for (int m = 0; m < NKT; ++m) {
+          fq[m] = tr_frag(st + C::S_QH, ci, m);
+          fh[m] = tr_frag(st + C::S_KH, ci, m);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NKT; ++m)
+#pragma unroll
+          for (int j = 0; j < NCT; ++j) {
+            S[j][ci] = F::mma(S[j][ci], fq[m], dob[j][m]);
+            S[j][ci] = F::mma(S[j][ci], fh[m], yb[j][m]);
+          }
+      }
+    }
+  }
+
   // Segment pass: once a wave's map columns are all exactly zero they stay
   // zero for finite inputs (their value rows are zero, and every step of the
   // chain is linear in the columns it updates), so the wave stops running the
   // chain for them and keeps only its share of the score tiles.  The columns are
   // checked after every second chunk.
   __device__ __forceinline__ void chain_step(VRaw& vr, int cc) {
+    if constexpr (BWD) {
+      chain_bw(vr, cc);
+      return;
+    }
     if constexpr (!PREFILL) {
       if (mzero) return;
     }
@@ -958,6 +1158,7 @@ struct ChunkKernel {
     if ((W & 7) == 0) id = (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
     const int seq = id / a.vsplit;
     const int vs = id - seq * a.vsplit;
+    bh_seq = seq;
     const int gseg = seq / a.BH;
     const int bh = seq - gseg * a.BH;
     const int seg0 = a.t0 + gseg * a.Tseg;  // first token of this segment
@@ -976,22 +1177,28 @@ struct ChunkKernel {
     const uint32_t rowbytes = (uint32_t)Tlen * D * C::ES;
     const size_t base = tok0 * D * C::ES;
     rk = make_rsrc(reinterpret_cast<const char*>(a.k) + base, rowbytes);
-    rv = make_rsrc(reinterpret_cast<const char*>(a.v) + base, rowbytes);
+    // a missing v (the backward chain's dO may be absent) reads as zeros
+    rv = make_rsrc(a.v ? reinterpret_cast<const char*>(a.v) + base : nullptr, a.v ? rowbytes : 0u);
     rla = make_rsrc(reinterpret_cast<const char*>(a.la) + base, rowbytes);
     rbeta = make_rsrc(reinterpret_cast<const char*>(a.beta) + tok0 * C::ES, (uint32_t)Tlen * C::ES);
-    if constexpr (PREFILL) {
-      rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, rowbytes);
-      ro = make_rsrc(reinterpret_cast<const char*>(a.o) + base, rowbytes);
-    }
+    if constexpr (PREFILL) rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, rowbytes);
+    // without o (a forward pass run for its state checkpoints) every store is dropped
+    if constexpr (PREFILL && !BWD)
+      ro = make_rsrc(a.o ? reinterpret_cast<const char*>(a.o) + base : nullptr, a.o ? rowbytes : 0u);
 
     // Every LDS byte the kernel reads is written by it first, except the halves
     // of the 32-deep P lane slots that pair a diagonal tile with the tile above
-    // it (tiles (0,1) and (2,3)): nothing writes them, and they must hold the
-    // zeros of P's upper triangle.
+    // it (tiles (0,1) and (2,3); for the backward chain's P^T, tiles (1,0) and
+    // (3,2) of P^T): nothing writes them, and they must hold the zeros of P's
+    // upper triangle.
     if constexpr (PREFILL && C::JPB == 2) {
       for (uint32_t t = threadIdx.x; t < 2u * 64u * C::STAGES; t += C::THREADS) {
-        const uint32_t slot = (t & 64u) ? 2u * (CH / KB) + 1u : 0u;  // (I = 2, m = 1) or (I = 0, m = 0)
-        lds_st<u32x2>(smem, (t >> 7) * C::STAGE + C::S_P + (slot * 64u + (t & 63u)) * 16u + 8u, u32x2{0u, 0u});
+        // forward: slots (I = 2, m = 1) and (I = 0, m = 0), second half;
+        // backward: slots (J = 3, m = 1) and (J = 1, m = 0), first half
+        const uint32_t slot = BWD ? ((t & 64u) ? 3u * (CH / KB) + 1u : 1u * (CH / KB))
+                                  : ((t & 64u) ? 2u * (CH / KB) + 1u : 0u);
+        lds_st<u32x2>(smem, (t >> 7) * C::STAGE + C::S_P + (slot * 64u + (t & 63u)) * 16u + (BWD ? 0u : 8u),
+                      u32x2{0u, 0u});
       }
     }
 
@@ -1060,11 +1267,11 @@ struct ChunkKernel {
   }
 };
 
-template <typename T, int D, int NC, bool PREFILL>
+template <typename T, int D, int NC, bool PREFILL, bool BWD = false>
 __global__ __launch_bounds__(64 * (NC + D / 32), 1)
 void kda_chunk_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[ChunkCfg<T, D, NC, PREFILL>::LDS];
-  ChunkKernel<T, D, NC, PREFILL> kern;
+  ChunkKernel<T, D, NC, PREFILL, BWD> kern;
   kern.smem = smem;
   kern.a = a;
   kern.run();
@@ -1090,6 +1297,32 @@ static hipError_t launch_nc(const ChunkArgs& a, int nc, int nwg, hipStream_t str
       else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int D, int NC>
+static hipError_t launch_bwd_one(const ChunkArgs& a, int nwg, hipStream_t stream) {
+  using Cf = ChunkCfg<bf16, D, NC, true>;
+  hipLaunchKernelGGL((kda_chunk_kernel<bf16, D, NC, true, true>), dim3(nwg), dim3(Cf::THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd(const ChunkArgs& a, int D, int nc, int nwg, hipStream_t stream) {
+  if (D == 128) {
+    switch (nc) {
+      case 1: return launch_bwd_one<128, 1>(a, nwg, stream);
+      case 2: return launch_bwd_one<128, 2>(a, nwg, stream);
+      case 4: return launch_bwd_one<128, 4>(a, nwg, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (D == 64) {
+    switch (nc) {
+      case 1: return launch_bwd_one<64, 1>(a, nwg, stream);
+      case 2: return launch_bwd_one<64, 2>(a, nwg, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_chunk(const ChunkArgs& a, bool bf16_io, int D, bool prefill, int nc, int nwg,

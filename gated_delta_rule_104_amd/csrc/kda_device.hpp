@@ -135,4 +135,49 @@ static_assert(kpos(0) == 0 && kpos(3) == 3 && kpos(4) == 8 && kpos(16) == 4 && k
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// ---------------------------------------------------------------------------
+// Buffer resources, DPP row moves and raw 16-byte row loads.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer over [p, p + bytes): loads past the end return 0, stores are dropped.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// DPP moves within rows of 16 lanes (gfx9 encoding): row_shr:n shifts values
+// n lanes up inside the row; lanes below n read 0 (bound control), so no old
+// value has to be materialised.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int DPP_ROW_SHR = 0x110;
+
+// 8 consecutive elements of a token row, as loaded from HBM.
+template <typename T> struct Raw8 { u32x4 p[sizeof(T) / 2]; };
+
+template <typename T>
+__device__ __forceinline__ void raw_load(Raw8<T>& r, rsrc_t rs, uint32_t off) {
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 2); ++i) r.p[i] = bload128(rs, off + 16 * i);
+}
+
+template <typename T>
+__device__ __forceinline__ void raw_f32(const Raw8<T>& r, float* out) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(r.p[0][i] << 16);
+      out[2 * i + 1] = __uint_as_float(r.p[0][i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = __uint_as_float(r.p[i >> 2][i & 3]);
+  }
+}
+
+
 }  // namespace kda

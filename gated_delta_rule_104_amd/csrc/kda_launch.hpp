@@ -38,7 +38,14 @@ struct ChunkArgs {
   // segment pass: a wave stops updating its map columns once they are all
   // exactly zero (they stay zero for finite inputs); 0 keeps updating them
   int map_skip = 1;
+  // backward chain only: dU = Diag(Gam) dS' of every chunk, [BH, nch, D, D] fp32
+  float* dU_out = nullptr;
 };
+
+// Reverse chain of the prefill gradients (bf16 inputs, one segment per head):
+// S0 = dS_T [BH, D, D] or null, S_out = dS0, v = dO, dU_out as above; nc
+// consumer waves per workgroup ({1, 2, 4} at D = 128, {1, 2} at D = 64).
+hipError_t launch_chunk_bwd(const ChunkArgs& a, int D, int nc, int nwg, hipStream_t stream);
 
 // 16-column state tiles each consumer wave of the chunk kernel owns.
 inline int chunk_tiles_per_wave(bool bf16_io) { return bf16_io ? 2 : 1; }
@@ -81,6 +88,31 @@ struct BackwardArgs {
   int T;
 };
 size_t backward_ws_floats(long long BH, int T, int D);
+
+// Per-chunk gradients of the prefill (bf16 inputs), one workgroup per
+// (head, chunk): from the chunk's start state (S0 for chunk 0, else the
+// forward's checkpoint after the previous chunk) and dU = Diag(Gam) dS' of the
+// chunk (from the reverse chain).
+struct BwGradArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* la;
+  const void* beta;
+  const void* dO;      // [BH, T, D] or null (= 0)
+  const float* S0;     // [BH, D, D] or null (= 0)
+  const float* ckpt;   // [B, nckpt, H, D, D]: state after chunk j at index j
+  int nckpt;
+  int H;
+  const float* dU;     // [BH, nch, D, D]
+  float* dq;           // [BH, T, D]
+  float* dk;
+  float* dv;
+  float* dla;
+  float* dbeta;        // [BH, T]
+  int T;
+};
+hipError_t launch_bwgrad(const BwGradArgs& a, int BH, int D, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, int split, hipStream_t stream);
 
 hipError_t launch_merge(const float* S_in, const float* Z, const float* M, float* S_start,

@@ -248,23 +248,31 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
  * Gradients of the prefill, for training (the K3 report credits FlashKDA with
  * faster training as well as inference: myzaker "Kimi K3 开源日来了", section
  * "FlashKDA").  For a loss L with dL/do = dO and dL/dS_T = dS_T this computes
- * the gradients with respect to every input of kda_chunk_prefill, by running
- * the recurrence's token steps backwards (reverse-mode chain rule), token by
- * token, one workgroup per head.
+ * the gradients with respect to every input of kda_chunk_prefill
+ * (reverse-mode chain rule).
  *   q, k, v, log_alpha, beta, S0 : as for kda_chunk_prefill (S0 NULL = zero)
  *   dO   : [B, H, T, dv] dtype, or NULL (= 0)
  *   dS_T : [B, H, dk, dv] fp32, or NULL (= 0)
  *   dq, dk_, dlog_alpha : [B, H, T, dk] fp32;  dv_ : [B, H, T, dv] fp32;
  *   dbeta : [B, H, T] fp32;  dS0 : [B, H, dk, dv] fp32.
- * The workspace (device memory, at least kda_backward_workspace_bytes, 16-byte
- * aligned) holds a state checkpoint every 64 tokens, and the entering states
- * and the vectors u = (Diag(alpha) S)^T k of one 64-token interval, per head;
- * its contents on return are undefined.  No
- * output may alias an input or the workspace.  Errors: KDA_ERR_NULL for a
- * missing required pointer, KDA_ERR_WORKSPACE for a missing workspace or one
- * below the required size.
+ * bf16 inputs run in the chunked form, on the matrix cores (bf16 operands,
+ * fp32 accumulation): a forward pass that keeps the state after every 64-token
+ * chunk, beside it the reverse chain over the chunks (dS' -> dS, which needs
+ * no forward state), then every (head, chunk)'s gradients in parallel.  fp32
+ * inputs run the recurrence's token steps backwards in fp32, token by token,
+ * one workgroup (or two, each with half of the state's columns) per head.
+ * The workspace (device memory, at least kda_backward_workspace_bytes for the
+ * same dtype, 16-byte aligned) holds, for bf16, the state after every whole
+ * chunk and dU = Diag(Gam) dS' of every chunk (fp32, 64 KiB per chunk-head at
+ * d = 128 each); for fp32, a state checkpoint every 64 tokens, the entering
+ * states and vectors u = (Diag(alpha) S)^T k of one 64-token interval, per
+ * head, and the two halves' row sums.  Its contents on return are undefined.
+ * No output may alias an input or the workspace.  The bf16 path forks part of
+ * its work to the same per-caller-stream side stream as the sequence-split
+ * prefill.  Errors: KDA_ERR_NULL for a missing required pointer,
+ * KDA_ERR_WORKSPACE for a missing workspace or one below the required size.
  */
-size_t kda_backward_workspace_bytes(int B, int H, int T, int dk, int dv);
+size_t kda_backward_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtype dtype);
 kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const void* log_alpha,
                                 const void* beta, const float* S0, const void* dO, const float* dS_T,
                                 float* dq, float* dk_, float* dv_, float* dlog_alpha, float* dbeta,

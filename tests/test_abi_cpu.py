@@ -219,21 +219,28 @@ def backward(lib, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, dO=FAKE, 
              dq=FAKE, dk=FAKE, dv=FAKE, dla=FAKE, db=FAKE, dS0=FAKE, B=1, H=1, T=64, D=64, dt=BF16,
              ws=FAKE, ws_bytes=None):
     if ws_bytes is None:
-        ws_bytes = lib.kda_backward_workspace_bytes(B, H, T, D, D)
+        ws_bytes = lib.kda_backward_workspace_bytes(B, H, T, D, D, dt)
     return lib.kda_prefill_backward(*P(q, k, v, la, beta, S0, dO, dST, dq, dk, dv, dla, db, dS0),
                                     B, H, T, D, D, dt, ctypes.c_void_p(ws) if ws else None, ws_bytes, None)
 
 
 def test_backward_workspace_query(lib):
-    """A checkpoint every 64 tokens plus 64 entering states (fp32 D x D) and 64
+    """bf16 (chunked form): the state after every whole chunk, dU of every chunk
+    and one discarded end state, fp32 D x D each per head.  fp32 (token steps):
+    a checkpoint every 64 tokens plus 64 entering states (fp32 D x D) and 64
     fp32 D-vectors per head, then two halves of every token's row sums (dq, dk,
     dlog_alpha, dbeta: 3D + 1 floats)."""
     q = lib.kda_backward_workspace_bytes
     q.restype = ctypes.c_size_t
-    assert q(1, 1, 64, 64, 64) == ((1 + 64) * 64 * 64 + 64 * 64 + 2 * 64 * (3 * 64 + 1)) * 4
-    assert q(2, 3, 65, 128, 128) == 6 * ((2 + 64) * 128 * 128 + 64 * 128 + 2 * 65 * (3 * 128 + 1)) * 4
-    assert q(1, 1, 0, 64, 64) == (64 * 64 * 64 + 64 * 64) * 4
-    assert q(1, 1, 64, 64, 128) == 0 and q(1, 1, 64, 96, 96) == 0 and q(0, 1, 64, 64, 64) == 0
+    assert q(1, 1, 64, 64, 64, F32) == ((1 + 64) * 64 * 64 + 64 * 64 + 2 * 64 * (3 * 64 + 1)) * 4
+    assert q(2, 3, 65, 128, 128, F32) == 6 * ((2 + 64) * 128 * 128 + 64 * 128 + 2 * 65 * (3 * 128 + 1)) * 4
+    assert q(1, 1, 0, 64, 64, F32) == (64 * 64 * 64 + 64 * 64) * 4
+    assert q(1, 1, 64, 64, 64, BF16) == (1 + 1 + 1) * 64 * 64 * 4
+    assert q(2, 3, 65, 128, 128, BF16) == 6 * (1 + 2 + 1) * 128 * 128 * 4
+    assert q(4, 32, 8192, 128, 128, BF16) == 128 * (128 + 128 + 1) * 128 * 128 * 4
+    assert q(1, 1, 0, 64, 64, BF16) == 64 * 64 * 4
+    assert q(1, 1, 64, 64, 128, BF16) == 0 and q(1, 1, 64, 96, 96, F32) == 0 and q(0, 1, 64, 64, 64, BF16) == 0
+    assert q(1, 1, 64, 64, 64, 5) == 0
 
 
 def test_backward_validation(lib):

@@ -3,8 +3,9 @@ C-ABI) against the fp64 oracle's reverse-mode gradients.
 
 The loss is L = sum(dO * o) + sum(dS_T * S_T) with seeded random dO and dS_T.
 Errors are the largest relative L2 error over (b, h) slices, per gradient; the
-bars are those of the forward outputs (1e-4 for fp32 inputs, 2e-2 for bf16
-inputs), although the kernel evaluates every step in fp32 on both.
+bars are those of the forward outputs: 1e-4 for fp32 inputs (the token-step
+kernel, every step in fp32) and 2e-2 for bf16 inputs (the chunked form on the
+matrix cores: bf16 operands, fp32 accumulation, like the forward).
 """
 import numpy as np
 import pytest
@@ -91,10 +92,11 @@ def test_backward_many_intervals():
 
 
 @pytest.mark.parametrize("split", ["1", "2"])
-@pytest.mark.parametrize("dtype,D,T", [("bf16", 128, 130), ("f32", 64, 100)])
+@pytest.mark.parametrize("dtype,D,T", [("f32", 128, 130), ("f32", 64, 100)])
 def test_backward_split_choice(split, dtype, D, T, kda_opts):
-    """One workgroup per head, or two each owning half of the state's columns
-    (their row sums added by a second kernel): both match the oracle."""
+    """fp32 token-step kernel: one workgroup per head, or two each owning half
+    of the state's columns (their row sums added by a second kernel): both match
+    the oracle."""
     kda_opts("bw_split", int(split))
     err = grads_case(1, 3, T, D, dtype, 98, variant="slow")
     assert max(err.values()) <= TOL[dtype], err
@@ -157,3 +159,57 @@ def test_backward_full_b4_h32_t8k():
             err[n] = oracle.max_rel_l2(got, ref[n], 2 if n != "dbeta" else 1, floor=1e-6)
         print(f"    head ({b},{h}) " + "  ".join(f"{k} {v:.2e}" for k, v in err.items()), flush=True)
         assert max(err.values()) <= TOL["bf16"], err
+
+
+# ----------------------------------------------------------------- chunked form (bf16)
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 128, 200, 1000])
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_chunked_tails(T, D):
+    """Ragged last chunks, one to sixteen chunks, both head sizes."""
+    err = grads_case(1, 2, T, D, "bf16", 300 + T, variant="slow")
+    assert max(err.values()) <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("variant", ["none", "alpha_one", "alpha_min", "beta_zero", "beta_one"])
+def test_backward_chunked_gates(variant):
+    """The workloads' gates, no decay, the lower bound log alpha = -1, beta = 0
+    (dk and dv are then exactly zero) and beta = 1."""
+    err = grads_case(2, 2, 300, 128, "bf16", 310, variant=variant)
+    assert max(err.values()) <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("with_dO,with_dST", [(True, False), (False, True)])
+def test_backward_chunked_one_loss_term(with_dO, with_dST):
+    """Only the outputs, or only the end state, carry the loss (dO or dS_T NULL)."""
+    err = grads_case(1, 3, 260, 128, "bf16", 320, variant="slow", with_dO=with_dO, with_dST=with_dST)
+    assert max(err.values()) <= TOL["bf16"], err
+
+
+def test_backward_chunked_zero_tokens():
+    """T = 0 on the chunked path: dS0 = dS_T exactly."""
+    B, H, D = 2, 2, 128
+    e = torch.empty(B, H, 0, D, dtype=torch.bfloat16, device=dev())
+    beta = torch.empty(B, H, 0, dtype=torch.bfloat16, device=dev())
+    dST = torch.randn(B, H, D, D, device=dev())
+    out = kda.prefill_backward(e, e, e, e, beta, None, None, dST)
+    torch.cuda.synchronize()
+    assert torch.equal(out["dS0"], dST)
+
+
+@pytest.mark.parametrize("nc", [1, 2, 4])
+def test_backward_chunked_column_split_invariant(nc, kda_opts):
+    """The reverse chain's consumer-wave count (state columns per workgroup)
+    changes the launch, not the result."""
+    d = ki.gen_prefill(1, 2, 200, 128, 128, "bf16", seed=330, s0_std=0.1, variant="slow")
+    g = {n: (x.to(dev()) if x is not None else None) for n, x in d.items()}
+    dO = torch.randn(1, 2, 200, 128, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).to(dev())
+    dST = torch.randn(1, 2, 128, 128, generator=torch.Generator().manual_seed(4)).to(dev())
+    args = (g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], dO, dST)
+    kda_opts("nc", nc)
+    a = kda.prefill_backward(*args)
+    kda_opts("nc", None)
+    b = kda.prefill_backward(*args)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
