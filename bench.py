@@ -271,22 +271,32 @@ def bench_prefill_slow_decay(args, dev):
 
 def backward_bytes(B, H, T, D):
     """Algorithmic bytes of kda_prefill_backward with bf16 inputs: q, k, v,
-    log_alpha, dO (2 B x D each) and beta read per token-head; dq, dk, dv,
-    dlog_alpha (4 B x D each) and dbeta written; S0 and dS_T read and dS0
-    written per head.  The workspace's checkpoints are not counted."""
-    return B * H * T * (2 * 5 * D + 2 + 4 * 4 * D + 4) + 3 * B * H * D * D * 4
+    log_alpha, dO (2 B x D each) and beta read once per token-head; dq, dk, dv,
+    dlog_alpha (2 B x D each, the inputs' dtype) and dbeta written once; S0 and
+    dS_T read and dS0 written (fp32) per head.  The checkpoints the three
+    kernels pass to each other through the workspace are not counted."""
+    return B * H * T * (2 * 5 * D + 2 + 2 * 4 * D + 2) + 3 * B * H * D * D * 4
 
 
-PEAK_F32_TFLOPS = 157.3
-
-
-def backward_flops(B, H, T, D):
-    """fp32 arithmetic of one gradient evaluation per token-head: the forward
-    step (decay, u = D^T k, the rank-1 update: 5 D^2) that rebuilds the entering
-    state, and the backward step (decay, u and d_delta, dq, the two dS updates,
-    dk's two terms, dlog_alpha, the decay of dS: 20 D^2).  The kernel's second
-    forward pass over each interval (checkpoint recompute) is not counted."""
-    return B * H * T * 25 * D * D
+def backward_flops(B, H, T, D, C=CH):
+    """Matrix flops the chunked backward issues per call, on dense 16x16 tiles
+    (triangles and the 16-row diagonal blocks counted whole):
+      forward checkpoint pass per chunk-head: scores Kh Kb^T (2C^2K), Kh S and
+        Kb^T Delta (2CKV each), the 16-row block solve (C^2 V);
+      reverse chain: scores L and P (2C^2K each), Kb dU and Qh^T dO and
+        Kh^T Xbar (2CKV each), P^T dO (2C^2V), the block solve (C^2 V);
+      per-chunk gradients: L both ways and P (3 x 2C^2K), Kh S, Kb dU (2CKV
+        each), P^T dO (2C^2V), both solves (2 C^2 V), the five 64x64 products
+        dP, dP^T, Abar, Abar^T, Kh Kb^T (5 x 2C^2V), dO S^T, Xbar S^T,
+        Delta dU^T (3 x 2CKV), and the four products with the 64x64 gradients,
+        each run twice on split operands (8 x 2C^2K)."""
+    K = V = D
+    fwd = 2 * C * C * K + 2 * (2 * C * K * V) + C * C * V
+    chain = 2 * (2 * C * C * K) + 3 * (2 * C * K * V) + 2 * C * C * V + C * C * V
+    grads = 3 * (2 * C * C * K) + 2 * (2 * C * K * V) + 2 * C * C * V + 2 * C * C * V + 5 * (2 * C * C * V) \
+        + 3 * (2 * C * K * V) + 8 * (2 * C * C * K)
+    nchunks = -(-T // C)
+    return B * H * nchunks * (fwd + chain + grads)
 
 
 def bench_backward(args, dev):
@@ -303,7 +313,8 @@ def bench_backward(args, dev):
     def call():
         kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], dO, dST, workspace=ws)
 
-    call()
+    for _ in range(3):
+        call()
     torch.cuda.synchronize()
     ms, _ = time_launches(call, MIN_TIMED)
     nbytes = backward_bytes(B, H, T, D)
@@ -311,8 +322,9 @@ def bench_backward(args, dev):
     del g, dO, ws
     return {"B": B, "H": H, "T": T, "D": D, "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
             "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "bound": "alu", "alu_tflops": fl / (ms * 1e-3) / 1e12,
-            "alu_frac": fl / (ms * 1e-3) / 1e12 / PEAK_F32_TFLOPS, "alu_peak_tflops": PEAK_F32_TFLOPS}
+            "bound": "mfma", "issued_mfma_tflops": fl / (ms * 1e-3) / 1e12,
+            "mfma_frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
+            "kernels": "forward checkpoint pass beside the reverse chain, then per-chunk gradients"}
 
 
 def bench_snapshots(pf, args, interval=512):

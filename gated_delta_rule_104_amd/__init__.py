@@ -397,8 +397,8 @@ def backward_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype: to
 
 def prefill_backward(q, k, v, log_alpha, beta, S0=None, dO=None, dS_T=None, workspace=None):
     """Gradients of L = sum(dO * o) + sum(dS_T * S_T) of the prefill with respect
-    to its inputs.  Returns a dict of fp32 tensors: dq, dk, dlog_alpha [B,H,T,dk],
-    dv [B,H,T,dv], dbeta [B,H,T], dS0 [B,H,dk,dv]."""
+    to its inputs.  Returns a dict: dq, dk, dlog_alpha [B,H,T,dk], dv [B,H,T,dv],
+    dbeta [B,H,T] in the inputs' dtype, and dS0 [B,H,dk,dv] fp32."""
     B, H, T, dk = k.shape
     dv = v.shape[-1]
     dt = k.dtype
@@ -414,10 +414,10 @@ def prefill_backward(q, k, v, log_alpha, beta, S0=None, dO=None, dS_T=None, work
     if dS_T is not None:
         _io(dS_T, "dS_T", torch.float32, (B, H, dk, dv))
     dev = k.device
-    f32 = dict(dtype=torch.float32, device=dev)
-    out = dict(dq=torch.empty(B, H, T, dk, **f32), dk=torch.empty(B, H, T, dk, **f32),
-               dv=torch.empty(B, H, T, dv, **f32), dlog_alpha=torch.empty(B, H, T, dk, **f32),
-               dbeta=torch.empty(B, H, T, **f32), dS0=torch.empty(B, H, dk, dv, **f32))
+    io = dict(dtype=dt, device=dev)
+    out = dict(dq=torch.empty(B, H, T, dk, **io), dk=torch.empty(B, H, T, dk, **io),
+               dv=torch.empty(B, H, T, dv, **io), dlog_alpha=torch.empty(B, H, T, dk, **io),
+               dbeta=torch.empty(B, H, T, **io), dS0=torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev))
     need = backward_workspace_bytes(B, H, T, dk, dv, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)

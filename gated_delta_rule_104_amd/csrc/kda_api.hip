@@ -307,7 +307,7 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
                                   const void* beta, const float* Sst, void* o, float* S_T,
                                   long long BH, int T, int t0, int Tend, int Tseg, int D, bool bf,
                                   hipStream_t stream, const char* what, const Snap& sn = Snap(),
-                                  int nc = 0) {
+                                  int nc = 0, kda::bf16* ck_rows = nullptr, kda::bf16* ck_cols = nullptr) {
   const int n = Tend - t0;
   const int G = n > 0 ? (int)(((long long)n + Tseg - 1) / Tseg) : 1;  // no tokens: copy the start state
   const long long nseq = BH * G;
@@ -320,6 +320,7 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
   a.vsplit = nt / (nc * kda::chunk_tiles_per_wave(bf));
   a.snap = sn.n > 0 ? sn.p : nullptr; a.snap_chunks = sn.chunks > 0 ? sn.chunks : 1;
   a.nsnap = sn.n; a.H = sn.H;
+  a.ck_rows = ck_rows; a.ck_cols = ck_cols;
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (log_on())
@@ -546,13 +547,13 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
   return st == KDA_OK ? ok() : st;
 }
 
-// Workspace of the chunked backward (bf16 inputs), fp32: the forward's state
-// after every whole chunk ([B, T / 64, H, D, D], the layout of the prefill's
-// snapshots), dU = Diag(Gam) dS' of every chunk ([BH, nch, D, D]), and the
-// forward pass's end state, which is not needed ([BH, D, D]).
+// Workspace of the chunked backward (bf16 inputs): the start state of every
+// chunk and dU = Diag(Gam) dS' of every chunk, each as two bf16 [BH, nch, D, D]
+// matrices (row-major and transposed, kpos-ordered rows), then the forward
+// pass's end state, which is not needed (fp32 [BH, D, D]).  In floats.
 size_t chunk_bw_ws_floats(long long BH, int T, int D) {
   const long long nch = (T + 63) / 64;
-  return (size_t)(BH * (T / 64) + BH * nch + BH) * D * D;
+  return (size_t)(2 * BH * nch + BH) * D * D;
 }
 
 // Gradients of the prefill in the chunked form (bf16 inputs; arguments already
@@ -563,21 +564,24 @@ size_t chunk_bw_ws_floats(long long BH, int T, int D) {
 //     dU = Diag(Gam) dS' of every chunk and dS0 (it needs no forward state);
 //  2. the per-chunk gradients, one workgroup per (head, chunk).
 kda_status chunk_backward(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
-                          const float* S0, const void* dO, const float* dS_T, float* dq, float* dk_, float* dv_,
-                          float* dlog_alpha, float* dbeta, float* dS0, int B, int H, int T, int D, float* ws,
+                          const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
+                          void* dlog_alpha, void* dbeta, float* dS0, int B, int H, int T, int D, float* ws,
                           hipStream_t stream) {
   const long long BH = (long long)B * H;
   const long long nch = (T + 63) / 64;
-  const size_t nS = (size_t)D * D;
-  float* ckpt = ws;                          // [B, T / 64, H, D, D]
-  float* dU = ckpt + (size_t)BH * (T / 64) * nS;  // [BH, nch, D, D]
-  float* ST = dU + (size_t)BH * nch * nS;    // [BH, D, D], discarded
+  const size_t nS = (size_t)BH * nch * D * D;  // elements of one checkpoint array
+  kda::bf16* S_rows = reinterpret_cast<kda::bf16*>(ws);
+  kda::bf16* S_cols = S_rows + nS;
+  kda::bf16* dU_rows = S_cols + nS;
+  kda::bf16* dU_cols = dU_rows + nS;
+  float* ST = reinterpret_cast<float*>(dU_cols + nS);  // [BH, D, D], discarded
   const int nt = D / 16;
   kda::ChunkArgs r;
   r.q = q; r.k = k; r.v = dO; r.la = log_alpha; r.beta = beta;
   r.S0 = dS_T; r.o = nullptr; r.S_out = dS0; r.M_out = nullptr;
   r.BH = (int)BH; r.G = 1; r.Tseg = T > 0 ? T : 1; r.Ttot = T; r.t0 = 0; r.Tend = T;
-  r.dU_out = dU;
+  r.dU_rows = dU_rows;
+  r.dU_cols = dU_cols;
   // The forward pass and the reverse chain run side by side: their column
   // split is chosen so that both together fill the chip once.
   const int ncb = pick_nc(2 * BH, nt, true);
@@ -599,13 +603,8 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
     std::lock_guard<std::mutex> lk(ss->mu);
     if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess || (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
       return hip_fail(e, "kda_prefill_backward fork");
-    Snap sn;
-    sn.p = ckpt;
-    sn.chunks = 1;
-    sn.n = T / 64;
-    sn.H = H;
     st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, nullptr, ST, BH, T, 0, T, T, D, true, ss->s,
-                                "kda_prefill_backward forward checkpoints", sn, ncb);
+                                "kda_prefill_backward forward checkpoints", Snap(), ncb, S_rows, S_cols);
     if (st == KDA_OK && (e = kda::launch_chunk_bwd(r, D, ncb, (int)(BH * r.vsplit), stream)) != hipSuccess)
       st = hip_fail(e, "kda_prefill_backward reverse chain");
     // join even if a launch above failed, so the side stream's work is waited for
@@ -614,9 +613,10 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
     if (st != KDA_OK) return st;
   }
   kda::BwGradArgs g;
-  g.q = q; g.k = k; g.v = v; g.la = log_alpha; g.beta = beta; g.dO = dO; g.S0 = S0;
-  g.ckpt = ckpt; g.nckpt = T / 64; g.H = H; g.dU = dU;
-  g.dq = dq; g.dk = dk_; g.dv = dv_; g.dla = dlog_alpha; g.dbeta = dbeta; g.T = T;
+  g.q = q; g.k = k; g.v = v; g.la = log_alpha; g.beta = beta; g.dO = dO;
+  g.S_rows = S_rows; g.S_cols = S_cols; g.dU_rows = dU_rows; g.dU_cols = dU_cols;
+  g.dq = static_cast<kda::bf16*>(dq); g.dk = static_cast<kda::bf16*>(dk_); g.dv = static_cast<kda::bf16*>(dv_);
+  g.dla = static_cast<kda::bf16*>(dlog_alpha); g.dbeta = static_cast<kda::bf16*>(dbeta); g.T = T;
   if ((e = kda::launch_bwgrad(g, (int)BH, D, stream)) != hipSuccess) return hip_fail(e, "kda_prefill_backward gradients");
   return ok();
 }
@@ -787,7 +787,7 @@ size_t kda_backward_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dty
 
 kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const void* log_alpha,
                                 const void* beta, const float* S0, const void* dO, const float* dS_T,
-                                float* dq, float* dk_, float* dv_, float* dlog_alpha, float* dbeta,
+                                void* dq, void* dk_, void* dv_, void* dlog_alpha, void* dbeta,
                                 float* dS0, int B, int H, int T, int dk, int dv, kda_dtype dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || H < 0 || T < 0) return fail(KDA_ERR_SHAPE, "negative size B=%d H=%d T=%d", B, H, T);
@@ -824,7 +824,8 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
                                 T, dk, static_cast<float*>(workspace), stream);
   kda::BackwardArgs a;
   a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta; a.S0 = S0; a.dO = dO; a.dS_T = dS_T;
-  a.dq = dq; a.dk = dk_; a.dv = dv_; a.dla = dlog_alpha; a.dbeta = dbeta; a.dS0 = dS0;
+  a.dq = static_cast<float*>(dq); a.dk = static_cast<float*>(dk_); a.dv = static_cast<float*>(dv_);
+  a.dla = static_cast<float*>(dlog_alpha); a.dbeta = static_cast<float*>(dbeta); a.dS0 = dS0;
   a.ws = static_cast<float*>(workspace);
   a.T = T;
   // two workgroups per head (each with half of the state's columns) when that

@@ -99,7 +99,7 @@ struct GradKernel {
   BwGradArgs a;
   int wave, l, g4, s0;
   int nrows;  // valid tokens of this chunk
-  rsrc_t rq, rk, rv, rla, rbeta, rdo, rdq, rdk, rdv, rdla, rdb, rS, rU;
+  rsrc_t rq, rk, rv, rla, rbeta, rdo, rdq, rdk, rdv, rdla, rSr, rSc, rUr, rUc;
   uint32_t oTD[NKD];   // A fragments of [64][D] tiles, row tile 0
   int tr_f, tr_q;      // transposing reads: the lane's row and channel quad
 
@@ -339,26 +339,16 @@ struct GradKernel {
   // accumulator tile, rows 16t + 4g + e of column c_j = 16 ct + l%16.
   __device__ __forceinline__ int col(int j) const { return 16 * (NCT * wave + j) + s0; }
 
-  // fp32 state columns as B fragments over the state's rows (channels)
-  __device__ __forceinline__ void state_cols(rsrc_t r, bf16x8 (*out)[NKD]) const {
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      f32x4 t[D / 16];
-#pragma unroll
-      for (int ci = 0; ci < D / 16; ++ci)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          t[ci][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              r, (uint32_t)((16 * ci + g4 + e) * D + col(j)) * 4u, 0, 0));
-#pragma unroll
-      for (int m = 0; m < NKD; ++m) out[j][m] = pack8(t[2 * m], t[2 * m + 1]);
-    }
+  // Row c of a checkpoint matrix stored with kpos-ordered rows (the state's
+  // columns, or dU's), k block m: one 16-byte read is the B fragment over that
+  // block (from the transposed copy: column c of the matrix over its rows).
+  __device__ __forceinline__ bf16x8 ck_frag(rsrc_t r, int c, int m) const {
+    return __builtin_bit_cast(bf16x8, bload128(r, (uint32_t)(c * D + 32 * m + 2 * g4) * 2u));
   }
 
-  // bf16 value at (row, column) of the chunk's [64][D] input
-  __device__ __forceinline__ float in_val(rsrc_t r, int row, int c) const {
-    return __uint_as_float((uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
-                               r, (uint32_t)(row * D + c) * 2u, 0, 0) << 16);
+  // one gradient, rounded to bf16, at (row, column) of the chunk's [64][D] output
+  __device__ __forceinline__ static void st_bf16(rsrc_t r, int row, int c, float x) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)x), r, (uint32_t)(row * D + c) * 2u, 0, 0);
   }
 
   // sum over the 16 lanes of each lane row; lane 15 of the row holds it
@@ -380,9 +370,54 @@ struct GradKernel {
           lds_st<bf16>(smem, tile + td(16 * t + g4 + e, 2 * kpos(col(j))), (bf16)x[j][t][e]);
   }
 
-  __device__ __forceinline__ void phase3() {
-    bf16x8 sb[NCT][NKD];
-    state_cols(rS, sb);
+  // Global data of phases 3 and 5, loaded one phase ahead so that the loads
+  // are in flight across the preceding phase (the barriers wait only for LDS).
+  // bf16 values at this lane's accumulator positions (rows 16t + 4g + e of its
+  // columns) are kept as raw 16-bit loads.
+  struct Pre3 {
+    bf16x8 sb[NCT][NKD], ub[NCT][NKD];  // S and dU columns as B fragments over their rows
+    uint32_t v[NCT][16];
+  };
+  struct Pre5 {
+    bf16x8 sr[NCT][NKD], ur[NCT][NKD];  // S and dU rows as B fragments over their columns
+    uint32_t la[NCT][16], q[NCT][16], k[NCT][16];
+  };
+  __device__ __forceinline__ uint32_t raw16(rsrc_t r, int row, int c) const {
+    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)(row * D + c) * 2u, 0, 0);
+  }
+  __device__ __forceinline__ static float f16raw(uint32_t x) { return __uint_as_float(x << 16); }
+  __device__ __forceinline__ void load_pre3(Pre3& p) const {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+#pragma unroll
+      for (int m = 0; m < NKD; ++m) {
+        p.sb[j][m] = ck_frag(rSc, col(j), m);
+        p.ub[j][m] = ck_frag(rUc, col(j), m);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p.v[j][i] = raw16(rv, 16 * (i >> 2) + g4 + (i & 3), col(j));
+    }
+  }
+  __device__ __forceinline__ void load_pre5(Pre5& p) const {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+#pragma unroll
+      for (int m = 0; m < NKD; ++m) {
+        p.sr[j][m] = ck_frag(rSr, col(j), m);
+        p.ur[j][m] = ck_frag(rUr, col(j), m);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 16 * (i >> 2) + g4 + (i & 3);
+        p.la[j][i] = raw16(rla, row, col(j));
+        p.q[j][i] = raw16(rq, row, col(j));
+        p.k[j][i] = raw16(rk, row, col(j));
+      }
+    }
+  }
+
+  __device__ __forceinline__ void phase3(const Pre3& p) {
+    const auto& sb = p.sb;
     // W = V - Kh S, from -V
     f32x4 X[NCT][4];
 #pragma unroll
@@ -390,7 +425,7 @@ struct GradKernel {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) X[j][t][e] = -in_val(rv, 16 * t + g4 + e, col(j));
+        for (int e = 0; e < 4; ++e) X[j][t][e] = -f16raw(p.v[j][4 * t + e]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       bf16x8 fk[NKD];
@@ -436,8 +471,7 @@ struct GradKernel {
     }
     store_tile_lds(C::DL, Dl);
     // dDelta = Kb dU + P^T dO
-    bf16x8 ub[NCT][NKD];
-    state_cols(rU, ub);
+    const auto& ub = p.ub;
     bf16x8 dob[NCT][NKT];
 #pragma unroll
     for (int j = 0; j < NCT; ++j)
@@ -491,8 +525,7 @@ struct GradKernel {
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bet[e] * Xb[j][t][e]), rdv,
-                                                (uint32_t)(row * D + col(j)) * 4u, 0, 0);
+          st_bf16(rdv, row, col(j), bet[e] * Xb[j][t][e]);
           s += Xb[j][t][e] * W[j][t][e];
         }
         s = row_sum16(s);
@@ -601,25 +634,17 @@ struct GradKernel {
   // this lane's own positions (tokens 16t + 4g + e of column c: exactly the
   // positions of its B fragments over tokens), and fed as a bf16 part plus the
   // bf16 of the remainder.
-  __device__ __forceinline__ void phase5_6(int j) {
+  __device__ __forceinline__ void phase5_6(int j, const Pre5& p) {
     const int c = col(j);
-    // rows c of S and dU as B fragments over the state's columns (the kpos
-    // positions of each 32-wide block), and rowsum(dU . S) over the lane's
-    // positions in fp32
-    bf16x8 sr[NKD], ur[NKD];
+    // rows c of S and dU as B fragments over the state's columns, and
+    // rowsum(dU . S) over the lane's positions
+    const bf16x8* sr = p.sr[j];
+    const bf16x8* ur = p.ur[j];
     float dgc = 0.f;
 #pragma unroll
-    for (int m = 0; m < NKD; ++m) {
-      const uint32_t base = (uint32_t)(c * D + 32 * m + g4) * 4u;
-      const f32x4 s_lo = __builtin_bit_cast(f32x4, bload128(rS, base));
-      const f32x4 s_hi = __builtin_bit_cast(f32x4, bload128(rS, base + 64u));
-      const f32x4 u_lo = __builtin_bit_cast(f32x4, bload128(rU, base));
-      const f32x4 u_hi = __builtin_bit_cast(f32x4, bload128(rU, base + 64u));
+    for (int m = 0; m < NKD; ++m)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dgc += s_lo[e] * u_lo[e] + s_hi[e] * u_hi[e];
-      sr[m] = pack8(s_lo, s_hi);
-      ur[m] = pack8(u_lo, u_hi);
-    }
+      for (int e = 0; e < 8; ++e) dgc += (float)sr[m][e] * (float)ur[m][e];
     // rowsum(dU . S): the four lane groups (l%16 fixed) hold the rest of the row's sum
     dgc += __shfl_xor(dgc, 16);
     dgc += __shfl_xor(dgc, 32);
@@ -634,11 +659,10 @@ struct GradKernel {
         float run = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int row = 16 * t + g4 + e;
-          run += in_val(rla, row, c);
+          run += f16raw(p.la[j][4 * t + e]);
           gv[t][e] = run;
-          qv[t][e] = in_val(rq, row, c);
-          kv[t][e] = in_val(rk, row, c);
+          qv[t][e] = f16raw(p.q[j][4 * t + e]);
+          kv[t][e] = f16raw(p.k[j][4 * t + e]);
         }
         tot[t] = run;
       }
@@ -711,9 +735,8 @@ struct GradKernel {
         const int row = 16 * t + g4 + e;
         const float dq = dqh[t][e] * eg[t][e];
         const float t1 = dkh[t][e] * eg[t][e], t2 = dkb[t][e] * emg[t][e], t3 = dks[t][e] * emg[t][e];
-        const uint32_t off = (uint32_t)(row * D + c) * 4u;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dq), rdq, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(t1 + t2 + t3), rdk, off, 0, 0);
+        st_bf16(rdq, row, c, dq);
+        st_bf16(rdk, row, c, t1 + t2 + t3);
         dg[t][e] = qv[t][e] * dq + kv[t][e] * (t1 - t2);
         ps[t][e] = kv[t][e] * t3;
       }
@@ -756,8 +779,7 @@ struct GradKernel {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * t + g4 + e;
-        const float dla = (dg[t][e] + post + after) + dgc + ps[t][e];
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dla), rdla, (uint32_t)(row * D + c) * 4u, 0, 0);
+        st_bf16(rdla, row, c, (dg[t][e] + post + after) + dgc + ps[t][e]);
       }
       after += (a0 + a1) + (a2 + a3);
     }
@@ -773,7 +795,7 @@ struct GradKernel {
     s0 = l & 15;
     nrows = min(GCH, a.T - n * GCH);
     const size_t tok0 = (size_t)bh * a.T + (size_t)n * GCH;
-    const uint32_t in_bytes = (uint32_t)nrows * D * 2u, out_bytes = (uint32_t)nrows * D * 4u;
+    const uint32_t in_bytes = (uint32_t)nrows * D * 2u, out_bytes = in_bytes;
     rq = make_rsrc(static_cast<const bf16*>(a.q) + tok0 * D, in_bytes);
     rk = make_rsrc(static_cast<const bf16*>(a.k) + tok0 * D, in_bytes);
     rv = make_rsrc(static_cast<const bf16*>(a.v) + tok0 * D, in_bytes);
@@ -784,17 +806,12 @@ struct GradKernel {
     rdk = make_rsrc(a.dk + tok0 * D, out_bytes);
     rdv = make_rsrc(a.dv + tok0 * D, out_bytes);
     rdla = make_rsrc(a.dla + tok0 * D, out_bytes);
-    // the chunk's start state: S0 for the first chunk, else the forward's
-    // checkpoint after the previous chunk ([B, nsnap, H, D, D])
-    const float* S = nullptr;
-    if (n == 0) {
-      S = a.S0 ? a.S0 + (size_t)bh * D * D : nullptr;
-    } else {
-      const int b = bh / a.H, h = bh - b * a.H;
-      S = a.ckpt + (((size_t)b * a.nckpt + (n - 1)) * a.H + h) * D * D;
-    }
-    rS = make_rsrc(S, S ? D * D * 4u : 0u);
-    rU = make_rsrc(a.dU + ((size_t)bh * nch + n) * D * D, D * D * 4u);
+    // the chunk's start state and dU, from the forward pass and the reverse chain
+    const size_t ck = ((size_t)bh * nch + n) * D * D;
+    rSr = make_rsrc(a.S_rows + ck, D * D * 2u);
+    rSc = make_rsrc(a.S_cols + ck, D * D * 2u);
+    rUr = make_rsrc(a.dU_rows + ck, D * D * 2u);
+    rUc = make_rsrc(a.dU_cols + ck, D * D * 2u);
     init_offsets();
     // zero halves of the 32-deep slots that pair a block of the upper triangle
     // with a stored one (nothing writes them): dP and Abar slots (0, 0) and
@@ -812,22 +829,26 @@ struct GradKernel {
       lds_st<u32x2>(smem, off, u32x2{0u, 0u});
     }
     for (int i = threadIdx.x; i < 2 * C::NW * GCH; i += C::THREADS) lds_st<float>(smem, C::DBP + 4 * i, 0.f);
+    Pre3 p3;
+    load_pre3(p3);
     phase1();
-    __syncthreads();
+    sync_lds();
     p2_tasks<0>();
-    __syncthreads();
-    phase3();
-    __syncthreads();
+    sync_lds();
+    phase3(p3);
+    Pre5 p5;
+    load_pre5(p5);
+    sync_lds();
     p4_tasks<0>();
-    __syncthreads();
+    sync_lds();
     if (wave == 0 && l < nrows) {
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < 2 * C::NW; ++w) s += lds_ld<float>(smem, C::DBP + 4 * (w * GCH + l));
-      a.dbeta[tok0 + l] = s;
+      a.dbeta[tok0 + l] = (bf16)s;
     }
 #pragma unroll
-    for (int j = 0; j < NCT; ++j) phase5_6(j);
+    for (int j = 0; j < NCT; ++j) phase5_6(j, p5);
   }
 };
 

@@ -825,6 +825,7 @@ struct ChunkKernel {
 
   __device__ __forceinline__ void c2(uint32_t st, int chunk) {
     if constexpr (PREFILL && !BWD) {
+      if (!a.o) return;  // a pass run only for its state checkpoints
       c2_half<0>(st, chunk);
       c2_half<2>(st, chunk);
     }
@@ -889,6 +890,32 @@ struct ChunkKernel {
       }
   }
 
+  // This lane's entries of the state (bf16 columns only) as bf16, twice: into a
+  // row-major D x D matrix and into its transpose, each with the positions
+  // inside every 32-wide block of a row in the kpos order.  A row of either one
+  // then gives an MFMA fragment over the state's columns (rows) in one 16-byte
+  // read: the layouts the per-chunk gradients read the state and dU in.
+  __device__ __forceinline__ void store_state_bf16(bf16* rows, bf16* cols) const {
+    if constexpr (C::BF) {
+      const rsrc_t rr = make_rsrc(rows, D * D * 2), rc = make_rsrc(cols, D * D * 2);
+      const int g4 = 4 * (l >> 4);
+      const uint32_t pc = (uint32_t)kpos(colb);  // colb even: colb + 1 sits at pc + 1
+#pragma unroll
+      for (int ci = 0; ci < D / 16; ++ci) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(cvt2(S[0][ci][e], S[1][ci][e]), rr,
+                                                (uint32_t)((16 * ci + g4 + e) * D + pc) * 2u, 0, 0);
+        const uint32_t pr = (uint32_t)kpos(16 * ci + g4);  // 4 consecutive rows, consecutive positions
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          const u32x2 x = {cvt2(S[j][ci][0], S[j][ci][1]), cvt2(S[j][ci][2], S[j][ci][3])};
+          __builtin_amdgcn_raw_buffer_store_b64(x, rc, (uint32_t)((colb + j) * D + pr) * 2u, 0, 0);
+        }
+      }
+    }
+  }
+
   // Snapshot after chunk cc when it closes a snapshot interval of the sequence.
   __device__ __forceinline__ void snapshot(int cc) const {
     if constexpr (PREFILL && !BWD) {
@@ -915,6 +942,13 @@ struct ChunkKernel {
 #pragma unroll
         for (int e = 0; e < 4; ++e) X[j][t][e] = -vval(vr, j, 4 * t + e);
     if constexpr (!TIGHT) load_v(vr, cc + 1);
+    if constexpr (PREFILL && !BWD) {
+      // state checkpoints for the gradients: the start state of every chunk
+      if (a.ck_rows) {
+        const size_t o = ((size_t)bh_seq * nch + cc) * D * D;
+        store_state_bf16(a.ck_rows + o, a.ck_cols + o);
+      }
+    }
     c1(X, stage(cc));
     if constexpr (TIGHT) load_v(vr, cc + 1);
     c2(stage(cc), cc);
@@ -961,7 +995,10 @@ struct ChunkKernel {
 #pragma unroll
         for (int j = 0; j < NCT; ++j) S[j][ci] = S[j][ci] * gm;
       }
-      store_state(a.dU_out + ((size_t)bh_seq * nch + chunk) * D * D, colb);
+      {
+        const size_t o = ((size_t)bh_seq * nch + chunk) * D * D;
+        store_state_bf16(a.dU_rows + o, a.dU_cols + o);
+      }
 #pragma unroll
       for (int j = 0; j < NCT; ++j)
 #pragma unroll

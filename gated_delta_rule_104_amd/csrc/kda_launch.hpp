@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "kda_device.hpp"
+
 namespace kda {
 
 // One chunked pass over `G * BH` independent sequences (segments).  Sequence
@@ -38,12 +40,18 @@ struct ChunkArgs {
   // segment pass: a wave stops updating its map columns once they are all
   // exactly zero (they stay zero for finite inputs); 0 keeps updating them
   int map_skip = 1;
-  // backward chain only: dU = Diag(Gam) dS' of every chunk, [BH, nch, D, D] fp32
-  float* dU_out = nullptr;
+  // gradients' checkpoints, [BH, nch, D, D] bf16 each, as a row-major matrix
+  // and its transpose, with the positions inside each 32-wide block of a row in
+  // the kpos order (null: none).  Prefill (bf16, one segment per head): the
+  // start state of every chunk; backward chain: dU = Diag(Gam) dS' of every chunk.
+  bf16* ck_rows = nullptr;
+  bf16* ck_cols = nullptr;
+  bf16* dU_rows = nullptr;
+  bf16* dU_cols = nullptr;
 };
 
 // Reverse chain of the prefill gradients (bf16 inputs, one segment per head):
-// S0 = dS_T [BH, D, D] or null, S_out = dS0, v = dO, dU_out as above; nc
+// S0 = dS_T [BH, D, D] or null, S_out = dS0, v = dO, dU_rows/cols as above; nc
 // consumer waves per workgroup ({1, 2, 4} at D = 128, {1, 2} at D = 64).
 hipError_t launch_chunk_bwd(const ChunkArgs& a, int D, int nc, int nwg, hipStream_t stream);
 
@@ -100,16 +108,16 @@ struct BwGradArgs {
   const void* la;
   const void* beta;
   const void* dO;      // [BH, T, D] or null (= 0)
-  const float* S0;     // [BH, D, D] or null (= 0)
-  const float* ckpt;   // [B, nckpt, H, D, D]: state after chunk j at index j
-  int nckpt;
-  int H;
-  const float* dU;     // [BH, nch, D, D]
-  float* dq;           // [BH, T, D]
-  float* dk;
-  float* dv;
-  float* dla;
-  float* dbeta;        // [BH, T]
+  // [BH, nch, D, D] bf16, row-major and transposed as in ChunkArgs::ck_rows:
+  const bf16* S_rows;  // the start state of every chunk
+  const bf16* S_cols;
+  const bf16* dU_rows; // dU = Diag(Gam) dS' of every chunk
+  const bf16* dU_cols;
+  bf16* dq;            // [BH, T, D], the inputs' dtype
+  bf16* dk;
+  bf16* dv;
+  bf16* dla;
+  bf16* dbeta;         // [BH, T]
   int T;
 };
 hipError_t launch_bwgrad(const BwGradArgs& a, int BH, int D, hipStream_t stream);

@@ -253,8 +253,10 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
  *   q, k, v, log_alpha, beta, S0 : as for kda_chunk_prefill (S0 NULL = zero)
  *   dO   : [B, H, T, dv] dtype, or NULL (= 0)
  *   dS_T : [B, H, dk, dv] fp32, or NULL (= 0)
- *   dq, dk_, dlog_alpha : [B, H, T, dk] fp32;  dv_ : [B, H, T, dv] fp32;
- *   dbeta : [B, H, T] fp32;  dS0 : [B, H, dk, dv] fp32.
+ *   dq, dk_, dlog_alpha : [B, H, T, dk] dtype;  dv_ : [B, H, T, dv] dtype;
+ *   dbeta : [B, H, T] dtype;  dS0 : [B, H, dk, dv] fp32.
+ * Each gradient takes the dtype of the input it belongs to (the states' is
+ * fp32), as autograd frameworks expect.
  * bf16 inputs run in the chunked form, on the matrix cores (bf16 operands,
  * fp32 accumulation): a forward pass that keeps the state after every 64-token
  * chunk, beside it the reverse chain over the chunks (dS' -> dS, which needs
@@ -262,9 +264,9 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
  * inputs run the recurrence's token steps backwards in fp32, token by token,
  * one workgroup (or two, each with half of the state's columns) per head.
  * The workspace (device memory, at least kda_backward_workspace_bytes for the
- * same dtype, 16-byte aligned) holds, for bf16, the state after every whole
- * chunk and dU = Diag(Gam) dS' of every chunk (fp32, 64 KiB per chunk-head at
- * d = 128 each); for fp32, a state checkpoint every 64 tokens, the entering
+ * same dtype, 16-byte aligned) holds, for bf16, the start state and
+ * dU = Diag(Gam) dS' of every chunk (bf16, twice each: 128 KiB per chunk-head
+ * at d = 128 in all); for fp32, a state checkpoint every 64 tokens, the entering
  * states and vectors u = (Diag(alpha) S)^T k of one 64-token interval, per
  * head, and the two halves' row sums.  Its contents on return are undefined.
  * No output may alias an input or the workspace.  The bf16 path forks part of
@@ -275,7 +277,7 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
 size_t kda_backward_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtype dtype);
 kda_status kda_prefill_backward(const void* q, const void* k, const void* v, const void* log_alpha,
                                 const void* beta, const float* S0, const void* dO, const float* dS_T,
-                                float* dq, float* dk_, float* dv_, float* dlog_alpha, float* dbeta,
+                                void* dq, void* dk_, void* dv_, void* dlog_alpha, void* dbeta,
                                 float* dS0, int B, int H, int T, int dk, int dv, kda_dtype dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 

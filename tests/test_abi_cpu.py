@@ -225,8 +225,8 @@ def backward(lib, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, dO=FAKE, 
 
 
 def test_backward_workspace_query(lib):
-    """bf16 (chunked form): the state after every whole chunk, dU of every chunk
-    and one discarded end state, fp32 D x D each per head.  fp32 (token steps):
+    """bf16 (chunked form): the start state and dU of every chunk, each as two
+    bf16 D x D matrices, and one discarded fp32 end state per head.  fp32 (token steps):
     a checkpoint every 64 tokens plus 64 entering states (fp32 D x D) and 64
     fp32 D-vectors per head, then two halves of every token's row sums (dq, dk,
     dlog_alpha, dbeta: 3D + 1 floats)."""
@@ -235,9 +235,9 @@ def test_backward_workspace_query(lib):
     assert q(1, 1, 64, 64, 64, F32) == ((1 + 64) * 64 * 64 + 64 * 64 + 2 * 64 * (3 * 64 + 1)) * 4
     assert q(2, 3, 65, 128, 128, F32) == 6 * ((2 + 64) * 128 * 128 + 64 * 128 + 2 * 65 * (3 * 128 + 1)) * 4
     assert q(1, 1, 0, 64, 64, F32) == (64 * 64 * 64 + 64 * 64) * 4
-    assert q(1, 1, 64, 64, 64, BF16) == (1 + 1 + 1) * 64 * 64 * 4
-    assert q(2, 3, 65, 128, 128, BF16) == 6 * (1 + 2 + 1) * 128 * 128 * 4
-    assert q(4, 32, 8192, 128, 128, BF16) == 128 * (128 + 128 + 1) * 128 * 128 * 4
+    assert q(1, 1, 64, 64, 64, BF16) == (2 * 1 + 1) * 64 * 64 * 4
+    assert q(2, 3, 65, 128, 128, BF16) == 6 * (2 * 2 + 1) * 128 * 128 * 4
+    assert q(4, 32, 8192, 128, 128, BF16) == 128 * (2 * 128 + 1) * 128 * 128 * 4
     assert q(1, 1, 0, 64, 64, BF16) == 64 * 64 * 4
     assert q(1, 1, 64, 64, 128, BF16) == 0 and q(1, 1, 64, 96, 96, F32) == 0 and q(0, 1, 64, 64, 64, BF16) == 0
     assert q(1, 1, 64, 64, 64, 5) == 0
