@@ -101,6 +101,14 @@ int cu_count() {
   return cache[dev];
 }
 
+// Workgroups per head of the fp32 (token-step) backward: two, each with half
+// of the state's columns, when that still fits the chip in one round; option
+// bw_split forces the choice.
+int bw_split(long long BH) {
+  if (const long long v = opt(OPT_BW_SPLIT); v == 1 || v == 2) return (int)v;
+  return 2 * BH <= cu_count() ? 2 : 1;
+}
+
 // Option map_skip = 0 keeps the segment pass updating map columns that have
 // become exactly zero (for tests that compare both ways); by default it stops.
 bool map_skip_enabled() { return opt(OPT_MAP_SKIP) != 0; }
@@ -781,7 +789,8 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
 size_t kda_backward_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtype dtype) {
   if (B <= 0 || H <= 0 || T < 0 || dk != dv || (dk != 64 && dk != 128)) return 0;
   if (dtype == KDA_BF16) return chunk_bw_ws_floats((long long)B * H, T, dk) * sizeof(float);
-  if (dtype == KDA_F32) return kda::backward_ws_floats((long long)B * H, T, dk) * sizeof(float);
+  if (dtype == KDA_F32)
+    return kda::backward_ws_floats((long long)B * H, T, dk, bw_split((long long)B * H)) * sizeof(float);
   return 0;
 }
 
@@ -814,7 +823,8 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
     if (!dbeta) return fail(KDA_ERR_NULL, "dbeta is NULL");
   }
   const bool bf = dtype == KDA_BF16;
-  const size_t need = (bf ? chunk_bw_ws_floats(BH, T, dk) : kda::backward_ws_floats(BH, T, dk)) * sizeof(float);
+  const int split = bw_split(BH);
+  const size_t need = (bf ? chunk_bw_ws_floats(BH, T, dk) : kda::backward_ws_floats(BH, T, dk, split)) * sizeof(float);
   if (!workspace) return fail(KDA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (!aligned(workspace)) return fail(KDA_ERR_ALIGN, "workspace is not 16-byte aligned");
   if (workspace_bytes < need)
@@ -828,11 +838,7 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
   a.dla = static_cast<float*>(dlog_alpha); a.dbeta = static_cast<float*>(dbeta); a.dS0 = dS0;
   a.ws = static_cast<float*>(workspace);
   a.T = T;
-  // two workgroups per head (each with half of the state's columns) when that
-  // still fits the chip in one round; option bw_split forces the choice
-  int split = 2 * BH <= cu_count() ? 2 : 1;
-  if (const long long v = opt(OPT_BW_SPLIT); v == 1 || v == 2) split = (int)v;
-  hipError_t e = kda::launch_backward(a, (int)BH, dk, dtype == KDA_BF16, split, stream);
+  hipError_t e = kda::launch_backward(a, (int)BH, dk, split, stream);
   if (e != hipSuccess) return hip_fail(e, "kda_prefill_backward launch");
   return ok();
 }

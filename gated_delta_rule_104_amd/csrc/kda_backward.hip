@@ -133,8 +133,9 @@ __global__ __launch_bounds__(4 * (D / SPLIT), 1) void kda_backward_kernel(Backwa
   float* ckpt = a.ws + (size_t)bh * hf + (size_t)hc * (hf / SPLIT);
   float* hist = ckpt + (size_t)nch * NS;
   float* hu = hist + (size_t)kBwInterval * NS;  // u of each token of the interval, own columns
-  // SPLIT = 2: this half's row sums, [hc][bh][t][3D + 1] after every head's area
-  float* part_sums = a.ws + (size_t)nbh * hf + ((size_t)hc * nbh + bh) * (size_t)nt * (3 * D + 1);
+  // SPLIT = 2: the second half's row sums, [bh][t][3D + 1] after every head's
+  // area (the first half writes its own straight to the outputs)
+  float* part_sums = a.ws + (size_t)nbh * hf + (size_t)bh * (size_t)nt * (3 * D + 1);
   const size_t my = (size_t)i * DC + c0;  // this thread's first entry of the slice
 
   // Token vectors: threads < D fetch one row channel (k, log_alpha, q) and
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(4 * (D / SPLIT), 1) void kda_backward_kernel(Backwa
       dla = row_sum<TPR>(dla);
       db = row_sum<TPR>(db);
       const size_t o = (tok0 + t) * D;
-      if (SPLIT == 1) {
+      if (SPLIT == 1 || hc == 0) {
         if (part == 0) {
           a.dq[o + i] = dq;
           a.dk[o + i] = dk;
@@ -313,9 +314,9 @@ __global__ __launch_bounds__(4 * (D / SPLIT), 1) void kda_backward_kernel(Backwa
   for (int c = 0; c < CPT; ++c) a.dS0[st0 + (size_t)i * D + col0 + c0 + c] = dS[c];
 }
 
-// SPLIT = 2: adds the two workgroups' row sums of every token, [2][n] with
-// n = BH T (3D + 1), into dq, dk, dlog_alpha and dbeta (fixed order, so the
-// result is deterministic).
+// SPLIT = 2: adds the second workgroup's row sums of every token, [n] with
+// n = BH T (3D + 1), to the first one's, already in dq, dk, dlog_alpha and
+// dbeta (one add per element, so the result is deterministic).
 __global__ __launch_bounds__(256) void kda_backward_sum_kernel(const float* __restrict__ ps, float* dq, float* dk,
                                                                 float* dla, float* dbeta, long long rows, int D) {
   const int W = 3 * D + 1;
@@ -323,19 +324,19 @@ __global__ __launch_bounds__(256) void kda_backward_sum_kernel(const float* __re
   for (long long x = (long long)blockIdx.x * blockDim.x + threadIdx.x; x < n; x += (long long)gridDim.x * blockDim.x) {
     const long long row = x / W;
     const int e = (int)(x - row * W);
-    const float s = ps[x] + ps[x + n];
-    if (e < D) dq[row * D + e] = s;
-    else if (e < 2 * D) dk[row * D + e - D] = s;
-    else if (e < 3 * D) dla[row * D + e - 2 * D] = s;
-    else dbeta[row] = s;
+    const float s = ps[x];
+    if (e < D) dq[row * D + e] += s;
+    else if (e < 2 * D) dk[row * D + e - D] += s;
+    else if (e < 3 * D) dla[row * D + e - 2 * D] += s;
+    else dbeta[row] += s;
   }
 }
 
-size_t backward_ws_floats(long long BH, int T, int D) {
-  return (size_t)BH * bw_head_floats(T, D) + 2 * (size_t)BH * (size_t)T * (3 * D + 1);
+size_t backward_ws_floats(long long BH, int T, int D, int split) {
+  return (size_t)BH * bw_head_floats(T, D) + (split == 2 ? (size_t)BH * (size_t)T * (3 * D + 1) : 0);
 }
 
-hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, int split, hipStream_t stream) {
+hipError_t launch_backward(const BackwardArgs& a, int BH, int D, int split, hipStream_t stream) {
   if (BH <= 0) return hipSuccess;
 #define KDA_BW(TY, DD, SP)                                                                             \
   hipLaunchKernelGGL((kda_backward_kernel<TY, DD, SP>), dim3((long long)BH * SP),                    \
@@ -345,13 +346,8 @@ hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, i
     if (D == 128) KDA_BW(TY, 128, SP); \
     else KDA_BW(TY, 64, SP);           \
   } while (0)
-  if (split == 2) {
-    if (bf16_io) KDA_BW_D(bf16, 2);
-    else KDA_BW_D(float, 2);
-  } else {
-    if (bf16_io) KDA_BW_D(bf16, 1);
-    else KDA_BW_D(float, 1);
-  }
+  if (split == 2) KDA_BW_D(float, 2);
+  else KDA_BW_D(float, 1);
 #undef KDA_BW_D
 #undef KDA_BW
   hipError_t e = hipGetLastError();

@@ -70,12 +70,13 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, const void
                          const void* beta, const float* S_in, float* S_out, void* o, float* S_pos,
                          int NH, int H, int ntok, int D, bool bf16_io, hipStream_t stream);
 
-// Prefill gradients over [BH, T, D] inputs, split workgroups (1 or 2) per
-// head.  The workspace holds, per head, (ceil(T / kBwInterval) + kBwInterval)
-// fp32 D x D states (a checkpoint at the start of every interval and the
-// entering state of every token of the interval being walked) and kBwInterval
-// fp32 D-vectors (u = D^T k of each token of that interval), then, for all
-// heads, two halves of the row sums of every token (2 BH T (3D + 1) floats).
+// Prefill gradients over [BH, T, D] fp32 inputs, token by token, split
+// workgroups (1 or 2) per head.  The workspace holds, per head,
+// (ceil(T / kBwInterval) + kBwInterval) fp32 D x D states (a checkpoint at the
+// start of every interval and the entering state of every token of the
+// interval being walked) and kBwInterval fp32 D-vectors (u = D^T k of each
+// token of that interval), then, with two workgroups per head, the second
+// one's row sums of every token (BH T (3D + 1) floats).
 constexpr int kBwInterval = 64;
 struct BackwardArgs {
   const void* q;
@@ -95,7 +96,7 @@ struct BackwardArgs {
   float* ws;
   int T;
 };
-size_t backward_ws_floats(long long BH, int T, int D);
+size_t backward_ws_floats(long long BH, int T, int D, int split);
 
 // Per-chunk gradients of the prefill (bf16 inputs), one workgroup per
 // (head, chunk): from the chunk's start state (S0 for chunk 0, else the
@@ -121,7 +122,7 @@ struct BwGradArgs {
   int T;
 };
 hipError_t launch_bwgrad(const BwGradArgs& a, int BH, int D, hipStream_t stream);
-hipError_t launch_backward(const BackwardArgs& a, int BH, int D, bool bf16_io, int split, hipStream_t stream);
+hipError_t launch_backward(const BackwardArgs& a, int BH, int D, int split, hipStream_t stream);
 
 hipError_t launch_merge(const float* S_in, const float* Z, const float* M, float* S_start,
                         float* S_T, int BH, int G, int D, hipStream_t stream);

@@ -228,12 +228,15 @@ def test_backward_workspace_query(lib):
     """bf16 (chunked form): the start state and dU of every chunk, each as two
     bf16 D x D matrices, and one discarded fp32 end state per head.  fp32 (token steps):
     a checkpoint every 64 tokens plus 64 entering states (fp32 D x D) and 64
-    fp32 D-vectors per head, then two halves of every token's row sums (dq, dk,
-    dlog_alpha, dbeta: 3D + 1 floats)."""
+    fp32 D-vectors per head, then, with two workgroups per head (few heads),
+    the second one's row sums of every token (dq, dk, dlog_alpha, dbeta:
+    3D + 1 floats); with one workgroup per head none."""
     q = lib.kda_backward_workspace_bytes
     q.restype = ctypes.c_size_t
-    assert q(1, 1, 64, 64, 64, F32) == ((1 + 64) * 64 * 64 + 64 * 64 + 2 * 64 * (3 * 64 + 1)) * 4
-    assert q(2, 3, 65, 128, 128, F32) == 6 * ((2 + 64) * 128 * 128 + 64 * 128 + 2 * 65 * (3 * 128 + 1)) * 4
+    kda.set_option("bw_split", None)  # the default: two workgroups per head while 2 B H fits the CUs
+    assert q(1, 1, 64, 64, 64, F32) == ((1 + 64) * 64 * 64 + 64 * 64 + 64 * (3 * 64 + 1)) * 4
+    assert q(2, 3, 65, 128, 128, F32) == 6 * ((2 + 64) * 128 * 128 + 64 * 128 + 65 * (3 * 128 + 1)) * 4
+    assert q(64, 32, 65, 128, 128, F32) == 2048 * ((2 + 64) * 128 * 128 + 64 * 128) * 4
     assert q(1, 1, 0, 64, 64, F32) == (64 * 64 * 64 + 64 * 64) * 4
     assert q(1, 1, 64, 64, 64, BF16) == (2 * 1 + 1) * 64 * 64 * 4
     assert q(2, 3, 65, 128, 128, BF16) == 6 * (2 * 2 + 1) * 128 * 128 * 4
