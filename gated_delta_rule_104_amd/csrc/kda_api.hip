@@ -315,7 +315,8 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
                                   const void* beta, const float* Sst, void* o, float* S_T,
                                   long long BH, int T, int t0, int Tend, int Tseg, int D, bool bf,
                                   hipStream_t stream, const char* what, const Snap& sn = Snap(),
-                                  int nc = 0, kda::bf16* ck_rows = nullptr, kda::bf16* ck_cols = nullptr) {
+                                  int nc = 0, kda::bf16* ck_rows = nullptr, kda::bf16* ck_w = nullptr,
+                                  kda::bf16* ck_d = nullptr) {
   const int n = Tend - t0;
   const int G = n > 0 ? (int)(((long long)n + Tseg - 1) / Tseg) : 1;  // no tokens: copy the start state
   const long long nseq = BH * G;
@@ -328,7 +329,7 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
   a.vsplit = nt / (nc * kda::chunk_tiles_per_wave(bf));
   a.snap = sn.n > 0 ? sn.p : nullptr; a.snap_chunks = sn.chunks > 0 ? sn.chunks : 1;
   a.nsnap = sn.n; a.H = sn.H;
-  a.ck_rows = ck_rows; a.ck_cols = ck_cols;
+  a.ck_rows = ck_rows; a.ck_w = ck_w; a.ck_d = ck_d;
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (log_on())
@@ -555,21 +556,22 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
   return st == KDA_OK ? ok() : st;
 }
 
-// Workspace of the chunked backward (bf16 inputs): the start state of every
-// chunk and dU = Diag(Gam) dS' of every chunk, each as two bf16 [BH, nch, D, D]
-// matrices (row-major and transposed, kpos-ordered rows), then the forward
-// pass's end state, which is not needed (fp32 [BH, D, D]).  In floats.
+// Workspace of the chunked backward (bf16 inputs), per chunk-head: the start
+// state and dU = Diag(Gam) dS' (bf16 D x D each), W = V - Kh S, Delta and
+// Xbar (bf16 64 x D each), all row-major with kpos-ordered positions; then the
+// forward pass's end state, which is not needed (fp32 [BH, D, D]).  In floats.
 size_t chunk_bw_ws_floats(long long BH, int T, int D) {
   const long long nch = (T + 63) / 64;
-  return (size_t)(2 * BH * nch + BH) * D * D;
+  return (size_t)(BH * nch * (2 * D + 3 * 64) * D / 2 + BH * D * D);
 }
 
 // Gradients of the prefill in the chunked form (bf16 inputs; arguments already
 // validated):
-//  1. beside each other: the forward pass from S0 with a state checkpoint after
-//     every chunk (its outputs are not written), on the side stream; and the
-//     reverse chain from dS_T over the chunks, last to first, which writes
-//     dU = Diag(Gam) dS' of every chunk and dS0 (it needs no forward state);
+//  1. beside each other: the forward pass from S0, which keeps the start state,
+//     W = V - Kh S and Delta of every chunk (its outputs are not written), on
+//     the side stream; and the reverse chain from dS_T over the chunks, last to
+//     first, which keeps dU = Diag(Gam) dS' and Xbar of every chunk and writes
+//     dv and dS0 (it needs no forward state);
 //  2. the per-chunk gradients, one workgroup per (head, chunk).
 kda_status chunk_backward(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                           const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
@@ -577,19 +579,20 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
                           hipStream_t stream) {
   const long long BH = (long long)B * H;
   const long long nch = (T + 63) / 64;
-  const size_t nS = (size_t)BH * nch * D * D;  // elements of one checkpoint array
+  const size_t nS = (size_t)BH * nch * D * D, nC = (size_t)BH * nch * 64 * D;  // elements per array
   kda::bf16* S_rows = reinterpret_cast<kda::bf16*>(ws);
-  kda::bf16* S_cols = S_rows + nS;
-  kda::bf16* dU_rows = S_cols + nS;
-  kda::bf16* dU_cols = dU_rows + nS;
-  float* ST = reinterpret_cast<float*>(dU_cols + nS);  // [BH, D, D], discarded
+  kda::bf16* dU_rows = S_rows + nS;
+  kda::bf16* W = dU_rows + nS;
+  kda::bf16* Dl = W + nC;
+  kda::bf16* Xb = Dl + nC;
+  float* ST = reinterpret_cast<float*>(Xb + nC);  // [BH, D, D], discarded
   const int nt = D / 16;
   kda::ChunkArgs r;
   r.q = q; r.k = k; r.v = dO; r.la = log_alpha; r.beta = beta;
-  r.S0 = dS_T; r.o = nullptr; r.S_out = dS0; r.M_out = nullptr;
+  r.S0 = dS_T; r.o = dv_; r.S_out = dS0; r.M_out = nullptr;
   r.BH = (int)BH; r.G = 1; r.Tseg = T > 0 ? T : 1; r.Ttot = T; r.t0 = 0; r.Tend = T;
   r.dU_rows = dU_rows;
-  r.dU_cols = dU_cols;
+  r.ck_xb = Xb;
   // The forward pass and the reverse chain run side by side: their column
   // split is chosen so that both together fill the chip once.
   const int ncb = pick_nc(2 * BH, nt, true);
@@ -612,7 +615,7 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
     if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess || (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
       return hip_fail(e, "kda_prefill_backward fork");
     st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, nullptr, ST, BH, T, 0, T, T, D, true, ss->s,
-                                "kda_prefill_backward forward checkpoints", Snap(), ncb, S_rows, S_cols);
+                                "kda_prefill_backward forward checkpoints", Snap(), ncb, S_rows, W, Dl);
     if (st == KDA_OK && (e = kda::launch_chunk_bwd(r, D, ncb, (int)(BH * r.vsplit), stream)) != hipSuccess)
       st = hip_fail(e, "kda_prefill_backward reverse chain");
     // join even if a launch above failed, so the side stream's work is waited for
@@ -621,9 +624,9 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
     if (st != KDA_OK) return st;
   }
   kda::BwGradArgs g;
-  g.q = q; g.k = k; g.v = v; g.la = log_alpha; g.beta = beta; g.dO = dO;
-  g.S_rows = S_rows; g.S_cols = S_cols; g.dU_rows = dU_rows; g.dU_cols = dU_cols;
-  g.dq = static_cast<kda::bf16*>(dq); g.dk = static_cast<kda::bf16*>(dk_); g.dv = static_cast<kda::bf16*>(dv_);
+  g.q = q; g.k = k; g.la = log_alpha; g.beta = beta; g.dO = dO;
+  g.S_rows = S_rows; g.W = W; g.Dl = Dl; g.dU_rows = dU_rows; g.Xb = Xb;
+  g.dq = static_cast<kda::bf16*>(dq); g.dk = static_cast<kda::bf16*>(dk_);
   g.dla = static_cast<kda::bf16*>(dlog_alpha); g.dbeta = static_cast<kda::bf16*>(dbeta); g.T = T;
   if ((e = kda::launch_bwgrad(g, (int)BH, D, stream)) != hipSuccess) return hip_fail(e, "kda_prefill_backward gradients");
   return ok();

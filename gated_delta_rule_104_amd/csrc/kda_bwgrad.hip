@@ -2,22 +2,22 @@
 //
 // For a loss L with dL/do = dO and dL/dS_T = dS_T, the gradients of a 64-token
 // chunk follow from its start state S, the gradient dU = Diag(Gam) dS' with
-// respect to its end state (scaled by the chunk's decay; the reverse chain
-// computes it), and the chunk's own inputs.  With the chunked form of the
-// recurrence (blog.csdn.net article on the Kimi K3 report, section 一.1, for the
-// gated delta rule; "Kimi K3 开源日来了", section "FlashKDA", for the chunking;
-// training is what the K3 report also speeds up with FlashKDA)
+// respect to its end state (scaled by the chunk's decay), and the chunk's own
+// inputs.  With the chunked form of the recurrence (blog.csdn.net article on
+// the Kimi K3 report, section 一.1, for the gated delta rule; "Kimi K3
+// 开源日来了", section "FlashKDA", for the chunking; training is what the K3
+// report also speeds up with FlashKDA)
 //   g = cumsum(log alpha),  Qh = q e^g,  Kh = k e^g,  Kb = k e^-g,  Gam = e^(g_C)
 //   L = diag(b) strict_lower(Kh Kb^T),  P = lower(Qh Kb^T),  T = (I + L)^-1
 //   W = V - Kh S,  X = diag(b) W,  Delta = T X
 //   O = Qh S + P Delta,  S' = Diag(Gam) (S + Kb^T Delta)
 // the chain rule gives, per chunk:
-//   dDelta = Kb dU + P^T dO,  Xbar = T^T dDelta
+//   dDelta = Kb dU + P^T dO,  Xbar = T^T dDelta,  dv = diag(b) Xbar
 //   dP = lower(dO Delta^T),  Lbar = strict_lower(-Xbar Delta^T),  Abar = diag(b) Lbar
 //   dQh = dO S^T + dP Kb
 //   dKh = -diag(b) Xbar S^T + Abar Kb
 //   dKb = Delta dU^T + Abar^T Kh + dP^T Qh
-//   dv = diag(b) Xbar,  dbeta_r = sum_j Xbar_rj W_rj + sum_{s<r} Lbar_rs (Kh Kb^T)_rs
+//   dbeta_r = sum_j Xbar_rj W_rj + sum_{s<r} Lbar_rs (Kh Kb^T)_rs
 //   dq = dQh e^g,  dk = dKh e^g + dKb e^-g
 //   dlog_alpha_r = sum_{t >= r} dg_t + rowsum(dU . S) + sum_{s < r} k_s e^-g_s (Delta dU^T)_s
 //     with dg = q dq + k (dKh e^g - (dKb - Delta dU^T) e^-g)
@@ -27,24 +27,21 @@
 // the Delta dU^T piece of dKb cancel for s >= r, so that sum_{s < r} is formed
 // directly, which in bf16 products avoids a cancellation between large terms.
 //
-// One workgroup per (head, chunk), one wave per 16 columns of the head
-// dimension (8 waves at d = 128, two per SIMD).  Phases, each ended by a
-// workgroup barrier:
+// The forward pass stores S, W and Delta of every chunk, and the reverse chain
+// dU and Xbar (and writes dv); this kernel reads them.  One workgroup per
+// (head, chunk), one wave per 16 columns of the head dimension (8 waves at
+// d = 128, two per SIMD).  Phases, each ended by a workgroup barrier:
 //   1. elementwise: the cumulative gate (DPP row scan) and the bf16 operand
-//      tiles Qh, Kh, Kb, dO, with Gam and beta, into LDS;
-//   2. score tiles: T_ii, -L (forward solve), T_ii^T, -L^T (back solve), P^T;
-//   3. per wave, 16-column tiles of the value dimension: W, Delta, dDelta,
-//      Xbar, dv and the first part of dbeta; Delta and Xbar go to LDS;
-//   4. the 64 x 64 gradients dP, dP^T, Abar, Abar^T (as MFMA A fragments) and
-//      the second part of dbeta;
-//   5. per wave, 16-column tiles of the key dimension: dQh, dKh, dKb (the
+//      tiles Kh, Kb, with beta, into LDS; beside it the other waves copy dO,
+//      Delta and Xbar into LDS tiles;
+//   2. the 64 x 64 gradients dP, dP^T, Abar, Abar^T (as MFMA A fragments) and
+//      dbeta;
+//   3. per wave, a 16-column tile of the key dimension: dQh, dKh, dKb (the
 //      products with the 64 x 64 gradients on fp32 Kb, Kh, Qh split into two
-//      bf16 parts);
-//   6. the gate's chain rule, written out per (token, channel).
+//      bf16 parts), then the gate's chain rule, written out per (token, channel).
 // Operand conventions are those of the chunk kernel: bf16 MFMA 16x16x32 tiles,
-// time-major LDS tiles with 32-wide k blocks in the kpos order, transposing LDS
-// reads for operands that contract over tokens, and 16x16 tiles that feed a
-// product as A operands stored in fragment order.
+// time-major LDS tiles with 32-wide k blocks in the kpos order, and 16x16
+// tiles that feed a product as A operands stored in fragment order.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -57,34 +54,26 @@ constexpr float G_LOG2E = 1.4426950408889634f;
 
 template <int D>
 struct GradCfg {
-  static constexpr int NW = D / 16;            // waves: one 16-column tile of the value (key) dimension each
+  static constexpr int NW = D / 16;            // waves: one 16-column tile of the head dimension each
   static constexpr int THREADS = 64 * NW;
-  static constexpr int NCT = D / (16 * NW);    // 16-column tiles per wave
+  static constexpr int NCT = 1;                // 16-column tiles per wave
   static constexpr int NKD = D / 32;           // 32-deep k blocks over channels
   static constexpr int NKT = GCH / 32;         // 32-deep k blocks over the chunk's tokens
   static constexpr int NP = D / 32;            // waves that build the elementwise tiles
   static constexpr int R_TD = D * 2;           // bf16 row of a [64][D] tile
   static constexpr int TD_TILE = 16 * R_TD + 16;
   static constexpr int TD_SZ = 4 * TD_TILE;
-  static constexpr int FR16 = 64 * 4 * 2;      // a 16x16 tile as 16-deep bf16 A fragments
   static constexpr int FR64 = 4 * NKT * 64 * 16;  // a 64x64 matrix as 32-deep A fragments
   static constexpr uint32_t KH = 0;
-  static constexpr uint32_t QH = KH + TD_SZ;
-  static constexpr uint32_t KB = QH + TD_SZ;
+  static constexpr uint32_t KB = KH + TD_SZ;
   static constexpr uint32_t DO = KB + TD_SZ;
-  static constexpr uint32_t DL = DO + TD_SZ;   // Delta
-  static constexpr uint32_t XB = DL + TD_SZ;   // Xbar
-  static constexpr uint32_t TI = XB + TD_SZ;   // T_ii as A fragments (forward solve)
-  static constexpr uint32_t LO = TI + 4 * FR16;  // -L_ij, i > j
-  static constexpr uint32_t TT = LO + 6 * FR16;  // T_ii^T (back solve)
-  static constexpr uint32_t LT = TT + 4 * FR16;  // -L_ij^T, i > j
-  static constexpr uint32_t PT = LT + 6 * FR16;  // P^T, 32-deep over tokens
-  static constexpr uint32_t DP = PT + FR64;      // dP
+  static constexpr uint32_t DL = DO + TD_SZ;     // Delta
+  static constexpr uint32_t XB = DL + TD_SZ;     // Xbar
+  static constexpr uint32_t DP = XB + TD_SZ;     // dP
   static constexpr uint32_t DPT = DP + FR64;     // dP^T
   static constexpr uint32_t AB = DPT + FR64;     // Abar
   static constexpr uint32_t ABT = AB + FR64;     // Abar^T
-  static constexpr uint32_t GM = ABT + FR64;     // Gam [D] fp32
-  static constexpr uint32_t BETA = GM + 4 * D;   // beta [64] fp32
+  static constexpr uint32_t BETA = ABT + FR64;   // beta [64] fp32
   static constexpr uint32_t DBP = BETA + 4 * GCH;  // dbeta partials [2 NW][64] fp32
   static constexpr uint32_t LDS = DBP + 4 * GCH * 2 * NW;
   static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -99,9 +88,8 @@ struct GradKernel {
   BwGradArgs a;
   int wave, l, g4, s0;
   int nrows;  // valid tokens of this chunk
-  rsrc_t rq, rk, rv, rla, rbeta, rdo, rdq, rdk, rdv, rdla, rSr, rSc, rUr, rUc;
+  rsrc_t rq, rk, rla, rbeta, rdo, rdq, rdk, rdla, rSr, rUr, rW, rDl, rXb;
   uint32_t oTD[NKD];   // A fragments of [64][D] tiles, row tile 0
-  int tr_f, tr_q;      // transposing reads: the lane's row and channel quad
 
   __device__ __forceinline__ static uint32_t td(int row, int byte) {
     return (uint32_t)(row >> 4) * C::TD_TILE + swz<C::R_TD>(row & 15, byte);
@@ -109,18 +97,6 @@ struct GradKernel {
   // A fragment of row tile t, k block m (channels) of a [64][D] tile
   __device__ __forceinline__ bf16x8 ar(uint32_t tile, int t, int m) const {
     return lds_ld<bf16x8>(smem, tile + oTD[m] + t * C::TD_TILE);
-  }
-  // Fragment of channels 16ct .. 16ct+15 over tokens 32m .. 32m+31 of a [64][D]
-  // tile, read with transposing LDS reads: lane i of lane group g receives the
-  // tokens of its k positions of channel 16ct + i (the A fragment of the tile's
-  // transpose, equally the B fragment of the tile over tokens).
-  __device__ __forceinline__ bf16x8 tr_frag(uint32_t tile, int ct, int m) const {
-    // (computed, not tabled: ct depends on the wave, and a table indexed at run
-    // time would live in scratch memory)
-    const uint32_t base = tile + swz<C::R_TD>(tr_f, 2 * kpos(32 * (ct >> 1) + 4 * tr_q)) + 8u * (uint32_t)(ct & 1);
-    const bf16x4 lo = lds_tr16(smem, base + (uint32_t)(2 * m) * C::TD_TILE);
-    const bf16x4 hi = lds_tr16(smem, base + (uint32_t)(2 * m + 1) * C::TD_TILE);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   // 32-deep A fragment slot of a 64x64 matrix stored at `base`: row tile t, k block m
   __device__ __forceinline__ bf16x8 fr64(uint32_t base, int t, int m) const {
@@ -137,25 +113,20 @@ struct GradKernel {
     const int kg = 8 * (l >> 4);
 #pragma unroll
     for (int m = 0; m < NKD; ++m) oTD[m] = swz<C::R_TD>(r16, 2 * (32 * m + kg));
-    tr_f = 4 * (l >> 4) + (r16 >> 2);
-    tr_q = r16 & 3;
   }
 
   // ------------------------------------------------------------ phase 1
   // Wave pw < NP: lane (tg = l%16, cs = l/16) owns tokens 4tg .. 4tg+3 and
   // channels 32pw + 8cs .. +7; a channel's 16 token groups form one DPP row.
-  __device__ __forceinline__ void phase1() {
-    if (wave >= C::NP) return;
+  __device__ __forceinline__ void elementwise() {
     const int tg = l & 15, cs = l >> 4;
     const int ch = 32 * wave + 8 * cs;
-    Raw8<bf16> rla_[4], rk_[4], rq_[4], rdo_[4];
+    Raw8<bf16> rla_[4], rk_[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t off = (uint32_t)((4 * tg + i) * D + ch) * 2;
       raw_load<bf16>(rla_[i], rla, off);
       raw_load<bf16>(rk_[i], rk, off);
-      raw_load<bf16>(rq_[i], rq, off);
-      raw_load<bf16>(rdo_[i], rdo, off);
     }
     float bet = 0.f;
     if (wave == 0)
@@ -180,175 +151,56 @@ struct GradKernel {
       x += dpp<DPP_ROW_SHR + 8>(x);
       exc[c] = dpp<DPP_ROW_SHR + 1>(x);
     }
-    float eg3[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float kk[8], qq[8];
+      float kk[8];
       raw_f32<bf16>(rk_[i], kk);
-      raw_f32<bf16>(rq_[i], qq);
-      float vkh[8], vkb[8], vq[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float gg = g[i][c] + exc[c];
-        const float eg = __builtin_amdgcn_exp2f(gg);
-        const float emg = __builtin_amdgcn_exp2f(-gg);
-        if (i == 3) eg3[c] = eg;
-        vkh[c] = kk[c] * eg;
-        vkb[c] = kk[c] * emg;
-        vq[c] = qq[c] * eg;
-      }
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
-        bf16x4 h, b, qv;
+        bf16x4 h, b;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          h[c] = (bf16)vkh[4 * hlf + c];
-          b[c] = (bf16)vkb[4 * hlf + c];
-          qv[c] = (bf16)vq[4 * hlf + c];
+          const float gg = g[i][4 * hlf + c] + exc[4 * hlf + c];
+          h[c] = (bf16)(kk[4 * hlf + c] * __builtin_amdgcn_exp2f(gg));
+          b[c] = (bf16)(kk[4 * hlf + c] * __builtin_amdgcn_exp2f(-gg));
         }
         const uint32_t o = td(4 * tg + i, 2 * kpos(ch + 4 * hlf));
         lds_st<bf16x4>(smem, C::KH + o, h);
         lds_st<bf16x4>(smem, C::KB + o, b);
-        lds_st<bf16x4>(smem, C::QH + o, qv);
-        lds_st<u32x2>(smem, C::DO + o, u32x2{rdo_[i].p[0][2 * hlf], rdo_[i].p[0][2 * hlf + 1]});
       }
-    }
-    if (tg == 15) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) lds_st<float>(smem, C::GM + 4 * (ch + c), eg3[c]);
     }
     if (wave == 0) lds_st<float>(smem, C::BETA + 4 * l, bet);
   }
 
-  // ------------------------------------------------------------ phase 2
-  // Score tile tasks.  With fx = rows of X's row tile I and fb = rows of Kb's row
-  // tile J (both as A/B fragments over channels), mma(A = fb, B = fx) leaves lane
-  // l holding M[16I + l%16][16J + 4g + e] (the A fragment of M_IJ) and
-  // mma(A = fx, B = fb) leaves M[16I + 4g + e][16J + l%16] (the accumulator
-  // tile of M_IJ: the A fragment of M_IJ^T).
-  template <int KIND, int I, int J>  // KIND 0: diagonal, 1: off-diagonal L, 2: P
-  __device__ __forceinline__ void p2_tile() {
-    const int ln = fresh_lane(l);
-    const uint32_t xb = (KIND == 2 ? C::QH : C::KH) + I * C::TD_TILE;
-    bf16x8 fx[NKD], fb[NKD];
+  // Waves NP .. NW-1: dO (the input, plain channel order) and Delta, Xbar (the
+  // checkpoints, already kpos-ordered) into their LDS tiles, 16 bytes at a
+  // time: every load is issued before the first store, so that their latencies
+  // overlap.
+  __device__ __forceinline__ void copy_tiles() {
+    constexpr int PIECES = GCH * D / 8;  // 16-byte pieces of one tile
+    constexpr int NL = (C::NW - C::NP) * 64;
+    static_assert(PIECES % NL == 0, "each load stays in one tile");
+    constexpr int PER = 3 * PIECES / NL, PER_TILE = PIECES / NL;
+    const int x0 = (wave - C::NP) * 64 + l;
+    u32x4 w[PER];
 #pragma unroll
-    for (int m = 0; m < NKD; ++m) {
-      fx[m] = lds_ld<bf16x8>(smem, xb + oTD[m]);
-      fb[m] = lds_ld<bf16x8>(smem, C::KB + J * C::TD_TILE + oTD[m]);
+    for (int i = 0; i < PER; ++i) {
+      const int y = i % PER_TILE * NL + x0;  // piece within tile i / PER_TILE
+      const int row = y / (D / 8), p8 = 8 * (y - row * (D / 8));
+      const rsrc_t r = i < PER_TILE ? rdo : i < 2 * PER_TILE ? rDl : rXb;
+      w[i] = bload128(r, (uint32_t)(row * D + p8) * 2u);
     }
-    const float bl = lds_ld<float>(smem, C::BETA + 4 * (16 * I + s0));
-    const f32x4 bet4 = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * I + g4));
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 at = zero4();  // M[16I + 4g + e][16J + s0]
 #pragma unroll
-    for (int m = 0; m < NKD; ++m) at = mfma_bf16_k32(at, fx[m], fb[m]);
-    if constexpr (KIND == 2) {
-      f32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (I > J || g4 + e >= s0) ? at[e] : 0.f;
-      put16(slot64(C::PT, J, I), v);  // P_IJ^T: row tile J, token tile I
-      return;
-    }
-    f32x4 af = zero4();  // M[16I + s0][16J + 4g + e]
-#pragma unroll
-    for (int m = 0; m < NKD; ++m) af = mfma_bf16_k32(af, fb[m], fx[m]);
-    if constexpr (KIND == 1) {
-      f32x4 vf, vb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[e] = -bl * af[e];
-        vb[e] = -bet4[e] * at[e];
+    for (int i = 0; i < PER; ++i) {
+      const int y = i % PER_TILE * NL + x0;
+      const int row = y / (D / 8), p8 = 8 * (y - row * (D / 8));
+      if (i < PER_TILE) {
+        lds_st<u32x2>(smem, C::DO + td(row, 2 * kpos(p8)), u32x2{w[i][0], w[i][1]});
+        lds_st<u32x2>(smem, C::DO + td(row, 2 * kpos(p8 + 4)), u32x2{w[i][2], w[i][3]});
+      } else {
+        lds_st<u32x4>(smem, (i < 2 * PER_TILE ? C::DL : C::XB) + td(row, 2 * p8), w[i]);
       }
-      put16(C::LO + (I * (I - 1) / 2 + J) * C::FR16 + ln * 8, vf);
-      put16(C::LT + (I * (I - 1) / 2 + J) * C::FR16 + ln * 8, vb);
-    } else {
-      // N = L_II (strictly lower).  T_ii = (I - N)(I + N^2)(I + N^4)(I + N^8); both
-      // T_ii and T_ii^T are accumulated, from the accumulators of N and N^T.
-      f32x4 Nt, Nn, Zf, Zb;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Nt[e] = g4 + e < s0 ? bl * af[e] : 0.f;      // N[16I + s0][16I + g4 + e]
-        Nn[e] = s0 < g4 + e ? bet4[e] * at[e] : 0.f;  // N[16I + g4 + e][16I + s0]
-        const float id = g4 + e == s0 ? 1.f : 0.f;
-        Zf[e] = id - Nt[e];  // acc(T^T)
-        Zb[e] = id - Nn[e];  // acc(T)
-      }
-      const f32x4 N2 = mfma_bf16_k16(zero4(), pack4(Nt), pack4(Nn));
-      const f32x4 Nt2 = mfma_bf16_k16(zero4(), pack4(Nn), pack4(Nt));
-      Zf = mfma_bf16_k16(Zf, pack4(N2), pack4(Zf));
-      Zb = mfma_bf16_k16(Zb, pack4(Nt2), pack4(Zb));
-      const f32x4 N4 = mfma_bf16_k16(zero4(), pack4(Nt2), pack4(N2));
-      const f32x4 Nt4 = mfma_bf16_k16(zero4(), pack4(N2), pack4(Nt2));
-      Zf = mfma_bf16_k16(Zf, pack4(N4), pack4(Zf));
-      Zb = mfma_bf16_k16(Zb, pack4(Nt4), pack4(Zb));
-      const f32x4 N8 = mfma_bf16_k16(zero4(), pack4(Nt4), pack4(N4));
-      const f32x4 Nt8 = mfma_bf16_k16(zero4(), pack4(N4), pack4(Nt4));
-      Zf = mfma_bf16_k16(Zf, pack4(N8), pack4(Zf));
-      Zb = mfma_bf16_k16(Zb, pack4(Nt8), pack4(Zb));
-      put16(C::TI + I * C::FR16 + ln * 8, Zf);
-      put16(C::TT + I * C::FR16 + ln * 8, Zb);
     }
-  }
-  // tasks: 4 diagonal (weight 3), 6 off-diagonal (2), 10 P (1), greedy over the waves
-  static constexpr int p2_kind(int K) { return K < 4 ? 0 : (K < 10 ? 1 : 2); }
-  static constexpr int p2_i(int K) {
-    if (K < 4) return K;
-    if (K < 10) {
-      const int io[6] = {3, 3, 3, 2, 2, 1};
-      return io[K - 4];
-    }
-    const int ii[10] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
-    return ii[K - 10];
-  }
-  static constexpr int p2_j(int K) {
-    if (K < 4) return K;
-    if (K < 10) {
-      const int jo[6] = {2, 1, 0, 1, 0, 0};
-      return jo[K - 4];
-    }
-    const int jj[10] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
-    return jj[K - 10];
-  }
-  static constexpr int greedy_wave(int K, int ntask, const int* weight) {
-    int load[C::NW] = {};
-    int w = 0;
-    for (int k = 0; k <= K && k < ntask; ++k) {
-      w = 0;
-      for (int i = 1; i < C::NW; ++i)
-        if (load[i] < load[w]) w = i;
-      load[w] += weight[k];
-    }
-    return w;
-  }
-  static constexpr int p2_wave(int K) {
-    int wt[20] = {};
-    for (int k = 0; k < 20; ++k) wt[k] = k < 4 ? 3 : (k < 10 ? 2 : 1);
-    return greedy_wave(K, 20, wt);
-  }
-  template <int K>
-  __device__ __forceinline__ void p2_tasks() {
-    if constexpr (K < 20) {
-      constexpr int W = p2_wave(K);  // evaluated at compile time
-      if (W == wave) p2_tile<p2_kind(K), p2_i(K), p2_j(K)>();
-      p2_tasks<K + 1>();
-    }
-  }
-
-  // ------------------------------------------------------------ phase 3
-  // Wave w owns value columns of tiles ct = NCT w + j: lane l holds, in an
-  // accumulator tile, rows 16t + 4g + e of column c_j = 16 ct + l%16.
-  __device__ __forceinline__ int col(int j) const { return 16 * (NCT * wave + j) + s0; }
-
-  // Row c of a checkpoint matrix stored with kpos-ordered rows (the state's
-  // columns, or dU's), k block m: one 16-byte read is the B fragment over that
-  // block (from the transposed copy: column c of the matrix over its rows).
-  __device__ __forceinline__ bf16x8 ck_frag(rsrc_t r, int c, int m) const {
-    return __builtin_bit_cast(bf16x8, bload128(r, (uint32_t)(c * D + 32 * m + 2 * g4) * 2u));
-  }
-
-  // one gradient, rounded to bf16, at (row, column) of the chunk's [64][D] output
-  __device__ __forceinline__ static void st_bf16(rsrc_t r, int row, int c, float x) {
-    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)x), r, (uint32_t)(row * D + c) * 2u, 0, 0);
   }
 
   // sum over the 16 lanes of each lane row; lane 15 of the row holds it
@@ -360,44 +212,32 @@ struct GradKernel {
     return x;
   }
 
-  __device__ __forceinline__ void store_tile_lds(uint32_t tile, const f32x4 (*x)[4]) {
-#pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          lds_st<bf16>(smem, tile + td(16 * t + g4 + e, 2 * kpos(col(j))), (bf16)x[j][t][e]);
+  // one gradient, rounded to bf16, at (row, column) of the chunk's [64][D] output
+  __device__ __forceinline__ static void st_bf16(rsrc_t r, int row, int c, float x) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)x), r, (uint32_t)(row * D + c) * 2u, 0, 0);
   }
 
-  // Global data of phases 3 and 5, loaded one phase ahead so that the loads
-  // are in flight across the preceding phase (the barriers wait only for LDS).
-  // bf16 values at this lane's accumulator positions (rows 16t + 4g + e of its
-  // columns) are kept as raw 16-bit loads.
-  struct Pre3 {
-    bf16x8 sb[NCT][NKD], ub[NCT][NKD];  // S and dU columns as B fragments over their rows
-    uint32_t v[NCT][16];
-  };
+  // Lane l works on column c = 16 wave + l%16 of the head dimension, rows
+  // 16t + 4g + e of the chunk (accumulator layout).
+  __device__ __forceinline__ int col(int j) const { return 16 * (NCT * wave + j) + s0; }
+
+  // Row c of a checkpoint matrix stored with kpos-ordered rows, k block m: one
+  // 16-byte read is the B fragment over that block.
+  __device__ __forceinline__ bf16x8 ck_frag(rsrc_t r, int c, int m) const {
+    return __builtin_bit_cast(bf16x8, bload128(r, (uint32_t)(c * D + 32 * m + 2 * g4) * 2u));
+  }
+
+  // Global data of phases 2 and 3, loaded at the start so that the loads are in
+  // flight across phase 1 (the barriers wait only for LDS).  bf16 values at this
+  // lane's accumulator positions are kept as raw 16-bit loads.
   struct Pre5 {
     bf16x8 sr[NCT][NKD], ur[NCT][NKD];  // S and dU rows as B fragments over their columns
-    uint32_t la[NCT][16], q[NCT][16], k[NCT][16];
+    uint32_t la[NCT][16], q[NCT][16], k[NCT][16], w[NCT][16];
   };
-  __device__ __forceinline__ uint32_t raw16(rsrc_t r, int row, int c) const {
-    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)(row * D + c) * 2u, 0, 0);
+  __device__ __forceinline__ uint32_t raw16(rsrc_t r, uint32_t off) const {
+    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
   }
   __device__ __forceinline__ static float f16raw(uint32_t x) { return __uint_as_float(x << 16); }
-  __device__ __forceinline__ void load_pre3(Pre3& p) const {
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-#pragma unroll
-      for (int m = 0; m < NKD; ++m) {
-        p.sb[j][m] = ck_frag(rSc, col(j), m);
-        p.ub[j][m] = ck_frag(rUc, col(j), m);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p.v[j][i] = raw16(rv, 16 * (i >> 2) + g4 + (i & 3), col(j));
-    }
-  }
   __device__ __forceinline__ void load_pre5(Pre5& p) const {
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
@@ -406,135 +246,48 @@ struct GradKernel {
         p.sr[j][m] = ck_frag(rSr, col(j), m);
         p.ur[j][m] = ck_frag(rUr, col(j), m);
       }
+      const uint32_t pc = (uint32_t)kpos(col(j));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 16 * (i >> 2) + g4 + (i & 3);
-        p.la[j][i] = raw16(rla, row, col(j));
-        p.q[j][i] = raw16(rq, row, col(j));
-        p.k[j][i] = raw16(rk, row, col(j));
+        const uint32_t off = (uint32_t)(row * D + col(j)) * 2u;
+        p.la[j][i] = raw16(rla, off);
+        p.q[j][i] = raw16(rq, off);
+        p.k[j][i] = raw16(rk, off);
+        p.w[j][i] = raw16(rW, (uint32_t)(row * D + pc) * 2u);  // checkpoint layout
       }
     }
   }
 
-  __device__ __forceinline__ void phase3(const Pre3& p) {
-    const auto& sb = p.sb;
-    // W = V - Kh S, from -V
-    f32x4 X[NCT][4];
+  // first part of dbeta: sum_j Xbar_rj W_rj over this wave's columns
+  __device__ __forceinline__ void dbeta_w(const Pre5& p) {
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) X[j][t][e] = -f16raw(p.v[j][4 * t + e]);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      bf16x8 fk[NKD];
-#pragma unroll
-      for (int m = 0; m < NKD; ++m) fk[m] = ar(C::KH, t, m);
-#pragma unroll
-      for (int m = 0; m < NKD; ++m)
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) X[j][t] = mfma_bf16_k32(X[j][t], fk[m], sb[j][m]);
-    }
-    f32x4 W[NCT][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const f32x4 bet = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * t + g4));
-#pragma unroll
-      for (int j = 0; j < NCT; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          W[j][t][e] = -X[j][t][e];
-          X[j][t][e] = bet[e] * W[j][t][e];
-        }
-    }
-    // Delta = T X: Delta_t = T_tt (X_t - sum_{u<t} L_tu Delta_u)
-    const uint32_t lo = (uint32_t)fresh_lane(l) * 8;
-    f32x4 Dl[NCT][4];
-    {
-      bf16x4 ft[4], fl[4][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        ft[t] = lds_ld<bf16x4>(smem, C::TI + t * C::FR16 + lo);
-#pragma unroll
-        for (int u = 0; u < t; ++u) fl[t][u] = lds_ld<bf16x4>(smem, C::LO + (t * (t - 1) / 2 + u) * C::FR16 + lo);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) {
-          f32x4 rr = X[j][t];
-#pragma unroll
-          for (int u = 0; u < t; ++u) rr = mfma_bf16_k16(rr, fl[t][u], pack4(Dl[j][u]));
-          Dl[j][t] = mfma_bf16_k16(zero4(), ft[t], pack4(rr));
-        }
-    }
-    store_tile_lds(C::DL, Dl);
-    // dDelta = Kb dU + P^T dO
-    const auto& ub = p.ub;
-    bf16x8 dob[NCT][NKT];
-#pragma unroll
-    for (int j = 0; j < NCT; ++j)
-#pragma unroll
-      for (int m = 0; m < NKT; ++m) dob[j][m] = tr_frag(C::DO, NCT * wave + j, m);
-    f32x4 Xb[NCT][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      bf16x8 fk[NKD], fp[NKT];
-#pragma unroll
-      for (int m = 0; m < NKD; ++m) fk[m] = ar(C::KB, t, m);
-#pragma unroll
-      for (int m = t / 2; m < NKT; ++m) fp[m] = fr64(C::PT, t, m);
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int m = 0; m < NKD; ++m) acc = mfma_bf16_k32(acc, fk[m], ub[j][m]);
-#pragma unroll
-        for (int m = t / 2; m < NKT; ++m) acc = mfma_bf16_k32(acc, fp[m], dob[j][m]);
-        Xb[j][t] = acc;
-      }
-    }
-    // Xbar = T^T dDelta: Xbar_t = T_tt^T (dDelta_t - sum_{u>t} L_ut^T Xbar_u)
-    {
-      bf16x4 ft[4], fl[4][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        ft[t] = lds_ld<bf16x4>(smem, C::TT + t * C::FR16 + lo);
-#pragma unroll
-        for (int u = t + 1; u < 4; ++u) fl[t][u] = lds_ld<bf16x4>(smem, C::LT + (u * (u - 1) / 2 + t) * C::FR16 + lo);
-      }
-#pragma unroll
-      for (int t = 3; t >= 0; --t)
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) {
-          f32x4 rr = Xb[j][t];
-#pragma unroll
-          for (int u = t + 1; u < 4; ++u) rr = mfma_bf16_k16(rr, fl[t][u], pack4(Xb[j][u]));
-          Xb[j][t] = mfma_bf16_k16(zero4(), ft[t], pack4(rr));
-        }
-    }
-    store_tile_lds(C::XB, Xb);
-    // dv = diag(b) Xbar; first part of dbeta: sum_j Xbar_rj W_rj over this wave's columns
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const f32x4 bet = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * t + g4));
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int row = 16 * t + g4 + e;
-        float s = 0.f;
+        float x = 0.f;
 #pragma unroll
-        for (int j = 0; j < NCT; ++j) {
-          st_bf16(rdv, row, col(j), bet[e] * Xb[j][t][e]);
-          s += Xb[j][t][e] * W[j][t][e];
-        }
-        s = row_sum16(s);
-        if (s0 == 15) lds_st<float>(smem, C::DBP + 4 * (wave * GCH + row), s);
+        for (int j = 0; j < NCT; ++j)
+          x += (float)lds_ld<bf16>(smem, C::XB + td(row, 2 * kpos(col(j)))) * f16raw(p.w[j][4 * t + e]);
+        x = row_sum16(x);
+        if (s0 == 15) lds_st<float>(smem, C::DBP + 4 * (wave * GCH + row), x);
       }
-    }
   }
 
-  // ------------------------------------------------------------ phase 4
+  static constexpr int greedy_wave(int K, int ntask, const int* weight) {
+    int load[C::NW] = {};
+    int w = 0;
+    for (int k = 0; k <= K && k < ntask; ++k) {
+      w = 0;
+      for (int i = 1; i < C::NW; ++i)
+        if (load[i] < load[w]) w = i;
+      load[w] += weight[k];
+    }
+    return w;
+  }
+
+  // ------------------------------------------------------------ phase 2
   // Block (R, S), R >= S, of the 64x64 gradients, from row tiles of dO, Xbar, Kh
   // (R) and of Delta, Kb (S), contracting over D.
   template <int R, int S>
@@ -607,7 +360,7 @@ struct GradKernel {
     }
   }
 
-  // ------------------------------------------------------------ phase 5 / 6
+  // ------------------------------------------------------------ phase 3
   // fp32 values a (rows 4g+e of one 16-row tile) and b (the next tile) as a
   // 32-deep B fragment over tokens, split into a bf16 part and the bf16 of the
   // remainder: two products with them carry about 16 bits of the operand.
@@ -726,7 +479,7 @@ struct GradKernel {
         dkb[t] = mfma_bf16_k32(dkb[t], fdpt, qhL);
       }
     }
-    // phase 6: the gate's chain rule
+    // the gate's chain rule
     float dg[4][4], ps[4][4];  // dg, and k e^-g (Delta dU^T) for the prefix over earlier tokens
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -795,50 +548,45 @@ struct GradKernel {
     s0 = l & 15;
     nrows = min(GCH, a.T - n * GCH);
     const size_t tok0 = (size_t)bh * a.T + (size_t)n * GCH;
-    const uint32_t in_bytes = (uint32_t)nrows * D * 2u, out_bytes = in_bytes;
+    const uint32_t in_bytes = (uint32_t)nrows * D * 2u;
     rq = make_rsrc(static_cast<const bf16*>(a.q) + tok0 * D, in_bytes);
     rk = make_rsrc(static_cast<const bf16*>(a.k) + tok0 * D, in_bytes);
-    rv = make_rsrc(static_cast<const bf16*>(a.v) + tok0 * D, in_bytes);
     rla = make_rsrc(static_cast<const bf16*>(a.la) + tok0 * D, in_bytes);
     rdo = make_rsrc(a.dO ? static_cast<const bf16*>(a.dO) + tok0 * D : nullptr, a.dO ? in_bytes : 0u);
     rbeta = make_rsrc(static_cast<const bf16*>(a.beta) + tok0, (uint32_t)nrows * 2u);
-    rdq = make_rsrc(a.dq + tok0 * D, out_bytes);
-    rdk = make_rsrc(a.dk + tok0 * D, out_bytes);
-    rdv = make_rsrc(a.dv + tok0 * D, out_bytes);
-    rdla = make_rsrc(a.dla + tok0 * D, out_bytes);
-    // the chunk's start state and dU, from the forward pass and the reverse chain
-    const size_t ck = ((size_t)bh * nch + n) * D * D;
-    rSr = make_rsrc(a.S_rows + ck, D * D * 2u);
-    rSc = make_rsrc(a.S_cols + ck, D * D * 2u);
-    rUr = make_rsrc(a.dU_rows + ck, D * D * 2u);
-    rUc = make_rsrc(a.dU_cols + ck, D * D * 2u);
+    rdq = make_rsrc(a.dq + tok0 * D, in_bytes);
+    rdk = make_rsrc(a.dk + tok0 * D, in_bytes);
+    rdla = make_rsrc(a.dla + tok0 * D, in_bytes);
+    // the chunk's checkpoints from the forward pass and the reverse chain
+    const size_t ck = (size_t)bh * nch + n;
+    rSr = make_rsrc(a.S_rows + ck * D * D, D * D * 2u);
+    rUr = make_rsrc(a.dU_rows + ck * D * D, D * D * 2u);
+    rW = make_rsrc(a.W + ck * GCH * D, GCH * D * 2u);
+    rDl = make_rsrc(a.Dl + ck * GCH * D, GCH * D * 2u);
+    rXb = make_rsrc(a.Xb + ck * GCH * D, GCH * D * 2u);
     init_offsets();
+    Pre5 p5;
+    load_pre5(p5);
     // zero halves of the 32-deep slots that pair a block of the upper triangle
     // with a stored one (nothing writes them): dP and Abar slots (0, 0) and
-    // (2, 1), second half; P^T, dP^T and Abar^T slots (1, 0) and (3, 1), first half
-    for (int t = threadIdx.x; t < 64 * 2 * 5; t += C::THREADS) {
+    // (2, 1), second half; dP^T and Abar^T slots (1, 0) and (3, 1), first half
+    for (int t = threadIdx.x; t < 64 * 2 * 4; t += C::THREADS) {
       const int which = t >> 7, lane = t & 63, sel = (t >> 6) & 1;
       uint32_t off;
       if (which < 2) {
         const uint32_t base = which == 0 ? C::DP : C::AB;
         off = base + (uint32_t)(((sel ? 2 * NKT + 1 : 0) * 64 + lane) * 16 + 8);
       } else {
-        const uint32_t base = which == 2 ? C::PT : (which == 3 ? C::DPT : C::ABT);
+        const uint32_t base = which == 2 ? C::DPT : C::ABT;
         off = base + (uint32_t)(((sel ? 3 * NKT + 1 : 1 * NKT) * 64 + lane) * 16);
       }
       lds_st<u32x2>(smem, off, u32x2{0u, 0u});
     }
     for (int i = threadIdx.x; i < 2 * C::NW * GCH; i += C::THREADS) lds_st<float>(smem, C::DBP + 4 * i, 0.f);
-    Pre3 p3;
-    load_pre3(p3);
-    phase1();
+    if (wave < C::NP) elementwise();
+    else copy_tiles();
     sync_lds();
-    p2_tasks<0>();
-    sync_lds();
-    phase3(p3);
-    Pre5 p5;
-    load_pre5(p5);
-    sync_lds();
+    dbeta_w(p5);
     p4_tasks<0>();
     sync_lds();
     if (wave == 0 && l < nrows) {

@@ -177,6 +177,8 @@ struct ChunkKernel {
   rsrc_t rq, rk, rv, rla, rbeta, ro;
   int Tlen, nch;
   int bh_seq;        // the sequence (segment) this workgroup works on
+  bf16* ck_w;        // this chunk's W = V - Kh S and Delta checkpoints (prefill with
+  bf16* ck_d;        // gradient checkpoints), else null
   int chunk0;        // chunks of the head's sequence before this segment
   float* snap_head;  // snapshot 0 of this head (prefill with snapshots), else null
   int wave, l;
@@ -691,6 +693,12 @@ struct ChunkKernel {
       for (int h = 0; h < C1B; ++h)
 #pragma unroll
         for (int j = 0; j < NCT; ++j) X[j][H0 + h] = F::mma(X[j][H0 + h], fk[h][m], sb[j][m]);
+    if constexpr (PREFILL && !BWD && NCT == 2) {
+      if (ck_w) {  // W = V - Kh S = -X here
+#pragma unroll
+        for (int h = 0; h < C1B; ++h) store_tile_bf16(ck_w, X[0], X[1], H0 + h, -1.f);
+      }
+    }
     const int kk = 4 * (l >> 4);
 #pragma unroll
     for (int h = 0; h < C1B; ++h) {
@@ -768,6 +776,12 @@ struct ChunkKernel {
 #pragma unroll
         for (int jj = 0; jj < ti; ++jj) rr = F::mma16(rr, fl[ti][jj], Dl[j][jj]);  // fl holds -L
         Dl[j][ti] = F::mma16(zero4(), ft[ti], rr);
+      }
+    }
+    if constexpr (PREFILL && !BWD && NCT == 2) {
+      if (ck_d) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) store_tile_bf16(ck_d, Dl[0], Dl[1], t, 1.f);
       }
     }
 #pragma unroll
@@ -890,14 +904,15 @@ struct ChunkKernel {
       }
   }
 
-  // This lane's entries of the state (bf16 columns only) as bf16, twice: into a
-  // row-major D x D matrix and into its transpose, each with the positions
-  // inside every 32-wide block of a row in the kpos order.  A row of either one
-  // then gives an MFMA fragment over the state's columns (rows) in one 16-byte
-  // read: the layouts the per-chunk gradients read the state and dU in.
+  // This lane's entries of the state (bf16 columns only) as bf16 into a
+  // row-major D x D matrix, and into its transpose unless cols is null, each
+  // with the positions inside every 32-wide block of a row in the kpos order.
+  // A row of either one then gives an MFMA fragment over the state's columns
+  // (rows) in one 16-byte read: the layout the per-chunk gradients read the
+  // state and dU in.
   __device__ __forceinline__ void store_state_bf16(bf16* rows, bf16* cols) const {
     if constexpr (C::BF) {
-      const rsrc_t rr = make_rsrc(rows, D * D * 2), rc = make_rsrc(cols, D * D * 2);
+      const rsrc_t rr = make_rsrc(rows, D * D * 2), rc = make_rsrc(cols, cols ? D * D * 2 : 0);
       const int g4 = 4 * (l >> 4);
       const uint32_t pc = (uint32_t)kpos(colb);  // colb even: colb + 1 sits at pc + 1
 #pragma unroll
@@ -907,6 +922,7 @@ struct ChunkKernel {
           __builtin_amdgcn_raw_buffer_store_b32(cvt2(S[0][ci][e], S[1][ci][e]), rr,
                                                 (uint32_t)((16 * ci + g4 + e) * D + pc) * 2u, 0, 0);
         const uint32_t pr = (uint32_t)kpos(16 * ci + g4);  // 4 consecutive rows, consecutive positions
+        if (!cols) continue;
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
           const u32x2 x = {cvt2(S[j][ci][0], S[j][ci][1]), cvt2(S[j][ci][2], S[j][ci][3])};
@@ -914,6 +930,19 @@ struct ChunkKernel {
         }
       }
     }
+  }
+
+  // Row tile t of a [CH][D] matrix held in accumulators (x[j]: this lane's
+  // columns colb + j), scaled by `sc`, as bf16 into a row-major [CH][D] matrix
+  // with kpos-ordered positions in each row (the gradients' checkpoint layout).
+  __device__ __forceinline__ void store_tile_bf16(bf16* dst, const f32x4* x0, const f32x4* x1, int t, float sc) const {
+    const rsrc_t r = make_rsrc(dst, CH * D * 2);
+    const int g4 = 4 * (l >> 4);
+    const uint32_t pc = (uint32_t)kpos(colb);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      __builtin_amdgcn_raw_buffer_store_b32(cvt2(sc * x0[t][e], sc * x1[t][e]), r,
+                                            (uint32_t)((16 * t + g4 + e) * D + pc) * 2u, 0, 0);
   }
 
   // Snapshot after chunk cc when it closes a snapshot interval of the sequence.
@@ -943,10 +972,14 @@ struct ChunkKernel {
         for (int e = 0; e < 4; ++e) X[j][t][e] = -vval(vr, j, 4 * t + e);
     if constexpr (!TIGHT) load_v(vr, cc + 1);
     if constexpr (PREFILL && !BWD) {
-      // state checkpoints for the gradients: the start state of every chunk
+      // checkpoints for the gradients: the start state of every chunk, and its
+      // W = V - Kh S and Delta (stored from c1)
+      ck_w = ck_d = nullptr;
       if (a.ck_rows) {
-        const size_t o = ((size_t)bh_seq * nch + cc) * D * D;
-        store_state_bf16(a.ck_rows + o, a.ck_cols + o);
+        const size_t o = (size_t)bh_seq * nch + cc;
+        store_state_bf16(a.ck_rows + o * D * D, nullptr);
+        ck_w = a.ck_w + o * CH * D;
+        ck_d = a.ck_d + o * CH * D;
       }
     }
     c1(X, stage(cc));
@@ -995,10 +1028,7 @@ struct ChunkKernel {
 #pragma unroll
         for (int j = 0; j < NCT; ++j) S[j][ci] = S[j][ci] * gm;
       }
-      {
-        const size_t o = ((size_t)bh_seq * nch + chunk) * D * D;
-        store_state_bf16(a.dU_rows + o, a.dU_cols + o);
-      }
+      store_state_bf16(a.dU_rows + ((size_t)bh_seq * nch + chunk) * D * D, nullptr);
 #pragma unroll
       for (int j = 0; j < NCT; ++j)
 #pragma unroll
@@ -1045,6 +1075,22 @@ struct ChunkKernel {
             for (int u = t + 1; u < 4; ++u) rr = F::mma16(rr, fl[t][u], Xb[j][u]);  // fl holds -L^T
             Xb[j][t] = F::mma16(zero4(), ft[t], rr);
           }
+        }
+      }
+      // Xbar for the per-chunk gradients, and dv = diag(b) Xbar (the output o
+      // pointer is dv here, in the inputs' dtype)
+      {
+        bf16* xb = a.ck_xb + ((size_t)bh_seq * nch + chunk) * CH * D;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) store_tile_bf16(xb, Xb[0], Xb[1], t, 1.f);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const f32x4 bet = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * t + kk));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                cvt2(bet[e] * Xb[0][t][e], bet[e] * Xb[1][t][e]), ro,
+                (uint32_t)((chunk * CH + 16 * t + kk + e) * D + colb) * 2u, 0, 0);
         }
       }
       // -diag(b) Xbar as B fragments over the chunk's tokens
@@ -1219,8 +1265,9 @@ struct ChunkKernel {
     rla = make_rsrc(reinterpret_cast<const char*>(a.la) + base, rowbytes);
     rbeta = make_rsrc(reinterpret_cast<const char*>(a.beta) + tok0 * C::ES, (uint32_t)Tlen * C::ES);
     if constexpr (PREFILL) rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, rowbytes);
-    // without o (a forward pass run for its state checkpoints) every store is dropped
-    if constexpr (PREFILL && !BWD)
+    // without o (a forward pass run for its state checkpoints) every store is
+    // dropped; the backward chain writes dv through it
+    if constexpr (PREFILL)
       ro = make_rsrc(a.o ? reinterpret_cast<const char*>(a.o) + base : nullptr, a.o ? rowbytes : 0u);
 
     // Every LDS byte the kernel reads is written by it first, except the halves

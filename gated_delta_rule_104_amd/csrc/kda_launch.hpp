@@ -40,18 +40,22 @@ struct ChunkArgs {
   // segment pass: a wave stops updating its map columns once they are all
   // exactly zero (they stay zero for finite inputs); 0 keeps updating them
   int map_skip = 1;
-  // gradients' checkpoints, [BH, nch, D, D] bf16 each, as a row-major matrix
-  // and its transpose, with the positions inside each 32-wide block of a row in
-  // the kpos order (null: none).  Prefill (bf16, one segment per head): the
-  // start state of every chunk; backward chain: dU = Diag(Gam) dS' of every chunk.
+  // gradients' checkpoints, bf16 row-major matrices with the positions inside
+  // each 32-wide block of a row in the kpos order (null: none).  Prefill (bf16,
+  // one segment per head): the start state of every chunk [BH, nch, D, D] and
+  // its W = V - Kh S and Delta [BH, nch, CH, D].  Backward chain: dU =
+  // Diag(Gam) dS' [BH, nch, D, D] and Xbar [BH, nch, CH, D] of every chunk
+  // (and dv through o).
   bf16* ck_rows = nullptr;
-  bf16* ck_cols = nullptr;
+  bf16* ck_w = nullptr;
+  bf16* ck_d = nullptr;
   bf16* dU_rows = nullptr;
-  bf16* dU_cols = nullptr;
+  bf16* ck_xb = nullptr;
 };
 
 // Reverse chain of the prefill gradients (bf16 inputs, one segment per head):
-// S0 = dS_T [BH, D, D] or null, S_out = dS0, v = dO, dU_rows/cols as above; nc
+// S0 = dS_T [BH, D, D] or null, S_out = dS0, v = dO, o = dv [BH, T, D],
+// dU_rows and ck_xb as above; nc
 // consumer waves per workgroup ({1, 2, 4} at D = 128, {1, 2} at D = 64).
 hipError_t launch_chunk_bwd(const ChunkArgs& a, int D, int nc, int nwg, hipStream_t stream);
 
@@ -105,18 +109,17 @@ size_t backward_ws_floats(long long BH, int T, int D, int split);
 struct BwGradArgs {
   const void* q;
   const void* k;
-  const void* v;
   const void* la;
   const void* beta;
   const void* dO;      // [BH, T, D] or null (= 0)
-  // [BH, nch, D, D] bf16, row-major and transposed as in ChunkArgs::ck_rows:
-  const bf16* S_rows;  // the start state of every chunk
-  const bf16* S_cols;
-  const bf16* dU_rows; // dU = Diag(Gam) dS' of every chunk
-  const bf16* dU_cols;
+  // checkpoints, bf16 row-major with kpos-ordered positions (ChunkArgs::ck_*):
+  const bf16* S_rows;  // the start state of every chunk [BH, nch, D, D]
+  const bf16* W;       // W = V - Kh S of every chunk [BH, nch, CH, D]
+  const bf16* Dl;      // Delta of every chunk
+  const bf16* dU_rows; // dU = Diag(Gam) dS' of every chunk [BH, nch, D, D]
+  const bf16* Xb;      // Xbar of every chunk [BH, nch, CH, D]
   bf16* dq;            // [BH, T, D], the inputs' dtype
   bf16* dk;
-  bf16* dv;
   bf16* dla;
   bf16* dbeta;         // [BH, T]
   int T;

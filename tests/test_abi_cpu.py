@@ -225,8 +225,9 @@ def backward(lib, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, dO=FAKE, 
 
 
 def test_backward_workspace_query(lib):
-    """bf16 (chunked form): the start state and dU of every chunk, each as two
-    bf16 D x D matrices, and one discarded fp32 end state per head.  fp32 (token steps):
+    """bf16 (chunked form): per chunk the start state and dU (bf16 D x D each)
+    and W, Delta, Xbar (bf16 64 x D each), and one discarded fp32 end state per
+    head.  fp32 (token steps):
     a checkpoint every 64 tokens plus 64 entering states (fp32 D x D) and 64
     fp32 D-vectors per head, then, with two workgroups per head (few heads),
     the second one's row sums of every token (dq, dk, dlog_alpha, dbeta:
@@ -238,9 +239,11 @@ def test_backward_workspace_query(lib):
     assert q(2, 3, 65, 128, 128, F32) == 6 * ((2 + 64) * 128 * 128 + 64 * 128 + 65 * (3 * 128 + 1)) * 4
     assert q(64, 32, 65, 128, 128, F32) == 2048 * ((2 + 64) * 128 * 128 + 64 * 128) * 4
     assert q(1, 1, 0, 64, 64, F32) == (64 * 64 * 64 + 64 * 64) * 4
-    assert q(1, 1, 64, 64, 64, BF16) == (2 * 1 + 1) * 64 * 64 * 4
-    assert q(2, 3, 65, 128, 128, BF16) == 6 * (2 * 2 + 1) * 128 * 128 * 4
-    assert q(4, 32, 8192, 128, 128, BF16) == 128 * (2 * 128 + 1) * 128 * 128 * 4
+    def chunked(BH, nch, D):
+        return BH * (nch * (2 * D * D + 3 * 64 * D) * 2 + D * D * 4)
+    assert q(1, 1, 64, 64, 64, BF16) == chunked(1, 1, 64) == 57344
+    assert q(2, 3, 65, 128, 128, BF16) == chunked(6, 2, 128)
+    assert q(4, 32, 8192, 128, 128, BF16) == chunked(128, 128, 128)
     assert q(1, 1, 0, 64, 64, BF16) == 64 * 64 * 4
     assert q(1, 1, 64, 64, 128, BF16) == 0 and q(1, 1, 64, 96, 96, F32) == 0 and q(0, 1, 64, 64, 64, BF16) == 0
     assert q(1, 1, 64, 64, 64, 5) == 0
