@@ -316,7 +316,7 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
                                   long long BH, int T, int t0, int Tend, int Tseg, int D, bool bf,
                                   hipStream_t stream, const char* what, const Snap& sn = Snap(),
                                   int nc = 0, kda::bf16* ck_rows = nullptr, kda::bf16* ck_w = nullptr,
-                                  kda::bf16* ck_d = nullptr) {
+                                  kda::bf16* ck_d = nullptr, kda::bf16* ck_a = nullptr) {
   const int n = Tend - t0;
   const int G = n > 0 ? (int)(((long long)n + Tseg - 1) / Tseg) : 1;  // no tokens: copy the start state
   const long long nseq = BH * G;
@@ -329,7 +329,7 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
   a.vsplit = nt / (nc * kda::chunk_tiles_per_wave(bf));
   a.snap = sn.n > 0 ? sn.p : nullptr; a.snap_chunks = sn.chunks > 0 ? sn.chunks : 1;
   a.nsnap = sn.n; a.H = sn.H;
-  a.ck_rows = ck_rows; a.ck_w = ck_w; a.ck_d = ck_d;
+  a.ck_rows = ck_rows; a.ck_w = ck_w; a.ck_d = ck_d; a.ck_a = ck_a;
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (log_on())
@@ -558,21 +558,24 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
 
 // Workspace of the chunked backward (bf16 inputs), per chunk-head: the start
 // state and dU = Diag(Gam) dS' (bf16 D x D each), W = V - Kh S, Delta and
-// Xbar (bf16 64 x D each), all row-major with kpos-ordered positions; then the
+// Xbar (bf16 64 x D each), all row-major with kpos-ordered positions, and the
+// 10 lower 16x16 blocks of strict_lower(Kh Kb^T) (bf16, lane order); then the
 // forward pass's end state, which is not needed (fp32 [BH, D, D]).  In floats.
+constexpr long long kAckElems = 10 * 256;  // bf16 elements of the blocks of one chunk
 size_t chunk_bw_ws_floats(long long BH, int T, int D) {
   const long long nch = (T + 63) / 64;
-  return (size_t)(BH * nch * (2 * D + 3 * 64) * D / 2 + BH * D * D);
+  return (size_t)(BH * nch * ((2 * D + 3 * 64) * D + kAckElems) / 2 + BH * D * D);
 }
 
 // Gradients of the prefill in the chunked form (bf16 inputs; arguments already
 // validated):
 //  1. beside each other: the forward pass from S0, which keeps the start state,
-//     W = V - Kh S and Delta of every chunk (its outputs are not written), on
+//     W = V - Kh S, Delta and strict_lower(Kh Kb^T) of every chunk (its outputs
+//     are not written), on
 //     the side stream; and the reverse chain from dS_T over the chunks, last to
 //     first, which keeps dU = Diag(Gam) dS' and Xbar of every chunk and writes
 //     dv and dS0 (it needs no forward state);
-//  2. the per-chunk gradients, one workgroup per (head, chunk).
+//  2. the per-chunk gradients, two workgroups (column halves) per (head, chunk).
 kda_status chunk_backward(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                           const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                           void* dlog_alpha, void* dbeta, float* dS0, int B, int H, int T, int D, float* ws,
@@ -585,7 +588,8 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
   kda::bf16* W = dU_rows + nS;
   kda::bf16* Dl = W + nC;
   kda::bf16* Xb = Dl + nC;
-  float* ST = reinterpret_cast<float*>(Xb + nC);  // [BH, D, D], discarded
+  kda::bf16* Ack = Xb + nC;
+  float* ST = reinterpret_cast<float*>(Ack + (size_t)BH * nch * kAckElems);  // [BH, D, D], discarded
   const int nt = D / 16;
   kda::ChunkArgs r;
   r.q = q; r.k = k; r.v = dO; r.la = log_alpha; r.beta = beta;
@@ -615,7 +619,7 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
     if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess || (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
       return hip_fail(e, "kda_prefill_backward fork");
     st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, nullptr, ST, BH, T, 0, T, T, D, true, ss->s,
-                                "kda_prefill_backward forward checkpoints", Snap(), ncb, S_rows, W, Dl);
+                                "kda_prefill_backward forward checkpoints", Snap(), ncb, S_rows, W, Dl, Ack);
     if (st == KDA_OK && (e = kda::launch_chunk_bwd(r, D, ncb, (int)(BH * r.vsplit), stream)) != hipSuccess)
       st = hip_fail(e, "kda_prefill_backward reverse chain");
     // join even if a launch above failed, so the side stream's work is waited for
@@ -625,7 +629,7 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
   }
   kda::BwGradArgs g;
   g.q = q; g.k = k; g.la = log_alpha; g.beta = beta; g.dO = dO;
-  g.S_rows = S_rows; g.W = W; g.Dl = Dl; g.dU_rows = dU_rows; g.Xb = Xb;
+  g.S_rows = S_rows; g.W = W; g.Dl = Dl; g.A = Ack; g.dU_rows = dU_rows; g.Xb = Xb;
   g.dq = static_cast<kda::bf16*>(dq); g.dk = static_cast<kda::bf16*>(dk_);
   g.dla = static_cast<kda::bf16*>(dlog_alpha); g.dbeta = static_cast<kda::bf16*>(dbeta); g.T = T;
   if ((e = kda::launch_bwgrad(g, (int)BH, D, stream)) != hipSuccess) return hip_fail(e, "kda_prefill_backward gradients");

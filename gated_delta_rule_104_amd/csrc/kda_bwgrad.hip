@@ -8,7 +8,7 @@
 // 开源日来了", section "FlashKDA", for the chunking; training is what the K3
 // report also speeds up with FlashKDA)
 //   g = cumsum(log alpha),  Qh = q e^g,  Kh = k e^g,  Kb = k e^-g,  Gam = e^(g_C)
-//   L = diag(b) strict_lower(Kh Kb^T),  P = lower(Qh Kb^T),  T = (I + L)^-1
+//   A = strict_lower(Kh Kb^T),  L = diag(b) A,  P = lower(Qh Kb^T),  T = (I + L)^-1
 //   W = V - Kh S,  X = diag(b) W,  Delta = T X
 //   O = Qh S + P Delta,  S' = Diag(Gam) (S + Kb^T Delta)
 // the chain rule gives, per chunk:
@@ -17,7 +17,7 @@
 //   dQh = dO S^T + dP Kb
 //   dKh = -diag(b) Xbar S^T + Abar Kb
 //   dKb = Delta dU^T + Abar^T Kh + dP^T Qh
-//   dbeta_r = sum_j Xbar_rj W_rj + sum_{s<r} Lbar_rs (Kh Kb^T)_rs
+//   dbeta_r = sum_j Xbar_rj W_rj + sum_{s<r} Lbar_rs A_rs
 //   dq = dQh e^g,  dk = dKh e^g + dKb e^-g
 //   dlog_alpha_r = sum_{t >= r} dg_t + rowsum(dU . S) + sum_{s < r} k_s e^-g_s (Delta dU^T)_s
 //     with dg = q dq + k (dKh e^g - (dKb - Delta dU^T) e^-g)
@@ -27,15 +27,16 @@
 // the Delta dU^T piece of dKb cancel for s >= r, so that sum_{s < r} is formed
 // directly, which in bf16 products avoids a cancellation between large terms.
 //
-// The forward pass stores S, W and Delta of every chunk, and the reverse chain
-// dU and Xbar (and writes dv); this kernel reads them.  One workgroup per
-// (head, chunk), one wave per 16 columns of the head dimension (8 waves at
-// d = 128, two per SIMD).  Phases, each ended by a workgroup barrier:
-//   1. elementwise: the cumulative gate (DPP row scan) and the bf16 operand
-//      tiles Kh, Kb, with beta, into LDS; beside it the other waves copy dO,
-//      Delta and Xbar into LDS tiles;
-//   2. the 64 x 64 gradients dP, dP^T, Abar, Abar^T (as MFMA A fragments) and
-//      dbeta;
+// The forward pass stores S, W, Delta and A of every chunk, and the reverse
+// chain dU and Xbar (and writes dv); this kernel reads them.  Two workgroups
+// per (head, chunk), each owning half of the key dimension's columns with one
+// wave per 16 columns (4 waves at d = 128).  Each needs about 74 KiB of LDS,
+// so two run on a CU at once and one's loads overlap the other's arithmetic.
+// Phases, each ended by a workgroup barrier:
+//   1. every wave copies its share of dO, Delta and Xbar into LDS tiles (all
+//      loads issued before the first store);
+//   2. the 64 x 64 gradients dP, dP^T, Abar, Abar^T (as MFMA A fragments), and
+//      in the first half's workgroup dbeta;
 //   3. per wave, a 16-column tile of the key dimension: dQh, dKh, dKb (the
 //      products with the 64 x 64 gradients on fp32 Kb, Kh, Qh split into two
 //      bf16 parts), then the gate's chain rule, written out per (token, channel).
@@ -54,41 +55,44 @@ constexpr float G_LOG2E = 1.4426950408889634f;
 
 template <int D>
 struct GradCfg {
-  static constexpr int NW = D / 16;            // waves: one 16-column tile of the head dimension each
+  static constexpr int NW = D / 32;            // waves per workgroup: 16 columns each, half of D
   static constexpr int THREADS = 64 * NW;
   static constexpr int NCT = 1;                // 16-column tiles per wave
   static constexpr int NKD = D / 32;           // 32-deep k blocks over channels
   static constexpr int NKT = GCH / 32;         // 32-deep k blocks over the chunk's tokens
-  static constexpr int NP = D / 32;            // waves that build the elementwise tiles
   static constexpr int R_TD = D * 2;           // bf16 row of a [64][D] tile
   static constexpr int TD_TILE = 16 * R_TD + 16;
   static constexpr int TD_SZ = 4 * TD_TILE;
-  static constexpr int FR64 = 4 * NKT * 64 * 16;  // a 64x64 matrix as 32-deep A fragments
-  static constexpr uint32_t KH = 0;
-  static constexpr uint32_t KB = KH + TD_SZ;
-  static constexpr uint32_t DO = KB + TD_SZ;
+  // A 64x64 block-triangular matrix as 32-deep A fragments: the 6 of its 8
+  // (row tile, k block) slots that hold a nonzero block
+  static constexpr int FRC = 6 * 64 * 16;
+  static constexpr uint32_t DO = 0;
   static constexpr uint32_t DL = DO + TD_SZ;     // Delta
   static constexpr uint32_t XB = DL + TD_SZ;     // Xbar
-  static constexpr uint32_t DP = XB + TD_SZ;     // dP
-  static constexpr uint32_t DPT = DP + FR64;     // dP^T
-  static constexpr uint32_t AB = DPT + FR64;     // Abar
-  static constexpr uint32_t ABT = AB + FR64;     // Abar^T
-  static constexpr uint32_t BETA = ABT + FR64;   // beta [64] fp32
-  static constexpr uint32_t DBP = BETA + 4 * GCH;  // dbeta partials [2 NW][64] fp32
-  static constexpr uint32_t LDS = DBP + 4 * GCH * 2 * NW;
-  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static constexpr uint32_t DP = XB + TD_SZ;     // dP (lower)
+  static constexpr uint32_t DPT = DP + FRC;      // dP^T (upper)
+  static constexpr uint32_t AB = DPT + FRC;      // Abar (lower)
+  static constexpr uint32_t ABT = AB + FRC;      // Abar^T (upper)
+  static constexpr uint32_t BETA = ABT + FRC;    // beta [64] fp32
+  static constexpr uint32_t DBP = BETA + 4 * GCH;  // dbeta partials [1 + NW][64] fp32
+  static constexpr uint32_t LDS = DBP + 4 * GCH * (1 + NW);
+  static_assert(2 * LDS <= 160 * 1024, "two workgroups per CU");
   static_assert(LDS % 16 == 0, "LDS alignment");
+  static_assert(D / NW == 32, "a row of dbeta's first part is 32 channels per lane");
 };
 
 template <int D>
 struct GradKernel {
   using C = GradCfg<D>;
-  static constexpr int NCT = C::NCT, NKD = C::NKD, NKT = C::NKT;
+  static constexpr int NW = C::NW, NCT = C::NCT, NKD = C::NKD, NKT = C::NKT;
+  static constexpr int NP4 = 10;                   // lower blocks (R, S) of the 64x64 gradients
+  static constexpr int NTW = (NP4 + NW - 1) / NW;  // of them per wave
   char* smem;
   BwGradArgs a;
   int wave, l, g4, s0;
+  int half;   // which half of the key dimension's columns
   int nrows;  // valid tokens of this chunk
-  rsrc_t rq, rk, rla, rbeta, rdo, rdq, rdk, rdla, rSr, rUr, rW, rDl, rXb;
+  rsrc_t rq, rk, rla, rbeta, rdo, rdq, rdk, rdla, rSr, rUr, rW, rDl, rXb, rA;
   uint32_t oTD[NKD];   // A fragments of [64][D] tiles, row tile 0
 
   __device__ __forceinline__ static uint32_t td(int row, int byte) {
@@ -98,14 +102,30 @@ struct GradKernel {
   __device__ __forceinline__ bf16x8 ar(uint32_t tile, int t, int m) const {
     return lds_ld<bf16x8>(smem, tile + oTD[m] + t * C::TD_TILE);
   }
-  // 32-deep A fragment slot of a 64x64 matrix stored at `base`: row tile t, k block m
-  __device__ __forceinline__ bf16x8 fr64(uint32_t base, int t, int m) const {
-    return lds_ld<bf16x8>(smem, base + ((t * NKT + m) * 64 + fresh_lane(l)) * 16);
+  // Compact slots of the 32-deep A fragments of a 64x64 matrix: row tile t, k
+  // block m.  Lower block-triangular (dP, Abar): m <= t/2; upper (their
+  // transposes): m >= (t-1)/2.
+  __device__ __forceinline__ static constexpr int lo_idx(int t, int m) { return t < 2 ? t : 2 * t - 2 + m; }
+  __device__ __forceinline__ static constexpr int up_idx(int t, int m) { return t < 2 ? 2 * t + m : t + 2; }
+  __device__ __forceinline__ bf16x8 frlo(uint32_t base, int t, int m) const {
+    return lds_ld<bf16x8>(smem, base + (lo_idx(t, m) * 64 + fresh_lane(l)) * 16);
+  }
+  __device__ __forceinline__ bf16x8 frup(uint32_t base, int t, int m) const {
+    return lds_ld<bf16x8>(smem, base + (up_idx(t, m) * 64 + fresh_lane(l)) * 16);
   }
   __device__ __forceinline__ void put16(uint32_t off, const f32x4& v) { lds_st<bf16x4>(smem, off, pack4(v)); }
-  // 32-deep slot of block (row tile R, column tile S) of a 64x64 matrix: its 4 values
-  __device__ __forceinline__ uint32_t slot64(uint32_t base, int R, int S) const {
-    return base + ((R * NKT + S / 2) * 64 + fresh_lane(l)) * 16 + (S % 2) * 8;
+  // this lane's 4 values of block (R, S) in the slot of a lower / upper matrix
+  __device__ __forceinline__ uint32_t slot_lo(uint32_t base, int R, int S) const {
+    return base + (lo_idx(R, S / 2) * 64 + fresh_lane(l)) * 16 + (S % 2) * 8;
+  }
+  __device__ __forceinline__ uint32_t slot_up(uint32_t base, int R, int S) const {
+    return base + (up_idx(R, S / 2) * 64 + fresh_lane(l)) * 16 + (S % 2) * 8;
+  }
+  // x + a.b over bf16 pair e of two 8-element fragments, in fp32
+  __device__ __forceinline__ static float dot2(const bf16x8& a, const bf16x8& b, int e, float x) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+    const bf16x2 u = {a[2 * e], a[2 * e + 1]}, v = {b[2 * e], b[2 * e + 1]};
+    return __builtin_amdgcn_fdot2_f32_bf16(u, v, x, false);
   }
 
   __device__ __forceinline__ void init_offsets() {
@@ -116,72 +136,15 @@ struct GradKernel {
   }
 
   // ------------------------------------------------------------ phase 1
-  // Wave pw < NP: lane (tg = l%16, cs = l/16) owns tokens 4tg .. 4tg+3 and
-  // channels 32pw + 8cs .. +7; a channel's 16 token groups form one DPP row.
-  __device__ __forceinline__ void elementwise() {
-    const int tg = l & 15, cs = l >> 4;
-    const int ch = 32 * wave + 8 * cs;
-    Raw8<bf16> rla_[4], rk_[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t off = (uint32_t)((4 * tg + i) * D + ch) * 2;
-      raw_load<bf16>(rla_[i], rla, off);
-      raw_load<bf16>(rk_[i], rk, off);
-    }
-    float bet = 0.f;
-    if (wave == 0)
-      bet = __uint_as_float((uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rbeta, 2 * l, 0, 0) << 16);
-    float g[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      raw_f32<bf16>(rla_[i], g[i]);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) g[i][c] *= G_LOG2E;
-    }
-    float exc[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      g[1][c] += g[0][c];
-      g[2][c] += g[1][c];
-      g[3][c] += g[2][c];
-      float x = g[3][c];
-      x += dpp<DPP_ROW_SHR + 1>(x);
-      x += dpp<DPP_ROW_SHR + 2>(x);
-      x += dpp<DPP_ROW_SHR + 4>(x);
-      x += dpp<DPP_ROW_SHR + 8>(x);
-      exc[c] = dpp<DPP_ROW_SHR + 1>(x);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float kk[8];
-      raw_f32<bf16>(rk_[i], kk);
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        bf16x4 h, b;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float gg = g[i][4 * hlf + c] + exc[4 * hlf + c];
-          h[c] = (bf16)(kk[4 * hlf + c] * __builtin_amdgcn_exp2f(gg));
-          b[c] = (bf16)(kk[4 * hlf + c] * __builtin_amdgcn_exp2f(-gg));
-        }
-        const uint32_t o = td(4 * tg + i, 2 * kpos(ch + 4 * hlf));
-        lds_st<bf16x4>(smem, C::KH + o, h);
-        lds_st<bf16x4>(smem, C::KB + o, b);
-      }
-    }
-    if (wave == 0) lds_st<float>(smem, C::BETA + 4 * l, bet);
-  }
-
-  // Waves NP .. NW-1: dO (the input, plain channel order) and Delta, Xbar (the
-  // checkpoints, already kpos-ordered) into their LDS tiles, 16 bytes at a
-  // time: every load is issued before the first store, so that their latencies
-  // overlap.
+  // dO (the input, plain channel order) and Delta, Xbar (the checkpoints,
+  // already kpos-ordered) into their LDS tiles, 16 bytes at a time: every load
+  // is issued before the first store, so that their latencies overlap.
   __device__ __forceinline__ void copy_tiles() {
     constexpr int PIECES = GCH * D / 8;  // 16-byte pieces of one tile
-    constexpr int NL = (C::NW - C::NP) * 64;
+    constexpr int NL = NW * 64;
     static_assert(PIECES % NL == 0, "each load stays in one tile");
     constexpr int PER = 3 * PIECES / NL, PER_TILE = PIECES / NL;
-    const int x0 = (wave - C::NP) * 64 + l;
+    const int x0 = wave * 64 + l;
     u32x4 w[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -217,9 +180,9 @@ struct GradKernel {
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (bf16)x), r, (uint32_t)(row * D + c) * 2u, 0, 0);
   }
 
-  // Lane l works on column c = 16 wave + l%16 of the head dimension, rows
-  // 16t + 4g + e of the chunk (accumulator layout).
-  __device__ __forceinline__ int col(int j) const { return 16 * (NCT * wave + j) + s0; }
+  // Lane l works on column c = D/2 half + 16 wave + l%16 of the head
+  // dimension, rows 16t + 4g + e of the chunk (accumulator layout).
+  __device__ __forceinline__ int col(int j) const { return half * (D / 2) + 16 * (NCT * wave + j) + s0; }
 
   // Row c of a checkpoint matrix stored with kpos-ordered rows, k block m: one
   // 16-byte read is the B fragment over that block.
@@ -227,12 +190,12 @@ struct GradKernel {
     return __builtin_bit_cast(bf16x8, bload128(r, (uint32_t)(c * D + 32 * m + 2 * g4) * 2u));
   }
 
-  // Global data of phases 2 and 3, loaded at the start so that the loads are in
-  // flight across phase 1 (the barriers wait only for LDS).  bf16 values at this
-  // lane's accumulator positions are kept as raw 16-bit loads.
+  // Global data of phase 3, loaded at the start so that the loads are in
+  // flight across phases 1 and 2 (the barriers wait only for LDS).  bf16
+  // values at this lane's accumulator positions are kept as raw 16-bit loads.
   struct Pre5 {
     bf16x8 sr[NCT][NKD], ur[NCT][NKD];  // S and dU rows as B fragments over their columns
-    uint32_t la[NCT][16], q[NCT][16], k[NCT][16], w[NCT][16];
+    uint32_t la[NCT][16], q[NCT][16], k[NCT][16];
   };
   __device__ __forceinline__ uint32_t raw16(rsrc_t r, uint32_t off) const {
     return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
@@ -246,7 +209,6 @@ struct GradKernel {
         p.sr[j][m] = ck_frag(rSr, col(j), m);
         p.ur[j][m] = ck_frag(rUr, col(j), m);
       }
-      const uint32_t pc = (uint32_t)kpos(col(j));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 16 * (i >> 2) + g4 + (i & 3);
@@ -254,64 +216,69 @@ struct GradKernel {
         p.la[j][i] = raw16(rla, off);
         p.q[j][i] = raw16(rq, off);
         p.k[j][i] = raw16(rk, off);
-        p.w[j][i] = raw16(rW, (uint32_t)(row * D + pc) * 2u);  // checkpoint layout
       }
     }
   }
 
-  // first part of dbeta: sum_j Xbar_rj W_rj over this wave's columns
-  __device__ __forceinline__ void dbeta_w(const Pre5& p) {
+  // dbeta's inputs, first half's workgroup only: W over 32 channels of a row
+  // (lane x = 64 wave + l: row x / NW, channels 32 (x % NW) ..), and the blocks
+  // of A of this wave's phase-2 tasks (task K: block 9 - K of the forward's
+  // order, this lane's 4 values)
+  struct PreB {
+    u32x4 w[4];
+    u32x2 ar[NTW];
+  };
+  __device__ __forceinline__ void load_preb(PreB& p) const {
+    const int x = wave * 64 + l, row = x / NW, c0 = 32 * (x % NW);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 4; ++i) p.w[i] = bload128(rW, (uint32_t)(row * D + c0 + 8 * i) * 2u);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * t + g4 + e;
-        float x = 0.f;
-#pragma unroll
-        for (int j = 0; j < NCT; ++j)
-          x += (float)lds_ld<bf16>(smem, C::XB + td(row, 2 * kpos(col(j)))) * f16raw(p.w[j][4 * t + e]);
-        x = row_sum16(x);
-        if (s0 == 15) lds_st<float>(smem, C::DBP + 4 * (wave * GCH + row), x);
-      }
+    for (int i = 0; i < NTW; ++i) {
+      const int K = wave + NW * i;
+      const uint32_t off = (uint32_t)(((NP4 - 1 - min(K, NP4 - 1)) * 64 + l) * 8);
+      p.ar[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rA, off, 0, 0));
+    }
   }
 
-  static constexpr int greedy_wave(int K, int ntask, const int* weight) {
-    int load[C::NW] = {};
-    int w = 0;
-    for (int k = 0; k <= K && k < ntask; ++k) {
-      w = 0;
-      for (int i = 1; i < C::NW; ++i)
-        if (load[i] < load[w]) w = i;
-      load[w] += weight[k];
+  // first part of dbeta: sum_j Xbar_rj W_rj (both checkpoints in the kpos order)
+  __device__ __forceinline__ void dbeta_w(const PreB& p) {
+    const int x = wave * 64 + l, row = x / NW, c0 = 32 * (x % NW);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 xb = lds_ld<bf16x8>(smem, C::XB + td(row, 2 * (c0 + 8 * i)));
+      const bf16x8 w = __builtin_bit_cast(bf16x8, p.w[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = dot2(xb, w, e, s);
     }
-    return w;
+#pragma unroll
+    for (int o = 1; o < NW; o <<= 1) s += __shfl_xor(s, o);
+    if (x % NW == 0) lds_st<float>(smem, C::DBP + 4 * row, s);
   }
 
   // ------------------------------------------------------------ phase 2
-  // Block (R, S), R >= S, of the 64x64 gradients, from row tiles of dO, Xbar, Kh
-  // (R) and of Delta, Kb (S), contracting over D.
-  template <int R, int S>
-  __device__ __forceinline__ void p4_tile() {
-    bf16x8 fo[NKD], fd[NKD], fxb[NKD], fkh[NKD], fkb[NKD];
+  // Block (R, S), R >= S, of the 64x64 gradients, from row tiles of dO, Xbar
+  // (R) and of Delta (S), contracting over D; with dbeta, its second part from
+  // the block of A (ar: this lane's values A[16R + l%16][16S + 4g + e]).
+  template <int R, int S, bool DB>
+  __device__ __forceinline__ void p4_tile(const u32x2& ar) {
+    bf16x8 fo[NKD], fd[NKD], fxb[NKD];
 #pragma unroll
     for (int m = 0; m < NKD; ++m) {
-      fo[m] = ar(C::DO, R, m);
-      fd[m] = ar(C::DL, S, m);
-      fxb[m] = ar(C::XB, R, m);
-      fkh[m] = ar(C::KH, R, m);
-      fkb[m] = ar(C::KB, S, m);
+      fo[m] = this->ar(C::DO, R, m);
+      fd[m] = this->ar(C::DL, S, m);
+      fxb[m] = this->ar(C::XB, R, m);
     }
     const float bl = lds_ld<float>(smem, C::BETA + 4 * (16 * R + s0));
     const f32x4 bet4 = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * R + g4));
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4(), a4 = zero4(), a5 = zero4();
+    f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4(), a4 = zero4();
 #pragma unroll
     for (int m = 0; m < NKD; ++m) {
       a1 = mfma_bf16_k32(a1, fd[m], fo[m]);    // dP[16R + s0][16S + 4g + e]
       a2 = mfma_bf16_k32(a2, fo[m], fd[m]);    // dP[16R + 4g + e][16S + s0]
       a3 = mfma_bf16_k32(a3, fd[m], fxb[m]);   // -Lbar[16R + s0][16S + 4g + e]
       a4 = mfma_bf16_k32(a4, fxb[m], fd[m]);   // -Lbar[16R + 4g + e][16S + s0]
-      a5 = mfma_bf16_k32(a5, fkh[m], fkb[m]);  // (Kh Kb^T)[16R + 4g + e][16S + s0]
     }
     f32x4 v1, v2, v3, v4;
 #pragma unroll
@@ -323,40 +290,44 @@ struct GradKernel {
       v3[e] = st1 ? -bl * a3[e] : 0.f;       // Abar = diag(b) Lbar
       v4[e] = st2 ? -bet4[e] * a4[e] : 0.f;
     }
-    put16(slot64(C::DP, R, S), v1);
-    put16(slot64(C::DPT, S, R), v2);
-    put16(slot64(C::AB, R, S), v3);
-    put16(slot64(C::ABT, S, R), v4);
-    // second part of dbeta: sum_{s < r} Lbar_rs (Kh Kb^T)_rs, rows 16R + 4g + e
+    put16(slot_lo(C::DP, R, S), v1);
+    put16(slot_up(C::DPT, S, R), v2);
+    put16(slot_lo(C::AB, R, S), v3);
+    put16(slot_up(C::ABT, S, R), v4);
+    if constexpr (DB) {
+      // sum_{s < r} Lbar_rs A_rs over the block, row r = 16R + l%16
+      const float av[4] = {__uint_as_float(ar[0] << 16), __uint_as_float(ar[0] & 0xffff0000u),
+                           __uint_as_float(ar[1] << 16), __uint_as_float(ar[1] & 0xffff0000u)};
+      float x = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool st2 = R > S || g4 + e > s0;
-      float x = st2 ? -a4[e] * a5[e] : 0.f;
-      x = row_sum16(x);
-      if (s0 == 15) {
-        const uint32_t o = C::DBP + 4 * ((C::NW + wave) * GCH + 16 * R + g4 + e);
+      for (int e = 0; e < 4; ++e) {
+        const bool st1 = R > S || s0 > g4 + e;
+        x -= st1 ? a3[e] * av[e] : 0.f;
+      }
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      if (l < 16) {
+        const uint32_t o = C::DBP + 4 * ((1 + wave) * GCH + 16 * R + s0);
         lds_st<float>(smem, o, lds_ld<float>(smem, o) + x);
       }
     }
   }
   static constexpr int p4_r(int K) {
-    const int rr[10] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
+    const int rr[NP4] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
     return rr[K];
   }
   static constexpr int p4_s(int K) {
-    const int ss[10] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
+    const int ss[NP4] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
     return ss[K];
   }
-  static constexpr int p4_wave(int K) {
-    int wt[10] = {1, 1, 1, 1, 1, 1, 1, 1, 1, 1};
-    return greedy_wave(K, 10, wt);
-  }
-  template <int K>
-  __device__ __forceinline__ void p4_tasks() {
-    if constexpr (K < 10) {
-      constexpr int W = p4_wave(K);
-      if (W == wave) p4_tile<p4_r(K), p4_s(K)>();
-      p4_tasks<K + 1>();
+  // task K (block (p4_r, p4_s), at I(I+1)/2 + J = 9 - K in the forward's
+  // order) runs on wave K % NW
+  template <int K, bool DB>
+  __device__ __forceinline__ void p4_tasks(const PreB& pb) {
+    if constexpr (K < NP4) {
+      static_assert(p4_r(K) * (p4_r(K) + 1) / 2 + p4_s(K) == NP4 - 1 - K, "block order");
+      if (K % NW == wave) p4_tile<p4_r(K), p4_s(K), DB>(pb.ar[K / NW]);
+      p4_tasks<K + 1, DB>(pb);
     }
   }
 
@@ -397,7 +368,7 @@ struct GradKernel {
 #pragma unroll
     for (int m = 0; m < NKD; ++m)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dgc += (float)sr[m][e] * (float)ur[m][e];
+      for (int e = 0; e < 4; ++e) dgc = dot2(sr[m], ur[m], e, dgc);
     // rowsum(dU . S): the four lane groups (l%16 fixed) hold the rest of the row's sum
     dgc += __shfl_xor(dgc, 16);
     dgc += __shfl_xor(dgc, 32);
@@ -464,7 +435,7 @@ struct GradKernel {
       split8(qv[2 * m] * eg[2 * m], qv[2 * m + 1] * eg[2 * m + 1], qhH, qhL);
 #pragma unroll
       for (int t = 2 * m; t < 4; ++t) {  // m <= t / 2
-        const bf16x8 fdp = fr64(C::DP, t, m), fab = fr64(C::AB, t, m);
+        const bf16x8 fdp = frlo(C::DP, t, m), fab = frlo(C::AB, t, m);
         dqh[t] = mfma_bf16_k32(dqh[t], fdp, kbH);
         dqh[t] = mfma_bf16_k32(dqh[t], fdp, kbL);
         dkh[t] = mfma_bf16_k32(dkh[t], fab, kbH);
@@ -472,7 +443,7 @@ struct GradKernel {
       }
 #pragma unroll
       for (int t = 0; t <= 2 * m + 1; ++t) {  // m >= t / 2
-        const bf16x8 fabt = fr64(C::ABT, t, m), fdpt = fr64(C::DPT, t, m);
+        const bf16x8 fabt = frup(C::ABT, t, m), fdpt = frup(C::DPT, t, m);
         dkb[t] = mfma_bf16_k32(dkb[t], fabt, khH);
         dkb[t] = mfma_bf16_k32(dkb[t], fabt, khL);
         dkb[t] = mfma_bf16_k32(dkb[t], fdpt, qhH);
@@ -540,8 +511,15 @@ struct GradKernel {
 
   __device__ __forceinline__ void run() {
     const int nch = (a.T + GCH - 1) / GCH;
-    const int bh = blockIdx.x / nch;
-    const int n = blockIdx.x - bh * nch;
+    // Consecutive blockIdx go to different XCDs (round-robin over 8): regroup
+    // so that the two halves of a chunk run on one XCD and share its L2.
+    const int nwg = gridDim.x;
+    int id = blockIdx.x;
+    if ((nwg & 7) == 0) id = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    half = id & 1;
+    const int unit = id >> 1;
+    const int bh = unit / nch;
+    const int n = unit - bh * nch;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     l = lane_id();
     g4 = 4 * (l >> 4);
@@ -564,9 +542,13 @@ struct GradKernel {
     rW = make_rsrc(a.W + ck * GCH * D, GCH * D * 2u);
     rDl = make_rsrc(a.Dl + ck * GCH * D, GCH * D * 2u);
     rXb = make_rsrc(a.Xb + ck * GCH * D, GCH * D * 2u);
+    rA = make_rsrc(a.A + ck * NP4 * 256, NP4 * 256 * 2u);
+    const bool db = half == 0;  // this workgroup writes dbeta
     init_offsets();
     Pre5 p5;
     load_pre5(p5);
+    PreB pb;
+    if (db) load_preb(pb);
     // zero halves of the 32-deep slots that pair a block of the upper triangle
     // with a stored one (nothing writes them): dP and Abar slots (0, 0) and
     // (2, 1), second half; dP^T and Abar^T slots (1, 0) and (3, 1), first half
@@ -575,24 +557,31 @@ struct GradKernel {
       uint32_t off;
       if (which < 2) {
         const uint32_t base = which == 0 ? C::DP : C::AB;
-        off = base + (uint32_t)(((sel ? 2 * NKT + 1 : 0) * 64 + lane) * 16 + 8);
+        off = base + (uint32_t)(((sel ? lo_idx(2, 1) : lo_idx(0, 0)) * 64 + lane) * 16 + 8);
       } else {
         const uint32_t base = which == 2 ? C::DPT : C::ABT;
-        off = base + (uint32_t)(((sel ? 3 * NKT + 1 : 1 * NKT) * 64 + lane) * 16);
+        off = base + (uint32_t)(((sel ? up_idx(3, 1) : up_idx(1, 0)) * 64 + lane) * 16);
       }
       lds_st<u32x2>(smem, off, u32x2{0u, 0u});
     }
-    for (int i = threadIdx.x; i < 2 * C::NW * GCH; i += C::THREADS) lds_st<float>(smem, C::DBP + 4 * i, 0.f);
-    if (wave < C::NP) elementwise();
-    else copy_tiles();
+    for (int i = threadIdx.x; i < (1 + NW) * GCH; i += C::THREADS) lds_st<float>(smem, C::DBP + 4 * i, 0.f);
+    if (wave == 0) {
+      const float b = __uint_as_float((uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rbeta, 2 * l, 0, 0) << 16);
+      lds_st<float>(smem, C::BETA + 4 * l, b);
+    }
+    copy_tiles();
     sync_lds();
-    dbeta_w(p5);
-    p4_tasks<0>();
+    if (db) {
+      dbeta_w(pb);
+      p4_tasks<0, true>(pb);
+    } else {
+      p4_tasks<0, false>(pb);
+    }
     sync_lds();
-    if (wave == 0 && l < nrows) {
+    if (db && wave == 0 && l < nrows) {
       float s = 0.f;
 #pragma unroll
-      for (int w = 0; w < 2 * C::NW; ++w) s += lds_ld<float>(smem, C::DBP + 4 * (w * GCH + l));
+      for (int w = 0; w < 1 + NW; ++w) s += lds_ld<float>(smem, C::DBP + 4 * (w * GCH + l));
       a.dbeta[tok0 + l] = (bf16)s;
     }
 #pragma unroll
@@ -601,7 +590,7 @@ struct GradKernel {
 };
 
 template <int D>
-__global__ __launch_bounds__(GradCfg<D>::THREADS, 1) void kda_bwgrad_kernel(BwGradArgs a) {
+__global__ __launch_bounds__(GradCfg<D>::THREADS, 2) void kda_bwgrad_kernel(BwGradArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[GradCfg<D>::LDS];
   GradKernel<D> k;
   k.smem = smem;
@@ -613,7 +602,7 @@ __global__ __launch_bounds__(GradCfg<D>::THREADS, 1) void kda_bwgrad_kernel(BwGr
 
 hipError_t launch_bwgrad(const BwGradArgs& a, int BH, int D, hipStream_t stream) {
   const long long nch = (a.T + GCH - 1) / GCH;
-  const long long nwg = (long long)BH * nch;
+  const long long nwg = 2LL * BH * nch;  // two workgroups (column halves) per (head, chunk)
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   if (D == 128) {

@@ -382,7 +382,7 @@ struct ChunkKernel {
   //                  transpose, and Z = T_ii^T = (I + N^T)^-1 is accumulated as
   //                  Z += (N^T)^(2^k) Z from Z = I - N^T.  Z is T_ii's A fragment.
   template <int MAT, int I, int J>
-  __device__ __forceinline__ void p2_tile(uint32_t st) {
+  __device__ __forceinline__ void p2_tile(uint32_t st, int it) {
     constexpr bool DIAG = MAT == 0 && I == J;
     const int ln = fresh_lane(l);
     const int g4 = 4 * (ln >> 4), s0 = ln & 15;
@@ -404,6 +404,16 @@ struct ChunkKernel {
     f32x4 acc = zero4();
 #pragma unroll
     for (int m = 0; m < NKD; ++m) acc = F::mma(acc, fb[m], fx[m]);
+    if constexpr (PREFILL && !BWD && C::BF && MAT == 0) {
+      // the gradients' checkpoint of this block of strict_lower(Kh Kb^T)
+      if (a.ck_a) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (!DIAG || g4 + e < s0) ? acc[e] : 0.f;
+        const size_t o = (((size_t)bh_seq * nch + it) * 10 + I * (I + 1) / 2 + J) * 256 + ln * 4;
+        *reinterpret_cast<bf16x4*>(a.ck_a + o) = pack4(v);
+      }
+    }
     if constexpr (MAT == 0 && !DIAG) {
       f32x4 v;
 #pragma unroll
@@ -488,17 +498,18 @@ struct ChunkKernel {
   }
 
   template <int K>
-  __device__ __forceinline__ void p2_task(uint32_t st) {
+  __device__ __forceinline__ void p2_task(uint32_t st, int it) {
     if constexpr (K < NT2) {
       constexpr int W = task_wave(K);  // evaluated at compile time
-      if (W == wave) p2_tile<task_mat(K), task_i(K), task_j(K)>(st);
-      p2_task<K + 1>(st);
+      if (W == wave) p2_tile<task_mat(K), task_i(K), task_j(K)>(st, it);
+      p2_task<K + 1>(st, it);
     }
   }
 
-  __device__ __forceinline__ void p2(uint32_t st) {
+  // it: the chunk whose tiles are built (its index in the segment)
+  __device__ __forceinline__ void p2(uint32_t st, int it) {
     if constexpr (BWD) p2_task_bw<0>(st);
-    else p2_task<0>(st);
+    else p2_task<0>(st, it);
   }
   // ------------------------------------------------ backward-chain tile tasks
   // The reverse chain needs the transposes of the forward's A operands: P^T,
@@ -1185,7 +1196,7 @@ struct ChunkKernel {
     p1(r, stage(it), it + PD);
     sync_lds();
     if (C::LAG && it == nch) return;
-    p2(stage(it));
+    p2(stage(it), it);
     sync_lds();
     if (!C::LAG) sync_lds();
   }
@@ -1224,7 +1235,7 @@ struct ChunkKernel {
       if (C::LAG && cc >= 0) chain_step(vr, cc);
       sync_lds();
       if (C::LAG && it == nch) break;  // the chunk past the end: no score tiles
-      p2(stage(it));
+      p2(stage(it), it);
       sync_lds();
       if (!C::LAG) {
         chain_step(vr, cc);

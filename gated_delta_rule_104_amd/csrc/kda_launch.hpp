@@ -43,12 +43,15 @@ struct ChunkArgs {
   // gradients' checkpoints, bf16 row-major matrices with the positions inside
   // each 32-wide block of a row in the kpos order (null: none).  Prefill (bf16,
   // one segment per head): the start state of every chunk [BH, nch, D, D] and
-  // its W = V - Kh S and Delta [BH, nch, CH, D].  Backward chain: dU =
-  // Diag(Gam) dS' [BH, nch, D, D] and Xbar [BH, nch, CH, D] of every chunk
-  // (and dv through o).
+  // its W = V - Kh S and Delta [BH, nch, CH, D], and the strictly lower
+  // blocks of Kh Kb^T [BH, nch, 10, 64 lanes, 4] (block (I, J), J <= I, at
+  // I(I+1)/2 + J; lane l holds row 16I + l%16, columns 16J + 4(l/16) + e).
+  // Backward chain: dU = Diag(Gam) dS' [BH, nch, D, D] and Xbar
+  // [BH, nch, CH, D] of every chunk (and dv through o).
   bf16* ck_rows = nullptr;
   bf16* ck_w = nullptr;
   bf16* ck_d = nullptr;
+  bf16* ck_a = nullptr;
   bf16* dU_rows = nullptr;
   bf16* ck_xb = nullptr;
 };
@@ -116,6 +119,7 @@ struct BwGradArgs {
   const bf16* S_rows;  // the start state of every chunk [BH, nch, D, D]
   const bf16* W;       // W = V - Kh S of every chunk [BH, nch, CH, D]
   const bf16* Dl;      // Delta of every chunk
+  const bf16* A;       // strictly lower blocks of Kh Kb^T of every chunk [BH, nch, 10, 64, 4]
   const bf16* dU_rows; // dU = Diag(Gam) dS' of every chunk [BH, nch, D, D]
   const bf16* Xb;      // Xbar of every chunk [BH, nch, CH, D]
   bf16* dq;            // [BH, T, D], the inputs' dtype

@@ -225,9 +225,9 @@ def backward(lib, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, dO=FAKE, 
 
 
 def test_backward_workspace_query(lib):
-    """bf16 (chunked form): per chunk the start state and dU (bf16 D x D each)
-    and W, Delta, Xbar (bf16 64 x D each), and one discarded fp32 end state per
-    head.  fp32 (token steps):
+    """bf16 (chunked form): per chunk the start state and dU (bf16 D x D each),
+    W, Delta, Xbar (bf16 64 x D each) and the 10 lower 16x16 blocks of
+    strict_lower(Kh Kb^T) (bf16), and one discarded fp32 end state per head.  fp32 (token steps):
     a checkpoint every 64 tokens plus 64 entering states (fp32 D x D) and 64
     fp32 D-vectors per head, then, with two workgroups per head (few heads),
     the second one's row sums of every token (dq, dk, dlog_alpha, dbeta:
@@ -240,8 +240,8 @@ def test_backward_workspace_query(lib):
     assert q(64, 32, 65, 128, 128, F32) == 2048 * ((2 + 64) * 128 * 128 + 64 * 128) * 4
     assert q(1, 1, 0, 64, 64, F32) == (64 * 64 * 64 + 64 * 64) * 4
     def chunked(BH, nch, D):
-        return BH * (nch * (2 * D * D + 3 * 64 * D) * 2 + D * D * 4)
-    assert q(1, 1, 64, 64, 64, BF16) == chunked(1, 1, 64) == 57344
+        return BH * (nch * (2 * D * D + 3 * 64 * D + 10 * 256) * 2 + D * D * 4)
+    assert q(1, 1, 64, 64, 64, BF16) == chunked(1, 1, 64) == 62464
     assert q(2, 3, 65, 128, 128, BF16) == chunked(6, 2, 128)
     assert q(4, 32, 8192, 128, 128, BF16) == chunked(128, 128, 128)
     assert q(1, 1, 0, 64, 64, BF16) == 64 * 64 * 4
