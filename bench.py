@@ -278,23 +278,43 @@ def backward_bytes(B, H, T, D):
     return B * H * T * (2 * 5 * D + 2 + 2 * 4 * D + 2) + 3 * B * H * D * D * 4
 
 
+def backward_path_bytes(B, H, T, D, C=CH):
+    """HBM bytes the three kernels of the bf16 backward move by design, per
+    chunk-head (2-byte elements unless noted):
+      forward checkpoint pass: reads q, k, v, log_alpha, beta; writes the chunk's
+        start state S (D x D), W and Delta (C x D each) and the 10 lower 16x16
+        blocks of strict_lower(Kh Kb^T);
+      reverse chain: reads q, k, log_alpha, dO, beta; writes dv, dU (D x D) and
+        Xbar (C x D);
+      per-chunk gradients: reads q, k, log_alpha, dO, beta and every checkpoint;
+        writes dq, dk, dlog_alpha, dbeta;
+    plus S0, dS_T read and dS0 written once per head (fp32)."""
+    ins = C * (2 * 4 * D + 2)           # four [C][D] inputs and beta
+    ck_f = D * D * 2 + 2 * C * D * 2 + 10 * 256 * 2
+    ck_b = D * D * 2 + C * D * 2
+    k1 = ins + ck_f
+    k2 = ins + C * D * 2 + ck_b
+    k3 = ins + ck_f + ck_b + C * (2 * 3 * D + 2)
+    nchunks = -(-T // C)
+    return B * H * nchunks * (k1 + k2 + k3) + 3 * B * H * D * D * 4
+
+
 def backward_flops(B, H, T, D, C=CH):
     """Matrix flops the chunked backward issues per call, on dense 16x16 tiles
     (triangles and the 16-row diagonal blocks counted whole):
-      forward checkpoint pass per chunk-head: scores Kh Kb^T (2C^2K), Kh S and
-        Kb^T Delta (2CKV each), the 16-row block solve (C^2 V);
-      reverse chain: scores L and P (2C^2K each), Kb dU and Qh^T dO and
-        Kh^T Xbar (2CKV each), P^T dO (2C^2V), the block solve (C^2 V);
-      per-chunk gradients: L both ways and P (3 x 2C^2K), Kh S, Kb dU (2CKV
-        each), P^T dO (2C^2V), both solves (2 C^2 V), the five 64x64 products
-        dP, dP^T, Abar, Abar^T, Kh Kb^T (5 x 2C^2V), dO S^T, Xbar S^T,
-        Delta dU^T (3 x 2CKV), and the four products with the 64x64 gradients,
-        each run twice on split operands (8 x 2C^2K)."""
+      forward checkpoint pass per chunk-head: scores Kh Kb^T and Qh Kb^T
+        (2C^2K each), Kh S and Kb^T Delta (2CKV each), the 16-row block solve
+        (C^2 V);
+      reverse chain: scores L and P (2C^2K each), Kb dU, Qh^T dO and Kh^T Xbar
+        (2CKV each), P^T dO (2C^2V), the block solve (C^2 V);
+      per-chunk gradients: the four 64x64 products dP, dP^T, Abar, Abar^T
+        (2C^2D each), dO S^T, Xbar S^T and Delta dU^T (2CKV each), and the four
+        products with the 64x64 gradients, each run twice on split operands
+        (8 x 2C^2K)."""
     K = V = D
-    fwd = 2 * C * C * K + 2 * (2 * C * K * V) + C * C * V
+    fwd = 2 * (2 * C * C * K) + 2 * (2 * C * K * V) + C * C * V
     chain = 2 * (2 * C * C * K) + 3 * (2 * C * K * V) + 2 * C * C * V + C * C * V
-    grads = 3 * (2 * C * C * K) + 2 * (2 * C * K * V) + 2 * C * C * V + 2 * C * C * V + 5 * (2 * C * C * V) \
-        + 3 * (2 * C * K * V) + 8 * (2 * C * C * K)
+    grads = 4 * (2 * C * C * D) + 3 * (2 * C * K * V) + 8 * (2 * C * C * K)
     nchunks = -(-T // C)
     return B * H * nchunks * (fwd + chain + grads)
 
@@ -318,11 +338,15 @@ def bench_backward(args, dev):
     torch.cuda.synchronize()
     ms, _ = time_launches(call, MIN_TIMED)
     nbytes = backward_bytes(B, H, T, D)
+    pbytes = backward_path_bytes(B, H, T, D)
     fl = backward_flops(B, H, T, D)
     del g, dO, ws
     return {"B": B, "H": H, "T": T, "D": D, "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
             "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "bound": "mfma", "issued_mfma_tflops": fl / (ms * 1e-3) / 1e12,
+            # the bound: HBM over the bytes the three kernels move with their checkpoints
+            "bound": "hbm", "path_bytes": pbytes, "path_GBs": pbytes / (ms * 1e-3) / 1e9,
+            "path_hbm_frac": pbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "issued_mfma_tflops": fl / (ms * 1e-3) / 1e12,
             "mfma_frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
             "kernels": "forward checkpoint pass beside the reverse chain, then per-chunk gradients"}
 
@@ -526,6 +550,53 @@ def cpu_baseline(pf, budget_s):
             "sample": f"{what} ({el:.1f} s, fp64, outputs and end states); tokens/s over all {H} heads"}
 
 
+def summarize_profiles(paths):
+    """Summaries of rocprofv3 CSV output (no GPU needed): the `--stats` table
+    (`*_kernel_stats.csv`) per kernel name; a kernel trace
+    (`*_kernel_trace.csv`) grouped by kernel name and grid size, with dispatch
+    count and mean / median / min / max duration in microseconds; a counter
+    collection (`*_counter_collection.csv`) grouped the same way, each counter
+    summed over its dimensions per dispatch, then averaged over dispatches."""
+    import collections
+    import csv
+
+    def short(name):
+        return name.replace("void ", "")[:110]
+
+    for path in paths:
+        with open(path, newline="") as fh:
+            rows = list(csv.DictReader(fh))
+        print(f"## {os.path.basename(path)} ({len(rows)} rows)")
+        if not rows:
+            continue
+        if "AverageNs" in rows[0]:  # the --stats summary, per kernel name
+            for r in rows:
+                print(f"  {short(r['Name'])} | n={r['Calls']} mean {float(r['AverageNs']) / 1e3:.1f} us  "
+                      f"min {float(r['MinNs']) / 1e3:.1f}  max {float(r['MaxNs']) / 1e3:.1f}  "
+                      f"share {float(r['Percentage']):.2f}%")
+        elif "Counter_Name" in rows[0]:
+            agg = collections.defaultdict(lambda: collections.defaultdict(lambda: collections.defaultdict(float)))
+            for r in rows:
+                key = (short(r["Kernel_Name"]), r["Grid_Size"])
+                agg[key][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+            for (kname, grid), cs in sorted(agg.items()):
+                parts = [f"{c}={statistics.mean(per.values()):.6g} (n={len(per)})" for c, per in sorted(cs.items())]
+                print(f"  {kname} | grid {grid} | " + " ".join(parts))
+        else:
+            agg = collections.defaultdict(list)
+            meta = {}
+            for r in rows:
+                key = (short(r["Kernel_Name"]), r.get("Grid_Size", ""))
+                agg[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+                meta[key] = (r.get("Workgroup_Size", ""), r.get("LDS_Block_Size", r.get("Lds_Size", "")),
+                             r.get("Scratch_Size", ""), r.get("Arch_VGPR_Count", r.get("VGPR_Count", "")))
+            for key, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+                wg, lds, scr, vgpr = meta[key]
+                print(f"  {key[0]} | grid {key[1]} wg {wg} lds {lds} scratch {scr} vgpr {vgpr} | n={len(ds)} "
+                      f"mean {statistics.mean(ds):.1f} us  median {statistics.median(ds):.1f}  "
+                      f"min {min(ds):.1f}  max {max(ds):.1f}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -546,7 +617,12 @@ def main():
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "known-size reference for HBM traffic counters) and exit")
+    ap.add_argument("--summarize", nargs="+", metavar="CSV",
+                    help="only summarise rocprofv3 kernel-trace / counter-collection CSV files and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args.summarize)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the KDA hot path here is single-GPU "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
