@@ -54,12 +54,15 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "d2d17f927d162314",
+    "sources_sha": "a04af9ac561bf7a5",
     "direct_part": 0.1855e9 + 0.0482e9,
     "segment_transfer": 1.3029e9 + 0.0294e9,
     "segment_merge": 0.0316e9 + 0.0168e9,
-    "segment_prefill": 1.9842e9 + 0.4929e9,
+    "segment_prefill": 1.9841e9 + 0.4928e9,
     "decode_step": 0.5455e9 + 0.5390e9,
+    # the backward's three kernels at B=4, H=32, T=8192, d=128: forward
+    # checkpoint pass, reverse chain, per-chunk gradients
+    "backward": (1.0848e9 + 1.1660e9) + (1.0848e9 + 1.0821e9) + (3.0392e9 + 0.8077e9),
 }
 
 
@@ -67,7 +70,7 @@ def kernel_sources_sha():
     import hashlib
     h = hashlib.sha256()
     for f in ("kda_api.hip", "kda_chunk.hip", "kda_decode.hip", "kda_device.hpp", "kda_launch.hpp",
-              "kda_merge.hip"):
+              "kda_merge.hip", "kda_bwgrad.hip"):
         with open(os.path.join(ROOT, "gated_delta_rule_104_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -340,12 +343,13 @@ def bench_backward(args, dev):
     nbytes = backward_bytes(B, H, T, D)
     pbytes = backward_path_bytes(B, H, T, D)
     fl = backward_flops(B, H, T, D)
+    traffic = TRAFFIC["backward"] if kernel_sources_sha() == TRAFFIC["sources_sha"] else None
     del g, dO, ws
     return {"B": B, "H": H, "T": T, "D": D, "ms": ms, "tokens_per_s": B * T / (ms * 1e-3),
             "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             # the bound: HBM over the bytes the three kernels move with their checkpoints
             "bound": "hbm", "path_bytes": pbytes, "path_GBs": pbytes / (ms * 1e-3) / 1e9,
-            "path_hbm_frac": pbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "path_hbm_frac": pbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
             "issued_mfma_tflops": fl / (ms * 1e-3) / 1e12,
             "mfma_frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
             "kernels": "forward checkpoint pass beside the reverse chain, then per-chunk gradients"}
@@ -586,13 +590,14 @@ def summarize_profiles(paths):
             agg = collections.defaultdict(list)
             meta = {}
             for r in rows:
-                key = (short(r["Kernel_Name"]), r.get("Grid_Size", ""))
+                key = (short(r["Kernel_Name"]), r.get("Grid_Size", r.get("Grid_Size_X", "")))
                 agg[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
-                meta[key] = (r.get("Workgroup_Size", ""), r.get("LDS_Block_Size", r.get("Lds_Size", "")),
-                             r.get("Scratch_Size", ""), r.get("Arch_VGPR_Count", r.get("VGPR_Count", "")))
+                meta[key] = (r.get("Workgroup_Size", r.get("Workgroup_Size_X", "")),
+                             r.get("LDS_Block_Size", r.get("Lds_Size", "")), r.get("Scratch_Size", ""),
+                             r.get("Arch_VGPR_Count", r.get("VGPR_Count", "")))
             for key, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
                 wg, lds, scr, vgpr = meta[key]
-                print(f"  {key[0]} | grid {key[1]} wg {wg} lds {lds} scratch {scr} vgpr {vgpr} | n={len(ds)} "
+                print(f"  {key[0]} | grid {key[1]} wg {wg} lds {lds} scratch {scr} vgpr column {vgpr} | n={len(ds)} "
                       f"mean {statistics.mean(ds):.1f} us  median {statistics.median(ds):.1f}  "
                       f"min {min(ds):.1f}  max {max(ds):.1f}")
 
