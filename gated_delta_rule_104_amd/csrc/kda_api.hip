@@ -560,7 +560,9 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
 // state and dU = Diag(Gam) dS' (bf16 D x D each), W = V - Kh S, Delta and
 // Xbar (bf16 64 x D each), all row-major with kpos-ordered positions, and the
 // 10 lower 16x16 blocks of strict_lower(Kh Kb^T) (bf16, lane order); then the
-// forward pass's end state, which is not needed (fp32 [BH, D, D]).  In floats.
+// forward pass's end state, which is not needed (fp32 [BH, D, D]).  W, Xbar
+// and the blocks are written (and read) only in the rows of tokens with beta
+// below kTinyBeta.  In floats.
 constexpr long long kAckElems = 10 * 256;  // bf16 elements of the blocks of one chunk
 size_t chunk_bw_ws_floats(long long BH, int T, int D) {
   const long long nch = (T + 63) / 64;
@@ -569,12 +571,12 @@ size_t chunk_bw_ws_floats(long long BH, int T, int D) {
 
 // Gradients of the prefill in the chunked form (bf16 inputs; arguments already
 // validated):
-//  1. beside each other: the forward pass from S0, which keeps the start state,
-//     W = V - Kh S, Delta and strict_lower(Kh Kb^T) of every chunk (its outputs
-//     are not written), on
-//     the side stream; and the reverse chain from dS_T over the chunks, last to
-//     first, which keeps dU = Diag(Gam) dS' and Xbar of every chunk and writes
-//     dv and dS0 (it needs no forward state);
+//  1. beside each other: the forward pass from S0, which keeps the start state
+//     and Delta of every chunk (its outputs are not written), on the side
+//     stream; and the reverse chain from dS_T over the chunks, last to first,
+//     which keeps dU = Diag(Gam) dS' of every chunk and writes dv and dS0 (it
+//     needs no forward state).  For the rows with beta below kTinyBeta only,
+//     they also keep W = V - Kh S, the row of strict_lower(Kh Kb^T) and Xbar;
 //  2. the per-chunk gradients, two workgroups (column halves) per (head, chunk).
 kda_status chunk_backward(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                           const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
@@ -629,6 +631,7 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
   }
   kda::BwGradArgs g;
   g.q = q; g.k = k; g.la = log_alpha; g.beta = beta; g.dO = dO;
+  g.dv = static_cast<const kda::bf16*>(dv_);
   g.S_rows = S_rows; g.W = W; g.Dl = Dl; g.A = Ack; g.dU_rows = dU_rows; g.Xb = Xb;
   g.dq = static_cast<kda::bf16*>(dq); g.dk = static_cast<kda::bf16*>(dk_);
   g.dla = static_cast<kda::bf16*>(dlog_alpha); g.dbeta = static_cast<kda::bf16*>(dbeta); g.T = T;

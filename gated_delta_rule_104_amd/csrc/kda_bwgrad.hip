@@ -13,11 +13,11 @@
 //   O = Qh S + P Delta,  S' = Diag(Gam) (S + Kb^T Delta)
 // the chain rule gives, per chunk:
 //   dDelta = Kb dU + P^T dO,  Xbar = T^T dDelta,  dv = diag(b) Xbar
-//   dP = lower(dO Delta^T),  Lbar = strict_lower(-Xbar Delta^T),  Abar = diag(b) Lbar
+//   dP = lower(dO Delta^T),  Abar = diag(b) strict_lower(-Xbar Delta^T) = -strict_lower(dv Delta^T)
 //   dQh = dO S^T + dP Kb
-//   dKh = -diag(b) Xbar S^T + Abar Kb
+//   dKh = -dv S^T + Abar Kb
 //   dKb = Delta dU^T + Abar^T Kh + dP^T Qh
-//   dbeta_r = sum_j Xbar_rj W_rj + sum_{s<r} Lbar_rs A_rs
+//   dbeta_r = sum_j Xbar_rj W_rj - sum_{s<r} (Xbar Delta^T)_rs A_rs = Xbar_r . Y_r,  Y = W - A Delta
 //   dq = dQh e^g,  dk = dKh e^g + dKb e^-g
 //   dlog_alpha_r = sum_{t >= r} dg_t + rowsum(dU . S) + sum_{s < r} k_s e^-g_s (Delta dU^T)_s
 //     with dg = q dq + k (dKh e^g - (dKb - Delta dU^T) e^-g)
@@ -27,13 +27,17 @@
 // the Delta dU^T piece of dKb cancel for s >= r, so that sum_{s < r} is formed
 // directly, which in bf16 products avoids a cancellation between large terms.
 //
-// The forward pass stores S, W, Delta and A of every chunk, and the reverse
-// chain dU and Xbar (and writes dv); this kernel reads them.  Two workgroups
+// The forward equations give Delta = diag(b) Y exactly ((I + diag(b) A) Delta
+// = diag(b) W), so for b_r != 0, dbeta_r = dv_r . Delta_r / b_r^2, and no
+// product needs Xbar, W or A itself.  The forward pass stores S and Delta of
+// every chunk and the reverse chain dU (and writes dv); only for the rows with
+// b below kTinyBeta do they also keep W, A's row and Xbar, from which this
+// kernel forms dbeta_r = Xbar_r . (W_r - sum_{s<r} A_rs Delta_s).  Two workgroups
 // per (head, chunk), each owning half of the key dimension's columns with one
 // wave per 16 columns (4 waves at d = 128).  Each needs about 74 KiB of LDS,
 // so two run on a CU at once and one's loads overlap the other's arithmetic.
 // Phases, each ended by a workgroup barrier:
-//   1. every wave copies its share of dO, Delta and Xbar into LDS tiles (all
+//   1. every wave copies its share of dO, Delta and dv into LDS tiles (all
 //      loads issued before the first store);
 //   2. the 64 x 64 gradients dP, dP^T, Abar, Abar^T (as MFMA A fragments), and
 //      in the first half's workgroup dbeta;
@@ -68,17 +72,16 @@ struct GradCfg {
   static constexpr int FRC = 6 * 64 * 16;
   static constexpr uint32_t DO = 0;
   static constexpr uint32_t DL = DO + TD_SZ;     // Delta
-  static constexpr uint32_t XB = DL + TD_SZ;     // Xbar
-  static constexpr uint32_t DP = XB + TD_SZ;     // dP (lower)
+  static constexpr uint32_t DV = DL + TD_SZ;     // dv
+  static constexpr uint32_t DP = DV + TD_SZ;     // dP (lower)
   static constexpr uint32_t DPT = DP + FRC;      // dP^T (upper)
   static constexpr uint32_t AB = DPT + FRC;      // Abar (lower)
   static constexpr uint32_t ABT = AB + FRC;      // Abar^T (upper)
   static constexpr uint32_t BETA = ABT + FRC;    // beta [64] fp32
-  static constexpr uint32_t DBP = BETA + 4 * GCH;  // dbeta partials [1 + NW][64] fp32
-  static constexpr uint32_t LDS = DBP + 4 * GCH * (1 + NW);
+  static constexpr uint32_t LDS = BETA + 4 * GCH;
   static_assert(2 * LDS <= 160 * 1024, "two workgroups per CU");
   static_assert(LDS % 16 == 0, "LDS alignment");
-  static_assert(D / NW == 32, "a row of dbeta's first part is 32 channels per lane");
+  static_assert(D / NW == 32, "dbeta: 32 channels of a row per lane");
 };
 
 template <int D>
@@ -86,13 +89,12 @@ struct GradKernel {
   using C = GradCfg<D>;
   static constexpr int NW = C::NW, NCT = C::NCT, NKD = C::NKD, NKT = C::NKT;
   static constexpr int NP4 = 10;                   // lower blocks (R, S) of the 64x64 gradients
-  static constexpr int NTW = (NP4 + NW - 1) / NW;  // of them per wave
   char* smem;
   BwGradArgs a;
   int wave, l, g4, s0;
   int half;   // which half of the key dimension's columns
   int nrows;  // valid tokens of this chunk
-  rsrc_t rq, rk, rla, rbeta, rdo, rdq, rdk, rdla, rSr, rUr, rW, rDl, rXb, rA;
+  rsrc_t rq, rk, rla, rbeta, rdo, rdv, rdq, rdk, rdla, rSr, rUr, rW, rDl, rXb, rA;
   uint32_t oTD[NKD];   // A fragments of [64][D] tiles, row tile 0
 
   __device__ __forceinline__ static uint32_t td(int row, int byte) {
@@ -136,9 +138,9 @@ struct GradKernel {
   }
 
   // ------------------------------------------------------------ phase 1
-  // dO (the input, plain channel order) and Delta, Xbar (the checkpoints,
-  // already kpos-ordered) into their LDS tiles, 16 bytes at a time: every load
-  // is issued before the first store, so that their latencies overlap.
+  // dO and dv (plain channel order) and Delta (the checkpoint, already
+  // kpos-ordered) into their LDS tiles, 16 bytes at a time: every load is
+  // issued before the first store, so that their latencies overlap.
   __device__ __forceinline__ void copy_tiles() {
     constexpr int PIECES = GCH * D / 8;  // 16-byte pieces of one tile
     constexpr int NL = NW * 64;
@@ -150,18 +152,19 @@ struct GradKernel {
     for (int i = 0; i < PER; ++i) {
       const int y = i % PER_TILE * NL + x0;  // piece within tile i / PER_TILE
       const int row = y / (D / 8), p8 = 8 * (y - row * (D / 8));
-      const rsrc_t r = i < PER_TILE ? rdo : i < 2 * PER_TILE ? rDl : rXb;
+      const rsrc_t r = i < PER_TILE ? rdo : i < 2 * PER_TILE ? rDl : rdv;
       w[i] = bload128(r, (uint32_t)(row * D + p8) * 2u);
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int y = i % PER_TILE * NL + x0;
       const int row = y / (D / 8), p8 = 8 * (y - row * (D / 8));
-      if (i < PER_TILE) {
-        lds_st<u32x2>(smem, C::DO + td(row, 2 * kpos(p8)), u32x2{w[i][0], w[i][1]});
-        lds_st<u32x2>(smem, C::DO + td(row, 2 * kpos(p8 + 4)), u32x2{w[i][2], w[i][3]});
+      if (i < PER_TILE || i >= 2 * PER_TILE) {  // plain channel order: to the kpos positions
+        const uint32_t base = i < PER_TILE ? C::DO : C::DV;
+        lds_st<u32x2>(smem, base + td(row, 2 * kpos(p8)), u32x2{w[i][0], w[i][1]});
+        lds_st<u32x2>(smem, base + td(row, 2 * kpos(p8 + 4)), u32x2{w[i][2], w[i][3]});
       } else {
-        lds_st<u32x4>(smem, (i < 2 * PER_TILE ? C::DL : C::XB) + td(row, 2 * p8), w[i]);
+        lds_st<u32x4>(smem, C::DL + td(row, 2 * p8), w[i]);
       }
     }
   }
@@ -220,65 +223,72 @@ struct GradKernel {
     }
   }
 
-  // dbeta's inputs, first half's workgroup only: W over 32 channels of a row
-  // (lane x = 64 wave + l: row x / NW, channels 32 (x % NW) ..), and the blocks
-  // of A of this wave's phase-2 tasks (task K: block 9 - K of the forward's
-  // order, this lane's 4 values)
-  struct PreB {
-    u32x4 w[4];
-    u32x2 ar[NTW];
-  };
-  __device__ __forceinline__ void load_preb(PreB& p) const {
+  // dbeta of every row of the chunk, first half's workgroup only: lane x =
+  // 64 wave + l takes 32 channels c0 = 32 (x % NW) .. of row x / NW (both
+  // tiles and checkpoints in the kpos order), the NW lanes of a row add their
+  // parts.  b_r >= kTinyBeta: dbeta_r = (dv_r . Delta_r) / b_r^2.  Otherwise
+  // dbeta_r = Xbar_r . (W_r - sum_{s<r} A_rs Delta_s), from the rows the chain
+  // kernels keep for such tokens.
+  __device__ __forceinline__ void dbeta_rows(size_t tok0) const {
     const int x = wave * 64 + l, row = x / NW, c0 = 32 * (x % NW);
+    const float b = lds_ld<float>(smem, C::BETA + 4 * row);
+    float part = 0.f;
+    if (b >= kTinyBeta) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p.w[i] = bload128(rW, (uint32_t)(row * D + c0 + 8 * i) * 2u);
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 dv8 = lds_ld<bf16x8>(smem, C::DV + td(row, 2 * (c0 + 8 * i)));
+        const bf16x8 dl8 = lds_ld<bf16x8>(smem, C::DL + td(row, 2 * (c0 + 8 * i)));
 #pragma unroll
-    for (int i = 0; i < NTW; ++i) {
-      const int K = wave + NW * i;
-      const uint32_t off = (uint32_t)(((NP4 - 1 - min(K, NP4 - 1)) * 64 + l) * 8);
-      p.ar[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rA, off, 0, 0));
+        for (int e = 0; e < 4; ++e) part = dot2(dv8, dl8, e, part);
+      }
+    } else {
+      // A_rs: block (row/16, s/16) at I(I+1)/2 + J, lane row%16 + 16 ((s%16)/4), value s%4
+      const int I = row >> 4;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off = (uint32_t)(row * D + c0 + 8 * i) * 2u;
+        const bf16x8 xb8 = __builtin_bit_cast(bf16x8, bload128(rXb, off));
+        const bf16x8 w8 = __builtin_bit_cast(bf16x8, bload128(rW, off));
+        float y[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = (float)w8[k];
+        for (int s = 0; s < row; ++s) {
+          const int J = s >> 4;
+          const uint32_t ao = (uint32_t)(((I * (I + 1) / 2 + J) * 256 + ((row & 15) + 16 * ((s & 15) >> 2)) * 4 +
+                                          (s & 3)) * 2);
+          const float av = f16raw(raw16(rA, ao));
+          const bf16x8 d8 = lds_ld<bf16x8>(smem, C::DL + td(s, 2 * (c0 + 8 * i)));
+#pragma unroll
+          for (int k = 0; k < 8; ++k) y[k] -= av * (float)d8[k];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) part += (float)xb8[k] * y[k];
+      }
     }
-  }
-
-  // first part of dbeta: sum_j Xbar_rj W_rj (both checkpoints in the kpos order)
-  __device__ __forceinline__ void dbeta_w(const PreB& p) {
-    const int x = wave * 64 + l, row = x / NW, c0 = 32 * (x % NW);
-    float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16x8 xb = lds_ld<bf16x8>(smem, C::XB + td(row, 2 * (c0 + 8 * i)));
-      const bf16x8 w = __builtin_bit_cast(bf16x8, p.w[i]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s = dot2(xb, w, e, s);
-    }
-#pragma unroll
-    for (int o = 1; o < NW; o <<= 1) s += __shfl_xor(s, o);
-    if (x % NW == 0) lds_st<float>(smem, C::DBP + 4 * row, s);
+    for (int o = 1; o < NW; o <<= 1) part += __shfl_xor(part, o);
+    if (x % NW == 0 && row < nrows) a.dbeta[tok0 + row] = (bf16)(b >= kTinyBeta ? part / (b * b) : part);
   }
 
   // ------------------------------------------------------------ phase 2
-  // Block (R, S), R >= S, of the 64x64 gradients, from row tiles of dO, Xbar
-  // (R) and of Delta (S), contracting over D; with dbeta, its second part from
-  // the block of A (ar: this lane's values A[16R + l%16][16S + 4g + e]).
-  template <int R, int S, bool DB>
-  __device__ __forceinline__ void p4_tile(const u32x2& ar) {
-    bf16x8 fo[NKD], fd[NKD], fxb[NKD];
+  // Block (R, S), R >= S, of the 64x64 gradients, from row tiles of dO, dv (R)
+  // and of Delta (S), contracting over D.
+  template <int R, int S>
+  __device__ __forceinline__ void p4_tile() {
+    bf16x8 fo[NKD], fd[NKD], fdv[NKD];
 #pragma unroll
     for (int m = 0; m < NKD; ++m) {
-      fo[m] = this->ar(C::DO, R, m);
-      fd[m] = this->ar(C::DL, S, m);
-      fxb[m] = this->ar(C::XB, R, m);
+      fo[m] = ar(C::DO, R, m);
+      fd[m] = ar(C::DL, S, m);
+      fdv[m] = ar(C::DV, R, m);
     }
-    const float bl = lds_ld<float>(smem, C::BETA + 4 * (16 * R + s0));
-    const f32x4 bet4 = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * R + g4));
     __builtin_amdgcn_sched_barrier(0);
     f32x4 a1 = zero4(), a2 = zero4(), a3 = zero4(), a4 = zero4();
 #pragma unroll
     for (int m = 0; m < NKD; ++m) {
       a1 = mfma_bf16_k32(a1, fd[m], fo[m]);    // dP[16R + s0][16S + 4g + e]
       a2 = mfma_bf16_k32(a2, fo[m], fd[m]);    // dP[16R + 4g + e][16S + s0]
-      a3 = mfma_bf16_k32(a3, fd[m], fxb[m]);   // -Lbar[16R + s0][16S + 4g + e]
-      a4 = mfma_bf16_k32(a4, fxb[m], fd[m]);   // -Lbar[16R + 4g + e][16S + s0]
+      a3 = mfma_bf16_k32(a3, fd[m], fdv[m]);   // -Abar[16R + s0][16S + 4g + e]
+      a4 = mfma_bf16_k32(a4, fdv[m], fd[m]);   // -Abar[16R + 4g + e][16S + s0]
     }
     f32x4 v1, v2, v3, v4;
 #pragma unroll
@@ -287,30 +297,13 @@ struct GradKernel {
       const bool lo2 = R > S || g4 + e >= s0, st2 = R > S || g4 + e > s0;  // (row 4g+e, col s0)
       v1[e] = lo1 ? a1[e] : 0.f;
       v2[e] = lo2 ? a2[e] : 0.f;
-      v3[e] = st1 ? -bl * a3[e] : 0.f;       // Abar = diag(b) Lbar
-      v4[e] = st2 ? -bet4[e] * a4[e] : 0.f;
+      v3[e] = st1 ? -a3[e] : 0.f;
+      v4[e] = st2 ? -a4[e] : 0.f;
     }
     put16(slot_lo(C::DP, R, S), v1);
     put16(slot_up(C::DPT, S, R), v2);
     put16(slot_lo(C::AB, R, S), v3);
     put16(slot_up(C::ABT, S, R), v4);
-    if constexpr (DB) {
-      // sum_{s < r} Lbar_rs A_rs over the block, row r = 16R + l%16
-      const float av[4] = {__uint_as_float(ar[0] << 16), __uint_as_float(ar[0] & 0xffff0000u),
-                           __uint_as_float(ar[1] << 16), __uint_as_float(ar[1] & 0xffff0000u)};
-      float x = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool st1 = R > S || s0 > g4 + e;
-        x -= st1 ? a3[e] * av[e] : 0.f;
-      }
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      if (l < 16) {
-        const uint32_t o = C::DBP + 4 * ((1 + wave) * GCH + 16 * R + s0);
-        lds_st<float>(smem, o, lds_ld<float>(smem, o) + x);
-      }
-    }
   }
   static constexpr int p4_r(int K) {
     const int rr[NP4] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
@@ -320,14 +313,12 @@ struct GradKernel {
     const int ss[NP4] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
     return ss[K];
   }
-  // task K (block (p4_r, p4_s), at I(I+1)/2 + J = 9 - K in the forward's
-  // order) runs on wave K % NW
-  template <int K, bool DB>
-  __device__ __forceinline__ void p4_tasks(const PreB& pb) {
+  // task K (block (p4_r, p4_s)) runs on wave K % NW
+  template <int K>
+  __device__ __forceinline__ void p4_tasks() {
     if constexpr (K < NP4) {
-      static_assert(p4_r(K) * (p4_r(K) + 1) / 2 + p4_s(K) == NP4 - 1 - K, "block order");
-      if (K % NW == wave) p4_tile<p4_r(K), p4_s(K), DB>(pb.ar[K / NW]);
-      p4_tasks<K + 1, DB>(pb);
+      if (K % NW == wave) p4_tile<p4_r(K), p4_s(K)>();
+      p4_tasks<K + 1>();
     }
   }
 
@@ -413,20 +404,18 @@ struct GradKernel {
       for (int m = 0; m < NKD; ++m) {
         b = mfma_bf16_k32(b, ar(C::DL, t, m), ur[m]);  // Delta dU^T
         q = mfma_bf16_k32(q, ar(C::DO, t, m), sr[m]);  // dO S^T
-        h = mfma_bf16_k32(h, ar(C::XB, t, m), sr[m]);  // Xbar S^T
+        h = mfma_bf16_k32(h, ar(C::DV, t, m), sr[m]);  // dv S^T
       }
       dks[t] = b;
       dkb[t] = zero4();
       dqh[t] = q;
       dkh[t] = h;
     }
-    // dKh = -diag(b) Xbar S^T + Abar Kb;  dQh += dP Kb;  dKb = Abar^T Kh + dP^T Qh (+ dks)
+    // dKh = -dv S^T + Abar Kb;  dQh += dP Kb;  dKb = Abar^T Kh + dP^T Qh (+ dks)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const f32x4 bet = lds_ld<f32x4>(smem, C::BETA + 4 * (16 * t + g4));
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dkh[t][e] *= -bet[e];
-    }
+      for (int e = 0; e < 4; ++e) dkh[t][e] = -dkh[t][e];
 #pragma unroll
     for (int m = 0; m < NKT; ++m) {
       bf16x8 kbH, kbL, khH, khL, qhH, qhL;
@@ -531,11 +520,13 @@ struct GradKernel {
     rk = make_rsrc(static_cast<const bf16*>(a.k) + tok0 * D, in_bytes);
     rla = make_rsrc(static_cast<const bf16*>(a.la) + tok0 * D, in_bytes);
     rdo = make_rsrc(a.dO ? static_cast<const bf16*>(a.dO) + tok0 * D : nullptr, a.dO ? in_bytes : 0u);
+    rdv = make_rsrc(a.dv + tok0 * D, in_bytes);
     rbeta = make_rsrc(static_cast<const bf16*>(a.beta) + tok0, (uint32_t)nrows * 2u);
     rdq = make_rsrc(a.dq + tok0 * D, in_bytes);
     rdk = make_rsrc(a.dk + tok0 * D, in_bytes);
     rdla = make_rsrc(a.dla + tok0 * D, in_bytes);
-    // the chunk's checkpoints from the forward pass and the reverse chain
+    // the chunk's checkpoints from the forward pass and the reverse chain (W,
+    // Xbar and A are read only for rows with beta below kTinyBeta)
     const size_t ck = (size_t)bh * nch + n;
     rSr = make_rsrc(a.S_rows + ck * D * D, D * D * 2u);
     rUr = make_rsrc(a.dU_rows + ck * D * D, D * D * 2u);
@@ -547,8 +538,6 @@ struct GradKernel {
     init_offsets();
     Pre5 p5;
     load_pre5(p5);
-    PreB pb;
-    if (db) load_preb(pb);
     // zero halves of the 32-deep slots that pair a block of the upper triangle
     // with a stored one (nothing writes them): dP and Abar slots (0, 0) and
     // (2, 1), second half; dP^T and Abar^T slots (1, 0) and (3, 1), first half
@@ -564,26 +553,15 @@ struct GradKernel {
       }
       lds_st<u32x2>(smem, off, u32x2{0u, 0u});
     }
-    for (int i = threadIdx.x; i < (1 + NW) * GCH; i += C::THREADS) lds_st<float>(smem, C::DBP + 4 * i, 0.f);
     if (wave == 0) {
       const float b = __uint_as_float((uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rbeta, 2 * l, 0, 0) << 16);
       lds_st<float>(smem, C::BETA + 4 * l, b);
     }
     copy_tiles();
     sync_lds();
-    if (db) {
-      dbeta_w(pb);
-      p4_tasks<0, true>(pb);
-    } else {
-      p4_tasks<0, false>(pb);
-    }
+    p4_tasks<0>();
+    if (db) dbeta_rows(tok0);
     sync_lds();
-    if (db && wave == 0 && l < nrows) {
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < 1 + NW; ++w) s += lds_ld<float>(smem, C::DBP + 4 * (w * GCH + l));
-      a.dbeta[tok0 + l] = (bf16)s;
-    }
 #pragma unroll
     for (int j = 0; j < NCT; ++j) phase5_6(j, p5);
   }

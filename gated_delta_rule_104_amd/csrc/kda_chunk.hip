@@ -405,8 +405,9 @@ struct ChunkKernel {
 #pragma unroll
     for (int m = 0; m < NKD; ++m) acc = F::mma(acc, fb[m], fx[m]);
     if constexpr (PREFILL && !BWD && C::BF && MAT == 0) {
-      // the gradients' checkpoint of this block of strict_lower(Kh Kb^T)
-      if (a.ck_a) {
+      // the gradients' checkpoint of this block of strict_lower(Kh Kb^T), for
+      // the lane's row (16I + l%16) only if its beta is below kTinyBeta
+      if (a.ck_a && bl < kTinyBeta) {
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (!DIAG || g4 + e < s0) ? acc[e] : 0.f;
@@ -704,16 +705,14 @@ struct ChunkKernel {
       for (int h = 0; h < C1B; ++h)
 #pragma unroll
         for (int j = 0; j < NCT; ++j) X[j][H0 + h] = F::mma(X[j][H0 + h], fk[h][m], sb[j][m]);
-    if constexpr (PREFILL && !BWD && NCT == 2) {
-      if (ck_w) {  // W = V - Kh S = -X here
-#pragma unroll
-        for (int h = 0; h < C1B; ++h) store_tile_bf16(ck_w, X[0], X[1], H0 + h, -1.f);
-      }
-    }
     const int kk = 4 * (l >> 4);
 #pragma unroll
     for (int h = 0; h < C1B; ++h) {
       const f32x4 bet = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * (H0 + h) + kk));
+      if constexpr (PREFILL && !BWD && NCT == 2) {
+        // W = V - Kh S = -X here, kept for the rows with beta below kTinyBeta
+        if (ck_w) store_tile_bf16(ck_w, X[0], X[1], H0 + h, -1.f, &bet);
+      }
 #pragma unroll
       for (int j = 0; j < NCT; ++j)
 #pragma unroll
@@ -946,14 +945,18 @@ struct ChunkKernel {
   // Row tile t of a [CH][D] matrix held in accumulators (x[j]: this lane's
   // columns colb + j), scaled by `sc`, as bf16 into a row-major [CH][D] matrix
   // with kpos-ordered positions in each row (the gradients' checkpoint layout).
-  __device__ __forceinline__ void store_tile_bf16(bf16* dst, const f32x4* x0, const f32x4* x1, int t, float sc) const {
+  // With `bet` (the beta of the lane's rows 16t + 4(l/16) + e), only the rows
+  // whose beta is below kTinyBeta are stored.
+  __device__ __forceinline__ void store_tile_bf16(bf16* dst, const f32x4* x0, const f32x4* x1, int t, float sc,
+                                                  const f32x4* bet = nullptr) const {
     const rsrc_t r = make_rsrc(dst, CH * D * 2);
     const int g4 = 4 * (l >> 4);
     const uint32_t pc = (uint32_t)kpos(colb);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      __builtin_amdgcn_raw_buffer_store_b32(cvt2(sc * x0[t][e], sc * x1[t][e]), r,
-                                            (uint32_t)((16 * t + g4 + e) * D + pc) * 2u, 0, 0);
+      if (!bet || (*bet)[e] < kTinyBeta)
+        __builtin_amdgcn_raw_buffer_store_b32(cvt2(sc * x0[t][e], sc * x1[t][e]), r,
+                                              (uint32_t)((16 * t + g4 + e) * D + pc) * 2u, 0, 0);
   }
 
   // Snapshot after chunk cc when it closes a snapshot interval of the sequence.
@@ -1088,15 +1091,15 @@ struct ChunkKernel {
           }
         }
       }
-      // Xbar for the per-chunk gradients, and dv = diag(b) Xbar (the output o
-      // pointer is dv here, in the inputs' dtype)
+      // dv = diag(b) Xbar (the output o pointer is dv here, in the inputs'
+      // dtype), and Xbar itself for the rows with beta below kTinyBeta (the
+      // per-chunk gradients recover every other row's from dv)
       {
         bf16* xb = a.ck_xb + ((size_t)bh_seq * nch + chunk) * CH * D;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) store_tile_bf16(xb, Xb[0], Xb[1], t, 1.f);
-#pragma unroll
         for (int t = 0; t < 4; ++t) {
           const f32x4 bet = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * t + kk));
+          store_tile_bf16(xb, Xb[0], Xb[1], t, 1.f, &bet);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             __builtin_amdgcn_raw_buffer_store_b32(

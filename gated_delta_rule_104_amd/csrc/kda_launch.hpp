@@ -43,11 +43,12 @@ struct ChunkArgs {
   // gradients' checkpoints, bf16 row-major matrices with the positions inside
   // each 32-wide block of a row in the kpos order (null: none).  Prefill (bf16,
   // one segment per head): the start state of every chunk [BH, nch, D, D] and
-  // its W = V - Kh S and Delta [BH, nch, CH, D], and the strictly lower
-  // blocks of Kh Kb^T [BH, nch, 10, 64 lanes, 4] (block (I, J), J <= I, at
-  // I(I+1)/2 + J; lane l holds row 16I + l%16, columns 16J + 4(l/16) + e).
-  // Backward chain: dU = Diag(Gam) dS' [BH, nch, D, D] and Xbar
-  // [BH, nch, CH, D] of every chunk (and dv through o).
+  // its Delta [BH, nch, CH, D]; for the rows (tokens) with beta < kTinyBeta
+  // only, W = V - Kh S [BH, nch, CH, D] and the row's part of the strictly
+  // lower blocks of Kh Kb^T [BH, nch, 10, 64 lanes, 4] (block (I, J), J <= I,
+  // at I(I+1)/2 + J; lane l holds row 16I + l%16, columns 16J + 4(l/16) + e).
+  // Backward chain: dU = Diag(Gam) dS' [BH, nch, D, D] of every chunk, and
+  // Xbar [BH, nch, CH, D] of its rows with beta < kTinyBeta (dv through o).
   bf16* ck_rows = nullptr;
   bf16* ck_w = nullptr;
   bf16* ck_d = nullptr;
@@ -105,23 +106,30 @@ struct BackwardArgs {
 };
 size_t backward_ws_floats(long long BH, int T, int D, int split);
 
-// Per-chunk gradients of the prefill (bf16 inputs), one workgroup per
-// (head, chunk): from the chunk's start state (S0 for chunk 0, else the
-// forward's checkpoint after the previous chunk) and dU = Diag(Gam) dS' of the
-// chunk (from the reverse chain).
+// Rows (tokens) whose beta is below this get the gradient checkpoints that
+// only they need (W, Xbar and their part of Kh Kb^T); every other row's dbeta
+// follows from dv and Delta, which are proportional to its beta.
+constexpr float kTinyBeta = 0x1p-30f;
+
+// Per-chunk gradients of the prefill (bf16 inputs), two workgroups per
+// (head, chunk): from the chunk's start state (the forward's checkpoint), its
+// Delta, dU = Diag(Gam) dS' (from the reverse chain) and dv (the reverse
+// chain's output).
 struct BwGradArgs {
   const void* q;
   const void* k;
   const void* la;
   const void* beta;
   const void* dO;      // [BH, T, D] or null (= 0)
+  const bf16* dv;      // [BH, T, D], written by the reverse chain
   // checkpoints, bf16 row-major with kpos-ordered positions (ChunkArgs::ck_*):
   const bf16* S_rows;  // the start state of every chunk [BH, nch, D, D]
-  const bf16* W;       // W = V - Kh S of every chunk [BH, nch, CH, D]
-  const bf16* Dl;      // Delta of every chunk
-  const bf16* A;       // strictly lower blocks of Kh Kb^T of every chunk [BH, nch, 10, 64, 4]
+  const bf16* Dl;      // Delta of every chunk [BH, nch, CH, D]
   const bf16* dU_rows; // dU = Diag(Gam) dS' of every chunk [BH, nch, D, D]
-  const bf16* Xb;      // Xbar of every chunk [BH, nch, CH, D]
+  // rows with beta < kTinyBeta only:
+  const bf16* W;       // W = V - Kh S [BH, nch, CH, D]
+  const bf16* A;       // strictly lower blocks of Kh Kb^T [BH, nch, 10, 64, 4]
+  const bf16* Xb;      // Xbar [BH, nch, CH, D]
   bf16* dq;            // [BH, T, D], the inputs' dtype
   bf16* dk;
   bf16* dla;
