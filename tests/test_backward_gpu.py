@@ -26,10 +26,12 @@ def dev():
     return torch.device("cuda:0")
 
 
-def grads_case(B, H, T, D, dtype, seed, s0_std=0.1, variant="none", with_dO=True, with_dST=True):
+def grads_case(B, H, T, D, dtype, seed, s0_std=0.1, variant="none", with_dO=True, with_dST=True, edit=None):
     print(f"[case] backward B={B} H={H} T={T} D={D} {dtype} {variant} dO={with_dO} dS_T={with_dST}",
           flush=True)
     d = ki.gen_prefill(B, H, T, D, D, dtype, seed=seed, s0_std=s0_std, variant=variant)
+    if edit is not None:
+        edit(d)
     gen = torch.Generator().manual_seed(1000 + seed)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     dO = torch.randn(B, H, T, D, generator=gen).to(tdt) if with_dO else None
@@ -176,6 +178,20 @@ def test_backward_chunked_gates(variant):
     """The workloads' gates, no decay, the lower bound log alpha = -1, beta = 0
     (dk and dv are then exactly zero) and beta = 1."""
     err = grads_case(2, 2, 300, 128, "bf16", 310, variant=variant)
+    assert max(err.values()) <= TOL["bf16"], err
+
+
+def test_backward_chunked_tiny_beta_rows():
+    """Tokens with beta = 0 or beta = 1e-12 (below 2^-30) among ordinary ones:
+    their dbeta comes from the rows of Xbar, W and Kh Kb^T the chain kernels
+    keep for them; every other token's from dv and Delta."""
+    def edit(d):
+        beta = d["beta"]
+        t = torch.arange(beta.shape[-1])
+        beta[..., t % 7 == 3] = 0.0
+        beta[..., t % 11 == 5] = 1e-12
+        beta[..., t % 13 == 1] = 1e-6
+    err = grads_case(1, 2, 200, 128, "bf16", 340, variant="slow", edit=edit)
     assert max(err.values()) <= TOL["bf16"], err
 
 
