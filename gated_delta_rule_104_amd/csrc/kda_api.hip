@@ -335,7 +335,9 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
   if (log_on())
     fprintf(stderr, "[libkda] %s BH=%lld T=%d tokens [%d,%d) Tseg=%d G=%d D=%d nc=%d vsplit=%d grid=%lld\n",
             what, BH, T, t0, Tend, Tseg, G, D, nc, a.vsplit, nwg);
-  const hipError_t e = kda::launch_chunk(a, bf, D, true, nc, (int)nwg, stream);
+  // with checkpoints (and no outputs) the checkpoint-only variant runs
+  const hipError_t e = ck_rows ? kda::launch_chunk_ckpt(a, D, nc, (int)nwg, stream)
+                               : kda::launch_chunk(a, bf, D, true, nc, (int)nwg, stream);
   if (e != hipSuccess) return hip_fail(e, what);
   return KDA_OK;
 }

@@ -151,13 +151,17 @@ template <> struct Frag<false> {
   __device__ __forceinline__ static A16 a16(f32x4 t) { return t; }
 };
 
-template <typename T, int D, int NC, bool PREFILL, bool BWD = false>
+template <typename T, int D, int NC, bool PREFILL, bool BWD = false, bool CKPT = false>
 struct ChunkKernel {
   // BWD: the reverse chain of the prefill's gradients (see chain_bw); it uses
   // the prefill's stage layout and producer, visits the chunks last to first,
   // and is built for bf16 inputs (its transposed operands use the 16-bit
   // transposing LDS read).
+  // CKPT: the prefill run only for the gradients' checkpoints: no outputs, so
+  // neither q nor Qh nor the P tiles.
   static_assert(!BWD || (PREFILL && sizeof(T) == 2), "the backward chain is a bf16 prefill-layout mode");
+  static_assert(!CKPT || (PREFILL && !BWD && sizeof(T) == 2), "the checkpoint pass is a bf16 prefill mode");
+  static constexpr bool QP = PREFILL && !CKPT;  // q, Qh, P and the outputs are used
   using C = ChunkCfg<T, D, NC, PREFILL>;
   using F = Frag<C::BF>;
   typedef typename F::A16 A16;
@@ -226,7 +230,7 @@ struct ChunkKernel {
   }
   __device__ __forceinline__ void load_kq(ProdRaw<T>& r, int chunk, int i) const {
     raw_load<T>(r.k[i], rk, prod_off(chunk, i));
-    if constexpr (PREFILL) raw_load<T>(r.q[i], rq, prod_off(chunk, i));
+    if constexpr (QP) raw_load<T>(r.q[i], rq, prod_off(chunk, i));
   }
   __device__ __forceinline__ void load_beta(ProdRaw<T>& r, int chunk) const {
     if (wave == NC) {
@@ -301,7 +305,7 @@ struct ChunkKernel {
     for (int i = 0; i < 4; ++i) {
       float kk[8], qq[8], vq[8], vkh[8];
       raw_f32<T>(r.k[i], kk);
-      if constexpr (PREFILL) raw_f32<T>(r.q[i], qq);
+      if constexpr (QP) raw_f32<T>(r.q[i], qq);
       load_kq(r, next, i);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -317,7 +321,7 @@ struct ChunkKernel {
         if (i == 3) eg3[c] = eg;
         vkh[c] = kk[c] * eg;
         kb[i][c] = kk[c] * emg;
-        if constexpr (PREFILL) vq[c] = qq[c] * eg;
+        if constexpr (QP) vq[c] = qq[c] * eg;
       }
       if constexpr (C::BF) {
         // channels ch..ch+3 and ch+4..ch+7 go to their stored positions
@@ -328,12 +332,12 @@ struct ChunkKernel {
           for (int c = 0; c < 4; ++c) {
             h[c] = (bf16)vkh[4 * hlf + c];
             b[c] = (bf16)kb[i][4 * hlf + c];
-            qv[c] = (bf16)vq[4 * hlf + c];
+            if constexpr (QP) qv[c] = (bf16)vq[4 * hlf + c];
           }
           const uint32_t o = p_td[i][hlf];
           lds_st<bf16x4>(smem, st + C::S_KH + o, h);
           lds_st<bf16x4>(smem, st + C::S_KB + o, b);
-          if constexpr (PREFILL) lds_st<bf16x4>(smem, st + C::S_QH + o, qv);
+          if constexpr (QP) lds_st<bf16x4>(smem, st + C::S_QH + o, qv);
         }
       } else {
 #pragma unroll
@@ -342,7 +346,7 @@ struct ChunkKernel {
           f32x4 b = {kb[i][4 * hlf], kb[i][4 * hlf + 1], kb[i][4 * hlf + 2], kb[i][4 * hlf + 3]};
           lds_st<f32x4>(smem, st + C::S_KH + p_td[i][hlf], h);
           lds_st<f32x4>(smem, C::X_KB + p_td[i][hlf], b);
-          if constexpr (PREFILL) {
+          if constexpr (QP) {
             f32x4 qv = {vq[4 * hlf], vq[4 * hlf + 1], vq[4 * hlf + 2], vq[4 * hlf + 3]};
             lds_st<f32x4>(smem, st + C::S_QH + p_td[i][hlf], qv);
           }
@@ -458,7 +462,7 @@ struct ChunkKernel {
   // the work of a tile) first, then the P tiles (prefill only), then the
   // off-diagonal L tiles.  Each task goes to the wave with the least work so far
   // (greedy, at compile time), every wave of the workgroup taking part.
-  static constexpr int NT2 = PREFILL ? 20 : 10;
+  static constexpr int NT2 = QP ? 20 : 10;
   static constexpr int task_wave(int K) {
     int load[C::NW] = {};
     int w = 0;
@@ -470,11 +474,11 @@ struct ChunkKernel {
     }
     return w;
   }
-  static constexpr int task_mat(int K) { return K < 4 ? 0 : (PREFILL && K < 14 ? 1 : 0); }
+  static constexpr int task_mat(int K) { return K < 4 ? 0 : (QP && K < 14 ? 1 : 0); }
   static constexpr int task_i(int K) {
     if (K < 4) return K;
     int k = K - 4;
-    if (PREFILL) {
+    if (QP) {
       if (k < 10) {
         const int ii[10] = {3, 3, 3, 3, 2, 2, 2, 1, 1, 0};
         return ii[k];
@@ -487,7 +491,7 @@ struct ChunkKernel {
   static constexpr int task_j(int K) {
     if (K < 4) return K;
     int k = K - 4;
-    if (PREFILL) {
+    if (QP) {
       if (k < 10) {
         const int jj[10] = {3, 2, 1, 0, 2, 1, 0, 1, 0, 0};
         return jj[k];
@@ -848,8 +852,8 @@ struct ChunkKernel {
   }
 
   __device__ __forceinline__ void c2(uint32_t st, int chunk) {
-    if constexpr (PREFILL && !BWD) {
-      if (!a.o) return;  // a pass run only for its state checkpoints
+    if constexpr (QP && !BWD) {
+      if (!a.o) return;
       c2_half<0>(st, chunk);
       c2_half<2>(st, chunk);
     }
@@ -1278,7 +1282,7 @@ struct ChunkKernel {
     rv = make_rsrc(a.v ? reinterpret_cast<const char*>(a.v) + base : nullptr, a.v ? rowbytes : 0u);
     rla = make_rsrc(reinterpret_cast<const char*>(a.la) + base, rowbytes);
     rbeta = make_rsrc(reinterpret_cast<const char*>(a.beta) + tok0 * C::ES, (uint32_t)Tlen * C::ES);
-    if constexpr (PREFILL) rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, rowbytes);
+    if constexpr (QP) rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, rowbytes);
     // without o (a forward pass run for its state checkpoints) every store is
     // dropped; the backward chain writes dv through it
     if constexpr (PREFILL)
@@ -1289,7 +1293,7 @@ struct ChunkKernel {
     // it (tiles (0,1) and (2,3); for the backward chain's P^T, tiles (1,0) and
     // (3,2) of P^T): nothing writes them, and they must hold the zeros of P's
     // upper triangle.
-    if constexpr (PREFILL && C::JPB == 2) {
+    if constexpr (QP && C::JPB == 2) {
       for (uint32_t t = threadIdx.x; t < 2u * 64u * C::STAGES; t += C::THREADS) {
         // forward: slots (I = 2, m = 1) and (I = 0, m = 0), second half;
         // backward: slots (J = 3, m = 1) and (J = 1, m = 0), first half
@@ -1365,11 +1369,11 @@ struct ChunkKernel {
   }
 };
 
-template <typename T, int D, int NC, bool PREFILL, bool BWD = false>
+template <typename T, int D, int NC, bool PREFILL, bool BWD = false, bool CKPT = false>
 __global__ __launch_bounds__(64 * (NC + D / 32), 1)
 void kda_chunk_kernel(ChunkArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[ChunkCfg<T, D, NC, PREFILL>::LDS];
-  ChunkKernel<T, D, NC, PREFILL, BWD> kern;
+  ChunkKernel<T, D, NC, PREFILL, BWD, CKPT> kern;
   kern.smem = smem;
   kern.a = a;
   kern.run();
@@ -1417,6 +1421,32 @@ hipError_t launch_chunk_bwd(const ChunkArgs& a, int D, int nc, int nwg, hipStrea
     switch (nc) {
       case 1: return launch_bwd_one<64, 1>(a, nwg, stream);
       case 2: return launch_bwd_one<64, 2>(a, nwg, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int D, int NC>
+static hipError_t launch_ckpt_one(const ChunkArgs& a, int nwg, hipStream_t stream) {
+  using Cf = ChunkCfg<bf16, D, NC, true>;
+  hipLaunchKernelGGL((kda_chunk_kernel<bf16, D, NC, true, false, true>), dim3(nwg), dim3(Cf::THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_ckpt(const ChunkArgs& a, int D, int nc, int nwg, hipStream_t stream) {
+  if (D == 128) {
+    switch (nc) {
+      case 1: return launch_ckpt_one<128, 1>(a, nwg, stream);
+      case 2: return launch_ckpt_one<128, 2>(a, nwg, stream);
+      case 4: return launch_ckpt_one<128, 4>(a, nwg, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (D == 64) {
+    switch (nc) {
+      case 1: return launch_ckpt_one<64, 1>(a, nwg, stream);
+      case 2: return launch_ckpt_one<64, 2>(a, nwg, stream);
       default: return hipErrorInvalidValue;
     }
   }

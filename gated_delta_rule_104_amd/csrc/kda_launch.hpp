@@ -63,6 +63,10 @@ struct ChunkArgs {
 // consumer waves per workgroup ({1, 2, 4} at D = 128, {1, 2} at D = 64).
 hipError_t launch_chunk_bwd(const ChunkArgs& a, int D, int nc, int nwg, hipStream_t stream);
 
+// Prefill run only for the gradients' checkpoints (bf16; a.o null, q unused):
+// the ck_* pointers above; nc as for launch_chunk_bwd.
+hipError_t launch_chunk_ckpt(const ChunkArgs& a, int D, int nc, int nwg, hipStream_t stream);
+
 // 16-column state tiles each consumer wave of the chunk kernel owns.
 inline int chunk_tiles_per_wave(bool bf16_io) { return bf16_io ? 2 : 1; }
 
