@@ -1051,6 +1051,18 @@ struct ChunkKernel {
       for (int j = 0; j < NCT; ++j)
 #pragma unroll
         for (int m = 0; m < NKD; ++m) sb[j][m] = F::bfrag(S[j], m);
+      // dS = dU + Qh^T dO + ...: the Qh^T dO part needs nothing from this
+      // chunk's solve, so it is issued first
+#pragma unroll
+      for (int ci = 0; ci < D / 16; ++ci) {
+        typename F::A fq[NKT];
+#pragma unroll
+        for (int m = 0; m < NKT; ++m) fq[m] = tr_frag(st + C::S_QH, ci, m);
+#pragma unroll
+        for (int m = 0; m < NKT; ++m)
+#pragma unroll
+          for (int j = 0; j < NCT; ++j) S[j][ci] = F::mma(S[j][ci], fq[m], dob[j][m]);
+      }
       // dDelta = Kb dU + P^T dO, row tile by row tile
       f32x4 Xb[NCT][4];
 #pragma unroll
@@ -1125,23 +1137,17 @@ struct ChunkKernel {
       for (int j = 0; j < NCT; ++j)
 #pragma unroll
         for (int m = 0; m < NKT; ++m) yb[j][m] = F::bfrag(Xb[j], m);
-      // dS = dU + Qh^T dO + Kh^T (-diag(b) Xbar), state row tile by row tile
+      // ... + Kh^T (-diag(b) Xbar), state row tile by row tile
 #pragma unroll
       for (int ci = 0; ci < D / 16; ++ci) {
-        typename F::A fq[NKT], fh[NKT];
+        typename F::A fh[NKT];
 #pragma unroll
-        for (int m = 0; m < NKT; ++m) {
-          fq[m] = tr_frag(st + C::S_QH, ci, m);
-          fh[m] = tr_frag(st + C::S_KH, ci, m);
-        }
+        for (int m = 0; m < NKT; ++m) fh[m] = tr_frag(st + C::S_KH, ci, m);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < NKT; ++m)
 #pragma unroll
-          for (int j = 0; j < NCT; ++j) {
-            S[j][ci] = F::mma(S[j][ci], fq[m], dob[j][m]);
-            S[j][ci] = F::mma(S[j][ci], fh[m], yb[j][m]);
-          }
+          for (int j = 0; j < NCT; ++j) S[j][ci] = F::mma(S[j][ci], fh[m], yb[j][m]);
       }
     }
   }
