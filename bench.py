@@ -289,7 +289,8 @@ def backward_path_bytes(B, H, T, D, C=CH):
       reverse chain: reads q, k, log_alpha, dO, beta; writes dv and dU (D x D);
       per-chunk gradients: reads q, k, log_alpha, dO, dv, beta and S, dU,
         Delta; writes dq, dk, dlog_alpha, dbeta;
-    plus S0, dS_T read and dS0 written once per head (fp32).  The rows the
+    plus S0, dS_T read and dS0 and the forward pass's (unused) end state
+    written once per head (fp32).  The rows the
     chain kernels keep only for tokens with beta below 2^-30 (none in the
     benchmark's inputs) are not counted."""
     tok = C * 2 * D                     # one [C][D] bf16 tile
@@ -297,7 +298,7 @@ def backward_path_bytes(B, H, T, D, C=CH):
     k2 = 4 * tok + 2 * C + tok + D * D * 2
     k3 = 5 * tok + 2 * C + 2 * D * D * 2 + tok + 3 * tok + 2 * C
     nchunks = -(-T // C)
-    return B * H * nchunks * (k1 + k2 + k3) + 3 * B * H * D * D * 4
+    return B * H * nchunks * (k1 + k2 + k3) + 4 * B * H * D * D * 4
 
 
 def backward_flops(B, H, T, D, C=CH):
