@@ -34,7 +34,7 @@
 // b below kTinyBeta do they also keep W, A's row and Xbar, from which this
 // kernel forms dbeta_r = Xbar_r . (W_r - sum_{s<r} A_rs Delta_s).  Two workgroups
 // per (head, chunk), each owning half of the key dimension's columns with one
-// wave per 16 columns (4 waves at d = 128).  Each needs about 74 KiB of LDS,
+// wave per 16 columns (4 waves at d = 128).  Each needs about 72 KiB of LDS,
 // so two run on a CU at once and one's loads overlap the other's arithmetic.
 // Phases, each ended by a workgroup barrier:
 //   1. every wave copies its share of dO, Delta and dv into LDS tiles (all
