@@ -259,16 +259,19 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
  * fp32), as autograd frameworks expect.
  * bf16 inputs run in the chunked form, on the matrix cores (bf16 operands,
  * fp32 accumulation): a forward pass that keeps, for every 64-token chunk, its
- * start state S, W = V - Kh S, Delta and strict_lower(Kh Kb^T); beside it the reverse chain over the
- * chunks (dS' -> dS, which needs no forward state), which keeps
- * dU = Diag(Gam) dS' and Xbar of every chunk and writes dv_; then every
- * (head, chunk)'s remaining gradients in parallel.  fp32
+ * start state S and Delta; beside it the reverse chain over the chunks
+ * (dS' -> dS, which needs no forward state), which keeps dU = Diag(Gam) dS'
+ * of every chunk and writes dv_; then every (head, chunk)'s remaining
+ * gradients in parallel.  For tokens with beta below 2^-30 the two chains
+ * also keep W = V - Kh S, Xbar and the token's row of strict_lower(Kh Kb^T),
+ * from which such a token's dbeta is formed.  fp32
  * inputs run the recurrence's token steps backwards in fp32, token by token,
  * one workgroup (or two, each with half of the state's columns) per head.
  * The workspace (device memory, at least kda_backward_workspace_bytes for the
- * same dtype, 16-byte aligned) holds, for bf16, those per-chunk values (bf16:
- * S and dU dk x dv each, W, Delta and Xbar 64 x dv each, the 64 x 64 lower
- * blocks; 117 KiB per chunk-head at d = 128) and one fp32 end state per head; for fp32, a state
+ * same dtype, 16-byte aligned) holds, for bf16, room for those per-chunk
+ * values (bf16: S and dU dk x dv each, W, Delta and Xbar 64 x dv each, the
+ * 64 x 64 lower blocks; 117 KiB per chunk-head at d = 128) and one fp32 end
+ * state per head; for fp32, a state
  * checkpoint every 64 tokens, the entering
  * states and vectors u = (Diag(alpha) S)^T k of one 64-token interval, per
  * head, and the two halves' row sums.  Its contents on return are undefined.
