@@ -14,8 +14,9 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Every tensor pointer is a DEVICE pointer to a contiguous row-major array,
- *    aligned to 16 bytes.  The caller owns all memory; the library allocates,
- *    frees and synchronises nothing inside these calls.
+ *    aligned to 16 bytes.  The caller owns all memory; the library allocates
+ *    and frees no device memory inside these calls, and synchronises nothing
+ *    except in the check mode described below.
  *  - `dtype` gives the element type of q, k, v, log_alpha, beta and o.  States
  *    (S0, S_T, S, S_zero_end, M, S_in, S_start) are always fp32.
  *  - The gate is passed in log space: log_alpha = log(alpha), one value per key
