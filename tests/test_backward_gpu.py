@@ -202,6 +202,23 @@ def test_backward_chunked_one_loss_term(with_dO, with_dST):
     assert max(err.values()) <= TOL["bf16"], err
 
 
+def test_backward_chunked_single_long_head():
+    """One head over 4100 tokens (65 chunks, the last one ragged): one
+    workgroup per chain beside 130 gradient workgroups."""
+    err = grads_case(1, 1, 4100, 128, "bf16", 350, variant="slow")
+    assert max(err.values()) <= TOL["bf16"], err
+
+
+def test_backward_chunked_no_loss():
+    """dO and dS_T both NULL: the loss is zero and so is every gradient."""
+    d = ki.gen_prefill(2, 2, 150, 128, 128, "bf16", seed=351, s0_std=0.1, variant="slow")
+    g = {n: (x.to(dev()) if x is not None else None) for n, x in d.items()}
+    out = kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], None, None)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.count_nonzero(out[n]).item() == 0, n
+
+
 def test_backward_chunked_zero_tokens():
     """T = 0 on the chunked path: dS0 = dS_T exactly."""
     B, H, D = 2, 2, 128
