@@ -349,8 +349,15 @@ struct GradKernel {
   // this lane's own positions (tokens 16t + 4g + e of column c: exactly the
   // positions of its B fragments over tokens), and fed as a bf16 part plus the
   // bf16 of the remainder.
-  __device__ __forceinline__ void phase5_6(int j, const Pre5& p) {
-    const int c = col(j);
+  // Phase 3 runs in two parts: what needs only the chunk's tiles and rows of
+  // S and dU (phase5a: rowsum(dU . S), the gate, dO S^T, dv S^T, Delta dU^T)
+  // goes before the barrier that hands over the 64 x 64 gradients, so that the
+  // waves with fewer of those tasks do it while the others finish theirs.
+  struct Part3 {
+    f32x4 qv[4], kv[4], eg[4], emg[4], dqh[4], dkh[4], dks[4];
+    float dgc;
+  };
+  __device__ __forceinline__ void phase5a(int j, const Pre5& p, Part3& z) {
     // rows c of S and dU as B fragments over the state's columns, and
     // rowsum(dU . S) over the lane's positions
     const bf16x8* sr = p.sr[j];
@@ -363,9 +370,13 @@ struct GradKernel {
     // rowsum(dU . S): the four lane groups (l%16 fixed) hold the rest of the row's sum
     dgc += __shfl_xor(dgc, 16);
     dgc += __shfl_xor(dgc, 32);
+    z.dgc = dgc;
     // the gate at this lane's positions: g from log_alpha by a prefix over the
     // lane's 4 rows, then over the lane groups and row tiles
-    f32x4 qv[4], kv[4], eg[4], emg[4];
+    f32x4* qv = z.qv;
+    f32x4* kv = z.kv;
+    f32x4* eg = z.eg;
+    f32x4* emg = z.emg;
     {
       float tot[4];
       f32x4 gv[4];
@@ -396,7 +407,6 @@ struct GradKernel {
         base += (a0 + a1) + (a2 + a3);
       }
     }
-    f32x4 dqh[4], dkh[4], dks[4], dkb[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x4 b = zero4(), q = zero4(), h = zero4();
@@ -406,16 +416,27 @@ struct GradKernel {
         q = mfma_bf16_k32(q, ar(C::DO, t, m), sr[m]);  // dO S^T
         h = mfma_bf16_k32(h, ar(C::DV, t, m), sr[m]);  // dv S^T
       }
-      dks[t] = b;
-      dkb[t] = zero4();
-      dqh[t] = q;
-      dkh[t] = h;
+      z.dks[t] = b;
+      z.dqh[t] = q;
+      z.dkh[t] = -h;  // dKh = -dv S^T + ...
     }
-    // dKh = -dv S^T + Abar Kb;  dQh += dP Kb;  dKb = Abar^T Kh + dP^T Qh (+ dks)
+  }
+
+  // dQh += dP Kb;  dKh += Abar Kb;  dKb = Abar^T Kh + dP^T Qh (+ dks), then
+  // the gate's chain rule
+  __device__ __forceinline__ void phase5b(int j, Part3& z) {
+    const int c = col(j);
+    const f32x4* qv = z.qv;
+    const f32x4* kv = z.kv;
+    const f32x4* eg = z.eg;
+    const f32x4* emg = z.emg;
+    f32x4* dqh = z.dqh;
+    f32x4* dkh = z.dkh;
+    const f32x4* dks = z.dks;
+    const float dgc = z.dgc;
+    f32x4 dkb[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dkh[t][e] = -dkh[t][e];
+    for (int t = 0; t < 4; ++t) dkb[t] = zero4();
 #pragma unroll
     for (int m = 0; m < NKT; ++m) {
       bf16x8 kbH, kbL, khH, khL, qhH, qhL;
@@ -561,9 +582,12 @@ struct GradKernel {
     sync_lds();
     p4_tasks<0>();
     if (db) dbeta_rows(tok0);
+    Part3 z[NCT];
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) phase5a(j, p5, z[j]);
     sync_lds();
 #pragma unroll
-    for (int j = 0; j < NCT; ++j) phase5_6(j, p5);
+    for (int j = 0; j < NCT; ++j) phase5b(j, z[j]);
   }
 };
 
