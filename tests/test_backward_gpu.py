@@ -209,6 +209,29 @@ def test_backward_chunked_single_long_head():
     assert max(err.values()) <= TOL["bf16"], err
 
 
+def test_backward_chunked_d64_many_heads():
+    """d = 64 with 64 heads over 2048 tokens: the chains' d = 64 variants and
+    2048 gradient workgroups; sampled heads against the oracle."""
+    B, H, T, D = 2, 32, 2048, 64
+    print(f"[case] backward d64 B={B} H={H} T={T}", flush=True)
+    d = ki.gen_prefill(B, H, T, D, D, "bf16", seed=352, s0_std=0.1, variant="slow")
+    gen = torch.Generator().manual_seed(353)
+    dO = torch.randn(B, H, T, D, generator=gen).to(torch.bfloat16)
+    dST = torch.randn(B, H, D, D, generator=gen)
+    g = {n: (x.to(dev()) if x is not None else None) for n, x in d.items()}
+    out = kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], dO.to(dev()),
+                               dST.to(dev()))
+    torch.cuda.synchronize()
+    for (b, h) in ((0, 0), (1, 31), (0, 17)):
+        sl = lambda x: x[b:b + 1, h:h + 1]
+        ref = oracle.backward(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["log_alpha"]), sl(d["beta"]),
+                              sl(d["S0"]), sl(dO), sl(dST))
+        err = {n: oracle.max_rel_l2(sl(out[n]).cpu(), ref[n], 2 if n != "dbeta" else 1, floor=1e-6)
+               for n in NAMES}
+        print(f"    head ({b},{h}) " + "  ".join(f"{k} {v:.2e}" for k, v in err.items()), flush=True)
+        assert max(err.values()) <= TOL["bf16"], err
+
+
 def test_backward_chunked_no_loss():
     """dO and dS_T both NULL: the loss is zero and so is every gradient."""
     d = ki.gen_prefill(2, 2, 150, 128, 128, "bf16", seed=351, s0_std=0.1, variant="slow")
