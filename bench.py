@@ -54,7 +54,7 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "5054cd1e2c2a7c29",
+    "sources_sha": "ac771db01840b17b",
     "direct_part": 0.1855e9 + 0.0482e9,
     "segment_transfer": 1.3029e9 + 0.0294e9,
     "segment_merge": 0.0316e9 + 0.0168e9,

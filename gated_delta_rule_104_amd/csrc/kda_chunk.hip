@@ -181,8 +181,8 @@ struct ChunkKernel {
   rsrc_t rq, rk, rv, rla, rbeta, ro;
   int Tlen, nch;
   int bh_seq;        // the sequence (segment) this workgroup works on
-  bf16* ck_w;        // this chunk's W = V - Kh S and Delta checkpoints (prefill with
-  bf16* ck_d;        // gradient checkpoints), else null
+  bf16* ck_w;        // this chunk's checkpoints of W = V - Kh S (rows with tiny beta
+  bf16* ck_d;        // only) and Delta (prefill with gradient checkpoints), else null
   int chunk0;        // chunks of the head's sequence before this segment
   float* snap_head;  // snapshot 0 of this head (prefill with snapshots), else null
   int wave, l;
@@ -991,7 +991,8 @@ struct ChunkKernel {
     if constexpr (!TIGHT) load_v(vr, cc + 1);
     if constexpr (PREFILL && !BWD) {
       // checkpoints for the gradients: the start state of every chunk, and its
-      // W = V - Kh S and Delta (stored from c1)
+      // Delta and, for the rows with beta below kTinyBeta, W = V - Kh S
+      // (stored from c1)
       ck_w = ck_d = nullptr;
       if (a.ck_rows) {
         const size_t o = (size_t)bh_seq * nch + cc;
