@@ -66,6 +66,10 @@ TRAFFIC = {
 }
 
 
+# the kernels one kda_chunk_prefill call launches at the headline workload
+TRAFFIC_PATH = ("segment_pass_launches", "zero_start_segments", "segment_merge", "corrected_heads")
+
+
 def kernel_sources_sha():
     import hashlib
     h = hashlib.sha256()
@@ -138,18 +142,19 @@ def direct_part_bytes(B, H, T0, D):
     return B * H * T0 * (2 * 5 * D + 2) + B * H * D * D * 4
 
 
+HEAD_CHUNKS = 4  # the library's default for option head_chunks
+
+
 def bench_decomposition(pf, args):
     """Per-kernel durations of the sequence-split prefill, through the public calls
-    it is made of, with the same launch shapes as kda_chunk_prefill: the direct
-    prefill of the first T0 tokens (one workgroup per head), the segment pass over
-    the G-1 segments after it (the last segment's zero-start state and map are not
-    needed), the merge of those from the direct part's end state, and the prefill
-    of all G segments.  Inside kda_chunk_prefill the first two run side by side."""
+    it is made of, with the same launch shapes as kda_chunk_prefill."""
     g = pf["g"]
     B, H, T, D = pf["B"], pf["H"], pf["T"], pf["D"]
     T0, G, Tseg = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
     if G == 1:
         return None
+    if T0 == 0:
+        return bench_decomposition_heads(pf, args, G, Tseg)
     dev = g["k"].device
     T1 = T0 + (G - 1) * Tseg
     names = ("q", "k", "v", "log_alpha", "beta")
@@ -192,6 +197,71 @@ def bench_decomposition(pf, args):
         res[name] = {"ms": ms, "algorithmic_bytes": nbytes, "GBs": nbytes / (ms * 1e-3) / 1e9}
     del head, mid, tail
     return res
+
+
+def bench_decomposition_heads(pf, args, G, Tseg):
+    """The default split pipeline (segments from zero, heads corrected), piece by
+    piece through public calls with the launch shapes it uses:
+    - head_walk: the segment pass over the first HEAD_CHUNKS chunks of segments
+      1 .. G-1 (224 workgroups here); inside the call only the map columns run,
+      so the public call, which also carries the state columns, bounds it above;
+    - zero_start_segments: the prefill of all G segments from zero (one
+      workgroup per segment and head), the dominant kernel; inside the call it
+      also writes every segment's end state;
+    - segment_merge: the merge over segments 1 .. G-1; inside the call the maps
+      that vanished are neither read nor applied, so this bounds it above;
+    - corrected_heads: the prefill of the first HEAD_CHUNKS chunks of segments
+      1 .. G-1 from their start states.
+    With the workloads' gates every map vanishes within the head, so the
+    segment pass over the other segments does no work (its workgroups exit)."""
+    g = pf["g"]
+    B, H, T, D = pf["B"], pf["H"], pf["T"], pf["D"]
+    dev = g["k"].device
+    Lh = HEAD_CHUNKS * CH
+    starts = [i * Tseg for i in range(1, G)]
+    if any(s + Lh > T for s in starts):
+        return None
+    names = ("q", "k", "v", "log_alpha", "beta")
+    heads = {n: torch.cat([g[n][:, :, s:s + Lh] for s in starts], dim=2).contiguous() for n in names}
+    Zh = torch.empty(G - 1, B, H, D, D, dtype=torch.float32, device=dev)
+    Mh = torch.empty_like(Zh)
+    S_start = torch.empty_like(Zh)
+    S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    S_T2 = torch.empty_like(S_T)
+    o_all = torch.empty(B, H, T, D, dtype=torch.bfloat16, device=dev)
+    o_heads = torch.empty(B, H, (G - 1) * Lh, D, dtype=torch.bfloat16, device=dev)
+    Ztot = torch.randn(G - 1, B, H, D, D, device=dev)
+    Mtot = torch.randn(G - 1, B, H, D, D, device=dev) * 0.01
+    S1 = torch.randn(B, H, D, D, device=dev)
+    parts = {
+        "head_walk": (lambda: kda.segment_transfer(heads["k"], heads["v"], heads["log_alpha"], heads["beta"],
+                                                   G - 1, S_zero_end=Zh, M=Mh),
+                      segment_pass_bytes(B, H, (G - 1) * Lh, D, G - 1)),
+        "zero_start_segments": (lambda: kda.prefill_segments(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"],
+                                                             None, Tseg, o=o_all, S_T=S_T),
+                                zero_start_bytes(B, H, T, D, G)),
+        "segment_merge": (lambda: kda.segment_merge(Ztot, Mtot, S1, S_start=S_start, S_T=S_T2),
+                          merge_bytes(B, H, D, G - 1)),
+        "corrected_heads": (lambda: kda.prefill_segments(heads["q"], heads["k"], heads["v"], heads["log_alpha"],
+                                                         heads["beta"], S_start, Lh, o=o_heads, S_T=S_T2),
+                            segment_prefill_bytes(B, H, (G - 1) * Lh, D, G - 1)),
+    }
+    for fn, _ in parts.values():
+        fn()
+    torch.cuda.synchronize()
+    res = {"T0": 0, "G": G, "Tseg": Tseg, "head_chunks": HEAD_CHUNKS}
+    n = max(5, args.steps)
+    for name, (fn, nbytes) in parts.items():
+        ms, _ = time_launches(fn, n)
+        res[name] = {"ms": ms, "algorithmic_bytes": nbytes, "GBs": nbytes / (ms * 1e-3) / 1e9}
+    del heads, o_all, o_heads
+    return res
+
+
+def zero_start_bytes(B, H, T, D, G):
+    """Prefill of every segment from zero: q, k, log_alpha, v, beta read and o
+    written once, an end state written per segment and head."""
+    return B * H * T * (2 * 5 * D + 2) + G * B * H * D * D * 4
 
 
 def bench_prefill(args, dev):
@@ -652,23 +722,30 @@ def main():
     fl_dense = prefill_flops(B, H, T, D)
     fl_tri = prefill_flops(B, H, T, D, triangle=True)
     dec = bench_decomposition(pf, args)
-    if dec is not None:
+    if dec is not None and dec["T0"] == 0:
+        names = ("head_walk", "zero_start_segments", "segment_merge", "corrected_heads")
+        kern = {"head_walk": "kda_chunk_kernel<bf16,128,8,segment> (first chunks of segments 1..G-1)",
+                "zero_start_segments": "kda_chunk_kernel<bf16,128,4,prefill> (every segment from zero)",
+                "segment_merge": "kda_merge_kernel<128>",
+                "corrected_heads": "kda_chunk_kernel<bf16,128,4,prefill> (first chunks from the start states)"}
+    elif dec is not None:
         names = ("direct_part", "segment_transfer", "segment_merge", "segment_prefill")
         kern = {"direct_part": "kda_chunk_kernel<bf16,128,4,prefill> (first part, one workgroup per head)",
                 "segment_transfer": "kda_chunk_kernel<bf16,128,8,segment>",
                 "segment_merge": "kda_merge_kernel<128>",
                 "segment_prefill": "kda_chunk_kernel<bf16,128,4,prefill>"}
+    if dec is not None:
         dom = max(names, key=lambda n: dec[n]["ms"])
         r = dec[dom]
         traffic = TRAFFIC.get(dom) if kernel_sources_sha() == TRAFFIC["sources_sha"] else None
         counters_valid = kernel_sources_sha() == TRAFFIC["sources_sha"]
-        path_counter = sum(TRAFFIC[n] for n in names) if counters_valid else None
+        path_counter = sum(TRAFFIC.get(n, 0.0) for n in TRAFFIC_PATH) if counters_valid else None
         roofline = {"bound": "hbm", "achieved": r["GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": r["GBs"] / PEAK_HBM_GBS, "traffic": traffic, "kernel": kern[dom],
                     "kernel_ms": r["ms"], "algorithmic_bytes": r["algorithmic_bytes"],
                     "path_GBs": gbs, "path_frac": gbs / PEAK_HBM_GBS,
-                    # whole call: the four kernels' counter bytes against the single-pass
-                    # algorithmic bytes (the split path re-reads k, v, log_alpha, beta)
+                    # whole call: its kernels' counter bytes against the single-pass
+                    # algorithmic bytes
                     "path_traffic": {"counter_bytes": path_counter, "algorithmic_bytes": nbytes,
                                      "ratio": path_counter / nbytes if path_counter else None}}
     else:

@@ -42,7 +42,10 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0
 // ------------------------------------------------------------------ options
 // Process-wide switches (see kda_set_option in libkda.h).  Each starts from its
 // environment variable, read once; -1 means the library's default.
-enum Opt { OPT_SPLIT, OPT_COST16, OPT_MAP_SKIP, OPT_NC, OPT_BW_SPLIT, OPT_CHECK, OPT_LOG, OPT_COUNT };
+enum Opt {
+  OPT_SPLIT, OPT_COST16, OPT_MAP_SKIP, OPT_NC, OPT_BW_SPLIT, OPT_CHECK, OPT_LOG, OPT_FIXUP, OPT_HEAD,
+  OPT_COUNT
+};
 struct OptDesc {
   const char* name;
   const char* env;
@@ -50,7 +53,8 @@ struct OptDesc {
 const OptDesc kOpts[OPT_COUNT] = {{"split", "KDA_SPLIT"},       {"transfer_cost16", "KDA_TRANSFER_COST16"},
                                   {"map_skip", "KDA_MAP_SKIP"}, {"nc", "KDA_NC"},
                                   {"bw_split", "KDA_BW_SPLIT"}, {"check", "KDA_CHECK"},
-                                  {"log", "KDA_LOG"}};
+                                  {"log", "KDA_LOG"},           {"fixup", "KDA_FIXUP"},
+                                  {"head_chunks", "KDA_HEAD_CHUNKS"}};
 std::atomic<long long> g_opt[OPT_COUNT];
 std::once_flag g_opt_once;
 
@@ -61,7 +65,8 @@ bool opt_valid(int o, long long v) {
     case OPT_COST16: return v >= 1 && v <= 64;
     case OPT_NC: return v == 1 || v == 2 || v == 4 || v == 8;
     case OPT_BW_SPLIT: return v == 1 || v == 2;
-    default: return v == 0 || v == 1;  // map_skip, check, log
+    case OPT_HEAD: return v >= 1 && v <= 1024;
+    default: return v == 0 || v == 1;  // map_skip, check, log, fixup
   }
 }
 
@@ -138,7 +143,22 @@ int pick_nc(long long nseq, int ncol_tiles, bool bf16_io, bool allow8 = false) {
 // Prefill of few heads over a long sequence: rather than splitting each head's
 // state columns over many workgroups (each of which then repeats the whole
 // per-chunk preparation), cut the sequence and use the context-parallel
-// decomposition.  The first T0 tokens start from the known S0 and are simply
+// decomposition.
+//
+// Default (option fixup = 1): G segments of Tseg tokens (the last one may be
+// shorter).  Segment 0 starts from S0, every other one from zero, and all of
+// them are prefilled at once, outputs included.  A segment's true outputs
+// differ from its zero-start ones by O_M S_start, where O_M is what the
+// segment's transfer map contributes to each output; once the map is exactly
+// zero (it stays zero for finite inputs) that term is exactly zero.  So a short
+// walk over the first head_chunks chunks of every segment's map decides, per
+// (segment, head), whether the map has vanished there.  If it has, only those
+// first chunks are walked again from the true start state, after the merge;
+// if not, the segment takes the path below (its zero-start end state and map
+// from the segment pass, then its whole prefill again).  Which of the two a
+// segment takes is decided on the device, so nothing waits on the host.
+//
+// Option fixup = 0: the first T0 tokens start from the known S0 and are simply
 // prefilled; meanwhile the segment pass computes the zero-start end state and
 // transfer map of each of the next G - 1 segments of Tseg tokens.  A sequential
 // merge then gives the true start state of each of the G remaining segments
@@ -160,6 +180,14 @@ struct PrefillPlan {
 };
 
 constexpr int kTransferCost16 = 12;  // segment pass / prefill time per token, in 16ths
+constexpr int kHeadChunks = 4;       // chunks walked to decide whether a segment's map has vanished
+
+int head_chunks() {
+  const long long v = opt(OPT_HEAD);
+  return v >= 1 && v <= 1024 ? (int)v : kHeadChunks;
+}
+
+bool fixup_enabled() { return opt(OPT_FIXUP) != 0; }
 
 PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
   PrefillPlan pl;
@@ -167,7 +195,7 @@ PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
   if (dt != KDA_BF16 || BH <= 0 || T <= 0) return pl;
   const long long cus = cu_count();
   const int ntiles = D / 16;
-  long long G = opt(OPT_SPLIT);  // 0: never; >= 2: that many segments after the first part
+  long long G = opt(OPT_SPLIT);  // 0: never; >= 2: that many segments (after the first part)
   if (G >= 0) {
     if (G < 2) return pl;
   } else {
@@ -176,6 +204,21 @@ PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
     G = (cus + BH - 1) / BH;  // one round of segment prefills
     if (G > T / 1024) G = T / 1024;
     if (G < 2) return pl;
+  }
+  if (fixup_enabled()) {
+    // G equal segments, the first from S0
+    const long long Tseg = ((T + G - 1) / G + 63) / 64 * 64;
+    const long long Geff = (T + Tseg - 1) / Tseg;
+    if (Geff < 2) return pl;
+    pl.split = true;
+    pl.T0 = 0;
+    pl.G = (int)Geff;
+    pl.Tseg = (int)Tseg;
+    // Z of all G segments, M and start states of the G - 1 after the first,
+    // and their records
+    pl.ws = (size_t)(3 * Geff - 2) * BH * D * D * sizeof(float) +
+            (size_t)(Geff - 1) * BH * kda::kFlagSlots * sizeof(uint32_t);
+    return pl;
   }
   long long cost16 = opt(OPT_COST16);
   if (cost16 < 1 || cost16 > 64) cost16 = kTransferCost16;
@@ -307,16 +350,30 @@ struct Snap {
   int H = 1;
 };
 
+// Per-segment control of a prefill launch in the split path with corrected
+// heads (ChunkArgs::seg_flag and the fields after it).
+struct SegCtl {
+  uint32_t* rec = nullptr;
+  int mode = kda::FLAG_NONE;
+  int g0 = 0;
+  int head = 0;
+  float* Z_out = nullptr;
+  bool s0_first = false;
+  const float* Z_prev = nullptr;
+};
+
 // Prefill of the G = ceil((Tend - t0) / Tseg) consecutive segments of tokens
 // [t0, Tend) of every head (sequences of T tokens), segment i from Sst[i] (null:
-// zero); S_T receives the end state of the last segment.  nc = 0 picks the
-// consumer-wave count.
+// zero; with sc.s0_first, Sst [BH, D, D] is segment 0's start and the others
+// start from zero); S_T (if not null) receives the end state of the last
+// segment.  nc = 0 picks the consumer-wave count.
 kda_status launch_segment_prefill(const void* q, const void* k, const void* v, const void* log_alpha,
                                   const void* beta, const float* Sst, void* o, float* S_T,
                                   long long BH, int T, int t0, int Tend, int Tseg, int D, bool bf,
                                   hipStream_t stream, const char* what, const Snap& sn = Snap(),
                                   int nc = 0, kda::bf16* ck_rows = nullptr, kda::bf16* ck_w = nullptr,
-                                  kda::bf16* ck_d = nullptr, kda::bf16* ck_a = nullptr) {
+                                  kda::bf16* ck_d = nullptr, kda::bf16* ck_a = nullptr,
+                                  const SegCtl& sc = SegCtl()) {
   const int n = Tend - t0;
   const int G = n > 0 ? (int)(((long long)n + Tseg - 1) / Tseg) : 1;  // no tokens: copy the start state
   const long long nseq = BH * G;
@@ -330,6 +387,8 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
   a.snap = sn.n > 0 ? sn.p : nullptr; a.snap_chunks = sn.chunks > 0 ? sn.chunks : 1;
   a.nsnap = sn.n; a.H = sn.H;
   a.ck_rows = ck_rows; a.ck_w = ck_w; a.ck_d = ck_d; a.ck_a = ck_a;
+  a.seg_flag = sc.rec; a.flag_mode = sc.mode; a.flag_g0 = sc.g0; a.head_chunks = sc.head;
+  a.Z_out = sc.Z_out; a.s0_first = sc.s0_first ? 1 : 0; a.Z_prev = sc.Z_prev;
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (log_on())
@@ -463,6 +522,91 @@ kda_status scratch_ptr(void** out) {
   return KDA_OK;
 }
 
+// The split prefill with corrected segment heads (plan T0 = 0): G segments of
+// Ts tokens, segment 0 from S0.  The workspace holds Z [G, BH, D, D] (the
+// zero-start end states; segment 0's from S0), M and the start states
+// [G - 1, BH, D, D] of segments 1 .. G-1, and their records [G - 1, BH,
+// kFlagSlots].  On the caller's stream, with the segment pass's step on the
+// side stream:
+//  1. the head walk: the first head_chunks chunks of every later segment's
+//     transfer map, which writes the records (nonzero: the map has not
+//     vanished there);
+//  2. beside each other: the prefill of segment 0 and of every segment whose map
+//     vanished, from zero, outputs and end states included; and the segment
+//     pass over the others (their Z and M);
+//  3. the merge, which runs the chain only through the segments whose map did
+//     not vanish (after a segment whose map vanished, the next one's start
+//     state is that segment's zero-start end state, read from Z directly);
+//  4. the prefill from the true start states: the first head_chunks chunks of
+//     the segments whose map vanished (their outputs are replaced), the whole
+//     of the others.
+kda_status prefill_split_heads(const void* q, const void* k, const void* v, const void* log_alpha,
+                               const void* beta, const float* S0, void* o, float* S_T, long long BH,
+                               int T, int D, bool bf, int G, int Ts, float* ws, const Snap& sn,
+                               hipStream_t stream) {
+  const int G1 = G - 1;
+  const size_t nS = (size_t)BH * D * D;
+  float* Z = ws;              // [G]
+  float* M = Z + G * nS;      // [G - 1], segments 1 .. G-1
+  float* Sst = M + G1 * nS;   // [G - 1]
+  uint32_t* rec = reinterpret_cast<uint32_t*>(Sst + G1 * nS);
+  const int head = head_chunks();
+  SideStream* ss = nullptr;
+  kda_status st;
+  if ((st = side_stream(stream, &ss)) != KDA_OK) return st;
+  // the segment pass's launches cover segments 1 .. G-1
+  kda::ChunkArgs t;
+  t.q = nullptr; t.k = k; t.v = v; t.la = log_alpha; t.beta = beta;
+  t.S0 = nullptr; t.o = nullptr; t.S_out = nullptr; t.M_out = nullptr;
+  t.BH = (int)BH; t.G = G1; t.Tseg = Ts; t.Ttot = T; t.t0 = Ts; t.Tend = T;
+  const int nt2 = 2 * D / 16, nc2 = pick_nc(BH * G1, nt2, bf, D == 128);
+  t.vsplit = nt2 / (nc2 * kda::chunk_tiles_per_wave(bf));
+  t.map_skip = map_skip_enabled();
+  t.seg_flag = rec; t.flag_g0 = 0; t.head_chunks = head;
+  const int nwg2 = (int)(BH * G1 * t.vsplit);
+  const int nc1 = D / 16 / kda::chunk_tiles_per_wave(bf);  // one workgroup per sequence
+  if (log_on())
+    fprintf(stderr, "[libkda] prefill split BH=%lld T=%d D=%d: %d x %d-token segments, heads of %d chunks "
+            "corrected; transfer nc=%d vsplit=%d\n", BH, T, D, G, Ts, head, nc2, t.vsplit);
+  hipError_t e;
+  // 1. the head walk
+  t.flag_mode = kda::FLAG_HEAD;
+  if ((e = kda::launch_chunk(t, bf, D, false, nc2, nwg2, stream)) != hipSuccess)
+    return hip_fail(e, "kda_chunk_prefill head walk");
+  {
+    // 2. the segment pass over the segments whose map did not vanish (side
+    //    stream), beside the prefill of all the others from zero
+    std::lock_guard<std::mutex> lk(ss->mu);
+    if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess ||
+        (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
+      return hip_fail(e, "kda_chunk_prefill fork");
+    t.flag_mode = kda::FLAG_SLOW_ONLY;
+    t.S_out = Z + nS;
+    t.M_out = M;
+    if ((e = kda::launch_chunk(t, bf, D, false, nc2, nwg2, ss->s)) != hipSuccess)
+      return hip_fail(e, "kda_chunk_prefill segment pass");
+    SegCtl sc;
+    sc.rec = rec; sc.mode = kda::FLAG_FAST_ONLY; sc.g0 = 1; sc.Z_out = Z; sc.s0_first = true;
+    st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, o, nullptr, BH, T, 0, T, Ts, D, bf, stream,
+                                "kda_chunk_prefill zero-start segments", sn, nc1, nullptr, nullptr, nullptr,
+                                nullptr, sc);
+    // join even if the launch above failed, so the side stream's work is waited for
+    if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess ||
+        (e = hipStreamWaitEvent(stream, ss->join, 0)) != hipSuccess)
+      return hip_fail(e, "kda_chunk_prefill join");
+    if (st != KDA_OK) return st;
+  }
+  // 3. the merge, from segment 0's end state
+  if ((e = kda::launch_merge(Z, Z + nS, M, Sst, S_T, (int)BH, G1, D, stream, rec)) != hipSuccess)
+    return hip_fail(e, "kda_chunk_prefill merge");
+  // 4. the heads (or whole segments) again from the true start states
+  SegCtl sc;
+  sc.rec = rec; sc.mode = kda::FLAG_FIX; sc.g0 = 0; sc.head = head; sc.Z_prev = Z;
+  return launch_segment_prefill(q, k, v, log_alpha, beta, Sst, o, nullptr, BH, T, Ts, T, Ts, D, bf, stream,
+                                "kda_chunk_prefill corrected heads", sn, nc1, nullptr, nullptr, nullptr,
+                                nullptr, sc);
+}
+
 // The prefill with or without snapshots.  noalloc: the split path's workspace is
 // the library's scratch array (workspace / workspace_bytes are ignored), and a
 // plan that needs more than the array holds is refused.
@@ -502,6 +646,11 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
       if ((st = scratch_ptr(&workspace)) != KDA_OK) return st;
       workspace_bytes = kScratchBytes;
     }
+  }
+  if (pl.split && workspace && workspace_bytes >= pl.ws && pl.T0 == 0) {
+    st = prefill_split_heads(q, k, v, log_alpha, beta, S0, o, S_T, BH, T, D, bf, pl.G, pl.Tseg,
+                             static_cast<float*>(workspace), sn, stream);
+    return st == KDA_OK ? ok() : st;
   }
   if (pl.split && workspace && workspace_bytes >= pl.ws) {
     const int G = pl.G, G1 = G - 1, T0 = pl.T0, Ts = pl.Tseg;

@@ -1263,7 +1263,10 @@ struct ChunkKernel {
     int id = blockIdx.x;
     // Consecutive blockIdx go to different XCDs (round-robin over 8); regroup so
     // that the workgroups sharing a sequence land on one XCD and share its L2.
-    if ((W & 7) == 0) id = (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
+    // With one workgroup per sequence nothing is shared, and the launch order is
+    // kept: the sequences that run while others exit at once (the split
+    // prefill's segment 0) then spread over all XCDs instead of filling one.
+    if ((W & 7) == 0 && a.vsplit > 1) id = (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
     const int seq = id / a.vsplit;
     const int vs = id - seq * a.vsplit;
     bh_seq = seq;
@@ -1274,6 +1277,34 @@ struct ChunkKernel {
     Tlen = min(a.Tseg, a.Tend - seg0);
     nch = (Tlen + CH - 1) / CH;
     chunk0 = seg0 / CH;
+    // Segments with corrected heads: whether this one runs, and how far (the
+    // decision is the same for every wave of the workgroup, taken before any
+    // barrier).
+    const int rec = (gseg - a.flag_g0) * a.BH + bh;
+    // whether record r (>= 0) says the map has not vanished
+    auto rec_live = [&](int r) -> bool {
+      const uint32_t* f = a.seg_flag + (size_t)r * kFlagSlots;
+      uint32_t x = 0u;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) x |= f[i];
+      return x != 0u;
+    };
+    bool pred_live = true;  // FLAG_FIX: the previous segment's map had not vanished
+    if (a.flag_mode != FLAG_NONE) {
+      const bool has_rec = gseg >= a.flag_g0;
+      const bool live = has_rec && a.flag_mode != FLAG_HEAD && rec_live(rec);
+      if (a.flag_mode == FLAG_FIX) pred_live = gseg > a.flag_g0 && rec_live(rec - a.BH);
+      switch (a.flag_mode) {
+        case FLAG_HEAD: nch = min(nch, a.head_chunks); break;
+        case FLAG_SLOW_ONLY: if (!has_rec || !live) return; break;
+        case FLAG_FAST_ONLY: if (has_rec && live) return; break;
+        case FLAG_FIX:
+          if (!has_rec) return;
+          if (!live) nch = min(nch, a.head_chunks);
+          break;
+        default: break;
+      }
+    }
     snap_head = nullptr;
     if (PREFILL && a.snap) {
       const int b = bh / a.H, h = bh - b * a.H;
@@ -1314,12 +1345,19 @@ struct ChunkKernel {
     colb = vs * 16 * NC * NCT + 16 * NCT * wave + NCT * (l & 15);
     isv = PREFILL || colb < D;  // a wave's tiles lie on one side of D
     mskip = !PREFILL && a.map_skip && __builtin_amdgcn_readfirstlane(isv ? 0 : 1);
-    mzero = false;
+    // the head walk carries the map columns only
+    mzero = !PREFILL && a.flag_mode == FLAG_HEAD && __builtin_amdgcn_readfirstlane(isv ? 1 : 0);
     const size_t sbase = (size_t)seq * D * D;
+    // prefill start state: one per sequence, or (s0_first) S0 [BH, D, D] for
+    // segment 0 and zero for the others; when correcting a head whose previous
+    // segment's map vanished, that segment's zero-start end state (Z_prev)
+    const float* s0 = nullptr;
+    if (PREFILL && a.flag_mode == FLAG_FIX && !pred_live) s0 = a.Z_prev + sbase;
+    else if (PREFILL && a.S0) s0 = !a.s0_first ? a.S0 + sbase : gseg == 0 ? a.S0 + (size_t)bh * D * D : nullptr;
     if (wave < NC) {
-      if (PREFILL && NCT == 2 && a.S0) {
+      if (PREFILL && NCT == 2 && s0) {
         // the lane's two adjacent columns of a row as one 8-byte load
-        const rsrc_t rs = make_rsrc(a.S0 + sbase, D * D * 4);
+        const rsrc_t rs = make_rsrc(s0, D * D * 4);
 #pragma unroll
         for (int ci = 0; ci < D / 16; ++ci)
 #pragma unroll
@@ -1340,7 +1378,7 @@ struct ChunkKernel {
               const int c = colb + j;
               float x = 0.f;
               if (PREFILL) {
-                if (a.S0) x = a.S0[sbase + (size_t)r * D + c];
+                if (s0) x = s0[(size_t)r * D + c];
               } else if (!isv) {
                 x = (r == c - D) ? 1.f : 0.f;
               }
@@ -1360,12 +1398,25 @@ struct ChunkKernel {
     }
     consumer_loop();
 
-    // prefill over several segments: only the last one's end state is the result
+    if (!PREFILL && a.flag_mode == FLAG_HEAD) {
+      // the segment's record: one word per consumer wave, nonzero while any of
+      // the wave's map columns is not exactly zero
+      const bool live = !isv && !state_is_zero();
+      if (l == 0) a.seg_flag[(size_t)rec * kFlagSlots + vs * NC + wave] = live ? 1u : 0u;
+      return;
+    }
+    // prefill over several segments: every segment's end state (Z_out), or only
+    // the last one's (S_out, if given)
     float* dst;
     int c = colb;
     if (PREFILL) {
-      if (a.G > 1 && gseg != a.G - 1) return;
-      dst = a.S_out + (size_t)bh * D * D;
+      if (a.Z_out) {
+        dst = a.Z_out + sbase;
+      } else {
+        if (a.G > 1 && gseg != a.G - 1) return;
+        if (!a.S_out) return;
+        dst = a.S_out + (size_t)bh * D * D;
+      }
     } else if (isv) {
       dst = a.S_out + sbase;
     } else {

@@ -55,6 +55,45 @@ struct ChunkArgs {
   bf16* ck_a = nullptr;
   bf16* dU_rows = nullptr;
   bf16* ck_xb = nullptr;
+  // Segments started from zero whose heads are corrected afterwards (the
+  // split prefill): one record of kFlagSlots words per (segment, bh), nonzero
+  // when the segment's transfer map was not exactly zero after head_chunks
+  // chunks.  Segment g of this launch (g >= flag_g0) has record
+  // (g - flag_g0) * BH + bh; see FlagMode for what each launch does with it.
+  uint32_t* seg_flag = nullptr;
+  int flag_mode = 0;
+  int flag_g0 = 0;
+  int head_chunks = 0;
+  // prefill: the end state of every segment [G*BH, D, D] (null: S_out only)
+  float* Z_out = nullptr;
+  // prefill: S0 is segment 0's start state [BH, D, D] and the other segments
+  // start from zero (0: S0 holds one start state per sequence)
+  int s0_first = 0;
+  // FLAG_FIX: the end state of the segment before each sequence's, from zero
+  // (the first one's: from the true start) [G*BH, D, D]; a sequence whose
+  // previous segment's map vanished starts from it instead of S0
+  const float* Z_prev = nullptr;
+};
+
+// Words per segment record (one per consumer wave of the segment pass, up to
+// D/16 of them).
+constexpr int kFlagSlots = 8;
+
+enum FlagMode {
+  FLAG_NONE = 0,
+  // segment pass: walk the first head_chunks chunks of the map columns only
+  // (the state columns stay idle) and write the records instead of Z and M
+  FLAG_HEAD = 1,
+  // segment pass: run only the segments with a nonzero record
+  FLAG_SLOW_ONLY = 2,
+  // prefill: skip the segments with a nonzero record (segments below flag_g0
+  // have none and always run)
+  FLAG_FAST_ONLY = 3,
+  // prefill: segments with a zero record walk only their first head_chunks
+  // chunks, the others all of theirs; segments below flag_g0 do nothing.  A
+  // segment whose previous one has a zero record (or is the first, below
+  // flag_g0) starts from Z_prev, the others from S0
+  FLAG_FIX = 4,
 };
 
 // Reverse chain of the prefill gradients (bf16 inputs, one segment per head):
@@ -143,8 +182,15 @@ struct BwGradArgs {
 hipError_t launch_bwgrad(const BwGradArgs& a, int BH, int D, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, int BH, int D, int split, hipStream_t stream);
 
+// flags: records of the G segments as in ChunkArgs::seg_flag (record i * BH + bh;
+// a zero record means that segment's map is exactly zero), or null: every map
+// is applied.  With records, S_start[i] is written only where segment i - 1's
+// map did not vanish (elsewhere the start state is Z[i - 1], or S_in for i = 0,
+// and is read from there), and the chain runs only through the segments whose
+// map did not vanish.
 hipError_t launch_merge(const float* S_in, const float* Z, const float* M, float* S_start,
-                        float* S_T, int BH, int G, int D, hipStream_t stream);
+                        float* S_T, int BH, int G, int D, hipStream_t stream,
+                        const uint32_t* flags = nullptr);
 
 // Reads n_la gate values and n_beta betas (bf16 or fp32) on `stream`, waits for
 // the result, and sets *bits_out to bit 0 if a log_alpha value lies outside

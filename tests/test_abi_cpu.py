@@ -80,34 +80,56 @@ def test_prefill_validation(lib):
     assert prefill(lib, B=0) == OK
 
 
-def test_prefill_workspace_query(lib):
-    """The sequence-split path asks for 3G - 1 fp32 states per head (G segments
-    after the directly prefilled first part); it is not used for fp32 inputs,
-    short sequences or many heads."""
+STATE = 32 * 128 * 128 * 4  # bytes of one fp32 state per head, 32 heads
+FLAG_SLOTS = 8              # words of one segment record
+
+
+def split_ws(g, fixup=True, bh=32, d=128):
+    """Workspace of the split path for g segments: Z of all g, M and start states
+    of the g - 1 after the first, and their records (fixup); Z and M of g - 1
+    segments, the first part's end state and g start states (fixup = 0)."""
+    if fixup:
+        return (3 * g - 2) * bh * d * d * 4 + (g - 1) * bh * FLAG_SLOTS * 4
+    return (3 * g - 1) * bh * d * d * 4
+
+
+def test_prefill_workspace_query(lib, kda_opts):
+    """The sequence-split path asks for its states and segment records (see
+    split_ws); it is not used for fp32 inputs, short sequences or many heads."""
     ws = lib.kda_prefill_workspace_bytes
     ws.restype = ctypes.c_size_t
-    assert ws(1, 32, 65536, 128, 128, F32) == 0
-    assert ws(1, 32, 1024, 128, 128, BF16) == 0
-    assert ws(64, 32, 65536, 128, 128, BF16) == 0
-    assert ws(1, 32, 65536, 128, 64, BF16) == 0
+    for fixup in (None, 0):
+        kda_opts("fixup", fixup)
+        assert ws(1, 32, 65536, 128, 128, F32) == 0
+        assert ws(1, 32, 1024, 128, 128, BF16) == 0
+        assert ws(64, 32, 65536, 128, 128, BF16) == 0
+        assert ws(1, 32, 65536, 128, 64, BF16) == 0
+    kda_opts("fixup", None)
+    assert ws(1, 32, 65536, 128, 128, BF16) == split_ws(8)
+    kda_opts("fixup", 0)
     n = ws(1, 32, 65536, 128, 128, BF16)
-    assert n > 0 and n % (32 * 128 * 128 * 4) == 0 and (n // (32 * 128 * 128 * 4)) % 3 == 2
+    assert n > 0 and n % STATE == 0 and (n // STATE) % 3 == 2
 
 
-def test_prefill_plan(lib):
+def test_prefill_plan(lib, kda_opts):
     """The plan matches the workspace query: split exactly when workspace is asked
-    for; the first part and the segments are whole chunks and cover T exactly,
-    the last segment being the only short one."""
+    for; the first part (none by default: segment 0 starts from S0) and the
+    segments are whole chunks and cover T exactly, the last segment being the
+    only short one."""
     T0, G, Ts = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     plan = lambda *a: lib.kda_prefill_plan(*a, ctypes.byref(T0), ctypes.byref(G), ctypes.byref(Ts))
     ws = lib.kda_prefill_workspace_bytes
     ws.restype = ctypes.c_size_t
-    for T in (4096, 10000, 65536, 1 << 20):
-        assert plan(1, 32, T, 128, 128, BF16) == OK
-        t0, g, ts = T0.value, G.value, Ts.value
-        assert g > 1 and ts % 64 == 0 and t0 % 64 == 0 and t0 > 0, (T, t0, g, ts)
-        assert t0 + (g - 1) * ts < T <= t0 + g * ts, (T, t0, g, ts)
-        assert ws(1, 32, T, 128, 128, BF16) == (3 * g - 1) * 32 * 128 * 128 * 4
+    for fixup in (None, 0):
+        kda_opts("fixup", fixup)
+        for T in (4096, 10000, 65536, 1 << 20):
+            assert plan(1, 32, T, 128, 128, BF16) == OK
+            t0, g, ts = T0.value, G.value, Ts.value
+            assert g > 1 and ts % 64 == 0 and t0 % 64 == 0 and (t0 == 0) == (fixup is None), (T, t0, g, ts)
+            assert t0 + (g - 1) * ts < T <= t0 + g * ts, (T, t0, g, ts)
+            assert ws(1, 32, T, 128, 128, BF16) == split_ws(g, fixup is None)
+    kda_opts("fixup", None)
+    assert plan(1, 32, 65536, 128, 128, BF16) == OK and (T0.value, G.value, Ts.value) == (0, 8, 8192)
     assert plan(64, 32, 65536, 128, 128, BF16) == OK and (T0.value, G.value, Ts.value) == (0, 1, 65536)
     assert plan(1, 32, 65536, 128, 128, F32) == OK and (T0.value, G.value) == (0, 1)
     assert plan(1, 32, 100, 96, 96, BF16) == ERR_UNSUPPORTED
@@ -116,9 +138,10 @@ def test_prefill_plan(lib):
 
 def test_prefill_plan_cost_override(lib, kda_opts):
     """Option transfer_cost16 (the segment pass's cost per token relative to
-    the prefill, in 16ths) moves the first part's length; the cut still covers T
-    exactly, and values outside 1..64 are refused."""
+    the prefill, in 16ths) moves the first part's length of the fixup = 0 plan;
+    the cut still covers T exactly, and values outside 1..64 are refused."""
     T0, G, Ts = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    kda_opts("fixup", 0)
 
     def plan(T=65536):
         assert lib.kda_prefill_plan(1, 32, T, 128, 128, BF16, ctypes.byref(T0), ctypes.byref(G),
@@ -277,7 +300,8 @@ def test_options(lib, kda_opts):
     get = lambda n: (lib.kda_get_option(n, ctypes.byref(v)), v.value)[1]
     for name, good, bad in ((b"split", (0, 2, 64), (1, -2)), (b"transfer_cost16", (1, 64), (0, 65)),
                             (b"map_skip", (0, 1), (2,)), (b"nc", (1, 2, 4, 8), (3, 16)),
-                            (b"bw_split", (1, 2), (3,)), (b"check", (0, 1), (2,)), (b"log", (0, 1), (5,))):
+                            (b"bw_split", (1, 2), (3,)), (b"check", (0, 1), (2,)), (b"log", (0, 1), (5,)),
+                            (b"fixup", (0, 1), (2,)), (b"head_chunks", (1, 4, 1024), (0, 1025))):
         kda_opts(name.decode(), None)
         assert get(name) == -1
         for x in good:

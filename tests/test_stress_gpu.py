@@ -44,17 +44,25 @@ def window_errors(o, o_ref, starts, n=CH):
     return {s: oracle.rel_l2(o[s:s + n], o_ref[s:s + n]) for s in starts}
 
 
-def test_full_h32_t64k_slow_split_boundaries(kda_opts, capfd):
-    """B=1, H=32, T=65536, d=128, bf16, slow-decay gates, through the default
-    sequence-split launch (direct first part beside the 12-wave segment pass over
-    G - 1 segments, merge, prefill of G segments).  Sampled heads are compared
-    with the oracle over the whole sequence, and on the 64-token window right
-    after the first part and after every segment boundary."""
+@pytest.mark.parametrize("variant,fixup,win_len", [("slow", None, CH), ("none", None, 16), ("slow", 0, CH)])
+def test_full_h32_t64k_split_boundaries(variant, fixup, win_len, kda_opts, capfd):
+    """B=1, H=32, T=65536, d=128, bf16, through the default sequence-split
+    launch (the head walk of every later segment's map, the prefill from zero
+    of the segments whose map vanished beside the 12-wave segment pass over the
+    others, merge, the corrected heads or whole segments) and through the
+    other pipeline (fixup = 0: direct first part beside the segment pass over
+    G - 1 segments, merge, prefill of G segments).  With slow-decay gates no map
+    vanishes; with the workloads' gates every map does within the corrected
+    head, and the start states then matter for the first tokens of each
+    segment only, which the short windows isolate.  Sampled heads are compared
+    with the oracle over the whole sequence, and on the window right after the
+    first part and after every segment boundary."""
+    kda_opts("fixup", fixup)
     B, H, T, D = 1, 32, 65536, 128
     T0, G, Tseg = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
-    print(f"[case] h32_t64k slow, plan T0={T0} G={G} Tseg={Tseg}", flush=True)
-    assert G > 1 and T0 > 0
-    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=2, device=dev(), variant="slow")
+    print(f"[case] h32_t64k {variant} fixup={fixup}, plan T0={T0} G={G} Tseg={Tseg}", flush=True)
+    assert G > 1 and (T0 > 0) == (fixup == 0)
+    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=2, device=dev(), variant=variant)
     kda_opts("log", 1)
     o, S_T = kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None)
     torch.cuda.synchronize()
@@ -70,7 +78,7 @@ def test_full_h32_t64k_slow_split_boundaries(kda_opts, capfd):
         oh = o[0, h].cpu().double().numpy()
         eo = oracle.rel_l2(oh, o_ref[0, 0])
         es = oracle.rel_l2(S_T[0, h].cpu(), S_ref[0, 0])
-        win = window_errors(oh, o_ref[0, 0], [0] + bounds)
+        win = window_errors(oh, o_ref[0, 0], sorted(set([0] + bounds)), win_len)
         print(f"    head {h}: o {eo:.3e}  S_T {es:.3e}  boundary windows "
               + " ".join(f"{s}:{e:.2e}" for s, e in win.items()), flush=True)
         worst[h] = max(eo, es, *win.values())
