@@ -54,11 +54,15 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "ac771db01840b17b",
-    "direct_part": 0.1855e9 + 0.0482e9,
-    "segment_transfer": 1.3029e9 + 0.0294e9,
-    "segment_merge": 0.0316e9 + 0.0168e9,
-    "segment_prefill": 1.9841e9 + 0.4928e9,
+    "sources_sha": "4721b2af7231beed",
+    # the kernels of one kda_chunk_prefill call at h32_t64k: the two segment-pass
+    # launches (the head walk, and the pass over segments whose map did not
+    # vanish, whose workgroups all exit here), the prefill of every segment from
+    # zero, the merge, the corrected heads
+    "segment_pass_launches": 0.03354e9,
+    "zero_start_segments": 2.15273e9 + 0.55367e9,
+    "segment_merge": 0.00219e9 + 0.00210e9,
+    "corrected_heads": 0.07419e9 + 0.01468e9,
     "decode_step": 0.5455e9 + 0.5390e9,
     # the backward's three kernels at B=4, H=32, T=8192, d=128: forward
     # checkpoint pass, reverse chain, per-chunk gradients
@@ -233,6 +237,13 @@ def bench_decomposition_heads(pf, args, G, Tseg):
     Ztot = torch.randn(G - 1, B, H, D, D, device=dev)
     Mtot = torch.randn(G - 1, B, H, D, D, device=dev) * 0.01
     S1 = torch.randn(B, H, D, D, device=dev)
+
+    def corrected():
+        # the call's launch shape for this piece: 4 consumer waves, one workgroup per segment
+        with kda.options(nc=4):
+            kda.prefill_segments(heads["q"], heads["k"], heads["v"], heads["log_alpha"], heads["beta"], S_start,
+                                 Lh, o=o_heads, S_T=S_T2)
+
     parts = {
         "head_walk": (lambda: kda.segment_transfer(heads["k"], heads["v"], heads["log_alpha"], heads["beta"],
                                                    G - 1, S_zero_end=Zh, M=Mh),
@@ -242,9 +253,7 @@ def bench_decomposition_heads(pf, args, G, Tseg):
                                 zero_start_bytes(B, H, T, D, G)),
         "segment_merge": (lambda: kda.segment_merge(Ztot, Mtot, S1, S_start=S_start, S_T=S_T2),
                           merge_bytes(B, H, D, G - 1)),
-        "corrected_heads": (lambda: kda.prefill_segments(heads["q"], heads["k"], heads["v"], heads["log_alpha"],
-                                                         heads["beta"], S_start, Lh, o=o_heads, S_T=S_T2),
-                            segment_prefill_bytes(B, H, (G - 1) * Lh, D, G - 1)),
+        "corrected_heads": (corrected, segment_prefill_bytes(B, H, (G - 1) * Lh, D, G - 1)),
     }
     for fn, _ in parts.values():
         fn()
@@ -626,7 +635,9 @@ def summarize_profiles(paths):
     """Summaries of rocprofv3 CSV output (no GPU needed): the `--stats` table
     (`*_kernel_stats.csv`) per kernel name; a kernel trace
     (`*_kernel_trace.csv`) grouped by kernel name and grid size, with dispatch
-    count and mean / median / min / max duration in microseconds; a counter
+    count and mean / median / quartiles / min / max duration in microseconds
+    (the quartiles separate two launches of one shape that take different
+    times, such as the split prefill's two segment-pass launches); a counter
     collection (`*_counter_collection.csv`) grouped the same way, each counter
     summed over its dimensions per dispatch, then averaged over dispatches."""
     import collections
@@ -665,9 +676,10 @@ def summarize_profiles(paths):
                              r.get("Arch_VGPR_Count", r.get("VGPR_Count", "")))
             for key, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
                 wg, lds, scr, vgpr = meta[key]
+                q1, _, q3 = statistics.quantiles(ds, n=4) if len(ds) > 1 else (ds[0], ds[0], ds[0])
                 print(f"  {key[0]} | grid {key[1]} wg {wg} lds {lds} scratch {scr} vgpr column {vgpr} | n={len(ds)} "
                       f"mean {statistics.mean(ds):.1f} us  median {statistics.median(ds):.1f}  "
-                      f"min {min(ds):.1f}  max {max(ds):.1f}")
+                      f"quartiles {q1:.1f} / {q3:.1f}  min {min(ds):.1f}  max {max(ds):.1f}")
 
 
 def main():
@@ -686,6 +698,9 @@ def main():
     ap.add_argument("--no-tokens", action="store_true", help="skip the several-token decode")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-calib", action="store_true", help="skip the GEMM and copy reference rates")
+    ap.add_argument("--no-decomp", action="store_true",
+                    help="skip timing the split prefill's pieces through the public calls (the roofline "
+                         "then takes the whole call)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
@@ -721,7 +736,7 @@ def main():
     gbs = nbytes / (ms * 1e-3) / 1e9
     fl_dense = prefill_flops(B, H, T, D)
     fl_tri = prefill_flops(B, H, T, D, triangle=True)
-    dec = bench_decomposition(pf, args)
+    dec = None if args.no_decomp else bench_decomposition(pf, args)
     if dec is not None and dec["T0"] == 0:
         names = ("head_walk", "zero_start_segments", "segment_merge", "corrected_heads")
         kern = {"head_walk": "kda_chunk_kernel<bf16,128,8,segment> (first chunks of segments 1..G-1)",
@@ -737,9 +752,12 @@ def main():
     if dec is not None:
         dom = max(names, key=lambda n: dec[n]["ms"])
         r = dec[dom]
-        traffic = TRAFFIC.get(dom) if kernel_sources_sha() == TRAFFIC["sources_sha"] else None
         counters_valid = kernel_sources_sha() == TRAFFIC["sources_sha"]
-        path_counter = sum(TRAFFIC.get(n, 0.0) for n in TRAFFIC_PATH) if counters_valid else None
+        traffic = TRAFFIC.get(dom) if counters_valid else None
+        # counters are kept for the default pipeline's kernels only
+        path_names = TRAFFIC_PATH if dec["T0"] == 0 else names
+        path_counter = (sum(TRAFFIC[n] for n in path_names)
+                        if counters_valid and all(n in TRAFFIC for n in path_names) else None)
         roofline = {"bound": "hbm", "achieved": r["GBs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": r["GBs"] / PEAK_HBM_GBS, "traffic": traffic, "kernel": kern[dom],
                     "kernel_ms": r["ms"], "algorithmic_bytes": r["algorithmic_bytes"],

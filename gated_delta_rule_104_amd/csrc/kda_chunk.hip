@@ -1304,6 +1304,9 @@ struct ChunkKernel {
           break;
         default: break;
       }
+      // a walk cut short reads nothing past its chunks (the prefetch of the
+      // chunks after them then reads zeros without touching memory)
+      Tlen = min(Tlen, nch * CH);
     }
     snap_head = nullptr;
     if (PREFILL && a.snap) {

@@ -84,18 +84,27 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * Any T >= 0 is accepted (a last partial chunk is masked); T == 0 copies S0
  * (or zeros) to S_T.
  *
- * With few heads and a long sequence, the call can cut every sequence and
- * apply the context-parallel decomposition of the same section ("针对适配的
- * Infra", KDA context parallelism) on this GPU.  The first T0 tokens are
- * prefilled directly from S0 while, beside them, the segment pass computes the
- * zero-start states and transfer maps of the next G - 1 segments; a sequential
- * merge then gives the start states of the G segments after the first part,
- * and each of them runs its own prefill (kda_prefill_plan reports T0, G and
- * the segment length).  That path needs kda_prefill_workspace_bytes() of
- * workspace (fp32 states, 3G - 1 per head); with a smaller or NULL workspace
- * the call runs the single-pass path instead.  The workspace is only used by
- * work enqueued by this call; calls on one stream may share it.
- * The side-by-side part runs on a second stream of the library's own, one per
+ * With few heads and a long sequence, the call can cut every sequence into G
+ * segments and apply the context-parallel decomposition of the same section
+ * ("针对适配的 Infra", KDA context parallelism) on this GPU (kda_prefill_plan
+ * reports the cut).  By default every segment is prefilled at once, segment 0
+ * from S0 and the others from zero, outputs included.  A short walk over the
+ * first chunks of every later segment's transfer map decides, on the device,
+ * whether the map is exactly zero there (it then stays zero).  If so, the
+ * segment's outputs past those chunks and its end state are already the true
+ * ones up to rounding, and only those first chunks are prefilled again from
+ * the segment's true start state (from a merge of the segments' end states
+ * and maps).  If not, the segment takes the longer way: its zero-start state
+ * and map from the segment pass, then its whole prefill again from its start
+ * state.  Option "fixup" 0 selects the earlier pipeline instead: the first T0
+ * tokens prefilled directly beside the segment pass over the G - 1 segments
+ * after them, the merge, then the prefill of those G segments.
+ * The split path needs kda_prefill_workspace_bytes() of workspace (fp32
+ * states, 3G - 2 per head, and G - 1 small segment records; 3G - 1 states
+ * with fixup 0); with a smaller or NULL workspace the call runs the
+ * single-pass path instead.  The workspace is only used by work enqueued by
+ * this call; calls on one stream may share it.
+ * The segment pass runs on a second stream of the library's own, one per
  * (device, caller stream) pair (created at the first split call on that stream,
  * default priority), forked from and joined back to `stream` with events, so
  * all of the call's work is ordered after earlier work on `stream` and before
@@ -157,9 +166,10 @@ kda_status kda_chunk_prefill_snap(const void* q, const void* k, const void* v, c
  * The cut kda_chunk_prefill would use for this shape when given
  * kda_prefill_workspace_bytes() of workspace: a first part of *T0 tokens
  * prefilled directly, then *G segments of *Tseg tokens (the last one possibly
- * shorter, ending at T).  *T0 == 0 and *G == 1 (*Tseg == T) mean the
- * single-pass path.  T0 and Tseg are multiples of 64 on the split path.
- * Writes nothing else and launches nothing.
+ * shorter, ending at T).  *G == 1 (*T0 == 0, *Tseg == T) means the
+ * single-pass path.  With the default pipeline *T0 is 0 and segment 0 starts
+ * from S0; with option "fixup" 0, *T0 > 0.  T0 and Tseg are multiples of 64
+ * on the split path.  Writes nothing else and launches nothing.
  */
 kda_status kda_prefill_plan(int B, int H, int T, int dk, int dv, kda_dtype dtype, int* T0, int* G,
                             int* Tseg);
@@ -294,10 +304,19 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
  * call that needs the options; kda_set_option changes one for every later call
  * (thread-safe; calls already enqueued are not affected).  value -1 restores the
  * library's default.  Names:
- *   "split"            segments after the first part of the sequence-split
- *                      prefill (0 = never split, >= 2 = that many; default:
- *                      chosen from the shape and the compute-unit count)
- *   "transfer_cost16"  that path's first-part length ratio, in 16ths (1..64)
+ *   "split"            segments of the sequence-split prefill (after the first
+ *                      part with fixup 0; 0 = never split, >= 2 = that many;
+ *                      default: chosen from the shape and the compute-unit
+ *                      count)
+ *   "fixup"            0: the split prefill's earlier pipeline (first part
+ *                      beside the segment pass, merge, prefill of every
+ *                      segment); default 1 (segments from zero, heads
+ *                      corrected)
+ *   "head_chunks"      chunks of every segment's map walked before deciding
+ *                      whether it has vanished, and prefilled again when it
+ *                      has (1..1024; default 4)
+ *   "transfer_cost16"  with fixup 0: the first part's length ratio, in 16ths
+ *                      (1..64)
  *   "map_skip"         0: the segment pass keeps updating transfer-map columns
  *                      that have become exactly zero (same results bit for bit
  *                      for finite inputs); default 1
