@@ -31,6 +31,15 @@ def build(out: str = LIB, verbose: bool = False, extra=()) -> str:
     return out
 
 
+def build_stamps(verbose: bool = False) -> str:
+    """The profiling variant, with the chunk kernel's phase timestamps
+    (kda_debug_phase_stamps), as libkda_stamps.so beside libkda.so."""
+    return build(os.path.join(HERE, "libkda_stamps.so"), verbose, extra=("-DKDA_PHASE_STAMPS",))
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--stamps" in sys.argv[1:]:
+        print(build_stamps(verbose=True))
+    else:
+        print(build(verbose=True))
     sys.exit(0)

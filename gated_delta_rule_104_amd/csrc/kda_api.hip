@@ -350,6 +350,10 @@ struct Snap {
   int H = 1;
 };
 
+// Phase timestamps of the profiling build (kda_debug_phase_stamps).
+std::atomic<unsigned long long*> g_stamps{nullptr};
+std::atomic<size_t> g_stamps_n{0};
+
 // Per-segment control of a prefill launch in the split path with corrected
 // heads (ChunkArgs::seg_flag and the fields after it).
 struct SegCtl {
@@ -389,6 +393,10 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
   a.ck_rows = ck_rows; a.ck_w = ck_w; a.ck_d = ck_d; a.ck_a = ck_a;
   a.seg_flag = sc.rec; a.flag_mode = sc.mode; a.flag_g0 = sc.g0; a.head_chunks = sc.head;
   a.Z_out = sc.Z_out; a.s0_first = sc.s0_first ? 1 : 0; a.Z_prev = sc.Z_prev;
+  if (sc.mode == kda::FLAG_FAST_ONLY) {  // the split prefill's main launch
+    a.stamps = g_stamps.load(std::memory_order_relaxed);
+    a.stamps_n = g_stamps_n.load(std::memory_order_relaxed);
+  }
   const long long nwg = nseq * a.vsplit;
   if (nwg > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
   if (log_on())
@@ -467,6 +475,19 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";
+}
+
+kda_status kda_debug_phase_stamps(unsigned long long* stamps, size_t count) {
+#ifdef KDA_PHASE_STAMPS
+  if (!stamps) count = 0;
+  g_stamps.store(count ? stamps : nullptr, std::memory_order_relaxed);
+  g_stamps_n.store(count, std::memory_order_relaxed);
+  return ok();
+#else
+  (void)stamps;
+  (void)count;
+  return fail(KDA_ERR_UNSUPPORTED, "phase timestamps need the profiling build (KDA_PHASE_STAMPS)");
+#endif
 }
 
 size_t kda_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtype dtype) {

@@ -1207,11 +1207,16 @@ struct ChunkKernel {
   // tiles and their barrier are skipped, by every wave alike.
   template <int PD>
   __device__ __forceinline__ void producer_step(ProdRaw<T>& r, int it) {
+    stamp(it, 0);
     p1(r, stage(it), it + PD);
+    stamp(it, 1);
     sync_lds();
+    stamp(it, 2);
     if (C::LAG && it == nch) return;
     p2(stage(it), it);
+    stamp(it, 3);
     sync_lds();
+    stamp(it, 4);
     if (!C::LAG) sync_lds();
   }
 
@@ -1219,6 +1224,23 @@ struct ChunkKernel {
   // loop unrolled by two with the odd step peeled off, so that the loop's back
   // edge always follows both steps), except in the ONESET variants, which keep
   // one set and prefetch one chunk ahead.
+#ifdef KDA_PHASE_STAMPS
+  // Profiling build only: per-wave timestamps (s_memtime, shader-clock cycles)
+  // at the phase boundaries of pipeline steps kStampFirst .. +kStampSteps - 1:
+  // the step's start, the end of the elementwise phase (producers) or of the
+  // chain (consumers), after the first barrier, the end of the score tiles,
+  // after the second barrier; [workgroup][step][wave][5].
+  unsigned long long* stp = nullptr;
+  __device__ __forceinline__ void stamp(int it, int k) const {
+    const int c = it - kStampFirst;
+    if (!stp || c < 0 || c >= kStampSteps) return;
+    const unsigned long long t = __builtin_amdgcn_s_memtime();
+    if (l == 0) stp[((size_t)c * kStampWaves + wave) * 5 + k] = t;
+  }
+#else
+  __device__ __forceinline__ void stamp(int, int) const {}
+#endif
+
   __device__ __forceinline__ void producer_loop() {
     init_offsets();
     init_p1_offsets();
@@ -1246,11 +1268,16 @@ struct ChunkKernel {
     if (nch > 0) load_v(vr, 0);
     for (int it = 0; it < nch + C::LAG; ++it) {
       const int cc = it - C::LAG;
+      stamp(it, 0);
       if (C::LAG && cc >= 0) chain_step(vr, cc);
+      stamp(it, 1);
       sync_lds();
+      stamp(it, 2);
       if (C::LAG && it == nch) break;  // the chunk past the end: no score tiles
       p2(stage(it), it);
+      stamp(it, 3);
       sync_lds();
+      stamp(it, 4);
       if (!C::LAG) {
         chain_step(vr, cc);
         sync_lds();
@@ -1315,6 +1342,12 @@ struct ChunkKernel {
     }
     wave = threadIdx.x >> 6;
     l = lane_id();
+#ifdef KDA_PHASE_STAMPS
+    if constexpr (PREFILL && !BWD && !CKPT && NC + D / 32 <= kStampWaves) {
+      const size_t per = (size_t)kStampSteps * kStampWaves * 5;
+      if (a.stamps && (size_t)(blockIdx.x + 1) * per <= a.stamps_n) stp = a.stamps + blockIdx.x * per;
+    }
+#endif
     const int g4 = 4 * (l >> 4);
     const uint32_t rowbytes = (uint32_t)Tlen * D * C::ES;
     const size_t base = tok0 * D * C::ES;

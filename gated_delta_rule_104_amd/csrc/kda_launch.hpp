@@ -73,7 +73,17 @@ struct ChunkArgs {
   // (the first one's: from the true start) [G*BH, D, D]; a sequence whose
   // previous segment's map vanished starts from it instead of S0
   const float* Z_prev = nullptr;
+  // profiling build (KDA_PHASE_STAMPS) only: phase timestamps of every
+  // workgroup of this launch, stamps_n entries (see the chunk kernel)
+  unsigned long long* stamps = nullptr;
+  size_t stamps_n = 0;
 };
+
+// Phase timestamps of the profiling build: pipeline steps and waves recorded
+// per workgroup.
+constexpr int kStampFirst = 32;
+constexpr int kStampSteps = 16;
+constexpr int kStampWaves = 8;
 
 // Words per segment record (one per consumer wave of the segment pass, up to
 // D/16 of them).

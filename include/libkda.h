@@ -333,6 +333,22 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
 kda_status kda_set_option(const char* name, long long value);
 kda_status kda_get_option(const char* name, long long* value);
 
+/*
+ * Profiling only.  In a library built with KDA_PHASE_STAMPS (build.py
+ * --stamps, libkda_stamps.so), every later sequence-split prefill records,
+ * for each workgroup of its main launch (the prefill of every segment from
+ * zero), the shader clock (s_memtime) of every wave at five points of
+ * pipeline steps 32 .. 47: the step's start, the end of the elementwise phase
+ * (producer waves) or of the chain (consumer waves), after the first barrier,
+ * the end of the score tiles, after the second barrier.
+ *   stamps : device buffer of count 64-bit entries, indexed
+ *            [workgroup][step - 32][wave][point] with 8 wave slots; a
+ *            workgroup whose entries do not fit records nothing; NULL (or
+ *            count 0) stops recording
+ * The regular library returns KDA_ERR_UNSUPPORTED and records nothing.
+ */
+kda_status kda_debug_phase_stamps(unsigned long long* stamps, size_t count);
+
 const char* kda_status_string(kda_status status);
 const char* kda_last_error(void);
 int kda_abi_version(void);
