@@ -201,7 +201,10 @@ PrefillPlan plan_prefill(long long BH, int T, int D, kda_dtype dt) {
   } else {
     // worth it when one pass cannot fill the chip without 4+ workgroups per head
     if (BH * ntiles / 4 >= cus || T < 4096) return pl;
-    G = (cus + BH - 1) / BH;  // one round of segment prefills
+    // one round of segment prefills: with G * BH above the CU count the last
+    // workgroups would walk a whole segment again on their own (at 48 heads,
+    // 6 segments took 1.36 ms against 0.95 ms for 5)
+    G = cus / BH;
     if (G > T / 1024) G = T / 1024;
     if (G < 2) return pl;
   }
