@@ -523,10 +523,10 @@ kda_status kda_prefill_plan(int B, int H, int T, int dk, int dv, kda_dtype dtype
 namespace {
 
 // Scratch of the no-allocation prefill entry point: the sequence-split path's
-// states (Z, M, the first part's end state, the segments' start states) when
-// the caller cannot pass a workspace.  Every default plan on a 256-CU device
-// fits (at most 63.5 MiB, for 127 heads of d = 128); each device the library
-// runs on holds its own copy until the process ends.
+// states and segment records when the caller cannot pass a workspace.  Every
+// default plan on a 256-CU device fits (at most 48 MiB: one head of d = 128
+// cut into 256 segments); each device the library runs on holds its own copy
+// until the process ends.
 constexpr size_t kScratchBytes = (size_t)64 << 20;
 __device__ __align__(256) char scratch[kScratchBytes];
 
