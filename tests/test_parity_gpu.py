@@ -714,10 +714,12 @@ def test_full_decode_tokens_n256_h32():
     assert worst <= TOL["bf16"]
 
 
-def test_prefill_snapshots_split_batched(kda_opts):
+@pytest.mark.parametrize("T,variant", [(1500, "slow"), (3000, "none")])
+def test_prefill_snapshots_split_batched(T, variant, kda_opts):
     """Snapshots on the sequence-split path with several sequences: each
-    sequence's snapshots land at [b, j, h] whichever segment writes them."""
-    es = run_snap_case(2, 3, 1500, 128, "bf16", 256, seed=540, split=3, kda_opts=kda_opts)
+    sequence's snapshots land at [b, j, h] whichever segment (or corrected
+    head) writes them."""
+    es = run_snap_case(2, 3, T, 128, "bf16", 256, seed=540, variant=variant, split=3, kda_opts=kda_opts)
     assert es <= TOL["bf16"]
 
 
