@@ -567,7 +567,9 @@ def bench_kcp(args, dev):
     segments of 131,072 tokens (H = 32): the segment pass (each segment's
     zero-start end state and transfer map), the sequential merge (every
     segment's true start state), and the prefill of every segment from its start
-    state, which produces the outputs."""
+    state, which produces the outputs.  Beside them, kda_chunk_prefill on the
+    same sequence (its plan cuts the same 8 segments; it prefills them from
+    zero and corrects their heads)."""
     B, H, G, Tseg, D = 1, 32, 8, 131072, 128
     T = G * Tseg
     print(f"[bench] generating kcp inputs H={H} T={T} G={G}", file=sys.stderr, flush=True)
@@ -588,20 +590,28 @@ def bench_kcp(args, dev):
     def prefill():
         kda.prefill_segments(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], S_start, Tseg, o=o, S_T=S_T2)
 
-    transfer(); merge(); prefill()
+    ws = torch.empty(kda.prefill_workspace_bytes(B, H, T, D, D, torch.bfloat16), dtype=torch.uint8, device=dev)
+
+    def call():
+        kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None, o=o, S_T=S_T2, workspace=ws)
+
+    transfer(); merge(); prefill(); call()
     torch.cuda.synchronize()
     t_ms, _ = time_launches(transfer, MIN_TIMED)
     m_ms, _ = time_launches(merge, MIN_TIMED)
     p_ms, _ = time_launches(prefill, MIN_TIMED)
+    c_ms, _ = time_launches(call, MIN_TIMED)
+    plan = list(kda.prefill_plan(B, H, T, D, D, torch.bfloat16))
     nbytes = B * H * T * (2 * (2 * D + D) + 2) + 2 * G * B * H * D * D * 4
     pbytes = segment_prefill_bytes(B, H, T, D, G)
-    del g, o
+    del g, o, ws
     return dict(H=H, T=T, G=G, Tseg=Tseg, transfer_ms=t_ms, merge_ms=m_ms,
                 tokens_per_s=T / ((t_ms + m_ms) * 1e-3),
                 transfer_GBs=nbytes / (t_ms * 1e-3) / 1e9,
                 segment_prefill_ms=p_ms, segment_prefill_GBs=pbytes / (p_ms * 1e-3) / 1e9,
                 with_outputs_ms=t_ms + m_ms + p_ms,
-                with_outputs_tokens_per_s=T / ((t_ms + m_ms + p_ms) * 1e-3))
+                with_outputs_tokens_per_s=T / ((t_ms + m_ms + p_ms) * 1e-3),
+                prefill_call_ms=c_ms, prefill_call_plan=plan, prefill_call_tokens_per_s=T / (c_ms * 1e-3))
 
 
 def bench_calibration(dev):
