@@ -461,10 +461,14 @@ struct ChunkKernel {
   // Phase-2 tasks: the four diagonal L blocks (with their inverses, about twice
   // the work of a tile) first, then the P tiles (prefill only), then the
   // off-diagonal L tiles.  Each task goes to the wave with the least work so far
-  // (greedy, at compile time), every wave of the workgroup taking part.
+  // (greedy, at compile time), every wave of the workgroup taking part.  When
+  // the consumers compute the previous chunk's outputs in this interval
+  // (DEFER_O), each consumer wave starts with that step's weight.
   static constexpr int NT2 = QP ? 20 : 10;
   static constexpr int task_wave(int K) {
     int load[C::NW] = {};
+    if (DEFER_O)
+      for (int i = 0; i < NC; ++i) load[i] = kOutWeight;
     int w = 0;
     for (int k = 0; k <= K; ++k) {
       w = 0;
@@ -689,6 +693,19 @@ struct ChunkKernel {
   // three-waves-per-SIMD variant, and fp32 at D = 128, whose 8-byte-per-element
   // rows make two sets too large for 256 registers.
   static constexpr bool ONESET = TIGHT || (!C::BF && D > 64);
+  // The outputs O = Qh S + P Delta feed nothing later in the chain, so with a
+  // double-buffered stage (bf16 prefill) the consumers compute chunk n's in the
+  // second interval, beside chunk n+1's score tiles, instead of in the first,
+  // whose length the chain sets; their score-tile share shrinks to match.  The
+  // bf16 copies of S (sb) and Delta (db) stay live across the barrier.
+  static constexpr bool DEFER_O = QP && !BWD && C::LAG && C::BF;
+  // Weight of the outputs of one chunk in score-tile units (a tile is one unit,
+  // a diagonal block with its inverse two) when handing out the score tiles.
+  // Per-wave timestamps put the outputs at about 2.1K cycles against about
+  // 0.55K per unit, but measured over weights 0 to 8 the call is fastest at 1
+  // or 2 (h32_t64k 0.617-0.622 ms against 0.628-0.639 for 3 and for outputs
+  // computed in the first interval; 6 and 8 were slower still).
+  static constexpr int kOutWeight = 2;
   static constexpr int C1B = 2;                    // row tiles per batch in c1
   static constexpr int C3B = TIGHT ? 2 : D / 32;   // state row tiles per batch in c3
 
@@ -1003,7 +1020,7 @@ struct ChunkKernel {
     }
     c1(X, stage(cc));
     if constexpr (TIGHT) load_v(vr, cc + 1);
-    c2(stage(cc), cc);
+    if constexpr (!DEFER_O) c2(stage(cc), cc);
     c3(stage(cc));
     snapshot(cc);
   }
@@ -1273,8 +1290,16 @@ struct ChunkKernel {
       stamp(it, 1);
       sync_lds();
       stamp(it, 2);
-      if (C::LAG && it == nch) break;  // the chunk past the end: no score tiles
+      if (C::LAG && it == nch) {  // the chunk past the end: no score tiles
+        if constexpr (DEFER_O) {
+          if (cc >= 0) c2(stage(cc), cc);
+        }
+        break;
+      }
       p2(stage(it), it);
+      if constexpr (DEFER_O) {
+        if (cc >= 0) c2(stage(cc), cc);
+      }
       stamp(it, 3);
       sync_lds();
       stamp(it, 4);
