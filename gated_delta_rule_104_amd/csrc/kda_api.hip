@@ -44,7 +44,7 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0
 // environment variable, read once; -1 means the library's default.
 enum Opt {
   OPT_SPLIT, OPT_COST16, OPT_MAP_SKIP, OPT_NC, OPT_BW_SPLIT, OPT_CHECK, OPT_LOG, OPT_FIXUP, OPT_HEAD,
-  OPT_COUNT
+  OPT_BW_OVERLAP, OPT_COUNT
 };
 struct OptDesc {
   const char* name;
@@ -54,7 +54,7 @@ const OptDesc kOpts[OPT_COUNT] = {{"split", "KDA_SPLIT"},       {"transfer_cost1
                                   {"map_skip", "KDA_MAP_SKIP"}, {"nc", "KDA_NC"},
                                   {"bw_split", "KDA_BW_SPLIT"}, {"check", "KDA_CHECK"},
                                   {"log", "KDA_LOG"},           {"fixup", "KDA_FIXUP"},
-                                  {"head_chunks", "KDA_HEAD_CHUNKS"}};
+                                  {"head_chunks", "KDA_HEAD_CHUNKS"}, {"bw_overlap", "KDA_BW_OVERLAP"}};
 std::atomic<long long> g_opt[OPT_COUNT];
 std::once_flag g_opt_once;
 
@@ -66,7 +66,7 @@ bool opt_valid(int o, long long v) {
     case OPT_NC: return v == 1 || v == 2 || v == 4 || v == 8;
     case OPT_BW_SPLIT: return v == 1 || v == 2;
     case OPT_HEAD: return v >= 1 && v <= 1024;
-    default: return v == 0 || v == 1;  // map_skip, check, log, fixup
+    default: return v == 0 || v == 1;  // map_skip, check, log, fixup, bw_overlap
   }
 }
 
@@ -263,6 +263,7 @@ struct SideStream {
   hipStream_t owner = nullptr;  // the caller stream this slot serves
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t mid = nullptr, mid2 = nullptr;  // two more cross-stream points (the chunked backward)
   std::mutex mu;
 };
 constexpr int kSideSlots = 64;
@@ -289,7 +290,9 @@ kda_status side_stream(hipStream_t caller, SideStream** out) {
       ss->owner = caller;
       if ((e = hipStreamCreateWithFlags(&ss->s, hipStreamNonBlocking)) != hipSuccess ||
           (e = hipEventCreateWithFlags(&ss->fork, hipEventDisableTiming)) != hipSuccess ||
-          (e = hipEventCreateWithFlags(&ss->join, hipEventDisableTiming)) != hipSuccess) {
+          (e = hipEventCreateWithFlags(&ss->join, hipEventDisableTiming)) != hipSuccess ||
+          (e = hipEventCreateWithFlags(&ss->mid, hipEventDisableTiming)) != hipSuccess ||
+          (e = hipEventCreateWithFlags(&ss->mid2, hipEventDisableTiming)) != hipSuccess) {
         delete ss;  // (a partly created stream or event is left to process exit)
         return hip_fail(e, "creating the side stream");
       }
@@ -759,6 +762,15 @@ size_t chunk_bw_ws_floats(long long BH, int T, int D) {
 //     needs no forward state).  For the rows with beta below kTinyBeta only,
 //     they also keep W = V - Kh S, the row of strict_lower(Kh Kb^T) and Xbar;
 //  2. the per-chunk gradients, two workgroups (column halves) per (head, chunk).
+// With the overlap (option bw_overlap, on by default from kBwOverlapChunks
+// chunks per head) the reverse chain runs as two launches, the later half of
+// the chunks and then the earlier half (dS at the halves' boundary carried in
+// dS0, which each workgroup reads before it writes), and the later half's
+// gradients run on the side stream as soon as the forward pass and that half
+// of the reverse chain are done: on the CUs the forward pass leaves, beside the
+// earlier half of the reverse chain.  The earlier half's gradients follow it
+// on the caller's stream.
+constexpr long long kBwOverlapChunks = 16;
 kda_status chunk_backward(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                           const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
                           void* dlog_alpha, void* dbeta, float* dS0, int B, int H, int T, int D, float* ws,
@@ -785,30 +797,16 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
   const int ncb = pick_nc(2 * BH, nt, true);
   r.vsplit = nt / (ncb * kda::chunk_tiles_per_wave(true));
   if (BH * r.vsplit > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
+  const bool overlap = opt(OPT_BW_OVERLAP) != 0 && nch >= kBwOverlapChunks;
+  const int c1 = overlap ? (int)(nch / 2) : 0;  // first chunk of the later half
   if (log_on())
-    fprintf(stderr, "[libkda] backward BH=%lld T=%d D=%d: reverse chain nc=%d vsplit=%d, %lld x %lld chunk gradients\n",
-            BH, T, D, ncb, r.vsplit, BH, nch);
+    fprintf(stderr, "[libkda] backward BH=%lld T=%d D=%d: reverse chain nc=%d vsplit=%d, %lld x %lld chunk gradients%s\n",
+            BH, T, D, ncb, r.vsplit, BH, nch, overlap ? ", the later half's beside the earlier half's chain" : "");
   hipError_t e;
   if (T == 0) {  // dS0 = dS_T
     if ((e = kda::launch_chunk_bwd(r, D, ncb, (int)(BH * r.vsplit), stream)) != hipSuccess)
       return hip_fail(e, "kda_prefill_backward reverse chain");
     return ok();
-  }
-  SideStream* ss = nullptr;
-  kda_status st;
-  if ((st = side_stream(stream, &ss)) != KDA_OK) return st;
-  {
-    std::lock_guard<std::mutex> lk(ss->mu);
-    if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess || (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
-      return hip_fail(e, "kda_prefill_backward fork");
-    st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, nullptr, ST, BH, T, 0, T, T, D, true, ss->s,
-                                "kda_prefill_backward forward checkpoints", Snap(), ncb, S_rows, W, Dl, Ack);
-    if (st == KDA_OK && (e = kda::launch_chunk_bwd(r, D, ncb, (int)(BH * r.vsplit), stream)) != hipSuccess)
-      st = hip_fail(e, "kda_prefill_backward reverse chain");
-    // join even if a launch above failed, so the side stream's work is waited for
-    if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess || (e = hipStreamWaitEvent(stream, ss->join, 0)) != hipSuccess)
-      return hip_fail(e, "kda_prefill_backward join");
-    if (st != KDA_OK) return st;
   }
   kda::BwGradArgs g;
   g.q = q; g.k = k; g.la = log_alpha; g.beta = beta; g.dO = dO;
@@ -816,8 +814,53 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
   g.S_rows = S_rows; g.W = W; g.Dl = Dl; g.A = Ack; g.dU_rows = dU_rows; g.Xb = Xb;
   g.dq = static_cast<kda::bf16*>(dq); g.dk = static_cast<kda::bf16*>(dk_);
   g.dla = static_cast<kda::bf16*>(dlog_alpha); g.dbeta = static_cast<kda::bf16*>(dbeta); g.T = T;
-  if ((e = kda::launch_bwgrad(g, (int)BH, D, stream)) != hipSuccess) return hip_fail(e, "kda_prefill_backward gradients");
-  return ok();
+  SideStream* ss = nullptr;
+  kda_status st;
+  if ((st = side_stream(stream, &ss)) != KDA_OK) return st;
+  std::lock_guard<std::mutex> lk(ss->mu);
+  if ((e = hipEventRecord(ss->fork, stream)) != hipSuccess || (e = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess)
+    return hip_fail(e, "kda_prefill_backward fork");
+  st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, nullptr, ST, BH, T, 0, T, T, D, true, ss->s,
+                              "kda_prefill_backward forward checkpoints", Snap(), ncb, S_rows, W, Dl, Ack);
+  if (!overlap) {
+    if (st == KDA_OK && (e = kda::launch_chunk_bwd(r, D, ncb, (int)(BH * r.vsplit), stream)) != hipSuccess)
+      st = hip_fail(e, "kda_prefill_backward reverse chain");
+    // join even if a launch above failed, so the side stream's work is waited for
+    if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess || (e = hipStreamWaitEvent(stream, ss->join, 0)) != hipSuccess)
+      return hip_fail(e, "kda_prefill_backward join");
+    if (st != KDA_OK) return st;
+    if ((e = kda::launch_bwgrad(g, (int)BH, D, stream)) != hipSuccess)
+      return hip_fail(e, "kda_prefill_backward gradients");
+    return ok();
+  }
+  // the reverse chain's later half (the tokens from 64 c1 on), from dS_T into
+  // dS0, then its earlier half, from dS0 into dS0
+  kda::ChunkArgs rh = r, rl = r;
+  rh.t0 = 64 * c1; rh.Tseg = T - rh.t0;
+  rl.S0 = dS0; rl.Tseg = 64 * c1; rl.Tend = 64 * c1;
+  kda::BwGradArgs gh = g, gl = g;
+  gh.n0 = c1; gh.n1 = (int)nch;
+  gl.n0 = 0; gl.n1 = c1;
+  if (st == KDA_OK && (e = hipEventRecord(ss->mid, ss->s)) != hipSuccess) st = hip_fail(e, "kda_prefill_backward event");
+  if (st == KDA_OK && (e = kda::launch_chunk_bwd(rh, D, ncb, (int)(BH * r.vsplit), stream)) != hipSuccess)
+    st = hip_fail(e, "kda_prefill_backward reverse chain");
+  if (st == KDA_OK && (e = hipEventRecord(ss->mid2, stream)) != hipSuccess) st = hip_fail(e, "kda_prefill_backward event");
+  if (st == KDA_OK && (e = kda::launch_chunk_bwd(rl, D, ncb, (int)(BH * r.vsplit), stream)) != hipSuccess)
+    st = hip_fail(e, "kda_prefill_backward reverse chain");
+  // side stream, after the forward pass: the later half's gradients once that
+  // half of the reverse chain is done
+  if (st == KDA_OK && (e = hipStreamWaitEvent(ss->s, ss->mid2, 0)) != hipSuccess) st = hip_fail(e, "kda_prefill_backward wait");
+  if (st == KDA_OK && (e = kda::launch_bwgrad(gh, (int)BH, D, ss->s)) != hipSuccess)
+    st = hip_fail(e, "kda_prefill_backward gradients");
+  // caller's stream, after the earlier half of the chain: that half's
+  // gradients once the forward pass is done
+  if (st == KDA_OK && (e = hipStreamWaitEvent(stream, ss->mid, 0)) != hipSuccess) st = hip_fail(e, "kda_prefill_backward wait");
+  if (st == KDA_OK && (e = kda::launch_bwgrad(gl, (int)BH, D, stream)) != hipSuccess)
+    st = hip_fail(e, "kda_prefill_backward gradients");
+  // join even if a launch above failed, so the side stream's work is waited for
+  if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess || (e = hipStreamWaitEvent(stream, ss->join, 0)) != hipSuccess)
+    return hip_fail(e, "kda_prefill_backward join");
+  return st == KDA_OK ? ok() : st;
 }
 
 }  // namespace

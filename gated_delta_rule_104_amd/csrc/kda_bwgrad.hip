@@ -528,8 +528,9 @@ struct GradKernel {
     if ((nwg & 7) == 0) id = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
     half = id & 1;
     const int unit = id >> 1;
-    const int bh = unit / nch;
-    const int n = unit - bh * nch;
+    const int ncnt = (a.n1 < 0 ? nch : a.n1) - a.n0;  // chunks of each head in this launch
+    const int bh = unit / ncnt;
+    const int n = a.n0 + (unit - bh * ncnt);
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     l = lane_id();
     g4 = 4 * (l >> 4);
@@ -604,7 +605,9 @@ __global__ __launch_bounds__(GradCfg<D>::THREADS, 2) void kda_bwgrad_kernel(BwGr
 
 hipError_t launch_bwgrad(const BwGradArgs& a, int BH, int D, hipStream_t stream) {
   const long long nch = (a.T + GCH - 1) / GCH;
-  const long long nwg = 2LL * BH * nch;  // two workgroups (column halves) per (head, chunk)
+  const long long n1 = a.n1 < 0 ? nch : a.n1;
+  if (a.n0 < 0 || n1 > nch || a.n0 > n1) return hipErrorInvalidValue;
+  const long long nwg = 2LL * BH * (n1 - a.n0);  // two workgroups (column halves) per (head, chunk)
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   if (D == 128) {

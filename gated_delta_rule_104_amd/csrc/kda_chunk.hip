@@ -184,6 +184,7 @@ struct ChunkKernel {
   bf16* ck_w;        // this chunk's checkpoints of W = V - Kh S (rows with tiny beta
   bf16* ck_d;        // only) and Delta (prefill with gradient checkpoints), else null
   int chunk0;        // chunks of the head's sequence before this segment
+  size_t ck0;        // gradients' checkpoints: index of this segment's first chunk
   float* snap_head;  // snapshot 0 of this head (prefill with snapshots), else null
   int wave, l;
   // consumer: NCT adjacent 16-column tiles of the state, sharing every A fragment
@@ -415,7 +416,7 @@ struct ChunkKernel {
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (!DIAG || g4 + e < s0) ? acc[e] : 0.f;
-        const size_t o = (((size_t)bh_seq * nch + it) * 10 + I * (I + 1) / 2 + J) * 256 + ln * 4;
+        const size_t o = ((ck0 + it) * 10 + I * (I + 1) / 2 + J) * 256 + ln * 4;
         *reinterpret_cast<bf16x4*>(a.ck_a + o) = pack4(v);
       }
     }
@@ -1012,7 +1013,7 @@ struct ChunkKernel {
       // (stored from c1)
       ck_w = ck_d = nullptr;
       if (a.ck_rows) {
-        const size_t o = (size_t)bh_seq * nch + cc;
+        const size_t o = ck0 + cc;
         store_state_bf16(a.ck_rows + o * D * D, nullptr);
         ck_w = a.ck_w + o * CH * D;
         ck_d = a.ck_d + o * CH * D;
@@ -1064,7 +1065,7 @@ struct ChunkKernel {
 #pragma unroll
         for (int j = 0; j < NCT; ++j) S[j][ci] = S[j][ci] * gm;
       }
-      store_state_bf16(a.dU_rows + ((size_t)bh_seq * nch + chunk) * D * D, nullptr);
+      store_state_bf16(a.dU_rows + (ck0 + chunk) * D * D, nullptr);
 #pragma unroll
       for (int j = 0; j < NCT; ++j)
 #pragma unroll
@@ -1129,7 +1130,7 @@ struct ChunkKernel {
       // dtype), and Xbar itself for the rows with beta below kTinyBeta (the
       // per-chunk gradients recover every other row's from dv)
       {
-        bf16* xb = a.ck_xb + ((size_t)bh_seq * nch + chunk) * CH * D;
+        bf16* xb = a.ck_xb + (ck0 + chunk) * CH * D;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const f32x4 bet = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * t + kk));
@@ -1329,6 +1330,7 @@ struct ChunkKernel {
     Tlen = min(a.Tseg, a.Tend - seg0);
     nch = (Tlen + CH - 1) / CH;
     chunk0 = seg0 / CH;
+    ck0 = (size_t)bh * ((a.Ttot + CH - 1) / CH) + chunk0;
     // Segments with corrected heads: whether this one runs, and how far (the
     // decision is the same for every wave of the workgroup, taken before any
     // barrier).

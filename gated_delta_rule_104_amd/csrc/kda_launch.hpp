@@ -41,7 +41,9 @@ struct ChunkArgs {
   // exactly zero (they stay zero for finite inputs); 0 keeps updating them
   int map_skip = 1;
   // gradients' checkpoints, bf16 row-major matrices with the positions inside
-  // each 32-wide block of a row in the kpos order (null: none).  Prefill (bf16,
+  // each 32-wide block of a row in the kpos order (null: none), indexed by the
+  // chunk of the head's whole sequence (nch = ceil(Ttot / 64) per head; a
+  // launch may cover the chunks from t0 / 64 on).  Prefill (bf16,
   // one segment per head): the start state of every chunk [BH, nch, D, D] and
   // its Delta [BH, nch, CH, D]; for the rows (tokens) with beta < kTinyBeta
   // only, W = V - Kh S [BH, nch, CH, D] and the row's part of the strictly
@@ -188,6 +190,9 @@ struct BwGradArgs {
   bf16* dla;
   bf16* dbeta;         // [BH, T]
   int T;
+  // chunks [n0, n1) of every head (n1 < 0: to the last one)
+  int n0 = 0;
+  int n1 = -1;
 };
 hipError_t launch_bwgrad(const BwGradArgs& a, int BH, int D, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs& a, int BH, int D, int split, hipStream_t stream);

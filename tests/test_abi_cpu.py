@@ -301,7 +301,8 @@ def test_options(lib, kda_opts):
     for name, good, bad in ((b"split", (0, 2, 64), (1, -2)), (b"transfer_cost16", (1, 64), (0, 65)),
                             (b"map_skip", (0, 1), (2,)), (b"nc", (1, 2, 4, 8), (3, 16)),
                             (b"bw_split", (1, 2), (3,)), (b"check", (0, 1), (2,)), (b"log", (0, 1), (5,)),
-                            (b"fixup", (0, 1), (2,)), (b"head_chunks", (1, 4, 1024), (0, 1025))):
+                            (b"fixup", (0, 1), (2,)), (b"head_chunks", (1, 4, 1024), (0, 1025)),
+                            (b"bw_overlap", (0, 1), (2,))):
         kda_opts(name.decode(), None)
         assert get(name) == -1
         for x in good:

@@ -202,6 +202,35 @@ def test_backward_chunked_one_loss_term(with_dO, with_dST):
     assert max(err.values()) <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("T,D,tiny", [(1024, 128, False), (4100, 128, True), (2000, 64, False)])
+def test_backward_chunked_overlap_bitwise(T, D, tiny, kda_opts):
+    """From 16 chunks per head the reverse chain runs as two launches (the
+    later half of the chunks, then the earlier half, dS carried in fp32) and
+    the later half's per-chunk gradients beside the earlier half's chain:
+    every output equals, bit for bit, the one of the chain run whole followed
+    by every chunk's gradients (option bw_overlap 0).  Ragged last chunk, both
+    head sizes, and tokens with tiny beta (their rows of W, Xbar and Kh Kb^T
+    are indexed by the chunk of the whole sequence)."""
+    B, H = 1, 3
+    print(f"[case] backward overlap B={B} H={H} T={T} D={D} tiny={tiny}", flush=True)
+    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=360 + T, s0_std=0.1, variant="slow", device=dev())
+    if tiny:
+        t = torch.arange(T, device=dev())
+        g["beta"][..., t % 7 == 3] = 0.0
+        g["beta"][..., t % 11 == 5] = 1e-12
+    gen = torch.Generator(device=dev()).manual_seed(361 + T)
+    dO = torch.randn(B, H, T, D, generator=gen, device=dev()).to(torch.bfloat16)
+    dST = torch.randn(B, H, D, D, generator=gen, device=dev())
+    out = {}
+    for ov in (0, 1):
+        kda_opts("bw_overlap", ov)
+        out[ov] = kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], dO, dST)
+        torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.isfinite(out[1][n]).all(), n
+        assert torch.equal(out[0][n], out[1][n]), n
+
+
 def test_backward_chunked_single_long_head():
     """One head over 4100 tokens (65 chunks, the last one ragged): one
     workgroup per chain beside 130 gradient workgroups."""
