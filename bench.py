@@ -64,9 +64,9 @@ TRAFFIC = {
     "segment_merge": 0.00219e9 + 0.00210e9,
     "corrected_heads": 0.07422e9 + 0.01468e9,
     "decode_step": 0.5455e9 + 0.5390e9,
-    # the backward's kernels at B=4, H=32, T=8192, d=128: forward checkpoint
-    # pass, the reverse chain's two halves, the per-chunk gradients' two halves
-    "backward": (0.8164e9 + 0.8137e9) + (1.0939e9 + 0.8221e9) + (2.6870e9 + 0.8075e9),
+    # the backward's three kernels at B=4, H=32, T=8192, d=128: forward
+    # checkpoint pass, reverse chain, per-chunk gradients
+    "backward": (0.8164e9 + 0.8137e9) + (1.0848e9 + 0.8137e9) + (2.6867e9 + 0.8075e9),
 }
 
 
@@ -401,7 +401,7 @@ def backward_bytes(B, H, T, D):
     return B * H * T * (2 * 5 * D + 2 + 2 * 4 * D + 2) + 3 * B * H * D * D * 4
 
 
-def backward_path_bytes(B, H, T, D, C=CH):
+def backward_path_bytes(B, H, T, D, C=CH, halves=False):
     """HBM bytes the kernels of the bf16 backward move by design, per
     chunk-head (2-byte elements unless noted):
       forward checkpoint pass: reads k, v, log_alpha, beta; writes the chunk's
@@ -410,8 +410,9 @@ def backward_path_bytes(B, H, T, D, C=CH):
       per-chunk gradients: reads q, k, log_alpha, dO, dv, beta and S, dU,
         Delta; writes dq, dk, dlog_alpha, dbeta;
     plus S0, dS_T read and dS0 and the forward pass's (unused) end state
-    written once per head (fp32); with the reverse chain in two halves (16
-    chunks per head and more), dS at their boundary written and read once more.
+    written once per head (fp32); with the reverse chain in two halves (option
+    bw_overlap, 16 chunks per head and more), dS at their boundary written and
+    read once more.
     The rows the chain kernels keep only for tokens with beta below 2^-30 (none
     in the benchmark's inputs) are not counted."""
     tok = C * 2 * D                     # one [C][D] bf16 tile
@@ -419,8 +420,8 @@ def backward_path_bytes(B, H, T, D, C=CH):
     k2 = 4 * tok + 2 * C + tok + D * D * 2
     k3 = 5 * tok + 2 * C + 2 * D * D * 2 + tok + 3 * tok + 2 * C
     nchunks = -(-T // C)
-    halves = 2 if nchunks >= 16 else 0
-    return B * H * nchunks * (k1 + k2 + k3) + (4 + halves) * B * H * D * D * 4
+    extra = 2 if halves and nchunks >= 16 else 0
+    return B * H * nchunks * (k1 + k2 + k3) + (4 + extra) * B * H * D * D * 4
 
 
 def backward_flops(B, H, T, D, C=CH):
@@ -472,8 +473,7 @@ def bench_backward(args, dev):
             "path_hbm_frac": pbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": traffic,
             "issued_mfma_tflops": fl / (ms * 1e-3) / 1e12,
             "mfma_frac": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
-            "kernels": "forward checkpoint pass beside the reverse chain's later half, the earlier half "
-                       "beside the later half's per-chunk gradients, then the earlier half's"}
+            "kernels": "forward checkpoint pass beside the reverse chain, then per-chunk gradients"}
 
 
 def bench_snapshots(pf, args, interval=512):

@@ -762,14 +762,16 @@ size_t chunk_bw_ws_floats(long long BH, int T, int D) {
 //     needs no forward state).  For the rows with beta below kTinyBeta only,
 //     they also keep W = V - Kh S, the row of strict_lower(Kh Kb^T) and Xbar;
 //  2. the per-chunk gradients, two workgroups (column halves) per (head, chunk).
-// With the overlap (option bw_overlap, on by default from kBwOverlapChunks
-// chunks per head) the reverse chain runs as two launches, the later half of
-// the chunks and then the earlier half (dS at the halves' boundary carried in
-// dS0, which each workgroup reads before it writes), and the later half's
-// gradients run on the side stream as soon as the forward pass and that half
-// of the reverse chain are done: on the CUs the forward pass leaves, beside the
-// earlier half of the reverse chain.  The earlier half's gradients follow it
-// on the caller's stream.
+// With the overlap (option bw_overlap 1, from kBwOverlapChunks chunks per
+// head) the reverse chain runs as two launches, the later half of the chunks
+// and then the earlier half (dS at the halves' boundary carried in dS0, which
+// each workgroup reads before it writes), and the later half's gradients run
+// on the side stream as soon as the forward pass and that half of the reverse
+// chain are done: on the CUs the forward pass leaves, beside the earlier half
+// of the reverse chain.  The earlier half's gradients follow it on the
+// caller's stream.  It is off by default: the gradients running beside the
+// earlier half slow that half, which is the critical path, about as much as
+// the idle CUs gain.
 constexpr long long kBwOverlapChunks = 16;
 kda_status chunk_backward(const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
                           const float* S0, const void* dO, const float* dS_T, void* dq, void* dk_, void* dv_,
@@ -797,7 +799,7 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
   const int ncb = pick_nc(2 * BH, nt, true);
   r.vsplit = nt / (ncb * kda::chunk_tiles_per_wave(true));
   if (BH * r.vsplit > INT32_MAX) return fail(KDA_ERR_SHAPE, "problem too large");
-  const bool overlap = opt(OPT_BW_OVERLAP) != 0 && nch >= kBwOverlapChunks;
+  const bool overlap = opt(OPT_BW_OVERLAP) == 1 && nch >= kBwOverlapChunks;
   const int c1 = overlap ? (int)(nch / 2) : 0;  // first chunk of the later half
   if (log_on())
     fprintf(stderr, "[libkda] backward BH=%lld T=%d D=%d: reverse chain nc=%d vsplit=%d, %lld x %lld chunk gradients%s\n",

@@ -936,47 +936,53 @@ struct ChunkKernel {
       }
   }
 
+  // Row-major bf16 D-wide matrices with the positions inside every 32-wide
+  // block of a row in the kpos order (the layout the per-chunk gradients read
+  // the state, dU and Delta in: a row of one gives an MFMA fragment over its
+  // columns in one 16-byte read).  A lane holds two adjacent columns of four
+  // rows; the lanes 2j, 2j+1, 2j+8, 2j+9 of a 16-lane row hold the columns of
+  // position group j (positions 8j .. 8j+7 of the block: columns 4j .. 4j+3 and
+  // 4j+16 .. 4j+19), so after a 4 x 4 transpose among them each stores one row
+  // of the group with one 16-byte store instead of four 4-byte ones.
+  // rows 16t + 4(l/16) + e of the lane's columns (dword e: the two bf16)
+  __device__ __forceinline__ void store_kpos_rows(rsrc_t r, int t, u32x4 d) const {
+    const int r16 = l & 15;
+    d = transpose4<DPP_ROW_ROR8>(d, (r16 & 8) != 0, (r16 & 1) != 0);
+    const int row = 16 * t + 4 * (l >> 4) + 2 * ((r16 >> 3) & 1) + (r16 & 1);
+    const int pos = (colb & ~31) + 8 * ((r16 & 7) >> 1);
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, (uint32_t)(row * D + pos) * 2u, 0, 0);
+  }
+
   // This lane's entries of the state (bf16 columns only) as bf16 into a
-  // row-major D x D matrix, and into its transpose unless cols is null, each
-  // with the positions inside every 32-wide block of a row in the kpos order.
-  // A row of either one then gives an MFMA fragment over the state's columns
-  // (rows) in one 16-byte read: the layout the per-chunk gradients read the
-  // state and dU in.
-  __device__ __forceinline__ void store_state_bf16(bf16* rows, bf16* cols) const {
+  // row-major D x D matrix in the layout above.
+  __device__ __forceinline__ void store_state_bf16(bf16* rows) const {
     if constexpr (C::BF) {
-      const rsrc_t rr = make_rsrc(rows, D * D * 2), rc = make_rsrc(cols, cols ? D * D * 2 : 0);
-      const int g4 = 4 * (l >> 4);
-      const uint32_t pc = (uint32_t)kpos(colb);  // colb even: colb + 1 sits at pc + 1
+      const rsrc_t rr = make_rsrc(rows, D * D * 2);
 #pragma unroll
-      for (int ci = 0; ci < D / 16; ++ci) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(cvt2(S[0][ci][e], S[1][ci][e]), rr,
-                                                (uint32_t)((16 * ci + g4 + e) * D + pc) * 2u, 0, 0);
-        const uint32_t pr = (uint32_t)kpos(16 * ci + g4);  // 4 consecutive rows, consecutive positions
-        if (!cols) continue;
-#pragma unroll
-        for (int j = 0; j < NCT; ++j) {
-          const u32x2 x = {cvt2(S[j][ci][0], S[j][ci][1]), cvt2(S[j][ci][2], S[j][ci][3])};
-          __builtin_amdgcn_raw_buffer_store_b64(x, rc, (uint32_t)((colb + j) * D + pr) * 2u, 0, 0);
-        }
-      }
+      for (int ci = 0; ci < D / 16; ++ci)
+        store_kpos_rows(rr, ci, u32x4{cvt2(S[0][ci][0], S[1][ci][0]), cvt2(S[0][ci][1], S[1][ci][1]),
+                                      cvt2(S[0][ci][2], S[1][ci][2]), cvt2(S[0][ci][3], S[1][ci][3])});
     }
   }
 
   // Row tile t of a [CH][D] matrix held in accumulators (x[j]: this lane's
   // columns colb + j), scaled by `sc`, as bf16 into a row-major [CH][D] matrix
-  // with kpos-ordered positions in each row (the gradients' checkpoint layout).
-  // With `bet` (the beta of the lane's rows 16t + 4(l/16) + e), only the rows
-  // whose beta is below kTinyBeta are stored.
+  // in the layout above.  With `bet` (the beta of the lane's rows 16t +
+  // 4(l/16) + e), only the rows whose beta is below kTinyBeta are stored (one
+  // 4-byte store each).
   __device__ __forceinline__ void store_tile_bf16(bf16* dst, const f32x4* x0, const f32x4* x1, int t, float sc,
                                                   const f32x4* bet = nullptr) const {
     const rsrc_t r = make_rsrc(dst, CH * D * 2);
+    if (!bet) {
+      store_kpos_rows(r, t, u32x4{cvt2(sc * x0[t][0], sc * x1[t][0]), cvt2(sc * x0[t][1], sc * x1[t][1]),
+                                  cvt2(sc * x0[t][2], sc * x1[t][2]), cvt2(sc * x0[t][3], sc * x1[t][3])});
+      return;
+    }
     const int g4 = 4 * (l >> 4);
     const uint32_t pc = (uint32_t)kpos(colb);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (!bet || (*bet)[e] < kTinyBeta)
+      if ((*bet)[e] < kTinyBeta)
         __builtin_amdgcn_raw_buffer_store_b32(cvt2(sc * x0[t][e], sc * x1[t][e]), r,
                                               (uint32_t)((16 * t + g4 + e) * D + pc) * 2u, 0, 0);
   }
@@ -1014,7 +1020,7 @@ struct ChunkKernel {
       ck_w = ck_d = nullptr;
       if (a.ck_rows) {
         const size_t o = ck0 + cc;
-        store_state_bf16(a.ck_rows + o * D * D, nullptr);
+        store_state_bf16(a.ck_rows + o * D * D);
         ck_w = a.ck_w + o * CH * D;
         ck_d = a.ck_d + o * CH * D;
       }
@@ -1065,7 +1071,7 @@ struct ChunkKernel {
 #pragma unroll
         for (int j = 0; j < NCT; ++j) S[j][ci] = S[j][ci] * gm;
       }
-      store_state_bf16(a.dU_rows + (ck0 + chunk) * D * D, nullptr);
+      store_state_bf16(a.dU_rows + (ck0 + chunk) * D * D);
 #pragma unroll
       for (int j = 0; j < NCT; ++j)
 #pragma unroll
@@ -1135,11 +1141,16 @@ struct ChunkKernel {
         for (int t = 0; t < 4; ++t) {
           const f32x4 bet = lds_ld<f32x4>(smem, st + C::S_BETA + 4 * (16 * t + kk));
           store_tile_bf16(xb, Xb[0], Xb[1], t, 1.f, &bet);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            __builtin_amdgcn_raw_buffer_store_b32(
-                cvt2(bet[e] * Xb[0][t][e], bet[e] * Xb[1][t][e]), ro,
-                (uint32_t)((chunk * CH + 16 * t + kk + e) * D + colb) * 2u, 0, 0);
+          // dv is row-major in plain column order: the four lanes of a quad
+          // hold 8 adjacent columns, and after a 4 x 4 transpose each stores
+          // one of their rows with one 16-byte store
+          const int q = l & 3;
+          const u32x4 d = transpose4<DPP_QUAD_SWAP2>(
+              u32x4{cvt2(bet[0] * Xb[0][t][0], bet[0] * Xb[1][t][0]), cvt2(bet[1] * Xb[0][t][1], bet[1] * Xb[1][t][1]),
+                    cvt2(bet[2] * Xb[0][t][2], bet[2] * Xb[1][t][2]), cvt2(bet[3] * Xb[0][t][3], bet[3] * Xb[1][t][3])},
+              (q & 2) != 0, (q & 1) != 0);
+          __builtin_amdgcn_raw_buffer_store_b128(d, ro,
+                                                 (uint32_t)((chunk * CH + 16 * t + kk + q) * D + (colb & ~7)) * 2u, 0, 0);
         }
       }
       // -diag(b) Xbar as B fragments over the chunk's tokens

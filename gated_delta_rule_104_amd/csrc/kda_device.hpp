@@ -155,6 +155,46 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 constexpr int DPP_ROW_SHR = 0x110;
+// integer moves: a rotation by 8 within each 16-lane row, and quad permutes
+// that swap neighbouring lanes ([1,0,3,2]) and lane pairs ([2,3,0,1])
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+constexpr int DPP_ROW_ROR8 = 0x128;
+constexpr int DPP_QUAD_SWAP1 = 0xB1;
+constexpr int DPP_QUAD_SWAP2 = 0x4E;
+
+// Four lanes a, b, c, d hold the rows e = 0..3 of a 4 x 4 matrix of dwords
+// (lane q: M[q][0..3]); afterwards lane q holds its column, M[0..3][q].  The
+// partner across the first pair of lane pairs is reached with CTRL1 (a
+// rotation by 8 within the row, or a quad permute), the neighbour with a quad
+// swap; h and p are lane q's bits (q = 2h + p).
+template <int CTRL1>
+__device__ __forceinline__ u32x4 transpose4(u32x4 d, bool h, bool p) {
+  uint32_t s0 = h ? d[0] : d[2], s1 = h ? d[1] : d[3];
+  s0 = dppu<CTRL1>(s0);
+  s1 = dppu<CTRL1>(s1);
+  if (h) {
+    d[0] = s0;
+    d[1] = s1;
+  } else {
+    d[2] = s0;
+    d[3] = s1;
+  }
+  s0 = p ? d[0] : d[1];
+  s1 = p ? d[2] : d[3];
+  s0 = dppu<DPP_QUAD_SWAP1>(s0);
+  s1 = dppu<DPP_QUAD_SWAP1>(s1);
+  if (p) {
+    d[0] = s0;
+    d[2] = s1;
+  } else {
+    d[1] = s0;
+    d[3] = s1;
+  }
+  return d;
+}
 
 // 8 consecutive elements of a token row, as loaded from HBM.
 template <typename T> struct Raw8 { u32x4 p[sizeof(T) / 2]; };

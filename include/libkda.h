@@ -324,12 +324,12 @@ kda_status kda_prefill_backward(const void* q, const void* k, const void* v, con
  *                      (1, 2, 4, 8 where built; default: chosen from the shape)
  *   "bw_split"         workgroups per head of the backward's chunk kernels (1 or
  *                      2; default: chosen from the shape)
- *   "bw_overlap"       bf16 backward from 16 chunks per head: 1 (default) runs
- *                      the reverse chain in two launches (later half of the
+ *   "bw_overlap"       bf16 backward from 16 chunks per head: 1 runs the
+ *                      reverse chain in two launches (later half of the
  *                      chunks, then earlier half) and the later half's per-chunk
  *                      gradients beside the earlier half's chain, on the side
- *                      stream; 0 runs the chain whole, then every chunk's
- *                      gradients.  Same results bit for bit
+ *                      stream; 0 (default) runs the chain whole, then every
+ *                      chunk's gradients.  Same results bit for bit
  *   "check"            1: validate log_alpha and beta on the device before every
  *                      call that reads them (see the conventions above); default 0
  *   "log"              1: print every launch's shape to stderr; default 0
