@@ -54,19 +54,19 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "053f3bb601b6a896",
+    "sources_sha": "09cedf4d98433bad",
     # the kernels of one kda_chunk_prefill call at h32_t64k: the two segment-pass
     # launches (the head walk, and the pass over segments whose map did not
     # vanish, whose workgroups all exit here), the prefill of every segment from
     # zero, the merge, the corrected heads
-    "segment_pass_launches": 0.03353e9,
-    "zero_start_segments": 2.15292e9 + 0.55367e9,
+    "segment_pass_launches": 0.03354e9,
+    "zero_start_segments": 2.15312e9 + 0.55366e9,
     "segment_merge": 0.00219e9 + 0.00210e9,
-    "corrected_heads": 0.07422e9 + 0.01468e9,
+    "corrected_heads": 0.07440e9 + 0.01468e9,
     "decode_step": 0.5455e9 + 0.5390e9,
     # the backward's three kernels at B=4, H=32, T=8192, d=128: forward
     # checkpoint pass, reverse chain, per-chunk gradients
-    "backward": (0.8164e9 + 0.8137e9) + (1.0848e9 + 0.8137e9) + (2.6867e9 + 0.8075e9),
+    "backward": (0.8164e9 + 0.8137e9) + (1.0849e9 + 0.8137e9) + (2.6868e9 + 0.8075e9),
 }
 
 
