@@ -89,6 +89,10 @@ def load() -> ctypes.CDLL:
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_abi_version.restype = i
+    lib.kda_debug_time_main_launches.argtypes = [i]
+    lib.kda_debug_time_main_launches.restype = i
+    lib.kda_debug_main_launch_ms.argtypes = [ctypes.POINTER(ctypes.c_float), i, ctypes.POINTER(i)]
+    lib.kda_debug_main_launch_ms.restype = i
     _lib = lib
     return lib
 
@@ -110,6 +114,23 @@ def get_option(name: str) -> Optional[int]:
     v = ctypes.c_longlong(0)
     _check(load().kda_get_option(name.encode(), ctypes.byref(v)), f"get_option({name})")
     return None if v.value == -1 else int(v.value)
+
+
+def debug_time_main_launches(count: int) -> None:
+    """Arm HIP events around the main launch of the next `count` sequence-split
+    prefills (kda_debug_time_main_launches; 0 disarms)."""
+    _check(load().kda_debug_time_main_launches(int(count)), "debug_time_main_launches")
+
+
+def debug_main_launch_ms() -> list:
+    """Durations (ms) of the main launches timed since the arming
+    (kda_debug_main_launch_ms; waits for them)."""
+    lib = load()
+    n = ctypes.c_int(0)
+    _check(lib.kda_debug_main_launch_ms(None, 0, ctypes.byref(n)), "debug_main_launch_ms")
+    buf = (ctypes.c_float * max(n.value, 1))()
+    _check(lib.kda_debug_main_launch_ms(buf, n.value, ctypes.byref(n)), "debug_main_launch_ms")
+    return [float(buf[i]) for i in range(n.value)]
 
 
 @contextlib.contextmanager

@@ -366,6 +366,30 @@ struct Snap {
 std::atomic<unsigned long long*> g_stamps{nullptr};
 std::atomic<size_t> g_stamps_n{0};
 
+// Events around the main launch of the next sequence-split prefills
+// (kda_debug_time_main_launches): pair i brackets the i-th armed launch.
+constexpr int kMaxTimedLaunches = 256;
+struct MainTimer {
+  std::mutex mu;
+  int dev = -1;
+  int cap = 0;    // armed pairs
+  int n = 0;      // pairs recorded so far
+  int made = 0;   // pairs created on `dev`
+  hipEvent_t ev[2 * kMaxTimedLaunches] = {};
+};
+MainTimer g_mt;
+
+// The next armed event pair on the current device, or nulls when none is armed.
+void main_timer_slot(hipEvent_t* start, hipEvent_t* stop) {
+  *start = *stop = nullptr;
+  std::lock_guard<std::mutex> lk(g_mt.mu);
+  int dev = -1;
+  if (g_mt.n >= g_mt.cap || hipGetDevice(&dev) != hipSuccess || dev != g_mt.dev) return;
+  *start = g_mt.ev[2 * g_mt.n];
+  *stop = g_mt.ev[2 * g_mt.n + 1];
+  ++g_mt.n;
+}
+
 // Per-segment control of a prefill launch in the split path with corrected
 // heads (ChunkArgs::seg_flag and the fields after it).
 struct SegCtl {
@@ -502,6 +526,42 @@ kda_status kda_debug_phase_stamps(unsigned long long* stamps, size_t count) {
 #endif
 }
 
+kda_status kda_debug_time_main_launches(int count) {
+  if (count < 0 || count > kMaxTimedLaunches)
+    return fail(KDA_ERR_SHAPE, "count %d out of range (0 .. %d)", count, kMaxTimedLaunches);
+  std::lock_guard<std::mutex> lk(g_mt.mu);
+  g_mt.cap = g_mt.n = 0;
+  if (count == 0) return ok();
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != g_mt.dev) {  // events belong to the device current when they were created
+    for (int i = 0; i < 2 * g_mt.made; ++i) (void)hipEventDestroy(g_mt.ev[i]);
+    g_mt.made = 0;
+    g_mt.dev = dev;
+  }
+  for (; g_mt.made < count; ++g_mt.made)
+    if ((e = hipEventCreate(&g_mt.ev[2 * g_mt.made])) != hipSuccess ||
+        (e = hipEventCreate(&g_mt.ev[2 * g_mt.made + 1])) != hipSuccess)
+      return hip_fail(e, "hipEventCreate");
+  g_mt.cap = count;
+  return ok();
+}
+
+kda_status kda_debug_main_launch_ms(float* ms, int count, int* recorded) {
+  if (!recorded) return fail(KDA_ERR_NULL, "recorded is NULL");
+  if (count < 0) return fail(KDA_ERR_SHAPE, "count %d is negative", count);
+  if (count > 0 && !ms) return fail(KDA_ERR_NULL, "ms is NULL");
+  std::lock_guard<std::mutex> lk(g_mt.mu);
+  *recorded = g_mt.n;
+  for (int i = 0; i < g_mt.n && i < count; ++i) {
+    hipError_t e = hipEventSynchronize(g_mt.ev[2 * i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms[i], g_mt.ev[2 * i], g_mt.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "reading the launch events");
+  }
+  return ok();
+}
+
 size_t kda_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, kda_dtype dtype) {
   if (B <= 0 || H <= 0 || T <= 0 || dk != dv || (dk != 64 && dk != 128)) return 0;
   return plan_prefill((long long)B * H, T, dk, dtype).ws;
@@ -620,9 +680,15 @@ kda_status prefill_split_heads(const void* q, const void* k, const void* v, cons
       return hip_fail(e, "kda_chunk_prefill segment pass");
     SegCtl sc;
     sc.rec = rec; sc.mode = kda::FLAG_FAST_ONLY; sc.g0 = 1; sc.Z_out = Z; sc.s0_first = true;
-    st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, o, nullptr, BH, T, 0, T, Ts, D, bf, stream,
-                                "kda_chunk_prefill zero-start segments", sn, nc1, nullptr, nullptr, nullptr,
-                                nullptr, sc);
+    hipEvent_t t0 = nullptr, t1 = nullptr;  // profiling hook: this launch's duration
+    main_timer_slot(&t0, &t1);
+    if (t0 && (e = hipEventRecord(t0, stream)) != hipSuccess) st = hip_fail(e, "kda_chunk_prefill event");
+    if (st == KDA_OK)
+      st = launch_segment_prefill(q, k, v, log_alpha, beta, S0, o, nullptr, BH, T, 0, T, Ts, D, bf, stream,
+                                  "kda_chunk_prefill zero-start segments", sn, nc1, nullptr, nullptr, nullptr,
+                                  nullptr, sc);
+    if (st == KDA_OK && t1 && (e = hipEventRecord(t1, stream)) != hipSuccess)
+      st = hip_fail(e, "kda_chunk_prefill event");
     // join even if the launch above failed, so the side stream's work is waited for
     if ((e = hipEventRecord(ss->join, ss->s)) != hipSuccess ||
         (e = hipStreamWaitEvent(stream, ss->join, 0)) != hipSuccess)

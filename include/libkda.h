@@ -355,6 +355,24 @@ kda_status kda_get_option(const char* name, long long* value);
  */
 kda_status kda_debug_phase_stamps(unsigned long long* stamps, size_t count);
 
+/*
+ * Profiling only (any build): the duration of the main launch (the prefill of
+ * every segment from zero) of sequence-split prefills, timed with HIP events
+ * recorded on the caller's stream around that launch, so that the calls
+ * themselves are not synchronised.
+ *   kda_debug_time_main_launches(count): arms count event pairs (1 .. 256)
+ *     for the next count sequence-split prefills on the current device, and
+ *     forgets what an earlier arming recorded; 0 disarms.  KDA_ERR_SHAPE for a
+ *     count out of range.
+ *   kda_debug_main_launch_ms(ms, count, recorded): *recorded = the launches
+ *     timed since the arming; waits for them and writes the first
+ *     min(count, *recorded) durations in milliseconds to ms (host memory).
+ * One caller at a time: calls that overlap on other threads may take each
+ * other's pairs.
+ */
+kda_status kda_debug_time_main_launches(int count);
+kda_status kda_debug_main_launch_ms(float* ms, int count, int* recorded);
+
 const char* kda_status_string(kda_status status);
 const char* kda_last_error(void);
 int kda_abi_version(void);

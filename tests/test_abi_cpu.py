@@ -293,6 +293,20 @@ def test_backward_validation(lib):
     assert backward(lib, B=0, ws=None, ws_bytes=0) == OK
 
 
+def test_main_launch_timer_validation(lib):
+    """The main-launch timer checks its arguments on the host; disarming and
+    reading back nothing touch no device."""
+    n = ctypes.c_int(-1)
+    assert lib.kda_debug_time_main_launches(-1) == ERR_SHAPE
+    assert lib.kda_debug_time_main_launches(257) == ERR_SHAPE
+    assert lib.kda_debug_time_main_launches(0) == OK
+    assert lib.kda_debug_main_launch_ms(None, 0, ctypes.byref(n)) == OK and n.value == 0
+    assert lib.kda_debug_main_launch_ms(None, 0, None) == ERR_NULL
+    assert lib.kda_debug_main_launch_ms(None, 1, ctypes.byref(n)) == ERR_NULL
+    buf = (ctypes.c_float * 1)()
+    assert lib.kda_debug_main_launch_ms(buf, -1, ctypes.byref(n)) == ERR_SHAPE
+
+
 def test_options(lib, kda_opts):
     """Options are validated by name and value, read back as set, and -1 restores
     the library default; calls that only validate are unaffected."""

@@ -773,3 +773,39 @@ def test_prefill_split_mixed_heads(head_chunks, kda_opts):
     eo, es = oracle.max_rel_l2(o.cpu(), o_ref), oracle.max_rel_l2(S_T.cpu(), S_ref)
     print(f"    o {eo:.3e}  S_T {es:.3e}  first 16 tokens of every segment {win:.3e}", flush=True)
     assert eo <= TOL["bf16"] and es <= TOL["bf16"] and win <= TOL["bf16"]
+
+
+def test_main_launch_timer():
+    """kda_debug_time_main_launches / kda_debug_main_launch_ms: the armed
+    sequence-split prefills each record their main launch's duration, which
+    lies inside the call's own; calls past the armed count record nothing, and
+    re-arming forgets the earlier durations.  Results are unchanged."""
+    B, H, T, D = 1, 8, 8192, 128
+    print(f"[case] main-launch timer B={B} H={H} T={T}", flush=True)
+    T0, G, _ = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
+    assert T0 == 0 and G > 1
+    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=77, device=dev())
+    call = lambda: kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None)
+    ref = call()
+    kda.debug_time_main_launches(2)
+    try:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+        outs = []
+        for a, b in evs:
+            a.record()
+            outs.append(call())
+            b.record()
+        torch.cuda.synchronize()
+        ms = kda.debug_main_launch_ms()
+        assert len(ms) == 2, ms
+        for t, (a, b) in zip(ms, evs):
+            assert 0.0 < t <= a.elapsed_time(b) + 1e-3, (t, a.elapsed_time(b))
+        for o, S in outs:
+            assert torch.equal(o, ref[0]) and torch.equal(S, ref[1])
+        kda.debug_time_main_launches(1)
+        assert kda.debug_main_launch_ms() == []
+        call()
+        assert len(kda.debug_main_launch_ms()) == 1
+    finally:
+        kda.debug_time_main_launches(0)
+    assert kda.debug_main_launch_ms() == []
