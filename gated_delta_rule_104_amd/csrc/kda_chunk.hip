@@ -180,7 +180,6 @@ struct ChunkKernel {
   ChunkArgs a;
   rsrc_t rq, rk, rv, rla, rbeta, ro;
   int Tlen, nch;
-  int bh_seq;        // the sequence (segment) this workgroup works on
   bf16* ck_w;        // this chunk's checkpoints of W = V - Kh S (rows with tiny beta
   bf16* ck_d;        // only) and Delta (prefill with gradient checkpoints), else null
   int chunk0;        // chunks of the head's sequence before this segment
@@ -1333,7 +1332,6 @@ struct ChunkKernel {
     if ((W & 7) == 0 && a.vsplit > 1) id = (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
     const int seq = id / a.vsplit;
     const int vs = id - seq * a.vsplit;
-    bh_seq = seq;
     const int gseg = seq / a.BH;
     const int bh = seq - gseg * a.BH;
     const int seg0 = a.t0 + gseg * a.Tseg;  // first token of this segment
