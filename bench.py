@@ -54,7 +54,7 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "3e809d540accdfe1",
+    "sources_sha": "1b13feb642b55b40",
     # the kernels of one kda_chunk_prefill call at h32_t64k: the two segment-pass
     # launches (the head walk, and the pass over segments whose map did not
     # vanish, whose workgroups all exit here), the prefill of every segment from
@@ -276,38 +276,54 @@ def zero_start_bytes(B, H, T, D, G):
 STAMP_FIRST, STAMP_STEPS, STAMP_WAVES = 32, 16, 8  # the profiling build's recording window
 
 
-def phase_stamps(dev):
-    """Where a pipeline step of the h32_t64k prefill's main kernel (every segment
-    from zero) goes, from the profiling build's per-wave shader-clock stamps of
-    steps 32 .. 47 on every workgroup: median cycles of each phase for consumer
-    waves (the chain) and producer waves (the elementwise phase), the waits at
-    the two barriers, and the step period (start to the next step's start,
-    earliest wave)."""
+def phase_stamps(dev, which="prefill"):
+    """Where a pipeline step of a chunk kernel goes, from the profiling build's
+    per-wave shader-clock stamps of steps 32 .. 47 on every workgroup: median
+    cycles of each phase for consumer waves (the chain) and producer waves (the
+    elementwise phase), the waits at the two barriers, and the step period
+    (start to the next step's start, earliest wave).  which: "prefill", the
+    h32_t64k prefill's main kernel (every segment from zero); "ckpt" or
+    "reverse", the checkpoint pass or the reverse chain of the b4_h32_t8k
+    prefill gradients."""
     import ctypes
     import numpy as np
     kda.LIB_PATH = os.path.join(ROOT, "gated_delta_rule_104_amd", "libkda_stamps.so")
     lib = kda.load()
-    B, H, T, D = 1, 32, 65536, 128
-    T0, G, Tseg = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
-    assert T0 == 0 and G > 1, "the phase split is recorded on the split prefill's main launch"
-    nwg = B * H * G
-    g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=2, device=dev)
+    if which == "prefill":
+        B, H, T, D = 1, 32, 65536, 128
+        T0, G, Tseg = kda.prefill_plan(B, H, T, D, D, torch.bfloat16)
+        assert T0 == 0 and G > 1, "the phase split is recorded on the split prefill's main launch"
+        nwg = B * H * G
+        g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=2, device=dev)
+        call = lambda: kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None)
+    else:
+        B, H, T, D = 4, 32, 8192, 128
+        nwg = B * H  # one workgroup per head (both chains, side by side, fill the chip once)
+        g = ki.gen_prefill(B, H, T, D, D, "bf16", seed=1, s0_std=0.1, device=dev)
+        gen = torch.Generator(device=dev).manual_seed(6)
+        dO = torch.randn(B, H, T, D, generator=gen, device=dev).to(torch.bfloat16)
+        dST = torch.randn(B, H, D, D, generator=gen, device=dev)
+        ws = torch.empty(kda.backward_workspace_bytes(B, H, T, D, D, torch.bfloat16), dtype=torch.uint8, device=dev)
+        call = lambda: kda.prefill_backward(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], g["S0"], dO, dST,
+                                            workspace=ws)
     st = torch.zeros(nwg * STAMP_STEPS * STAMP_WAVES * 5, dtype=torch.int64, device=dev)
-    call = lambda: kda.prefill(g["q"], g["k"], g["v"], g["log_alpha"], g["beta"], None)
-    for _ in range(30):
+    for _ in range(30 if which == "prefill" else 10):
         call()
     torch.cuda.synchronize()
+    os.environ["KDA_STAMP_TARGET"] = which
     kda._check(lib.kda_debug_phase_stamps(ctypes.c_void_p(st.data_ptr()), ctypes.c_size_t(st.numel())),
                "kda_debug_phase_stamps")
     call()
     torch.cuda.synchronize()
     kda._check(lib.kda_debug_phase_stamps(None, ctypes.c_size_t(0)), "kda_debug_phase_stamps")
     s = st.cpu().numpy().reshape(nwg, STAMP_STEPS, STAMP_WAVES, 5).astype(np.float64)
-    nc = 4  # consumer waves of the main launch (the rest produce)
+    s = s[(s[:, :, :, 0] > 0).all(axis=(1, 2))]  # workgroups that ran these steps (an exited one records none)
+    assert len(s), "no workgroup recorded its steps"
+    nc = 4  # consumer waves (the rest produce)
     cons, prod = s[:, :-1, :nc], s[:, :-1, nc:]
     med = lambda x: float(np.median(x))
-    out = {"workgroups": nwg, "steps": f"{STAMP_FIRST}..{STAMP_FIRST + STAMP_STEPS - 1}", "unit": "cycles",
-           "period": med(s[:, 1:, :, 0].min(axis=2) - s[:, :-1, :, 0].min(axis=2))}
+    out = {"launch": which, "workgroups": len(s), "steps": f"{STAMP_FIRST}..{STAMP_FIRST + STAMP_STEPS - 1}",
+           "unit": "cycles", "period": med(s[:, 1:, :, 0].min(axis=2) - s[:, :-1, :, 0].min(axis=2))}
     for name, w, first in (("consumers", cons, "chain"), ("producers", prod, "elementwise")):
         out[name] = {first: med(w[..., 1] - w[..., 0]), "wait_barrier_1": med(w[..., 2] - w[..., 1]),
                      "score_tiles": med(w[..., 3] - w[..., 2]), "wait_barrier_2": med(w[..., 4] - w[..., 3])}
@@ -761,9 +777,11 @@ def main():
     ap.add_argument("--no-tokens", action="store_true", help="skip the several-token decode")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-calib", action="store_true", help="skip the GEMM and copy reference rates")
-    ap.add_argument("--phase-stamps", action="store_true",
+    ap.add_argument("--phase-stamps", nargs="?", const="prefill", default=None,
+                    choices=["prefill", "ckpt", "reverse"],
                     help="with the profiling build (build.py --stamps): the phase split of the h32_t64k "
-                         "prefill's main kernel, from per-wave timestamps, instead of the bench line")
+                         "prefill's main kernel (or of the b4_h32_t8k gradients' checkpoint pass or reverse "
+                         "chain), from per-wave timestamps, instead of the bench line")
     ap.add_argument("--no-decomp", action="store_true",
                     help="skip timing the split prefill's pieces through the public calls (the roofline "
                          "then takes the whole call)")
@@ -793,7 +811,7 @@ def main():
         print(json.dumps({"copy_calib_bytes": n, "launches": 3}), flush=True)
         return
     if args.phase_stamps:
-        print(json.dumps({"phase_stamps": phase_stamps(dev)}), flush=True)
+        print(json.dumps({"phase_stamps": phase_stamps(dev, args.phase_stamps)}), flush=True)
         return
     kda.load()
 

@@ -362,9 +362,12 @@ struct Snap {
   int H = 1;
 };
 
-// Phase timestamps of the profiling build (kda_debug_phase_stamps).
+// Phase timestamps of the profiling build (kda_debug_phase_stamps), and the
+// launch that records them: 0 the sequence-split prefill's main launch, 1 the
+// backward's checkpoint pass, 2 the backward's reverse chain.
 std::atomic<unsigned long long*> g_stamps{nullptr};
 std::atomic<size_t> g_stamps_n{0};
+std::atomic<int> g_stamp_target{0};
 
 // Events around the main launch of the next sequence-split prefills
 // (kda_debug_time_main_launches): pair i brackets the i-th armed launch.
@@ -429,7 +432,8 @@ kda_status launch_segment_prefill(const void* q, const void* k, const void* v, c
   a.ck_rows = ck_rows; a.ck_w = ck_w; a.ck_d = ck_d; a.ck_a = ck_a;
   a.seg_flag = sc.rec; a.flag_mode = sc.mode; a.flag_g0 = sc.g0; a.head_chunks = sc.head;
   a.Z_out = sc.Z_out; a.s0_first = sc.s0_first ? 1 : 0; a.Z_prev = sc.Z_prev;
-  if (sc.mode == kda::FLAG_FAST_ONLY) {  // the split prefill's main launch
+  const int stamp_target = g_stamp_target.load(std::memory_order_relaxed);
+  if ((sc.mode == kda::FLAG_FAST_ONLY && stamp_target == 0) || (ck_rows && stamp_target == 1)) {
     a.stamps = g_stamps.load(std::memory_order_relaxed);
     a.stamps_n = g_stamps_n.load(std::memory_order_relaxed);
   }
@@ -516,6 +520,8 @@ const char* kda_status_string(kda_status s) {
 kda_status kda_debug_phase_stamps(unsigned long long* stamps, size_t count) {
 #ifdef KDA_PHASE_STAMPS
   if (!stamps) count = 0;
+  const char* t = getenv("KDA_STAMP_TARGET");
+  g_stamp_target.store(t && !strcmp(t, "ckpt") ? 1 : t && !strcmp(t, "reverse") ? 2 : 0, std::memory_order_relaxed);
   g_stamps.store(count ? stamps : nullptr, std::memory_order_relaxed);
   g_stamps_n.store(count, std::memory_order_relaxed);
   return ok();
@@ -860,6 +866,10 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
   r.BH = (int)BH; r.G = 1; r.Tseg = T > 0 ? T : 1; r.Ttot = T; r.t0 = 0; r.Tend = T;
   r.dU_rows = dU_rows;
   r.ck_xb = Xb;
+  if (g_stamp_target.load(std::memory_order_relaxed) == 2) {
+    r.stamps = g_stamps.load(std::memory_order_relaxed);
+    r.stamps_n = g_stamps_n.load(std::memory_order_relaxed);
+  }
   // The forward pass and the reverse chain run side by side: their column
   // split is chosen so that both together fill the chip once.
   const int ncb = pick_nc(2 * BH, nt, true);

@@ -1379,7 +1379,7 @@ struct ChunkKernel {
     wave = threadIdx.x >> 6;
     l = lane_id();
 #ifdef KDA_PHASE_STAMPS
-    if constexpr (PREFILL && !BWD && !CKPT && NC + D / 32 <= kStampWaves) {
+    if constexpr (PREFILL && NC + D / 32 <= kStampWaves) {
       const size_t per = (size_t)kStampSteps * kStampWaves * 5;
       if (a.stamps && (size_t)(blockIdx.x + 1) * per <= a.stamps_n) stp = a.stamps + blockIdx.x * per;
     }

@@ -346,7 +346,10 @@ kda_status kda_get_option(const char* name, long long* value);
  * zero), the shader clock (s_memtime) of every wave at five points of
  * pipeline steps 32 .. 47: the step's start, the end of the elementwise phase
  * (producer waves) or of the chain (consumer waves), after the first barrier,
- * the end of the score tiles, after the second barrier.
+ * the end of the score tiles, after the second barrier.  With the environment
+ * variable KDA_STAMP_TARGET set to "ckpt" or "reverse" when this is called,
+ * the bf16 prefill backward's checkpoint pass or its reverse chain (in the
+ * reverse chain, step i is chunk nch - 1 - i) records them instead.
  *   stamps : device buffer of count 64-bit entries, indexed
  *            [workgroup][step - 32][wave][point] with 8 wave slots; a
  *            workgroup whose entries do not fit records nothing; NULL (or
