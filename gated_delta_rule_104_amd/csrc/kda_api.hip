@@ -813,7 +813,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
 }
 
 // Workspace of the chunked backward (bf16 inputs), per chunk-head: the start
-// state and dU = Diag(Gam) dS' (bf16 D x D each), W = V - Kh S, Delta and
+// state and dS' (bf16 D x D each), W = V - Kh S, Delta and
 // Xbar (bf16 64 x D each), all row-major with kpos-ordered positions, and the
 // 10 lower 16x16 blocks of strict_lower(Kh Kb^T) (bf16, lane order); then the
 // forward pass's end state, which is not needed (fp32 [BH, D, D]).  W, Xbar
@@ -830,7 +830,7 @@ size_t chunk_bw_ws_floats(long long BH, int T, int D) {
 //  1. beside each other: the forward pass from S0, which keeps the start state
 //     and Delta of every chunk (its outputs are not written), on the side
 //     stream; and the reverse chain from dS_T over the chunks, last to first,
-//     which keeps dU = Diag(Gam) dS' of every chunk and writes dv and dS0 (it
+//     which keeps dS' of every chunk and writes dv and dS0 (it
 //     needs no forward state).  For the rows with beta below kTinyBeta only,
 //     they also keep W = V - Kh S, the row of strict_lower(Kh Kb^T) and Xbar;
 //  2. the per-chunk gradients, two workgroups (column halves) per (head, chunk).
@@ -853,8 +853,8 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
   const long long nch = (T + 63) / 64;
   const size_t nS = (size_t)BH * nch * D * D, nC = (size_t)BH * nch * 64 * D;  // elements per array
   kda::bf16* S_rows = reinterpret_cast<kda::bf16*>(ws);
-  kda::bf16* dU_rows = S_rows + nS;
-  kda::bf16* W = dU_rows + nS;
+  kda::bf16* dSp_rows = S_rows + nS;
+  kda::bf16* W = dSp_rows + nS;
   kda::bf16* Dl = W + nC;
   kda::bf16* Xb = Dl + nC;
   kda::bf16* Ack = Xb + nC;
@@ -864,7 +864,7 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
   r.q = q; r.k = k; r.v = dO; r.la = log_alpha; r.beta = beta;
   r.S0 = dS_T; r.o = dv_; r.S_out = dS0; r.M_out = nullptr;
   r.BH = (int)BH; r.G = 1; r.Tseg = T > 0 ? T : 1; r.Ttot = T; r.t0 = 0; r.Tend = T;
-  r.dU_rows = dU_rows;
+  r.dSp_rows = dSp_rows;
   r.ck_xb = Xb;
   if (g_stamp_target.load(std::memory_order_relaxed) == 2) {
     r.stamps = g_stamps.load(std::memory_order_relaxed);
@@ -889,7 +889,7 @@ kda_status chunk_backward(const void* q, const void* k, const void* v, const voi
   kda::BwGradArgs g;
   g.q = q; g.k = k; g.la = log_alpha; g.beta = beta; g.dO = dO;
   g.dv = static_cast<const kda::bf16*>(dv_);
-  g.S_rows = S_rows; g.W = W; g.Dl = Dl; g.A = Ack; g.dU_rows = dU_rows; g.Xb = Xb;
+  g.S_rows = S_rows; g.W = W; g.Dl = Dl; g.A = Ack; g.dSp_rows = dSp_rows; g.Xb = Xb;
   g.dq = static_cast<kda::bf16*>(dq); g.dk = static_cast<kda::bf16*>(dk_);
   g.dla = static_cast<kda::bf16*>(dlog_alpha); g.dbeta = static_cast<kda::bf16*>(dbeta); g.T = T;
   SideStream* ss = nullptr;

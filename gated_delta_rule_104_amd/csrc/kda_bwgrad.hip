@@ -30,7 +30,7 @@
 // The forward equations give Delta = diag(b) Y exactly ((I + diag(b) A) Delta
 // = diag(b) W), so for b_r != 0, dbeta_r = dv_r . Delta_r / b_r^2, and no
 // product needs Xbar, W or A itself.  The forward pass stores S and Delta of
-// every chunk and the reverse chain dU (and writes dv); only for the rows with
+// every chunk and the reverse chain dS' (and writes dv); only for the rows with
 // b below kTinyBeta do they also keep W, A's row and Xbar, from which this
 // kernel forms dbeta_r = Xbar_r . (W_r - sum_{s<r} A_rs Delta_s).  Two workgroups
 // per (head, chunk), each owning half of the key dimension's columns with one
@@ -197,7 +197,7 @@ struct GradKernel {
   // flight across phases 1 and 2 (the barriers wait only for LDS).  bf16
   // values at this lane's accumulator positions are kept as raw 16-bit loads.
   struct Pre5 {
-    bf16x8 sr[NCT][NKD], ur[NCT][NKD];  // S and dU rows as B fragments over their columns
+    bf16x8 sr[NCT][NKD], ur[NCT][NKD];  // S and dS' rows as B fragments over their columns
     uint32_t la[NCT][16], q[NCT][16], k[NCT][16];
   };
   __device__ __forceinline__ uint32_t raw16(rsrc_t r, uint32_t off) const {
@@ -357,9 +357,12 @@ struct GradKernel {
     f32x4 qv[4], kv[4], eg[4], emg[4], dqh[4], dkh[4], dks[4];
     float dgc;
   };
+  // The reverse chain keeps dS', so row c of dU = Diag(Gam) dS' is Gam_c =
+  // e^(g_C) (column c's gate over the whole chunk) times row c of dS': the
+  // products with dU's row below take that factor after the products.
   __device__ __forceinline__ void phase5a(int j, const Pre5& p, Part3& z) {
-    // rows c of S and dU as B fragments over the state's columns, and
-    // rowsum(dU . S) over the lane's positions
+    // rows c of S and dS' as B fragments over the state's columns, and
+    // rowsum(dS' . S) over the lane's positions
     const bf16x8* sr = p.sr[j];
     const bf16x8* ur = p.ur[j];
     float dgc = 0.f;
@@ -367,16 +370,16 @@ struct GradKernel {
     for (int m = 0; m < NKD; ++m)
 #pragma unroll
       for (int e = 0; e < 4; ++e) dgc = dot2(sr[m], ur[m], e, dgc);
-    // rowsum(dU . S): the four lane groups (l%16 fixed) hold the rest of the row's sum
+    // rowsum(dS' . S): the four lane groups (l%16 fixed) hold the rest of the row's sum
     dgc += __shfl_xor(dgc, 16);
     dgc += __shfl_xor(dgc, 32);
-    z.dgc = dgc;
     // the gate at this lane's positions: g from log_alpha by a prefix over the
     // lane's 4 rows, then over the lane groups and row tiles
     f32x4* qv = z.qv;
     f32x4* kv = z.kv;
     f32x4* eg = z.eg;
     f32x4* emg = z.emg;
+    float gam;  // Gam_c
     {
       float tot[4];
       f32x4 gv[4];
@@ -406,17 +409,19 @@ struct GradKernel {
         }
         base += (a0 + a1) + (a2 + a3);
       }
+      gam = __builtin_amdgcn_exp2f(base * G_LOG2E);
     }
+    z.dgc = gam * dgc;  // rowsum(dU . S)
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x4 b = zero4(), q = zero4(), h = zero4();
 #pragma unroll
       for (int m = 0; m < NKD; ++m) {
-        b = mfma_bf16_k32(b, ar(C::DL, t, m), ur[m]);  // Delta dU^T
+        b = mfma_bf16_k32(b, ar(C::DL, t, m), ur[m]);  // Delta dS'^T
         q = mfma_bf16_k32(q, ar(C::DO, t, m), sr[m]);  // dO S^T
         h = mfma_bf16_k32(h, ar(C::DV, t, m), sr[m]);  // dv S^T
       }
-      z.dks[t] = b;
+      z.dks[t] = gam * b;  // Delta dU^T
       z.dqh[t] = q;
       z.dkh[t] = -h;  // dKh = -dv S^T + ...
     }
@@ -551,7 +556,7 @@ struct GradKernel {
     // Xbar and A are read only for rows with beta below kTinyBeta)
     const size_t ck = (size_t)bh * nch + n;
     rSr = make_rsrc(a.S_rows + ck * D * D, D * D * 2u);
-    rUr = make_rsrc(a.dU_rows + ck * D * D, D * D * 2u);
+    rUr = make_rsrc(a.dSp_rows + ck * D * D, D * D * 2u);
     rW = make_rsrc(a.W + ck * GCH * D, GCH * D * 2u);
     rDl = make_rsrc(a.Dl + ck * GCH * D, GCH * D * 2u);
     rXb = make_rsrc(a.Xb + ck * GCH * D, GCH * D * 2u);

@@ -699,6 +699,14 @@ struct ChunkKernel {
   // whose length the chain sets; their score-tile share shrinks to match.  The
   // bf16 copies of S (sb) and Delta (db) stay live across the barrier.
   static constexpr bool DEFER_O = QP && !BWD && C::LAG && C::BF;
+  // The checkpoint pass stores the start state of chunk n + 1 (the end state of
+  // chunk n) after the first barrier of the step that ran chunk n's chain, so
+  // that the 32 KiB of stores drain beside the score tiles instead of inside
+  // the chain (the first chunk's start state is stored in its chain).
+  static constexpr bool CK_LATE = CKPT && C::LAG;
+  // Likewise the reverse chain stores dS' of chunk c - 1 (the gradient at
+  // chunk c's start, which its chain has just formed) after the first barrier.
+  static constexpr bool DSP_LATE = BWD && C::LAG;
   // Weight of the outputs of one chunk in score-tile units (a tile is one unit,
   // a diagonal block with its inverse two) when handing out the score tiles.
   // Per-wave timestamps put the outputs at about 2.1K cycles against about
@@ -1019,7 +1027,7 @@ struct ChunkKernel {
       ck_w = ck_d = nullptr;
       if (a.ck_rows) {
         const size_t o = ck0 + cc;
-        store_state_bf16(a.ck_rows + o * D * D);
+        if (!CK_LATE || cc == 0) store_state_bf16(a.ck_rows + o * D * D);
         ck_w = a.ck_w + o * CH * D;
         ck_d = a.ck_d + o * CH * D;
       }
@@ -1037,7 +1045,7 @@ struct ChunkKernel {
   // columns.  With the chunk's forward S' = Diag(Gam) (S + Kb^T Delta),
   // (I + L) Delta = diag(b) (V - Kh S) and O = Qh S + P Delta, the chain rule
   // gives, column by column (nothing here depends on the forward state):
-  //   dU = Diag(Gam) dS'                     (stored: the per-chunk gradients use it)
+  //   dU = Diag(Gam) dS'                     (dS' is stored: the per-chunk gradients use it)
   //   dDelta = Kb dU + P^T dO
   //   Xbar = (I + L)^-T dDelta               (block back substitution with T_ii^T, L^T)
   //   dS = dU + Qh^T dO - Kh^T diag(b) Xbar  (the gradient at the chunk's start)
@@ -1063,14 +1071,16 @@ struct ChunkKernel {
           for (int m = 0; m < NKT; ++m) dob[j][m] = F::bfrag(dt[j], m);
       }
       load_v(vr, cc + 1);
-      // dU = Diag(Gam) dS', in place, and stored for the per-chunk gradients
+      // dS' for the per-chunk gradients: the launch's first chunk's here, the
+      // others' after the first barrier of the step before (DSP_LATE)
+      if (!DSP_LATE || cc == 0) store_state_bf16(a.dSp_rows + (ck0 + chunk) * D * D);
+      // dU = Diag(Gam) dS', in place
 #pragma unroll
       for (int ci = 0; ci < D / 16; ++ci) {
         const f32x4 gm = lds_ld<f32x4>(smem, st + C::S_GM + 4 * (16 * ci + kk));
 #pragma unroll
         for (int j = 0; j < NCT; ++j) S[j][ci] = S[j][ci] * gm;
       }
-      store_state_bf16(a.dU_rows + (ck0 + chunk) * D * D);
 #pragma unroll
       for (int j = 0; j < NCT; ++j)
 #pragma unroll
@@ -1301,6 +1311,12 @@ struct ChunkKernel {
       stamp(it, 1);
       sync_lds();
       stamp(it, 2);
+      if constexpr (CK_LATE) {
+        if (a.ck_rows && cc >= 0 && cc + 1 < nch) store_state_bf16(a.ck_rows + (ck0 + cc + 1) * D * D);
+      }
+      if constexpr (DSP_LATE) {
+        if (cc >= 0 && chunk_of(cc) >= 1) store_state_bf16(a.dSp_rows + (ck0 + chunk_of(cc) - 1) * D * D);
+      }
       if (C::LAG && it == nch) {  // the chunk past the end: no score tiles
         if constexpr (DEFER_O) {
           if (cc >= 0) c2(stage(cc), cc);

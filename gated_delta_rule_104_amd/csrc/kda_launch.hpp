@@ -49,13 +49,14 @@ struct ChunkArgs {
   // only, W = V - Kh S [BH, nch, CH, D] and the row's part of the strictly
   // lower blocks of Kh Kb^T [BH, nch, 10, 64 lanes, 4] (block (I, J), J <= I,
   // at I(I+1)/2 + J; lane l holds row 16I + l%16, columns 16J + 4(l/16) + e).
-  // Backward chain: dU = Diag(Gam) dS' [BH, nch, D, D] of every chunk, and
+  // Backward chain: dS' (the gradient with respect to the chunk's end state)
+  // [BH, nch, D, D] of every chunk, and
   // Xbar [BH, nch, CH, D] of its rows with beta < kTinyBeta (dv through o).
   bf16* ck_rows = nullptr;
   bf16* ck_w = nullptr;
   bf16* ck_d = nullptr;
   bf16* ck_a = nullptr;
-  bf16* dU_rows = nullptr;
+  bf16* dSp_rows = nullptr;
   bf16* ck_xb = nullptr;
   // Segments started from zero whose heads are corrected afterwards (the
   // split prefill): one record of kFlagSlots words per (segment, bh), nonzero
@@ -110,7 +111,7 @@ enum FlagMode {
 
 // Reverse chain of the prefill gradients (bf16 inputs, one segment per head):
 // S0 = dS_T [BH, D, D] or null, S_out = dS0, v = dO, o = dv [BH, T, D],
-// dU_rows and ck_xb as above; nc
+// dSp_rows and ck_xb as above; nc
 // consumer waves per workgroup ({1, 2, 4} at D = 128, {1, 2} at D = 64).
 hipError_t launch_chunk_bwd(const ChunkArgs& a, int D, int nc, int nwg, hipStream_t stream);
 
@@ -168,8 +169,7 @@ constexpr float kTinyBeta = 0x1p-30f;
 
 // Per-chunk gradients of the prefill (bf16 inputs), two workgroups per
 // (head, chunk): from the chunk's start state (the forward's checkpoint), its
-// Delta, dU = Diag(Gam) dS' (from the reverse chain) and dv (the reverse
-// chain's output).
+// Delta, dS' (from the reverse chain) and dv (the reverse chain's output).
 struct BwGradArgs {
   const void* q;
   const void* k;
@@ -180,7 +180,7 @@ struct BwGradArgs {
   // checkpoints, bf16 row-major with kpos-ordered positions (ChunkArgs::ck_*):
   const bf16* S_rows;  // the start state of every chunk [BH, nch, D, D]
   const bf16* Dl;      // Delta of every chunk [BH, nch, CH, D]
-  const bf16* dU_rows; // dU = Diag(Gam) dS' of every chunk [BH, nch, D, D]
+  const bf16* dSp_rows; // dS' of every chunk [BH, nch, D, D] (dU = Diag(Gam) dS')
   // rows with beta < kTinyBeta only:
   const bf16* W;       // W = V - Kh S [BH, nch, CH, D]
   const bf16* A;       // strictly lower blocks of Kh Kb^T [BH, nch, 10, 64, 4]

@@ -248,7 +248,7 @@ def backward(lib, q=FAKE, k=FAKE, v=FAKE, la=FAKE, beta=FAKE, S0=None, dO=FAKE, 
 
 
 def test_backward_workspace_query(lib):
-    """bf16 (chunked form): per chunk the start state and dU (bf16 D x D each),
+    """bf16 (chunked form): per chunk the start state and dS' (bf16 D x D each),
     W, Delta, Xbar (bf16 64 x D each) and the 10 lower 16x16 blocks of
     strict_lower(Kh Kb^T) (bf16), and one discarded fp32 end state per head.  fp32 (token steps):
     a checkpoint every 64 tokens plus 64 entering states (fp32 D x D) and 64
