@@ -195,6 +195,7 @@ struct ChunkKernel {
   bool mzero;       // ... and they have all become exactly zero
   f32x4 S[NCT][D / 16];
   typename F::B sb[NCT][NKD], db[NCT][NKT];
+  u32x4 dvq[4];  // reverse chain: the chunk's dv row pieces, stored after the first barrier
   // Per-lane LDS byte offsets of the consumer's A fragments inside a tile of
   // each row size, for row tile 0 (the swizzle term depends only on the lane's
   // row within 16, so row tile t adds 16*t*rowbytes).  [k block]
@@ -707,6 +708,13 @@ struct ChunkKernel {
   // Likewise the reverse chain stores dS' of chunk c - 1 (the gradient at
   // chunk c's start, which its chain has just formed) after the first barrier.
   static constexpr bool DSP_LATE = BWD && C::LAG;
+  // and its dv rows, kept in registers until then.
+  static constexpr bool DV_LATE = BWD && C::LAG;
+  // row t of this lane's dv pieces of chunk `chunk` (dv is the output o here)
+  __device__ __forceinline__ void store_dv(int chunk, int t, const u32x4& d) const {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        d, ro, (uint32_t)((chunk * CH + 16 * t + 4 * (l >> 4) + (l & 3)) * D + (colb & ~7)) * 2u, 0, 0);
+  }
   // Weight of the outputs of one chunk in score-tile units (a tile is one unit,
   // a diagonal block with its inverse two) when handing out the score tiles.
   // Per-wave timestamps put the outputs at about 2.1K cycles against about
@@ -1158,8 +1166,10 @@ struct ChunkKernel {
               u32x4{cvt2(bet[0] * Xb[0][t][0], bet[0] * Xb[1][t][0]), cvt2(bet[1] * Xb[0][t][1], bet[1] * Xb[1][t][1]),
                     cvt2(bet[2] * Xb[0][t][2], bet[2] * Xb[1][t][2]), cvt2(bet[3] * Xb[0][t][3], bet[3] * Xb[1][t][3])},
               (q & 2) != 0, (q & 1) != 0);
-          __builtin_amdgcn_raw_buffer_store_b128(d, ro,
-                                                 (uint32_t)((chunk * CH + 16 * t + kk + q) * D + (colb & ~7)) * 2u, 0, 0);
+          if constexpr (DV_LATE)
+            dvq[t] = d;
+          else
+            store_dv(chunk, t, d);
         }
       }
       // -diag(b) Xbar as B fragments over the chunk's tokens
@@ -1316,6 +1326,12 @@ struct ChunkKernel {
       }
       if constexpr (DSP_LATE) {
         if (cc >= 0 && chunk_of(cc) >= 1) store_state_bf16(a.dSp_rows + (ck0 + chunk_of(cc) - 1) * D * D);
+      }
+      if constexpr (DV_LATE) {
+        if (cc >= 0) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) store_dv(chunk_of(cc), t, dvq[t]);
+        }
       }
       if (C::LAG && it == nch) {  // the chunk past the end: no score tiles
         if constexpr (DEFER_O) {
