@@ -464,12 +464,13 @@ struct ChunkKernel {
   // off-diagonal L tiles.  Each task goes to the wave with the least work so far
   // (greedy, at compile time), every wave of the workgroup taking part.  When
   // the consumers compute the previous chunk's outputs in this interval
-  // (DEFER_O), each consumer wave starts with that step's weight.
+  // (DEFER_O), or the reverse chain's consumers store dS' and dv in it
+  // (DSP_LATE), each consumer wave starts with that step's weight.
   static constexpr int NT2 = QP ? 20 : 10;
   static constexpr int task_wave(int K) {
     int load[C::NW] = {};
-    if (DEFER_O)
-      for (int i = 0; i < NC; ++i) load[i] = kOutWeight;
+    if (DEFER_O || DSP_LATE)
+      for (int i = 0; i < NC; ++i) load[i] = DEFER_O ? kOutWeight : kStoreWeight;
     int w = 0;
     for (int k = 0; k <= K; ++k) {
       w = 0;
@@ -722,6 +723,9 @@ struct ChunkKernel {
   // or 2 (h32_t64k 0.617-0.622 ms against 0.628-0.639 for 3 and for outputs
   // computed in the first interval; 6 and 8 were slower still).
   static constexpr int kOutWeight = 2;
+  // Likewise the reverse chain's dS' and dv stores (48 KiB per chunk-head),
+  // which the consumer waves issue in this interval.
+  static constexpr int kStoreWeight = 3;
   static constexpr int C1B = 2;                    // row tiles per batch in c1
   static constexpr int C3B = TIGHT ? 2 : D / 32;   // state row tiles per batch in c3
 
