@@ -54,7 +54,7 @@ CH = 64
 # taken on: KERNEL_SOURCES_SHA is the first 16 hex digits of the SHA-256 of the
 # sources listed in kernel_sources_sha(); any change makes `traffic` null.
 TRAFFIC = {
-    "sources_sha": "ff5b9f729cb7f680",
+    "sources_sha": "c29bc817e698ec8d",
     # the kernels of one kda_chunk_prefill call at h32_t64k: the two segment-pass
     # launches (the head walk, and the pass over segments whose map did not
     # vanish, whose workgroups all exit here), the prefill of every segment from

@@ -957,7 +957,7 @@ struct ChunkKernel {
 
   // Row-major bf16 D-wide matrices with the positions inside every 32-wide
   // block of a row in the kpos order (the layout the per-chunk gradients read
-  // the state, dU and Delta in: a row of one gives an MFMA fragment over its
+  // the state, dS' and Delta in: a row of one gives an MFMA fragment over its
   // columns in one 16-byte read).  A lane holds two adjacent columns of four
   // rows; the lanes 2j, 2j+1, 2j+8, 2j+9 of a 16-lane row hold the columns of
   // position group j (positions 8j .. 8j+7 of the block: columns 4j .. 4j+3 and

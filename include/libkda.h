@@ -280,7 +280,7 @@ kda_status kda_segment_merge(const float* S_in, const float* S_zero_end, const f
  * one workgroup (or two, each with half of the state's columns) per head.
  * The workspace (device memory, at least kda_backward_workspace_bytes for the
  * same dtype, 16-byte aligned) holds, for bf16, room for those per-chunk
- * values (bf16: S and dU dk x dv each, W, Delta and Xbar 64 x dv each, the
+ * values (bf16: S and dS' dk x dv each, W, Delta and Xbar 64 x dv each, the
  * 64 x 64 lower blocks; 117 KiB per chunk-head at d = 128) and one fp32 end
  * state per head; for fp32, a state
  * checkpoint every 64 tokens, the entering
